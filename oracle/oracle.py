@@ -1,0 +1,238 @@
+"""ctypes wrapper around the C oracle (liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg import this module; the library never does. It shares no code
+with the HIP path. Inputs are promoted to float64 before the call.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "splat_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+CAM_STRIDE = 24
+NPD, NPI = 17, 13
+G_OFF = 8
+
+FLAG_ALPHA_MIN, FLAG_T_STOP, FLAG_CLAMP, FLAG_SPH_EDGE, FLAG_SPH_STOP = 1, 2, 4, 8, 16
+IMAGE_FLAGS = FLAG_ALPHA_MIN | FLAG_T_STOP | FLAG_SPH_EDGE | FLAG_SPH_STOP
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (double precision, no FP contraction)."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = C.CDLL(_SO)
+        vp, dp, ip = C.c_void_p, C.POINTER(C.c_double), C.c_int
+        L.or_create.restype = vp
+        L.or_create.argtypes = [ip, ip, ip, dp, dp, dp, dp, dp, dp, ip, dp, dp]
+        L.or_destroy.argtypes = [vp]
+        L.or_total_tiles.restype = C.c_longlong
+        L.or_total_tiles.argtypes = [vp]
+        L.or_total_pix.restype = C.c_longlong
+        L.or_total_pix.argtypes = [vp]
+        L.or_get_proj.argtypes = [vp, vp, vp]
+        L.or_bin.restype = C.c_longlong
+        L.or_bin.argtypes = [vp]
+        L.or_get_pairs.argtypes = [vp, vp, vp, vp]
+        L.or_render.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.or_render_bruteforce.argtypes = [vp, ip, vp, vp, vp, vp]
+        L.or_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _d(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.POINTER(C.c_double))
+
+
+def _vp(a):
+    return None if a is None else C.c_void_p(a.ctypes.data)
+
+
+def pack_cams(cams) -> np.ndarray:
+    out = np.zeros((len(cams), CAM_STRIDE), dtype=np.float64)
+    for v, c in enumerate(cams):
+        out[v, 0] = c.kind
+        out[v, 1] = c.width
+        out[v, 2] = c.height
+        out[v, 3:12] = np.asarray(c.R, dtype=np.float64).reshape(9)
+        out[v, 12:15] = np.asarray(c.t, dtype=np.float64)
+        out[v, 15:23] = [c.fx, c.fy, c.cx, c.cy, c.el_min_deg, c.el_max_deg, c.znear, c.zfar]
+    return out
+
+
+def pack_params(params, channels) -> np.ndarray:
+    bg = np.zeros(channels) if params.background is None else np.asarray(params.background, np.float64)
+    head = [params.alpha_min, params.alpha_max, params.T_min, params.gamma, params.bg_weight,
+            params.tau, params.top_k]
+    return np.ascontiguousarray(np.concatenate([np.asarray(head, np.float64), bg]))
+
+
+class Oracle:
+    """Projection, binning, compositing and gradients of one scene in float64.
+
+    Arrays may be float32 (promoted exactly) or float64 (for finite differences).
+    """
+
+    def __init__(self, scene, pos=None, scale=None, rot=None, opacity=None, feat=None,
+                 depth=None, cams=None, params=None, packed_cams=None):
+        s = scene
+        self.kind, self.n, self.C = s.kind, s.n, s.channels
+        self.cams = list(cams if cams is not None else s.cams)
+        self.V = len(self.cams)
+        self.params = params if params is not None else s.params
+        self.K = self.params.top_k
+        pick = lambda a, b: _d(a if a is not None else b)
+        self._keep = [pick(pos, s.pos), pick(scale, s.scale), pick(rot, s.rot),
+                      pick(opacity, s.opacity), pick(depth, s.depth), pick(feat, s.feat),
+                      pack_cams(self.cams) if packed_cams is None else _d(packed_cams),
+                      pack_params(self.params, self.C)]
+        a = self._keep
+        self.h = lib().or_create(self.kind, self.n, self.C, _p(a[0]), _p(a[1]), _p(a[2]), _p(a[3]),
+                                 _p(a[4]), _p(a[5]), self.V, _p(a[6]), _p(a[7]))
+        self.total_tiles = lib().or_total_tiles(self.h)
+        self.total_pix = lib().or_total_pix(self.h)
+        self.npairs = None
+
+    def close(self):
+        if self.h:
+            lib().or_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- projection -----------------------------------------------------
+    def proj(self) -> dict:
+        NV = self.V * self.n
+        d = np.zeros((NV, NPD), np.float64)
+        i = np.zeros((NV, NPI), np.int64)
+        lib().or_get_proj(self.h, _vp(d), _vp(i))
+        names_d = ["u", "v", "sxx", "sxy", "syy", "ca", "cb", "cc", "depth", "m0", "m1", "m2",
+                   "r_eff", "e", "b", "zhat", "opac"]
+        names_i = ["valid", "x0", "x1", "y0", "y1", "tx0", "ntx", "ty0", "ty1", "ntiles",
+                   "key_bits", "floored", "gated"]
+        out = {k: d[:, j] for j, k in enumerate(names_d)}
+        out.update({k: i[:, j] for j, k in enumerate(names_i)})
+        return out
+
+    # ---- binning --------------------------------------------------------
+    def bin(self) -> int:
+        self.npairs = lib().or_bin(self.h)
+        return self.npairs
+
+    def pairs(self):
+        if self.npairs is None:
+            self.bin()
+        keys = np.zeros(self.npairs, np.uint64)
+        vals = np.zeros(self.npairs, np.uint32)
+        ranges = np.zeros((self.total_tiles, 2), np.uint32)
+        lib().or_get_pairs(self.h, _vp(keys), _vp(vals), _vp(ranges))
+        return keys, vals, ranges
+
+    # ---- forward --------------------------------------------------------
+    def render(self, pix=None) -> dict:
+        """Composite the given global pixel ids (default: every pixel of every view)."""
+        if self.npairs is None:
+            self.bin()
+        if pix is not None:
+            pix = np.ascontiguousarray(np.asarray(pix, dtype=np.int64))
+            cnt = len(pix)
+        else:
+            cnt = self.total_pix
+        Cm = max(self.C, 2)
+        img = np.zeros((cnt, Cm))
+        T = np.zeros(cnt)
+        last = np.zeros(cnt, np.int64)
+        N = np.zeros(cnt)
+        top = np.zeros((cnt, max(self.K, 1)), np.int32)
+        flags = np.zeros(cnt, np.int32)
+        proc = np.zeros(cnt, np.int64)
+        ncon = np.zeros(cnt, np.int64)
+        lib().or_render(self.h, cnt, _vp(pix), _vp(img), _vp(T), _vp(last), _vp(N), _vp(top),
+                        _vp(flags), _vp(proc), _vp(ncon))
+        return dict(img=img, T=T, last=last, N=N, top=top[:, :self.K], flags=flags,
+                    processed=proc, ncontrib=ncon)
+
+    def render_views(self) -> list:
+        """Full images per view as dicts of [C,H,W] / [H,W] arrays."""
+        r = self.render()
+        out, off = [], 0
+        for c in self.cams:
+            hw = c.width * c.height
+            sl = slice(off, off + hw)
+            Cv = 2 if c.kind == 1 else self.C
+            out.append(dict(img=r["img"][sl, :Cv].T.reshape(Cv, c.height, c.width),
+                            T=r["T"][sl].reshape(c.height, c.width),
+                            last=r["last"][sl].reshape(c.height, c.width),
+                            N=r["N"][sl].reshape(c.height, c.width),
+                            top=r["top"][sl].reshape(c.height, c.width, self.K),
+                            flags=r["flags"][sl].reshape(c.height, c.width),
+                            processed=r["processed"][sl].reshape(c.height, c.width),
+                            ncontrib=r["ncontrib"][sl].reshape(c.height, c.width)))
+            off += hw
+        return out
+
+    def render_bruteforce(self, view=0) -> dict:
+        c = self.cams[view]
+        hw = c.width * c.height
+        Cm = max(self.C, 2)
+        img = np.zeros((hw, Cm))
+        T = np.zeros(hw)
+        N = np.zeros(hw)
+        top = np.zeros((hw, max(self.K, 1)), np.int32)
+        lib().or_render_bruteforce(self.h, view, _vp(img), _vp(T), _vp(N), _vp(top))
+        Cv = 2 if c.kind == 1 else self.C
+        return dict(img=img[:, :Cv].T.reshape(Cv, c.height, c.width), T=T.reshape(c.height, c.width),
+                    N=N.reshape(c.height, c.width), top=top[:, :self.K].reshape(c.height, c.width, self.K))
+
+    # ---- backward -------------------------------------------------------
+    def backward(self, dimg_views) -> dict:
+        """dimg_views: list of [Cv,H,W] arrays (one per view). Returns float64 grads."""
+        if self.npairs is None:
+            self.bin()
+        g = np.ascontiguousarray(np.concatenate([np.asarray(a, np.float32).reshape(-1)
+                                                 for a in dimg_views]))
+        n, Cc = self.n, self.C
+        pd = 2 if self.kind == 0 else 3
+        sd = 3 if self.kind == 1 else 1
+        dpos = np.zeros((n, pd))
+        dscale = np.zeros((n, sd)) if sd > 1 else np.zeros(n)
+        drot = np.zeros((n, 4)) if self.kind == 1 else None
+        dop = np.zeros(n)
+        dfeat = np.zeros((n, Cc)) if Cc > 0 else None
+        dR = np.zeros((self.V, 3, 3))
+        dt = np.zeros((self.V, 3))
+        acc = np.zeros((self.V * n, G_OFF + Cc))
+        lib().or_backward(self.h, _vp(g), _vp(dpos), _vp(dscale), _vp(drot), _vp(dop), _vp(dfeat),
+                          _vp(dR), _vp(dt), _vp(acc))
+        return dict(pos=dpos, scale=dscale, rot=drot, opacity=dop, feat=dfeat, cam_R=dR, cam_t=dt,
+                    acc=acc)

@@ -1,0 +1,973 @@
+/*
+ * CPU oracle for the tile rasterizer of point primitives.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the library's product path may link,
+ * load or call this file; only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg do. It shares no code with the HIP kernels.
+ *
+ * Plain, slow, double precision. It follows the method step by step:
+ *   project every primitive            (Pulsar, sec. B.1.1 "Step 0: enclosing
+ *                                        rectangle"; EWA splatting for Gaussians)
+ *   bin to 16x16 tiles and sort each    (Pulsar, sec. B.1.1 depth sort and
+ *   tile's list by depth                 sec. B.1.2 16x16 blocks)
+ *   composite per pixel front to back   (Pulsar sec. 3.2 and B.1.3 for spheres;
+ *                                        alpha blending for Gaussian splats)
+ *   reverse-mode gradients per pixel,   (Pulsar sec. B.2; NuRec page,
+ *   then chain rule per primitive        "renderBackward")
+ * The exact formulas are readings of the pages (they print none); each one is
+ * listed with its reading in the design notes of the repository.
+ *
+ * Integer outputs (pixel rectangles, tile lists, sort keys) come from the same
+ * double-precision expressions the GPU evaluates, written in the same operand
+ * order with no contraction (build with -ffp-contract=off), so that both sides
+ * take the binning decisions identically.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { PRIM_GAUSS2D = 0, PRIM_GAUSS3D = 1, PRIM_SPHERE = 2 };
+enum { CAM_PINHOLE = 0, CAM_SPHERICAL = 1 };
+
+/* near-tie flag bits (per pixel) */
+enum {
+  FLAG_ALPHA_MIN = 1,   /* an alpha within 1e-5 (relative) of the skip threshold */
+  FLAG_T_STOP = 2,      /* transmittance within 2e-4 (relative) of the stop threshold */
+  FLAG_CLAMP = 4,       /* opacity*G within 1e-5 (relative) of the 0.99 clamp */
+  FLAG_SPH_EDGE = 8,    /* a sphere's distance factor within 1e-5 of 0 (top-K may flip) */
+  FLAG_SPH_STOP = 16    /* a stop bound within 1e-4 (relative) of tau*N */
+};
+
+#define CAM_STRIDE 24
+#define TILE 16
+/* support constant of the Gaussian footprint: 2 ln 255 (alpha >= 1/255 needs power <= ln 255) */
+static double k_support(void) { return 2.0 * log(255.0); }
+
+typedef struct {
+  int kind, width, height, tiles_x, tiles_y;
+  long long tile_off, pix_off;
+  double R[9], t[3], fx, fy, cx, cy, el_min, el_max, znear, zfar;
+} ocam;
+
+typedef struct {
+  int valid;
+  long long x0, x1, y0, y1;     /* inclusive pixel range (x unclipped for spherical) */
+  int tx0, ntx, ty0, ty1;       /* tile columns tx0..tx0+ntx-1 (mod tiles_x), rows ty0..ty1 */
+  long long ntiles;
+  float key_depth;
+  double depth;                 /* m_z, range, given depth, or sphere front depth */
+  double m[3];                  /* sensor-frame centre */
+  double u, v;
+  double sxx, sxy, syy;         /* 2D covariance */
+  double ca, cb, cc;            /* conic */
+  double opac;
+  /* sphere */
+  double r, r_eff, e, b, zhat;
+  int floored, gated;
+} orec;
+
+typedef struct {
+  int kind, n, C, V, K;
+  double *pos, *scale, *rot, *opac, *depth, *feat;   /* inputs, promoted to double */
+  double alpha_min, alpha_max, T_min, gamma, bg_weight, tau;
+  double *bg;
+  ocam *cams;
+  long long total_tiles, total_pix;
+  orec *rec;                    /* [V*n] */
+  /* tile lists */
+  long long npairs;
+  long long *tile_start;        /* [total_tiles+1] */
+  uint32_t *pair_id;            /* [npairs] record index v*n+i, sorted per tile */
+  uint32_t *pair_bits;          /* [npairs] fp32 depth bits */
+} octx;
+
+static int pdim(int kind) { return kind == PRIM_GAUSS2D ? 2 : 3; }
+static int sdim(int kind) { return kind == PRIM_GAUSS3D ? 3 : 1; }
+
+static double *dup_d(const double *a, long long count) {
+  if (!a) return NULL;
+  double *p = (double *)malloc(sizeof(double) * (size_t)(count > 0 ? count : 1));
+  memcpy(p, a, sizeof(double) * (size_t)count);
+  return p;
+}
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* ------------------------------------------------------------------------- */
+/* Projection (Pulsar sec. B.1.1; EWA splatting for the Gaussian covariance)  */
+/* ------------------------------------------------------------------------- */
+
+/* world -> sensor: m = R x + t, each row summed left to right */
+static void cam_xform(const ocam *c, const double x[3], double m[3]) {
+  for (int i = 0; i < 3; i++)
+    m[i] = c->R[3 * i + 0] * x[0] + c->R[3 * i + 1] * x[1] + c->R[3 * i + 2] * x[2] + c->t[i];
+}
+
+/* Unit-quaternion (w,x,y,z) rotation matrix, row-major. */
+static void quat_rot(const double qn[4], double Rq[9]) {
+  double w = qn[0], x = qn[1], y = qn[2], z = qn[3];
+  Rq[0] = 1.0 - 2.0 * (y * y + z * z);
+  Rq[1] = 2.0 * (x * y - w * z);
+  Rq[2] = 2.0 * (x * z + w * y);
+  Rq[3] = 2.0 * (x * y + w * z);
+  Rq[4] = 1.0 - 2.0 * (x * x + z * z);
+  Rq[5] = 2.0 * (y * z - w * x);
+  Rq[6] = 2.0 * (x * z - w * y);
+  Rq[7] = 2.0 * (y * z + w * x);
+  Rq[8] = 1.0 - 2.0 * (x * x + y * y);
+}
+
+/* Jacobian of the image mapping at sensor point m, and mean 2D position.
+ * Pinhole: u = fx mx/mz + cx. Spherical: u = (pi - atan2(my,mx)) W/(2pi),
+ * v = (el_max - atan2(mz, rho)) H/(el_max - el_min). */
+static void image_map(const ocam *c, const double m[3], double J[6], double *u, double *v) {
+  if (c->kind == CAM_PINHOLE) {
+    J[0] = c->fx / m[2];
+    J[1] = 0.0;
+    J[2] = -(c->fx * m[0]) / (m[2] * m[2]);
+    J[3] = 0.0;
+    J[4] = c->fy / m[2];
+    J[5] = -(c->fy * m[1]) / (m[2] * m[2]);
+    *u = c->fx * m[0] / m[2] + c->cx;
+    *v = c->fy * m[1] / m[2] + c->cy;
+  } else {
+    double rho2 = m[0] * m[0] + m[1] * m[1];
+    double rho = sqrt(rho2);
+    double r2 = rho2 + m[2] * m[2];
+    double th_max = c->el_max * (M_PI / 180.0), th_min = c->el_min * (M_PI / 180.0);
+    double a = (double)c->width / (2.0 * M_PI);
+    double b = (double)c->height / (th_max - th_min);
+    J[0] = a * m[1] / rho2;
+    J[1] = -(a * m[0]) / rho2;
+    J[2] = 0.0;
+    J[3] = b * m[0] * m[2] / (r2 * rho);
+    J[4] = b * m[1] * m[2] / (r2 * rho);
+    J[5] = -(b * rho) / r2;
+    *u = (M_PI - atan2(m[1], m[0])) * a;
+    *v = (th_max - atan2(m[2], rho)) * b;
+  }
+}
+
+static void set_rect_empty(orec *o) { o->valid = 0; o->ntiles = 0; }
+
+/* Pixel rectangle [xl, xh] x [yl, yh] (pixel-centre coordinates, double) to
+ * clipped pixel and tile ranges; columns wrap for the spherical sensor. */
+static void set_rect(const ocam *c, orec *o, double xl, double xh, double yl, double yh) {
+  double fx0 = ceil(xl - 0.5), fx1 = floor(xh - 0.5);
+  double fy0 = ceil(yl - 0.5), fy1 = floor(yh - 0.5);
+  if (fy0 < 0.0) fy0 = 0.0;
+  if (fy1 > (double)(c->height - 1)) fy1 = (double)(c->height - 1);
+  if (c->kind != CAM_SPHERICAL) {
+    if (fx0 < 0.0) fx0 = 0.0;
+    if (fx1 > (double)(c->width - 1)) fx1 = (double)(c->width - 1);
+  } else if (fx1 - fx0 + 1.0 >= (double)c->width) {
+    /* a span of a full turn or more covers every column once */
+    fx0 = 0.0;
+    fx1 = (double)(c->width - 1);
+  }
+  if (!(fx0 <= fx1) || !(fy0 <= fy1)) { set_rect_empty(o); return; }
+  o->x0 = (long long)fx0; o->x1 = (long long)fx1;
+  o->y0 = (long long)fy0; o->y1 = (long long)fy1;
+  o->ty0 = (int)(o->y0 / TILE); o->ty1 = (int)(o->y1 / TILE);
+  if (c->kind != CAM_SPHERICAL) {
+    o->tx0 = (int)(o->x0 / TILE);
+    o->ntx = (int)(o->x1 / TILE) - o->tx0 + 1;
+  } else {
+    long long a0 = o->x0 >= 0 ? o->x0 / TILE : -((-o->x0 + TILE - 1) / TILE);
+    long long a1 = o->x1 >= 0 ? o->x1 / TILE : -((-o->x1 + TILE - 1) / TILE);
+    long long nt = a1 - a0 + 1;
+    if (nt > c->tiles_x) nt = c->tiles_x;
+    long long m = a0 % c->tiles_x;
+    if (m < 0) m += c->tiles_x;
+    o->tx0 = (int)m;
+    o->ntx = (int)nt;
+  }
+  o->ntiles = (long long)o->ntx * (long long)(o->ty1 - o->ty0 + 1);
+  o->valid = 1;
+}
+
+static void project_one(const octx *X, int view, int i, orec *o) {
+  const ocam *c = &X->cams[view];
+  memset(o, 0, sizeof(*o));
+  o->opac = (double)X->opac[i];
+  const double K = k_support();
+  if (X->kind == PRIM_SPHERE) {
+    double p[3] = {X->pos[3 * i], X->pos[3 * i + 1], X->pos[3 * i + 2]};
+    double r = (double)X->scale[i];
+    double q[3];
+    cam_xform(c, p, q);
+    double fmin = c->fx < c->fy ? c->fx : c->fy;
+    double rfl = 0.75 * q[2] / fmin;          /* at least one pixel (Pulsar B.1.1) */
+    double re = r >= rfl ? r : rfl;
+    o->m[0] = q[0]; o->m[1] = q[1]; o->m[2] = q[2];
+    o->r = r; o->r_eff = re; o->floored = r < rfl;
+    double zf = q[2] - re;
+    if (!(zf > c->znear) || !(zf > 0.0) || !isfinite(r) || !(r > 0.0)) { set_rect_empty(o); return; }
+    /* tangent planes through the sensor origin, trig-free (Pulsar B.1.1) */
+    double den = q[2] * q[2] - re * re;
+    double sx = sqrt(q[0] * q[0] + q[2] * q[2] - re * re);
+    double sy = sqrt(q[1] * q[1] + q[2] * q[2] - re * re);
+    double xl = c->fx * ((q[0] * q[2] - re * sx) / den) + c->cx;
+    double xh = c->fx * ((q[0] * q[2] + re * sx) / den) + c->cx;
+    double yl = c->fy * ((q[1] * q[2] - re * sy) / den) + c->cy;
+    double yh = c->fy * ((q[1] * q[2] + re * sy) / den) + c->cy;
+    if (!isfinite(xl) || !isfinite(xh) || !isfinite(yl) || !isfinite(yh)) { set_rect_empty(o); return; }
+    o->u = c->fx * q[0] / q[2] + c->cx;
+    o->v = c->fy * q[1] / q[2] + c->cy;
+    o->depth = zf;
+    o->key_depth = (float)zf;
+    double span = c->zfar - c->znear;
+    o->zhat = (c->zfar - q[2]) / span;
+    o->e = exp(o->opac * o->zhat / X->gamma);
+    o->b = exp(((c->zfar - (double)o->key_depth) / span) / X->gamma);
+    double area = M_PI * (c->fx * r / q[2]) * (c->fy * r / q[2]);
+    o->gated = !(area > 3.0);                   /* Pulsar sec. 6 / A: > 3 projected pixels */
+    set_rect(c, o, xl, xh, yl, yh);
+    return;
+  }
+  double m[3], u, v, sxx, sxy, syy;
+  if (X->kind == PRIM_GAUSS2D) {
+    u = (double)X->pos[2 * i];
+    v = (double)X->pos[2 * i + 1];
+    double s = (double)X->scale[i];
+    sxx = s * s; syy = s * s; sxy = 0.0;
+    o->depth = X->depth[i];
+    o->key_depth = (float)X->depth[i];
+    m[0] = m[1] = 0.0; m[2] = o->depth;
+  } else {
+    double mu[3] = {X->pos[3 * i], X->pos[3 * i + 1], X->pos[3 * i + 2]};
+    double s[3] = {X->scale[3 * i], X->scale[3 * i + 1], X->scale[3 * i + 2]};
+    double qq[4] = {X->rot[4 * i], X->rot[4 * i + 1], X->rot[4 * i + 2], X->rot[4 * i + 3]};
+    double nq = sqrt(qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3]);
+    double qn[4] = {qq[0] / nq, qq[1] / nq, qq[2] / nq, qq[3] / nq};
+    double Rq[9], M[9], S3[9];
+    quat_rot(qn, Rq);
+    for (int a = 0; a < 3; a++)
+      for (int b = 0; b < 3; b++) M[3 * a + b] = Rq[3 * a + b] * s[b];
+    for (int a = 0; a < 3; a++)
+      for (int b = 0; b < 3; b++)
+        S3[3 * a + b] = M[3 * a] * M[3 * b] + M[3 * a + 1] * M[3 * b + 1] + M[3 * a + 2] * M[3 * b + 2];
+    cam_xform(c, mu, m);
+    if (c->kind == CAM_PINHOLE) {
+      if (!(m[2] > c->znear)) { set_rect_empty(o); return; }
+      o->depth = m[2];
+    } else {
+      double rho2 = m[0] * m[0] + m[1] * m[1];
+      double rr = sqrt(rho2 + m[2] * m[2]);
+      if (!(rr > c->znear) || !(rho2 > 0.0)) { set_rect_empty(o); return; }
+      o->depth = rr;
+    }
+    o->key_depth = (float)o->depth;
+    double J[6], T[6], U[6];
+    image_map(c, m, J, &u, &v);
+    for (int a = 0; a < 2; a++)
+      for (int b = 0; b < 3; b++)
+        T[3 * a + b] = J[3 * a] * c->R[b] + J[3 * a + 1] * c->R[3 + b] + J[3 * a + 2] * c->R[6 + b];
+    for (int a = 0; a < 2; a++)
+      for (int b = 0; b < 3; b++)
+        U[3 * a + b] = T[3 * a] * S3[b] + T[3 * a + 1] * S3[3 + b] + T[3 * a + 2] * S3[6 + b];
+    sxx = U[0] * T[0] + U[1] * T[1] + U[2] * T[2];
+    sxy = U[0] * T[3] + U[1] * T[4] + U[2] * T[5];
+    syy = U[3] * T[3] + U[4] * T[4] + U[5] * T[5];
+  }
+  o->m[0] = m[0]; o->m[1] = m[1]; o->m[2] = m[2];
+  o->u = u; o->v = v; o->sxx = sxx; o->sxy = sxy; o->syy = syy;
+  double det = sxx * syy - sxy * sxy;
+  if (!(det > 0.0) || !(o->depth > 0.0) || !isfinite(u) || !isfinite(v)) { set_rect_empty(o); return; }
+  o->ca = syy / det; o->cb = -sxy / det; o->cc = sxx / det;
+  double hx = sqrt(K * sxx), hy = sqrt(K * syy);
+  if (!isfinite(hx) || !isfinite(hy)) { set_rect_empty(o); return; }
+  set_rect(c, o, u - hx, u + hx, v - hy, v + hy);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Context                                                                    */
+/* ------------------------------------------------------------------------- */
+
+void or_destroy(octx *X) {
+  if (!X) return;
+  free(X->pos); free(X->scale); free(X->rot); free(X->opac); free(X->depth); free(X->feat);
+  free(X->bg); free(X->cams); free(X->rec); free(X->tile_start); free(X->pair_id); free(X->pair_bits);
+  free(X);
+}
+
+/* params: alpha_min, alpha_max, T_min, gamma, bg_weight, tau, top_k, then bg[C] */
+octx *or_create(int kind, int n, int C, const double *pos, const double *scale, const double *rot,
+                const double *opac, const double *depth, const double *feat, int V, const double *cams,
+                const double *params) {
+  octx *X = (octx *)calloc(1, sizeof(octx));
+  X->kind = kind; X->n = n; X->C = C; X->V = V;
+  X->pos = dup_d(pos, (long long)n * pdim(kind));
+  X->scale = dup_d(scale, (long long)n * sdim(kind));
+  X->rot = dup_d(rot, kind == PRIM_GAUSS3D ? (long long)n * 4 : 0);
+  X->opac = dup_d(opac, n);
+  X->depth = dup_d(depth, kind == PRIM_GAUSS2D ? n : 0);
+  X->feat = feat ? dup_d(feat, (long long)n * C) : NULL;
+  X->alpha_min = params[0]; X->alpha_max = params[1]; X->T_min = params[2];
+  X->gamma = params[3]; X->bg_weight = params[4]; X->tau = params[5]; X->K = (int)params[6];
+  X->bg = (double *)calloc((size_t)(C > 0 ? C : 1), sizeof(double));
+  for (int c = 0; c < C; c++) X->bg[c] = params[7 + c];
+  X->cams = (ocam *)calloc((size_t)V, sizeof(ocam));
+  long long toff = 0, poff = 0;
+  for (int v = 0; v < V; v++) {
+    const double *a = cams + (size_t)CAM_STRIDE * v;
+    ocam *c = &X->cams[v];
+    c->kind = (int)a[0]; c->width = (int)a[1]; c->height = (int)a[2];
+    for (int k = 0; k < 9; k++) c->R[k] = a[3 + k];
+    for (int k = 0; k < 3; k++) c->t[k] = a[12 + k];
+    c->fx = a[15]; c->fy = a[16]; c->cx = a[17]; c->cy = a[18];
+    c->el_min = a[19]; c->el_max = a[20]; c->znear = a[21]; c->zfar = a[22];
+    c->tiles_x = (c->width + TILE - 1) / TILE;
+    c->tiles_y = (c->height + TILE - 1) / TILE;
+    c->tile_off = toff; c->pix_off = poff;
+    toff += (long long)c->tiles_x * c->tiles_y;
+    poff += (long long)c->width * c->height;
+  }
+  X->total_tiles = toff; X->total_pix = poff;
+  X->rec = (orec *)calloc((size_t)V * (size_t)n + 1, sizeof(orec));
+  #pragma omp parallel for schedule(static)
+  for (long long k = 0; k < (long long)V * n; k++) project_one(X, (int)(k / n), (int)(k % n), &X->rec[k]);
+  return X;
+}
+
+long long or_total_tiles(const octx *X) { return X->total_tiles; }
+long long or_total_pix(const octx *X) { return X->total_pix; }
+
+/* Per record: [u, v, sxx, sxy, syy, ca, cb, cc, depth, m0, m1, m2, r_eff, e, b, zhat, opac]
+ * and ints [valid, x0, x1, y0, y1, tx0, ntx, ty0, ty1, ntiles, key_bits, floored, gated] */
+#define NPD 17
+#define NPI 13
+void or_get_proj(const octx *X, double *d, long long *ii) {
+  for (long long k = 0; k < (long long)X->V * X->n; k++) {
+    const orec *o = &X->rec[k];
+    double *p = d + NPD * k;
+    p[0] = o->u; p[1] = o->v; p[2] = o->sxx; p[3] = o->sxy; p[4] = o->syy;
+    p[5] = o->ca; p[6] = o->cb; p[7] = o->cc; p[8] = o->depth;
+    p[9] = o->m[0]; p[10] = o->m[1]; p[11] = o->m[2];
+    p[12] = o->r_eff; p[13] = o->e; p[14] = o->b; p[15] = o->zhat; p[16] = o->opac;
+    long long *q = ii + NPI * k;
+    q[0] = o->valid; q[1] = o->x0; q[2] = o->x1; q[3] = o->y0; q[4] = o->y1;
+    q[5] = o->tx0; q[6] = o->ntx; q[7] = o->ty0; q[8] = o->ty1; q[9] = o->valid ? o->ntiles : 0;
+    q[10] = o->valid ? f32_bits(o->key_depth) : 0; q[11] = o->floored; q[12] = o->gated;
+  }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Binning and per-tile depth sort                                            */
+/* ------------------------------------------------------------------------- */
+
+typedef struct { uint32_t bits, id; } opair;
+
+static int cmp_pair(const void *a, const void *b) {
+  const opair *x = (const opair *)a, *y = (const opair *)b;
+  if (x->bits != y->bits) return x->bits < y->bits ? -1 : 1;
+  if (x->id != y->id) return x->id < y->id ? -1 : 1;
+  return 0;
+}
+
+/* Every (tile, record) overlap, then each tile's list sorted by (fp32 depth bits, id). */
+long long or_bin(octx *X) {
+  long long T = X->total_tiles, NV = (long long)X->V * X->n;
+  long long *cnt = (long long *)calloc((size_t)T + 1, sizeof(long long));
+  for (long long k = 0; k < NV; k++) {
+    const orec *o = &X->rec[k];
+    if (!o->valid) continue;
+    const ocam *c = &X->cams[k / X->n];
+    for (int ty = o->ty0; ty <= o->ty1; ty++)
+      for (int a = 0; a < o->ntx; a++) {
+        int tx = (o->tx0 + a) % c->tiles_x;
+        cnt[c->tile_off + (long long)ty * c->tiles_x + tx]++;
+      }
+  }
+  free(X->tile_start); free(X->pair_id); free(X->pair_bits);
+  X->tile_start = (long long *)calloc((size_t)T + 1, sizeof(long long));
+  for (long long t = 0; t < T; t++) X->tile_start[t + 1] = X->tile_start[t] + cnt[t];
+  X->npairs = X->tile_start[T];
+  opair *pairs = (opair *)malloc(sizeof(opair) * (size_t)(X->npairs + 1));
+  for (long long t = 0; t < T; t++) cnt[t] = X->tile_start[t];
+  for (long long k = 0; k < NV; k++) {
+    const orec *o = &X->rec[k];
+    if (!o->valid) continue;
+    const ocam *c = &X->cams[k / X->n];
+    for (int ty = o->ty0; ty <= o->ty1; ty++)
+      for (int a = 0; a < o->ntx; a++) {
+        int tx = (o->tx0 + a) % c->tiles_x;
+        long long t = c->tile_off + (long long)ty * c->tiles_x + tx;
+        opair pr = {f32_bits(o->key_depth), (uint32_t)k};
+        pairs[cnt[t]++] = pr;
+      }
+  }
+  #pragma omp parallel for schedule(dynamic, 16)
+  for (long long t = 0; t < T; t++) {
+    long long s = X->tile_start[t], e = X->tile_start[t + 1];
+    if (e - s > 1) qsort(pairs + s, (size_t)(e - s), sizeof(opair), cmp_pair);
+  }
+  X->pair_id = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(X->npairs + 1));
+  X->pair_bits = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(X->npairs + 1));
+  for (long long p = 0; p < X->npairs; p++) { X->pair_id[p] = pairs[p].id; X->pair_bits[p] = pairs[p].bits; }
+  free(pairs); free(cnt);
+  return X->npairs;
+}
+
+/* keys = (global tile << 32) | depth bits, vals = record index; ranges [T][2] */
+void or_get_pairs(const octx *X, uint64_t *keys, uint32_t *vals, uint32_t *ranges) {
+  for (long long t = 0; t < X->total_tiles; t++) {
+    long long s = X->tile_start[t], e = X->tile_start[t + 1];
+    if (ranges) { ranges[2 * t] = (uint32_t)(e > s ? s : 0); ranges[2 * t + 1] = (uint32_t)(e > s ? e : 0); }
+    for (long long p = s; p < e; p++) {
+      if (keys) keys[p] = ((uint64_t)t << 32) | X->pair_bits[p];
+      if (vals) vals[p] = X->pair_id[p];
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Per-pixel compositing                                                      */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {          /* per-entry trace kept for the backward pass */
+  int idx;                /* position in the tile list */
+  uint32_t rec;
+  double alpha, T_before, G, dx, dy;   /* alpha path */
+  int clamped;
+  double w, D, dist2;                  /* sphere path */
+  double d[3], dd;
+} otrace;
+
+typedef struct {
+  double col[64 + 2];
+  double T, N, dep;
+  long long last, ncontrib, processed;
+  int32_t top[16];
+  int ntop, flags;
+} opix;
+
+static int find_view(const octx *X, long long gpix) {
+  int v = 0;
+  while (v + 1 < X->V && X->cams[v + 1].pix_off <= gpix) v++;
+  return v;
+}
+
+static double wrap_dx(double dx, int W) {
+  double h = 0.5 * (double)W;
+  if (dx >= h) dx -= (double)W;
+  else if (dx < -h) dx += (double)W;
+  return dx;
+}
+
+/* Composite one pixel over its tile's sorted list. tr (optional) receives the
+ * composited entries in front-to-back order; returns their number. */
+static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_cap) {
+  int v = find_view(X, gpix);
+  const ocam *c = &X->cams[v];
+  long long lp = gpix - c->pix_off;
+  int i = (int)(lp % c->width), j = (int)(lp / c->width);
+  long long t = c->tile_off + (long long)(j / TILE) * c->tiles_x + (i / TILE);
+  long long s = X->tile_start[t], e = X->tile_start[t + 1];
+  int C = X->C, ntr = 0;
+  memset(P, 0, sizeof(*P));
+  for (int k = 0; k < 16; k++) P->top[k] = -1;
+  double px = (double)i + 0.5, py = (double)j + 0.5;
+  if (X->kind == PRIM_SPHERE) {
+    double d[3] = {(px - c->cx) / c->fx, (py - c->cy) / c->fy, 1.0};
+    double dd = d[0] * d[0] + d[1] * d[1] + d[2] * d[2];
+    double N = X->bg_weight;
+    double S[64];
+    for (int ch = 0; ch < C; ch++) S[ch] = X->bg_weight * X->bg[ch];
+    for (long long p = s; p < e; p++) {
+      const orec *o = &X->rec[X->pair_id[p]];
+      P->processed++;
+      double lim = X->tau * N;
+      if (fabs(o->b - lim) <= 1e-4 * lim) P->flags |= FLAG_SPH_STOP;
+      if (o->b < lim) break;                                   /* early stop (Pulsar 3.2, B.1.3) */
+      const double *q = o->m;
+      double qd = q[0] * d[0] + q[1] * d[1] + q[2] * d[2];
+      double qq = q[0] * q[0] + q[1] * q[1] + q[2] * q[2];
+      double dist2 = qq - qd * qd / dd;                        /* orthogonal ray distance^2 */
+      double r2 = o->r_eff * o->r_eff;
+      double D = 1.0 - dist2 / r2;
+      if (fabs(D) < 1e-5 && P->ntop < X->K) P->flags |= FLAG_SPH_EDGE;
+      if (!(dist2 < r2)) continue;
+      double w = o->opac * D * o->e;
+      N += w;
+      uint32_t id = X->pair_id[p] % (uint32_t)X->n;
+      for (int ch = 0; ch < C; ch++) S[ch] += w * X->feat[(size_t)id * C + ch];
+      P->ncontrib++;
+      P->last = p - s + 1;
+      if (P->ntop < X->K) {
+        P->top[P->ntop++] = (int32_t)id;
+        if (tr && ntr < tr_cap) {
+          otrace *r = &tr[ntr++];
+          r->idx = (int)(p - s); r->rec = X->pair_id[p]; r->w = w; r->D = D; r->dist2 = dist2;
+          r->d[0] = d[0]; r->d[1] = d[1]; r->d[2] = d[2]; r->dd = dd;
+        }
+      }
+    }
+    P->N = N;
+    for (int ch = 0; ch < C; ch++) P->col[ch] = S[ch] / N;
+    return ntr;
+  }
+  /* alpha compositing of Gaussian splats, front to back */
+  int lidar = c->kind == CAM_SPHERICAL;
+  double T = 1.0, dep = 0.0;
+  double Ccol[64];
+  for (int ch = 0; ch < C; ch++) Ccol[ch] = 0.0;
+  for (long long p = s; p < e; p++) {
+    const orec *o = &X->rec[X->pair_id[p]];
+    P->processed++;
+    double dx = px - o->u, dy = py - o->v;
+    if (lidar) dx = wrap_dx(dx, c->width);
+    double power = 0.5 * (o->ca * dx * dx + 2.0 * o->cb * dx * dy + o->cc * dy * dy);
+    double G = exp(-power);
+    double og = o->opac * G;
+    double a = og > X->alpha_max ? X->alpha_max : og;
+    if (fabs(og - X->alpha_max) <= 1e-5 * X->alpha_max) P->flags |= FLAG_CLAMP;
+    if (fabs(a - X->alpha_min) <= 1e-5 * X->alpha_min) P->flags |= FLAG_ALPHA_MIN;
+    if (a < X->alpha_min) continue;
+    double w = T * a;
+    uint32_t id = X->pair_id[p] % (uint32_t)X->n;
+    if (!lidar)
+      for (int ch = 0; ch < C; ch++) Ccol[ch] += w * X->feat[(size_t)id * C + ch];
+    else
+      dep += w * o->depth;
+    if (tr && ntr < tr_cap) {
+      otrace *r = &tr[ntr++];
+      r->idx = (int)(p - s); r->rec = X->pair_id[p]; r->alpha = a; r->T_before = T; r->G = G;
+      r->dx = dx; r->dy = dy; r->clamped = og > X->alpha_max;
+    }
+    T = T * (1.0 - a);
+    P->ncontrib++;
+    P->last = p - s + 1;
+    if (fabs(T - X->T_min) <= 2e-4 * X->T_min) P->flags |= FLAG_T_STOP;
+    if (T < X->T_min) break;                                   /* include, then stop */
+  }
+  P->T = T;
+  if (!lidar) for (int ch = 0; ch < C; ch++) P->col[ch] = Ccol[ch];
+  else { P->col[0] = dep; P->col[1] = 1.0 - T; }
+  P->dep = dep;
+  return ntr;
+}
+
+/* Forward over npix global pixel ids (or all pixels when pix == NULL).
+ * img: [npix][Cmax] with Cmax = max(C, 2); top: [npix][K]. */
+void or_render(const octx *X, long long npix, const long long *pix, double *img, double *T,
+               long long *last, double *N, int32_t *top, int32_t *flags, long long *processed,
+               long long *ncontrib) {
+  int Cm = X->C > 2 ? X->C : 2;
+  long long cnt = pix ? npix : X->total_pix;
+  #pragma omp parallel for schedule(dynamic, 256)
+  for (long long q = 0; q < cnt; q++) {
+    long long g = pix ? pix[q] : q;
+    opix P;
+    composite(X, g, &P, NULL, 0);
+    for (int ch = 0; ch < Cm; ch++) img[q * Cm + ch] = P.col[ch];
+    if (T) T[q] = P.T;
+    if (last) last[q] = P.last;
+    if (N) N[q] = P.N;
+    if (top) for (int k = 0; k < X->K; k++) top[q * X->K + k] = P.top[k];
+    if (flags) flags[q] = P.flags;
+    if (processed) processed[q] = P.processed;
+    if (ncontrib) ncontrib[q] = P.ncontrib;
+  }
+}
+
+/* Brute force: every valid record, globally sorted by (depth bits, id), with
+ * no tiles. Spheres: pixels outside a sphere's box are rejected by the
+ * distance test itself; Gaussians: by the 1/255 alpha test. */
+static int cmp_rec_order(const void *a, const void *b) { return cmp_pair(a, b); }
+
+void or_render_bruteforce(const octx *X, int v, double *img, double *T, double *N, int32_t *top) {
+  const ocam *c = &X->cams[v];
+  int C = X->C, Cm = X->C > 2 ? X->C : 2;
+  opair *ord = (opair *)malloc(sizeof(opair) * (size_t)(X->n + 1));
+  int m = 0;
+  for (int i = 0; i < X->n; i++) {
+    const orec *o = &X->rec[(long long)v * X->n + i];
+    if (!o->valid) continue;
+    opair pr = {f32_bits(o->key_depth), (uint32_t)((long long)v * X->n + i)};
+    ord[m++] = pr;
+  }
+  qsort(ord, (size_t)m, sizeof(opair), cmp_rec_order);
+  int lidar = c->kind == CAM_SPHERICAL;
+  #pragma omp parallel for schedule(dynamic, 16)
+  for (int j = 0; j < c->height; j++) {
+    for (int i = 0; i < c->width; i++) {
+      long long q = (long long)j * c->width + i;
+      double px = i + 0.5, py = j + 0.5;
+      int ntop = 0;
+      if (top) for (int k = 0; k < X->K; k++) top[q * X->K + k] = -1;
+      if (X->kind == PRIM_SPHERE) {
+        double d[3] = {(px - c->cx) / c->fx, (py - c->cy) / c->fy, 1.0};
+        double dd = d[0] * d[0] + d[1] * d[1] + d[2] * d[2];
+        double Nn = X->bg_weight, S[64];
+        for (int ch = 0; ch < C; ch++) S[ch] = X->bg_weight * X->bg[ch];
+        for (int k = 0; k < m; k++) {
+          const orec *o = &X->rec[ord[k].id];
+          if (o->b < X->tau * Nn) break;
+          const double *qq = o->m;
+          double qd = qq[0] * d[0] + qq[1] * d[1] + qq[2] * d[2];
+          double dist2 = (qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2]) - qd * qd / dd;
+          double r2 = o->r_eff * o->r_eff;
+          if (!(dist2 < r2)) continue;
+          double w = o->opac * (1.0 - dist2 / r2) * o->e;
+          Nn += w;
+          uint32_t id = ord[k].id % (uint32_t)X->n;
+          for (int ch = 0; ch < C; ch++) S[ch] += w * X->feat[(size_t)id * C + ch];
+          if (top && ntop < X->K) top[q * X->K + ntop] = (int32_t)id;
+          ntop++;
+        }
+        for (int ch = 0; ch < C; ch++) img[q * Cm + ch] = S[ch] / Nn;
+        if (N) N[q] = Nn;
+        if (T) T[q] = 0.0;
+      } else {
+        double Tt = 1.0, dep = 0.0, Cc[64];
+        for (int ch = 0; ch < C; ch++) Cc[ch] = 0.0;
+        for (int k = 0; k < m; k++) {
+          const orec *o = &X->rec[ord[k].id];
+          double dx = px - o->u, dy = py - o->v;
+          if (lidar) dx = wrap_dx(dx, c->width);
+          double power = 0.5 * (o->ca * dx * dx + 2.0 * o->cb * dx * dy + o->cc * dy * dy);
+          double og = o->opac * exp(-power);
+          double a = og > X->alpha_max ? X->alpha_max : og;
+          if (a < X->alpha_min) continue;
+          uint32_t id = ord[k].id % (uint32_t)X->n;
+          if (!lidar) for (int ch = 0; ch < C; ch++) Cc[ch] += Tt * a * X->feat[(size_t)id * C + ch];
+          else dep += Tt * a * o->depth;
+          Tt = Tt * (1.0 - a);
+          if (Tt < X->T_min) break;
+        }
+        if (!lidar) for (int ch = 0; ch < C; ch++) img[q * Cm + ch] = Cc[ch];
+        else { img[q * Cm] = dep; img[q * Cm + 1] = 1.0 - Tt; }
+        if (T) T[q] = Tt;
+        if (N) N[q] = 0.0;
+      }
+    }
+  }
+  free(ord);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward                                                                   */
+/* ------------------------------------------------------------------------- */
+
+/* Per-record 2D accumulator layout, NG = 8 + C doubles:
+ * Gaussians: [du, dv, d_ca, d_cb, d_cc, d_opac, d_depth, 0, d_feat...]
+ * spheres:   [dq0, dq1, dq2, d_reff, d_opac, 0, 0, 0, d_feat...]          */
+#define G_OFF 8
+
+/* Reverse pass of one pixel; loc[list position][NG] accumulates. */
+static void pixel_backward(const octx *X, long long gpix, const double *g, double *loc, int NG,
+                           otrace *tr, int tr_cap) {
+  int C = X->C;
+  opix P;
+  int v = find_view(X, gpix);
+  const ocam *c = &X->cams[v];
+  int ntr = composite(X, gpix, &P, tr, tr_cap);
+  if (X->kind == PRIM_SPHERE) {
+    double N = P.N;
+    for (int k = 0; k < ntr; k++) {
+      const otrace *r = &tr[k];
+      const orec *o = &X->rec[r->rec];
+      uint32_t id = r->rec % (uint32_t)X->n;
+      double *A = loc + (size_t)r->idx * NG;
+      double dw = 0.0;
+      for (int ch = 0; ch < C; ch++) {
+        A[G_OFF + ch] += g[ch] * r->w / N;
+        dw += g[ch] * (X->feat[(size_t)id * C + ch] - P.col[ch]) / N;
+      }
+      /* w = o * D * exp(o * zhat / gamma) */
+      double e = o->e, oo = o->opac;
+      A[4] += dw * (r->D * e + r->w * o->zhat / X->gamma);
+      if (o->gated) continue;                       /* tiny spheres: features and opacity only */
+      double dD = dw * oo * e;
+      double dzhat = dw * r->w * oo / X->gamma;
+      double r2 = o->r_eff * o->r_eff;
+      double ddist2 = -dD / r2;
+      const double *q = o->m;
+      double qd = q[0] * r->d[0] + q[1] * r->d[1] + q[2] * r->d[2];
+      for (int a = 0; a < 3; a++) A[a] += ddist2 * (2.0 * q[a] - 2.0 * qd * r->d[a] / r->dd);
+      A[2] += dzhat * (-1.0 / (c->zfar - c->znear));
+      if (!o->floored) A[3] += dD * 2.0 * r->dist2 / (r2 * o->r_eff);
+    }
+    return;
+  }
+  int lidar = c->kind == CAM_SPHERICAL;
+  int nC = lidar ? 0 : C;
+  double Sb[64], Sd = 0.0;
+  for (int ch = 0; ch < nC; ch++) Sb[ch] = 0.0;
+  double gD = lidar ? g[0] : 0.0, gA = lidar ? g[1] : 0.0;
+  double Tfin = P.T;
+  for (int k = ntr - 1; k >= 0; k--) {
+    const otrace *r = &tr[k];
+    const orec *o = &X->rec[r->rec];
+    uint32_t id = r->rec % (uint32_t)X->n;
+    double *A = loc + (size_t)r->idx * NG;
+    double a = r->alpha, Tk = r->T_before;
+    double da = 0.0;
+    for (int ch = 0; ch < nC; ch++) {
+      double f = X->feat[(size_t)id * C + ch];
+      A[G_OFF + ch] += Tk * a * g[ch];
+      da += Tk * (f - Sb[ch]) * g[ch];
+      Sb[ch] = a * f + (1.0 - a) * Sb[ch];
+    }
+    if (lidar) {
+      A[6] += Tk * a * gD;
+      da += Tk * (o->depth - Sd) * gD + Tfin / (1.0 - a) * gA;
+      Sd = a * o->depth + (1.0 - a) * Sd;
+    }
+    if (r->clamped) continue;                      /* alpha = 0.99 constant there */
+    A[5] += r->G * da;
+    double dpower = -a * da;
+    double dx = r->dx, dy = r->dy;
+    A[0] -= dpower * (o->ca * dx + o->cb * dy);
+    A[1] -= dpower * (o->cb * dx + o->cc * dy);
+    A[2] += dpower * 0.5 * dx * dx;
+    A[3] += dpower * dx * dy;
+    A[4] += dpower * 0.5 * dy * dy;
+  }
+}
+
+/* Derivative of the image-map Jacobian entries J[k] with respect to m[a]: dJ[k][a]. */
+static void image_map_dJ(const ocam *c, const double m[3], double dJ[6][3]) {
+  memset(dJ, 0, sizeof(double) * 18);
+  if (c->kind == CAM_PINHOLE) {
+    double z2 = m[2] * m[2], z3 = z2 * m[2];
+    dJ[0][2] = -c->fx / z2;
+    dJ[2][0] = -c->fx / z2;
+    dJ[2][2] = 2.0 * c->fx * m[0] / z3;
+    dJ[4][2] = -c->fy / z2;
+    dJ[5][1] = -c->fy / z2;
+    dJ[5][2] = 2.0 * c->fy * m[1] / z3;
+  } else {
+    double th_max = c->el_max * (M_PI / 180.0), th_min = c->el_min * (M_PI / 180.0);
+    double a = (double)c->width / (2.0 * M_PI), b = (double)c->height / (th_max - th_min);
+    double x = m[0], y = m[1], z = m[2];
+    double rho2 = x * x + y * y, rho = sqrt(rho2), r2 = rho2 + z * z;
+    double rho4 = rho2 * rho2, r4 = r2 * r2;
+    dJ[0][0] = -2.0 * a * x * y / rho4;
+    dJ[0][1] = a * (x * x - y * y) / rho4;
+    dJ[1][0] = a * (x * x - y * y) / rho4;
+    dJ[1][1] = 2.0 * a * x * y / rho4;
+    double h = 1.0 / (r2 * rho);
+    double hx = -x * (2.0 * rho2 + r2) / (r4 * rho2 * rho);
+    double hy = -y * (2.0 * rho2 + r2) / (r4 * rho2 * rho);
+    double hz = -2.0 * z / (r4 * rho);
+    dJ[3][0] = b * z * (h + x * hx);
+    dJ[3][1] = b * x * z * hy;
+    dJ[3][2] = b * x * (h + z * hz);
+    dJ[4][0] = b * y * z * hx;
+    dJ[4][1] = b * z * (h + y * hy);
+    dJ[4][2] = b * y * (h + z * hz);
+    dJ[5][0] = -b * x * (r2 - 2.0 * rho2) / (rho * r4);
+    dJ[5][1] = -b * y * (r2 - 2.0 * rho2) / (rho * r4);
+    dJ[5][2] = 2.0 * b * rho * z / r4;
+  }
+}
+
+/* Chain rule from the 2D accumulator of one record to the primitive parameters.
+ * out_* are per-primitive (summed over views by the caller, serially). */
+static void project_backward(const octx *X, long long k, const double *A, double *dpos, double *dscale,
+                             double *drot, double *dop) {
+  const orec *o = &X->rec[k];
+  int i = (int)(k % X->n), v = (int)(k / X->n);
+  const ocam *c = &X->cams[v];
+  *dop += A[X->kind == PRIM_SPHERE ? 4 : 5];
+  if (X->kind == PRIM_SPHERE) {
+    const double *dq = A;
+    for (int a = 0; a < 3; a++)
+      for (int b = 0; b < 3; b++) dpos[a] += c->R[3 * b + a] * dq[b];   /* R^T dq */
+    dscale[0] += A[3];
+    return;
+  }
+  if (X->kind == PRIM_GAUSS2D) {
+    double s = (double)X->scale[i];
+    dpos[0] += A[0];
+    dpos[1] += A[1];
+    /* ca = cc = 1/s^2 */
+    dscale[0] += (A[2] + A[4]) * (-2.0 / (s * s * s));
+    return;
+  }
+  /* GAUSS3D: conic -> cov2D -> (T, Sigma3D) -> (m, Rq, s) -> (mu, quaternion) */
+  double Q[4] = {o->ca, o->cb, o->cb, o->cc};
+  double Gq[4] = {A[2], 0.5 * A[3], 0.5 * A[3], A[4]};
+  double QG[4], dS2[4];
+  QG[0] = Q[0] * Gq[0] + Q[1] * Gq[2]; QG[1] = Q[0] * Gq[1] + Q[1] * Gq[3];
+  QG[2] = Q[2] * Gq[0] + Q[3] * Gq[2]; QG[3] = Q[2] * Gq[1] + Q[3] * Gq[3];
+  dS2[0] = -(QG[0] * Q[0] + QG[1] * Q[2]); dS2[1] = -(QG[0] * Q[1] + QG[1] * Q[3]);
+  dS2[2] = -(QG[2] * Q[0] + QG[3] * Q[2]); dS2[3] = -(QG[2] * Q[1] + QG[3] * Q[3]);
+  /* recompute the forward quantities */
+  double s[3] = {X->scale[3 * i], X->scale[3 * i + 1], X->scale[3 * i + 2]};
+  double qq[4] = {X->rot[4 * i], X->rot[4 * i + 1], X->rot[4 * i + 2], X->rot[4 * i + 3]};
+  double nq = sqrt(qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3]);
+  double qn[4] = {qq[0] / nq, qq[1] / nq, qq[2] / nq, qq[3] / nq};
+  double Rq[9], M[9], S3[9], J[6], T[6], u, vv;
+  quat_rot(qn, Rq);
+  for (int a = 0; a < 3; a++) for (int b = 0; b < 3; b++) M[3 * a + b] = Rq[3 * a + b] * s[b];
+  for (int a = 0; a < 3; a++) for (int b = 0; b < 3; b++)
+    S3[3 * a + b] = M[3 * a] * M[3 * b] + M[3 * a + 1] * M[3 * b + 1] + M[3 * a + 2] * M[3 * b + 2];
+  const double *m = o->m;
+  image_map(c, m, J, &u, &vv);
+  for (int a = 0; a < 2; a++) for (int b = 0; b < 3; b++)
+    T[3 * a + b] = J[3 * a] * c->R[b] + J[3 * a + 1] * c->R[3 + b] + J[3 * a + 2] * c->R[6 + b];
+  /* Sigma2 = T S3 T^T: dS3 = T^T dS2 T ; dT = 2 dS2 T S3 */
+  double dS3[9], dT[6], TS3[6];
+  for (int a = 0; a < 3; a++) for (int b = 0; b < 3; b++) {
+    double acc = 0.0;
+    for (int p = 0; p < 2; p++) for (int q = 0; q < 2; q++) acc += T[3 * p + a] * dS2[2 * p + q] * T[3 * q + b];
+    dS3[3 * a + b] = acc;
+  }
+  for (int a = 0; a < 2; a++) for (int b = 0; b < 3; b++) {
+    double acc = 0.0;
+    for (int q = 0; q < 3; q++) acc += T[3 * a + q] * S3[3 * q + b];
+    TS3[3 * a + b] = acc;
+  }
+  for (int a = 0; a < 2; a++) for (int b = 0; b < 3; b++)
+    dT[3 * a + b] = 2.0 * (dS2[2 * a] * TS3[b] + dS2[2 * a + 1] * TS3[3 + b]);
+  /* T = J W: dJ = dT W^T */
+  double dJ[6];
+  for (int a = 0; a < 2; a++) for (int b = 0; b < 3; b++)
+    dJ[3 * a + b] = dT[3 * a] * c->R[3 * b] + dT[3 * a + 1] * c->R[3 * b + 1] + dT[3 * a + 2] * c->R[3 * b + 2];
+  double Jm[6][3];
+  image_map_dJ(c, m, Jm);
+  double dm[3] = {0, 0, 0};
+  for (int a = 0; a < 3; a++) {
+    for (int k2 = 0; k2 < 6; k2++) dm[a] += dJ[k2] * Jm[k2][a];
+    dm[a] += A[0] * J[a] + A[1] * J[3 + a];           /* mean 2D */
+  }
+  if (c->kind == CAM_SPHERICAL) {
+    double rr = o->depth;
+    for (int a = 0; a < 3; a++) dm[a] += A[6] * m[a] / rr;   /* range */
+  }
+  for (int a = 0; a < 3; a++)
+    dpos[a] += c->R[a] * dm[0] + c->R[3 + a] * dm[1] + c->R[6 + a] * dm[2];
+  /* Sigma3 = M M^T: dM = 2 dS3 M (dS3 symmetric) */
+  double dM[9];
+  for (int a = 0; a < 3; a++) for (int b = 0; b < 3; b++)
+    dM[3 * a + b] = 2.0 * (dS3[3 * a] * M[b] + dS3[3 * a + 1] * M[3 + b] + dS3[3 * a + 2] * M[6 + b]);
+  double dRq[9];
+  for (int a = 0; a < 3; a++) for (int b = 0; b < 3; b++) {
+    dscale[b] += dM[3 * a + b] * Rq[3 * a + b];
+    dRq[3 * a + b] = dM[3 * a + b] * s[b];
+  }
+  double w = qn[0], x = qn[1], y = qn[2], z = qn[3];
+  double dqn[4];
+  dqn[0] = 2.0 * (-z * dRq[1] + y * dRq[2] + z * dRq[3] - x * dRq[5] - y * dRq[6] + x * dRq[7]);
+  dqn[1] = 2.0 * (y * dRq[1] + z * dRq[2] + y * dRq[3] - 2.0 * x * dRq[4] - w * dRq[5] + z * dRq[6]
+                  + w * dRq[7] - 2.0 * x * dRq[8]);
+  dqn[2] = 2.0 * (-2.0 * y * dRq[0] + x * dRq[1] + w * dRq[2] + x * dRq[3] + z * dRq[5] - w * dRq[6]
+                  + z * dRq[7] - 2.0 * y * dRq[8]);
+  dqn[3] = 2.0 * (-2.0 * z * dRq[0] - w * dRq[1] + x * dRq[2] + w * dRq[3] - 2.0 * z * dRq[4]
+                  + y * dRq[5] + x * dRq[6] + y * dRq[7]);
+  double dot = qn[0] * dqn[0] + qn[1] * dqn[1] + qn[2] * dqn[2] + qn[3] * dqn[3];
+  for (int a = 0; a < 4; a++) drot[a] += (dqn[a] - qn[a] * dot) / nq;
+}
+
+/* Backward. dimg: concatenated per-view [Cv][H][W] float32 upstream gradients
+ * (Cv = C for pinhole views, 2 = (depth, opacity) for spherical views).
+ * Outputs are written (not accumulated). acc_out (optional) receives the
+ * per-record 2D accumulators [V*n][8+C]. */
+void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
+                 double *dop, double *dfeat, double *dR, double *dt, double *acc_out) {
+  int C = X->C, NG = G_OFF + C;
+  long long NV = (long long)X->V * X->n;
+  double *acc = (double *)calloc((size_t)NV * NG + 1, sizeof(double));
+  long long ntile = X->total_tiles;
+  /* Tiles run in parallel; each accumulates by tile-list position into a private
+     buffer, merged into the per-record sums in tile order (deterministic). */
+  #pragma omp parallel
+  {
+    double *loc = NULL;
+    otrace *tr = NULL;
+    long long cap = 0;
+    #pragma omp for schedule(dynamic, 4) ordered
+    for (long long t = 0; t < ntile; t++) {
+      int v = 0;
+      while (v + 1 < X->V && X->cams[v + 1].tile_off <= t) v++;
+      const ocam *c = &X->cams[v];
+      long long s = X->tile_start[t], e = X->tile_start[t + 1], len = e - s;
+      if (len > cap) {
+        free(loc); free(tr);
+        cap = len;
+        loc = (double *)malloc(sizeof(double) * (size_t)(cap * NG));
+        tr = (otrace *)malloc(sizeof(otrace) * (size_t)cap);
+      }
+      int lt = (int)(t - c->tile_off);
+      int tx = lt % c->tiles_x, ty = lt / c->tiles_x;
+      int Cv = c->kind == CAM_SPHERICAL ? 2 : C;
+      const float *gv = dimg;
+      for (int u = 0; u < v; u++)
+        gv += (size_t)(X->cams[u].kind == CAM_SPHERICAL ? 2 : C) * X->cams[u].width * X->cams[u].height;
+      int any = 0;
+      for (long long p = 0; p < len * NG; p++) loc[p] = 0.0;
+      for (int jj = 0; jj < TILE && len > 0; jj++)
+        for (int ii = 0; ii < TILE; ii++) {
+          int i = tx * TILE + ii, j = ty * TILE + jj;
+          if (i >= c->width || j >= c->height) continue;
+          double g[66];
+          int nz = 0;
+          for (int ch = 0; ch < Cv; ch++) {
+            g[ch] = (double)gv[(size_t)ch * c->width * c->height + (size_t)j * c->width + i];
+            nz |= g[ch] != 0.0;
+          }
+          if (!nz) continue;
+          any = 1;
+          pixel_backward(X, c->pix_off + (long long)j * c->width + i, g, loc, NG, tr, (int)len);
+        }
+      #pragma omp ordered
+      {
+        if (any)
+          for (long long p = s; p < e; p++) {
+            double *B = acc + (size_t)X->pair_id[p] * NG;
+            const double *L = loc + (p - s) * NG;
+            for (int q = 0; q < NG; q++) B[q] += L[q];
+          }
+      }
+    }
+    free(loc); free(tr);
+  }
+  /* per-primitive chain rule, views summed in order */
+  int n = X->n;
+  int pd = X->kind == PRIM_GAUSS2D ? 2 : 3, sd = X->kind == PRIM_GAUSS3D ? 3 : 1;
+  memset(dpos, 0, sizeof(double) * (size_t)n * pd);
+  memset(dscale, 0, sizeof(double) * (size_t)n * sd);
+  if (drot) memset(drot, 0, sizeof(double) * (size_t)n * 4);
+  memset(dop, 0, sizeof(double) * (size_t)n);
+  if (dfeat) memset(dfeat, 0, sizeof(double) * (size_t)n * C);
+  memset(dR, 0, sizeof(double) * 9 * (size_t)X->V);
+  memset(dt, 0, sizeof(double) * 3 * (size_t)X->V);
+  #pragma omp parallel for schedule(static)
+  for (int i = 0; i < n; i++) {
+    double lpos[3] = {0, 0, 0}, ls[3] = {0, 0, 0}, lr[4] = {0, 0, 0, 0}, lo = 0.0;
+    for (int v = 0; v < X->V; v++) {
+      long long k = (long long)v * n + i;
+      if (!X->rec[k].valid) continue;
+      const double *A = acc + (size_t)k * NG;
+      project_backward(X, k, A, lpos, ls, lr, &lo);
+      if (dfeat) for (int ch = 0; ch < C; ch++) dfeat[(size_t)i * C + ch] += A[G_OFF + ch];
+    }
+    for (int a = 0; a < pd; a++) dpos[(size_t)i * pd + a] = lpos[a];
+    for (int a = 0; a < sd; a++) dscale[(size_t)i * sd + a] = ls[a];
+    if (drot) for (int a = 0; a < 4; a++) drot[(size_t)i * 4 + a] = lr[a];
+    dop[i] = lo;
+  }
+  if (X->kind == PRIM_SPHERE) {
+    /* camera: sphere-wise contributions summed over all spheres (Pulsar B.2) */
+    for (int v = 0; v < X->V; v++)
+      for (int i = 0; i < n; i++) {
+        long long k = (long long)v * n + i;
+        if (!X->rec[k].valid) continue;
+        const double *A = acc + (size_t)k * NG;
+        double p[3] = {X->pos[3 * i], X->pos[3 * i + 1], X->pos[3 * i + 2]};
+        for (int a = 0; a < 3; a++) {
+          for (int b = 0; b < 3; b++) dR[9 * v + 3 * a + b] += A[a] * p[b];
+          dt[3 * v + a] += A[a];
+        }
+      }
+  }
+  if (acc_out) memcpy(acc_out, acc, sizeof(double) * (size_t)NV * NG);
+  free(acc);
+}

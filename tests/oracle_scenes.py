@@ -1,0 +1,68 @@
+"""Tiny hand-built scenes used to pin the oracle (CPU only)."""
+import math
+
+import numpy as np
+
+from sphere_rasterization_amd import scenes as S
+
+
+def pinhole(W, H, f, R=None, t=None, cx=None, cy=None, znear=0.2, zfar=100.0):
+    return S.Camera(S.CAM_PINHOLE, W, H, np.eye(3) if R is None else R,
+                    np.zeros(3) if t is None else t, fx=f, fy=f,
+                    cx=W / 2 if cx is None else cx, cy=H / 2 if cy is None else cy,
+                    znear=znear, zfar=zfar)
+
+
+def lidar(W=128, H=32, R=None, t=None, el_min=-25.0, el_max=15.0, znear=0.2):
+    return S.Camera(S.CAM_SPHERICAL, W, H, np.eye(3) if R is None else R,
+                    np.zeros(3) if t is None else t, el_min_deg=el_min, el_max_deg=el_max,
+                    znear=znear, zfar=1000.0)
+
+
+def scene2d(centres, sigmas, opac, depth, cols, W=32, H=32, params=None):
+    c = np.asarray(cols, np.float32)
+    n = len(sigmas)
+    return S.Scene(S.PRIM_GAUSS2D, n, c.shape[1], np.asarray(centres, np.float32).reshape(n, 2),
+                   np.asarray(sigmas, np.float32), np.asarray(opac, np.float32), c,
+                   depth=np.asarray(depth, np.float32), cams=[pinhole(W, H, 1.0, cx=0, cy=0, znear=0.0)],
+                   params=params or S.Params())
+
+
+def scene3d(mu, s, q, o, cols, cams, params=None):
+    c = np.asarray(cols, np.float32)
+    n = len(o)
+    return S.Scene(S.PRIM_GAUSS3D, n, c.shape[1], np.asarray(mu, np.float32).reshape(n, 3),
+                   np.asarray(s, np.float32).reshape(n, 3), np.asarray(o, np.float32), c,
+                   rot=np.asarray(q, np.float32).reshape(n, 4), cams=list(cams),
+                   params=params or S.Params())
+
+
+def spheres(p, r, o, f, cams, params=None):
+    f = np.asarray(f, np.float32)
+    n = len(r)
+    return S.Scene(S.PRIM_SPHERE, n, f.shape[1], np.asarray(p, np.float32).reshape(n, 3),
+                   np.asarray(r, np.float32), np.asarray(o, np.float32), f, cams=list(cams),
+                   params=params or S.Params())
+
+
+def random_spheres(rng, n, W, H, f, zmin=2.0, zmax=20.0, rmin=0.005, rmax=0.05, C=3, cam=None):
+    """Spheres uniform in image position and depth, seen by cam (world = camera frame)."""
+    cam = cam or pinhole(W, H, f, znear=1.0, zfar=21.0)
+    u = rng.uniform(0, W, n)
+    v = rng.uniform(0, H, n)
+    z = rng.uniform(zmin, zmax, n)
+    p = np.stack([z * (u - cam.cx) / cam.fx, z * (v - cam.cy) / cam.fy, z], 1)
+    r = np.exp(rng.uniform(math.log(rmin), math.log(rmax), n))
+    o = rng.uniform(0.1, 1.0, n)
+    feat = rng.uniform(0, 1, (n, C))
+    return spheres(p, r, o, feat, [cam])
+
+
+def rotation(rng):
+    """A random proper rotation (QR of a Gaussian matrix, signs fixed)."""
+    A = rng.standard_normal((3, 3))
+    Q, Rr = np.linalg.qr(A)
+    Q = Q * np.sign(np.diag(Rr))
+    if np.linalg.det(Q) < 0:
+        Q[:, 0] = -Q[:, 0]
+    return Q

@@ -1,0 +1,290 @@
+"""Gradient pins of the CPU oracle: central finite differences in float64 and a
+torch float64 autograd cross-check on a dense formulation (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sphere_rasterization_amd import scenes as S
+from tests import oracle_scenes as TS
+
+
+def _loss(scene, g_views, **over):
+    orc = O.Oracle(scene, **over)
+    r = orc.render_views()
+    return sum(float((np.asarray(g, np.float64) * rv["img"]).sum()) for g, rv in zip(g_views, r))
+
+
+def _fd_check(scene, g_views, names, rtol=2e-5, extra=None):
+    """Compare the oracle's backward with central differences for each named input."""
+    orc = O.Oracle(scene)
+    r = orc.render_views()
+    for rv in r:
+        assert (rv["flags"] == 0).all(), "scene sits on a threshold; pick another seed"
+    an = orc.backward(g_views)
+    base = {"pos": scene.pos, "scale": scene.scale, "rot": scene.rot, "opacity": scene.opacity,
+            "feat": scene.feat}
+    for name in names:
+        x0 = np.asarray(base[name], np.float64)
+        fd = np.zeros(x0.size)
+        flat = x0.reshape(-1)
+        for k in range(flat.size):
+            h = 1e-6 * max(abs(flat[k]), 0.1)
+            xp, xm = flat.copy(), flat.copy()
+            xp[k] += h
+            xm[k] -= h
+            lp = _loss(scene, g_views, **{name: xp.reshape(x0.shape)})
+            lm = _loss(scene, g_views, **{name: xm.reshape(x0.shape)})
+            fd[k] = (lp - lm) / (2 * h)
+        a = np.asarray(an[name], np.float64).reshape(-1)
+        scale = np.abs(fd).max()
+        assert scale > 0
+        np.testing.assert_allclose(a, fd, rtol=rtol, atol=rtol * 1e-2 * scale, err_msg=name)
+    return an
+
+
+def _fd_camera(scene, g_views, an, rtol=2e-5):
+    packed = O.pack_cams(scene.cams)
+    base = packed.copy()
+    for v in range(len(scene.cams)):
+        for j, (lo, name, shape) in enumerate(((3, "cam_R", 9), (12, "cam_t", 3))):
+            fd = np.zeros(shape)
+            for k in range(shape):
+                h = 1e-6
+                pp, pm = base.copy(), base.copy()
+                pp[v, lo + k] += h
+                pm[v, lo + k] -= h
+                fd[k] = (_loss(scene, g_views, packed_cams=pp) - _loss(scene, g_views, packed_cams=pm)) / (2 * h)
+            a = an[name][v].reshape(-1)
+            np.testing.assert_allclose(a, fd, rtol=rtol, atol=rtol * 1e-2 * np.abs(fd).max(), err_msg=name)
+
+
+def _g(rng, scene):
+    return [rng.standard_normal((scene.view_channels(v), c.height, c.width)).astype(np.float32)
+            for v, c in enumerate(scene.cams)]
+
+
+def test_fd_gauss2d():
+    rng = np.random.default_rng(21)
+    n = 5
+    sc = TS.scene2d(rng.uniform(6, 18, (n, 2)), rng.uniform(2, 4, n), rng.uniform(0.3, 0.7, n),
+                    rng.permutation(n) + 1.0, rng.uniform(0, 1, (n, 2)), W=24, H=24)
+    _fd_check(sc, _g(rng, sc), ["pos", "scale", "opacity", "feat"])
+
+
+def test_fd_gauss3d_pinhole():
+    rng = np.random.default_rng(22)
+    n = 5
+    R = TS.rotation(rng)
+    c0 = np.array([0.1, 0.2, -0.3])
+    cam = S.Camera(S.CAM_PINHOLE, 32, 32, R, -R @ c0, fx=30.0, fy=28.0, cx=15.0, cy=17.0,
+                   znear=0.2, zfar=100.0)
+    loc = np.stack([rng.uniform(-0.5, 0.5, n), rng.uniform(-0.5, 0.5, n), rng.uniform(3, 5, n)], 1)
+    mu = (R.T @ loc.T).T + c0
+    sc = TS.scene3d(mu, rng.uniform(0.1, 0.3, (n, 3)), rng.standard_normal((n, 4)) * 1.7,
+                    rng.uniform(0.3, 0.7, n), rng.uniform(0, 1, (n, 2)), [cam])
+    _fd_check(sc, _g(rng, sc), ["pos", "scale", "rot", "opacity", "feat"])
+
+
+def test_fd_gauss3d_lidar():
+    """Spherical sensor, one Gaussian straddling the azimuth seam."""
+    rng = np.random.default_rng(23)
+    n = 4
+    az = np.array([3.1, -2.0, 0.5, 1.7])
+    el = rng.uniform(-0.2, 0.1, n)
+    rr = rng.uniform(3, 5, n)
+    loc = np.stack([rr * np.cos(el) * np.cos(az), rr * np.cos(el) * np.sin(az), rr * np.sin(el)], 1)
+    R = TS.rotation(rng)
+    t = np.array([0.05, -0.1, 0.2])
+    mu = (R.T @ (loc - t).T).T
+    sc = TS.scene3d(mu, rng.uniform(0.15, 0.35, (n, 3)), rng.standard_normal((n, 4)),
+                    rng.uniform(0.3, 0.7, n), np.ones((n, 1)), [TS.lidar(128, 32, R=R, t=t)])
+    _fd_check(sc, _g(rng, sc), ["pos", "scale", "rot", "opacity"])
+
+
+def test_fd_spheres_with_camera():
+    rng = np.random.default_rng(24)
+    n = 4
+    R = TS.rotation(rng) * 0.3 + np.eye(3)      # any matrix: the projection is linear in R
+    t = np.array([0.1, -0.05, 0.2])
+    cam = S.Camera(S.CAM_PINHOLE, 32, 32, R, t, fx=32.0, fy=30.0, cx=16.0, cy=15.0,
+                   znear=1.0, zfar=21.0)
+    loc = np.stack([rng.uniform(-0.4, 0.4, n), rng.uniform(-0.4, 0.4, n), rng.uniform(4, 6, n)], 1)
+    Rf = np.asarray(cam.R, np.float64)
+    p = np.linalg.solve(Rf, (loc - np.asarray(cam.t, np.float64)).T).T
+    sc = TS.spheres(p, rng.uniform(0.5, 0.8, n), rng.uniform(0.3, 0.9, n), rng.uniform(0, 1, (n, 3)),
+                    [cam], params=S.Params(tau=0.0, gamma=0.5))
+    pr = O.Oracle(sc).proj()
+    assert not pr["gated"].any() and not pr["floored"].any()
+    g = _g(rng, sc)
+    an = _fd_check(sc, g, ["pos", "scale", "opacity", "feat"])
+    _fd_camera(sc, g, an)
+    # camera gradient is the sum of per-sphere sensor-space gradients
+    dq = an["acc"][:, :3]
+    np.testing.assert_allclose(an["cam_t"][0], dq.sum(0), rtol=1e-12)
+    np.testing.assert_allclose(an["cam_R"][0], dq.T @ np.asarray(sc.pos, np.float64), rtol=1e-12)
+
+
+# ------------------------------------------------------------ zero-gradient rules
+
+def test_gated_spheres_get_only_feature_and_opacity_grads():
+    """Spheres with <= 3 projected pixels: no position or radius gradient (Pulsar sec. 6, A)."""
+    rng = np.random.default_rng(25)
+    sc = TS.random_spheres(rng, 400, 48, 48, 48.0, rmin=0.01, rmax=0.3)
+    orc = O.Oracle(sc)
+    pr = orc.proj()
+    gated = pr["gated"].astype(bool)
+    assert 20 < gated.sum() < 380
+    gr = orc.backward(_g(rng, sc))
+    assert (gr["pos"][gated] == 0).all() and (gr["scale"][gated] == 0).all()
+    hit = np.abs(gr["feat"]).sum(1) > 0
+    assert (np.abs(gr["opacity"][gated & hit]) > 0).any()
+    assert (np.abs(gr["pos"][~gated & hit]).sum(1) > 0).any()
+
+
+def test_only_first_k_spheres_get_gradients():
+    """A stack of 7 spheres on one ray: gradients reach only the first 5 contributing."""
+    n = 7
+    cam = TS.pinhole(16, 16, 16.0, znear=1.0, zfar=21.0)
+    z = np.arange(n) * 1.5 + 3.0
+    p = np.stack([np.zeros(n), np.zeros(n), z], 1)
+    sc = TS.spheres(p, z * 0.1, np.full(n, 0.5), np.random.default_rng(0).uniform(0, 1, (n, 3)), [cam],
+                    params=S.Params(tau=0.0, gamma=1.0))
+    orc = O.Oracle(sc)
+    r = orc.render_views()[0]
+    assert list(r["top"][8, 8]) == [0, 1, 2, 3, 4]
+    g = np.zeros((3, 16, 16), np.float32)
+    g[:, 8, 8] = 1.0
+    gr = orc.backward([g])
+    assert (np.abs(gr["feat"][:5]).sum(1) > 0).all()
+    assert (gr["feat"][5:] == 0).all() and (gr["opacity"][5:] == 0).all() and (gr["pos"][5:] == 0).all()
+
+
+def test_not_requested_pixels_give_zero():
+    rng = np.random.default_rng(26)
+    sc = S.tiny_2d(n=300)
+    gr = O.Oracle(sc).backward([np.zeros((3, 128, 128), np.float32)])
+    for k in ("pos", "scale", "opacity", "feat"):
+        assert (gr[k] == 0).all()
+
+
+# ------------------------------------------------------------ autograd cross-check
+
+def _torch_quat(q):
+    q = q / q.norm(dim=1, keepdim=True)
+    w, x, y, z = q.unbind(1)
+    return torch.stack([1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y),
+                        2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x),
+                        2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)], 1).view(-1, 3, 3)
+
+
+def test_autograd_xcheck_gauss3d():
+    """Dense masked alpha compositing in torch float64 with autograd equals the oracle's
+    hand-derived reverse pass (thresholds decided under no_grad)."""
+    rng = np.random.default_rng(31)
+    n, W, H = 40, 40, 32
+    R = TS.rotation(rng)
+    cam = S.Camera(S.CAM_PINHOLE, W, H, R, [0.1, -0.2, 4.0], fx=35.0, fy=33.0, cx=19.0, cy=17.5,
+                   znear=0.2, zfar=100.0)
+    Rc = torch.tensor(np.asarray(cam.R, np.float64))
+    tc = torch.tensor(np.asarray(cam.t, np.float64))
+    mu = (R.T @ (np.stack([rng.uniform(-1.5, 1.5, n), rng.uniform(-1.2, 1.2, n), rng.uniform(3, 6, n)], 1)
+                 - np.asarray(cam.t, np.float64)).T).T
+    sc = TS.scene3d(mu, rng.uniform(0.05, 0.3, (n, 3)), rng.standard_normal((n, 4)),
+                    rng.uniform(0.2, 0.95, n), rng.uniform(0, 1, (n, 3)), [cam])
+    g = _g(rng, sc)
+    orc = O.Oracle(sc)
+    assert (orc.render_views()[0]["flags"] & (O.FLAG_ALPHA_MIN | O.FLAG_T_STOP)).sum() == 0
+    an = orc.backward(g)
+    P = {k: torch.tensor(np.asarray(getattr(sc, k), np.float64), requires_grad=True)
+         for k in ("pos", "scale", "rot", "opacity", "feat")}
+    Rq = _torch_quat(P["rot"])
+    S3 = Rq @ torch.diag_embed(P["scale"] ** 2) @ Rq.transpose(1, 2)
+    m = P["pos"] @ Rc.T + tc
+    zero = torch.zeros_like(m[:, 0])
+    J = torch.stack([torch.stack([cam.fx / m[:, 2], zero, -cam.fx * m[:, 0] / m[:, 2] ** 2], 1),
+                     torch.stack([zero, cam.fy / m[:, 2], -cam.fy * m[:, 1] / m[:, 2] ** 2], 1)], 1)
+    Tm = J @ Rc
+    S2 = Tm @ S3 @ Tm.transpose(1, 2)
+    conic = torch.linalg.inv(S2)
+    mean = torch.stack([cam.fx * m[:, 0] / m[:, 2] + cam.cx, cam.fy * m[:, 1] / m[:, 2] + cam.cy], 1)
+    order = np.lexsort((np.arange(n), m[:, 2].detach().numpy().astype(np.float32).view(np.uint32)))
+    ys, xs = torch.meshgrid(torch.arange(H, dtype=torch.float64) + 0.5,
+                            torch.arange(W, dtype=torch.float64) + 0.5, indexing="ij")
+    pix = torch.stack([xs, ys], -1).view(-1, 2)
+    Tr = torch.ones(pix.shape[0], dtype=torch.float64)
+    img = torch.zeros(3, pix.shape[0], dtype=torch.float64)
+    a_min = float(np.float32(1 / 255))
+    for k in order:
+        d = pix - mean[k]
+        power = 0.5 * (conic[k, 0, 0] * d[:, 0] ** 2 + 2 * conic[k, 0, 1] * d[:, 0] * d[:, 1]
+                       + conic[k, 1, 1] * d[:, 1] ** 2)
+        al = torch.clamp(P["opacity"][k] * torch.exp(-power), max=float(np.float32(0.99)))
+        with torch.no_grad():
+            use = (al >= a_min) & (Tr >= 1e-4)
+        al = torch.where(use, al, torch.zeros_like(al))
+        img = img + (Tr * al)[None] * P["feat"][k][:, None]
+        Tr = Tr * (1 - al)
+    loss = (img * torch.tensor(g[0].reshape(3, -1), dtype=torch.float64)).sum()
+    loss.backward()
+    for k in ("pos", "scale", "rot", "opacity", "feat"):
+        ref = P[k].grad.numpy()
+        np.testing.assert_allclose(an[k], ref, rtol=1e-9, atol=1e-11 * np.abs(ref).max(), err_msg=k)
+
+
+def test_autograd_xcheck_spheres():
+    """Dense normalized sphere blending in torch float64 (first-5 truncation via detach)
+    with autograd equals the oracle's reverse pass, camera R and t included."""
+    rng = np.random.default_rng(32)
+    n, W, H = 60, 40, 36
+    R = TS.rotation(rng)
+    cam = S.Camera(S.CAM_PINHOLE, W, H, R, [0.1, -0.1, 0.3], fx=40.0, fy=38.0, cx=20.0, cy=18.0,
+                   znear=1.0, zfar=21.0)
+    loc = np.stack([rng.uniform(-1.5, 1.5, n), rng.uniform(-1.5, 1.5, n), rng.uniform(3, 9, n)], 1)
+    p = (R.T @ (loc - np.asarray(cam.t, np.float64)).T).T
+    sc = TS.spheres(p, rng.uniform(0.35, 0.9, n), rng.uniform(0.2, 1.0, n), rng.uniform(0, 1, (n, 3)),
+                    [cam], params=S.Params(tau=0.0, gamma=0.3))
+    orc = O.Oracle(sc)
+    pr = orc.proj()
+    assert not pr["gated"].any() and not pr["floored"].any()
+    r = orc.render_views()[0]
+    assert (r["flags"] == 0).all() and (r["ncontrib"] > 5).any()
+    g = _g(rng, sc)
+    an = orc.backward(g)
+    P = {k: torch.tensor(np.asarray(getattr(sc, k), np.float64), requires_grad=True)
+         for k in ("pos", "scale", "opacity", "feat")}
+    Rc = torch.tensor(np.asarray(cam.R, np.float64), requires_grad=True)
+    tc = torch.tensor(np.asarray(cam.t, np.float64), requires_grad=True)
+    q = P["pos"] @ Rc.T + tc
+    gam = float(np.float32(0.3))
+    zhat = (21.0 - q[:, 2]) / 20.0
+    e = torch.exp(P["opacity"] * zhat / gam)
+    ys, xs = torch.meshgrid(torch.arange(H, dtype=torch.float64) + 0.5,
+                            torch.arange(W, dtype=torch.float64) + 0.5, indexing="ij")
+    d = torch.stack([(xs - cam.cx) / cam.fx, (ys - cam.cy) / cam.fy, torch.ones_like(xs)], -1).view(-1, 3)
+    dd = (d * d).sum(1)
+    qd = d @ q.T                                             # [pix, n]
+    dist2 = (q * q).sum(1)[None] - qd ** 2 / dd[:, None]
+    D = 1 - dist2 / P["scale"][None] ** 2
+    key = (q[:, 2] - P["scale"]).detach().numpy().astype(np.float32).view(np.uint32)
+    order = np.lexsort((np.arange(n), key))
+    with torch.no_grad():
+        hit = D > 0
+        rank = torch.cumsum(hit[:, order].to(torch.int64), 1)
+        first5 = torch.zeros_like(hit)
+        first5[:, order] = hit[:, order] & (rank <= 5)
+    w = torch.where(hit, P["opacity"][None] * D * e[None], torch.zeros_like(D))
+    w_live = torch.where(first5, w, torch.zeros_like(w))          # gradients flow
+    w_dead = torch.where(first5, torch.zeros_like(w), w).detach()  # contributes, no gradient
+    N = 1.0 + (w_live + w_dead).sum(1)
+    img = (w_live @ P["feat"] + w_dead @ P["feat"].detach()) / N[:, None]
+    loss = (img.T * torch.tensor(g[0].reshape(3, -1), dtype=torch.float64)).sum()
+    loss.backward()
+    np.testing.assert_allclose(r["img"].reshape(3, -1), img.detach().numpy().T, atol=1e-12)
+    for k in ("pos", "scale", "opacity", "feat"):
+        ref = P[k].grad.numpy()
+        np.testing.assert_allclose(an[k], ref, rtol=1e-9, atol=1e-11 * np.abs(ref).max(), err_msg=k)
+    np.testing.assert_allclose(an["cam_R"][0], Rc.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(an["cam_t"][0], tc.grad.numpy(), rtol=1e-9, atol=1e-12)
