@@ -1,0 +1,180 @@
+/*
+ * splat.h - C ABI of libsplat, a tile rasterizer for point primitives on
+ * AMD CDNA4 (gfx950).
+ *
+ * The method: project every primitive to the image, bin it to 16x16 pixel
+ * tiles, sort each tile's list by depth, composite front to back per pixel,
+ * and (optionally) send gradients back to the primitives and the camera.
+ * Sources: Pulsar, "Efficient Sphere-based Neural Rendering" (arXiv
+ * 2004.07484), sec. 3.2 and appendix B (enclosing rectangle, depth sort,
+ * 16x16 blocks, draw with closest-five tracking, backward buffer, pixel-wise
+ * backward, sphere-wise camera gradient); the NuRec profiling page
+ * ("Optimizing NVIDIA Omniverse NuRec with Nsight...", sections on the
+ * rendering kernel and renderBackward) for Gaussian splats, multi-sensor
+ * (camera + lidar) rendering and the split camera/lidar backward.
+ *
+ * Conventions for every call:
+ *  - All array pointers are caller-owned DEVICE memory unless marked HOST.
+ *    The library allocates nothing and keeps no mutable global state; calls
+ *    on different streams may overlap freely.
+ *  - Floating point arrays are fp32, row-major, C-contiguous.
+ *  - Work is enqueued on `stream` (0 = the null stream); no call blocks on
+ *    the device. Argument errors are detected on the host and returned before
+ *    anything is enqueued. A failed launch returns SPLAT_ERR_HIP.
+ *  - Pixel (i, j) is column i, row j, centred at (i + 0.5, j + 0.5).
+ *  - Tiles are 16x16; view v has TW = ceil(W/16) x TH = ceil(H/16) tiles
+ *    numbered ty*TW + tx; global tile ids stack the views in order.
+ *  - Images are per view [Cv][H][W] (Cv = channels for pinhole views, 2 =
+ *    (expected depth, opacity) for spherical views), views concatenated.
+ *    Per-pixel buffers are per view [H][W], views concatenated.
+ */
+#ifndef SPLAT_H
+#define SPLAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPLAT_OK = 0,
+  SPLAT_ERR_INVALID_ARG = -1,   /* bad pointer, size, kind or parameter (host check) */
+  SPLAT_ERR_CAPACITY = -2,      /* workspace or buffer smaller than the size query */
+  SPLAT_ERR_HIP = -3,           /* a HIP launch or query failed */
+  SPLAT_ERR_UNSUPPORTED = -4    /* combination not implemented */
+} splat_status;
+
+typedef enum {
+  SPLAT_PRIM_GAUSS2D = 0,       /* screen-space isotropic Gaussian splats */
+  SPLAT_PRIM_GAUSS3D = 1,       /* anisotropic 3D Gaussian splats (EWA projection) */
+  SPLAT_PRIM_SPHERE = 2         /* Pulsar-style spheres */
+} splat_prim_kind;
+
+typedef enum {
+  SPLAT_CAM_PINHOLE = 0,
+  SPLAT_CAM_SPHERICAL = 1       /* lidar-like range view: columns = azimuth, rows = elevation */
+} splat_cam_kind;
+
+#define SPLAT_MAX_VIEWS 16
+#define SPLAT_MAX_CHANNELS 64
+
+/* HOST struct, one per view. Sensor point q = R x + t (R row-major).
+ * Pinhole (x right, y down, z forward): u = fx qx/qz + cx, v = fy qy/qz + cy.
+ * Spherical (x forward, y left, z up; width must be a multiple of 16):
+ *   u = (pi - atan2(qy, qx)) W / (2 pi), v = (el_max - atan2(qz, |q_xy|)) H / (el_max - el_min).
+ * znear culls (depth <= znear); for spheres znear/zfar also normalise depth. */
+typedef struct {
+  int32_t kind, width, height;
+  float R[9], t[3];
+  float fx, fy, cx, cy;
+  float el_min_deg, el_max_deg;
+  float znear, zfar;
+} splat_camera;
+
+/* HOST struct of DEVICE pointers, one array per attribute (structure of arrays).
+ *   GAUSS2D: pos [n][2] pixel centres, scale [n] sigma (px), depth [n] (> 0)
+ *   GAUSS3D: pos [n][3] means, scale [n][3] axis scales, rot [n][4] quaternion (w,x,y,z),
+ *            normalised inside the library
+ *   SPHERE:  pos [n][3] centres, scale [n] radius
+ *   all:     opacity [n] in (0, 1], feat [n][channels] (may be NULL if only spherical views) */
+typedef struct {
+  int32_t kind, n, channels;
+  const float *pos, *scale, *rot, *opacity, *depth, *feat;
+} splat_prims;
+
+/* HOST struct. Gaussian alpha blending: alpha = min(alpha_max, o exp(-power)); entries
+ * with alpha < alpha_min are skipped; a pixel stops after the entry that brings its
+ * transmittance below T_min. Sphere blending: w = o D exp(o zhat / gamma) with
+ * D = 1 - dist^2/r^2 (orthogonal ray distance), zhat = (zfar - qz)/(zfar - znear);
+ * colour = (sum w f + bg_weight bg) / (sum w + bg_weight); a pixel stops at the first
+ * sphere whose bound exp(zhat(front depth)/gamma) < tau * (sum w + bg_weight); the first
+ * top_k contributing spheres per pixel are recorded and receive gradients. */
+typedef struct {
+  float alpha_min, alpha_max, T_min;
+  float gamma, bg_weight, tau;
+  int32_t top_k;                 /* 1..8 */
+  const float *background;       /* HOST [channels] or NULL (= 0) */
+} splat_params;
+
+/* Gradient outputs (DEVICE); NULL = not requested (skipped, nothing written).
+ * Shapes follow the inputs; cam_R [n_views][9], cam_t [n_views][3] (spheres only).
+ * accumulate = 0: outputs are overwritten (zeroed on-stream first);
+ * accumulate = 1: the call's gradients are added to what the buffers hold. */
+typedef struct {
+  float *pos, *scale, *rot, *opacity, *feat;
+  float *cam_R, *cam_t;
+  int32_t accumulate;
+} splat_grads;
+
+/* ---- size queries (host only, no device work) ---------------------------- */
+
+/* Bytes of the opaque projected-record buffer for n_views x n primitives. */
+size_t splat_projected_bytes(int n_views, int n);
+/* Total 16x16 tiles over the views; -1 on invalid cameras. */
+int64_t splat_total_tiles(const splat_camera *cams, int n_views);
+/* Workspace bytes for splat_bin_sort with the given pair capacity. */
+size_t splat_sort_workspace_bytes(const splat_camera *cams, int n_views, int n, int64_t capacity);
+/* Workspace bytes for splat_render_bwd. */
+size_t splat_bwd_workspace_bytes(int n_views, int n, int channels);
+
+/* ---- the four calls ------------------------------------------------------ */
+
+/* Project every (view, primitive): the per-primitive "Step 0" of Pulsar appendix B.1.1
+ * (enclosing rectangle, depth, blending constants) and EWA splatting for Gaussians.
+ * proj: [splat_projected_bytes] opaque records. pair_counts: [n_views*n] uint32, the
+ * number of tiles each record overlaps (0 = culled: behind znear, degenerate, off image). */
+int splat_project(const splat_camera *cams, int n_views, const splat_prims *prims,
+                  const splat_params *prm, void *proj, uint32_t *pair_counts, hipStream_t stream);
+
+/* Bin to tiles and depth-sort each tile's list (Pulsar B.1.1 depth sort, B.1.2 16x16 blocks):
+ * exclusive scan of pair_counts, emit one (key, value) per overlapped tile with
+ * key = (global tile << 32) | fp32 bits of the depth, value = record index (view*n + i),
+ * stable LSD radix sort on the key, then per-tile [start, end) ranges.
+ * keys/vals: [capacity]; tile_ranges: [total_tiles][2] uint32 (empty tiles: 0, 0).
+ * num_pairs (device int64) receives the needed pair count. If it exceeds capacity,
+ * *overflow (device int32) is set to 1 and nothing else is written; the render calls
+ * then return without writing. Otherwise *overflow is set to 0.
+ * workspace: [splat_sort_workspace_bytes] device bytes. */
+int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *proj,
+                   const uint32_t *pair_counts, int64_t capacity, uint64_t *keys, uint32_t *vals,
+                   uint32_t *tile_ranges, int64_t *num_pairs, int32_t *overflow, void *workspace,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* Composite front to back per pixel, one workgroup per tile with the tile's list staged
+ * through LDS in batches (Pulsar B.1.2-B.1.4; NuRec rendering kernel).
+ *   img: image layout above.
+ *   Gaussians: T_final [pixels] final transmittance, last [pixels] number of list entries
+ *     up to and including the last composited one (the backward replays from there).
+ *   Spheres: norm [pixels] the normalisation sum, topk [pixels][top_k] int32 primitive
+ *     ids of the first top_k contributing spheres (-1 padded) - the backward buffer of
+ *     Pulsar B.1.4. T_final/last may be NULL for spheres, norm/topk for Gaussians. */
+int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *prims,
+                     const splat_params *prm, const void *proj, const uint32_t *vals,
+                     const uint32_t *tile_ranges, const int32_t *overflow, float *img,
+                     float *T_final, uint32_t *last, float *norm, int32_t *topk,
+                     hipStream_t stream);
+
+/* Reverse pass for views [view_begin, view_begin + view_count): per-pixel gradients
+ * reduced per primitive within each wavefront before global atomics, then the chain
+ * rule per primitive and, for spheres, the sphere-wise camera gradient with a
+ * device-wide reduction (Pulsar B.2). Pinhole and spherical views run in separate
+ * kernels (the NuRec camera/lidar split). dL_dimg has the img layout (all views).
+ * The forward outputs must come from splat_render_fwd on the same inputs.
+ * workspace: [splat_bwd_workspace_bytes] device bytes. */
+int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int view_count,
+                     const splat_prims *prims, const splat_params *prm, const void *proj,
+                     const uint32_t *vals, const uint32_t *tile_ranges, const int32_t *overflow,
+                     const float *img, const float *T_final, const uint32_t *last,
+                     const float *norm, const int32_t *topk, const float *dL_dimg,
+                     const splat_grads *grads, void *workspace, size_t ws_bytes,
+                     hipStream_t stream);
+
+const char *splat_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPLAT_H */

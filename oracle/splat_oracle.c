@@ -38,8 +38,8 @@ enum {
   FLAG_ALPHA_MIN = 1,   /* an alpha within 1e-5 (relative) of the skip threshold */
   FLAG_T_STOP = 2,      /* transmittance within 2e-4 (relative) of the stop threshold */
   FLAG_CLAMP = 4,       /* opacity*G within 1e-5 (relative) of the 0.99 clamp */
-  FLAG_SPH_EDGE = 8,    /* a sphere's distance factor within 1e-5 of 0 (top-K may flip) */
-  FLAG_SPH_STOP = 16    /* a stop bound within 1e-4 (relative) of tau*N */
+  FLAG_SPH_EDGE = 8,    /* a sphere's distance factor within 1e-8 of 0 (top-K may flip) */
+  FLAG_SPH_STOP = 16    /* a stop bound within 2e-5 (relative) of tau*N */
 };
 
 #define CAM_STRIDE 24
@@ -482,7 +482,7 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       const orec *o = &X->rec[X->pair_id[p]];
       P->processed++;
       double lim = X->tau * N;
-      if (fabs(o->b - lim) <= 1e-4 * lim) P->flags |= FLAG_SPH_STOP;
+      if (fabs(o->b - lim) <= 2e-5 * lim) P->flags |= FLAG_SPH_STOP;
       if (o->b < lim) break;                                   /* early stop (Pulsar 3.2, B.1.3) */
       const double *q = o->m;
       double qd = q[0] * d[0] + q[1] * d[1] + q[2] * d[2];
@@ -490,7 +490,7 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       double dist2 = qq - qd * qd / dd;                        /* orthogonal ray distance^2 */
       double r2 = o->r_eff * o->r_eff;
       double D = 1.0 - dist2 / r2;
-      if (fabs(D) < 1e-5 && P->ntop < X->K) P->flags |= FLAG_SPH_EDGE;
+      if (fabs(D) < 1e-8 && P->ntop < X->K) P->flags |= FLAG_SPH_EDGE;
       if (!(dist2 < r2)) continue;
       double w = o->opac * D * o->e;
       N += w;

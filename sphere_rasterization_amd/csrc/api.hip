@@ -1,0 +1,256 @@
+// extern "C" entry points of libsplat: argument checks on the host, view-table
+// construction, then kernel launches on the caller's stream. No allocation, no
+// host synchronisation, no global mutable state.
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "render_common.h"
+#include "splat_internal.h"
+
+int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, void *proj, uint32_t *counts,
+                   hipStream_t stream);
+size_t sort_workspace_bytes(long long nrec, long long capacity);
+int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t *counts, long long capacity,
+                    uint64_t *keys, uint32_t *vals, uint32_t *ranges, int64_t *num_pairs, int32_t *overflow,
+                    void *workspace, hipStream_t stream);
+int launch_render_fwd(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t stream);
+size_t bwd_workspace_bytes(long long nrec, int C);
+int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, const BinRec *bin,
+                      const splat_grads *gr, hipStream_t stream);
+
+namespace {
+
+bool debug_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = getenv("SPLAT_DEBUG");
+    v = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+int fail(int code, const char *what) {
+  if (debug_enabled()) fprintf(stderr, "libsplat: %s (%d)\n", what, code);
+  return code;
+}
+
+#define CHECK(cond, code, msg) \
+  do {                         \
+    if (!(cond)) return fail(code, msg); \
+  } while (0)
+
+// Validate cameras and build the device view table. Returns SPLAT_OK or an error.
+int build_views(const splat_camera *cams, int n_views, int channels, ViewTable *vt) {
+  CHECK(cams != nullptr, SPLAT_ERR_INVALID_ARG, "cams is NULL");
+  CHECK(n_views >= 1 && n_views <= SPLAT_MAX_VIEWS, SPLAT_ERR_INVALID_ARG, "n_views out of range");
+  memset(vt, 0, sizeof(*vt));
+  vt->n = n_views;
+  long long toff = 0, poff = 0, ioff = 0;
+  for (int v = 0; v < n_views; v++) {
+    const splat_camera &c = cams[v];
+    ViewDev &d = vt->v[v];
+    CHECK(c.kind == SPLAT_CAM_PINHOLE || c.kind == SPLAT_CAM_SPHERICAL, SPLAT_ERR_INVALID_ARG, "camera kind");
+    CHECK(c.width > 0 && c.height > 0 && c.width <= (1 << 20) && c.height <= (1 << 20), SPLAT_ERR_INVALID_ARG,
+          "camera size");
+    for (int k = 0; k < 9; k++) CHECK(isfinite(c.R[k]), SPLAT_ERR_INVALID_ARG, "camera R not finite");
+    for (int k = 0; k < 3; k++) CHECK(isfinite(c.t[k]), SPLAT_ERR_INVALID_ARG, "camera t not finite");
+    CHECK(isfinite(c.znear) && isfinite(c.zfar) && c.znear >= 0.0f, SPLAT_ERR_INVALID_ARG, "camera depth range");
+    if (c.kind == SPLAT_CAM_PINHOLE) {
+      CHECK(isfinite(c.fx) && isfinite(c.fy) && c.fx > 0.0f && c.fy > 0.0f, SPLAT_ERR_INVALID_ARG, "focal length");
+      CHECK(isfinite(c.cx) && isfinite(c.cy), SPLAT_ERR_INVALID_ARG, "principal point");
+    } else {
+      CHECK(c.width % TILE == 0, SPLAT_ERR_INVALID_ARG, "spherical width must be a multiple of 16");
+      CHECK(isfinite(c.el_min_deg) && isfinite(c.el_max_deg) && c.el_max_deg > c.el_min_deg, SPLAT_ERR_INVALID_ARG,
+            "elevation range");
+    }
+    d.kind = c.kind;
+    d.W = c.width;
+    d.H = c.height;
+    d.TW = (c.width + TILE - 1) / TILE;
+    d.TH = (c.height + TILE - 1) / TILE;
+    CHECK(d.TW <= 65535 && d.TH <= 65535, SPLAT_ERR_INVALID_ARG, "too many tiles");
+    d.tile_off = (int)toff;
+    d.chan = c.kind == SPLAT_CAM_SPHERICAL ? 2 : channels;
+    d.pix_off = poff;
+    d.img_off = ioff;
+    memcpy(d.R, c.R, sizeof(d.R));
+    memcpy(d.t, c.t, sizeof(d.t));
+    d.fx = c.fx; d.fy = c.fy; d.cx = c.cx; d.cy = c.cy;
+    d.el_min = c.el_min_deg; d.el_max = c.el_max_deg; d.znear = c.znear; d.zfar = c.zfar;
+    toff += (long long)d.TW * d.TH;
+    poff += (long long)c.width * c.height;
+    ioff += (long long)d.chan * c.width * c.height;
+  }
+  CHECK(toff < (1ll << 31), SPLAT_ERR_INVALID_ARG, "too many tiles");
+  vt->total_tiles = (int)toff;
+  vt->total_pix = poff;
+  return SPLAT_OK;
+}
+
+int check_prims(const splat_prims *p, const ViewTable &vt) {
+  CHECK(p != nullptr, SPLAT_ERR_INVALID_ARG, "prims is NULL");
+  CHECK(p->kind == SPLAT_PRIM_GAUSS2D || p->kind == SPLAT_PRIM_GAUSS3D || p->kind == SPLAT_PRIM_SPHERE,
+        SPLAT_ERR_INVALID_ARG, "primitive kind");
+  CHECK(p->n >= 0, SPLAT_ERR_INVALID_ARG, "negative n");
+  CHECK(p->channels >= 0 && p->channels <= SPLAT_MAX_CHANNELS, SPLAT_ERR_INVALID_ARG, "channels out of range");
+  CHECK((long long)vt.n * p->n < (1ll << 32) - 1, SPLAT_ERR_INVALID_ARG, "too many records");
+  bool any_pin = false, any_sph = false;
+  for (int v = 0; v < vt.n; v++) {
+    if (vt.v[v].kind == SPLAT_CAM_SPHERICAL) any_sph = true;
+    else any_pin = true;
+  }
+  if (p->kind == SPLAT_PRIM_SPHERE) CHECK(!any_sph, SPLAT_ERR_UNSUPPORTED, "spheres need pinhole views");
+  if (p->kind == SPLAT_PRIM_GAUSS2D) CHECK(!any_sph, SPLAT_ERR_UNSUPPORTED, "screen-space Gaussians need pinhole views");
+  if (p->n == 0) return SPLAT_OK;
+  CHECK(p->pos && p->scale && p->opacity, SPLAT_ERR_INVALID_ARG, "missing primitive arrays");
+  if (p->kind == SPLAT_PRIM_GAUSS3D) CHECK(p->rot != nullptr, SPLAT_ERR_INVALID_ARG, "missing rotations");
+  if (p->kind == SPLAT_PRIM_GAUSS2D) CHECK(p->depth != nullptr, SPLAT_ERR_INVALID_ARG, "missing depths");
+  if (any_pin) CHECK(p->channels >= 1 && p->feat != nullptr, SPLAT_ERR_INVALID_ARG, "missing features");
+  return SPLAT_OK;
+}
+
+int check_params(const splat_params *m, int kind) {
+  CHECK(m != nullptr, SPLAT_ERR_INVALID_ARG, "params is NULL");
+  CHECK(isfinite(m->alpha_min) && isfinite(m->alpha_max) && isfinite(m->T_min), SPLAT_ERR_INVALID_ARG,
+        "alpha parameters");
+  CHECK(m->alpha_max > 0.0f && m->alpha_max < 1.0f, SPLAT_ERR_INVALID_ARG, "alpha_max must lie in (0, 1)");
+  CHECK(m->alpha_min >= 0.0f && m->T_min >= 0.0f, SPLAT_ERR_INVALID_ARG, "negative thresholds");
+  if (kind == SPLAT_PRIM_SPHERE) {
+    CHECK(isfinite(m->gamma) && m->gamma > 0.0f, SPLAT_ERR_INVALID_ARG, "gamma must be > 0");
+    CHECK(isfinite(m->tau) && m->tau >= 0.0f, SPLAT_ERR_INVALID_ARG, "tau must be >= 0");
+    CHECK(isfinite(m->bg_weight) && m->bg_weight > 0.0f, SPLAT_ERR_INVALID_ARG, "bg_weight must be > 0");
+    CHECK(m->top_k >= 1 && m->top_k <= SPLAT_TOPK_MAX, SPLAT_ERR_INVALID_ARG, "top_k must be in 1..8");
+  }
+  return SPLAT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t splat_projected_bytes(int n_views, int n) {
+  if (n_views < 1 || n < 0) return 0;
+  return proj_bytes((long long)n_views * n);
+}
+
+int64_t splat_total_tiles(const splat_camera *cams, int n_views) {
+  ViewTable vt;
+  if (build_views(cams, n_views, 1, &vt) != SPLAT_OK) return -1;
+  return vt.total_tiles;
+}
+
+size_t splat_sort_workspace_bytes(const splat_camera *cams, int n_views, int n, int64_t capacity) {
+  ViewTable vt;
+  if (build_views(cams, n_views, 1, &vt) != SPLAT_OK || n < 0 || capacity < 0) return 0;
+  return sort_workspace_bytes((long long)n_views * n, capacity);
+}
+
+size_t splat_bwd_workspace_bytes(int n_views, int n, int channels) {
+  if (n_views < 1 || n < 0 || channels < 0) return 0;
+  return bwd_workspace_bytes((long long)n_views * n, channels);
+}
+
+int splat_project(const splat_camera *cams, int n_views, const splat_prims *prims, const splat_params *prm,
+                  void *proj, uint32_t *pair_counts, hipStream_t stream) {
+  ViewTable vt;
+  int st = build_views(cams, n_views, prims ? prims->channels : 0, &vt);
+  if (st) return st;
+  if ((st = check_prims(prims, vt))) return st;
+  if ((st = check_params(prm, prims->kind))) return st;
+  if (prims->n == 0) return SPLAT_OK;
+  CHECK(proj && pair_counts, SPLAT_ERR_INVALID_ARG, "proj / pair_counts NULL");
+  return launch_project(vt, prims, (double)prm->gamma, proj, pair_counts, stream);
+}
+
+int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *proj, const uint32_t *pair_counts,
+                   int64_t capacity, uint64_t *keys, uint32_t *vals, uint32_t *tile_ranges, int64_t *num_pairs,
+                   int32_t *overflow, void *workspace, size_t ws_bytes, hipStream_t stream) {
+  ViewTable vt;
+  int st = build_views(cams, n_views, 1, &vt);
+  if (st) return st;
+  CHECK(n >= 0 && (long long)n_views * n < (1ll << 32) - 1, SPLAT_ERR_INVALID_ARG, "n out of range");
+  CHECK(capacity >= 0 && capacity < (1ll << 32) - 1, SPLAT_ERR_INVALID_ARG, "capacity out of range");
+  CHECK(tile_ranges && num_pairs && overflow, SPLAT_ERR_INVALID_ARG, "NULL output");
+  CHECK(n == 0 || (proj && pair_counts), SPLAT_ERR_INVALID_ARG, "NULL input");
+  CHECK(capacity == 0 || (keys && vals), SPLAT_ERR_INVALID_ARG, "NULL keys / vals");
+  CHECK(workspace != nullptr, SPLAT_ERR_INVALID_ARG, "NULL workspace");
+  CHECK(ws_bytes >= sort_workspace_bytes((long long)n_views * n, capacity), SPLAT_ERR_CAPACITY,
+        "sort workspace too small");
+  return launch_bin_sort(vt, n, proj, pair_counts, capacity, keys, vals, tile_ranges, num_pairs, overflow, workspace,
+                         stream);
+}
+
+int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *prims, const splat_params *prm,
+                     const void *proj, const uint32_t *vals, const uint32_t *tile_ranges, const int32_t *overflow,
+                     float *img, float *T_final, uint32_t *last, float *norm, int32_t *topk, hipStream_t stream) {
+  ViewTable vt;
+  int st = build_views(cams, n_views, prims ? prims->channels : 0, &vt);
+  if (st) return st;
+  if ((st = check_prims(prims, vt))) return st;
+  if ((st = check_params(prm, prims->kind))) return st;
+  CHECK(img && tile_ranges && overflow, SPLAT_ERR_INVALID_ARG, "NULL output");
+  CHECK(prims->n == 0 || (proj && vals), SPLAT_ERR_INVALID_ARG, "NULL proj / vals");
+  CHECK(prims->n > 0, SPLAT_ERR_INVALID_ARG, "render needs at least one primitive");
+  FwdArgs A;
+  memset(&A, 0, sizeof(A));
+  A.n = prims->n; A.C = prims->channels; A.top_k = prm->top_k;
+  A.alpha_min = prm->alpha_min; A.alpha_max = prm->alpha_max; A.T_min = prm->T_min;
+  A.tau = prm->tau; A.bg_weight = prm->bg_weight;
+  for (int c = 0; c < A.C; c++) A.bg[c] = prm->background ? prm->background[c] : 0.0f;
+  ProjLayout L = proj_layout(const_cast<void *>(proj), (long long)n_views * prims->n);
+  A.draw = L.draw; A.aux = L.aux; A.vals = vals; A.ranges = tile_ranges; A.overflow = overflow;
+  A.feat = prims->feat; A.img = img; A.T_final = T_final; A.last = last; A.norm = norm; A.topk = topk;
+  return launch_render_fwd(vt, A, prims->kind, stream);
+}
+
+int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int view_count, const splat_prims *prims,
+                     const splat_params *prm, const void *proj, const uint32_t *vals, const uint32_t *tile_ranges,
+                     const int32_t *overflow, const float *img, const float *T_final, const uint32_t *last,
+                     const float *norm, const int32_t *topk, const float *dL_dimg, const splat_grads *grads,
+                     void *workspace, size_t ws_bytes, hipStream_t stream) {
+  ViewTable vt;
+  int st = build_views(cams, n_views, prims ? prims->channels : 0, &vt);
+  if (st) return st;
+  if ((st = check_prims(prims, vt))) return st;
+  if ((st = check_params(prm, prims->kind))) return st;
+  CHECK(view_begin >= 0 && view_count >= 1 && view_begin + view_count <= n_views, SPLAT_ERR_INVALID_ARG,
+        "view range");
+  CHECK(grads != nullptr, SPLAT_ERR_INVALID_ARG, "grads is NULL");
+  CHECK(prims->n > 0, SPLAT_ERR_INVALID_ARG, "backward needs at least one primitive");
+  CHECK(proj && vals && tile_ranges && overflow && dL_dimg, SPLAT_ERR_INVALID_ARG, "NULL input");
+  if (prims->kind == SPLAT_PRIM_SPHERE) {
+    CHECK(img && norm && topk, SPLAT_ERR_INVALID_ARG, "sphere backward needs img, norm and topk");
+  } else {
+    CHECK(T_final && last, SPLAT_ERR_INVALID_ARG, "Gaussian backward needs T_final and last");
+  }
+  CHECK(workspace != nullptr, SPLAT_ERR_INVALID_ARG, "NULL workspace");
+  CHECK(ws_bytes >= bwd_workspace_bytes((long long)n_views * prims->n, prims->channels), SPLAT_ERR_CAPACITY,
+        "backward workspace too small");
+  BwdArgs A;
+  memset(&A, 0, sizeof(A));
+  A.n = prims->n; A.C = prims->channels; A.top_k = prm->top_k;
+  A.alpha_min = prm->alpha_min; A.alpha_max = prm->alpha_max; A.gamma = prm->gamma;
+  ProjLayout L = proj_layout(const_cast<void *>(proj), (long long)n_views * prims->n);
+  A.draw = L.draw; A.aux = L.aux; A.vals = vals; A.ranges = tile_ranges; A.overflow = overflow;
+  A.feat = prims->feat; A.img = img; A.T_final = T_final; A.last = last; A.norm = norm; A.topk = topk;
+  A.dimg = dL_dimg;
+  AccLayout acc = acc_layout(workspace, (long long)n_views * prims->n);
+  A.accg = acc.g;
+  A.accf = acc.f;
+  return launch_render_bwd(vt, view_begin, view_begin + view_count, A, prims, L.bin, grads, stream);
+}
+
+const char *splat_status_string(int status) {
+  switch (status) {
+    case SPLAT_OK: return "ok";
+    case SPLAT_ERR_INVALID_ARG: return "invalid argument";
+    case SPLAT_ERR_CAPACITY: return "buffer or workspace too small";
+    case SPLAT_ERR_HIP: return "HIP launch error";
+    case SPLAT_ERR_UNSUPPORTED: return "unsupported combination";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,624 @@
+// Backward pass.
+//
+// Pulsar appendix B.2: pixel-wise backward parallelisation reading the forward
+// pass's per-pixel buffer (no new intersection search), gradients only for the
+// first few spheres of each pixel, then a sphere-wise pass for the camera
+// gradient followed by a device-wide reduction. NuRec's renderBackward is split
+// into camera and lidar versions; here the pinhole and spherical views run as
+// separate kernel instantiations (different register and LDS budgets).
+//
+// Gradient accumulation per primitive: contributions of the lanes of a wave that
+// touch the same primitive are summed in registers with DPP row shifts before
+// any atomic (the DISTWAR observation, arXiv author page: most lanes of a warp
+// update the same addresses). Alpha blending: every lane of a wave walks the same
+// list entry, so each value is row-reduced and four lanes add into an LDS slot
+// per entry; one global atomic per entry and value leaves the tile. Spheres:
+// lanes are grouped by primitive id (ballot + readlane) and each group is
+// reduced across the wave before a single global atomic.
+#include "splat_internal.h"
+
+#include "render_common.h"
+
+namespace {
+
+// Sum within each 16-lane row (inclusive scan); lanes 15, 31, 47, 63 hold the row sums.
+__device__ __forceinline__ float row_sum_to_last(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
+  return x;
+}
+
+__global__ void k_fill_f32(float *p, long long n) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+__global__ void k_fill_f64(double *p, long long n) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0;
+}
+
+// ---------------------------------------------------------------------------
+// Alpha blending backward: replay each pixel's list back to front from `last`,
+// recovering T before entry k as T_after / (1 - alpha_k) (fp64).
+// Per entry and pixel the gradient is a common factor d loss / d power times
+// geometric terms of the offset (dx, dy); those terms and their sums are fp64,
+// colour and opacity terms fp32.
+// ---------------------------------------------------------------------------
+template <int CM, bool LIDAR>
+__global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int tile_begin) {
+  constexpr int NF = LIDAR ? 1 : CM;        // fp32 values per entry: features (or depth)
+  __shared__ double2 s_uv[256];
+  __shared__ double2 s_ab[256];
+  __shared__ double2 s_co[256];
+  __shared__ float s_f[NF][256];
+  __shared__ uint32_t s_rid[256];
+  __shared__ double s_ag[6][256];           // du, dv, d_ca, d_cb, d_cc, d_opac
+  __shared__ float s_af[NF][256];           // d_feat (or d_depth)
+  __shared__ uint32_t s_maxlast;
+  if (*A.overflow) return;
+  const int gtile = tile_begin + blockIdx.x;
+  const int view = view_of_tile(vt, gtile);
+  const ViewDev &c = vt.v[view];
+  if ((c.kind == SPLAT_CAM_SPHERICAL) != LIDAR) return;
+  const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
+  const uint32_t start = A.ranges[2 * gtile];
+  const uint32_t len = A.ranges[2 * gtile + 1] - start;
+  const unsigned lane = lane_id();
+  const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
+  const size_t plane = (size_t)c.W * c.H;
+  const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
+  const double pxr = tp.pxr, pyr = tp.pyr;
+  uint32_t lastp = 0;
+  double T = 1.0;      // transmittance after the current entry
+  float g[LIDAR ? 2 : CM];
+  float Sb[NF];        // colour (or depth) composited behind the current entry
+#pragma unroll
+  for (int ch = 0; ch < NF; ch++) Sb[ch] = 0.0f;
+  if (LIDAR) {
+    g[0] = tp.inside ? A.dimg[pofs] : 0.0f;
+    g[1] = tp.inside ? A.dimg[pofs + plane] : 0.0f;
+  } else {
+#pragma unroll
+    for (int ch = 0; ch < CM; ch++) g[ch] = (tp.inside && ch < A.C) ? A.dimg[pofs + ch * plane] : 0.0f;
+  }
+  if (tp.inside) {
+    lastp = min(A.last[p], len);     // a forward buffer never exceeds the tile's list
+    T = (double)A.T_final[p];
+  }
+  const double Tfin = T;
+  if (threadIdx.x == 0) s_maxlast = 0;
+  __syncthreads();
+  if (lastp) atomicMax(&s_maxlast, lastp);
+  __syncthreads();
+  const uint32_t maxlast = s_maxlast;
+  const long long vbase = (long long)view * A.n;
+  const float amin = A.alpha_min, amax = A.alpha_max;
+
+  for (int hi = (int)maxlast; hi > 0; hi -= 256) {
+    const int lo = hi > 256 ? hi - 256 : 0;
+    const int cnt = hi - lo;
+    if ((int)threadIdx.x < cnt) {
+      const uint32_t rid = A.vals[start + lo + threadIdx.x];
+      const DrawRec d = A.draw[rid];
+      s_rid[threadIdx.x] = rid;
+      s_uv[threadIdx.x] = stage_uv(c, tp, d, LIDAR);
+      const Conic cn = stage_conic(d);
+      s_ab[threadIdx.x] = cn.ab;
+      s_co[threadIdx.x] = cn.co;
+      if (LIDAR) {
+        s_f[0][threadIdx.x] = A.aux[rid].depth;
+      } else {
+        const long long id = (long long)rid - vbase;
+#pragma unroll
+        for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 6; q++) s_ag[q][threadIdx.x] = 0.0;
+#pragma unroll
+      for (int q = 0; q < NF; q++) s_af[q][threadIdx.x] = 0.0f;
+    }
+    __syncthreads();
+    for (int k = cnt - 1; k >= 0; k--) {
+      const uint32_t pos = (uint32_t)(lo + k);
+      const double2 ab = s_ab[k], co = s_co[k];
+      float G, og;
+      double dx, dy;
+      const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[k], ab, co, amax, G, og, dx, dy);
+      const bool act = pos < lastp && al >= amin;
+      if (ballot64(act) == 0) continue;
+      double vg[6];
+      float vf[NF];
+#pragma unroll
+      for (int q = 0; q < 6; q++) vg[q] = 0.0;
+#pragma unroll
+      for (int q = 0; q < NF; q++) vf[q] = 0.0f;
+      if (act) {
+        const float om = 1.0f - al;
+        const double Tkd = T / (1.0 - (double)al);
+        const float Tk = (float)Tkd;
+        float da = 0.0f;
+        if (LIDAR) {
+          const float dep = s_f[0][k];
+          vf[0] = Tk * al * g[0];
+          da = Tk * (dep - Sb[0]) * g[0] + (float)(Tfin / (1.0 - (double)al)) * g[1];
+          Sb[0] = __builtin_fmaf(al, dep, om * Sb[0]);
+        } else {
+#pragma unroll
+          for (int ch = 0; ch < CM; ch++) {
+            const float f = s_f[ch][k];
+            vf[ch] = Tk * al * g[ch];
+            da = __builtin_fmaf(Tk * (f - Sb[ch]), g[ch], da);
+            Sb[ch] = __builtin_fmaf(al, f, om * Sb[ch]);
+          }
+        }
+        T = Tkd;
+        if (!(og > amax)) {              // alpha is the constant amax where clamped
+          vg[5] = (double)(G * da);
+          const double dp = -(double)al * (double)da;     // d loss / d power
+          const double ha = ab.x, b = ab.y, hc = co.x;    // a/2, b, c/2
+          vg[0] = -dp * (2.0 * ha * dx + b * dy);
+          vg[1] = -dp * (b * dx + 2.0 * hc * dy);
+          vg[2] = dp * 0.5 * dx * dx;
+          vg[3] = dp * dx * dy;
+          vg[4] = dp * 0.5 * dy * dy;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 6; q++) {
+        const double r = row_sum_to_last_f64(vg[q]);
+        if ((lane & 15u) == 15u) atomicAdd(&s_ag[q][k], r);
+      }
+#pragma unroll
+      for (int q = 0; q < NF; q++) {
+        const float r = row_sum_to_last(vf[q]);
+        if ((lane & 15u) == 15u) atomicAdd(&s_af[q][k], r);
+      }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < cnt) {
+      const uint32_t rid = s_rid[threadIdx.x];
+      double *dg = A.accg + (size_t)rid * ACC_G;
+#pragma unroll
+      for (int q = 0; q < 6; q++) {
+        const double x = s_ag[q][threadIdx.x];
+        if (x != 0.0) atomicAdd(dg + q, x);
+      }
+      if (LIDAR) {
+        const float x = s_af[0][threadIdx.x];
+        if (x != 0.0f) atomicAdd(dg + 6, (double)x);
+      } else {
+        float *df = A.accf + (size_t)rid * A.C;
+#pragma unroll
+        for (int q = 0; q < CM; q++) {
+          const float x = s_af[q][threadIdx.x];
+          if (q < A.C && x != 0.0f) atomicAdd(df + q, x);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sphere backward over the first top_k contributing spheres of each pixel.
+// ---------------------------------------------------------------------------
+template <int CM>
+__global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int tile_begin) {
+  if (*A.overflow) return;
+  const int gtile = tile_begin + blockIdx.x;
+  const int view = view_of_tile(vt, gtile);
+  const ViewDev &c = vt.v[view];
+  const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
+  const SphereRay ray = sphere_ray(c, tp);
+  const unsigned lane = lane_id();
+  const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
+  const size_t plane = (size_t)c.W * c.H;
+  const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
+  float g[CM], Cimg[CM];
+  float invN = 0.0f;
+#pragma unroll
+  for (int ch = 0; ch < CM; ch++) {
+    const bool ok = tp.inside && ch < A.C;
+    g[ch] = ok ? A.dimg[pofs + ch * plane] : 0.0f;
+    Cimg[ch] = ok ? A.img[pofs + ch * plane] : 0.0f;
+  }
+  if (tp.inside) invN = 1.0f / A.norm[p];
+  const int K = A.top_k;
+  const float inv_span = 1.0f / (c.zfar - c.znear);
+  const float igam = 1.0f / A.gamma;
+  const long long vbase = (long long)view * A.n;
+
+  for (int s = 0; s < K; s++) {
+    const int id = tp.inside ? A.topk[p * K + s] : -1;
+    const bool valid = id >= 0 && id < A.n;
+    uint64_t pend = ballot64(valid);
+    if (pend == 0) break;              // slots fill in order
+    const long long rec = vbase + id;
+    double vg[5];          // dq0, dq1, dq2, d_reff, d_opac
+    float vf[CM];
+#pragma unroll
+    for (int q = 0; q < 5; q++) vg[q] = 0.0;
+#pragma unroll
+    for (int q = 0; q < CM; q++) vf[q] = 0.0f;
+    if (valid) {
+      const DrawRec d = A.draw[rec];
+      const AuxRec ax = A.aux[rec];
+      const SphereGeo sg = sphere_geo(c, tp, d);
+      double sx, sy;
+      const double Dd = sphere_D_ex(ray, sg.u, sg.v, sg.ax, sg.ay, sg.A, sx, sy);
+      const float D = (float)Dd;
+      const float w = d.w * D;             // the forward's weight, bit for bit
+      float dw = 0.0f;
+#pragma unroll
+      for (int ch = 0; ch < CM; ch++) {
+        const float f = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+        vf[ch] = g[ch] * w * invN;
+        dw = __builtin_fmaf(g[ch], f - Cimg[ch], dw);
+      }
+      dw *= invN;
+      const float o = ax.opac;
+      vg[4] = (double)(dw * w * (1.0f / o + ax.zhat * igam));
+      const int flags = (int)ax.flags;
+      if (!(flags & 2)) {
+        // dist^2 = |q|^2 - (q.d)^2 / |d|^2; its gradient 2 q_perp with
+        // q_perp = qz ((d.delta) g d - delta), delta = (sx, sy, 0).
+        const double dD = (double)dw * (double)d.w;
+        const double dz = (double)dw * (double)w * (double)o * (double)igam;
+        const double reff = ax.w;
+        const double dd2 = -dD / (reff * reff);
+        const double c1 = (ray.dx * sx + ray.dy * sy) * ray.g;
+        const double k2 = 2.0 * dd2 * (double)ax.z;
+        vg[0] = k2 * (c1 * ray.dx - sx);
+        vg[1] = k2 * (c1 * ray.dy - sy);
+        vg[2] = k2 * c1 - dz * (double)inv_span;
+        if (!(flags & 1)) vg[3] = dD * 2.0 * (1.0 - Dd) / reff;
+      }
+    }
+    while (pend) {
+      const int leader = __builtin_ctzll(pend);
+      const int lid = __builtin_amdgcn_readlane(id, leader);
+      const bool mine = valid && id == lid;
+      double *dg = A.accg + (size_t)(vbase + lid) * ACC_G;
+      float *df = A.accf + (size_t)(vbase + lid) * A.C;
+#pragma unroll
+      for (int q = 0; q < 5; q++) {
+        const double t = wave_sum_f64(mine ? vg[q] : 0.0);
+        if (lane == (unsigned)leader && t != 0.0) atomicAdd(dg + q, t);
+      }
+#pragma unroll
+      for (int q = 0; q < CM; q++) {
+        const float t = wave_sum(mine ? vf[q] : 0.0f);
+        if (lane == (unsigned)leader && q < A.C && t != 0.0f) atomicAdd(df + q, t);
+      }
+      pend &= ~ballot64(mine);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-primitive chain rule (fp64), one thread per primitive, views summed.
+// ---------------------------------------------------------------------------
+struct ProjBwdArgs {
+  int kind, n, C;
+  const float *pos, *scale, *rot;
+  const BinRec *bin;
+  const double *accg;
+  const float *accf;
+  float *gpos, *gscale, *grot, *gop, *gfeat, *gR, *gt;
+  int accumulate;
+};
+
+__device__ __forceinline__ void put(float *p, size_t i, double x, int accumulate) {
+  if (accumulate) p[i] += (float)x;
+  else p[i] = (float)x;
+}
+
+__device__ __forceinline__ bool rec_live(const BinRec &b) { return b.ntx != 0; }
+
+__global__ __launch_bounds__(256) void k_proj_bwd_sphere(ViewTable vt, ProjBwdArgs P, int vbeg, int vend) {
+  __shared__ float s_red[12][4];
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool ok = i < P.n;
+  const unsigned lane = lane_id(), w = threadIdx.x / WAVE;
+  double px = 0, py = 0, pz = 0;
+  if (ok) { px = P.pos[3 * i]; py = P.pos[3 * i + 1]; pz = P.pos[3 * i + 2]; }
+  double dp[3] = {0, 0, 0}, dr = 0, dop = 0;
+  for (int v = vbeg; v < vend; v++) {
+    const ViewDev &c = vt.v[v];
+    float cam[12];
+#pragma unroll
+    for (int q = 0; q < 12; q++) cam[q] = 0.0f;
+    if (ok) {
+      const long long rec = (long long)v * P.n + i;
+      if (rec_live(P.bin[rec])) {
+        const double *A = P.accg + (size_t)rec * ACC_G;
+        const double dq[3] = {A[0], A[1], A[2]};
+#pragma unroll
+        for (int a = 0; a < 3; a++)
+          dp[a] += (double)c.R[a] * dq[0] + (double)c.R[3 + a] * dq[1] + (double)c.R[6 + a] * dq[2];
+        dr += A[3];
+        dop += A[4];
+        const double pp[3] = {px, py, pz};
+#pragma unroll
+        for (int a = 0; a < 3; a++) {
+#pragma unroll
+          for (int b = 0; b < 3; b++) cam[3 * a + b] = (float)(dq[a] * pp[b]);
+          cam[9 + a] = (float)dq[a];
+        }
+      }
+    }
+    if (P.gR || P.gt) {
+#pragma unroll
+      for (int q = 0; q < 12; q++) {
+        const float t = wave_sum(cam[q]);
+        if (lane == 0) s_red[q][w] = t;
+      }
+      __syncthreads();
+      if (threadIdx.x < 12) {
+        const int q = threadIdx.x;
+        const float t = s_red[q][0] + s_red[q][1] + s_red[q][2] + s_red[q][3];
+        if (t != 0.0f) {
+          if (q < 9 && P.gR) atomicAdd(P.gR + 9 * v + q, t);
+          if (q >= 9 && P.gt) atomicAdd(P.gt + 3 * v + (q - 9), t);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!ok) return;
+  if (P.gpos)
+    for (int a = 0; a < 3; a++) put(P.gpos, 3 * (size_t)i + a, dp[a], P.accumulate);
+  if (P.gscale) put(P.gscale, i, dr, P.accumulate);
+  if (P.gop) put(P.gop, i, dop, P.accumulate);
+  if (P.gfeat)
+    for (int ch = 0; ch < P.C; ch++) {
+      double s = 0;
+      for (int v = vbeg; v < vend; v++) s += P.accf[((size_t)v * P.n + i) * P.C + ch];
+      put(P.gfeat, (size_t)i * P.C + ch, s, P.accumulate);
+    }
+}
+
+// Image-map Jacobian J (2x3) at sensor point m and its derivatives dJ[k][a] = dJ_k / dm_a.
+__device__ void jacobian_and_derivs(const ViewDev &c, const double m[3], double J[6], double dJ[6][3]) {
+#pragma unroll
+  for (int k = 0; k < 6; k++)
+#pragma unroll
+    for (int a = 0; a < 3; a++) dJ[k][a] = 0.0;
+  if (c.kind == SPLAT_CAM_PINHOLE) {
+    const double fx = c.fx, fy = c.fy;
+    const double iz = 1.0 / m[2], iz2 = iz * iz, iz3 = iz2 * iz;
+    J[0] = fx * iz; J[1] = 0.0; J[2] = -fx * m[0] * iz2;
+    J[3] = 0.0; J[4] = fy * iz; J[5] = -fy * m[1] * iz2;
+    dJ[0][2] = -fx * iz2;
+    dJ[2][0] = -fx * iz2;
+    dJ[2][2] = 2.0 * fx * m[0] * iz3;
+    dJ[4][2] = -fy * iz2;
+    dJ[5][1] = -fy * iz2;
+    dJ[5][2] = 2.0 * fy * m[1] * iz3;
+  } else {
+    const double kPi = 3.141592653589793;
+    const double th_max = (double)c.el_max * (kPi / 180.0), th_min = (double)c.el_min * (kPi / 180.0);
+    const double ka = (double)c.W / (2.0 * kPi), kb = (double)c.H / (th_max - th_min);
+    const double x = m[0], y = m[1], z = m[2];
+    const double rho2 = x * x + y * y, rho = sqrt(rho2), r2 = rho2 + z * z;
+    const double rho4 = rho2 * rho2, r4 = r2 * r2;
+    J[0] = ka * y / rho2; J[1] = -ka * x / rho2; J[2] = 0.0;
+    const double h = 1.0 / (r2 * rho);
+    J[3] = kb * x * z * h; J[4] = kb * y * z * h; J[5] = -kb * rho / r2;
+    dJ[0][0] = -2.0 * ka * x * y / rho4;
+    dJ[0][1] = ka * (x * x - y * y) / rho4;
+    dJ[1][0] = ka * (x * x - y * y) / rho4;
+    dJ[1][1] = 2.0 * ka * x * y / rho4;
+    const double hx = -x * (2.0 * rho2 + r2) / (r4 * rho2 * rho);
+    const double hy = -y * (2.0 * rho2 + r2) / (r4 * rho2 * rho);
+    const double hz = -2.0 * z / (r4 * rho);
+    dJ[3][0] = kb * z * (h + x * hx);
+    dJ[3][1] = kb * x * z * hy;
+    dJ[3][2] = kb * x * (h + z * hz);
+    dJ[4][0] = kb * y * z * hx;
+    dJ[4][1] = kb * z * (h + y * hy);
+    dJ[4][2] = kb * y * (h + z * hz);
+    dJ[5][0] = -kb * x * (r2 - 2.0 * rho2) / (rho * r4);
+    dJ[5][1] = -kb * y * (r2 - 2.0 * rho2) / (rho * r4);
+    dJ[5][2] = 2.0 * kb * rho * z / r4;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_proj_bwd_gauss(ViewTable vt, ProjBwdArgs P, int vbeg, int vend) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P.n) return;
+  double gpos[3] = {0, 0, 0}, gs[3] = {0, 0, 0}, gq[4] = {0, 0, 0, 0}, gop = 0;
+  if (P.kind == SPLAT_PRIM_GAUSS2D) {
+    const double s = P.scale[i];
+    for (int v = vbeg; v < vend; v++) {
+      const long long rec = (long long)v * P.n + i;
+      if (!rec_live(P.bin[rec])) continue;
+      const double *A = P.accg + (size_t)rec * ACC_G;
+      gpos[0] += A[0];
+      gpos[1] += A[1];
+      gs[0] += (A[2] + A[4]) * (-2.0 / (s * s * s));
+      gop += A[5];
+    }
+  } else {
+    // forward quantities shared by all views
+    const double s[3] = {P.scale[3 * i], P.scale[3 * i + 1], P.scale[3 * i + 2]};
+    const double q0[4] = {P.rot[4 * i], P.rot[4 * i + 1], P.rot[4 * i + 2], P.rot[4 * i + 3]};
+    const double nq = sqrt(q0[0] * q0[0] + q0[1] * q0[1] + q0[2] * q0[2] + q0[3] * q0[3]);
+    const double w = q0[0] / nq, x = q0[1] / nq, y = q0[2] / nq, z = q0[3] / nq;
+    double Rq[9];
+    Rq[0] = 1.0 - 2.0 * (y * y + z * z); Rq[1] = 2.0 * (x * y - w * z); Rq[2] = 2.0 * (x * z + w * y);
+    Rq[3] = 2.0 * (x * y + w * z); Rq[4] = 1.0 - 2.0 * (x * x + z * z); Rq[5] = 2.0 * (y * z - w * x);
+    Rq[6] = 2.0 * (x * z - w * y); Rq[7] = 2.0 * (y * z + w * x); Rq[8] = 1.0 - 2.0 * (x * x + y * y);
+    double M[9], S3[9];
+    for (int a = 0; a < 3; a++)
+      for (int b = 0; b < 3; b++) M[3 * a + b] = Rq[3 * a + b] * s[b];
+    for (int a = 0; a < 3; a++)
+      for (int b = 0; b < 3; b++)
+        S3[3 * a + b] = M[3 * a] * M[3 * b] + M[3 * a + 1] * M[3 * b + 1] + M[3 * a + 2] * M[3 * b + 2];
+    double dS3sum[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+    for (int v = vbeg; v < vend; v++) {
+      const long long rec = (long long)v * P.n + i;
+      if (!rec_live(P.bin[rec])) continue;
+      const ViewDev &c = vt.v[v];
+      const double *A = P.accg + (size_t)rec * ACC_G;
+      double W[9];
+      for (int k = 0; k < 9; k++) W[k] = c.R[k];
+      double m[3];
+      for (int a = 0; a < 3; a++)
+        m[a] = W[3 * a] * (double)P.pos[3 * i] + W[3 * a + 1] * (double)P.pos[3 * i + 1] +
+               W[3 * a + 2] * (double)P.pos[3 * i + 2] + (double)c.t[a];
+      double J[6], dJm[6][3];
+      jacobian_and_derivs(c, m, J, dJm);
+      double T[6];
+      for (int a = 0; a < 2; a++)
+        for (int b = 0; b < 3; b++) T[3 * a + b] = J[3 * a] * W[b] + J[3 * a + 1] * W[3 + b] + J[3 * a + 2] * W[6 + b];
+      double TS[6];
+      for (int a = 0; a < 2; a++)
+        for (int b = 0; b < 3; b++) TS[3 * a + b] = T[3 * a] * S3[b] + T[3 * a + 1] * S3[3 + b] + T[3 * a + 2] * S3[6 + b];
+      const double sxx = TS[0] * T[0] + TS[1] * T[1] + TS[2] * T[2];
+      const double sxy = TS[0] * T[3] + TS[1] * T[4] + TS[2] * T[5];
+      const double syy = TS[3] * T[3] + TS[4] * T[4] + TS[5] * T[5];
+      const double det = sxx * syy - sxy * sxy;
+      const double Q[4] = {syy / det, -sxy / det, -sxy / det, sxx / det};
+      // dL/dQ as a symmetric matrix (the off-diagonal parameter appears twice)
+      const double Gq[4] = {A[2], 0.5 * (double)A[3], 0.5 * (double)A[3], A[4]};
+      double QG[4], dS2[4];
+      QG[0] = Q[0] * Gq[0] + Q[1] * Gq[2]; QG[1] = Q[0] * Gq[1] + Q[1] * Gq[3];
+      QG[2] = Q[2] * Gq[0] + Q[3] * Gq[2]; QG[3] = Q[2] * Gq[1] + Q[3] * Gq[3];
+      dS2[0] = -(QG[0] * Q[0] + QG[1] * Q[2]); dS2[1] = -(QG[0] * Q[1] + QG[1] * Q[3]);
+      dS2[2] = -(QG[2] * Q[0] + QG[3] * Q[2]); dS2[3] = -(QG[2] * Q[1] + QG[3] * Q[3]);
+      // Sigma2 = T S3 T^T
+      for (int a = 0; a < 3; a++)
+        for (int b = 0; b < 3; b++) {
+          double acc = 0.0;
+          for (int pp = 0; pp < 2; pp++)
+            for (int qq = 0; qq < 2; qq++) acc += T[3 * pp + a] * dS2[2 * pp + qq] * T[3 * qq + b];
+          dS3sum[3 * a + b] += acc;
+        }
+      double dT[6];
+      for (int a = 0; a < 2; a++)
+        for (int b = 0; b < 3; b++) dT[3 * a + b] = 2.0 * (dS2[2 * a] * TS[b] + dS2[2 * a + 1] * TS[3 + b]);
+      double dJ[6];
+      for (int a = 0; a < 2; a++)
+        for (int b = 0; b < 3; b++) dJ[3 * a + b] = dT[3 * a] * W[3 * b] + dT[3 * a + 1] * W[3 * b + 1] + dT[3 * a + 2] * W[3 * b + 2];
+      double dm[3];
+      for (int a = 0; a < 3; a++) {
+        double t = (double)A[0] * J[a] + (double)A[1] * J[3 + a];
+        for (int k = 0; k < 6; k++) t += dJ[k] * dJm[k][a];
+        dm[a] = t;
+      }
+      if (c.kind == SPLAT_CAM_SPHERICAL) {
+        const double rr = sqrt(m[0] * m[0] + m[1] * m[1] + m[2] * m[2]);
+        for (int a = 0; a < 3; a++) dm[a] += (double)A[6] * m[a] / rr;
+      }
+      for (int a = 0; a < 3; a++) gpos[a] += W[a] * dm[0] + W[3 + a] * dm[1] + W[6 + a] * dm[2];
+      gop += A[5];
+    }
+    // Sigma3 = M M^T, M = Rq diag(s)
+    double dM[9], dRq[9];
+    for (int a = 0; a < 3; a++)
+      for (int b = 0; b < 3; b++)
+        dM[3 * a + b] = 2.0 * (dS3sum[3 * a] * M[b] + dS3sum[3 * a + 1] * M[3 + b] + dS3sum[3 * a + 2] * M[6 + b]);
+    for (int a = 0; a < 3; a++)
+      for (int b = 0; b < 3; b++) {
+        gs[b] += dM[3 * a + b] * Rq[3 * a + b];
+        dRq[3 * a + b] = dM[3 * a + b] * s[b];
+      }
+    double dqn[4];
+    dqn[0] = 2.0 * (-z * dRq[1] + y * dRq[2] + z * dRq[3] - x * dRq[5] - y * dRq[6] + x * dRq[7]);
+    dqn[1] = 2.0 * (y * dRq[1] + z * dRq[2] + y * dRq[3] - 2.0 * x * dRq[4] - w * dRq[5] + z * dRq[6] + w * dRq[7] -
+                    2.0 * x * dRq[8]);
+    dqn[2] = 2.0 * (-2.0 * y * dRq[0] + x * dRq[1] + w * dRq[2] + x * dRq[3] + z * dRq[5] - w * dRq[6] + z * dRq[7] -
+                    2.0 * y * dRq[8]);
+    dqn[3] = 2.0 * (-2.0 * z * dRq[0] - w * dRq[1] + x * dRq[2] + w * dRq[3] - 2.0 * z * dRq[4] + y * dRq[5] +
+                    x * dRq[6] + y * dRq[7]);
+    const double qn[4] = {w, x, y, z};
+    const double dot = qn[0] * dqn[0] + qn[1] * dqn[1] + qn[2] * dqn[2] + qn[3] * dqn[3];
+    for (int a = 0; a < 4; a++) gq[a] = (dqn[a] - qn[a] * dot) / nq;
+  }
+  const int pd = P.kind == SPLAT_PRIM_GAUSS2D ? 2 : 3;
+  const int sd = P.kind == SPLAT_PRIM_GAUSS3D ? 3 : 1;
+  if (P.gpos)
+    for (int a = 0; a < pd; a++) put(P.gpos, (size_t)pd * i + a, gpos[a], P.accumulate);
+  if (P.gscale)
+    for (int a = 0; a < sd; a++) put(P.gscale, (size_t)sd * i + a, gs[a], P.accumulate);
+  if (P.grot && P.kind == SPLAT_PRIM_GAUSS3D)
+    for (int a = 0; a < 4; a++) put(P.grot, 4 * (size_t)i + a, gq[a], P.accumulate);
+  if (P.gop) put(P.gop, i, gop, P.accumulate);
+  if (P.gfeat)
+    for (int ch = 0; ch < P.C; ch++) {
+      double sum = 0;
+      for (int v = vbeg; v < vend; v++)
+        if (vt.v[v].kind != SPLAT_CAM_SPHERICAL) sum += P.accf[((size_t)v * P.n + i) * P.C + ch];
+      put(P.gfeat, (size_t)i * P.C + ch, sum, P.accumulate);
+    }
+}
+
+template <int CM>
+void launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begin, int ntiles, bool has_pin,
+                   bool has_sph, hipStream_t stream) {
+  if (kind == SPLAT_PRIM_SPHERE) {
+    hipLaunchKernelGGL(k_bwd_sphere<CM>, dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
+  } else {
+    if (has_pin) hipLaunchKernelGGL((k_bwd_alpha<CM, false>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
+    if (has_sph) hipLaunchKernelGGL((k_bwd_alpha<1, true>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
+  }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(long long nrec, int C) { return acc_bytes(nrec, C); }
+
+int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, const BinRec *bin,
+                      const splat_grads *gr, hipStream_t stream) {
+  // accumulator rows of the requested views only
+  const long long r0 = (long long)vbeg * A.n, r1 = (long long)vend * A.n;
+  const long long ng = (r1 - r0) * ACC_G, nf = (r1 - r0) * A.C;
+  if (ng > 0)
+    hipLaunchKernelGGL(k_fill_f64, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, A.accg + r0 * ACC_G, ng);
+  if (nf > 0)
+    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, stream, A.accf + r0 * A.C, nf);
+  if (!gr->accumulate) {
+    if (gr->cam_R) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(256), 0, stream, gr->cam_R, 9ll * vt.n);
+    if (gr->cam_t) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(256), 0, stream, gr->cam_t, 3ll * vt.n);
+  }
+  SPLAT_LAUNCH_CHECK();
+  const int tile_begin = vt.v[vbeg].tile_off;
+  const int tile_end = vend < vt.n ? vt.v[vend].tile_off : vt.total_tiles;
+  const int ntiles = tile_end - tile_begin;
+  bool has_pin = false, has_sph = false;
+  for (int v = vbeg; v < vend; v++) {
+    if (vt.v[v].kind == SPLAT_CAM_SPHERICAL) has_sph = true;
+    else has_pin = true;
+  }
+  if (ntiles > 0) {
+    switch (channel_bucket(A.C)) {
+      case 1: launch_bwd_cm<1>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+      case 2: launch_bwd_cm<2>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+      case 3: launch_bwd_cm<3>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+      case 4: launch_bwd_cm<4>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+      case 8: launch_bwd_cm<8>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+      case 16: launch_bwd_cm<16>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+      case 32: launch_bwd_cm<32>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+      default: launch_bwd_cm<64>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+    }
+    SPLAT_LAUNCH_CHECK();
+  }
+  ProjBwdArgs P;
+  P.kind = pr->kind; P.n = pr->n; P.C = A.C;
+  P.pos = pr->pos; P.scale = pr->scale; P.rot = pr->rot;
+  P.bin = bin; P.accg = A.accg; P.accf = A.accf;
+  P.gpos = gr->pos; P.gscale = gr->scale; P.grot = gr->rot; P.gop = gr->opacity; P.gfeat = gr->feat;
+  P.gR = gr->cam_R; P.gt = gr->cam_t;
+  P.accumulate = gr->accumulate;
+  if (pr->n > 0) {
+    dim3 grid((pr->n + 255) / 256);
+    if (pr->kind == SPLAT_PRIM_SPHERE) hipLaunchKernelGGL(k_proj_bwd_sphere, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
+    else hipLaunchKernelGGL(k_proj_bwd_gauss, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
+    SPLAT_LAUNCH_CHECK();
+  }
+  return SPLAT_OK;
+}

@@ -1,0 +1,183 @@
+// Internal definitions shared by the libsplat HIP sources (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "splat.h"
+
+#define TILE 16
+#define TILE_PIX 256
+#define WAVE 64
+
+// ---------------------------------------------------------------------------
+// View table, passed by value to every kernel (fits the kernel-argument block).
+// ---------------------------------------------------------------------------
+struct ViewDev {
+  int kind, W, H, TW, TH;
+  int tile_off;         // first global tile of the view
+  int chan;             // image channels of the view (C, or 2 for spherical)
+  int pad0;
+  long long pix_off;    // first pixel of the view in per-pixel buffers
+  long long img_off;    // first float of the view in the image buffer
+  float R[9], t[3];
+  float fx, fy, cx, cy;
+  float el_min, el_max, znear, zfar;
+};
+
+struct ViewTable {
+  int n;
+  int total_tiles;
+  long long total_pix;
+  ViewDev v[SPLAT_MAX_VIEWS];
+};
+
+__device__ __forceinline__ int view_of_tile(const ViewTable &vt, int gtile) {
+  int v = 0;
+#pragma unroll 1
+  while (v + 1 < vt.n && vt.v[v + 1].tile_off <= gtile) v++;
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Projected records (structure of arrays inside the opaque proj buffer).
+// ---------------------------------------------------------------------------
+// Binning part, read by the emit kernel.
+struct __align__(16) BinRec {
+  uint32_t key;          // fp32 bits of the depth key
+  uint16_t tx0, ntx;     // tile columns tx0 .. tx0+ntx-1 (mod TW for spherical views)
+  uint16_t ty0, ty1;     // tile rows (inclusive)
+  uint32_t pad;
+};
+
+// Compositing part, staged into LDS by the render kernels (48 bytes).
+//  Gaussians: projected mean (u, v), conic (a, b, c) with power = (a dx^2 + 2 b dx dy + c dy^2)/2,
+//             w = opacity, e unused.
+//  Spheres:   projected centre (u, v), a = A = qz^2 / r_eff^2, w = o exp(o zhat / gamma),
+//             e = stop bound, b and c unused.
+// Positions and the quadratic form stay fp64: an elongated footprint makes the three
+// conic terms cancel by the covariance's condition number, and per-pixel offsets from
+// a far tile need the full mantissa.
+struct __align__(16) DrawRec {
+  double u, v;
+  double a, b, c;
+  float w, e;
+};
+
+// Backward-only part.
+//  Gaussians: depth (range for spherical views) in x; rest unused.
+//  Spheres:   sensor-frame centre q, r_eff, opacity, zhat, flags (bit0 floored, bit1 gated).
+struct __align__(16) AuxRec {
+  float x, y, z, w;
+  float opac, zhat, depth, flags;
+};
+
+struct ProjLayout {
+  BinRec *bin;
+  DrawRec *draw;
+  AuxRec *aux;
+};
+
+static inline size_t proj_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static inline ProjLayout proj_layout(void *base, long long nrec) {
+  char *p = (char *)base;
+  ProjLayout L;
+  L.bin = (BinRec *)p;
+  p += proj_align(sizeof(BinRec) * (size_t)nrec);
+  L.draw = (DrawRec *)p;
+  p += proj_align(sizeof(DrawRec) * (size_t)nrec);
+  L.aux = (AuxRec *)p;
+  return L;
+}
+
+static inline size_t proj_bytes(long long nrec) {
+  return proj_align(sizeof(BinRec) * (size_t)nrec) + proj_align(sizeof(DrawRec) * (size_t)nrec) +
+         proj_align(sizeof(AuxRec) * (size_t)nrec);
+}
+
+// Per-record gradient accumulators, two arrays in the backward workspace:
+//  geometric part, fp64 [records][ACC_G]:
+//    Gaussians: [du, dv, d_ca, d_cb, d_cc, d_opac, d_depth, -]
+//    Spheres:   [dq0, dq1, dq2, d_reff, d_opac, -, -, -]
+//  features, fp32 [records][channels].
+// The geometric sums feed an ill-conditioned chain (conic -> covariance ->
+// rotation), so they are formed and summed in double precision.
+#define ACC_G 8
+
+struct AccLayout {
+  double *g;
+  float *f;
+};
+
+static inline size_t acc_bytes(long long nrec, int C) {
+  return proj_align(sizeof(double) * ACC_G * (size_t)nrec) + proj_align(sizeof(float) * (size_t)nrec * C);
+}
+
+static inline AccLayout acc_layout(void *base, long long nrec) {
+  AccLayout a;
+  a.g = (double *)base;
+  a.f = (float *)((char *)base + proj_align(sizeof(double) * ACC_G * (size_t)nrec));
+  return a;
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 helpers.
+// ---------------------------------------------------------------------------
+// Inclusive prefix sum across the wave with DPP row shifts and row broadcasts;
+// lane 63 ends up holding the wave total.
+__device__ __forceinline__ float wave_sum_to_last(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));  // row_shr:1
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));  // row_shr:2
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));  // row_shr:4
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));  // row_shr:8
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false)); // row_bcast:15
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false)); // row_bcast:31
+  return x;
+}
+
+// Wave total, uniform across lanes.
+__device__ __forceinline__ float wave_sum(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_to_last(x)), 63));
+}
+
+// DPP move of a double (two 32-bit halves).
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long b = __builtin_bit_cast(long long, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), CTRL, ROWS, 0xf, BOUND);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROWS, 0xf, BOUND);
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+// fp64 sum within each 16-lane row; lanes 15, 31, 47, 63 hold the row sums.
+__device__ __forceinline__ double row_sum_to_last_f64(double x) {
+  x += dpp_f64<0x111, 0xf, true>(x);
+  x += dpp_f64<0x112, 0xf, true>(x);
+  x += dpp_f64<0x114, 0xf, true>(x);
+  x += dpp_f64<0x118, 0xf, true>(x);
+  return x;
+}
+
+// fp64 wave total, uniform across lanes.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  x = row_sum_to_last_f64(x);
+  x += dpp_f64<0x142, 0xa, false>(x);   // row_bcast:15
+  x += dpp_f64<0x143, 0xc, false>(x);   // row_bcast:31
+  const long long b = __builtin_bit_cast(long long, x);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+__device__ __forceinline__ unsigned lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// HIP error check used by the host-side launchers.
+#define SPLAT_LAUNCH_CHECK()                                   \
+  do {                                                         \
+    if (hipPeekAtLastError() != hipSuccess) {                  \
+      (void)hipGetLastError();                                 \
+      return SPLAT_ERR_HIP;                                    \
+    }                                                          \
+  } while (0)
