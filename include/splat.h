@@ -148,9 +148,11 @@ int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *pro
  *   img: image layout above.
  *   Gaussians: T_final [pixels] final transmittance, last [pixels] number of list entries
  *     up to and including the last composited one (the backward replays from there).
- *   Spheres: norm [pixels] the normalisation sum, topk [pixels][top_k] int32 primitive
- *     ids of the first top_k contributing spheres (-1 padded) - the backward buffer of
- *     Pulsar B.1.4. T_final/last may be NULL for spheres, norm/topk for Gaussians. */
+ *   Spheres: norm [pixels] the normalisation sum, topk [pixels][top_k] int32: for each of
+ *     the first top_k contributing spheres, its index into the sorted keys/vals arrays of
+ *     splat_bin_sort (-1 padded); vals[index] - view*n is the primitive id. Together they
+ *     are the backward buffer of Pulsar B.1.4. Sphere outputs need capacity < 2^31.
+ *     T_final/last may be NULL for spheres, norm/topk for Gaussians. */
 int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *prims,
                      const splat_params *prm, const void *proj, const uint32_t *vals,
                      const uint32_t *tile_ranges, const int32_t *overflow, float *img,

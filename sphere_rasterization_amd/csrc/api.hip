@@ -9,8 +9,8 @@
 #include "render_common.h"
 #include "splat_internal.h"
 
-int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, void *proj, uint32_t *counts,
-                   hipStream_t stream);
+int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, double alpha_min, void *proj,
+                   uint32_t *counts, hipStream_t stream);
 size_t sort_workspace_bytes(long long nrec, long long capacity);
 int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t *counts, long long capacity,
                     uint64_t *keys, uint32_t *vals, uint32_t *ranges, int64_t *num_pairs, int32_t *overflow,
@@ -161,7 +161,7 @@ int splat_project(const splat_camera *cams, int n_views, const splat_prims *prim
   if ((st = check_params(prm, prims->kind))) return st;
   if (prims->n == 0) return SPLAT_OK;
   CHECK(proj && pair_counts, SPLAT_ERR_INVALID_ARG, "proj / pair_counts NULL");
-  return launch_project(vt, prims, (double)prm->gamma, proj, pair_counts, stream);
+  return launch_project(vt, prims, (double)prm->gamma, (double)prm->alpha_min, proj, pair_counts, stream);
 }
 
 int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *proj, const uint32_t *pair_counts,

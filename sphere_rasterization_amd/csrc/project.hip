@@ -25,10 +25,11 @@ constexpr double kSupport = 11.082527090316852;  // 2 ln 255, correctly rounded
 struct Rect {
   int valid;
   int tx0, ntx, ty0, ty1;
+  int i0, i1, j0, j1;      // inclusive pixel range (columns unwrapped for spherical views)
 };
 
 __device__ Rect make_rect(const ViewDev &c, double xl, double xh, double yl, double yh) {
-  Rect r = {0, 0, 0, 0, 0};
+  Rect r = {0, 0, 0, 0, 0, 0, -1, 0, -1};
   double fx0 = ceil(xl - 0.5), fx1 = floor(xh - 0.5);
   double fy0 = ceil(yl - 0.5), fy1 = floor(yh - 0.5);
   if (fy0 < 0.0) fy0 = 0.0;
@@ -43,6 +44,7 @@ __device__ Rect make_rect(const ViewDev &c, double xl, double xh, double yl, dou
   if (!(fx0 <= fx1) || !(fy0 <= fy1)) return r;
   long long x0 = (long long)fx0, x1 = (long long)fx1;
   int y0 = (int)fy0, y1 = (int)fy1;
+  r.i0 = (int)x0; r.i1 = (int)x1; r.j0 = y0; r.j1 = y1;
   r.ty0 = y0 / TILE;
   r.ty1 = y1 / TILE;
   if (c.kind != SPLAT_CAM_SPHERICAL) {
@@ -88,7 +90,7 @@ __device__ void write_rect(const ProjLayout &L, long long k, uint32_t *counts, c
 struct PrimArgs {
   int kind, n;
   const float *pos, *scale, *rot, *opacity, *depth;
-  double gamma;
+  double gamma, alpha_min;
 };
 
 __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjLayout L, uint32_t *counts) {
@@ -130,13 +132,14 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
     double area = kPi * (fx * r / q[2]) * (fy * r / q[2]);
     int floored = r < rfl, gated = !(area > 3.0);
     DrawRec d;
-    d.u = u;
-    d.v = v;
-    d.a = q[2] * q[2] / (re * re);
-    d.b = 0.0;
-    d.c = 0.0;
+    d.u = q[0] / q[2];                 // normalised centre a = q / qz
+    d.v = q[1] / q[2];
+    d.a = q[2] * q[2] / (re * re);     // A = qz^2 / r_eff^2
+    d.b = u;                           // projected centre (pixels), informational
+    d.c = v;
     d.w = (float)(o * e);
     d.e = (float)bnd;
+    d.i0 = rc.i0; d.i1 = rc.i1; d.j0 = rc.j0; d.j1 = rc.j1;
     L.draw[k] = d;
     AuxRec a;
     a.x = (float)q[0]; a.y = (float)q[1]; a.z = (float)q[2]; a.w = (float)re;
@@ -245,6 +248,20 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
   d.c = sxx / det;
   d.w = (float)o;
   d.e = 0.0f;
+  // Pixels that can reach alpha >= alpha_min: power <= ln(o / alpha_min); the
+  // threshold is inflated by 1e-4 to cover fp32 rounding of alpha.
+  d.i0 = 0; d.i1 = -1; d.j0 = 0; d.j1 = -1;
+  const double lim = log(o / P.alpha_min) + 1e-4;
+  if (lim > 0.0) {
+    if (c.kind == SPLAT_CAM_SPHERICAL) {
+      d.i0 = -(1 << 30); d.i1 = 1 << 30;     // columns wrap: every quadrant
+      d.j0 = rc.j0; d.j1 = rc.j1;
+    } else {
+      const double ax = sqrt(2.0 * lim * sxx), ay = sqrt(2.0 * lim * syy);
+      const Rect dr = make_rect(c, u - ax, u + ax, v - ay, v + ay);
+      if (dr.valid) { d.i0 = dr.i0; d.i1 = dr.i1; d.j0 = dr.j0; d.j1 = dr.j1; }
+    }
+  }
   L.draw[k] = d;
   AuxRec a;
   a.x = (float)depth; a.y = 0.f; a.z = 0.f; a.w = 0.f;
@@ -254,14 +271,15 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
 
 }  // namespace
 
-int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, void *proj, uint32_t *counts,
-                   hipStream_t stream) {
+int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, double alpha_min, void *proj,
+                   uint32_t *counts, hipStream_t stream) {
   long long nrec = (long long)vt.n * pr->n;
   if (nrec == 0) return SPLAT_OK;
   PrimArgs P;
   P.kind = pr->kind; P.n = pr->n;
   P.pos = pr->pos; P.scale = pr->scale; P.rot = pr->rot; P.opacity = pr->opacity; P.depth = pr->depth;
   P.gamma = gamma;
+  P.alpha_min = alpha_min;
   ProjLayout L = proj_layout(proj, nrec);
   unsigned grid = (unsigned)((nrec + 255) / 256);
   hipLaunchKernelGGL(k_project, dim3(grid), dim3(256), 0, stream, vt, P, L, counts);

@@ -13,8 +13,8 @@
 // update the same addresses). Alpha blending: every lane of a wave walks the same
 // list entry, so each value is row-reduced and four lanes add into an LDS slot
 // per entry; one global atomic per entry and value leaves the tile. Spheres:
-// lanes are grouped by primitive id (ballot + readlane) and each group is
-// reduced across the wave before a single global atomic.
+// each pixel's first top_k spheres are tile-list positions, so contributions are
+// added into an LDS table indexed by position and flushed once per tile.
 #include "splat_internal.h"
 
 #include "render_common.h"
@@ -57,6 +57,7 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   __shared__ uint32_t s_rid[256];
   __shared__ double s_ag[6][256];           // du, dv, d_ca, d_cb, d_cc, d_opac
   __shared__ float s_af[NF][256];           // d_feat (or d_depth)
+  __shared__ QuadLists s_l;
   __shared__ uint32_t s_maxlast;
   if (*A.overflow) return;
   const int gtile = tile_begin + blockIdx.x;
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile];
   const uint32_t len = A.ranges[2 * gtile + 1] - start;
-  const unsigned lane = lane_id();
+  const unsigned lane = lane_id(), wq = threadIdx.x >> 6;
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
   const size_t plane = (size_t)c.W * c.H;
   const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   for (int hi = (int)maxlast; hi > 0; hi -= 256) {
     const int lo = hi > 256 ? hi - 256 : 0;
     const int cnt = hi - lo;
+    unsigned mask = 0;
     if ((int)threadIdx.x < cnt) {
       const uint32_t rid = A.vals[start + lo + threadIdx.x];
       const DrawRec d = A.draw[rid];
@@ -119,14 +121,16 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
       for (int q = 0; q < 6; q++) s_ag[q][threadIdx.x] = 0.0;
 #pragma unroll
       for (int q = 0; q < NF; q++) s_af[q][threadIdx.x] = 0.0f;
+      mask = quadrant_mask(tp, d);
     }
-    __syncthreads();
-    for (int k = cnt - 1; k >= 0; k--) {
-      const uint32_t pos = (uint32_t)(lo + k);
-      const double2 ab = s_ab[k], co = s_co[k];
+    build_quad_lists(s_l, mask);
+    for (int k = s_l.cnt[wq] - 1; k >= 0; k--) {
+      const int idx = s_l.idx[wq][k];
+      const uint32_t pos = (uint32_t)(lo + idx);
+      const double2 ab = s_ab[idx], co = s_co[idx];
       float G, og;
       double dx, dy;
-      const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[k], ab, co, amax, G, og, dx, dy);
+      const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
       const bool act = pos < lastp && al >= amin;
       if (ballot64(act) == 0) continue;
       double vg[6];
@@ -141,14 +145,14 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         const float Tk = (float)Tkd;
         float da = 0.0f;
         if (LIDAR) {
-          const float dep = s_f[0][k];
+          const float dep = s_f[0][idx];
           vf[0] = Tk * al * g[0];
           da = Tk * (dep - Sb[0]) * g[0] + (float)(Tfin / (1.0 - (double)al)) * g[1];
           Sb[0] = __builtin_fmaf(al, dep, om * Sb[0]);
         } else {
 #pragma unroll
           for (int ch = 0; ch < CM; ch++) {
-            const float f = s_f[ch][k];
+            const float f = s_f[ch][idx];
             vf[ch] = Tk * al * g[ch];
             da = __builtin_fmaf(Tk * (f - Sb[ch]), g[ch], da);
             Sb[ch] = __builtin_fmaf(al, f, om * Sb[ch]);
@@ -158,9 +162,9 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         if (!(og > amax)) {              // alpha is the constant amax where clamped
           vg[5] = (double)(G * da);
           const double dp = -(double)al * (double)da;     // d loss / d power
-          const double ha = ab.x, b = ab.y, hc = co.x;    // a/2, b, c/2
-          vg[0] = -dp * (2.0 * ha * dx + b * dy);
-          vg[1] = -dp * (b * dx + 2.0 * hc * dy);
+          const double ha = ab.x, bb = ab.y, hc = co.x;   // a/2, b, c/2
+          vg[0] = -dp * (2.0 * ha * dx + bb * dy);
+          vg[1] = -dp * (bb * dx + 2.0 * hc * dy);
           vg[2] = dp * 0.5 * dx * dx;
           vg[3] = dp * dx * dy;
           vg[4] = dp * 0.5 * dy * dy;
@@ -169,12 +173,12 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
 #pragma unroll
       for (int q = 0; q < 6; q++) {
         const double r = row_sum_to_last_f64(vg[q]);
-        if ((lane & 15u) == 15u) atomicAdd(&s_ag[q][k], r);
+        if ((lane & 15u) == 15u) atomicAdd(&s_ag[q][idx], r);
       }
 #pragma unroll
       for (int q = 0; q < NF; q++) {
         const float r = row_sum_to_last(vf[q]);
-        if ((lane & 15u) == 15u) atomicAdd(&s_af[q][k], r);
+        if ((lane & 15u) == 15u) atomicAdd(&s_af[q][idx], r);
       }
     }
     __syncthreads();
@@ -204,19 +208,38 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
 
 // ---------------------------------------------------------------------------
 // Sphere backward over the first top_k contributing spheres of each pixel.
+// The forward recorded each one as its index in the sorted pair list, i.e. a
+// position in this tile's list. The tile list is walked front to back in staged
+// batches up to the last recorded position; each wave takes the entries that
+// reach its quadrant, and a lane contributes when the entry is the next of its
+// recorded spheres. Contributions are row-reduced (DPP) into an LDS slot per
+// entry, and each touched entry leaves the tile with one atomic per value.
 // ---------------------------------------------------------------------------
 template <int CM>
 __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int tile_begin) {
+  constexpr int NV = 5 + CM;                  // dq0, dq1, dq2, d_reff, d_opac, d_feat...
+  __shared__ double2 s_a[256];                // normalised centre (ax, ay)
+  __shared__ double2 s_Aw[256];               // A, (oe, flags) packed
+  __shared__ float4 s_x[256];                 // qz, r_eff, opacity, zhat
+  __shared__ float s_f[CM][256];
+  __shared__ uint32_t s_rid[256];
+  __shared__ float s_acc[NV][256];
+  __shared__ uint32_t s_top[256 * SPLAT_TOPK_MAX];
+  __shared__ QuadLists s_l;
+  __shared__ uint32_t s_npos;
   if (*A.overflow) return;
   const int gtile = tile_begin + blockIdx.x;
   const int view = view_of_tile(vt, gtile);
   const ViewDev &c = vt.v[view];
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
+  const uint32_t start = A.ranges[2 * gtile];
+  const uint32_t len = A.ranges[2 * gtile + 1] - start;
   const SphereRay ray = sphere_ray(c, tp);
-  const unsigned lane = lane_id();
+  const unsigned lane = lane_id(), wq = threadIdx.x >> 6;
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
   const size_t plane = (size_t)c.W * c.H;
   const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
+  const int K = A.top_k;
   float g[CM], Cimg[CM];
   float invN = 0.0f;
 #pragma unroll
@@ -225,76 +248,120 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
     g[ch] = ok ? A.dimg[pofs + ch * plane] : 0.0f;
     Cimg[ch] = ok ? A.img[pofs + ch * plane] : 0.0f;
   }
+  // recorded positions, local to the tile and ascending
+  uint32_t *my_top = s_top + threadIdx.x * SPLAT_TOPK_MAX;
+  int ntop = 0;
+  for (int s = 0; s < K && tp.inside; s++) {
+    const int t = A.topk[p * K + s];
+    const uint32_t lp = (uint32_t)t - start;
+    if (t < 0 || lp >= len) break;
+    my_top[ntop++] = lp;
+  }
   if (tp.inside) invN = 1.0f / A.norm[p];
-  const int K = A.top_k;
-  const float inv_span = 1.0f / (c.zfar - c.znear);
-  const float igam = 1.0f / A.gamma;
+  if (threadIdx.x == 0) s_npos = 0;
+  __syncthreads();
+  if (ntop) atomicMax(&s_npos, my_top[ntop - 1] + 1);
+  __syncthreads();
+  const uint32_t npos = s_npos;
+  int nxt = 0;
+  uint32_t tgt = ntop ? my_top[0] : 0xffffffffu;
+  const double inv_span = 1.0 / ((double)c.zfar - (double)c.znear);
+  const double igam = 1.0 / (double)A.gamma;
   const long long vbase = (long long)view * A.n;
 
-  for (int s = 0; s < K; s++) {
-    const int id = tp.inside ? A.topk[p * K + s] : -1;
-    const bool valid = id >= 0 && id < A.n;
-    uint64_t pend = ballot64(valid);
-    if (pend == 0) break;              // slots fill in order
-    const long long rec = vbase + id;
-    double vg[5];          // dq0, dq1, dq2, d_reff, d_opac
-    float vf[CM];
+  for (uint32_t b = 0; b < npos; b += 256) {
+    const uint32_t cnt = min(256u, npos - b);
+    unsigned mask = 0;
+    if (threadIdx.x < cnt) {
+      const uint32_t rid = A.vals[start + b + threadIdx.x];
+      const DrawRec d = A.draw[rid];
+      const AuxRec ax = A.aux[rid];
+      const long long id = (long long)rid - vbase;
+      s_rid[threadIdx.x] = rid;
+      s_a[threadIdx.x] = make_double2(d.u, d.v);
+      s_Aw[threadIdx.x] = make_double2(d.a, __builtin_bit_cast(double, ((unsigned long long)__float_as_uint(ax.flags) << 32) |
+                                                                           (unsigned long long)__float_as_uint(d.w)));
+      s_x[threadIdx.x] = make_float4(ax.z, ax.w, ax.opac, ax.zhat);
 #pragma unroll
-    for (int q = 0; q < 5; q++) vg[q] = 0.0;
+      for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
 #pragma unroll
-    for (int q = 0; q < CM; q++) vf[q] = 0.0f;
-    if (valid) {
-      const DrawRec d = A.draw[rec];
-      const AuxRec ax = A.aux[rec];
-      const SphereGeo sg = sphere_geo(c, tp, d);
-      double sx, sy;
-      const double Dd = sphere_D_ex(ray, sg.u, sg.v, sg.ax, sg.ay, sg.A, sx, sy);
-      const float D = (float)Dd;
-      const float w = d.w * D;             // the forward's weight, bit for bit
-      float dw = 0.0f;
+      for (int q = 0; q < NV; q++) s_acc[q][threadIdx.x] = 0.0f;
+      mask = quadrant_mask(tp, d);
+    }
+    build_quad_lists(s_l, mask);
+    const int lc = s_l.cnt[wq];
+    for (int k = 0; k < lc; k++) {
+      const int idx = s_l.idx[wq][k];
+      const bool mine = tgt == b + (uint32_t)idx;
+      if (ballot64(mine) == 0) continue;
+      float v[NV];
 #pragma unroll
-      for (int ch = 0; ch < CM; ch++) {
-        const float f = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
-        vf[ch] = g[ch] * w * invN;
-        dw = __builtin_fmaf(g[ch], f - Cimg[ch], dw);
+      for (int q = 0; q < NV; q++) v[q] = 0.0f;
+      if (mine) {
+        const double2 aa = s_a[idx], Aw = s_Aw[idx];
+        const float4 x = s_x[idx];
+        const unsigned long long bits = __builtin_bit_cast(unsigned long long, Aw.y);
+        const float oe = __uint_as_float((unsigned)bits);
+        const int flags = (int)__uint_as_float((unsigned)(bits >> 32));
+        // D = 1 - A g |a x d|^2 with a x d from the offsets sx = x - ax, sy = y - ay
+        const double sx = ray.x - aa.x, sy = ray.y - aa.y;
+        const double cr = aa.x * sy - aa.y * sx;
+        const double Dd = 1.0 - Aw.x * ray.g * (sx * sx + sy * sy + cr * cr);
+        const float w = oe * (float)Dd;
+        float dw = 0.0f;
+#pragma unroll
+        for (int ch = 0; ch < CM; ch++) {
+          v[5 + ch] = g[ch] * w * invN;
+          dw = __builtin_fmaf(g[ch], s_f[ch][idx] - Cimg[ch], dw);
+        }
+        dw *= invN;
+        const float o = x.z;
+        v[4] = dw * w * (1.0f / o + x.w * (float)igam);
+        if (!(flags & 2)) {
+          // dist^2 = |q|^2 - (q.d)^2 / |d|^2 has gradient 2 q_perp, with
+          // q_perp = qz ((d.delta) g d - delta), delta = (sx, sy, 0).
+          const double dD = (double)dw * (double)oe;
+          const double dz = (double)dw * (double)w * (double)o * igam;
+          const double reff = x.y;
+          const double dd2 = -dD / (reff * reff);
+          const double c1 = (ray.x * sx + ray.y * sy) * ray.g;
+          const double k2 = 2.0 * dd2 * (double)x.x;
+          v[0] = (float)(k2 * (c1 * ray.x - sx));
+          v[1] = (float)(k2 * (c1 * ray.y - sy));
+          v[2] = (float)(k2 * c1 - dz * inv_span);
+          if (!(flags & 1)) v[3] = (float)(dD * 2.0 * (1.0 - Dd) / reff);
+        }
+        nxt++;
+        tgt = nxt < ntop ? my_top[nxt] : 0xffffffffu;
       }
-      dw *= invN;
-      const float o = ax.opac;
-      vg[4] = (double)(dw * w * (1.0f / o + ax.zhat * igam));
-      const int flags = (int)ax.flags;
-      if (!(flags & 2)) {
-        // dist^2 = |q|^2 - (q.d)^2 / |d|^2; its gradient 2 q_perp with
-        // q_perp = qz ((d.delta) g d - delta), delta = (sx, sy, 0).
-        const double dD = (double)dw * (double)d.w;
-        const double dz = (double)dw * (double)w * (double)o * (double)igam;
-        const double reff = ax.w;
-        const double dd2 = -dD / (reff * reff);
-        const double c1 = (ray.dx * sx + ray.dy * sy) * ray.g;
-        const double k2 = 2.0 * dd2 * (double)ax.z;
-        vg[0] = k2 * (c1 * ray.dx - sx);
-        vg[1] = k2 * (c1 * ray.dy - sy);
-        vg[2] = k2 * c1 - dz * (double)inv_span;
-        if (!(flags & 1)) vg[3] = dD * 2.0 * (1.0 - Dd) / reff;
+#pragma unroll
+      for (int q = 0; q < NV; q++) {
+        const float r = row_sum_to_last(v[q]);
+        if ((lane & 15u) == 15u && r != 0.0f) atomicAdd(&s_acc[q][idx], r);
       }
     }
-    while (pend) {
-      const int leader = __builtin_ctzll(pend);
-      const int lid = __builtin_amdgcn_readlane(id, leader);
-      const bool mine = valid && id == lid;
-      double *dg = A.accg + (size_t)(vbase + lid) * ACC_G;
-      float *df = A.accf + (size_t)(vbase + lid) * A.C;
+    __syncthreads();
+    if (threadIdx.x < cnt) {
+      float v[NV];
+      bool any = false;
 #pragma unroll
-      for (int q = 0; q < 5; q++) {
-        const double t = wave_sum_f64(mine ? vg[q] : 0.0);
-        if (lane == (unsigned)leader && t != 0.0) atomicAdd(dg + q, t);
+      for (int q = 0; q < NV; q++) {
+        v[q] = s_acc[q][threadIdx.x];
+        any |= v[q] != 0.0f;
       }
+      if (any) {
+        const uint32_t rid = s_rid[threadIdx.x];
+        double *dg = A.accg + (size_t)rid * ACC_G;
 #pragma unroll
-      for (int q = 0; q < CM; q++) {
-        const float t = wave_sum(mine ? vf[q] : 0.0f);
-        if (lane == (unsigned)leader && q < A.C && t != 0.0f) atomicAdd(df + q, t);
+        for (int q = 0; q < 5; q++)
+          if (v[q] != 0.0f) atomicAdd(dg + q, (double)v[q]);
+        float *df = A.accf + (size_t)rid * A.C;
+#pragma unroll
+        for (int q = 0; q < CM; q++)
+          if (q < A.C && v[5 + q] != 0.0f) atomicAdd(df + q, v[5 + q]);
       }
-      pend &= ~ballot64(mine);
     }
+    __syncthreads();
   }
 }
 
@@ -319,56 +386,21 @@ __device__ __forceinline__ void put(float *p, size_t i, double x, int accumulate
 __device__ __forceinline__ bool rec_live(const BinRec &b) { return b.ntx != 0; }
 
 __global__ __launch_bounds__(256) void k_proj_bwd_sphere(ViewTable vt, ProjBwdArgs P, int vbeg, int vend) {
-  __shared__ float s_red[12][4];
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const bool ok = i < P.n;
-  const unsigned lane = lane_id(), w = threadIdx.x / WAVE;
-  double px = 0, py = 0, pz = 0;
-  if (ok) { px = P.pos[3 * i]; py = P.pos[3 * i + 1]; pz = P.pos[3 * i + 2]; }
+  if (i >= P.n) return;
   double dp[3] = {0, 0, 0}, dr = 0, dop = 0;
   for (int v = vbeg; v < vend; v++) {
+    const long long rec = (long long)v * P.n + i;
+    if (!rec_live(P.bin[rec])) continue;
     const ViewDev &c = vt.v[v];
-    float cam[12];
+    const double *A = P.accg + (size_t)rec * ACC_G;
+    const double dq[3] = {A[0], A[1], A[2]};
 #pragma unroll
-    for (int q = 0; q < 12; q++) cam[q] = 0.0f;
-    if (ok) {
-      const long long rec = (long long)v * P.n + i;
-      if (rec_live(P.bin[rec])) {
-        const double *A = P.accg + (size_t)rec * ACC_G;
-        const double dq[3] = {A[0], A[1], A[2]};
-#pragma unroll
-        for (int a = 0; a < 3; a++)
-          dp[a] += (double)c.R[a] * dq[0] + (double)c.R[3 + a] * dq[1] + (double)c.R[6 + a] * dq[2];
-        dr += A[3];
-        dop += A[4];
-        const double pp[3] = {px, py, pz};
-#pragma unroll
-        for (int a = 0; a < 3; a++) {
-#pragma unroll
-          for (int b = 0; b < 3; b++) cam[3 * a + b] = (float)(dq[a] * pp[b]);
-          cam[9 + a] = (float)dq[a];
-        }
-      }
-    }
-    if (P.gR || P.gt) {
-#pragma unroll
-      for (int q = 0; q < 12; q++) {
-        const float t = wave_sum(cam[q]);
-        if (lane == 0) s_red[q][w] = t;
-      }
-      __syncthreads();
-      if (threadIdx.x < 12) {
-        const int q = threadIdx.x;
-        const float t = s_red[q][0] + s_red[q][1] + s_red[q][2] + s_red[q][3];
-        if (t != 0.0f) {
-          if (q < 9 && P.gR) atomicAdd(P.gR + 9 * v + q, t);
-          if (q >= 9 && P.gt) atomicAdd(P.gt + 3 * v + (q - 9), t);
-        }
-      }
-      __syncthreads();
-    }
+    for (int a = 0; a < 3; a++)
+      dp[a] += (double)c.R[a] * dq[0] + (double)c.R[3 + a] * dq[1] + (double)c.R[6 + a] * dq[2];   // R^T dq
+    dr += A[3];
+    dop += A[4];
   }
-  if (!ok) return;
   if (P.gpos)
     for (int a = 0; a < 3; a++) put(P.gpos, 3 * (size_t)i + a, dp[a], P.accumulate);
   if (P.gscale) put(P.gscale, i, dr, P.accumulate);
@@ -379,6 +411,44 @@ __global__ __launch_bounds__(256) void k_proj_bwd_sphere(ViewTable vt, ProjBwdAr
       for (int v = vbeg; v < vend; v++) s += P.accf[((size_t)v * P.n + i) * P.C + ch];
       put(P.gfeat, (size_t)i * P.C + ch, s, P.accumulate);
     }
+}
+
+// Camera gradient (Pulsar B.2): dL/dR = sum_k dq_k p_k^T, dL/dt = sum_k dq_k over all
+// spheres of view vbeg + blockIdx.y. Grid-stride over spheres with fp64 partial sums
+// in registers, a block reduction, then twelve atomics per block.
+__global__ __launch_bounds__(256) void k_cam_grad_sphere(ProjBwdArgs P, int vbeg) {
+  __shared__ double s_red[12][4];
+  const int v = vbeg + blockIdx.y;
+  double cam[12];
+#pragma unroll
+  for (int q = 0; q < 12; q++) cam[q] = 0.0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < P.n; i += gridDim.x * blockDim.x) {
+    const long long rec = (long long)v * P.n + i;
+    const double *A = P.accg + (size_t)rec * ACC_G;
+    const double dq[3] = {A[0], A[1], A[2]};      // zero for culled records
+    const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
+#pragma unroll
+    for (int a = 0; a < 3; a++) {
+#pragma unroll
+      for (int b = 0; b < 3; b++) cam[3 * a + b] = __builtin_fma(dq[a], pp[b], cam[3 * a + b]);
+      cam[9 + a] += dq[a];
+    }
+  }
+  const unsigned lane = lane_id(), w = threadIdx.x / WAVE;
+#pragma unroll
+  for (int q = 0; q < 12; q++) {
+    const double t = wave_sum_f64(cam[q]);
+    if (lane == 0) s_red[q][w] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < 12) {
+    const int q = threadIdx.x;
+    const double t = s_red[q][0] + s_red[q][1] + s_red[q][2] + s_red[q][3];
+    if (t != 0.0) {
+      if (q < 9 && P.gR) atomicAdd(P.gR + 9 * v + q, (float)t);
+      if (q >= 9 && P.gt) atomicAdd(P.gt + 3 * v + (q - 9), (float)t);
+    }
+  }
 }
 
 // Image-map Jacobian J (2x3) at sensor point m and its derivatives dJ[k][a] = dJ_k / dm_a.
@@ -616,7 +686,13 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   P.accumulate = gr->accumulate;
   if (pr->n > 0) {
     dim3 grid((pr->n + 255) / 256);
-    if (pr->kind == SPLAT_PRIM_SPHERE) hipLaunchKernelGGL(k_proj_bwd_sphere, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
+    if (pr->kind == SPLAT_PRIM_SPHERE) {
+      hipLaunchKernelGGL(k_proj_bwd_sphere, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
+      if (gr->cam_R || gr->cam_t) {
+        const unsigned nb = (unsigned)min((pr->n + 255) / 256, 512);
+        hipLaunchKernelGGL(k_cam_grad_sphere, dim3(nb, vend - vbeg), dim3(256), 0, stream, P, vbeg);
+      }
+    }
     else hipLaunchKernelGGL(k_proj_bwd_gauss, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
     SPLAT_LAUNCH_CHECK();
   }

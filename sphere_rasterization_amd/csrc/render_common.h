@@ -49,12 +49,13 @@ struct TilePix {
   float pxr, pyr;    // pixel centre relative to the tile origin
 };
 
-// Thread tid of a tile's workgroup owns pixel (tid % 16, tid / 16); a wave64
-// covers four rows of the tile.
+// Thread tid of a tile's workgroup: wave w = tid / 64 owns the 8x8 quadrant
+// (w & 1, w >> 1) of the 16x16 tile, lane l its pixel (l & 7, l >> 3).
 __device__ __forceinline__ TilePix tile_pixel(const ViewDev &c, int gtile, unsigned tid) {
   const int lt = gtile - c.tile_off;
   const int ty = lt / c.TW, tx = lt - ty * c.TW;
-  const int li = (int)(tid & 15u), lj = (int)(tid >> 4);
+  const unsigned w = tid >> 6, l = tid & 63u;
+  const int li = (int)((w & 1u) * 8u + (l & 7u)), lj = (int)((w >> 1) * 8u + (l >> 3));
   TilePix t;
   t.i = tx * TILE + li;
   t.j = ty * TILE + lj;
@@ -66,7 +67,49 @@ __device__ __forceinline__ TilePix tile_pixel(const ViewDev &c, int gtile, unsig
   return t;
 }
 
-__device__ __forceinline__ int channel_bucket_dev(int C) { return C; }
+// Which quadrants of the tile at (x0, y0) the pixel rectangle of d reaches (4 bits).
+__device__ __forceinline__ unsigned quadrant_mask(const TilePix &tp, const DrawRec &d) {
+  const int x0 = (int)tp.x0, y0 = (int)tp.y0;
+  const bool c0 = d.i0 <= x0 + 7 && d.i1 >= x0;
+  const bool c1 = d.i0 <= x0 + 15 && d.i1 >= x0 + 8;
+  const bool r0 = d.j0 <= y0 + 7 && d.j1 >= y0;
+  const bool r1 = d.j0 <= y0 + 15 && d.j1 >= y0 + 8;
+  return (unsigned)(c0 && r0) | ((unsigned)(c1 && r0) << 1) | ((unsigned)(c0 && r1) << 2) |
+         ((unsigned)(c1 && r1) << 3);
+}
+
+// Per-quadrant lists of the staged batch, in batch order: every wave then walks
+// only the entries that reach its quadrant.
+struct QuadLists {
+  unsigned char idx[4][256];
+  int cnt[4];
+  int wcnt[4][4];
+};
+
+// All 256 threads call this with their staged entry's mask (0 if none); it
+// synchronises twice and leaves L ready to read.
+__device__ __forceinline__ void build_quad_lists(QuadLists &L, unsigned mask) {
+  const unsigned tid = threadIdx.x, lane = tid & 63u, sw = tid >> 6;
+  const uint64_t below = lane ? (~0ull >> (64u - lane)) : 0ull;
+  unsigned rank[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint64_t b = __builtin_amdgcn_ballot_w64(((mask >> q) & 1u) != 0u);
+    rank[q] = (unsigned)__popcll(b & below);
+    if (lane == 0) L.wcnt[sw][q] = __popcll(b);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    if ((mask >> q) & 1u) {
+      int off = 0;
+      for (unsigned s2 = 0; s2 < sw; s2++) off += L.wcnt[s2][q];
+      L.idx[q][off + rank[q]] = (unsigned char)tid;
+    }
+  }
+  if (tid < 4) L.cnt[tid] = L.wcnt[0][tid] + L.wcnt[1][tid] + L.wcnt[2][tid] + L.wcnt[3][tid];
+  __syncthreads();
+}
 
 static inline int channel_bucket(int C) {
   if (C <= 1) return 1;
@@ -80,60 +123,76 @@ static inline int channel_bucket(int C) {
 }
 
 // ---------------------------------------------------------------------------
-// Spheres: orthogonal distance from the sphere centre q to the pixel ray d.
-// With a = q / qz and delta = d - a = (sx, sy, 0) (both in normalised image
-// coordinates), |q x d|^2 = qz^2 (sx^2 + sy^2 + (ax sy - ay sx)^2), so
-//   D = 1 - dist^2 / r^2 = 1 - (qz^2 / r^2) * g * s,  g = 1 / |d|^2,
-// with no cancellation between large terms (delta comes straight from the
-// tile-relative pixel offset).
-//
-// This runs in fp64: near a sphere's rim D is a small difference of numbers
-// close to 1, and a dominant sphere's weight is proportional to D there. On
-// CDNA4 an fp64 FMA issues at the same per-lane rate as a non-packed fp32 FMA,
-// so exact geometry costs register space, not issue slots.
+// Spheres: D = 1 - dist^2 / r_eff^2 with dist the orthogonal distance from the
+// sphere centre q to the pixel ray d = (x, y, 1). With a = q / qz and
+// A = qz^2 / r_eff^2,
+//   dist^2 / r_eff^2 = A |a x d|^2 / |d|^2,  so  D = g (|d|^2 - A |a x d|^2),
+// g = 1 / |d|^2. Both |d|^2 and |a x d|^2 are quadratic in the pixel offset
+// (X, Y) from the tile centre, so per (tile, sphere) the staging thread forms
+//   D / g = Q0 + Q1 X + Q2 Y + Q3 X^2 + Q4 X Y + Q5 Y^2
+// and each pixel evaluates it with five fp64 FMAs. fp64 matters: across a tile
+// the terms reach (8 px / r_px)^2 while near the rim their sum is ~D, and a
+// dominant sphere's weight is proportional to D there. On CDNA4 an fp64 FMA
+// issues at the non-packed fp32 rate.
 // ---------------------------------------------------------------------------
 struct SphereRay {
-  double ifx, ify;
-  double dx, dy;     // normalised ray direction (dx, dy, 1)
-  double g;          // 1 / (1 + dx^2 + dy^2)
-  double pxr, pyr;   // tile-relative pixel centre
+  double x, y;       // normalised ray direction (x, y, 1) through the pixel centre
+  double g;          // 1 / (1 + x^2 + y^2)
+  double X, Y;       // pixel centre minus tile centre (pixels)
 };
 
 __device__ __forceinline__ SphereRay sphere_ray(const ViewDev &c, const TilePix &tp) {
   SphereRay r;
-  r.ifx = 1.0 / (double)c.fx;
-  r.ify = 1.0 / (double)c.fy;
-  r.dx = ((double)tp.i + 0.5 - (double)c.cx) * r.ifx;
-  r.dy = ((double)tp.j + 0.5 - (double)c.cy) * r.ify;
-  r.g = 1.0 / (1.0 + r.dx * r.dx + r.dy * r.dy);
-  r.pxr = (double)tp.pxr;
-  r.pyr = (double)tp.pyr;
+  const double ifx = 1.0 / (double)c.fx, ify = 1.0 / (double)c.fy;
+  r.x = ((double)tp.i + 0.5 - (double)c.cx) * ifx;
+  r.y = ((double)tp.j + 0.5 - (double)c.cy) * ify;
+  r.g = 1.0 / (1.0 + r.x * r.x + r.y * r.y);
+  r.X = (double)tp.pxr - 8.0;
+  r.Y = (double)tp.pyr - 8.0;
   return r;
 }
 
-// Staged sphere geometry: tile-relative centre, normalised centre, A.
-struct SphereGeo {
-  double u, v, ax, ay, A;
+struct SphereQuad {
+  double2 q01, q23, q45;
 };
 
-__device__ __forceinline__ SphereGeo sphere_geo(const ViewDev &c, const TilePix &tp, const DrawRec &d) {
-  SphereGeo s;
-  s.u = d.u - (double)tp.x0;
-  s.v = d.v - (double)tp.y0;
-  s.ax = (d.u - (double)c.cx) / (double)c.fx;
-  s.ay = (d.v - (double)c.cy) / (double)c.fy;
-  s.A = d.a;
-  return s;
+// Coefficients of D / g over the tile of tp (d: the sphere's draw record).
+__device__ __forceinline__ SphereQuad sphere_quad(const ViewDev &c, const TilePix &tp, const DrawRec &d) {
+  const double ifx = 1.0 / (double)c.fx, ify = 1.0 / (double)c.fy;
+  const double xc = ((double)tp.x0 + 8.0 - (double)c.cx) * ifx;     // tile-centre ray
+  const double yc = ((double)tp.y0 + 8.0 - (double)c.cy) * ify;
+  const double ax = d.u, ay = d.v, A = d.a;
+  // a x d = alpha + beta X + gamma Y, component by component
+  const double al0 = ay - yc, ga0 = -ify;
+  const double al1 = xc - ax, be1 = ifx;
+  const double al2 = ax * yc - ay * xc, be2 = -ay * ifx, ga2 = ax * ify;
+  SphereQuad q;
+  q.q01.x = (1.0 + xc * xc + yc * yc) - A * (al0 * al0 + al1 * al1 + al2 * al2);
+  q.q01.y = 2.0 * xc * ifx - 2.0 * A * (al1 * be1 + al2 * be2);
+  q.q23.x = 2.0 * yc * ify - 2.0 * A * (al0 * ga0 + al2 * ga2);
+  q.q23.y = ifx * ifx - A * (be1 * be1 + be2 * be2);
+  q.q45.x = -2.0 * A * (be2 * ga2);
+  q.q45.y = ify * ify - A * (ga0 * ga0 + ga2 * ga2);
+  return q;
 }
 
-// Returns D = 1 - dist^2 / r_eff^2; sx, sy receive the normalised offsets.
-__device__ __forceinline__ double sphere_D_ex(const SphereRay &ray, double u, double v, double ax, double ay,
-                                              double A, double &sx, double &sy) {
-  sx = (ray.pxr - u) * ray.ifx;
-  sy = (ray.pyr - v) * ray.ify;
-  const double cr = __builtin_fma(ax, sy, -(ay * sx));
-  const double s = __builtin_fma(sx, sx, __builtin_fma(sy, sy, cr * cr));
-  return __builtin_fma(-(A * ray.g), s, 1.0);
+// D / g at the pixel.
+__device__ __forceinline__ double sphere_num(const SphereRay &r, const double2 q01, const double2 q23,
+                                             const double2 q45) {
+  double t = __builtin_fma(q23.y, r.X, q01.y);
+  t = __builtin_fma(q45.x, r.Y, t);
+  double num = __builtin_fma(r.X, t, q01.x);
+  const double v = __builtin_fma(q45.y, r.Y, q23.x);
+  return __builtin_fma(r.Y, v, num);
+}
+
+// Direct form for the backward: D and the normalised offsets sx = x - ax, sy = y - ay.
+__device__ __forceinline__ double sphere_D_direct(const SphereRay &r, const DrawRec &d, double &sx, double &sy) {
+  sx = r.x - d.u;
+  sy = r.y - d.v;
+  const double cr = d.u * sy - d.v * sx;
+  const double s = sx * sx + sy * sy + cr * cr;
+  return 1.0 - d.a * r.g * s;
 }
 
 // ---------------------------------------------------------------------------

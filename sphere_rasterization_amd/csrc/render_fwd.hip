@@ -21,19 +21,13 @@ namespace {
 // ---------------------------------------------------------------------------
 // Spheres
 // ---------------------------------------------------------------------------
-struct __align__(16) SphereWgt {
-  double A;      // qz^2 / r_eff^2
-  float oe;      // opacity * exp(opacity * zhat / gamma)
-  float bnd;     // weight bound of this and every later sphere
-};
-
 template <int CM>
 __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
-  __shared__ double2 s_uv[256];     // tile-relative centre (pixels)
-  __shared__ double2 s_ax[256];     // normalised centre
-  __shared__ SphereWgt s_w[256];
-  __shared__ int s_id[256];
+  __shared__ double2 s_q01[256], s_q23[256], s_q45[256];   // D / g over the tile
+  __shared__ float2 s_w[256];       // o exp(o zhat / gamma), stop limit bound / tau
   __shared__ float s_f[CM][256];
+  __shared__ QuadLists s_l;
+  __shared__ int s_top[256 * (SPLAT_TOPK_MAX + 1)];        // + one dummy slot per pixel
   if (*A.overflow) return;
   const int gtile = blockIdx.x;
   const int view = view_of_tile(vt, gtile);
@@ -41,61 +35,55 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
   const SphereRay ray = sphere_ray(c, tp);
+  const unsigned wq = threadIdx.x >> 6;                     // this wave's quadrant
   const float tau = A.tau;
   float N = A.bg_weight;
   float S[CM];
 #pragma unroll
   for (int ch = 0; ch < CM; ch++) S[ch] = A.bg_weight * A.bg[ch];
-  int top[SPLAT_TOPK_MAX];
-#pragma unroll
-  for (int k = 0; k < SPLAT_TOPK_MAX; k++) top[k] = -1;
-  int ntop = 0;
   const int K = A.top_k;
-  bool done = !tp.inside;
+  int ntop = 0;
+  int *my_top = s_top + threadIdx.x * (K + 1);
+  bool active = tp.inside;
   const long long vbase = (long long)view * A.n;
 
   for (uint32_t b = start; b < end; b += 256) {
     const uint32_t e = b + threadIdx.x;
+    unsigned mask = 0;
     if (e < end) {
       const uint32_t rid = A.vals[e];
       const DrawRec d = A.draw[rid];
-      const int id = (int)((long long)rid - vbase);
-      const SphereGeo sg = sphere_geo(c, tp, d);
-      s_uv[threadIdx.x] = make_double2(sg.u, sg.v);
-      s_ax[threadIdx.x] = make_double2(sg.ax, sg.ay);
-      SphereWgt w;
-      w.A = sg.A; w.oe = d.w; w.bnd = d.e;
-      s_w[threadIdx.x] = w;
-      s_id[threadIdx.x] = id;
+      const long long id = (long long)rid - vbase;
+      const SphereQuad q = sphere_quad(c, tp, d);
+      s_q01[threadIdx.x] = q.q01;
+      s_q23[threadIdx.x] = q.q23;
+      s_q45[threadIdx.x] = q.q45;
+      // stop when bound < tau N, i.e. N > bound / tau (never when tau = 0)
+      s_w[threadIdx.x] = make_float2(d.w, tau > 0.0f ? d.e / tau : __builtin_huge_valf());
 #pragma unroll
       for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      mask = quadrant_mask(tp, d);
     }
-    __syncthreads();
-    const int cnt = (int)min(256u, end - b);
-    if (!done) {
+    build_quad_lists(s_l, mask);
+    const int cnt = s_l.cnt[wq];
+    if (ballot64(active)) {
       for (int k = 0; k < cnt; k++) {
-        const SphereWgt wg = s_w[k];
-        if (wg.bnd < tau * N) { done = true; break; }       // no later sphere can matter
-        const double2 uv = s_uv[k];
-        const double2 ax = s_ax[k];
-        double sx, sy;
-        const double D = sphere_D_ex(ray, uv.x, uv.y, ax.x, ax.y, wg.A, sx, sy);
-        if (D > 0.0) {
-          const float w = wg.oe * (float)D;
-          N += w;
+        const int idx = s_l.idx[wq][k];
+        const float2 wv = s_w[idx];
+        active = active && !(N > wv.y);            // no later sphere can matter
+        const double num = sphere_num(ray, s_q01[idx], s_q23[idx], s_q45[idx]);
+        const bool hit = active && num > 0.0;
+        const float w = hit ? wv.x * (float)(num * ray.g) : 0.0f;
+        N += w;
 #pragma unroll
-          for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][k], S[ch]);
-          if (ntop < K) {
-            const int id = s_id[k];
-#pragma unroll
-            for (int q = 0; q < SPLAT_TOPK_MAX; q++)
-              if (q == ntop) top[q] = id;
-            ntop++;
-          }
-        }
+        for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][idx], S[ch]);
+        const bool rec = hit && ntop < K;
+        my_top[rec ? ntop : K] = (int)(b + (uint32_t)idx);
+        ntop += rec ? 1 : 0;
+        if ((k & 3) == 3 && ballot64(active) == 0) break;
       }
     }
-    if (__syncthreads_count(!done) == 0) break;
+    if (__syncthreads_count(active) == 0) break;
   }
   if (!tp.inside) return;
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
@@ -107,9 +95,7 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
     if (ch < A.C) img[ch * plane] = S[ch] * inv;
   if (A.norm) A.norm[p] = N;
   if (A.topk)
-#pragma unroll
-    for (int q = 0; q < SPLAT_TOPK_MAX; q++)
-      if (q < K) A.topk[p * K + q] = top[q];
+    for (int q = 0; q < K; q++) A.topk[p * K + q] = q < ntop ? my_top[q] : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -118,10 +104,12 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
 // ---------------------------------------------------------------------------
 template <int CM, bool LIDAR>
 __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
+  constexpr int NF = LIDAR ? 1 : CM;
   __shared__ double2 s_uv[256];     // tile-relative centre
   __shared__ double2 s_ab[256];     // a/2, b
   __shared__ double2 s_co[256];     // c/2, opacity
-  __shared__ float s_f[LIDAR ? 1 : CM][256];   // features, or depth for spherical views
+  __shared__ float s_f[NF][256];    // features, or depth for spherical views
+  __shared__ QuadLists s_l;
   if (*A.overflow) return;
   const int gtile = blockIdx.x;
   const int view = view_of_tile(vt, gtile);
@@ -129,23 +117,23 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
   if ((c.kind == SPLAT_CAM_SPHERICAL) != LIDAR) return;
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
+  const unsigned wq = threadIdx.x >> 6;
   // Transmittance runs in fp64 (same issue rate as fp32 on CDNA4): it is the
   // product of every (1 - alpha) so far and the backward divides it back out.
   double T = 1.0;
-  float S[LIDAR ? 1 : CM];
+  float S[NF];
 #pragma unroll
-  for (int ch = 0; ch < (LIDAR ? 1 : CM); ch++) S[ch] = 0.0f;
-  float dep = 0.0f;
+  for (int ch = 0; ch < NF; ch++) S[ch] = 0.0f;
   uint32_t last = 0;
-  bool done = !tp.inside;
+  bool active = tp.inside;
   const long long vbase = (long long)view * A.n;
   const float amin = A.alpha_min, amax = A.alpha_max;
   const double tmin = (double)A.T_min;
-
   const double pxr = tp.pxr, pyr = tp.pyr;
 
   for (uint32_t b = start; b < end; b += 256) {
     const uint32_t e = b + threadIdx.x;
+    unsigned mask = 0;
     if (e < end) {
       const uint32_t rid = A.vals[e];
       const DrawRec d = A.draw[rid];
@@ -160,35 +148,34 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
 #pragma unroll
         for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
       }
+      mask = quadrant_mask(tp, d);
     }
-    __syncthreads();
-    const int cnt = (int)min(256u, end - b);
-    if (!done) {
+    build_quad_lists(s_l, mask);
+    const int cnt = s_l.cnt[wq];
+    if (ballot64(active)) {
       for (int k = 0; k < cnt; k++) {
+        const int idx = s_l.idx[wq][k];
         float G, og;
         double dx, dy;
-        const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[k], s_ab[k], s_co[k], amax, G, og, dx, dy);
-        if (al < amin) continue;
-        const float w = (float)(T * (double)al);
-        if (LIDAR) {
-          dep = __builtin_fmaf(w, s_f[0][k], dep);
-        } else {
+        const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+        const bool hit = active && al >= amin;
+        const float w = hit ? (float)(T * (double)al) : 0.0f;
 #pragma unroll
-          for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][k], S[ch]);
-        }
-        T = T * (1.0 - (double)al);
-        last = b - start + (uint32_t)k + 1u;
-        if (T < tmin) { done = true; break; }
+        for (int ch = 0; ch < NF; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][idx], S[ch]);
+        T = hit ? T * (1.0 - (double)al) : T;
+        last = hit ? b - start + (uint32_t)idx + 1u : last;
+        active = active && !(T < tmin);            // include, then stop
+        if ((k & 3) == 3 && ballot64(active) == 0) break;
       }
     }
-    if (__syncthreads_count(!done) == 0) break;
+    if (__syncthreads_count(active) == 0) break;
   }
   if (!tp.inside) return;
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
   const size_t plane = (size_t)c.W * c.H;
   float *img = A.img + c.img_off + (size_t)tp.j * c.W + tp.i;
   if (LIDAR) {
-    img[0] = dep;
+    img[0] = S[0];
     img[plane] = (float)(1.0 - T);
   } else {
 #pragma unroll

@@ -52,15 +52,20 @@ struct __align__(16) BinRec {
 // Compositing part, staged into LDS by the render kernels (48 bytes).
 //  Gaussians: projected mean (u, v), conic (a, b, c) with power = (a dx^2 + 2 b dx dy + c dy^2)/2,
 //             w = opacity, e unused.
-//  Spheres:   projected centre (u, v), a = A = qz^2 / r_eff^2, w = o exp(o zhat / gamma),
-//             e = stop bound, b and c unused.
+//  Spheres:   (u, v) = normalised centre (qx/qz, qy/qz), a = A = qz^2 / r_eff^2,
+//             (b, c) = projected centre in pixels, w = o exp(o zhat / gamma), e = stop bound.
 // Positions and the quadratic form stay fp64: an elongated footprint makes the three
 // conic terms cancel by the covariance's condition number, and per-pixel offsets from
 // a far tile need the full mantissa.
+// (i0..i1) x (j0..j1) is the inclusive pixel rectangle outside which the primitive
+// cannot contribute (Gaussians: opacity-aware alpha support; spheres: tangent box);
+// the compositors use it to give each wave of a tile only the entries that reach
+// its quadrant.
 struct __align__(16) DrawRec {
   double u, v;
   double a, b, c;
   float w, e;
+  int i0, i1, j0, j1;
 };
 
 // Backward-only part.

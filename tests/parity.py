@@ -52,8 +52,13 @@ def gpu_pixel_outputs(rz, pix):
     last = _np(rz.last) if rz.last is not None else None
     N = _np(rz.norm) if rz.norm is not None else None
     K = rz.scene.params.top_k
-    top = _np(rz.topk).reshape(-1, K) if rz.topk is not None else None
     view = np.searchsorted(offs, pix, side="right") - 1
+    top = None
+    if rz.topk is not None:
+        # positions in the sorted pair list -> primitive ids
+        pos = _np(rz.topk).reshape(-1, K)[pix].astype(np.int64)
+        vals = _np(rz.vals).view(np.uint32).astype(np.int64)
+        top = np.where(pos >= 0, vals[np.clip(pos, 0, None)] - (view * rz.n)[:, None], -1)
     for v, c in enumerate(cams):
         sel = np.nonzero(view == v)[0]
         lp = pix[sel] - offs[v]
@@ -64,7 +69,7 @@ def gpu_pixel_outputs(rz, pix):
     if T is not None:
         res["T"], res["last"] = T[pix], last[pix]
     if N is not None:
-        res["N"], res["top"] = N[pix], top[pix]
+        res["N"], res["top"] = N[pix], top
     return res
 
 

@@ -138,6 +138,8 @@ def test_forward_deterministic_and_null_grads():
     g1 = rz.backward(dimg, want=("feat", "opacity"))
     g2 = rz.backward(dimg, want=("feat", "opacity"))
     torch.cuda.synchronize()
+    # float atomics make the summation order (not the result) run-dependent
+    from tests.parity import grad_check
     for k in g1:
-        torch.testing.assert_close(g1[k], g2[k], rtol=1e-5, atol=1e-6)
-    torch.testing.assert_close(g1["feat"], grads["feat"], rtol=1e-5, atol=1e-6)
+        grad_check(k, g1[k].cpu().numpy(), g2[k].cpu().numpy())
+    grad_check("feat", grads["feat"].cpu().numpy(), g1["feat"].cpu().numpy())
