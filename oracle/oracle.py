@@ -58,6 +58,7 @@ def lib():
         L.or_render.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.or_render_bruteforce.argtypes = [vp, ip, vp, vp, vp, vp]
         L.or_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.or_backward_mag.argtypes = [vp] * 17
         _lib = L
     return _lib
 
@@ -215,8 +216,13 @@ class Oracle:
                     N=N.reshape(c.height, c.width), top=top[:, :self.K].reshape(c.height, c.width, self.K))
 
     # ---- backward -------------------------------------------------------
-    def backward(self, dimg_views) -> dict:
-        """dimg_views: list of [Cv,H,W] arrays (one per view). Returns float64 grads."""
+    def backward(self, dimg_views, with_mag: bool = False) -> dict:
+        """dimg_views: list of [Cv,H,W] arrays (one per view). Returns float64 grads.
+
+        with_mag adds "mag": for every gradient the sum of the magnitudes of the
+        terms that make it up (a bound for what rounding in the terms can do to
+        the sum; it is not part of the gradient).
+        """
         if self.npairs is None:
             self.bin()
         g = np.ascontiguousarray(np.concatenate([np.asarray(a, np.float32).reshape(-1)
@@ -224,15 +230,23 @@ class Oracle:
         n, Cc = self.n, self.C
         pd = 2 if self.kind == 0 else 3
         sd = 3 if self.kind == 1 else 1
-        dpos = np.zeros((n, pd))
-        dscale = np.zeros((n, sd)) if sd > 1 else np.zeros(n)
-        drot = np.zeros((n, 4)) if self.kind == 1 else None
-        dop = np.zeros(n)
-        dfeat = np.zeros((n, Cc)) if Cc > 0 else None
-        dR = np.zeros((self.V, 3, 3))
-        dt = np.zeros((self.V, 3))
+
+        def outs():
+            return dict(pos=np.zeros((n, pd)), scale=np.zeros((n, sd)) if sd > 1 else np.zeros(n),
+                        rot=np.zeros((n, 4)) if self.kind == 1 else None, opacity=np.zeros(n),
+                        feat=np.zeros((n, Cc)) if Cc > 0 else None, cam_R=np.zeros((self.V, 3, 3)),
+                        cam_t=np.zeros((self.V, 3)))
+
+        o = outs()
         acc = np.zeros((self.V * n, G_OFF + Cc))
-        lib().or_backward(self.h, _vp(g), _vp(dpos), _vp(dscale), _vp(drot), _vp(dop), _vp(dfeat),
-                          _vp(dR), _vp(dt), _vp(acc))
-        return dict(pos=dpos, scale=dscale, rot=drot, opacity=dop, feat=dfeat, cam_R=dR, cam_t=dt,
-                    acc=acc)
+        args = [self.h, _vp(g)] + [_vp(o[k]) for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t")]
+        args.append(_vp(acc))
+        if with_mag:
+            m = outs()
+            lib().or_backward_mag(*args, *[_vp(m[k]) for k in ("pos", "scale", "rot", "opacity", "feat",
+                                                               "cam_R", "cam_t")])
+            o["mag"] = m
+        else:
+            lib().or_backward(*args)
+        o["acc"] = acc
+        return o

@@ -659,8 +659,15 @@ void or_render_bruteforce(const octx *X, int v, double *img, double *T, double *
  * spheres:   [dq0, dq1, dq2, d_reff, d_opac, 0, 0, 0, d_feat...]          */
 #define G_OFF 8
 
-/* Reverse pass of one pixel; loc[list position][NG] accumulates. */
-static void pixel_backward(const octx *X, long long gpix, const double *g, double *loc, int NG,
+/* Reverse pass of one pixel; loc[list position][NG] accumulates.
+ *
+ * mloc (optional, same layout) accumulates a running magnitude of every term:
+ * each factor replaced by its absolute value and each difference a - b by
+ * |a| + |b|. It bounds what rounding can do to the sums (an fp32 evaluation of
+ * a term carries an error relative to the term's magnitude, so a sum of many
+ * terms that cancel is only accurate relative to the sum of magnitudes). It
+ * plays no part in the gradient itself. */
+static void pixel_backward(const octx *X, long long gpix, const double *g, double *loc, double *mloc, int NG,
                            otrace *tr, int tr_cap) {
   int C = X->C;
   opix P;
@@ -674,14 +681,21 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
       const orec *o = &X->rec[r->rec];
       uint32_t id = r->rec % (uint32_t)X->n;
       double *A = loc + (size_t)r->idx * NG;
-      double dw = 0.0;
+      double *M = mloc ? mloc + (size_t)r->idx * NG : NULL;
+      double dw = 0.0, mdw = 0.0;
       for (int ch = 0; ch < C; ch++) {
+        double f = X->feat[(size_t)id * C + ch];
         A[G_OFF + ch] += g[ch] * r->w / N;
-        dw += g[ch] * (X->feat[(size_t)id * C + ch] - P.col[ch]) / N;
+        dw += g[ch] * (f - P.col[ch]) / N;
+        if (M) {
+          M[G_OFF + ch] += fabs(g[ch]) * r->w / N;
+          mdw += fabs(g[ch]) * (fabs(f) + fabs(P.col[ch])) / N;
+        }
       }
       /* w = o * D * exp(o * zhat / gamma) */
       double e = o->e, oo = o->opac;
       A[4] += dw * (r->D * e + r->w * o->zhat / X->gamma);
+      if (M) M[4] += mdw * (r->D * e + r->w * fabs(o->zhat) / X->gamma);
       if (o->gated) continue;                       /* tiny spheres: features and opacity only */
       double dD = dw * oo * e;
       double dzhat = dw * r->w * oo / X->gamma;
@@ -692,6 +706,12 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
       for (int a = 0; a < 3; a++) A[a] += ddist2 * (2.0 * q[a] - 2.0 * qd * r->d[a] / r->dd);
       A[2] += dzhat * (-1.0 / (c->zfar - c->znear));
       if (!o->floored) A[3] += dD * 2.0 * r->dist2 / (r2 * o->r_eff);
+      if (M) {
+        double mD = mdw * oo * e, mz = mdw * r->w * oo / X->gamma, m2 = mD / r2;
+        for (int a = 0; a < 3; a++) M[a] += m2 * (2.0 * fabs(q[a]) + 2.0 * fabs(qd * r->d[a]) / r->dd);
+        M[2] += mz / (c->zfar - c->znear);
+        if (!o->floored) M[3] += mD * 2.0 * r->dist2 / (r2 * o->r_eff);
+      }
     }
     return;
   }
@@ -706,17 +726,26 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
     const orec *o = &X->rec[r->rec];
     uint32_t id = r->rec % (uint32_t)X->n;
     double *A = loc + (size_t)r->idx * NG;
+    double *M = mloc ? mloc + (size_t)r->idx * NG : NULL;
     double a = r->alpha, Tk = r->T_before;
-    double da = 0.0;
+    double da = 0.0, mda = 0.0;
     for (int ch = 0; ch < nC; ch++) {
       double f = X->feat[(size_t)id * C + ch];
       A[G_OFF + ch] += Tk * a * g[ch];
       da += Tk * (f - Sb[ch]) * g[ch];
+      if (M) {
+        M[G_OFF + ch] += Tk * a * fabs(g[ch]);
+        mda += Tk * (fabs(f) + fabs(Sb[ch])) * fabs(g[ch]);
+      }
       Sb[ch] = a * f + (1.0 - a) * Sb[ch];
     }
     if (lidar) {
       A[6] += Tk * a * gD;
       da += Tk * (o->depth - Sd) * gD + Tfin / (1.0 - a) * gA;
+      if (M) {
+        M[6] += Tk * a * fabs(gD);
+        mda += Tk * (fabs(o->depth) + fabs(Sd)) * fabs(gD) + Tfin / (1.0 - a) * fabs(gA);
+      }
       Sd = a * o->depth + (1.0 - a) * Sd;
     }
     if (r->clamped) continue;                      /* alpha = 0.99 constant there */
@@ -728,6 +757,15 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
     A[2] += dpower * 0.5 * dx * dx;
     A[3] += dpower * dx * dy;
     A[4] += dpower * 0.5 * dy * dy;
+    if (M) {
+      double mp = a * mda;
+      M[5] += r->G * mda;
+      M[0] += mp * (fabs(o->ca * dx) + fabs(o->cb * dy));
+      M[1] += mp * (fabs(o->cb * dx) + fabs(o->cc * dy));
+      M[2] += mp * 0.5 * dx * dx;
+      M[3] += mp * fabs(dx * dy);
+      M[4] += mp * 0.5 * dy * dy;
+    }
   }
 }
 
@@ -866,21 +904,45 @@ static void project_backward(const octx *X, long long k, const double *A, double
   for (int a = 0; a < 4; a++) drot[a] += (dqn[a] - qn[a] * dot) / nq;
 }
 
+/* Magnitude through the chain rule: the map from a record's accumulator to the
+ * primitive's parameter gradients is linear, so each accumulator slot j moves
+ * the outputs by column j of that map; the magnitudes add |column j| * M[j]. */
+static void project_backward_mag(const octx *X, long long k, const double *M, double *mpos, double *mscale,
+                                 double *mrot, double *mop) {
+  double e[G_OFF];
+  for (int j = 0; j < G_OFF; j++) {
+    if (M[j] == 0.0) continue;
+    for (int q = 0; q < G_OFF; q++) e[q] = q == j ? 1.0 : 0.0;
+    double tp[3] = {0, 0, 0}, ts[3] = {0, 0, 0}, tr[4] = {0, 0, 0, 0}, to = 0.0;
+    project_backward(X, k, e, tp, ts, tr, &to);
+    for (int a = 0; a < 3; a++) mpos[a] += fabs(tp[a]) * M[j];
+    for (int a = 0; a < 3; a++) mscale[a] += fabs(ts[a]) * M[j];
+    for (int a = 0; a < 4; a++) mrot[a] += fabs(tr[a]) * M[j];
+    *mop += fabs(to) * M[j];
+  }
+}
+
+typedef struct {
+  double *pos, *scale, *rot, *op, *feat, *R, *t;
+} omag;
+
 /* Backward. dimg: concatenated per-view [Cv][H][W] float32 upstream gradients
  * (Cv = C for pinhole views, 2 = (depth, opacity) for spherical views).
  * Outputs are written (not accumulated). acc_out (optional) receives the
- * per-record 2D accumulators [V*n][8+C]. */
-void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
-                 double *dop, double *dfeat, double *dR, double *dt, double *acc_out) {
+ * per-record 2D accumulators [V*n][8+C]. mag (optional) receives the running
+ * magnitudes of every output, in the outputs' layouts. */
+static void backward_core(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
+                          double *dop, double *dfeat, double *dR, double *dt, double *acc_out, const omag *mag) {
   int C = X->C, NG = G_OFF + C;
   long long NV = (long long)X->V * X->n;
   double *acc = (double *)calloc((size_t)NV * NG + 1, sizeof(double));
+  double *macc = mag ? (double *)calloc((size_t)NV * NG + 1, sizeof(double)) : NULL;
   long long ntile = X->total_tiles;
   /* Tiles run in parallel; each accumulates by tile-list position into a private
      buffer, merged into the per-record sums in tile order (deterministic). */
   #pragma omp parallel
   {
-    double *loc = NULL;
+    double *loc = NULL, *mloc = NULL;
     otrace *tr = NULL;
     long long cap = 0;
     #pragma omp for schedule(dynamic, 4) ordered
@@ -890,9 +952,10 @@ void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale,
       const ocam *c = &X->cams[v];
       long long s = X->tile_start[t], e = X->tile_start[t + 1], len = e - s;
       if (len > cap) {
-        free(loc); free(tr);
+        free(loc); free(mloc); free(tr);
         cap = len;
         loc = (double *)malloc(sizeof(double) * (size_t)(cap * NG));
+        mloc = macc ? (double *)malloc(sizeof(double) * (size_t)(cap * NG)) : NULL;
         tr = (otrace *)malloc(sizeof(otrace) * (size_t)cap);
       }
       int lt = (int)(t - c->tile_off);
@@ -903,6 +966,7 @@ void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale,
         gv += (size_t)(X->cams[u].kind == CAM_SPHERICAL ? 2 : C) * X->cams[u].width * X->cams[u].height;
       int any = 0;
       for (long long p = 0; p < len * NG; p++) loc[p] = 0.0;
+      if (mloc) for (long long p = 0; p < len * NG; p++) mloc[p] = 0.0;
       for (int jj = 0; jj < TILE && len > 0; jj++)
         for (int ii = 0; ii < TILE; ii++) {
           int i = tx * TILE + ii, j = ty * TILE + jj;
@@ -915,7 +979,7 @@ void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale,
           }
           if (!nz) continue;
           any = 1;
-          pixel_backward(X, c->pix_off + (long long)j * c->width + i, g, loc, NG, tr, (int)len);
+          pixel_backward(X, c->pix_off + (long long)j * c->width + i, g, loc, mloc, NG, tr, (int)len);
         }
       #pragma omp ordered
       {
@@ -924,10 +988,15 @@ void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale,
             double *B = acc + (size_t)X->pair_id[p] * NG;
             const double *L = loc + (p - s) * NG;
             for (int q = 0; q < NG; q++) B[q] += L[q];
+            if (macc) {
+              double *MB = macc + (size_t)X->pair_id[p] * NG;
+              const double *ML = mloc + (p - s) * NG;
+              for (int q = 0; q < NG; q++) MB[q] += ML[q];
+            }
           }
       }
     }
-    free(loc); free(tr);
+    free(loc); free(mloc); free(tr);
   }
   /* per-primitive chain rule, views summed in order */
   int n = X->n;
@@ -953,6 +1022,20 @@ void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale,
     for (int a = 0; a < sd; a++) dscale[(size_t)i * sd + a] = ls[a];
     if (drot) for (int a = 0; a < 4; a++) drot[(size_t)i * 4 + a] = lr[a];
     dop[i] = lo;
+    if (mag) {
+      double mp[3] = {0, 0, 0}, ms[3] = {0, 0, 0}, mr[4] = {0, 0, 0, 0}, mo = 0.0;
+      for (int v = 0; v < X->V; v++) {
+        long long k = (long long)v * n + i;
+        if (!X->rec[k].valid) continue;
+        const double *M = macc + (size_t)k * NG;
+        project_backward_mag(X, k, M, mp, ms, mr, &mo);
+        if (mag->feat) for (int ch = 0; ch < C; ch++) mag->feat[(size_t)i * C + ch] += M[G_OFF + ch];
+      }
+      for (int a = 0; a < pd; a++) mag->pos[(size_t)i * pd + a] = mp[a];
+      for (int a = 0; a < sd; a++) mag->scale[(size_t)i * sd + a] = ms[a];
+      if (mag->rot) for (int a = 0; a < 4; a++) mag->rot[(size_t)i * 4 + a] = mr[a];
+      mag->op[i] = mo;
+    }
   }
   if (X->kind == PRIM_SPHERE) {
     /* camera: sphere-wise contributions summed over all spheres (Pulsar B.2) */
@@ -965,9 +1048,29 @@ void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale,
         for (int a = 0; a < 3; a++) {
           for (int b = 0; b < 3; b++) dR[9 * v + 3 * a + b] += A[a] * p[b];
           dt[3 * v + a] += A[a];
+          if (mag) {
+            const double *M = macc + (size_t)k * NG;
+            for (int b = 0; b < 3; b++) mag->R[9 * v + 3 * a + b] += M[a] * fabs(p[b]);
+            mag->t[3 * v + a] += M[a];
+          }
         }
       }
   }
   if (acc_out) memcpy(acc_out, acc, sizeof(double) * (size_t)NV * NG);
   free(acc);
+  free(macc);
+}
+
+void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
+                 double *dop, double *dfeat, double *dR, double *dt, double *acc_out) {
+  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, NULL);
+}
+
+/* Same as or_backward, plus the magnitudes (zero-initialised by the caller,
+ * same layouts as the gradients; mfeat and mrot may be NULL when absent). */
+void or_backward_mag(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
+                     double *dop, double *dfeat, double *dR, double *dt, double *acc_out, double *mpos,
+                     double *mscale, double *mrot, double *mop, double *mfeat, double *mR, double *mt) {
+  omag m = {mpos, mscale, mrot, mop, mfeat, mR, mt};
+  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, &m);
 }

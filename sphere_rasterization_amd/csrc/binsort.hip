@@ -19,11 +19,11 @@
 namespace {
 
 constexpr int SCAN_BLOCK = 256;
-constexpr int SCAN_ITEMS = 4;
+constexpr int SCAN_ITEMS = 1;
 constexpr int SCAN_CHUNK = SCAN_BLOCK * SCAN_ITEMS;   // records per scan block
 constexpr int SORT_BLOCK = 256;
-constexpr int SORT_ROUNDS = 16;
-constexpr int SORT_CHUNK = SORT_BLOCK * SORT_ROUNDS;   // pairs per sort block
+constexpr int SORT_ROUNDS = 8;
+constexpr int SORT_CHUNK = SORT_BLOCK * SORT_ROUNDS;   // pairs per sort block (many blocks per CU)
 constexpr int RADIX = 256;
 
 // Block-wide exclusive scan of one uint32 per thread (256 threads); returns the
@@ -68,28 +68,35 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_reduce(const uint32_t *coun
 }
 
 // Single workgroup: exclusive scan of the block sums in place, total and overflow.
+// Each thread owns TOP_ITEMS consecutive sums per round (serial scan in registers).
+constexpr int TOP_ITEMS = 16;
 __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_top(uint32_t *block_sums, int nblocks, long long capacity,
                                                           int64_t *num_pairs, int32_t *overflow, uint32_t *live) {
-  __shared__ unsigned long long s_carry;
-  if (threadIdx.x == 0) s_carry = 0;
-  __syncthreads();
-  for (int base = 0; base < nblocks; base += SCAN_BLOCK) {
-    int k = base + threadIdx.x;
-    uint32_t x = k < nblocks ? block_sums[k] : 0u;
+  unsigned long long carry = 0;
+  for (int base = 0; base < nblocks; base += SCAN_BLOCK * TOP_ITEMS) {
+    const int k0 = base + (int)threadIdx.x * TOP_ITEMS;
+    uint32_t x[TOP_ITEMS];
+    uint32_t s = 0;
+#pragma unroll
+    for (int r = 0; r < TOP_ITEMS; r++) {
+      x[r] = k0 + r < nblocks ? block_sums[k0 + r] : 0u;
+      s += x[r];
+    }
     uint32_t tot;
-    uint32_t ex = block_exclusive_scan(x, &tot);
-    unsigned long long carry = s_carry;
-    if (k < nblocks) block_sums[k] = (uint32_t)(carry + ex);
-    __syncthreads();
-    if (threadIdx.x == 0) s_carry = carry + tot;
-    __syncthreads();
+    uint32_t ex = block_exclusive_scan(s, &tot);
+    uint32_t run = (uint32_t)carry + ex;
+#pragma unroll
+    for (int r = 0; r < TOP_ITEMS; r++) {
+      if (k0 + r < nblocks) block_sums[k0 + r] = run;
+      run += x[r];
+    }
+    carry += tot;
   }
   if (threadIdx.x == 0) {
-    unsigned long long total = s_carry;
-    *num_pairs = (int64_t)total;
-    int of = total > (unsigned long long)capacity ? 1 : 0;
+    *num_pairs = (int64_t)carry;
+    int of = carry > (unsigned long long)capacity ? 1 : 0;
     *overflow = of;
-    *live = of ? 0u : (uint32_t)total;
+    *live = of ? 0u : (uint32_t)carry;
   }
 }
 
@@ -142,21 +149,44 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_hist(const uint64_t *keys,
                                                             const int32_t *overflow, int shift, int nblocks,
                                                             uint32_t *hist) {
   __shared__ uint32_t s_h[RADIX];
-  s_h[threadIdx.x] = 0;
-  __syncthreads();
   uint32_t P = *overflow ? 0u : *live;
   long long base = (long long)blockIdx.x * SORT_CHUNK;
+  if (base >= (long long)P) return;      // past the live pairs: nobody reads this column
+  s_h[threadIdx.x] = 0;
+  __syncthreads();
+  const unsigned lane = threadIdx.x & (WAVE - 1);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
+  uint64_t kr[SORT_ROUNDS];
+#pragma unroll
   for (int r = 0; r < SORT_ROUNDS; r++) {
     long long i = base + r * SORT_BLOCK + threadIdx.x;
-    if (i < (long long)P) atomicAdd(&s_h[(unsigned)(keys[i] >> shift) & (RADIX - 1)], 1u);
+    kr[r] = i < (long long)P ? keys[i] : 0ull;
+  }
+#pragma unroll
+  for (int r = 0; r < SORT_ROUNDS; r++) {
+    // one LDS add per distinct digit of the wave (few distinct values are common)
+    const bool valid = base + r * SORT_BLOCK + threadIdx.x < (long long)P;
+    const unsigned d = (unsigned)(kr[r] >> shift) & (RADIX - 1);
+    uint64_t peers = ballot64(valid);
+#pragma unroll
+    for (int b = 0; b < 8; b++) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t m = ballot64(bit);
+      peers &= bit ? m : ~m;
+    }
+    if (valid && (peers & below) == 0) atomicAdd(&s_h[d], (uint32_t)__popcll(peers));
   }
   __syncthreads();
   hist[(size_t)threadIdx.x * nblocks + blockIdx.x] = s_h[threadIdx.x];
 }
 
 // One workgroup per digit: exclusive scan of its row over the chunks, row total out.
-__global__ __launch_bounds__(SCAN_BLOCK) void k_radix_scan(uint32_t *hist, int nblocks, uint32_t *digit_total) {
+__global__ __launch_bounds__(SCAN_BLOCK) void k_radix_scan(uint32_t *hist, int nblocks, uint32_t *digit_total,
+                                                            const uint32_t *live, const int32_t *overflow) {
   uint32_t *row = hist + (size_t)blockIdx.x * nblocks;
+  const uint32_t P = *overflow ? 0u : *live;
+  const int nlive = (int)((P + SORT_CHUNK - 1) / SORT_CHUNK);
+  nblocks = nlive < nblocks ? nlive : nblocks;
   __shared__ uint32_t s_carry;
   if (threadIdx.x == 0) s_carry = 0;
   __syncthreads();
@@ -199,8 +229,9 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(const uint64_t *ki
   uint32_t dt = digit_total[tid];
   uint32_t tot;
   uint32_t dbase = block_exclusive_scan(dt, &tot);
+  const int nlive = (int)((P + SORT_CHUNK - 1) / SORT_CHUNK);
   uint32_t mine = hist[(size_t)tid * nblocks + blockIdx.x];
-  uint32_t next = (int)blockIdx.x + 1 < nblocks ? hist[(size_t)tid * nblocks + blockIdx.x + 1] : dt;
+  uint32_t next = (int)blockIdx.x + 1 < nlive ? hist[(size_t)tid * nblocks + blockIdx.x + 1] : dt;
   uint32_t lcount = next - mine;
   s_gbase[tid] = dbase + mine;
   s_lstart[tid] = block_exclusive_scan(lcount, &tot);
@@ -210,11 +241,20 @@ __global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(const uint64_t *ki
   __syncthreads();
 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
+  uint64_t keys_r[SORT_ROUNDS];
+  uint32_t vals_r[SORT_ROUNDS];
+#pragma unroll
+  for (int r = 0; r < SORT_ROUNDS; r++) {        // every load in flight before ranking
+    const int idx = r * SORT_BLOCK + (int)tid;
+    keys_r[r] = idx < cnt ? kin[base + idx] : 0ull;
+    vals_r[r] = idx < cnt ? vin[base + idx] : 0u;
+  }
+#pragma unroll
   for (int r = 0; r < SORT_ROUNDS; r++) {
     int idx = r * SORT_BLOCK + (int)tid;
     bool valid = idx < cnt;
-    uint64_t key = valid ? kin[base + idx] : 0ull;
-    uint32_t val = valid ? vin[base + idx] : 0u;
+    uint64_t key = keys_r[r];
+    uint32_t val = vals_r[r];
     unsigned d = (unsigned)(key >> shift) & (RADIX - 1);
     uint64_t peers = ballot64(valid);
 #pragma unroll
@@ -336,7 +376,8 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
     int shift = 8 * p;
     hipLaunchKernelGGL(k_radix_hist, dim3(nsort), dim3(SORT_BLOCK), 0, stream, k_a, ws.live, overflow, shift, nsort,
                        ws.hist);
-    hipLaunchKernelGGL(k_radix_scan, dim3(RADIX), dim3(SCAN_BLOCK), 0, stream, ws.hist, nsort, ws.digit_total);
+    hipLaunchKernelGGL(k_radix_scan, dim3(RADIX), dim3(SCAN_BLOCK), 0, stream, ws.hist, nsort, ws.digit_total, ws.live,
+                       overflow);
     hipLaunchKernelGGL(k_radix_scatter, dim3(nsort), dim3(SORT_BLOCK), 0, stream, k_a, v_a, k_b, v_b, ws.hist,
                        ws.digit_total, ws.live, overflow, shift, nsort);
     SPLAT_LAUNCH_CHECK();

@@ -194,11 +194,11 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         const float x = s_af[0][threadIdx.x];
         if (x != 0.0f) atomicAdd(dg + 6, (double)x);
       } else {
-        float *df = A.accf + (size_t)rid * A.C;
+        double *df = A.accf + (size_t)rid * A.C;
 #pragma unroll
         for (int q = 0; q < CM; q++) {
           const float x = s_af[q][threadIdx.x];
-          if (q < A.C && x != 0.0f) atomicAdd(df + q, x);
+          if (q < A.C && x != 0.0f) atomicAdd(df + q, (double)x);
         }
       }
     }
@@ -355,10 +355,10 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
 #pragma unroll
         for (int q = 0; q < 5; q++)
           if (v[q] != 0.0f) atomicAdd(dg + q, (double)v[q]);
-        float *df = A.accf + (size_t)rid * A.C;
+        double *df = A.accf + (size_t)rid * A.C;
 #pragma unroll
         for (int q = 0; q < CM; q++)
-          if (q < A.C && v[5 + q] != 0.0f) atomicAdd(df + q, v[5 + q]);
+          if (q < A.C && v[5 + q] != 0.0f) atomicAdd(df + q, (double)v[5 + q]);
       }
     }
     __syncthreads();
@@ -373,7 +373,7 @@ struct ProjBwdArgs {
   const float *pos, *scale, *rot;
   const BinRec *bin;
   const double *accg;
-  const float *accf;
+  const double *accf;
   float *gpos, *gscale, *grot, *gop, *gfeat, *gR, *gt;
   int accumulate;
 };
@@ -650,7 +650,7 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   if (ng > 0)
     hipLaunchKernelGGL(k_fill_f64, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, A.accg + r0 * ACC_G, ng);
   if (nf > 0)
-    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, stream, A.accf + r0 * A.C, nf);
+    hipLaunchKernelGGL(k_fill_f64, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, stream, A.accf + r0 * A.C, nf);
   if (!gr->accumulate) {
     if (gr->cam_R) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(256), 0, stream, gr->cam_R, 9ll * vt.n);
     if (gr->cam_t) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(256), 0, stream, gr->cam_t, 3ll * vt.n);

@@ -39,7 +39,7 @@ struct BwdArgs {
   const int32_t *topk;
   const float *dimg;
   double *accg;           // [records][ACC_G]
-  float *accf;            // [records][C]
+  double *accf;           // [records][C]
 };
 
 struct TilePix {

@@ -104,24 +104,27 @@ static inline size_t proj_bytes(long long nrec) {
 //  geometric part, fp64 [records][ACC_G]:
 //    Gaussians: [du, dv, d_ca, d_cb, d_cc, d_opac, d_depth, -]
 //    Spheres:   [dq0, dq1, dq2, d_reff, d_opac, -, -, -]
-//  features, fp32 [records][channels].
+//  features, fp64 [records][channels].
 // The geometric sums feed an ill-conditioned chain (conic -> covariance ->
-// rotation), so they are formed and summed in double precision.
+// rotation), so they are formed and summed in double precision. Both arrays
+// take one global atomic add per (tile, record): a primitive that covers the
+// whole frame receives thousands of per-tile partial sums, too many for a
+// single-precision running sum.
 #define ACC_G 8
 
 struct AccLayout {
   double *g;
-  float *f;
+  double *f;
 };
 
 static inline size_t acc_bytes(long long nrec, int C) {
-  return proj_align(sizeof(double) * ACC_G * (size_t)nrec) + proj_align(sizeof(float) * (size_t)nrec * C);
+  return proj_align(sizeof(double) * ACC_G * (size_t)nrec) + proj_align(sizeof(double) * (size_t)nrec * C);
 }
 
 static inline AccLayout acc_layout(void *base, long long nrec) {
   AccLayout a;
   a.g = (double *)base;
-  a.f = (float *)((char *)base + proj_align(sizeof(double) * ACC_G * (size_t)nrec));
+  a.f = (double *)((char *)base + proj_align(sizeof(double) * ACC_G * (size_t)nrec));
   return a;
 }
 

@@ -123,12 +123,16 @@ class Rasterizer:
                            _ptr(self.last), _ptr(self.norm), _ptr(self.topk), _stream())
 
     def ensure_capacity(self, slack: float = 1.25) -> bool:
-        """Read the pair count (one small device->host copy); grow and re-bin on overflow."""
+        """Read the pair count (one small device->host copy); grow and re-bin on
+        overflow, or shrink a capacity more than twice what is needed."""
         need = int(self.num_pairs.item())
         if need > self.capacity:
             self._alloc_pairs(int(need * slack) + 1024)
             self.bin_sort()
             return True
+        if self.capacity > 2 * (int(need * slack) + 1024):
+            self._alloc_pairs(int(need * slack) + 1024)
+            self.bin_sort()
         return False
 
     def forward(self, check: bool = True):

@@ -1,7 +1,11 @@
 """Element-wise comparison of the HIP path (through the C ABI) with the CPU oracle.
 
-Tolerances: images 1e-4 absolute; gradients |d| <= 1e-3 (|ref| + 1e-2 rms(ref))
-per tensor; integer outputs (pair counts, sorted keys and values, tile ranges,
+Tolerances: images 1e-4 absolute; gradients
+    |d| <= 1e-3 (|ref| + 1e-2 rms(ref)) + 32 u mag,   u = 2^-24,
+where mag is the oracle's sum of the magnitudes of the terms behind each
+gradient: the GPU forms every term in single precision, so a sum of many
+terms that cancel is accurate relative to mag, not to its own value (the extra
+term is negligible wherever mag is close to |ref|); integer outputs (pair counts, sorted keys and values, tile ranges,
 last index, top-K ids) bit-exact. Pixels the oracle flags as sitting within a
 few ulps of a discrete decision (skip threshold, stop rule, clamp, sphere edge)
 are left out of the image comparison and get zero upstream gradient on both
@@ -17,6 +21,7 @@ from oracle import oracle as O
 IMG_ATOL = 1e-4
 GRAD_RTOL = 1e-3
 GRAD_FLOOR = 1e-2
+EPS_SUM = 32.0 * 2.0 ** -24
 
 
 def _np(t):
@@ -133,11 +138,13 @@ def masked_grads(orc, g_views, pix_flags=None):
     return out, float((flags != 0).mean())
 
 
-def grad_check(name, got, ref):
+def grad_check(name, got, ref, mag=None):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     bound = GRAD_RTOL * (np.abs(ref) + GRAD_FLOOR * rms) + 1e-30
+    if mag is not None:
+        bound = bound + EPS_SUM * np.asarray(mag, np.float64).reshape(bound.shape)
     ratio = np.abs(got - ref) / bound
     worst = float(ratio.max()) if ratio.size else 0.0
     if worst > 1.0:
@@ -147,22 +154,28 @@ def grad_check(name, got, ref):
     return worst
 
 
-def compare_backward(rz, orc, ref, g_views, masked=None, names=None):
-    """Run both backward passes on the same (flag-masked) upstream gradient."""
+def compare_backward(rz, orc, ref, g_views, masked=None, names=None, view_groups=None):
+    """Run both backward passes on the same (flag-masked) upstream gradient.
+
+    view_groups: list of (view_begin, view_count) GPU calls accumulating into one
+    set of gradients (default: one call over all views)."""
     if masked is None:
         masked, _ = masked_grads(orc, g_views)
     dimg = torch.from_numpy(np.concatenate([m.reshape(-1) for m in masked])).to(rz.device)
-    grads = rz.backward(dimg)
+    if view_groups is None:
+        grads = rz.backward(dimg)
+    else:
+        grads = None
+        for b, c in view_groups:
+            grads = rz.backward(dimg, view_begin=b, view_count=c, grads=grads, accumulate=grads is not None)
     torch.cuda.synchronize()
-    og = orc.backward(masked)
+    og = orc.backward(masked, with_mag=True)
     names = names or [k for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t") if k in grads]
     worst = 0.0
     per = {}
     for k in names:
         got = _np(grads[k])
         refk = og[k]
-        if k in ("cam_R", "cam_t"):
-            refk = refk.reshape(got.shape)
-        per[k] = grad_check(k, got, refk.reshape(got.shape))
+        per[k] = grad_check(k, got, refk.reshape(got.shape), og["mag"][k])
         worst = max(worst, per[k])
     return dict(worst=worst, per=per)

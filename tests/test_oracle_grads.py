@@ -288,3 +288,51 @@ def test_autograd_xcheck_spheres():
         np.testing.assert_allclose(an[k], ref, rtol=1e-9, atol=1e-11 * np.abs(ref).max(), err_msg=k)
     np.testing.assert_allclose(an["cam_R"][0], Rc.grad.numpy(), rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(an["cam_t"][0], tc.grad.numpy(), rtol=1e-9, atol=1e-12)
+
+
+# ---- term magnitudes (the bound the gradient tolerance uses) ----------------
+
+def _mag_scenes():
+    rng = np.random.default_rng(77)
+    out = []
+    n = 40
+    pos = np.c_[rng.uniform(2, 30, n), rng.uniform(2, 20, n)]
+    out.append(("gauss2d", TS.scene2d(pos, rng.uniform(1, 4, n), rng.uniform(0.2, 0.9, n), rng.uniform(1, 9, n),
+                                      rng.uniform(-1, 1, (n, 3)), W=32, H=24)))
+    m = 60
+    mu = np.c_[rng.uniform(-2, 2, m), rng.uniform(-1.5, 1.5, m), rng.uniform(3, 8, m)]
+    sc = TS.scene3d(mu, rng.uniform(0.1, 0.4, (m, 3)), rng.standard_normal((m, 4)), rng.uniform(0.2, 0.9, m),
+                    rng.uniform(0, 1, (m, 3)), [TS.pinhole(40, 32, 40.0), TS.lidar(64, 16)])
+    out.append(("gauss3d+lidar", sc))
+    out.append(("spheres", TS.random_spheres(rng, 200, 40, 32, 40.0, rmin=0.05, rmax=0.4)))
+    return out
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_magnitudes_bound_and_scale(which):
+    """mag >= |grad| everywhere; mag ignores the sign of dL/dimg and scales with it."""
+    name, sc = _mag_scenes()[which]
+    orc = O.Oracle(sc)
+    g = [np.random.default_rng(5 + v).standard_normal((sc.view_channels(v), c.height, c.width)).astype(np.float32)
+         for v, c in enumerate(sc.cams)]
+    a = orc.backward(g, with_mag=True)
+    b = orc.backward([-x for x in g], with_mag=True)
+    c2 = orc.backward([2 * x for x in g], with_mag=True)
+    for k, m in a["mag"].items():
+        if m is None:
+            continue
+        gk = np.asarray(a[k]).reshape(m.shape)
+        assert np.all(m >= np.abs(gk) * (1 - 1e-12) - 1e-300), (name, k)
+        np.testing.assert_allclose(b["mag"][k], m, rtol=1e-12, atol=0, err_msg=f"{name} {k}")
+        np.testing.assert_allclose(c2["mag"][k], 2 * m, rtol=1e-12, atol=0, err_msg=f"{name} {k}")
+    assert a["mag"]["pos"].max() > 0
+
+
+def test_magnitudes_equal_grads_when_terms_share_a_sign():
+    """With dL/dimg >= 0, every feature term T a g is >= 0, so mag == grad."""
+    name, sc = _mag_scenes()[0]
+    orc = O.Oracle(sc)
+    g = [np.abs(np.random.default_rng(9).standard_normal((sc.view_channels(0), sc.cams[0].height,
+                                                           sc.cams[0].width))).astype(np.float32)]
+    a = orc.backward(g, with_mag=True)
+    np.testing.assert_allclose(a["mag"]["feat"], a["feat"], rtol=1e-12, atol=1e-300)
