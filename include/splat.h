@@ -130,9 +130,10 @@ int splat_project(const splat_camera *cams, int n_views, const splat_prims *prim
                   const splat_params *prm, void *proj, uint32_t *pair_counts, hipStream_t stream);
 
 /* Bin to tiles and depth-sort each tile's list (Pulsar B.1.1 depth sort, B.1.2 16x16 blocks):
- * exclusive scan of pair_counts, emit one (key, value) per overlapped tile with
- * key = (global tile << 32) | fp32 bits of the depth, value = record index (view*n + i),
- * stable LSD radix sort on the key, then per-tile [start, end) ranges.
+ * one (key, value) per overlapped tile with key = (global tile << 32) | fp32 bits of the
+ * depth and value = record index (view*n + i), ordered by (tile, depth bits, record index):
+ * pairs are counted per tile, bucketed by tile, and each tile's segment is sorted by
+ * (depth bits, record index); tile_ranges gives each tile's [start, end).
  * keys/vals: [capacity]; tile_ranges: [total_tiles][2] uint32 (empty tiles: 0, 0).
  * num_pairs (device int64) receives the needed pair count. If it exceeds capacity,
  * *overflow (device int32) is set to 1 and nothing else is written; the render calls

@@ -11,7 +11,7 @@
 
 int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, double alpha_min, void *proj,
                    uint32_t *counts, hipStream_t stream);
-size_t sort_workspace_bytes(long long nrec, long long capacity);
+size_t sort_workspace_bytes(const ViewTable &vt, int n, long long capacity);
 int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t *counts, long long capacity,
                     uint64_t *keys, uint32_t *vals, uint32_t *ranges, int64_t *num_pairs, int32_t *overflow,
                     void *workspace, hipStream_t stream);
@@ -144,7 +144,7 @@ int64_t splat_total_tiles(const splat_camera *cams, int n_views) {
 size_t splat_sort_workspace_bytes(const splat_camera *cams, int n_views, int n, int64_t capacity) {
   ViewTable vt;
   if (build_views(cams, n_views, 1, &vt) != SPLAT_OK || n < 0 || capacity < 0) return 0;
-  return sort_workspace_bytes((long long)n_views * n, capacity);
+  return sort_workspace_bytes(vt, n, capacity);
 }
 
 size_t splat_bwd_workspace_bytes(int n_views, int n, int channels) {
@@ -176,7 +176,7 @@ int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *pro
   CHECK(n == 0 || (proj && pair_counts), SPLAT_ERR_INVALID_ARG, "NULL input");
   CHECK(capacity == 0 || (keys && vals), SPLAT_ERR_INVALID_ARG, "NULL keys / vals");
   CHECK(workspace != nullptr, SPLAT_ERR_INVALID_ARG, "NULL workspace");
-  CHECK(ws_bytes >= sort_workspace_bytes((long long)n_views * n, capacity), SPLAT_ERR_CAPACITY,
+  CHECK(ws_bytes >= sort_workspace_bytes(vt, n, capacity), SPLAT_ERR_CAPACITY,
         "sort workspace too small");
   return launch_bin_sort(vt, n, proj, pair_counts, capacity, keys, vals, tile_ranges, num_pairs, overflow, workspace,
                          stream);

@@ -2,48 +2,68 @@
 //
 // Pulsar appendix B.1.1 sorts spheres by their earliest possible intersection
 // depth so that drawing can stop early; B.1.2 works on 16x16 pixel blocks.
-// Here every (tile, record) overlap becomes one 64-bit key
+// The output is every (tile, record) overlap as a 64-bit key
 //   (global tile << 32) | fp32 bits of the depth
-// (depths are positive, so their bits order like the values), the pairs are
-// emitted in record order and sorted with a stable LSD radix sort, which leaves
-// each tile's list contiguous and ordered by (depth, record index).
+// (depths are positive, so their bits order like the values) with the record
+// index as value, ordered by (tile, depth bits, record index).
 //
-// Pipeline (all on one stream, no host synchronisation):
-//   k_scan_reduce / k_scan_top / k_emit   exclusive scan of pair counts, emit
-//   per 8-bit digit: k_radix_hist, k_radix_scan, k_radix_scatter
-//   k_fill + k_ranges                     per-tile [start, end)
-// The pair count lives on the device; kernels are sized by the capacity and
-// blocks past the live count exit at once.
+// The sort is most-significant-digit first: the tile is a counting-sort digit
+// taken in one pass, then every tile's segment is sorted on its own by the
+// 64-bit word (depth bits << 32) | record index. That word is unique per pair,
+// so the order inside a tile before the segment sort does not matter and the
+// bucketing can use atomic cursors.
+//
+// Pipeline (one stream, no host synchronisation):
+//   k_thist                       each workgroup counts the tiles of a chunk of
+//                                 one view's records in LDS and stores the counts
+//                                 as one row of the view's [chunk][tile] matrix
+//   k_col_sum, k_col_scan,        per tile (column): pair total, and for every
+//   k_col_offsets                 chunk the exclusive prefix over earlier chunks
+//   k_scan_reduce, k_scan_top,    exclusive scan over tiles: tile ranges, the pair
+//   k_tile_ranges                 total, the overflow flag, tile starts
+//   k_tscatter                    each pair's word into its tile's segment, at
+//                                 tile start + chunk prefix + a rank from an LDS
+//                                 atomic
+//   k_seg_sort_small              one workgroup per tile, bitonic sort in LDS
+//                                 (segments up to SEG_SMALL), final keys/values
+//   k_seg_sort_big                longer segments: LSD radix sort by one
+//                                 workgroup over the segment in global memory
+// No global atomics on the counting path: device-wide atomics on a few thousand
+// tile counters serialise. Views with more tiles than LDS_TILES take a fallback
+// (k_tile_count, k_bucket) with global atomic counters and cursors.
 #include "splat_internal.h"
 
 namespace {
 
 constexpr int SCAN_BLOCK = 256;
-constexpr int SCAN_ITEMS = 1;
-constexpr int SCAN_CHUNK = SCAN_BLOCK * SCAN_ITEMS;   // records per scan block
-constexpr int SORT_BLOCK = 256;
-constexpr int SORT_ROUNDS = 8;
-constexpr int SORT_CHUNK = SORT_BLOCK * SORT_ROUNDS;   // pairs per sort block (many blocks per CU)
 constexpr int RADIX = 256;
+constexpr int SEG_SMALL = 2048;     // largest segment sorted in LDS
+constexpr int BIG_ROUNDS = 8;       // items per thread per chunk of the big-segment sort
+constexpr int BIG_CHUNK = SCAN_BLOCK * BIG_ROUNDS;
+constexpr int BIG_GRID = 1024;      // workgroups sharing the big segments
+constexpr int TH_RPT = 8;           // records per thread in the counting passes
+constexpr int TH_CHUNK = 256 * TH_RPT;
+constexpr int LDS_TILES = 16384;    // tiles of one view held as LDS counters (64 KiB)
+constexpr int COL_ROWS = 16;        // matrix rows (chunks) per thread in the column scan
 
-// Block-wide exclusive scan of one uint32 per thread (256 threads); returns the
+// Block-wide exclusive scan of one value per thread (256 threads); returns the
 // exclusive prefix and writes the block total to *total.
-__device__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *total) {
-  __shared__ uint32_t s_w[SCAN_BLOCK / WAVE];
+template <typename T>
+__device__ T block_exclusive_scan(T x, T *total) {
+  __shared__ T s_w[SCAN_BLOCK / WAVE];
   unsigned lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  // wave inclusive scan with shuffles
-  uint32_t inc = x;
+  T inc = x;
 #pragma unroll
   for (int d = 1; d < WAVE; d <<= 1) {
-    uint32_t y = __shfl_up(inc, d, WAVE);
+    T y = __shfl_up(inc, d, WAVE);
     if (lane >= (unsigned)d) inc += y;
   }
   if (lane == WAVE - 1) s_w[w] = inc;
   __syncthreads();
-  uint32_t wbase = 0, tot = 0;
+  T wbase = 0, tot = 0;
 #pragma unroll
   for (int k = 0; k < SCAN_BLOCK / WAVE; k++) {
-    uint32_t t = s_w[k];
+    T t = s_w[k];
     if ((unsigned)k < w) wbase += t;
     tot += t;
   }
@@ -52,39 +72,66 @@ __device__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *total) {
   return wbase + inc - x;
 }
 
-// ---- pair-count scan -------------------------------------------------------
+__global__ void k_fill_u32(uint32_t *p, long long n, uint32_t v) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
 
-__global__ __launch_bounds__(SCAN_BLOCK) void k_scan_reduce(const uint32_t *counts, long long nrec, uint32_t *block_sums) {
-  long long base = (long long)blockIdx.x * SCAN_CHUNK;
-  uint32_t s = 0;
-#pragma unroll
-  for (int r = 0; r < SCAN_ITEMS; r++) {
-    long long k = base + r * SCAN_BLOCK + threadIdx.x;
-    if (k < nrec) s += counts[k];
+// ---- pairs per tile ----------------------------------------------------------
+
+// Visit the global tile ids of one record's rectangle (tile columns wrap on
+// spherical views), row by row.
+template <typename F>
+__device__ __forceinline__ void for_each_tile(const ViewDev &cv, const BinRec &b, F f) {
+#pragma unroll 1
+  for (int ty = b.ty0; ty <= b.ty1; ty++) {
+    int tx = b.tx0;
+#pragma unroll 1
+    for (int a = 0; a < b.ntx; a++) {
+      f((uint32_t)(cv.tile_off + ty * cv.TW + tx));
+      if (++tx == cv.TW) tx = 0;
+    }
   }
-  uint32_t tot;
-  block_exclusive_scan(s, &tot);
+}
+
+__global__ __launch_bounds__(256) void k_tile_count(ViewTable vt, int n, const BinRec *bin, const uint32_t *counts,
+                                                     uint32_t *tile_cnt) {
+  const long long k = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= (long long)vt.n * n || counts[k] == 0) return;
+  const ViewDev &cv = vt.v[(int)(k / n)];
+  for_each_tile(cv, bin[k], [&](uint32_t gt) { atomicAdd(&tile_cnt[gt], 1u); });
+}
+
+// ---- exclusive scan over tiles -------------------------------------------------
+
+// Block totals in 64 bits (a total of 2^32 or more can only mean overflow).
+__global__ __launch_bounds__(SCAN_BLOCK) void k_scan_reduce(const uint32_t *cnt, long long m,
+                                                             unsigned long long *block_sums) {
+  const long long k = (long long)blockIdx.x * SCAN_BLOCK + threadIdx.x;
+  unsigned long long tot;
+  block_exclusive_scan<unsigned long long>(k < m ? cnt[k] : 0u, &tot);
   if (threadIdx.x == 0) block_sums[blockIdx.x] = tot;
 }
 
-// Single workgroup: exclusive scan of the block sums in place, total and overflow.
-// Each thread owns TOP_ITEMS consecutive sums per round (serial scan in registers).
+// Single workgroup: exclusive scan of the block sums in place; pair total,
+// overflow flag, live pair count, and the big-segment counter reset.
+// Each thread owns TOP_ITEMS consecutive sums per round.
 constexpr int TOP_ITEMS = 16;
-__global__ __launch_bounds__(SCAN_BLOCK) void k_scan_top(uint32_t *block_sums, int nblocks, long long capacity,
-                                                          int64_t *num_pairs, int32_t *overflow, uint32_t *live) {
+__global__ __launch_bounds__(SCAN_BLOCK) void k_scan_top(unsigned long long *block_sums, int nblocks,
+                                                          long long capacity, int64_t *num_pairs, int32_t *overflow,
+                                                          uint32_t *live) {
   unsigned long long carry = 0;
   for (int base = 0; base < nblocks; base += SCAN_BLOCK * TOP_ITEMS) {
     const int k0 = base + (int)threadIdx.x * TOP_ITEMS;
-    uint32_t x[TOP_ITEMS];
-    uint32_t s = 0;
+    unsigned long long x[TOP_ITEMS];
+    unsigned long long s = 0;
 #pragma unroll
     for (int r = 0; r < TOP_ITEMS; r++) {
-      x[r] = k0 + r < nblocks ? block_sums[k0 + r] : 0u;
+      x[r] = k0 + r < nblocks ? block_sums[k0 + r] : 0ull;
       s += x[r];
     }
-    uint32_t tot;
-    uint32_t ex = block_exclusive_scan(s, &tot);
-    uint32_t run = (uint32_t)carry + ex;
+    unsigned long long tot;
+    unsigned long long run = carry + block_exclusive_scan<unsigned long long>(s, &tot);
 #pragma unroll
     for (int r = 0; r < TOP_ITEMS; r++) {
       if (k0 + r < nblocks) block_sums[k0 + r] = run;
@@ -94,300 +141,429 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_top(uint32_t *block_sums, i
   }
   if (threadIdx.x == 0) {
     *num_pairs = (int64_t)carry;
-    int of = carry > (unsigned long long)capacity ? 1 : 0;
+    const int of = carry > (unsigned long long)capacity ? 1 : 0;
     *overflow = of;
-    *live = of ? 0u : (uint32_t)carry;
+    live[0] = of ? 0u : (uint32_t)carry;
+    live[1] = 0u;                       // big segments found by k_seg_sort_small
   }
 }
 
-// Re-scan each block's counts with its base offset and write the pairs.
-__global__ __launch_bounds__(SCAN_BLOCK) void k_emit(ViewTable vt, int n, const BinRec *bin, const uint32_t *counts,
-                                                      const uint32_t *block_sums, const int32_t *overflow,
-                                                      uint64_t *keys, uint32_t *vals) {
+// Per tile: [start, end) (0, 0 when empty) and the bucket cursor (in place of the count).
+// Without overflow every prefix is below the capacity (< 2^32).
+__global__ __launch_bounds__(SCAN_BLOCK) void k_tile_ranges(uint32_t *cnt_cursor, long long m,
+                                                             const unsigned long long *block_sums,
+                                                             const int32_t *overflow, uint32_t *ranges) {
   if (*overflow) return;
-  long long nrec = (long long)vt.n * n;
-  long long base = (long long)blockIdx.x * SCAN_CHUNK + (long long)threadIdx.x * SCAN_ITEMS;
-  uint32_t c[SCAN_ITEMS];
+  const long long t = (long long)blockIdx.x * SCAN_BLOCK + threadIdx.x;
+  const uint32_t c = t < m ? cnt_cursor[t] : 0u;
+  uint32_t tot;
+  const uint32_t start = (uint32_t)block_sums[blockIdx.x] + block_exclusive_scan<uint32_t>(c, &tot);
+  if (t < m) {
+    cnt_cursor[t] = start;
+    ranges[2 * t] = c ? start : 0u;
+    ranges[2 * t + 1] = c ? start + c : 0u;
+  }
+}
+
+// ---- bucketing -------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_bucket(ViewTable vt, int n, const BinRec *bin, const uint32_t *counts,
+                                                 const int32_t *overflow, uint32_t *cursor, uint64_t *words) {
+  if (*overflow) return;
+  const long long k = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= (long long)vt.n * n || counts[k] == 0) return;
+  const ViewDev &cv = vt.v[(int)(k / n)];
+  const BinRec b = bin[k];
+  const uint64_t w = ((uint64_t)b.key << 32) | (uint64_t)(uint32_t)k;
+  for_each_tile(cv, b, [&](uint32_t gt) {
+    const uint32_t pos = atomicAdd(&cursor[gt], 1u);
+    words[pos] = w;
+  });
+}
+
+// ---- counting in LDS -------------------------------------------------------------
+
+// Matrix of per-chunk tile counts: view v holds nchunk rows of T_v counters at off[v].
+struct MatTable {
+  long long off[SPLAT_MAX_VIEWS];
+};
+
+__device__ __forceinline__ long long mat_index(const MatTable &mt, const ViewDev &cv, int v, int chunk, int t) {
+  return mt.off[v] + (long long)chunk * (cv.TW * cv.TH) + t;
+}
+
+// Records of one chunk, loaded up front (every thread TH_RPT of them, coalesced).
+struct ChunkRecs {
+  uint32_t cnt[TH_RPT];
+  BinRec b[TH_RPT];
+};
+
+__device__ __forceinline__ void load_chunk(const BinRec *bin, const uint32_t *counts, long long rec0, int nvalid,
+                                           ChunkRecs &cr) {
+#pragma unroll
+  for (int r = 0; r < TH_RPT; r++) {
+    const int j = r * 256 + (int)threadIdx.x;
+    cr.cnt[r] = j < nvalid ? counts[rec0 + j] : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < TH_RPT; r++) {
+    const int j = r * 256 + (int)threadIdx.x;
+    if (cr.cnt[r]) cr.b[r] = bin[rec0 + j];
+  }
+}
+
+// View-local tile ids of one record's rectangle.
+template <typename F>
+__device__ __forceinline__ void for_each_local_tile(const ViewDev &cv, const BinRec &b, F f) {
+#pragma unroll 1
+  for (int ty = b.ty0; ty <= b.ty1; ty++) {
+    int tx = b.tx0;
+#pragma unroll 1
+    for (int a = 0; a < b.ntx; a++) {
+      f((uint32_t)(ty * cv.TW + tx));
+      if (++tx == cv.TW) tx = 0;
+    }
+  }
+}
+
+// grid: n_views * nchunk workgroups; dynamic LDS: 4 * max tiles per view.
+__global__ __launch_bounds__(256) void k_thist(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
+                                                const uint32_t *counts, uint32_t *M) {
+  extern __shared__ uint32_t s_cnt[];
+  const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+  const ViewDev &cv = vt.v[v];
+  const int T = cv.TW * cv.TH;
+  for (int t = threadIdx.x; t < T; t += 256) s_cnt[t] = 0;
+  ChunkRecs cr;
+  const int nvalid = min(TH_CHUNK, n - chunk * TH_CHUNK);
+  load_chunk(bin, counts, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);
+  __syncthreads();
+#pragma unroll 1
+  for (int r = 0; r < TH_RPT; r++)
+    if (cr.cnt[r]) for_each_local_tile(cv, cr.b[r], [&](uint32_t lt) { atomicAdd(&s_cnt[lt], 1u); });
+  __syncthreads();
+  uint32_t *row = M + mat_index(mt, cv, v, chunk, 0);
+  for (int t = threadIdx.x; t < T; t += 256) row[t] = s_cnt[t];
+}
+
+// Column (tile) partial sums over groups of COL_ROWS chunks: S[group][gtile].
+// grid: (ceil(tiles / 256), ngroups).
+__global__ __launch_bounds__(256) void k_col_sum(ViewTable vt, MatTable mt, int nchunk, const uint32_t *M,
+                                                  uint32_t *S) {
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  if (gt >= vt.total_tiles) return;
+  const int v = view_of_tile(vt, gt);
+  const ViewDev &cv = vt.v[v];
+  const int t = gt - cv.tile_off, c0 = blockIdx.y * COL_ROWS;
   uint32_t s = 0;
 #pragma unroll
-  for (int r = 0; r < SCAN_ITEMS; r++) {
-    long long k = base + r;
-    c[r] = k < nrec ? counts[k] : 0u;
-    s += c[r];
+  for (int r = 0; r < COL_ROWS; r++)
+    if (c0 + r < nchunk) s += M[mat_index(mt, cv, v, c0 + r, t)];
+  S[(size_t)blockIdx.y * vt.total_tiles + gt] = s;
+}
+
+// Per tile: exclusive scan of the group sums in place; the tile's pair count out.
+__global__ __launch_bounds__(256) void k_col_scan(int tiles, int ngroups, uint32_t *S, uint32_t *tile_cnt) {
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  if (gt >= tiles) return;
+  uint32_t run = 0;
+#pragma unroll 4
+  for (int g = 0; g < ngroups; g++) {
+    const uint32_t x = S[(size_t)g * tiles + gt];
+    S[(size_t)g * tiles + gt] = run;
+    run += x;
   }
-  uint32_t tot;
-  uint32_t off = block_sums[blockIdx.x] + block_exclusive_scan(s, &tot);
+  tile_cnt[gt] = run;
+}
+
+// Matrix entries become the exclusive prefix over earlier chunks of the same tile.
+__global__ __launch_bounds__(256) void k_col_offsets(ViewTable vt, MatTable mt, int nchunk, const uint32_t *S,
+                                                      uint32_t *M) {
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  if (gt >= vt.total_tiles) return;
+  const int v = view_of_tile(vt, gt);
+  const ViewDev &cv = vt.v[v];
+  const int t = gt - cv.tile_off, c0 = blockIdx.y * COL_ROWS;
+  uint32_t run = S[(size_t)blockIdx.y * vt.total_tiles + gt];
+#pragma unroll
+  for (int r = 0; r < COL_ROWS; r++)
+    if (c0 + r < nchunk) {
+      const long long i = mat_index(mt, cv, v, c0 + r, t);
+      const uint32_t x = M[i];
+      M[i] = run;
+      run += x;
+    }
+}
+
+// Same chunks as k_thist: words to tile start + chunk prefix + LDS rank.
+__global__ __launch_bounds__(256) void k_tscatter(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
+                                                   const uint32_t *counts, const uint32_t *M,
+                                                   const uint32_t *tile_start, const int32_t *overflow,
+                                                   uint64_t *words) {
+  extern __shared__ uint32_t s_base[];
+  if (*overflow) return;
+  const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+  const ViewDev &cv = vt.v[v];
+  const int T = cv.TW * cv.TH;
+  const uint32_t *row = M + mat_index(mt, cv, v, chunk, 0);
+  for (int t = threadIdx.x; t < T; t += 256) s_base[t] = tile_start[cv.tile_off + t] + row[t];
+  ChunkRecs cr;
+  const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
+  load_chunk(bin, counts, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
+  __syncthreads();
 #pragma unroll 1
-  for (int r = 0; r < SCAN_ITEMS; r++) {
-    long long k = base + r;
-    if (c[r] == 0) continue;
-    int view = (int)(k / n);
-    const ViewDev &cv = vt.v[view];
-    BinRec b = bin[k];
-    uint64_t lo = (uint64_t)b.key;
-    uint32_t o = off;
-#pragma unroll 1
-    for (int ty = b.ty0; ty <= b.ty1; ty++) {
-      int tx = b.tx0;
-#pragma unroll 1
-      for (int a = 0; a < b.ntx; a++) {
-        uint64_t gt = (uint64_t)(cv.tile_off + ty * cv.TW + tx);
-        keys[o] = (gt << 32) | lo;
-        vals[o] = (uint32_t)k;
-        o++;
-        if (++tx == cv.TW) tx = 0;
+  for (int r = 0; r < TH_RPT; r++) {
+    if (!cr.cnt[r]) continue;
+    const uint64_t w = ((uint64_t)cr.b[r].key << 32) | (uint64_t)(uint32_t)(rec0 + r * 256 + threadIdx.x);
+    for_each_local_tile(cv, cr.b[r], [&](uint32_t lt) { words[atomicAdd(&s_base[lt], 1u)] = w; });
+  }
+}
+
+// ---- segment sorts ---------------------------------------------------------------
+
+__device__ __forceinline__ void write_pair(uint64_t *keys, uint32_t *vals, uint32_t pos, uint32_t tile, uint64_t w) {
+  keys[pos] = ((uint64_t)tile << 32) | (w >> 32);
+  vals[pos] = (uint32_t)w;
+}
+
+// One workgroup per tile. Segments up to SEG_SMALL: bitonic sort of the words in
+// LDS (padded to a power of two with all-ones words, which sort last), then the
+// final key/value pairs. Longer segments are listed for k_seg_sort_big.
+__global__ __launch_bounds__(256) void k_seg_sort_small(const uint32_t *ranges, const uint64_t *words,
+                                                         const int32_t *overflow, uint64_t *keys, uint32_t *vals,
+                                                         uint32_t *live, uint32_t *big_list) {
+  __shared__ uint64_t s[SEG_SMALL];
+  if (*overflow) return;
+  const uint32_t tile = blockIdx.x;
+  const uint32_t start = ranges[2 * tile], len = ranges[2 * tile + 1] - start;
+  if (len == 0) return;
+  if (len > SEG_SMALL) {
+    if (threadIdx.x == 0) big_list[atomicAdd(&live[1], 1u)] = tile;
+    return;
+  }
+  const unsigned tid = threadIdx.x;
+  uint32_t P = 2;
+  while (P < len) P <<= 1;
+  for (uint32_t i = tid; i < P; i += 256) s[i] = i < len ? words[start + i] : ~0ull;
+  __syncthreads();
+  for (uint32_t k = 2; k <= P; k <<= 1) {
+    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+      for (uint32_t i = tid; i < P / 2; i += 256) {
+        const uint32_t lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const uint32_t hi = lo + j;
+        const uint64_t a = s[lo], b = s[hi];
+        const bool up = (lo & k) == 0;
+        if ((a > b) == up) {
+          s[lo] = b;
+          s[hi] = a;
+        }
       }
+      __syncthreads();
     }
-    off += c[r];
   }
+  for (uint32_t i = tid; i < len; i += 256) write_pair(keys, vals, start + i, tile, s[i]);
 }
 
-// ---- LSD radix sort, one 8-bit digit per pass --------------------------------
-
-// Digit histogram of each chunk, stored digit-major: hist[d * nblocks + block].
-__global__ __launch_bounds__(SORT_BLOCK) void k_radix_hist(const uint64_t *keys, const uint32_t *live,
-                                                            const int32_t *overflow, int shift, int nblocks,
-                                                            uint32_t *hist) {
-  __shared__ uint32_t s_h[RADIX];
-  uint32_t P = *overflow ? 0u : *live;
-  long long base = (long long)blockIdx.x * SORT_CHUNK;
-  if (base >= (long long)P) return;      // past the live pairs: nobody reads this column
-  s_h[threadIdx.x] = 0;
-  __syncthreads();
-  const unsigned lane = threadIdx.x & (WAVE - 1);
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-  uint64_t kr[SORT_ROUNDS];
-#pragma unroll
-  for (int r = 0; r < SORT_ROUNDS; r++) {
-    long long i = base + r * SORT_BLOCK + threadIdx.x;
-    kr[r] = i < (long long)P ? keys[i] : 0ull;
-  }
-#pragma unroll
-  for (int r = 0; r < SORT_ROUNDS; r++) {
-    // one LDS add per distinct digit of the wave (few distinct values are common)
-    const bool valid = base + r * SORT_BLOCK + threadIdx.x < (long long)P;
-    const unsigned d = (unsigned)(kr[r] >> shift) & (RADIX - 1);
-    uint64_t peers = ballot64(valid);
-#pragma unroll
-    for (int b = 0; b < 8; b++) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t m = ballot64(bit);
-      peers &= bit ? m : ~m;
-    }
-    if (valid && (peers & below) == 0) atomicAdd(&s_h[d], (uint32_t)__popcll(peers));
-  }
-  __syncthreads();
-  hist[(size_t)threadIdx.x * nblocks + blockIdx.x] = s_h[threadIdx.x];
-}
-
-// One workgroup per digit: exclusive scan of its row over the chunks, row total out.
-__global__ __launch_bounds__(SCAN_BLOCK) void k_radix_scan(uint32_t *hist, int nblocks, uint32_t *digit_total,
-                                                            const uint32_t *live, const int32_t *overflow) {
-  uint32_t *row = hist + (size_t)blockIdx.x * nblocks;
-  const uint32_t P = *overflow ? 0u : *live;
-  const int nlive = (int)((P + SORT_CHUNK - 1) / SORT_CHUNK);
-  nblocks = nlive < nblocks ? nlive : nblocks;
-  __shared__ uint32_t s_carry;
-  if (threadIdx.x == 0) s_carry = 0;
-  __syncthreads();
-  for (int base = 0; base < nblocks; base += SCAN_BLOCK) {
-    int k = base + threadIdx.x;
-    uint32_t x = k < nblocks ? row[k] : 0u;
-    uint32_t tot;
-    uint32_t ex = block_exclusive_scan(x, &tot);
-    uint32_t carry = s_carry;
-    if (k < nblocks) row[k] = carry + ex;
-    __syncthreads();
-    if (threadIdx.x == 0) s_carry = carry + tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) digit_total[blockIdx.x] = s_carry;
-}
-
-// Stable scatter of one chunk. Ranks inside a wave come from 8 ballots (lanes with
-// equal digits), across waves and rounds from LDS counters; the chunk is reordered
-// by digit in LDS, then each digit's run is written to its global slot.
-__global__ __launch_bounds__(SORT_BLOCK) void k_radix_scatter(const uint64_t *kin, const uint32_t *vin,
-                                                               uint64_t *kout, uint32_t *vout,
-                                                               const uint32_t *hist, const uint32_t *digit_total,
-                                                               const uint32_t *live, const int32_t *overflow,
-                                                               int shift, int nblocks) {
-  __shared__ uint64_t s_key[SORT_CHUNK];
-  __shared__ uint32_t s_val[SORT_CHUNK];
-  __shared__ uint32_t s_gbase[RADIX];   // global output start of digit d for this chunk
-  __shared__ uint32_t s_lstart[RADIX];  // chunk-local start of digit d
-  __shared__ uint32_t s_run[RADIX];     // digit d items placed so far
-  __shared__ uint32_t s_wcnt[SORT_BLOCK / WAVE][RADIX];
+// Segments longer than SEG_SMALL, one workgroup each (grid-stride over the list):
+// stable LSD radix sort of the words, 8 bits per pass, through global memory
+// (ping-pong between the bucket array and the caller's key array). Passes over
+// bytes that are equal in every word of the segment are skipped. Within a pass
+// the segment goes in chunks of BIG_CHUNK; ranks inside a wave come from 8
+// ballots, across waves from LDS counters.
+__global__ __launch_bounds__(256) void k_seg_sort_big(const uint32_t *ranges, uint64_t *words, const int32_t *overflow,
+                                                       uint64_t *keys, uint32_t *vals, const uint32_t *live,
+                                                       const uint32_t *big_list) {
+  __shared__ uint32_t s_hist[RADIX];
+  __shared__ uint32_t s_off[RADIX];
+  __shared__ uint32_t s_wcnt[SCAN_BLOCK / WAVE][RADIX];
+  __shared__ unsigned long long s_and, s_or;
   if (*overflow) return;
-  uint32_t P = *live;
-  long long base = (long long)blockIdx.x * SORT_CHUNK;
-  if (base >= (long long)P) return;
-  int cnt = (int)min((long long)SORT_CHUNK, (long long)P - base);
+  const uint32_t nbig = live[1];
   const unsigned tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-
-  // digit totals -> exclusive digit bases (one digit per thread)
-  uint32_t dt = digit_total[tid];
-  uint32_t tot;
-  uint32_t dbase = block_exclusive_scan(dt, &tot);
-  const int nlive = (int)((P + SORT_CHUNK - 1) / SORT_CHUNK);
-  uint32_t mine = hist[(size_t)tid * nblocks + blockIdx.x];
-  uint32_t next = (int)blockIdx.x + 1 < nlive ? hist[(size_t)tid * nblocks + blockIdx.x + 1] : dt;
-  uint32_t lcount = next - mine;
-  s_gbase[tid] = dbase + mine;
-  s_lstart[tid] = block_exclusive_scan(lcount, &tot);
-  s_run[tid] = 0;
-#pragma unroll
-  for (int k = 0; k < SORT_BLOCK / WAVE; k++) s_wcnt[k][tid] = 0;
-  __syncthreads();
-
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-  uint64_t keys_r[SORT_ROUNDS];
-  uint32_t vals_r[SORT_ROUNDS];
-#pragma unroll
-  for (int r = 0; r < SORT_ROUNDS; r++) {        // every load in flight before ranking
-    const int idx = r * SORT_BLOCK + (int)tid;
-    keys_r[r] = idx < cnt ? kin[base + idx] : 0ull;
-    vals_r[r] = idx < cnt ? vin[base + idx] : 0u;
-  }
-#pragma unroll
-  for (int r = 0; r < SORT_ROUNDS; r++) {
-    int idx = r * SORT_BLOCK + (int)tid;
-    bool valid = idx < cnt;
-    uint64_t key = keys_r[r];
-    uint32_t val = vals_r[r];
-    unsigned d = (unsigned)(key >> shift) & (RADIX - 1);
-    uint64_t peers = ballot64(valid);
-#pragma unroll
-    for (int b = 0; b < 8; b++) {
-      bool bit = (d >> b) & 1u;
-      uint64_t m = ballot64(bit);
-      peers &= bit ? m : ~m;
+  for (uint32_t b = blockIdx.x; b < nbig; b += gridDim.x) {
+    const uint32_t tile = big_list[b];
+    const uint32_t start = ranges[2 * tile], len = ranges[2 * tile + 1] - start;
+    uint64_t *src = words + start, *dst = keys + start;
+    // bytes that vary across the segment
+    uint64_t va = ~0ull, vo = 0ull;
+    for (uint32_t i = tid; i < len; i += 256) {
+      const uint64_t x = src[i];
+      va &= x;
+      vo |= x;
     }
-    unsigned rank = __popcll(peers & below);
-    if (valid && rank == 0) s_wcnt[w][d] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      uint32_t off = s_run[d] + rank;
-      for (unsigned k = 0; k < w; k++) off += s_wcnt[k][d];
-      uint32_t pos = s_lstart[d] + off;
-      s_key[pos] = key;
-      s_val[pos] = val;
+    if (tid == 0) {
+      s_and = ~0ull;
+      s_or = 0ull;
     }
     __syncthreads();
-    uint32_t add = 0;
+    atomicAnd(&s_and, (unsigned long long)va);
+    atomicOr(&s_or, (unsigned long long)vo);
+    __syncthreads();
+    const uint64_t vary = s_and ^ s_or;
+    __syncthreads();
+    for (int shift = 0; shift < 64; shift += 8) {
+      if (((vary >> shift) & 0xffull) == 0) continue;      // uniform over the workgroup
+      s_hist[tid] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < len; i += 256) atomicAdd(&s_hist[(unsigned)(src[i] >> shift) & (RADIX - 1)], 1u);
+      __syncthreads();
+      uint32_t tot;
+      s_off[tid] = block_exclusive_scan<uint32_t>(s_hist[tid], &tot);
 #pragma unroll
-    for (int k = 0; k < SORT_BLOCK / WAVE; k++) {
-      add += s_wcnt[k][tid];
-      s_wcnt[k][tid] = 0;
+      for (int q = 0; q < SCAN_BLOCK / WAVE; q++) s_wcnt[q][tid] = 0;
+      __syncthreads();
+      for (uint32_t base = 0; base < len; base += BIG_CHUNK) {
+        uint64_t x[BIG_ROUNDS];
+#pragma unroll
+        for (int r = 0; r < BIG_ROUNDS; r++) {
+          const uint32_t i = base + r * 256 + tid;
+          x[r] = i < len ? src[i] : 0ull;
+        }
+#pragma unroll
+        for (int r = 0; r < BIG_ROUNDS; r++) {
+          const bool valid = base + r * 256 + tid < len;
+          const unsigned d = (unsigned)(x[r] >> shift) & (RADIX - 1);
+          uint64_t peers = ballot64(valid);
+#pragma unroll
+          for (int bit = 0; bit < 8; bit++) {
+            const bool on = (d >> bit) & 1u;
+            const uint64_t m = ballot64(on);
+            peers &= on ? m : ~m;
+          }
+          const unsigned rank = __popcll(peers & below);
+          if (valid && rank == 0) s_wcnt[w][d] = __popcll(peers);
+          __syncthreads();
+          if (valid) {
+            uint32_t off = s_off[d] + rank;
+            for (unsigned q = 0; q < w; q++) off += s_wcnt[q][d];
+            dst[off] = x[r];
+          }
+          __syncthreads();
+          uint32_t add = 0;
+#pragma unroll
+          for (int q = 0; q < SCAN_BLOCK / WAVE; q++) {
+            add += s_wcnt[q][tid];
+            s_wcnt[q][tid] = 0;
+          }
+          s_off[tid] += add;
+          __syncthreads();
+        }
+      }
+      uint64_t *t = src;
+      src = dst;
+      dst = t;
     }
-    s_run[tid] += add;
+    // src holds the sorted words (in the key array or the bucket array)
+    for (uint32_t i = tid; i < len; i += 256) write_pair(keys, vals, start + i, tile, src[i]);
     __syncthreads();
   }
-  for (int i = (int)tid; i < cnt; i += SORT_BLOCK) {
-    uint64_t key = s_key[i];
-    unsigned d = (unsigned)(key >> shift) & (RADIX - 1);
-    uint32_t g = s_gbase[d] + (uint32_t)i - s_lstart[d];
-    kout[g] = key;
-    vout[g] = s_val[i];
-  }
-}
-
-// ---- tile ranges -------------------------------------------------------------
-
-__global__ void k_fill_u32(uint32_t *p, long long n, uint32_t v) {
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-__global__ __launch_bounds__(256) void k_ranges(const uint64_t *keys, const uint32_t *live, const int32_t *overflow,
-                                                 uint32_t *ranges) {
-  if (*overflow) return;
-  uint32_t P = *live;
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)P) return;
-  uint32_t t = (uint32_t)(keys[i] >> 32);
-  if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != t) ranges[2 * (size_t)t] = (uint32_t)i;
-  if (i == (long long)P - 1 || (uint32_t)(keys[i + 1] >> 32) != t) ranges[2 * (size_t)t + 1] = (uint32_t)(i + 1);
 }
 
 struct SortWs {
-  uint64_t *alt_keys;
-  uint32_t *alt_vals;
-  uint32_t *block_sums;
-  uint32_t *hist;
-  uint32_t *digit_total;
-  uint32_t *live;
+  uint64_t *words;      // [capacity] bucketed (depth << 32 | record) words
+  uint32_t *cursor;     // [tiles] counts, then tile starts (and cursors in the fallback)
+  uint32_t *big_list;   // [tiles] tiles with long segments
+  unsigned long long *block_sums;  // [ceil(tiles / 256) + 1]
+  uint32_t *live;       // [0] live pairs, [1] big segments
+  uint32_t *mat;        // per-chunk tile counts (LDS counting path)
+  uint32_t *colsum;     // [groups][tiles]
   size_t bytes;
 };
 
-SortWs sort_ws_layout(void *base, long long nrec, long long capacity) {
+struct CountPlan {
+  bool lds;             // every view's tiles fit the LDS counters
+  int nchunk, ngroups, max_tiles;
+  long long mat_elems;
+  MatTable mt;
+};
+
+CountPlan count_plan(const ViewTable &vt, int n) {
+  CountPlan cp{};
+  cp.nchunk = (n + TH_CHUNK - 1) / TH_CHUNK;
+  cp.ngroups = (cp.nchunk + COL_ROWS - 1) / COL_ROWS;
+  cp.lds = n > 0;
+  long long off = 0;
+  for (int v = 0; v < vt.n; v++) {
+    const int T = vt.v[v].TW * vt.v[v].TH;
+    cp.max_tiles = T > cp.max_tiles ? T : cp.max_tiles;
+    if (T > LDS_TILES) cp.lds = false;
+    cp.mt.off[v] = off;
+    off += (long long)cp.nchunk * T;
+  }
+  if (cp.ngroups > 65535) cp.lds = false;   // grid.y of the column kernels
+  cp.mat_elems = cp.lds ? off : 0;
+  return cp;
+}
+
+SortWs sort_ws_layout(void *base, const ViewTable &vt, int n, long long capacity) {
   SortWs w;
   char *p = (char *)base;
-  long long nscan = (nrec + SCAN_CHUNK - 1) / SCAN_CHUNK;
-  long long nsort = (capacity + SORT_CHUNK - 1) / SORT_CHUNK;
-  if (nsort < 1) nsort = 1;
-  w.alt_keys = (uint64_t *)p;  p += proj_align(sizeof(uint64_t) * (size_t)capacity);
-  w.alt_vals = (uint32_t *)p;  p += proj_align(sizeof(uint32_t) * (size_t)capacity);
-  w.block_sums = (uint32_t *)p; p += proj_align(sizeof(uint32_t) * (size_t)(nscan + 1));
-  w.hist = (uint32_t *)p;      p += proj_align(sizeof(uint32_t) * (size_t)RADIX * (size_t)nsort);
-  w.digit_total = (uint32_t *)p; p += proj_align(sizeof(uint32_t) * RADIX);
-  w.live = (uint32_t *)p;      p += proj_align(sizeof(uint32_t) * 4);
+  const long long tiles = vt.total_tiles;
+  const long long nscan = (tiles + SCAN_BLOCK - 1) / SCAN_BLOCK;
+  const CountPlan cp = count_plan(vt, n);
+  w.words = (uint64_t *)p;      p += proj_align(sizeof(uint64_t) * (size_t)(capacity > 0 ? capacity : 1));
+  w.cursor = (uint32_t *)p;     p += proj_align(sizeof(uint32_t) * (size_t)tiles);
+  w.big_list = (uint32_t *)p;   p += proj_align(sizeof(uint32_t) * (size_t)tiles);
+  w.block_sums = (unsigned long long *)p; p += proj_align(sizeof(unsigned long long) * (size_t)(nscan + 1));
+  w.live = (uint32_t *)p;       p += proj_align(sizeof(uint32_t) * 4);
+  w.mat = (uint32_t *)p;        p += proj_align(sizeof(uint32_t) * (size_t)cp.mat_elems);
+  w.colsum = (uint32_t *)p;     p += proj_align(sizeof(uint32_t) * (size_t)(cp.lds ? cp.ngroups * tiles : 0));
   w.bytes = (size_t)(p - (char *)base);
   return w;
 }
 
 }  // namespace
 
-size_t sort_workspace_bytes(long long nrec, long long capacity) {
-  return sort_ws_layout(nullptr, nrec, capacity).bytes;
-}
-
-int sort_key_bits(int total_tiles) {
-  int tb = 1;
-  while ((1ll << tb) < (long long)total_tiles) tb++;
-  return 32 + tb;
+size_t sort_workspace_bytes(const ViewTable &vt, int n, long long capacity) {
+  return sort_ws_layout(nullptr, vt, n, capacity).bytes;
 }
 
 int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t *counts, long long capacity,
                     uint64_t *keys, uint32_t *vals, uint32_t *ranges, int64_t *num_pairs, int32_t *overflow,
                     void *workspace, hipStream_t stream) {
-  long long nrec = (long long)vt.n * n;
-  SortWs ws = sort_ws_layout(workspace, nrec, capacity);
+  const long long nrec = (long long)vt.n * n;
+  const long long tiles = vt.total_tiles;
+  SortWs ws = sort_ws_layout(workspace, vt, n, capacity);
+  const CountPlan cp = count_plan(vt, n);
   ProjLayout L = proj_layout(const_cast<void *>(proj), nrec);
-  int nscan = (int)((nrec + SCAN_CHUNK - 1) / SCAN_CHUNK);
-  int nsort = (int)((capacity + SORT_CHUNK - 1) / SORT_CHUNK);
-  if (nsort < 1) nsort = 1;
-  int passes = (sort_key_bits(vt.total_tiles) + 7) / 8;
-  // emit into the buffer that makes the last pass land in the caller's arrays
-  uint64_t *k_a = (passes % 2 == 0) ? keys : ws.alt_keys;
-  uint32_t *v_a = (passes % 2 == 0) ? vals : ws.alt_vals;
-  uint64_t *k_b = (passes % 2 == 0) ? ws.alt_keys : keys;
-  uint32_t *v_b = (passes % 2 == 0) ? ws.alt_vals : vals;
+  const unsigned rec_blocks = (unsigned)((nrec + 255) / 256);
+  const int nscan = (int)((tiles + SCAN_BLOCK - 1) / SCAN_BLOCK);
+  const unsigned tile_blocks = (unsigned)((tiles + 255) / 256);
+  const size_t lds_bytes = sizeof(uint32_t) * (size_t)cp.max_tiles;
 
-  if (nscan > 0)
-    hipLaunchKernelGGL(k_scan_reduce, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, counts, nrec, ws.block_sums);
+  if (cp.lds) {
+    const unsigned grid = (unsigned)(vt.n * cp.nchunk);
+    hipLaunchKernelGGL(k_thist, dim3(grid), dim3(256), lds_bytes, stream, vt, cp.mt, n, cp.nchunk, L.bin, counts,
+                       ws.mat);
+    hipLaunchKernelGGL(k_col_sum, dim3(tile_blocks, cp.ngroups), dim3(256), 0, stream, vt, cp.mt, cp.nchunk, ws.mat,
+                       ws.colsum);
+    hipLaunchKernelGGL(k_col_scan, dim3(tile_blocks), dim3(256), 0, stream, (int)tiles, cp.ngroups, ws.colsum,
+                       ws.cursor);
+    hipLaunchKernelGGL(k_col_offsets, dim3(tile_blocks, cp.ngroups), dim3(256), 0, stream, vt, cp.mt, cp.nchunk,
+                       ws.colsum, ws.mat);
+  } else {
+    hipLaunchKernelGGL(k_fill_u32, dim3(tile_blocks), dim3(256), 0, stream, ws.cursor, tiles, 0u);
+    if (rec_blocks)
+      hipLaunchKernelGGL(k_tile_count, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, ws.cursor);
+  }
+  hipLaunchKernelGGL(k_scan_reduce, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums);
   hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(SCAN_BLOCK), 0, stream, ws.block_sums, nscan, capacity, num_pairs,
                      overflow, ws.live);
-  if (nscan > 0)
-    hipLaunchKernelGGL(k_emit, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, vt, n, L.bin, counts, ws.block_sums,
-                       overflow, k_a, v_a);
-  SPLAT_LAUNCH_CHECK();
-  for (int p = 0; p < passes; p++) {
-    int shift = 8 * p;
-    hipLaunchKernelGGL(k_radix_hist, dim3(nsort), dim3(SORT_BLOCK), 0, stream, k_a, ws.live, overflow, shift, nsort,
-                       ws.hist);
-    hipLaunchKernelGGL(k_radix_scan, dim3(RADIX), dim3(SCAN_BLOCK), 0, stream, ws.hist, nsort, ws.digit_total, ws.live,
-                       overflow);
-    hipLaunchKernelGGL(k_radix_scatter, dim3(nsort), dim3(SORT_BLOCK), 0, stream, k_a, v_a, k_b, v_b, ws.hist,
-                       ws.digit_total, ws.live, overflow, shift, nsort);
-    SPLAT_LAUNCH_CHECK();
-    uint64_t *tk = k_a; k_a = k_b; k_b = tk;
-    uint32_t *tv = v_a; v_a = v_b; v_b = tv;
-  }
-  long long nr = 2ll * vt.total_tiles;
-  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, stream, ranges, nr, 0u);
-  hipLaunchKernelGGL(k_ranges, dim3((unsigned)((capacity + 255) / 256)), dim3(256), 0, stream, keys, ws.live,
+  hipLaunchKernelGGL(k_tile_ranges, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums,
                      overflow, ranges);
+  SPLAT_LAUNCH_CHECK();
+  if (cp.lds) {
+    hipLaunchKernelGGL(k_tscatter, dim3((unsigned)(vt.n * cp.nchunk)), dim3(256), lds_bytes, stream, vt, cp.mt, n,
+                       cp.nchunk, L.bin, counts, ws.mat, ws.cursor, overflow, ws.words);
+  } else if (rec_blocks) {
+    hipLaunchKernelGGL(k_bucket, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, overflow, ws.cursor,
+                       ws.words);
+  }
+  hipLaunchKernelGGL(k_seg_sort_small, dim3((unsigned)tiles), dim3(256), 0, stream, ranges, ws.words, overflow, keys,
+                     vals, ws.live, ws.big_list);
+  hipLaunchKernelGGL(k_seg_sort_big, dim3((unsigned)(tiles < BIG_GRID ? tiles : BIG_GRID)), dim3(256), 0, stream,
+                     ranges, ws.words, overflow, keys, vals, ws.live, ws.big_list);
   SPLAT_LAUNCH_CHECK();
   return SPLAT_OK;
 }

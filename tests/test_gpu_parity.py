@@ -58,6 +58,18 @@ def test_ragged_gauss3d():
     _run(sc, 8, "gauss3d 30k @500x300 ragged")
 
 
+def test_long_tile_lists():
+    """Thousands of pairs per tile: the segments take the long-segment sort."""
+    sc = S.gauss3d(seed=15, n=400_000, width=128, height=96)
+    _run(sc, 9, "gauss3d 400k @128x96 long tile lists")
+
+
+def test_view_beyond_lds_counters():
+    """A view with more tiles than the LDS counters hold takes the global-counter binning."""
+    sc = S.gauss3d(seed=16, n=20_000, width=2304, height=2048)
+    _run(sc, 10, "gauss3d 20k @2304x2048 (18432 tiles)")
+
+
 def test_multiview_with_lidar():
     """Two pinhole views and a spherical view in one call; camera and lidar backward
     run as separate calls that accumulate into the same gradients."""
