@@ -33,6 +33,23 @@ HBM_PEAK_GBS = 8000.0
 # per list entry a pixel examines before it stops, and per contributing sphere.
 OPS_PER_ENTRY = 15
 OPS_PER_HIT_BASE = 5          # + one fma per channel
+# HBM bytes (read + written) per launch of the forward sphere compositor on this
+# workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
+# a plain copy of known size; they hold for the sources with this digest only.
+FWD_TRAFFIC_BYTES = 252952245
+FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
+                       "sphere_rasterization_amd/csrc/render_common.h",
+                       "sphere_rasterization_amd/csrc/splat_internal.h")
+FWD_TRAFFIC_SHA256 = "be139fb4bf9092e486fedd85c1818dfc8884729a7d48e04648f375b17a4a8a5c"
+# Algorithmic HBM bytes of the projection and binning stages:
+#   projection: per primitive read position, radius, opacity (20 B), write the
+#     bin, draw and aux records and the pair count (16 + 64 + 32 + 4 B)
+#   binning: per record the bin record and pair count twice (counting and
+#     scatter passes, 40 B); per pair the bucketed word written and read (16 B)
+#     and the sorted key and value written (12 B)
+PROJECT_BYTES_PER_PRIM = 20 + 16 + 64 + 32 + 4
+BIN_BYTES_PER_REC = 40
+BIN_BYTES_PER_PAIR = 28
 
 
 def parse():
@@ -43,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=1024,
                     help="image rows the CPU oracle renders (fwd + bwd) for the baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run three plain device copies of this many MiB (read + write of a "
+                         "known size, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -97,6 +117,14 @@ def main():
     t1 = time.perf_counter()
     assert int(rz.overflow.item()) == 0
     ms = (t1 - t0) * 1e3 / args.steps
+    if args.copy_calibration_mib > 0:
+        nf = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(nf, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)     # reads and writes nf * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
     stages = ["project", "bin_sort", "render_fwd", "render_bwd"]
     st_ms = {s: float(np.median([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
              for i, s in enumerate(stages)}
@@ -119,7 +147,28 @@ def main():
         cpu = cpu_baseline(scene, g_np, args.cpu_sample_rows)
         out["cpu_baseline"] = cpu["json"]
     out["roofline"] = roofline(st_ms, cpu, scene)
+    out["stage_hbm"] = stage_hbm(st_ms, scene.n, npairs)
     print(json.dumps(out), flush=True)
+
+
+def sources_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stage_hbm(st_ms, n, npairs):
+    """Projection and binning against the HBM peak, from their algorithmic bytes."""
+    out = {}
+    for name, nbytes in (("project", PROJECT_BYTES_PER_PRIM * n),
+                         ("bin_sort", BIN_BYTES_PER_REC * n + BIN_BYTES_PER_PAIR * npairs)):
+        gbs = nbytes / (st_ms[name] / 1e3) / 1e9
+        out[name] = {"bytes": nbytes, "GB/s": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def cpu_baseline(scene, g_np, rows):
@@ -155,14 +204,15 @@ def roofline(st_ms, cpu, scene):
     """Forward compositor against the single-issue VALU peak, from the oracle's
     exact count of list entries examined and contributions made per pixel."""
     fwd_ms = st_ms["render_fwd"]
+    traffic = FWD_TRAFFIC_BYTES if sources_digest(FWD_TRAFFIC_SOURCES) == FWD_TRAFFIC_SHA256 else None
     if cpu is None or cpu["rows"] != cpu["H"]:
         return {"bound": "alu", "kernel": "k_fwd_sphere", "achieved": None, "peak": round(VALU_PEAK_TOPS, 2),
-                "unit": "Tops/s", "frac": None, "traffic": None}
+                "unit": "Tops/s", "frac": None, "traffic": traffic}
     ops = cpu["processed"] * OPS_PER_ENTRY + cpu["hits"] * (OPS_PER_HIT_BASE + scene.channels)
     achieved = ops / (fwd_ms / 1e3) / 1e12
     return {"bound": "alu", "kernel": "k_fwd_sphere", "achieved": round(achieved, 3),
             "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s", "frac": round(achieved / VALU_PEAK_TOPS, 4),
-            "traffic": None, "ops_per_launch": ops}
+            "traffic": traffic, "ops_per_launch": ops}
 
 
 if __name__ == "__main__":

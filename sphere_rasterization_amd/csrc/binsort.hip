@@ -24,8 +24,9 @@
 //   k_tscatter                    each pair's word into its tile's segment, at
 //                                 tile start + chunk prefix + a rank from an LDS
 //                                 atomic
-//   k_seg_sort_small              one workgroup per tile, bitonic sort in LDS
-//                                 (segments up to SEG_SMALL), final keys/values
+//   k_seg_sort_small              one workgroup per tile, bitonic sort in
+//                                 registers, lane shuffles and LDS (segments up
+//                                 to SEG_SMALL), final keys/values
 //   k_seg_sort_big                longer segments: LSD radix sort by one
 //                                 workgroup over the segment in global memory
 // No global atomics on the counting path: device-wide atomics on a few thousand
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(256) void k_thist(ViewTable vt, MatTable mt, int n,
   const int nvalid = min(TH_CHUNK, n - chunk * TH_CHUNK);
   load_chunk(bin, counts, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);
   __syncthreads();
-#pragma unroll 1
+#pragma unroll      // constant indices keep the record arrays in registers
   for (int r = 0; r < TH_RPT; r++)
     if (cr.cnt[r]) for_each_local_tile(cv, cr.b[r], [&](uint32_t lt) { atomicAdd(&s_cnt[lt], 1u); });
   __syncthreads();
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(256) void k_tscatter(ViewTable vt, MatTable mt, int
   const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
   load_chunk(bin, counts, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
   __syncthreads();
-#pragma unroll 1
+#pragma unroll      // constant indices keep the record arrays in registers
   for (int r = 0; r < TH_RPT; r++) {
     if (!cr.cnt[r]) continue;
     const uint64_t w = ((uint64_t)cr.b[r].key << 32) | (uint64_t)(uint32_t)(rec0 + r * 256 + threadIdx.x);
@@ -326,8 +327,79 @@ __device__ __forceinline__ void write_pair(uint64_t *keys, uint32_t *vals, uint3
   vals[pos] = (uint32_t)w;
 }
 
-// One workgroup per tile. Segments up to SEG_SMALL: bitonic sort of the words in
-// LDS (padded to a power of two with all-ones words, which sort last), then the
+// Compare-exchange of register elements a and a|J of one thread (J < E).
+template <int J, int E>
+__device__ __forceinline__ void cx_local(uint64_t (&e)[E], uint32_t base, uint32_t k) {
+#pragma unroll
+  for (int a = 0; a < E; a++) {
+    if (a & J) continue;
+    const int b = a | J;
+    const bool up = ((base + a) & k) == 0;
+    const bool lt = e[a] < e[b];
+    const uint64_t lo = lt ? e[a] : e[b], hi = lt ? e[b] : e[a];
+    e[a] = up ? lo : hi;
+    e[b] = up ? hi : lo;
+  }
+}
+
+// Bitonic sort of P = 2^m words held E per thread (thread t holds t*E .. t*E+E-1).
+// A stage (k, j) pairs element x with x ^ j: inside the thread when j < E, with
+// lane t ^ (j/E) of the same wave by a lane shuffle when j < 64 E, through LDS
+// otherwise (at most three such stages). Element x keeps the smaller word when
+// it is the lower of its pair in an ascending block or the upper in a
+// descending one; for j >= E that choice is the same for all of a thread's
+// elements. Words are distinct (padding aside), so one compare decides.
+template <int E>
+__device__ void bitonic_block(uint64_t (&e)[E], uint32_t P, uint64_t *s) {
+  const uint32_t base = threadIdx.x * E;
+  for (uint32_t k = 2; k <= P; k <<= 1) {
+    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+      if (j >= (uint32_t)E) {
+        const bool keep_min = ((base & j) == 0) == ((base & k) == 0);
+        if (j >= 64u * E) {
+          __syncthreads();
+#pragma unroll
+          for (int a = 0; a < E; a++) s[base + a] = e[a];
+          __syncthreads();
+#pragma unroll
+          for (int a = 0; a < E; a++) {
+            const uint64_t o = s[(base + a) ^ j];
+            e[a] = ((o < e[a]) == keep_min) ? o : e[a];
+          }
+        } else {
+          const int m = (int)(j / E);
+#pragma unroll
+          for (int a = 0; a < E; a++) {
+            const uint64_t o = __shfl_xor(e[a], m, WAVE);
+            e[a] = ((o < e[a]) == keep_min) ? o : e[a];
+          }
+        }
+      } else if (j == 4) {
+        if constexpr (E > 4) cx_local<4, E>(e, base, k);
+      } else if (j == 2) {
+        if constexpr (E > 2) cx_local<2, E>(e, base, k);
+      } else {
+        cx_local<1, E>(e, base, k);
+      }
+    }
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void sort_small(const uint64_t *words, uint64_t *keys, uint32_t *vals, uint32_t start,
+                                           uint32_t len, uint32_t P, uint32_t tile, uint64_t *s) {
+  const uint32_t base = threadIdx.x * E;
+  uint64_t e[E];
+#pragma unroll
+  for (int a = 0; a < E; a++) e[a] = base + a < len ? words[start + base + a] : ~0ull;
+  bitonic_block<E>(e, P, s);
+#pragma unroll
+  for (int a = 0; a < E; a++)
+    if (base + a < len) write_pair(keys, vals, start + base + a, tile, e[a]);
+}
+
+// One workgroup per tile. Segments up to SEG_SMALL: bitonic sort of the words
+// (padded to a power of two with all-ones words, which sort last), then the
 // final key/value pairs. Longer segments are listed for k_seg_sort_big.
 __global__ __launch_bounds__(256) void k_seg_sort_small(const uint32_t *ranges, const uint64_t *words,
                                                          const int32_t *overflow, uint64_t *keys, uint32_t *vals,
@@ -341,27 +413,14 @@ __global__ __launch_bounds__(256) void k_seg_sort_small(const uint32_t *ranges, 
     if (threadIdx.x == 0) big_list[atomicAdd(&live[1], 1u)] = tile;
     return;
   }
-  const unsigned tid = threadIdx.x;
   uint32_t P = 2;
   while (P < len) P <<= 1;
-  for (uint32_t i = tid; i < P; i += 256) s[i] = i < len ? words[start + i] : ~0ull;
-  __syncthreads();
-  for (uint32_t k = 2; k <= P; k <<= 1) {
-    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
-      for (uint32_t i = tid; i < P / 2; i += 256) {
-        const uint32_t lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const uint32_t hi = lo + j;
-        const uint64_t a = s[lo], b = s[hi];
-        const bool up = (lo & k) == 0;
-        if ((a > b) == up) {
-          s[lo] = b;
-          s[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (uint32_t i = tid; i < len; i += 256) write_pair(keys, vals, start + i, tile, s[i]);
+  if (P <= 512)
+    sort_small<2>(words, keys, vals, start, len, P, tile, s);
+  else if (P == 1024)
+    sort_small<4>(words, keys, vals, start, len, P, tile, s);
+  else
+    sort_small<8>(words, keys, vals, start, len, P, tile, s);
 }
 
 // Segments longer than SEG_SMALL, one workgroup each (grid-stride over the list):
