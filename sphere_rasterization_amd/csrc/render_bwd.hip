@@ -30,6 +30,31 @@ __device__ __forceinline__ float row_sum_to_last(float x) {
   return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Eight values per lane summed over the wave, transposed: every lane l ends with
+// the total of v[l & 7]. Each exchange step halves the values a lane carries
+// (partner lanes keep opposite halves): the row half-mirror pairs lanes that
+// differ in bit 2 of the lane id, the quad permutes pair bits 1 and 0; what
+// is left is one value per lane, summed over the remaining lane bits 3..5.
+__device__ __forceinline__ float wave_sum8_transposed(const float (&v)[8]) {
+  const unsigned lane = lane_id();
+  const bool b2 = lane & 4u, b1 = lane & 2u, b0 = lane & 1u;
+  float a[4], c[2];
+#pragma unroll
+  for (int j = 0; j < 4; j++) a[j] = (b2 ? v[j + 4] : v[j]) + dpp_f32<0x141>(b2 ? v[j] : v[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; j++) c[j] = (b1 ? a[j + 2] : a[j]) + dpp_f32<0x4E>(b1 ? a[j] : a[j + 2]);
+  float e = (b0 ? c[1] : c[0]) + dpp_f32<0xB1>(b0 ? c[0] : c[1]);
+  e += dpp_f32<0x128>(e);                         // row rotate by 8: lane ^ 8
+  e += __shfl_xor(e, 16, WAVE);
+  e += __shfl_xor(e, 32, WAVE);
+  return e;
+}
+
 __global__ void k_fill_f32(float *p, long long n) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -209,18 +234,22 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
 // ---------------------------------------------------------------------------
 // Sphere backward over the first top_k contributing spheres of each pixel.
 // The forward recorded each one as its index in the sorted pair list, i.e. a
-// position in this tile's list. The tile list is walked front to back in staged
-// batches up to the last recorded position; each wave takes the entries that
-// reach its quadrant, and a lane contributes when the entry is the next of its
-// recorded spheres. Contributions are row-reduced (DPP) into an LDS slot per
-// entry, and each touched entry leaves the tile with one atomic per value.
+// position in this tile's list. The tile list is staged in batches up to the
+// deepest recorded position of the tile; each wave walks the entries that reach
+// its quadrant, and a lane contributes when the entry is the next of its
+// recorded spheres. The wave's contributions to an entry are summed with a
+// transposed reduction (one value per 8-lane group), so one lane per value adds
+// to the entry's LDS slot; each touched entry leaves the tile with one global
+// atomic per value.
 // ---------------------------------------------------------------------------
 template <int CM>
 __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int tile_begin) {
   constexpr int NV = 5 + CM;                  // dq0, dq1, dq2, d_reff, d_opac, d_feat...
+  constexpr int NG = (NV + 7) / 8;            // groups of eight for the reduction
   __shared__ double2 s_a[256];                // normalised centre (ax, ay)
-  __shared__ double2 s_Aw[256];               // A, (oe, flags) packed
-  __shared__ float4 s_x[256];                 // qz, r_eff, opacity, zhat
+  __shared__ double2 s_Ai[256];               // A, 1 / r_eff
+  __shared__ float4 s_x[256];                 // qz, oe, 1/o + zhat/gamma, o/gamma
+  __shared__ int s_flags[256];
   __shared__ float s_f[CM][256];
   __shared__ uint32_t s_rid[256];
   __shared__ float s_acc[NV][256];
@@ -235,7 +264,8 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
   const uint32_t start = A.ranges[2 * gtile];
   const uint32_t len = A.ranges[2 * gtile + 1] - start;
   const SphereRay ray = sphere_ray(c, tp);
-  const unsigned lane = lane_id(), wq = threadIdx.x >> 6;
+  const unsigned lane = lane_id();
+  const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
   const size_t plane = (size_t)c.W * c.H;
   const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
@@ -266,7 +296,7 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
   int nxt = 0;
   uint32_t tgt = ntop ? my_top[0] : 0xffffffffu;
   const double inv_span = 1.0 / ((double)c.zfar - (double)c.znear);
-  const double igam = 1.0 / (double)A.gamma;
+  const float igam = 1.0f / A.gamma;
   const long long vbase = (long long)view * A.n;
 
   for (uint32_t b = 0; b < npos; b += 256) {
@@ -279,9 +309,9 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
       const long long id = (long long)rid - vbase;
       s_rid[threadIdx.x] = rid;
       s_a[threadIdx.x] = make_double2(d.u, d.v);
-      s_Aw[threadIdx.x] = make_double2(d.a, __builtin_bit_cast(double, ((unsigned long long)__float_as_uint(ax.flags) << 32) |
-                                                                           (unsigned long long)__float_as_uint(d.w)));
-      s_x[threadIdx.x] = make_float4(ax.z, ax.w, ax.opac, ax.zhat);
+      s_Ai[threadIdx.x] = make_double2(d.a, 1.0 / (double)ax.w);
+      s_x[threadIdx.x] = make_float4(ax.z, d.w, 1.0f / ax.opac + ax.zhat * igam, ax.opac * igam);
+      s_flags[threadIdx.x] = (int)ax.flags;
 #pragma unroll
       for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
 #pragma unroll
@@ -289,24 +319,23 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
-    const int lc = s_l.cnt[wq];
+    const int lc = __builtin_amdgcn_readfirstlane(s_l.cnt[wq]);
     for (int k = 0; k < lc; k++) {
-      const int idx = s_l.idx[wq][k];
+      const int idx = __builtin_amdgcn_readfirstlane((int)s_l.idx[wq][k]);
       const bool mine = tgt == b + (uint32_t)idx;
       if (ballot64(mine) == 0) continue;
-      float v[NV];
+      float v[NG * 8];
 #pragma unroll
-      for (int q = 0; q < NV; q++) v[q] = 0.0f;
+      for (int q = 0; q < NG * 8; q++) v[q] = 0.0f;
       if (mine) {
-        const double2 aa = s_a[idx], Aw = s_Aw[idx];
+        const double2 aa = s_a[idx], Ai = s_Ai[idx];
         const float4 x = s_x[idx];
-        const unsigned long long bits = __builtin_bit_cast(unsigned long long, Aw.y);
-        const float oe = __uint_as_float((unsigned)bits);
-        const int flags = (int)__uint_as_float((unsigned)(bits >> 32));
+        const int flags = s_flags[idx];
+        const float oe = x.y;
         // D = 1 - A g |a x d|^2 with a x d from the offsets sx = x - ax, sy = y - ay
         const double sx = ray.x - aa.x, sy = ray.y - aa.y;
         const double cr = aa.x * sy - aa.y * sx;
-        const double Dd = 1.0 - Aw.x * ray.g * (sx * sx + sy * sy + cr * cr);
+        const double Dd = 1.0 - Ai.x * ray.g * (sx * sx + sy * sy + cr * cr);
         const float w = oe * (float)Dd;
         float dw = 0.0f;
 #pragma unroll
@@ -315,29 +344,29 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
           dw = __builtin_fmaf(g[ch], s_f[ch][idx] - Cimg[ch], dw);
         }
         dw *= invN;
-        const float o = x.z;
-        v[4] = dw * w * (1.0f / o + x.w * (float)igam);
+        v[4] = dw * w * x.z;
         if (!(flags & 2)) {
           // dist^2 = |q|^2 - (q.d)^2 / |d|^2 has gradient 2 q_perp, with
           // q_perp = qz ((d.delta) g d - delta), delta = (sx, sy, 0).
           const double dD = (double)dw * (double)oe;
-          const double dz = (double)dw * (double)w * (double)o * igam;
-          const double reff = x.y;
-          const double dd2 = -dD / (reff * reff);
+          const double dz = (double)dw * (double)w * (double)x.w;
+          const double dd2 = -dD * Ai.y * Ai.y;
           const double c1 = (ray.x * sx + ray.y * sy) * ray.g;
           const double k2 = 2.0 * dd2 * (double)x.x;
           v[0] = (float)(k2 * (c1 * ray.x - sx));
           v[1] = (float)(k2 * (c1 * ray.y - sy));
           v[2] = (float)(k2 * c1 - dz * inv_span);
-          if (!(flags & 1)) v[3] = (float)(dD * 2.0 * (1.0 - Dd) / reff);
+          if (!(flags & 1)) v[3] = (float)(dD * 2.0 * (1.0 - Dd) * Ai.y);
         }
         nxt++;
         tgt = nxt < ntop ? my_top[nxt] : 0xffffffffu;
       }
 #pragma unroll
-      for (int q = 0; q < NV; q++) {
-        const float r = row_sum_to_last(v[q]);
-        if ((lane & 15u) == 15u && r != 0.0f) atomicAdd(&s_acc[q][idx], r);
+      for (int gq = 0; gq < NG; gq++) {
+        const float (&vg)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * gq]);
+        const float r = wave_sum8_transposed(vg);
+        const int q = 8 * gq + (int)lane;
+        if (lane < 8u && q < NV && r != 0.0f) atomicAdd(&s_acc[q][idx], r);
       }
     }
     __syncthreads();

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   __shared__ float2 s_w[256];       // o exp(o zhat / gamma), stop limit bound / tau
   __shared__ float s_f[CM][256];
   __shared__ QuadLists s_l;
-  __shared__ int s_top[256 * (SPLAT_TOPK_MAX + 1)];        // + one dummy slot per pixel
+  __shared__ int s_top[256 * SPLAT_TOPK_MAX];
   if (*A.overflow) return;
   const int gtile = blockIdx.x;
   const int view = view_of_tile(vt, gtile);
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
   const SphereRay ray = sphere_ray(c, tp);
-  const unsigned wq = threadIdx.x >> 6;                     // this wave's quadrant
+  const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // this wave's quadrant
   const float tau = A.tau;
   float N = A.bg_weight;
   float S[CM];
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   for (int ch = 0; ch < CM; ch++) S[ch] = A.bg_weight * A.bg[ch];
   const int K = A.top_k;
   int ntop = 0;
-  int *my_top = s_top + threadIdx.x * (K + 1);
+  int *my_top = s_top + threadIdx.x * K;
   bool active = tp.inside;
   const long long vbase = (long long)view * A.n;
 
@@ -65,22 +65,31 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
-    const int cnt = s_l.cnt[wq];
+    // the list, its length and every index are the same for the whole wave
+    const int cnt = __builtin_amdgcn_readfirstlane(s_l.cnt[wq]);
     if (ballot64(active)) {
-      for (int k = 0; k < cnt; k++) {
-        const int idx = s_l.idx[wq][k];
-        const float2 wv = s_w[idx];
-        active = active && !(N > wv.y);            // no later sphere can matter
-        const double num = sphere_num(ray, s_q01[idx], s_q23[idx], s_q45[idx]);
-        const bool hit = active && num > 0.0;
-        const float w = hit ? wv.x * (float)(num * ray.g) : 0.0f;
-        N += w;
+      for (int k = 0; k < cnt; k += 4) {
+        const uint32_t four =
+            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(&s_l.idx[wq][k]));
 #pragma unroll
-        for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][idx], S[ch]);
-        const bool rec = hit && ntop < K;
-        my_top[rec ? ntop : K] = (int)(b + (uint32_t)idx);
-        ntop += rec ? 1 : 0;
-        if ((k & 3) == 3 && ballot64(active) == 0) break;
+        for (int u = 0; u < 4; u++) {
+          if (k + u >= cnt) break;
+          const int idx = (int)((four >> (8 * u)) & 0xffu);
+          const float2 wv = s_w[idx];
+          active = active && !(N > wv.y);          // no later sphere can matter
+          const double num = sphere_num(ray, s_q01[idx], s_q23[idx], s_q45[idx]);
+          const bool hit = active && num > 0.0;
+          const float w = hit ? wv.x * (float)(num * ray.g) : 0.0f;
+          N += w;
+#pragma unroll
+          for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][idx], S[ch]);
+          const bool rec = hit && ntop < K;
+          if (ballot64(rec)) {                     // most entries record nothing
+            if (rec) my_top[ntop] = (int)(b + (uint32_t)idx);
+            ntop += rec ? 1 : 0;
+          }
+        }
+        if (ballot64(active) == 0) break;
       }
     }
     if (__syncthreads_count(active) == 0) break;
