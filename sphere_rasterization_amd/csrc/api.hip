@@ -236,9 +236,10 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   A.draw = L.draw; A.aux = L.aux; A.vals = vals; A.ranges = tile_ranges; A.overflow = overflow;
   A.feat = prims->feat; A.img = img; A.T_final = T_final; A.last = last; A.norm = norm; A.topk = topk;
   A.dimg = dL_dimg;
-  AccLayout acc = acc_layout(workspace, (long long)n_views * prims->n);
+  AccLayout acc = acc_layout(workspace, (long long)n_views * prims->n, prims->channels);
   A.accg = acc.g;
   A.accf = acc.f;
+  A.cam_part = acc.cam;
   return launch_render_bwd(vt, view_begin, view_begin + view_count, A, prims, L.bin, grads, stream);
 }
 

@@ -55,15 +55,24 @@ __device__ __forceinline__ float wave_sum8_transposed(const float (&v)[8]) {
   return e;
 }
 
-__global__ void k_fill_f32(float *p, long long n) {
+// Up to two fp64 and two fp32 ranges cleared by one launch.
+struct ZeroRanges {
+  double *d0, *d1;
+  float *f0, *f1;
+  long long nd0, nd1, nf0, nf1;
+};
+
+__global__ __launch_bounds__(256) void k_zero(ZeroRanges z) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
+  if (i < z.nd0) { z.d0[i] = 0.0; return; }
+  i -= z.nd0;
+  if (i < z.nd1) { z.d1[i] = 0.0; return; }
+  i -= z.nd1;
+  if (i < z.nf0) { z.f0[i] = 0.0f; return; }
+  i -= z.nf0;
+  if (i < z.nf1) z.f1[i] = 0.0f;
 }
 
-__global__ void k_fill_f64(double *p, long long n) {
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0;
-}
 
 // ---------------------------------------------------------------------------
 // Alpha blending backward: replay each pixel's list back to front from `last`,
@@ -379,15 +388,11 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
         any |= v[q] != 0.0f;
       }
       if (any) {
-        const uint32_t rid = s_rid[threadIdx.x];
-        double *dg = A.accg + (size_t)rid * ACC_G;
+        // one fp64 row per record: dq0, dq1, dq2, d_reff, d_opac, d_feat...
+        double *row = A.accg + (size_t)s_rid[threadIdx.x] * (5 + A.C);
 #pragma unroll
-        for (int q = 0; q < 5; q++)
-          if (v[q] != 0.0f) atomicAdd(dg + q, (double)v[q]);
-        double *df = A.accf + (size_t)rid * A.C;
-#pragma unroll
-        for (int q = 0; q < CM; q++)
-          if (q < A.C && v[5 + q] != 0.0f) atomicAdd(df + q, (double)v[5 + q]);
+        for (int q = 0; q < NV; q++)
+          if ((q < 5 || q - 5 < A.C) && v[q] != 0.0f) atomicAdd(row + q, (double)v[q]);
       }
     }
     __syncthreads();
@@ -403,6 +408,7 @@ struct ProjBwdArgs {
   const BinRec *bin;
   const double *accg;
   const double *accf;
+  double *cam_part;
   float *gpos, *gscale, *grot, *gop, *gfeat, *gR, *gt;
   int accumulate;
 };
@@ -414,47 +420,101 @@ __device__ __forceinline__ void put(float *p, size_t i, double x, int accumulate
 
 __device__ __forceinline__ bool rec_live(const BinRec &b) { return b.ntx != 0; }
 
-__global__ __launch_bounds__(256) void k_proj_bwd_sphere(ViewTable vt, ProjBwdArgs P, int vbeg, int vend) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= P.n) return;
-  double dp[3] = {0, 0, 0}, dr = 0, dop = 0;
-  for (int v = vbeg; v < vend; v++) {
-    const long long rec = (long long)v * P.n + i;
-    if (!rec_live(P.bin[rec])) continue;
-    const ViewDev &c = vt.v[v];
-    const double *A = P.accg + (size_t)rec * ACC_G;
-    const double dq[3] = {A[0], A[1], A[2]};
-#pragma unroll
-    for (int a = 0; a < 3; a++)
-      dp[a] += (double)c.R[a] * dq[0] + (double)c.R[3 + a] * dq[1] + (double)c.R[6 + a] * dq[2];   // R^T dq
-    dr += A[3];
-    dop += A[4];
-  }
-  if (P.gpos)
-    for (int a = 0; a < 3; a++) put(P.gpos, 3 * (size_t)i + a, dp[a], P.accumulate);
-  if (P.gscale) put(P.gscale, i, dr, P.accumulate);
-  if (P.gop) put(P.gop, i, dop, P.accumulate);
-  if (P.gfeat)
-    for (int ch = 0; ch < P.C; ch++) {
-      double s = 0;
-      for (int v = vbeg; v < vend; v++) s += P.accf[((size_t)v * P.n + i) * P.C + ch];
-      put(P.gfeat, (size_t)i * P.C + ch, s, P.accumulate);
-    }
-}
-
-// Camera gradient (Pulsar B.2): dL/dR = sum_k dq_k p_k^T, dL/dt = sum_k dq_k over all
-// spheres of view vbeg + blockIdx.y. Grid-stride over spheres with fp64 partial sums
-// in registers, a block reduction, then twelve atomics per block.
-__global__ __launch_bounds__(256) void k_cam_grad_sphere(ProjBwdArgs P, int vbeg) {
+// Spheres, one fp64 accumulator row of 5 + C values per record. Grid-stride over
+// spheres: the chain rule sums R^T dq, d_reff, d_opac and the features over the
+// views; when the call covers one view, the same pass forms that view's camera
+// gradient (Pulsar B.2: dL/dR = sum_k dq_k p_k^T, dL/dt = sum_k dq_k) in fp64
+// registers. Each block stores its twelve sums and k_cam_final adds them up in
+// block order (deterministic, and no atomics contend on twelve outputs; a
+// device-scope fence per block would write back the L2 of every XCD).
+__global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs P, int vbeg, int vend, int cam_view) {
   __shared__ double s_red[12][4];
-  const int v = vbeg + blockIdx.y;
+  const int S = 5 + P.C;
   double cam[12];
 #pragma unroll
   for (int q = 0; q < 12; q++) cam[q] = 0.0;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < P.n; i += gridDim.x * blockDim.x) {
-    const long long rec = (long long)v * P.n + i;
-    const double *A = P.accg + (size_t)rec * ACC_G;
-    const double dq[3] = {A[0], A[1], A[2]};      // zero for culled records
+    double dp[3] = {0, 0, 0}, dr = 0, dop = 0;
+    for (int v = vbeg; v < vend; v++) {
+      const ViewDev &c = vt.v[v];
+      const double *A = P.accg + ((size_t)v * P.n + i) * S;     // zero for culled records
+      const double dq[3] = {A[0], A[1], A[2]};
+#pragma unroll
+      for (int a = 0; a < 3; a++)
+        dp[a] += (double)c.R[a] * dq[0] + (double)c.R[3 + a] * dq[1] + (double)c.R[6 + a] * dq[2];   // R^T dq
+      dr += A[3];
+      dop += A[4];
+      if (v == cam_view) {
+        const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
+#pragma unroll
+        for (int a = 0; a < 3; a++) {
+#pragma unroll
+          for (int b = 0; b < 3; b++) cam[3 * a + b] = __builtin_fma(dq[a], pp[b], cam[3 * a + b]);
+          cam[9 + a] += dq[a];
+        }
+      }
+    }
+    if (P.gpos)
+      for (int a = 0; a < 3; a++) put(P.gpos, 3 * (size_t)i + a, dp[a], P.accumulate);
+    if (P.gscale) put(P.gscale, i, dr, P.accumulate);
+    if (P.gop) put(P.gop, i, dop, P.accumulate);
+    if (P.gfeat)
+      for (int ch = 0; ch < P.C; ch++) {
+        double f = 0;
+        for (int v = vbeg; v < vend; v++) f += P.accg[((size_t)v * P.n + i) * S + 5 + ch];
+        put(P.gfeat, (size_t)i * P.C + ch, f, P.accumulate);
+      }
+  }
+  if (cam_view < 0) return;
+  const unsigned lane = lane_id(), w = threadIdx.x / WAVE;
+#pragma unroll
+  for (int q = 0; q < 12; q++) {
+    const double t = wave_sum_f64(cam[q]);
+    if (lane == 0) s_red[q][w] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < 12) {
+    const int q = threadIdx.x;
+    P.cam_part[12 * blockIdx.x + q] = s_red[q][0] + s_red[q][1] + s_red[q][2] + s_red[q][3];
+  }
+}
+
+// One block: the per-block camera sums of k_sphere_grads, added in block order.
+__global__ __launch_bounds__(256) void k_cam_final(ProjBwdArgs P, int nparts, int cam_view) {
+  __shared__ double s_red[12][4];
+  double cam[12];
+#pragma unroll
+  for (int q = 0; q < 12; q++) cam[q] = 0.0;
+  for (int b = threadIdx.x; b < nparts; b += blockDim.x)
+#pragma unroll
+    for (int q = 0; q < 12; q++) cam[q] += P.cam_part[12 * b + q];
+  const unsigned lane = lane_id(), w = threadIdx.x / WAVE;
+#pragma unroll
+  for (int q = 0; q < 12; q++) {
+    const double t = wave_sum_f64(cam[q]);
+    if (lane == 0) s_red[q][w] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < 12) {
+    const int q = threadIdx.x;
+    const double t = s_red[q][0] + s_red[q][1] + s_red[q][2] + s_red[q][3];
+    if (q < 9 && P.gR) P.gR[9 * cam_view + q] += (float)t;
+    if (q >= 9 && P.gt) P.gt[3 * cam_view + (q - 9)] += (float)t;
+  }
+}
+
+// Camera gradient of view vbeg + blockIdx.y when one call covers several views
+// (same sums as above, one view per grid row).
+__global__ __launch_bounds__(256) void k_cam_grad_sphere(ProjBwdArgs P, int vbeg) {
+  __shared__ double s_red[12][4];
+  const int v = vbeg + blockIdx.y;
+  const int S = 5 + P.C;
+  double cam[12];
+#pragma unroll
+  for (int q = 0; q < 12; q++) cam[q] = 0.0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < P.n; i += gridDim.x * blockDim.x) {
+    const double *A = P.accg + ((size_t)v * P.n + i) * S;
+    const double dq[3] = {A[0], A[1], A[2]};
     const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
 #pragma unroll
     for (int a = 0; a < 3; a++) {
@@ -673,17 +733,29 @@ size_t bwd_workspace_bytes(long long nrec, int C) { return acc_bytes(nrec, C); }
 
 int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, const BinRec *bin,
                       const splat_grads *gr, hipStream_t stream) {
-  // accumulator rows of the requested views only
+  // accumulator rows of the requested views only (spheres: one row of 5 + C
+  // values per record; Gaussians: ACC_G geometric values and C features)
+  const bool sph = pr->kind == SPLAT_PRIM_SPHERE;
   const long long r0 = (long long)vbeg * A.n, r1 = (long long)vend * A.n;
-  const long long ng = (r1 - r0) * ACC_G, nf = (r1 - r0) * A.C;
-  if (ng > 0)
-    hipLaunchKernelGGL(k_fill_f64, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, A.accg + r0 * ACC_G, ng);
-  if (nf > 0)
-    hipLaunchKernelGGL(k_fill_f64, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, stream, A.accf + r0 * A.C, nf);
-  if (!gr->accumulate) {
-    if (gr->cam_R) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(256), 0, stream, gr->cam_R, 9ll * vt.n);
-    if (gr->cam_t) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(256), 0, stream, gr->cam_t, 3ll * vt.n);
+  ZeroRanges z{};
+  if (sph) {
+    z.d0 = A.accg + r0 * (5 + A.C);
+    z.nd0 = (r1 - r0) * (5 + A.C);
+  } else {
+    z.d0 = A.accg + r0 * ACC_G;
+    z.nd0 = (r1 - r0) * ACC_G;
+    z.d1 = A.accf + r0 * A.C;
+    z.nd1 = (r1 - r0) * A.C;
   }
+  if (!gr->accumulate) {
+    z.f0 = gr->cam_R;
+    z.nf0 = gr->cam_R ? 9ll * vt.n : 0;
+    z.f1 = gr->cam_t;
+    z.nf1 = gr->cam_t ? 3ll * vt.n : 0;
+  }
+
+  const long long nz = z.nd0 + z.nd1 + z.nf0 + z.nf1;
+  if (nz > 0) hipLaunchKernelGGL(k_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, z);
   SPLAT_LAUNCH_CHECK();
   const int tile_begin = vt.v[vbeg].tile_off;
   const int tile_end = vend < vt.n ? vt.v[vend].tile_off : vt.total_tiles;
@@ -709,18 +781,21 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   ProjBwdArgs P;
   P.kind = pr->kind; P.n = pr->n; P.C = A.C;
   P.pos = pr->pos; P.scale = pr->scale; P.rot = pr->rot;
-  P.bin = bin; P.accg = A.accg; P.accf = A.accf;
+  P.bin = bin; P.accg = A.accg; P.accf = A.accf; P.cam_part = A.cam_part;
   P.gpos = gr->pos; P.gscale = gr->scale; P.grot = gr->rot; P.gop = gr->opacity; P.gfeat = gr->feat;
   P.gR = gr->cam_R; P.gt = gr->cam_t;
   P.accumulate = gr->accumulate;
   if (pr->n > 0) {
     dim3 grid((pr->n + 255) / 256);
-    if (pr->kind == SPLAT_PRIM_SPHERE) {
-      hipLaunchKernelGGL(k_proj_bwd_sphere, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
-      if (gr->cam_R || gr->cam_t) {
-        const unsigned nb = (unsigned)min((pr->n + 255) / 256, 512);
-        hipLaunchKernelGGL(k_cam_grad_sphere, dim3(nb, vend - vbeg), dim3(256), 0, stream, P, vbeg);
-      }
+    if (sph) {
+      // a bounded grid keeps the camera atomics few; one view: camera in the same pass
+      const bool cam = gr->cam_R || gr->cam_t;
+      const unsigned nb = (unsigned)min((pr->n + 255) / 256, SPLAT_CAM_BLOCKS);
+      const int cam_view = cam && vend - vbeg == 1 ? vbeg : -1;
+      hipLaunchKernelGGL(k_sphere_grads, dim3(nb), dim3(256), 0, stream, vt, P, vbeg, vend, cam_view);
+      if (cam_view >= 0) hipLaunchKernelGGL(k_cam_final, dim3(1), dim3(256), 0, stream, P, (int)nb, cam_view);
+      if (cam && vend - vbeg > 1)
+        hipLaunchKernelGGL(k_cam_grad_sphere, dim3(min(nb, 512u), vend - vbeg), dim3(256), 0, stream, P, vbeg);
     }
     else hipLaunchKernelGGL(k_proj_bwd_gauss, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
     SPLAT_LAUNCH_CHECK();

@@ -38,8 +38,9 @@ struct BwdArgs {
   const float *norm;
   const int32_t *topk;
   const float *dimg;
-  double *accg;           // [records][ACC_G]
-  double *accf;           // [records][C]
+  double *accg;           // Gaussians: [records][ACC_G]; spheres: [records][5 + C] (all values)
+  double *accf;           // Gaussians: [records][C]; unused for spheres
+  double *cam_part;       // [SPLAT_CAM_BLOCKS][12] per-block camera sums (spheres)
 };
 
 struct TilePix {

@@ -100,31 +100,40 @@ static inline size_t proj_bytes(long long nrec) {
          proj_align(sizeof(AuxRec) * (size_t)nrec);
 }
 
-// Per-record gradient accumulators, two arrays in the backward workspace:
-//  geometric part, fp64 [records][ACC_G]:
-//    Gaussians: [du, dv, d_ca, d_cb, d_cc, d_opac, d_depth, -]
-//    Spheres:   [dq0, dq1, dq2, d_reff, d_opac, -, -, -]
-//  features, fp64 [records][channels].
+// Per-record gradient accumulators in the backward workspace, fp64:
+//  Gaussians, two arrays: [records][ACC_G] = [du, dv, d_ca, d_cb, d_cc, d_opac,
+//    d_depth, -] and [records][channels] features;
+//  spheres, one array: [records][5 + channels] = [dq0, dq1, dq2, d_reff, d_opac,
+//    d_feat...] (one row of 64 bytes at three channels).
 // The geometric sums feed an ill-conditioned chain (conic -> covariance ->
-// rotation), so they are formed and summed in double precision. Both arrays
-// take one global atomic add per (tile, record): a primitive that covers the
+// rotation), so they are formed and summed in double precision. Every value
+// takes one global atomic add per (tile, record): a primitive that covers the
 // whole frame receives thousands of per-tile partial sums, too many for a
-// single-precision running sum.
+// single-precision running sum. The workspace is sized for the Gaussian layout,
+// which is the larger.
 #define ACC_G 8
+
+// After the accumulators: per-block camera partial sums of the sphere gradient
+// pass ([SPLAT_CAM_BLOCKS][12] fp64).
+#define SPLAT_CAM_BLOCKS 4096
 
 struct AccLayout {
   double *g;
   double *f;
+  double *cam;
 };
 
 static inline size_t acc_bytes(long long nrec, int C) {
-  return proj_align(sizeof(double) * ACC_G * (size_t)nrec) + proj_align(sizeof(double) * (size_t)nrec * C);
+  return proj_align(sizeof(double) * ACC_G * (size_t)nrec) + proj_align(sizeof(double) * (size_t)nrec * C) +
+         proj_align(sizeof(double) * 12 * SPLAT_CAM_BLOCKS);
 }
 
-static inline AccLayout acc_layout(void *base, long long nrec) {
+static inline AccLayout acc_layout(void *base, long long nrec, int C) {
   AccLayout a;
-  a.g = (double *)base;
-  a.f = (double *)((char *)base + proj_align(sizeof(double) * ACC_G * (size_t)nrec));
+  char *p = (char *)base;
+  a.g = (double *)p;    p += proj_align(sizeof(double) * ACC_G * (size_t)nrec);
+  a.f = (double *)p;    p += proj_align(sizeof(double) * (size_t)nrec * C);
+  a.cam = (double *)p;
   return a;
 }
 

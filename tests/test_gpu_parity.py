@@ -99,6 +99,27 @@ def test_multiview_with_lidar():
         _log(f"  {k} worst={w:.3f}")
 
 
+def test_spheres_two_views():
+    """Spheres seen by two pinhole views: one backward call over both views
+    (per-view camera reduction), and one call per view accumulating."""
+    sc = S.pulsar_spheres(seed=17, n=60_000, width=256, height=192)
+    c0 = sc.cams[0]
+    R1 = S._rot_y(-12.0) @ np.asarray(c0.R)
+    sc.cams = [c0, S.Camera(S.CAM_PINHOLE, 200, 160, R1, [0.4, 0.1, 0.5], fx=220.0, fy=230.0, cx=97.0, cy=83.0,
+                            znear=1.0, zfar=21.0)]
+    _log("[case] spheres, two views")
+    rz = _rz(sc)
+    rz.forward()
+    orc = O.Oracle(sc)
+    st = compare_forward(rz, orc)
+    _log(f"  fwd ok img_err={st['img_err']:.2e} flagged={st['flag_frac']:.2e}")
+    g = S.upstream_grads(sc, 31)
+    bw = compare_backward(rz, orc, None, g)
+    _log(f"  bwd (one call) worst={bw['worst']:.3f}")
+    bw = compare_backward(rz, orc, None, g, view_groups=[(0, 1), (1, 1)])
+    _log(f"  bwd (per view) worst={bw['worst']:.3f}")
+
+
 def test_all_culled_and_single():
     sc = TS.spheres([[0, 0, -5.0]], [0.5], [0.5], [[1, 0, 0]], [TS.pinhole(40, 30, 40.0, znear=1.0, zfar=21.0)])
     rz = _rz(sc)
