@@ -23,9 +23,13 @@ namespace {
 // ---------------------------------------------------------------------------
 template <int CM>
 __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
-  __shared__ double2 s_q01[256], s_q23[256], s_q45[256];   // D / g over the tile
-  __shared__ float2 s_w[256];       // o exp(o zhat / gamma), stop limit bound / tau
-  __shared__ float s_f[CM][256];
+  // One staged entry = NE 16-byte slots at a common stride, so every read of an
+  // entry uses one LDS address with constant offsets: three slots of D / g
+  // coefficients (fp64 pairs), then (o exp(o zhat / gamma), stop limit bound /
+  // tau, features...) in fp32.
+  constexpr int NF4 = (CM + 2 + 3) / 4;
+  constexpr int NE = 3 + NF4;
+  __shared__ float4 s_e[NE][256];
   __shared__ QuadLists s_l;
   __shared__ int s_top[256 * SPLAT_TOPK_MAX];
   if (*A.overflow) return;
@@ -43,6 +47,7 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   for (int ch = 0; ch < CM; ch++) S[ch] = A.bg_weight * A.bg[ch];
   const int K = A.top_k;
   int ntop = 0;
+  bool need = K > 0;                    // still recording contributing spheres
   int *my_top = s_top + threadIdx.x * K;
   bool active = tp.inside;
   const long long vbase = (long long)view * A.n;
@@ -55,13 +60,17 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
       const DrawRec d = A.draw[rid];
       const long long id = (long long)rid - vbase;
       const SphereQuad q = sphere_quad(c, tp, d);
-      s_q01[threadIdx.x] = q.q01;
-      s_q23[threadIdx.x] = q.q23;
-      s_q45[threadIdx.x] = q.q45;
+      s_e[0][threadIdx.x] = __builtin_bit_cast(float4, q.q01);
+      s_e[1][threadIdx.x] = __builtin_bit_cast(float4, q.q23);
+      s_e[2][threadIdx.x] = __builtin_bit_cast(float4, q.q45);
+      float t[4 * NF4];
       // stop when bound < tau N, i.e. N > bound / tau (never when tau = 0)
-      s_w[threadIdx.x] = make_float2(d.w, tau > 0.0f ? d.e / tau : __builtin_huge_valf());
+      t[0] = d.w;
+      t[1] = tau > 0.0f ? d.e / tau : __builtin_huge_valf();
 #pragma unroll
-      for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      for (int ch = 0; ch < 4 * NF4 - 2; ch++) t[2 + ch] = ch < CM && ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+#pragma unroll
+      for (int f = 0; f < NF4; f++) s_e[3 + f][threadIdx.x] = make_float4(t[4 * f], t[4 * f + 1], t[4 * f + 2], t[4 * f + 3]);
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
@@ -75,18 +84,28 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
         for (int u = 0; u < 4; u++) {
           if (k + u >= cnt) break;
           const int idx = (int)((four >> (8 * u)) & 0xffu);
-          const float2 wv = s_w[idx];
-          active = active && !(N > wv.y);          // no later sphere can matter
-          const double num = sphere_num(ray, s_q01[idx], s_q23[idx], s_q45[idx]);
+          float t[4 * NF4];
+#pragma unroll
+          for (int f = 0; f < NF4; f++) {
+            const float4 x = s_e[3 + f][idx];
+            t[4 * f] = x.x; t[4 * f + 1] = x.y; t[4 * f + 2] = x.z; t[4 * f + 3] = x.w;
+          }
+          active = active && !(N > t[1]);          // no later sphere can matter
+          const double num = sphere_num(ray, __builtin_bit_cast(double2, s_e[0][idx]),
+                                        __builtin_bit_cast(double2, s_e[1][idx]),
+                                        __builtin_bit_cast(double2, s_e[2][idx]));
           const bool hit = active && num > 0.0;
-          const float w = hit ? wv.x * (float)(num * ray.g) : 0.0f;
+          const float w = hit ? t[0] * (float)(num * ray.g) : 0.0f;
           N += w;
 #pragma unroll
-          for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][idx], S[ch]);
-          const bool rec = hit && ntop < K;
+          for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch]);
+          const bool rec = hit && need;
           if (ballot64(rec)) {                     // most entries record nothing
-            if (rec) my_top[ntop] = (int)(b + (uint32_t)idx);
-            ntop += rec ? 1 : 0;
+            if (rec) {
+              my_top[ntop] = (int)(b + (uint32_t)idx);
+              ntop++;
+              need = ntop < K;
+            }
           }
         }
         if (ballot64(active) == 0) break;
