@@ -17,21 +17,21 @@
 //   k_thist                       each workgroup counts the tiles of a chunk of
 //                                 one view's records in LDS and stores the counts
 //                                 as one row of the view's [chunk][tile] matrix
-//   k_col_sum, k_col_scan,        per tile (column): pair total, and for every
-//   k_col_offsets                 chunk the exclusive prefix over earlier chunks
-//   k_scan_reduce, k_scan_top,    exclusive scan over tiles: tile ranges, the pair
-//   k_tile_ranges                 total, the overflow flag, tile starts
+//   k_col_sum, k_col_offsets      per tile (column): for every chunk the
+//                                 exclusive prefix over earlier chunks, and the
+//                                 tile's pair total
+//   k_tile_scan1                  exclusive scan over tiles (one workgroup):
+//                                 tile ranges, pair total, overflow, tile starts
 //   k_tscatter                    each pair's word into its tile's segment, at
 //                                 tile start + chunk prefix + a rank from an LDS
 //                                 atomic
-//   k_seg_sort_small              one workgroup per tile, bitonic sort in
-//                                 registers, lane shuffles and LDS (segments up
-//                                 to SEG_SMALL), final keys/values
-//   k_seg_sort_big                longer segments: LSD radix sort by one
-//                                 workgroup over the segment in global memory
+//   k_seg_sort                    every segment sorted on its own: by one wave
+//                                 up to SEG_WAVE pairs, by a workgroup beyond
 // No global atomics on the counting path: device-wide atomics on a few thousand
 // tile counters serialise. Views with more tiles than LDS_TILES take a fallback
-// (k_tile_count, k_bucket) with global atomic counters and cursors.
+// (k_tile_count, k_bucket) with global atomic counters and cursors; more than
+// TILE_SCAN1_MAX tiles take a three-kernel scan (k_scan_reduce, k_scan_top,
+// k_tile_ranges).
 #include "splat_internal.h"
 
 namespace {
@@ -41,9 +41,11 @@ constexpr int RADIX = 256;
 constexpr int SEG_SMALL = 2048;     // largest segment sorted in LDS
 constexpr int BIG_ROUNDS = 8;       // items per thread per chunk of the big-segment sort
 constexpr int BIG_CHUNK = SCAN_BLOCK * BIG_ROUNDS;
-constexpr int BIG_GRID = 1024;      // workgroups sharing the big segments
+constexpr int TH_THREADS = 512;     // workgroup of the counting passes
 constexpr int TH_RPT = 8;           // records per thread in the counting passes
-constexpr int TH_CHUNK = 256 * TH_RPT;
+constexpr int TH_CHUNK = TH_THREADS * TH_RPT;
+constexpr int SEG_WAVE = 512;       // segments up to this length: one wave sorts them
+constexpr int TILE_SCAN1_MAX = 1 << 16;   // tiles scanned by a single workgroup
 constexpr int LDS_TILES = 16384;    // tiles of one view held as LDS counters (64 KiB)
 constexpr int COL_ROWS = 16;        // matrix rows (chunks) per thread in the column scan
 
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_reduce(const uint32_t *cnt,
 }
 
 // Single workgroup: exclusive scan of the block sums in place; pair total,
-// overflow flag, live pair count, and the big-segment counter reset.
+// overflow flag and live pair count.
 // Each thread owns TOP_ITEMS consecutive sums per round.
 constexpr int TOP_ITEMS = 16;
 __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_top(unsigned long long *block_sums, int nblocks,
@@ -145,7 +147,6 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_top(unsigned long long *blo
     const int of = carry > (unsigned long long)capacity ? 1 : 0;
     *overflow = of;
     live[0] = of ? 0u : (uint32_t)carry;
-    live[1] = 0u;                       // big segments found by k_seg_sort_small
   }
 }
 
@@ -163,6 +164,61 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_ranges(uint32_t *cnt_cursor
     cnt_cursor[t] = start;
     ranges[2 * t] = c ? start : 0u;
     ranges[2 * t + 1] = c ? start + c : 0u;
+  }
+}
+
+// Single workgroup, up to TILE_SCAN1_MAX tiles: pair total, overflow flag and
+// live count first, then, without overflow, the exclusive scan that writes the
+// tile ranges and turns the counts into tile starts. Every thread owns
+// TOP_ITEMS consecutive tiles per round; up to SCAN_BLOCK * TOP_ITEMS tiles in all
+// keep their counts in registers between the two phases.
+__device__ __forceinline__ void load_counts(const uint32_t *cnt, int m, int t0, uint32_t (&x)[TOP_ITEMS]) {
+#pragma unroll
+  for (int r = 0; r < TOP_ITEMS; r++) x[r] = t0 + r < m ? cnt[t0 + r] : 0u;
+}
+
+__global__ __launch_bounds__(SCAN_BLOCK) void k_tile_scan1(uint32_t *cnt_start, int m, long long capacity,
+                                                            int64_t *num_pairs, int32_t *overflow, uint32_t *live,
+                                                            uint32_t *ranges) {
+  __shared__ int s_of;
+  constexpr int ROUND = SCAN_BLOCK * TOP_ITEMS;
+  uint32_t x[TOP_ITEMS];
+  unsigned long long part = 0;
+  for (int base = 0; base < m; base += ROUND) {
+    load_counts(cnt_start, m, base + (int)threadIdx.x * TOP_ITEMS, x);
+#pragma unroll
+    for (int r = 0; r < TOP_ITEMS; r++) part += x[r];
+  }
+  unsigned long long total;
+  block_exclusive_scan<unsigned long long>(part, &total);
+  if (threadIdx.x == 0) {
+    const int of = total > (unsigned long long)capacity ? 1 : 0;
+    *num_pairs = (int64_t)total;
+    *overflow = of;
+    live[0] = of ? 0u : (uint32_t)total;
+    s_of = of;
+  }
+  __syncthreads();
+  if (s_of) return;
+  uint32_t carry = 0;                          // below the capacity (< 2^32) from here on
+  for (int base = 0; base < m; base += ROUND) {
+    const int t0 = base + (int)threadIdx.x * TOP_ITEMS;
+    if (m > ROUND) load_counts(cnt_start, m, t0, x);   // one round: still in registers
+    uint32_t sum = 0;
+#pragma unroll
+    for (int r = 0; r < TOP_ITEMS; r++) sum += x[r];
+    uint32_t tot;
+    uint32_t run = carry + block_exclusive_scan<uint32_t>(sum, &tot);
+#pragma unroll
+    for (int r = 0; r < TOP_ITEMS; r++) {
+      if (t0 + r < m) {
+        cnt_start[t0 + r] = run;
+        ranges[2 * (t0 + r)] = x[r] ? run : 0u;
+        ranges[2 * (t0 + r) + 1] = x[r] ? run + x[r] : 0u;
+      }
+      run += x[r];
+    }
+    carry += tot;
   }
 }
 
@@ -203,12 +259,12 @@ __device__ __forceinline__ void load_chunk(const BinRec *bin, const uint32_t *co
                                            ChunkRecs &cr) {
 #pragma unroll
   for (int r = 0; r < TH_RPT; r++) {
-    const int j = r * 256 + (int)threadIdx.x;
+    const int j = r * TH_THREADS + (int)threadIdx.x;
     cr.cnt[r] = j < nvalid ? counts[rec0 + j] : 0u;
   }
 #pragma unroll
   for (int r = 0; r < TH_RPT; r++) {
-    const int j = r * 256 + (int)threadIdx.x;
+    const int j = r * TH_THREADS + (int)threadIdx.x;
     if (cr.cnt[r]) cr.b[r] = bin[rec0 + j];
   }
 }
@@ -227,14 +283,14 @@ __device__ __forceinline__ void for_each_local_tile(const ViewDev &cv, const Bin
   }
 }
 
-// grid: n_views * nchunk workgroups; dynamic LDS: 4 * max tiles per view.
-__global__ __launch_bounds__(256) void k_thist(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
+// grid: n_views * nchunk workgroups of TH_THREADS; dynamic LDS: 4 * max tiles per view.
+__global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
                                                 const uint32_t *counts, uint32_t *M) {
   extern __shared__ uint32_t s_cnt[];
   const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
   const ViewDev &cv = vt.v[v];
   const int T = cv.TW * cv.TH;
-  for (int t = threadIdx.x; t < T; t += 256) s_cnt[t] = 0;
+  for (int t = threadIdx.x; t < T; t += TH_THREADS) s_cnt[t] = 0;
   ChunkRecs cr;
   const int nvalid = min(TH_CHUNK, n - chunk * TH_CHUNK);
   load_chunk(bin, counts, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);
@@ -244,7 +300,7 @@ __global__ __launch_bounds__(256) void k_thist(ViewTable vt, MatTable mt, int n,
     if (cr.cnt[r]) for_each_local_tile(cv, cr.b[r], [&](uint32_t lt) { atomicAdd(&s_cnt[lt], 1u); });
   __syncthreads();
   uint32_t *row = M + mat_index(mt, cv, v, chunk, 0);
-  for (int t = threadIdx.x; t < T; t += 256) row[t] = s_cnt[t];
+  for (int t = threadIdx.x; t < T; t += TH_THREADS) row[t] = s_cnt[t];
 }
 
 // Column (tile) partial sums over groups of COL_ROWS chunks: S[group][gtile].
@@ -263,29 +319,19 @@ __global__ __launch_bounds__(256) void k_col_sum(ViewTable vt, MatTable mt, int 
   S[(size_t)blockIdx.y * vt.total_tiles + gt] = s;
 }
 
-// Per tile: exclusive scan of the group sums in place; the tile's pair count out.
-__global__ __launch_bounds__(256) void k_col_scan(int tiles, int ngroups, uint32_t *S, uint32_t *tile_cnt) {
-  const int gt = blockIdx.x * 256 + threadIdx.x;
-  if (gt >= tiles) return;
-  uint32_t run = 0;
-#pragma unroll 4
-  for (int g = 0; g < ngroups; g++) {
-    const uint32_t x = S[(size_t)g * tiles + gt];
-    S[(size_t)g * tiles + gt] = run;
-    run += x;
-  }
-  tile_cnt[gt] = run;
-}
-
-// Matrix entries become the exclusive prefix over earlier chunks of the same tile.
-__global__ __launch_bounds__(256) void k_col_offsets(ViewTable vt, MatTable mt, int nchunk, const uint32_t *S,
-                                                      uint32_t *M) {
+// Matrix entries become the exclusive prefix over earlier chunks of the same
+// tile; the group's starting prefix is the sum of the earlier groups' partial
+// sums, and the last group also writes the tile's pair count.
+__global__ __launch_bounds__(256) void k_col_offsets(ViewTable vt, MatTable mt, int nchunk, int ngroups,
+                                                      const uint32_t *S, uint32_t *M, uint32_t *tile_cnt) {
   const int gt = blockIdx.x * 256 + threadIdx.x;
   if (gt >= vt.total_tiles) return;
   const int v = view_of_tile(vt, gt);
   const ViewDev &cv = vt.v[v];
   const int t = gt - cv.tile_off, c0 = blockIdx.y * COL_ROWS;
-  uint32_t run = S[(size_t)blockIdx.y * vt.total_tiles + gt];
+  uint32_t run = 0;
+#pragma unroll 8
+  for (int g = 0; g < (int)blockIdx.y; g++) run += S[(size_t)g * vt.total_tiles + gt];
 #pragma unroll
   for (int r = 0; r < COL_ROWS; r++)
     if (c0 + r < nchunk) {
@@ -294,10 +340,11 @@ __global__ __launch_bounds__(256) void k_col_offsets(ViewTable vt, MatTable mt, 
       M[i] = run;
       run += x;
     }
+  if ((int)blockIdx.y == ngroups - 1) tile_cnt[gt] = run;
 }
 
 // Same chunks as k_thist: words to tile start + chunk prefix + LDS rank.
-__global__ __launch_bounds__(256) void k_tscatter(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
+__global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
                                                    const uint32_t *counts, const uint32_t *M,
                                                    const uint32_t *tile_start, const int32_t *overflow,
                                                    uint64_t *words) {
@@ -307,7 +354,7 @@ __global__ __launch_bounds__(256) void k_tscatter(ViewTable vt, MatTable mt, int
   const ViewDev &cv = vt.v[v];
   const int T = cv.TW * cv.TH;
   const uint32_t *row = M + mat_index(mt, cv, v, chunk, 0);
-  for (int t = threadIdx.x; t < T; t += 256) s_base[t] = tile_start[cv.tile_off + t] + row[t];
+  for (int t = threadIdx.x; t < T; t += TH_THREADS) s_base[t] = tile_start[cv.tile_off + t] + row[t];
   ChunkRecs cr;
   const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
   load_chunk(bin, counts, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
@@ -315,7 +362,7 @@ __global__ __launch_bounds__(256) void k_tscatter(ViewTable vt, MatTable mt, int
 #pragma unroll      // constant indices keep the record arrays in registers
   for (int r = 0; r < TH_RPT; r++) {
     if (!cr.cnt[r]) continue;
-    const uint64_t w = ((uint64_t)cr.b[r].key << 32) | (uint64_t)(uint32_t)(rec0 + r * 256 + threadIdx.x);
+    const uint64_t w = ((uint64_t)cr.b[r].key << 32) | (uint64_t)(uint32_t)(rec0 + r * TH_THREADS + threadIdx.x);
     for_each_local_tile(cv, cr.b[r], [&](uint32_t lt) { words[atomicAdd(&s_base[lt], 1u)] = w; });
   }
 }
@@ -350,8 +397,7 @@ __device__ __forceinline__ void cx_local(uint64_t (&e)[E], uint32_t base, uint32
 // descending one; for j >= E that choice is the same for all of a thread's
 // elements. Words are distinct (padding aside), so one compare decides.
 template <int E>
-__device__ void bitonic_block(uint64_t (&e)[E], uint32_t P, uint64_t *s) {
-  const uint32_t base = threadIdx.x * E;
+__device__ void bitonic_regs(uint64_t (&e)[E], uint32_t P, uint32_t base, uint64_t *s) {
   for (uint32_t k = 2; k <= P; k <<= 1) {
     for (uint32_t j = k >> 1; j > 0; j >>= 1) {
       if (j >= (uint32_t)E) {
@@ -392,139 +438,151 @@ __device__ __forceinline__ void sort_small(const uint64_t *words, uint64_t *keys
   uint64_t e[E];
 #pragma unroll
   for (int a = 0; a < E; a++) e[a] = base + a < len ? words[start + base + a] : ~0ull;
-  bitonic_block<E>(e, P, s);
+  bitonic_regs<E>(e, P, base, s);
 #pragma unroll
   for (int a = 0; a < E; a++)
     if (base + a < len) write_pair(keys, vals, start + base + a, tile, e[a]);
 }
 
-// One workgroup per tile. Segments up to SEG_SMALL: bitonic sort of the words
-// (padded to a power of two with all-ones words, which sort last), then the
-// final key/value pairs. Longer segments are listed for k_seg_sort_big.
-__global__ __launch_bounds__(256) void k_seg_sort_small(const uint32_t *ranges, const uint64_t *words,
-                                                         const int32_t *overflow, uint64_t *keys, uint32_t *vals,
-                                                         uint32_t *live, uint32_t *big_list) {
-  __shared__ uint64_t s[SEG_SMALL];
-  if (*overflow) return;
-  const uint32_t tile = blockIdx.x;
-  const uint32_t start = ranges[2 * tile], len = ranges[2 * tile + 1] - start;
-  if (len == 0) return;
-  if (len > SEG_SMALL) {
-    if (threadIdx.x == 0) big_list[atomicAdd(&live[1], 1u)] = tile;
-    return;
-  }
-  uint32_t P = 2;
-  while (P < len) P <<= 1;
-  if (P <= 512)
-    sort_small<2>(words, keys, vals, start, len, P, tile, s);
-  else if (P == 1024)
-    sort_small<4>(words, keys, vals, start, len, P, tile, s);
-  else
-    sort_small<8>(words, keys, vals, start, len, P, tile, s);
-}
-
-// Segments longer than SEG_SMALL, one workgroup each (grid-stride over the list):
-// stable LSD radix sort of the words, 8 bits per pass, through global memory
-// (ping-pong between the bucket array and the caller's key array). Passes over
-// bytes that are equal in every word of the segment are skipped. Within a pass
-// the segment goes in chunks of BIG_CHUNK; ranks inside a wave come from 8
-// ballots, across waves from LDS counters.
-__global__ __launch_bounds__(256) void k_seg_sort_big(const uint32_t *ranges, uint64_t *words, const int32_t *overflow,
-                                                       uint64_t *keys, uint32_t *vals, const uint32_t *live,
-                                                       const uint32_t *big_list) {
+// Stable LSD radix sort of one long segment by the whole workgroup, 8 bits per
+// pass, through global memory (ping-pong between the bucket array and the
+// caller's key array), then the final key/value pairs. Passes over bytes that
+// are equal in every word of the segment are skipped. Within a pass the segment
+// goes in chunks of BIG_CHUNK; ranks inside a wave come from 8 ballots, across
+// waves from LDS counters.
+__device__ void seg_radix_block(uint64_t *words, uint64_t *keys, uint32_t *vals, uint32_t tile, uint32_t start,
+                                uint32_t len) {
   __shared__ uint32_t s_hist[RADIX];
   __shared__ uint32_t s_off[RADIX];
   __shared__ uint32_t s_wcnt[SCAN_BLOCK / WAVE][RADIX];
   __shared__ unsigned long long s_and, s_or;
-  if (*overflow) return;
-  const uint32_t nbig = live[1];
   const unsigned tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-  for (uint32_t b = blockIdx.x; b < nbig; b += gridDim.x) {
-    const uint32_t tile = big_list[b];
-    const uint32_t start = ranges[2 * tile], len = ranges[2 * tile + 1] - start;
-    uint64_t *src = words + start, *dst = keys + start;
-    // bytes that vary across the segment
-    uint64_t va = ~0ull, vo = 0ull;
-    for (uint32_t i = tid; i < len; i += 256) {
-      const uint64_t x = src[i];
-      va &= x;
-      vo |= x;
-    }
-    if (tid == 0) {
-      s_and = ~0ull;
-      s_or = 0ull;
-    }
+  uint64_t *src = words + start, *dst = keys + start;
+  // bytes that vary across the segment
+  uint64_t va = ~0ull, vo = 0ull;
+  for (uint32_t i = tid; i < len; i += SCAN_BLOCK) {
+    const uint64_t x = src[i];
+    va &= x;
+    vo |= x;
+  }
+  if (tid == 0) {
+    s_and = ~0ull;
+    s_or = 0ull;
+  }
+  __syncthreads();
+  atomicAnd(&s_and, (unsigned long long)va);
+  atomicOr(&s_or, (unsigned long long)vo);
+  __syncthreads();
+  const uint64_t vary = s_and ^ s_or;
+  __syncthreads();
+  for (int shift = 0; shift < 64; shift += 8) {
+    if (((vary >> shift) & 0xffull) == 0) continue;      // uniform over the workgroup
+    s_hist[tid] = 0;
     __syncthreads();
-    atomicAnd(&s_and, (unsigned long long)va);
-    atomicOr(&s_or, (unsigned long long)vo);
+    for (uint32_t i = tid; i < len; i += SCAN_BLOCK) atomicAdd(&s_hist[(unsigned)(src[i] >> shift) & (RADIX - 1)], 1u);
     __syncthreads();
-    const uint64_t vary = s_and ^ s_or;
+    uint32_t tot;
+    s_off[tid] = block_exclusive_scan<uint32_t>(s_hist[tid], &tot);
+#pragma unroll
+    for (int q = 0; q < SCAN_BLOCK / WAVE; q++) s_wcnt[q][tid] = 0;
     __syncthreads();
-    for (int shift = 0; shift < 64; shift += 8) {
-      if (((vary >> shift) & 0xffull) == 0) continue;      // uniform over the workgroup
-      s_hist[tid] = 0;
-      __syncthreads();
-      for (uint32_t i = tid; i < len; i += 256) atomicAdd(&s_hist[(unsigned)(src[i] >> shift) & (RADIX - 1)], 1u);
-      __syncthreads();
-      uint32_t tot;
-      s_off[tid] = block_exclusive_scan<uint32_t>(s_hist[tid], &tot);
+    for (uint32_t base = 0; base < len; base += BIG_CHUNK) {
+      uint64_t x[BIG_ROUNDS];
 #pragma unroll
-      for (int q = 0; q < SCAN_BLOCK / WAVE; q++) s_wcnt[q][tid] = 0;
-      __syncthreads();
-      for (uint32_t base = 0; base < len; base += BIG_CHUNK) {
-        uint64_t x[BIG_ROUNDS];
-#pragma unroll
-        for (int r = 0; r < BIG_ROUNDS; r++) {
-          const uint32_t i = base + r * 256 + tid;
-          x[r] = i < len ? src[i] : 0ull;
-        }
-#pragma unroll
-        for (int r = 0; r < BIG_ROUNDS; r++) {
-          const bool valid = base + r * 256 + tid < len;
-          const unsigned d = (unsigned)(x[r] >> shift) & (RADIX - 1);
-          uint64_t peers = ballot64(valid);
-#pragma unroll
-          for (int bit = 0; bit < 8; bit++) {
-            const bool on = (d >> bit) & 1u;
-            const uint64_t m = ballot64(on);
-            peers &= on ? m : ~m;
-          }
-          const unsigned rank = __popcll(peers & below);
-          if (valid && rank == 0) s_wcnt[w][d] = __popcll(peers);
-          __syncthreads();
-          if (valid) {
-            uint32_t off = s_off[d] + rank;
-            for (unsigned q = 0; q < w; q++) off += s_wcnt[q][d];
-            dst[off] = x[r];
-          }
-          __syncthreads();
-          uint32_t add = 0;
-#pragma unroll
-          for (int q = 0; q < SCAN_BLOCK / WAVE; q++) {
-            add += s_wcnt[q][tid];
-            s_wcnt[q][tid] = 0;
-          }
-          s_off[tid] += add;
-          __syncthreads();
-        }
+      for (int r = 0; r < BIG_ROUNDS; r++) {
+        const uint32_t i = base + r * SCAN_BLOCK + tid;
+        x[r] = i < len ? src[i] : 0ull;
       }
-      uint64_t *t = src;
-      src = dst;
-      dst = t;
+#pragma unroll
+      for (int r = 0; r < BIG_ROUNDS; r++) {
+        const bool valid = base + r * SCAN_BLOCK + tid < len;
+        const unsigned d = (unsigned)(x[r] >> shift) & (RADIX - 1);
+        uint64_t peers = ballot64(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; bit++) {
+          const bool on = (d >> bit) & 1u;
+          const uint64_t m = ballot64(on);
+          peers &= on ? m : ~m;
+        }
+        const unsigned rank = __popcll(peers & below);
+        if (valid && rank == 0) s_wcnt[w][d] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+          uint32_t off = s_off[d] + rank;
+          for (unsigned q = 0; q < w; q++) off += s_wcnt[q][d];
+          dst[off] = x[r];
+        }
+        __syncthreads();
+        uint32_t add = 0;
+#pragma unroll
+        for (int q = 0; q < SCAN_BLOCK / WAVE; q++) {
+          add += s_wcnt[q][tid];
+          s_wcnt[q][tid] = 0;
+        }
+        s_off[tid] += add;
+        __syncthreads();
+      }
     }
-    // src holds the sorted words (in the key array or the bucket array)
-    for (uint32_t i = tid; i < len; i += 256) write_pair(keys, vals, start + i, tile, src[i]);
-    __syncthreads();
+    uint64_t *t = src;
+    src = dst;
+    dst = t;
+  }
+  // src holds the sorted words (in the key array or the bucket array)
+  for (uint32_t i = tid; i < len; i += SCAN_BLOCK) write_pair(keys, vals, start + i, tile, src[i]);
+}
+
+// Segment sorts, four tiles per workgroup. A wave sorts its own tile when the
+// segment has at most SEG_WAVE pairs: bitonic with eight words per lane, the
+// rest of the network through lane shuffles (no LDS, no barriers). Longer
+// segments are then taken by the whole workgroup one after another: bitonic
+// over registers, shuffles and LDS (padded to a power of two with all-ones
+// words, which sort last) up to SEG_SMALL pairs, the radix sort beyond.
+__global__ __launch_bounds__(256) void k_seg_sort(const uint32_t *ranges, uint64_t *words, const int32_t *overflow,
+                                                   uint64_t *keys, uint32_t *vals, int tiles) {
+  __shared__ uint64_t s[SEG_SMALL];
+  if (*overflow) return;
+  const unsigned lane = lane_id();
+  const int own = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (own < tiles) {
+    const uint32_t start = ranges[2 * own], len = ranges[2 * own + 1] - start;
+    if (len > 0 && len <= SEG_WAVE) {
+      uint32_t P = 2;
+      while (P < len) P <<= 1;
+      const uint32_t base = lane * 8;
+      uint64_t e[8];
+#pragma unroll
+      for (int a = 0; a < 8; a++) e[a] = base + a < len ? words[start + base + a] : ~0ull;
+      bitonic_regs<8>(e, P, base, s);          // P <= 64 * 8: never reaches the LDS stages
+#pragma unroll
+      for (int a = 0; a < 8; a++)
+        if (base + a < len) write_pair(keys, vals, start + base + a, (uint32_t)own, e[a]);
+    }
+  }
+  for (int q = 0; q < 4; q++) {
+    const int t = (int)blockIdx.x * 4 + q;
+    if (t >= tiles) break;
+    const uint32_t start = ranges[2 * t], len = ranges[2 * t + 1] - start;
+    if (len <= SEG_WAVE) continue;
+    __syncthreads();                           // LDS reuse between tiles
+    if (len <= SEG_SMALL) {
+      uint32_t P = 2;
+      while (P < len) P <<= 1;
+      if (P == 1024)
+        sort_small<4>(words, keys, vals, start, len, P, (uint32_t)t, s);
+      else
+        sort_small<8>(words, keys, vals, start, len, P, (uint32_t)t, s);
+    } else {
+      seg_radix_block(words, keys, vals, (uint32_t)t, start, len);
+    }
   }
 }
 
 struct SortWs {
   uint64_t *words;      // [capacity] bucketed (depth << 32 | record) words
   uint32_t *cursor;     // [tiles] counts, then tile starts (and cursors in the fallback)
-  uint32_t *big_list;   // [tiles] tiles with long segments
   unsigned long long *block_sums;  // [ceil(tiles / 256) + 1]
-  uint32_t *live;       // [0] live pairs, [1] big segments
+  uint32_t *live;       // [0] live pairs
   uint32_t *mat;        // per-chunk tile counts (LDS counting path)
   uint32_t *colsum;     // [groups][tiles]
   size_t bytes;
@@ -563,7 +621,6 @@ SortWs sort_ws_layout(void *base, const ViewTable &vt, int n, long long capacity
   const CountPlan cp = count_plan(vt, n);
   w.words = (uint64_t *)p;      p += proj_align(sizeof(uint64_t) * (size_t)(capacity > 0 ? capacity : 1));
   w.cursor = (uint32_t *)p;     p += proj_align(sizeof(uint32_t) * (size_t)tiles);
-  w.big_list = (uint32_t *)p;   p += proj_align(sizeof(uint32_t) * (size_t)tiles);
   w.block_sums = (unsigned long long *)p; p += proj_align(sizeof(unsigned long long) * (size_t)(nscan + 1));
   w.live = (uint32_t *)p;       p += proj_align(sizeof(uint32_t) * 4);
   w.mat = (uint32_t *)p;        p += proj_align(sizeof(uint32_t) * (size_t)cp.mat_elems);
@@ -593,36 +650,37 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
 
   if (cp.lds) {
     const unsigned grid = (unsigned)(vt.n * cp.nchunk);
-    hipLaunchKernelGGL(k_thist, dim3(grid), dim3(256), lds_bytes, stream, vt, cp.mt, n, cp.nchunk, L.bin, counts,
-                       ws.mat);
+    hipLaunchKernelGGL(k_thist, dim3(grid), dim3(TH_THREADS), lds_bytes, stream, vt, cp.mt, n, cp.nchunk, L.bin,
+                       counts, ws.mat);
     hipLaunchKernelGGL(k_col_sum, dim3(tile_blocks, cp.ngroups), dim3(256), 0, stream, vt, cp.mt, cp.nchunk, ws.mat,
                        ws.colsum);
-    hipLaunchKernelGGL(k_col_scan, dim3(tile_blocks), dim3(256), 0, stream, (int)tiles, cp.ngroups, ws.colsum,
-                       ws.cursor);
     hipLaunchKernelGGL(k_col_offsets, dim3(tile_blocks, cp.ngroups), dim3(256), 0, stream, vt, cp.mt, cp.nchunk,
-                       ws.colsum, ws.mat);
+                       cp.ngroups, ws.colsum, ws.mat, ws.cursor);
   } else {
     hipLaunchKernelGGL(k_fill_u32, dim3(tile_blocks), dim3(256), 0, stream, ws.cursor, tiles, 0u);
     if (rec_blocks)
       hipLaunchKernelGGL(k_tile_count, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, ws.cursor);
   }
-  hipLaunchKernelGGL(k_scan_reduce, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums);
-  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(SCAN_BLOCK), 0, stream, ws.block_sums, nscan, capacity, num_pairs,
-                     overflow, ws.live);
-  hipLaunchKernelGGL(k_tile_ranges, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums,
-                     overflow, ranges);
+  if (tiles <= TILE_SCAN1_MAX) {
+    hipLaunchKernelGGL(k_tile_scan1, dim3(1), dim3(SCAN_BLOCK), 0, stream, ws.cursor, (int)tiles, capacity, num_pairs,
+                       overflow, ws.live, ranges);
+  } else {
+    hipLaunchKernelGGL(k_scan_reduce, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums);
+    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(SCAN_BLOCK), 0, stream, ws.block_sums, nscan, capacity, num_pairs,
+                       overflow, ws.live);
+    hipLaunchKernelGGL(k_tile_ranges, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums,
+                       overflow, ranges);
+  }
   SPLAT_LAUNCH_CHECK();
   if (cp.lds) {
-    hipLaunchKernelGGL(k_tscatter, dim3((unsigned)(vt.n * cp.nchunk)), dim3(256), lds_bytes, stream, vt, cp.mt, n,
-                       cp.nchunk, L.bin, counts, ws.mat, ws.cursor, overflow, ws.words);
+    hipLaunchKernelGGL(k_tscatter, dim3((unsigned)(vt.n * cp.nchunk)), dim3(TH_THREADS), lds_bytes, stream, vt, cp.mt,
+                       n, cp.nchunk, L.bin, counts, ws.mat, ws.cursor, overflow, ws.words);
   } else if (rec_blocks) {
     hipLaunchKernelGGL(k_bucket, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, overflow, ws.cursor,
                        ws.words);
   }
-  hipLaunchKernelGGL(k_seg_sort_small, dim3((unsigned)tiles), dim3(256), 0, stream, ranges, ws.words, overflow, keys,
-                     vals, ws.live, ws.big_list);
-  hipLaunchKernelGGL(k_seg_sort_big, dim3((unsigned)(tiles < BIG_GRID ? tiles : BIG_GRID)), dim3(256), 0, stream,
-                     ranges, ws.words, overflow, keys, vals, ws.live, ws.big_list);
+  hipLaunchKernelGGL(k_seg_sort, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream, ranges, ws.words, overflow,
+                     keys, vals, (int)tiles);
   SPLAT_LAUNCH_CHECK();
   return SPLAT_OK;
 }

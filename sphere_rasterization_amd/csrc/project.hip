@@ -1,13 +1,14 @@
-// Projection: one thread per (view, primitive).
+// Projection: one thread per (view, primitive); the grid's second dimension is
+// the view, so a workgroup's camera is uniform (scalar loads).
 //
 // Pulsar appendix B.1.1 ("Step 0: enclosing rectangle"): a sphere-parallel pass
 // that computes each primitive's screen rectangle and the data the draw step
 // needs, kept in separate binning and drawing records. Gaussians use EWA
 // splatting (covariance pushed through the Jacobian of the image mapping).
 //
-// Everything here runs in fp64: the work is per primitive and HBM-bound, and
-// double precision keeps the projected centre exact enough for the per-pixel
-// fp32 compositing (the centre is stored as an unevaluated sum hi + lo).
+// Everything here runs in fp64: the work is per primitive, and double
+// precision keeps the projected centre and the conic (or the sphere's
+// normalised centre and A) exact enough for the per-pixel compositing.
 // The expressions that decide integer outputs (pixel and tile ranges, depth
 // key) are evaluated in a fixed operand order with contraction disabled
 // (-ffp-contract=off), so any IEEE double implementation of the same
@@ -93,15 +94,16 @@ struct PrimArgs {
   double gamma, alpha_min;
 };
 
+template <int KIND>
 __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjLayout L, uint32_t *counts) {
-  long long k = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  long long nrec = (long long)vt.n * P.n;
-  if (k >= nrec) return;
-  int view = (int)(k / P.n), i = (int)(k - (long long)view * P.n);
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P.n) return;
+  const int view = blockIdx.y;
+  const long long k = (long long)view * P.n + i;
   const ViewDev &c = vt.v[view];
   double o = (double)P.opacity[i];
 
-  if (P.kind == SPLAT_PRIM_SPHERE) {
+  if (KIND == SPLAT_PRIM_SPHERE) {
     double q[3];
     sensor_point(c, (double)P.pos[3 * i], (double)P.pos[3 * i + 1], (double)P.pos[3 * i + 2], q);
     double r = (double)P.scale[i];
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
   }
 
   double u, v, sxx, sxy, syy, depth;
-  if (P.kind == SPLAT_PRIM_GAUSS2D) {
+  if (KIND == SPLAT_PRIM_GAUSS2D) {
     u = (double)P.pos[2 * i];
     v = (double)P.pos[2 * i + 1];
     double s = (double)P.scale[i];
@@ -281,8 +283,13 @@ int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, dou
   P.gamma = gamma;
   P.alpha_min = alpha_min;
   ProjLayout L = proj_layout(proj, nrec);
-  unsigned grid = (unsigned)((nrec + 255) / 256);
-  hipLaunchKernelGGL(k_project, dim3(grid), dim3(256), 0, stream, vt, P, L, counts);
+  const dim3 grid((unsigned)((pr->n + 255) / 256), (unsigned)vt.n);
+  if (pr->kind == SPLAT_PRIM_SPHERE)
+    hipLaunchKernelGGL(k_project<SPLAT_PRIM_SPHERE>, grid, dim3(256), 0, stream, vt, P, L, counts);
+  else if (pr->kind == SPLAT_PRIM_GAUSS2D)
+    hipLaunchKernelGGL(k_project<SPLAT_PRIM_GAUSS2D>, grid, dim3(256), 0, stream, vt, P, L, counts);
+  else
+    hipLaunchKernelGGL(k_project<SPLAT_PRIM_GAUSS3D>, grid, dim3(256), 0, stream, vt, P, L, counts);
   SPLAT_LAUNCH_CHECK();
   return SPLAT_OK;
 }

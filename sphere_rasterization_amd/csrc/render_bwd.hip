@@ -485,6 +485,7 @@ __global__ __launch_bounds__(256) void k_cam_final(ProjBwdArgs P, int nparts, in
   double cam[12];
 #pragma unroll
   for (int q = 0; q < 12; q++) cam[q] = 0.0;
+#pragma unroll 4
   for (int b = threadIdx.x; b < nparts; b += blockDim.x)
 #pragma unroll
     for (int q = 0; q < 12; q++) cam[q] += P.cam_part[12 * b + q];

@@ -115,7 +115,7 @@ static inline size_t proj_bytes(long long nrec) {
 
 // After the accumulators: per-block camera partial sums of the sphere gradient
 // pass ([SPLAT_CAM_BLOCKS][12] fp64).
-#define SPLAT_CAM_BLOCKS 4096
+#define SPLAT_CAM_BLOCKS 1024
 
 struct AccLayout {
   double *g;
