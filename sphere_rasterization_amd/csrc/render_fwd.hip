@@ -12,6 +12,8 @@
 // Positions are made tile-relative while staging and the per-pixel geometry runs
 // in fp64 (full rate on CDNA4), so a footprint's rim and an elongated Gaussian's
 // quadratic form keep their precision; weights and colours accumulate in fp32.
+#include <type_traits>
+
 #include "splat_internal.h"
 
 #include "render_common.h"
@@ -76,31 +78,34 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
     build_quad_lists(s_l, mask);
     // the list, its length and every index are the same for the whole wave
     const int cnt = __builtin_amdgcn_readfirstlane(s_l.cnt[wq]);
-    if (ballot64(active)) {
-      for (int k = 0; k < cnt; k += 4) {
-        const uint32_t four =
-            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(&s_l.idx[wq][k]));
+    // One pass over four entries; REC: some lane of the wave still records its
+    // first contributing spheres (only the first few hits of each pixel do).
+    // FULL: all four entries exist (no end-of-list checks inside the group).
+    auto four_entries = [&](auto REC, auto FULL, int k, uint32_t four) {
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+      for (int u = 0; u < 4; u++) {
+        if constexpr (!decltype(FULL)::value)
           if (k + u >= cnt) break;
-          const int idx = (int)((four >> (8 * u)) & 0xffu);
-          float t[4 * NF4];
+        const int idx = (int)((four >> (8 * u)) & 0xffu);
+        float t[4 * NF4];
 #pragma unroll
-          for (int f = 0; f < NF4; f++) {
-            const float4 x = s_e[3 + f][idx];
-            t[4 * f] = x.x; t[4 * f + 1] = x.y; t[4 * f + 2] = x.z; t[4 * f + 3] = x.w;
-          }
-          active = active && !(N > t[1]);          // no later sphere can matter
-          const double num = sphere_num(ray, __builtin_bit_cast(double2, s_e[0][idx]),
-                                        __builtin_bit_cast(double2, s_e[1][idx]),
-                                        __builtin_bit_cast(double2, s_e[2][idx]));
-          const bool hit = active && num > 0.0;
-          const float w = hit ? t[0] * (float)(num * ray.g) : 0.0f;
-          N += w;
+        for (int f = 0; f < NF4; f++) {
+          const float4 x = s_e[3 + f][idx];
+          t[4 * f] = x.x; t[4 * f + 1] = x.y; t[4 * f + 2] = x.z; t[4 * f + 3] = x.w;
+        }
+        active = active & !(N > t[1]);           // no later sphere can matter (& : no short-circuit branch)
+        const double num = sphere_num(ray, __builtin_bit_cast(double2, s_e[0][idx]),
+                                      __builtin_bit_cast(double2, s_e[1][idx]),
+                                      __builtin_bit_cast(double2, s_e[2][idx]));
+        const bool hit = active & (num > 0.0);
+        // 0 or 1 times a finite weight: straight-line code, no branch around it
+        const float w = (hit ? 1.0f : 0.0f) * (t[0] * (float)(num * ray.g));
+        N += w;
 #pragma unroll
-          for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch]);
-          const bool rec = hit && need;
-          if (ballot64(rec)) {                     // most entries record nothing
+        for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch]);
+        if constexpr (decltype(REC)::value) {
+          const bool rec = hit & need;
+          if (ballot64(rec)) {                   // most entries record nothing
             if (rec) {
               my_top[ntop] = (int)(b + (uint32_t)idx);
               ntop++;
@@ -108,7 +113,27 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
             }
           }
         }
+      }
+    };
+    if (ballot64(active)) {
+      bool recording = ballot64(need && active) != 0;
+      const int cnt4 = cnt & ~3;
+      int k = 0;
+      for (; k < cnt4; k += 4) {
+        const uint32_t four =
+            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(&s_l.idx[wq][k]));
+        if (recording) {
+          four_entries(std::true_type{}, std::true_type{}, k, four);
+          recording = ballot64(need && active) != 0;
+        } else {
+          four_entries(std::false_type{}, std::true_type{}, k, four);
+        }
         if (ballot64(active) == 0) break;
+      }
+      if (k == cnt4 && k < cnt && ballot64(active)) {     // the last one to three entries
+        const uint32_t four =
+            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(&s_l.idx[wq][k]));
+        four_entries(std::true_type{}, std::false_type{}, k, four);
       }
     }
     if (__syncthreads_count(active) == 0) break;
