@@ -36,11 +36,11 @@ OPS_PER_HIT_BASE = 5          # + one fma per channel
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 252952245
+FWD_TRAFFIC_BYTES = 253037331
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
-FWD_TRAFFIC_SHA256 = "be139fb4bf9092e486fedd85c1818dfc8884729a7d48e04648f375b17a4a8a5c"
+FWD_TRAFFIC_SHA256 = "f15d74addaf777817dce49d85d46e3e24ebe58a72dd56ef974bf15d17bcf798f"
 # Algorithmic HBM bytes of the projection and binning stages:
 #   projection: per primitive read position, radius, opacity (20 B), write the
 #     bin, draw and aux records and the pair count (16 + 64 + 32 + 4 B)
