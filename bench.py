@@ -1,6 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the sphere rasterizer: Mpixels/s forward + backward at one
-million spheres, 1024x1024, one GPU.
+million spheres, 1024x1024, one GPU (the default workload). --workload k runs
+the same protocol on another of the five synthetic workloads, with the pixel
+count summed over its views.
 
 A step is one pass of the whole path on resident inputs: splat_project,
 splat_bin_sort, splat_render_fwd, splat_render_bwd (compositor backward,
@@ -63,7 +65,17 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run three plain device copies of this many MiB (read + write of a "
                          "known size, to scale hardware byte counters)")
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="1: 4096 screen-space Gaussians 128x128; 2: 100k 3D Gaussians 512x512; 3: 1M spheres "
+                         "1024x1024 (default, the headline metric); 4: 2M Gaussians 1920x1080, 32 channels; "
+                         "5: the same scene from 6 cameras 1280x720 and a 2048x64 lidar view")
+    ap.add_argument("--hbm-copy", action="store_true",
+                    help="also time a plain 1 GiB device copy and report the measured HBM bandwidth")
     return ap.parse_args()
+
+
+WORKLOAD_NAMES = {1: "gauss2d_4096_128x128", 2: "gauss3d_100k_512x512", 3: "spheres_1m_1024x1024",
+                  4: "gauss3d_2m_1920x1080_c32", 5: "gauss3d_2m_6x1280x720_lidar_2048x64"}
 
 
 def main():
@@ -80,13 +92,24 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    scene = S.pulsar_spheres()
-    W, H = scene.cams[0].width, scene.cams[0].height
+    wl = args.workload
+    scene = S.make_config(wl)
+    pixels = sum(c.width * c.height for c in scene.cams)
     rz = Rasterizer(scene, device=dev)
     rz.forward(check=True)                       # sizes the pair buffers once
-    g_np = S.upstream_grads(scene, 103)
+    g_np = S.upstream_grads(scene, S.CONFIGS[wl]["grad_seed"])
     dimg = torch.from_numpy(np.concatenate([g.reshape(-1) for g in g_np])).to(dev)
-    grads = rz.alloc_grads(("pos", "scale", "opacity", "feat", "cam_R", "cam_t"))
+    want = ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t")
+    grads = rz.alloc_grads(want)
+    # camera and lidar views go through separate backward calls
+    groups, v = [], 0
+    while v < rz.V:
+        kind = scene.cams[v].kind
+        e = v
+        while e < rz.V and scene.cams[e].kind == kind:
+            e += 1
+        groups.append((v, e - v))
+        v = e
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -101,7 +124,8 @@ def main():
         rz.render_fwd()
         if ev is not None:
             ev[3].record()
-        rz.backward(dimg, grads=grads)
+        for gi, (b, cnt) in enumerate(groups):
+            rz.backward(dimg, grads=grads, view_begin=b, view_count=cnt, accumulate=gi > 0)
         if ev is not None:
             ev[4].record()
 
@@ -128,7 +152,6 @@ def main():
     stages = ["project", "bin_sort", "render_fwd", "render_bwd"]
     st_ms = {s: float(np.median([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
              for i, s in enumerate(stages)}
-    pixels = W * H
     value = pixels / (ms / 1e3) / 1e6
     npairs = int(rz.num_pairs.item())
 
@@ -137,18 +160,41 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "spheres_1m_1024x1024", "primitives": scene.n, "width": W, "height": H,
-                   "channels": scene.channels, "views": 1, "pairs": npairs},
+        "config": {"workload": WORKLOAD_NAMES[wl], "primitives": scene.n,
+                   "width": scene.cams[0].width, "height": scene.cams[0].height, "pixels": pixels,
+                   "channels": scene.channels, "views": rz.V, "pairs": npairs},
         "stage_ms": {k: round(v, 4) for k, v in st_ms.items()},
     }
 
+    if wl != 3:
+        out["metric"] = f"Mpixels/s fwd+bwd, {WORKLOAD_NAMES[wl]}"
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl == 3:
         cpu = cpu_baseline(scene, g_np, args.cpu_sample_rows)
         out["cpu_baseline"] = cpu["json"]
-    out["roofline"] = roofline(st_ms, cpu, scene)
-    out["stage_hbm"] = stage_hbm(st_ms, scene.n, npairs)
+    if wl == 3:
+        out["roofline"] = roofline(st_ms, cpu, scene)
+        out["stage_hbm"] = stage_hbm(st_ms, scene.n, npairs)
+    if args.hbm_copy:
+        out["hbm_copy_GBps"] = hbm_copy(torch, dev)
     print(json.dumps(out), flush=True)
+
+
+def hbm_copy(torch, dev, mib=1024, reps=10):
+    """Measured HBM bandwidth of a plain device copy (bytes read + written / time)."""
+    nf = mib * (1 << 20) // 4
+    src = torch.ones(nf, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    return round(2 * nf * 4 / sec / 1e9, 1)
 
 
 def sources_digest(paths):
