@@ -25,8 +25,12 @@
 //   k_tscatter                    each pair's word into its tile's segment, at
 //                                 tile start + chunk prefix + a rank from an LDS
 //                                 atomic
-//   k_seg_sort                    every segment sorted on its own: by one wave
-//                                 up to SEG_WAVE pairs, by a workgroup beyond
+//   k_seg_sort                    segments up to SEG_WAVE pairs: one wave each,
+//                                 bitonic in registers and lane shuffles
+//   k_seg_long                    longer segments from a work queue, one
+//                                 workgroup each: merge sort in LDS up to NV
+//                                 pairs, an MSD split into LDS-sized buckets
+//                                 beyond
 // No global atomics on the counting path: device-wide atomics on a few thousand
 // tile counters serialise. Views with more tiles than LDS_TILES take a fallback
 // (k_tile_count, k_bucket) with global atomic counters and cursors; more than
@@ -37,10 +41,6 @@
 namespace {
 
 constexpr int SCAN_BLOCK = 256;
-constexpr int RADIX = 256;
-constexpr int SEG_SMALL = 2048;     // largest segment sorted in LDS
-constexpr int BIG_ROUNDS = 8;       // items per thread per chunk of the big-segment sort
-constexpr int BIG_CHUNK = SCAN_BLOCK * BIG_ROUNDS;
 constexpr int TH_THREADS = 512;     // workgroup of the counting passes
 constexpr int TH_RPT = 8;           // records per thread in the counting passes
 constexpr int TH_CHUNK = TH_THREADS * TH_RPT;
@@ -48,6 +48,12 @@ constexpr int SEG_WAVE = 512;       // segments up to this length: one wave sort
 constexpr int TILE_SCAN1_MAX = 1 << 16;   // tiles scanned by a single workgroup
 constexpr int LDS_TILES = 16384;    // tiles of one view held as LDS counters (64 KiB)
 constexpr int COL_ROWS = 16;        // matrix rows (chunks) per thread in the column scan
+constexpr int LT = 512;             // threads of the long-segment sort
+constexpr int LE = 16;              // words per thread in the long-segment sort
+constexpr int NV = LT * LE;         // words one workgroup sorts in LDS (64 KiB)
+constexpr int NV_PHYS = NV + NV / LE;   // one pad word after every LE words
+constexpr int MAXLVL = 8;           // MSD split levels (8 bits of the word range each)
+constexpr int LONG_GRID = 512;      // workgroups of the long-segment sort (two per CU)
 
 // Block-wide exclusive scan of one value per thread (256 threads); returns the
 // exclusive prefix and writes the block total to *total.
@@ -147,14 +153,30 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_scan_top(unsigned long long *blo
     const int of = carry > (unsigned long long)capacity ? 1 : 0;
     *overflow = of;
     live[0] = of ? 0u : (uint32_t)carry;
+    live[1] = live[2] = live[3] = 0u;          // long-segment lists, filled by k_tile_ranges
   }
+}
+
+// Append tile t to a work list when p holds: one global atomic per wave.
+__device__ __forceinline__ void list_append(uint32_t *list, uint32_t *count, bool p, uint32_t t) {
+  const uint64_t m = ballot64(p);
+  if (m == 0) return;
+  const unsigned lane = lane_id();
+  const int leader = __builtin_ffsll((long long)m) - 1;
+  uint32_t base = 0;
+  if ((int)lane == leader) base = atomicAdd(count, (uint32_t)__popcll(m));
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+  if (p) list[base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = t;
 }
 
 // Per tile: [start, end) (0, 0 when empty) and the bucket cursor (in place of the count).
 // Without overflow every prefix is below the capacity (< 2^32).
+// Tiles with more than SEG_WAVE pairs also go on the work lists of the
+// long-segment sort (unordered here): list[0..) those above NV, list[m..) the rest.
 __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_ranges(uint32_t *cnt_cursor, long long m,
                                                              const unsigned long long *block_sums,
-                                                             const int32_t *overflow, uint32_t *ranges) {
+                                                             const int32_t *overflow, uint32_t *ranges,
+                                                             uint32_t *live, uint32_t *list) {
   if (*overflow) return;
   const long long t = (long long)blockIdx.x * SCAN_BLOCK + threadIdx.x;
   const uint32_t c = t < m ? cnt_cursor[t] : 0u;
@@ -165,13 +187,19 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_ranges(uint32_t *cnt_cursor
     ranges[2 * t] = c ? start : 0u;
     ranges[2 * t + 1] = c ? start + c : 0u;
   }
+  list_append(list, &live[1], c > (uint32_t)NV, (uint32_t)t);
+  list_append(list + m, &live[2], c > (uint32_t)SEG_WAVE && c <= (uint32_t)NV, (uint32_t)t);
 }
 
 // Single workgroup, up to TILE_SCAN1_MAX tiles: pair total, overflow flag and
 // live count first, then, without overflow, the exclusive scan that writes the
 // tile ranges and turns the counts into tile starts. Every thread owns
 // TOP_ITEMS consecutive tiles per round; up to SCAN_BLOCK * TOP_ITEMS tiles in all
-// keep their counts in registers between the two phases.
+// keep their counts in registers between the two phases. The same scan (three
+// fields packed in one 64-bit value) lists the tiles for the long-segment sort:
+// list[0..) those with more than NV pairs in tile order, list[m..) those with
+// SEG_WAVE < pairs <= NV; live[1], live[2] count them, live[3] = 0 is the queue
+// head.
 __device__ __forceinline__ void load_counts(const uint32_t *cnt, int m, int t0, uint32_t (&x)[TOP_ITEMS]) {
 #pragma unroll
   for (int r = 0; r < TOP_ITEMS; r++) x[r] = t0 + r < m ? cnt[t0 + r] : 0u;
@@ -179,7 +207,7 @@ __device__ __forceinline__ void load_counts(const uint32_t *cnt, int m, int t0, 
 
 __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_scan1(uint32_t *cnt_start, int m, long long capacity,
                                                             int64_t *num_pairs, int32_t *overflow, uint32_t *live,
-                                                            uint32_t *ranges) {
+                                                            uint32_t *ranges, uint32_t *list) {
   __shared__ int s_of;
   constexpr int ROUND = SCAN_BLOCK * TOP_ITEMS;
   uint32_t x[TOP_ITEMS];
@@ -200,25 +228,46 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_scan1(uint32_t *cnt_start, 
   }
   __syncthreads();
   if (s_of) return;
-  uint32_t carry = 0;                          // below the capacity (< 2^32) from here on
+  // below the capacity (< 2^32) from here on; the list counts of one round are
+  // at most ROUND < 2^16, so the packed fields never carry into each other
+  uint32_t carry = 0, carry_h = 0, carry_m = 0;
   for (int base = 0; base < m; base += ROUND) {
     const int t0 = base + (int)threadIdx.x * TOP_ITEMS;
     if (m > ROUND) load_counts(cnt_start, m, t0, x);   // one round: still in registers
-    uint32_t sum = 0;
+    uint32_t sum = 0, nh = 0, nm = 0;
 #pragma unroll
-    for (int r = 0; r < TOP_ITEMS; r++) sum += x[r];
-    uint32_t tot;
-    uint32_t run = carry + block_exclusive_scan<uint32_t>(sum, &tot);
+    for (int r = 0; r < TOP_ITEMS; r++) {
+      sum += x[r];
+      nh += x[r] > (uint32_t)NV ? 1u : 0u;
+      nm += (x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV) ? 1u : 0u;
+    }
+    const unsigned long long packed =
+        (unsigned long long)sum | ((unsigned long long)nh << 32) | ((unsigned long long)nm << 48);
+    unsigned long long tot;
+    const unsigned long long pre = block_exclusive_scan<unsigned long long>(packed, &tot);
+    uint32_t run = carry + (uint32_t)pre;
+    uint32_t ph = carry_h + (uint32_t)((pre >> 32) & 0xffffu), pm = carry_m + (uint32_t)(pre >> 48);
 #pragma unroll
     for (int r = 0; r < TOP_ITEMS; r++) {
       if (t0 + r < m) {
         cnt_start[t0 + r] = run;
         ranges[2 * (t0 + r)] = x[r] ? run : 0u;
         ranges[2 * (t0 + r) + 1] = x[r] ? run + x[r] : 0u;
+        if (x[r] > (uint32_t)NV)
+          list[ph++] = (uint32_t)(t0 + r);
+        else if (x[r] > (uint32_t)SEG_WAVE)
+          list[m + pm++] = (uint32_t)(t0 + r);
       }
       run += x[r];
     }
-    carry += tot;
+    carry += (uint32_t)tot;
+    carry_h += (uint32_t)((tot >> 32) & 0xffffu);
+    carry_m += (uint32_t)(tot >> 48);
+  }
+  if (threadIdx.x == 0) {
+    live[1] = carry_h;
+    live[2] = carry_m;
+    live[3] = 0u;
   }
 }
 
@@ -431,149 +480,299 @@ __device__ void bitonic_regs(uint64_t (&e)[E], uint32_t P, uint32_t base, uint64
   }
 }
 
-template <int E>
-__device__ __forceinline__ void sort_small(const uint64_t *words, uint64_t *keys, uint32_t *vals, uint32_t start,
-                                           uint32_t len, uint32_t P, uint32_t tile, uint64_t *s) {
-  const uint32_t base = threadIdx.x * E;
-  uint64_t e[E];
-#pragma unroll
-  for (int a = 0; a < E; a++) e[a] = base + a < len ? words[start + base + a] : ~0ull;
-  bitonic_regs<E>(e, P, base, s);
-#pragma unroll
-  for (int a = 0; a < E; a++)
-    if (base + a < len) write_pair(keys, vals, start + base + a, tile, e[a]);
-}
-
-// Stable LSD radix sort of one long segment by the whole workgroup, 8 bits per
-// pass, through global memory (ping-pong between the bucket array and the
-// caller's key array), then the final key/value pairs. Passes over bytes that
-// are equal in every word of the segment are skipped. Within a pass the segment
-// goes in chunks of BIG_CHUNK; ranks inside a wave come from 8 ballots, across
-// waves from LDS counters.
-__device__ void seg_radix_block(uint64_t *words, uint64_t *keys, uint32_t *vals, uint32_t tile, uint32_t start,
-                                uint32_t len) {
-  __shared__ uint32_t s_hist[RADIX];
-  __shared__ uint32_t s_off[RADIX];
-  __shared__ uint32_t s_wcnt[SCAN_BLOCK / WAVE][RADIX];
-  __shared__ unsigned long long s_and, s_or;
-  const unsigned tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-  uint64_t *src = words + start, *dst = keys + start;
-  // bytes that vary across the segment
-  uint64_t va = ~0ull, vo = 0ull;
-  for (uint32_t i = tid; i < len; i += SCAN_BLOCK) {
-    const uint64_t x = src[i];
-    va &= x;
-    vo |= x;
-  }
-  if (tid == 0) {
-    s_and = ~0ull;
-    s_or = 0ull;
-  }
-  __syncthreads();
-  atomicAnd(&s_and, (unsigned long long)va);
-  atomicOr(&s_or, (unsigned long long)vo);
-  __syncthreads();
-  const uint64_t vary = s_and ^ s_or;
-  __syncthreads();
-  for (int shift = 0; shift < 64; shift += 8) {
-    if (((vary >> shift) & 0xffull) == 0) continue;      // uniform over the workgroup
-    s_hist[tid] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < len; i += SCAN_BLOCK) atomicAdd(&s_hist[(unsigned)(src[i] >> shift) & (RADIX - 1)], 1u);
-    __syncthreads();
-    uint32_t tot;
-    s_off[tid] = block_exclusive_scan<uint32_t>(s_hist[tid], &tot);
-#pragma unroll
-    for (int q = 0; q < SCAN_BLOCK / WAVE; q++) s_wcnt[q][tid] = 0;
-    __syncthreads();
-    for (uint32_t base = 0; base < len; base += BIG_CHUNK) {
-      uint64_t x[BIG_ROUNDS];
-#pragma unroll
-      for (int r = 0; r < BIG_ROUNDS; r++) {
-        const uint32_t i = base + r * SCAN_BLOCK + tid;
-        x[r] = i < len ? src[i] : 0ull;
-      }
-#pragma unroll
-      for (int r = 0; r < BIG_ROUNDS; r++) {
-        const bool valid = base + r * SCAN_BLOCK + tid < len;
-        const unsigned d = (unsigned)(x[r] >> shift) & (RADIX - 1);
-        uint64_t peers = ballot64(valid);
-#pragma unroll
-        for (int bit = 0; bit < 8; bit++) {
-          const bool on = (d >> bit) & 1u;
-          const uint64_t m = ballot64(on);
-          peers &= on ? m : ~m;
-        }
-        const unsigned rank = __popcll(peers & below);
-        if (valid && rank == 0) s_wcnt[w][d] = __popcll(peers);
-        __syncthreads();
-        if (valid) {
-          uint32_t off = s_off[d] + rank;
-          for (unsigned q = 0; q < w; q++) off += s_wcnt[q][d];
-          dst[off] = x[r];
-        }
-        __syncthreads();
-        uint32_t add = 0;
-#pragma unroll
-        for (int q = 0; q < SCAN_BLOCK / WAVE; q++) {
-          add += s_wcnt[q][tid];
-          s_wcnt[q][tid] = 0;
-        }
-        s_off[tid] += add;
-        __syncthreads();
-      }
-    }
-    uint64_t *t = src;
-    src = dst;
-    dst = t;
-  }
-  // src holds the sorted words (in the key array or the bucket array)
-  for (uint32_t i = tid; i < len; i += SCAN_BLOCK) write_pair(keys, vals, start + i, tile, src[i]);
-}
-
-// Segment sorts, four tiles per workgroup. A wave sorts its own tile when the
-// segment has at most SEG_WAVE pairs: bitonic with eight words per lane, the
-// rest of the network through lane shuffles (no LDS, no barriers). Longer
-// segments are then taken by the whole workgroup one after another: bitonic
-// over registers, shuffles and LDS (padded to a power of two with all-ones
-// words, which sort last) up to SEG_SMALL pairs, the radix sort beyond.
-__global__ __launch_bounds__(256) void k_seg_sort(const uint32_t *ranges, uint64_t *words, const int32_t *overflow,
-                                                   uint64_t *keys, uint32_t *vals, int tiles) {
-  __shared__ uint64_t s[SEG_SMALL];
+// Segments of at most SEG_WAVE pairs: one wave per tile, four tiles per
+// workgroup, bitonic with eight words per lane and the rest of the network
+// through lane shuffles (no LDS, no barriers).
+__global__ __launch_bounds__(256) void k_seg_sort(const uint32_t *ranges, const uint64_t *words,
+                                                   const int32_t *overflow, uint64_t *keys, uint32_t *vals, int tiles) {
   if (*overflow) return;
   const unsigned lane = lane_id();
   const int own = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  if (own < tiles) {
-    const uint32_t start = ranges[2 * own], len = ranges[2 * own + 1] - start;
-    if (len > 0 && len <= SEG_WAVE) {
-      uint32_t P = 2;
-      while (P < len) P <<= 1;
-      const uint32_t base = lane * 8;
-      uint64_t e[8];
+  if (own >= tiles) return;
+  const uint32_t start = ranges[2 * own], len = ranges[2 * own + 1] - start;
+  if (len == 0 || len > SEG_WAVE) return;
+  uint32_t P = 2;
+  while (P < len) P <<= 1;
+  const uint32_t base = lane * 8;
+  uint64_t e[8];
 #pragma unroll
-      for (int a = 0; a < 8; a++) e[a] = base + a < len ? words[start + base + a] : ~0ull;
-      bitonic_regs<8>(e, P, base, s);          // P <= 64 * 8: never reaches the LDS stages
+  for (int a = 0; a < 8; a++) e[a] = base + a < len ? words[start + base + a] : ~0ull;
+  bitonic_regs<8>(e, P, base, nullptr);        // P <= 64 * 8: never reaches the LDS stages
 #pragma unroll
-      for (int a = 0; a < 8; a++)
-        if (base + a < len) write_pair(keys, vals, start + base + a, (uint32_t)own, e[a]);
+  for (int a = 0; a < 8; a++)
+    if (base + a < len) write_pair(keys, vals, start + base + a, (uint32_t)own, e[a]);
+}
+
+// ---- long segments: merge sort in LDS, MSD split beyond NV -----------------------
+
+// LDS slot of word x of the sort buffer: one pad word after every LE words, so
+// that a thread's LE consecutive words start LE + 1 words after the previous
+// thread's and the blocked reads and writes spread over the banks.
+__device__ __forceinline__ int lslot(int x) { return x + x / LE; }
+
+// Ascending sort of one thread's LE words: bitonic network, every index and
+// direction known at compile time (80 compare-exchanges).
+__device__ __forceinline__ void sort_regs(uint64_t (&e)[LE]) {
+#pragma unroll
+  for (int k = 2; k <= LE; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (int a = 0; a < LE; a++) {
+        if (a & j) continue;
+        const int b = a | j;
+        const bool up = (a & k) == 0;
+        const uint64_t x = e[a], y = e[b];
+        const bool sw = up ? (y < x) : (x < y);
+        e[a] = sw ? y : x;
+        e[b] = sw ? x : y;
+      }
     }
   }
-  for (int q = 0; q < 4; q++) {
-    const int t = (int)blockIdx.x * 4 + q;
-    if (t >= tiles) break;
-    const uint32_t start = ranges[2 * t], len = ranges[2 * t + 1] - start;
-    if (len <= SEG_WAVE) continue;
-    __syncthreads();                           // LDS reuse between tiles
-    if (len <= SEG_SMALL) {
-      uint32_t P = 2;
-      while (P < len) P <<= 1;
-      if (P == 1024)
-        sort_small<4>(words, keys, vals, start, len, P, (uint32_t)t, s);
-      else
-        sort_small<8>(words, keys, vals, start, len, P, (uint32_t)t, s);
-    } else {
-      seg_radix_block(words, keys, vals, (uint32_t)t, start, len);
+}
+
+// One merge round: the LE outputs from position o of the merge of the two
+// sorted runs of length R that contain o (the second run may be short or
+// empty). The split of the outputs between the runs comes from a binary search
+// along the cross diagonal (merge path); ties go to the first run, and the
+// only equal words are the all-ones padding, so every thread's split agrees
+// with its neighbours'. An exhausted run reads as all-ones.
+__device__ __forceinline__ void merge_round(const uint64_t *s, int R, int npad, int o, uint64_t (&e)[LE]) {
+  const int a0 = o & ~(2 * R - 1), b0 = a0 + R;
+  const int alen = min(R, npad - a0), blen = max(0, min(R, npad - b0));
+  const int diag = o - a0;
+  int lo = max(0, diag - blen), hi = min(diag, alen);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s[lslot(a0 + mid)] <= s[lslot(b0 + diag - 1 - mid)])
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  int ia = a0 + lo, ib = b0 + diag - lo;
+  const int ea = a0 + alen, eb = b0 + blen;
+  uint64_t a = s[lslot(min(ia, NV - 1))], b = s[lslot(min(ib, NV - 1))];
+  a = ia < ea ? a : ~0ull;
+  b = ib < eb ? b : ~0ull;
+#pragma unroll
+  for (int k = 0; k < LE; k++) {
+    const bool ta = a <= b;
+    e[k] = ta ? a : b;
+    if (k == LE - 1) break;
+    ia += ta ? 1 : 0;
+    ib += ta ? 0 : 1;
+    const int nx = ta ? ia : ib;
+    const bool ok = nx < (ta ? ea : eb);
+    uint64_t x = s[lslot(min(nx, NV - 1))];
+    x = ok ? x : ~0ull;
+    a = ta ? x : a;
+    b = ta ? b : x;
+  }
+}
+
+// Sort len <= NV words of global memory in LDS by the whole workgroup and
+// write the final (tile << 32 | depth bits, record) pairs. The words are padded
+// to a multiple of LE with all-ones words (they sort last and are not written);
+// every thread sorts its LE words in registers, then runs of LE, 2 LE, ... are
+// merged pairwise until one run remains.
+__device__ void lds_sort(const uint64_t *src, int len, uint64_t *kout, uint32_t *vout, uint32_t tile, uint64_t *s) {
+  const int tid = (int)threadIdx.x;
+  const int npad = (len + LE - 1) & ~(LE - 1);
+  uint64_t e[LE];
+#pragma unroll
+  for (int r = 0; r < LE; r++) {
+    const int i = r * LT + tid;
+    e[r] = i < len ? src[i] : ~0ull;
+  }
+  __syncthreads();                                   // earlier readers of s are done
+#pragma unroll
+  for (int r = 0; r < LE; r++) {
+    const int i = r * LT + tid;
+    if (i < npad) s[lslot(i)] = e[r];
+  }
+  __syncthreads();
+  const int o = tid * LE;
+  const bool act = o < npad;
+  if (act) {
+#pragma unroll
+    for (int k = 0; k < LE; k++) e[k] = s[tid * (LE + 1) + k];
+    sort_regs(e);
+  }
+  for (int R = LE; R < npad; R <<= 1) {
+    __syncthreads();
+    if (act) {
+#pragma unroll
+      for (int k = 0; k < LE; k++) s[tid * (LE + 1) + k] = e[k];
+    }
+    __syncthreads();
+    if (act) merge_round(s, R, npad, o, e);
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int k = 0; k < LE; k++) s[tid * (LE + 1) + k] = e[k];
+  }
+  __syncthreads();
+  for (int i = tid; i < len; i += LT) {
+    const uint64_t w = s[lslot(i)];
+    kout[i] = ((uint64_t)tile << 32) | (w >> 32);
+    vout[i] = (uint32_t)w;
+  }
+}
+
+struct SplitLds {
+  uint32_t off[MAXLVL][257];       // bucket starts of each open level (tile-relative), [256] = end
+  uint32_t cur[256];               // histogram, then scatter cursors
+  uint32_t wsum[4];
+  unsigned long long mm[2];        // segment minimum and maximum
+  int next[MAXLVL];                // first bucket still to visit on each open level
+  int item;
+};
+
+// MSD split of src[0, len) into dst[0, len): bucket b holds the words whose
+// offset from the minimum has b as its top 8 bits (of the offset range's bit
+// length), so buckets are in value order and each spans less than 2^(bits-8).
+// off[b] = base + start of bucket b, off[256] = base + len.
+__device__ void msd_split(const uint64_t *src, uint64_t *dst, int len, uint32_t base, uint32_t *off, SplitLds &sl) {
+  const int tid = (int)threadIdx.x;
+  const unsigned lane = (unsigned)tid & (WAVE - 1);
+  uint64_t mn = ~0ull, mx = 0ull;
+  for (int i0 = 0; i0 < len; i0 += 4 * LT) {
+    uint64_t x[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int i = i0 + r * LT + tid;
+      x[r] = i < len ? src[i] : ~0ull;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int i = i0 + r * LT + tid;
+      mn = x[r] < mn ? x[r] : mn;
+      mx = (i < len) & (x[r] > mx) ? x[r] : mx;
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const uint64_t a = __shfl_xor(mn, d, WAVE), b = __shfl_xor(mx, d, WAVE);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  __syncthreads();                                   // earlier readers of sl are done
+  if (tid == 0) {
+    sl.mm[0] = ~0ull;
+    sl.mm[1] = 0ull;
+  }
+  if (tid < 256) sl.cur[tid] = 0u;
+  __syncthreads();
+  if (lane == 0) {
+    atomicMin(&sl.mm[0], (unsigned long long)mn);
+    atomicMax(&sl.mm[1], (unsigned long long)mx);
+  }
+  __syncthreads();
+  const uint64_t lo = sl.mm[0], range = sl.mm[1] - lo;
+  const int bits = range ? 64 - __clzll((long long)range) : 0;
+  const int sh = bits > 8 ? bits - 8 : 0;
+  for (int i0 = 0; i0 < len; i0 += 4 * LT) {
+    uint64_t x[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int i = i0 + r * LT + tid;
+      x[r] = i < len ? src[i] : lo;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      if (i0 + r * LT + tid < len) atomicAdd(&sl.cur[(unsigned)((x[r] - lo) >> sh)], 1u);
+  }
+  __syncthreads();
+  // exclusive scan of the 256 counts by threads 0..255
+  const uint32_t c = tid < 256 ? sl.cur[tid] : 0u;
+  uint32_t inc = c;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const uint32_t y = __shfl_up(inc, d, WAVE);
+    if (lane >= (unsigned)d) inc += y;
+  }
+  if (tid < 256 && lane == WAVE - 1) sl.wsum[tid / WAVE] = inc;
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t pre = inc - c;
+    for (int q = 0; q < tid / WAVE; q++) pre += sl.wsum[q];
+    off[tid] = base + pre;
+    sl.cur[tid] = pre;
+  }
+  if (tid == 0) off[256] = base + (uint32_t)len;
+  __syncthreads();
+  for (int i0 = 0; i0 < len; i0 += 4 * LT) {
+    uint64_t x[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int i = i0 + r * LT + tid;
+      x[r] = i < len ? src[i] : lo;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      if (i0 + r * LT + tid < len) dst[atomicAdd(&sl.cur[(unsigned)((x[r] - lo) >> sh)], 1u)] = x[r];
+  }
+  __builtin_amdgcn_s_waitcnt(0);                     // the scattered words are written
+  __syncthreads();                                   // before any thread reads them back
+}
+
+// Segments longer than SEG_WAVE, one workgroup per tile from a work queue (the
+// tiles above NV first). Up to NV pairs: lds_sort straight from the bucketed
+// words. Beyond: MSD split into the key array (used as scratch), then every run
+// of adjacent buckets that fits NV words is sorted as one segment; a bucket
+// above NV is split again into the bucketed-word array, and so on, alternating.
+// Words are unique, so the offset range loses 8 bits per level and a bucket on
+// level MAXLVL - 1 holds at most one word: the split never goes deeper.
+__global__ __launch_bounds__(LT) void k_seg_long(const uint32_t *ranges, uint64_t *words, const int32_t *overflow,
+                                                  uint64_t *keys, uint32_t *vals, uint32_t *live,
+                                                  const uint32_t *list, int tiles) {
+  __shared__ uint64_t s[NV_PHYS];
+  __shared__ SplitLds sl;
+  if (*overflow) return;
+  const int nh = (int)live[1], nall = nh + (int)live[2];
+  if (nall == 0) return;
+  const int tid = (int)threadIdx.x;
+  for (;;) {
+    __syncthreads();                                 // every thread has read sl.item
+    if (tid == 0) sl.item = (int)atomicAdd(&live[3], 1u);
+    __syncthreads();
+    const int item = sl.item;
+    if (item >= nall) break;
+    const uint32_t t = item < nh ? list[item] : list[tiles + item - nh];
+    const uint32_t start = ranges[2 * t];
+    const int len = (int)(ranges[2 * t + 1] - start);
+    uint64_t *W = words + start, *K = keys + start;
+    uint32_t *V = vals + start;
+    if (len <= NV) {
+      lds_sort(W, len, K, V, t, s);
+      continue;
+    }
+    msd_split(W, K, len, 0u, sl.off[0], sl);
+    int L = 0, b = 0;
+    for (;;) {
+      if (b >= 256) {
+        if (L == 0) break;
+        L--;
+        b = sl.next[L];
+        continue;
+      }
+      const uint64_t *buf = (L & 1) ? W : K;         // level L buckets: K when L is even
+      const uint32_t g0 = sl.off[L][b];
+      const uint32_t blen = sl.off[L][b + 1] - g0;
+      if (blen > (uint32_t)NV && L + 1 < MAXLVL) {
+        __syncthreads();                             // every thread has read sl.next
+        if (tid == 0) sl.next[L] = b + 1;
+        msd_split(buf + g0, ((L & 1) ? K : W) + g0, (int)blen, g0, sl.off[L + 1], sl);
+        L++;
+        b = 0;
+        continue;
+      }
+      int e = b + 1;
+      while (e < 256 && sl.off[L][e + 1] - g0 <= (uint32_t)NV) e++;
+      const int glen = (int)(sl.off[L][e] - g0);
+      if (glen > 0 && glen <= NV) lds_sort(buf + g0, glen, K + g0, V + g0, t, s);
+      b = e;
     }
   }
 }
@@ -582,7 +781,8 @@ struct SortWs {
   uint64_t *words;      // [capacity] bucketed (depth << 32 | record) words
   uint32_t *cursor;     // [tiles] counts, then tile starts (and cursors in the fallback)
   unsigned long long *block_sums;  // [ceil(tiles / 256) + 1]
-  uint32_t *live;       // [0] live pairs
+  uint32_t *live;       // [0] live pairs, [1] [2] long-segment list counts, [3] queue head
+  uint32_t *list;       // [2 * tiles] long-segment work lists
   uint32_t *mat;        // per-chunk tile counts (LDS counting path)
   uint32_t *colsum;     // [groups][tiles]
   size_t bytes;
@@ -623,6 +823,7 @@ SortWs sort_ws_layout(void *base, const ViewTable &vt, int n, long long capacity
   w.cursor = (uint32_t *)p;     p += proj_align(sizeof(uint32_t) * (size_t)tiles);
   w.block_sums = (unsigned long long *)p; p += proj_align(sizeof(unsigned long long) * (size_t)(nscan + 1));
   w.live = (uint32_t *)p;       p += proj_align(sizeof(uint32_t) * 4);
+  w.list = (uint32_t *)p;       p += proj_align(sizeof(uint32_t) * 2 * (size_t)tiles);
   w.mat = (uint32_t *)p;        p += proj_align(sizeof(uint32_t) * (size_t)cp.mat_elems);
   w.colsum = (uint32_t *)p;     p += proj_align(sizeof(uint32_t) * (size_t)(cp.lds ? cp.ngroups * tiles : 0));
   w.bytes = (size_t)(p - (char *)base);
@@ -663,13 +864,13 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
   }
   if (tiles <= TILE_SCAN1_MAX) {
     hipLaunchKernelGGL(k_tile_scan1, dim3(1), dim3(SCAN_BLOCK), 0, stream, ws.cursor, (int)tiles, capacity, num_pairs,
-                       overflow, ws.live, ranges);
+                       overflow, ws.live, ranges, ws.list);
   } else {
     hipLaunchKernelGGL(k_scan_reduce, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums);
     hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(SCAN_BLOCK), 0, stream, ws.block_sums, nscan, capacity, num_pairs,
                        overflow, ws.live);
     hipLaunchKernelGGL(k_tile_ranges, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums,
-                       overflow, ranges);
+                       overflow, ranges, ws.live, ws.list);
   }
   SPLAT_LAUNCH_CHECK();
   if (cp.lds) {
@@ -681,6 +882,8 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
   }
   hipLaunchKernelGGL(k_seg_sort, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream, ranges, ws.words, overflow,
                      keys, vals, (int)tiles);
+  hipLaunchKernelGGL(k_seg_long, dim3(LONG_GRID), dim3(LT), 0, stream, ranges, ws.words, overflow, keys, vals, ws.live,
+                     ws.list, (int)tiles);
   SPLAT_LAUNCH_CHECK();
   return SPLAT_OK;
 }

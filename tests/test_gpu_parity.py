@@ -70,6 +70,30 @@ def test_view_beyond_lds_counters():
     _run(sc, 10, "gauss3d 20k @2304x2048 (18432 tiles)")
 
 
+def test_tile_scan_beyond_one_workgroup():
+    """More than 65536 tiles (the three-kernel tile scan, long-segment work lists
+    filled with atomics) and a cluster of large Gaussians whose tiles hold up to
+    12k pairs (the MSD split ahead of the LDS merge sort). Binning is compared in
+    full, the image on a pixel sample around and away from the cluster."""
+    sc = S.gauss3d(seed=18, n=120_000, width=4160, height=4128)
+    c = sc.cams[0]
+    sc.cams = [S.Camera(S.CAM_PINHOLE, 4160, 4128, c.R, c.t, fx=1500.0, fy=1500.0, cx=2000.0, cy=2100.0,
+                        znear=0.2, zfar=1000.0)]
+    rng = np.random.default_rng(5)
+    k = 12_000
+    sc.pos[:k] = rng.normal(0.0, 0.4, size=(k, 3)).astype(np.float32)
+    sc.scale[:k] = np.float32(0.25)
+    _log(f"[case] gauss3d 120k @4160x4128 clustered (67080 tiles)")
+    rz = _rz(sc)
+    rz.forward()
+    orc = O.Oracle(sc)
+    prng = np.random.default_rng(6)
+    pix = np.concatenate([prng.choice(4160 * 4128, 20_000, replace=False),
+                          (2100 + prng.integers(-300, 300, 20_000)) * 4160 + 2000 + prng.integers(-300, 300, 20_000)])
+    st = compare_forward(rz, orc, pix=np.unique(pix).astype(np.int64))
+    _log(f"  fwd ok pairs={st.get('pairs')} img_err={st['img_err']:.2e} flagged={st['flag_frac']:.2e}")
+
+
 def test_multiview_with_lidar():
     """Two pinhole views and a spherical view in one call; camera and lidar backward
     run as separate calls that accumulate into the same gradients."""
