@@ -332,10 +332,127 @@ __device__ __forceinline__ void for_each_local_tile(const ViewDev &cv, const Bin
   }
 }
 
+// Pairs of one chunk. A record with at most LIGHT tiles is walked by the thread
+// that loaded it; the others are staged in LDS (HB per batch) and their pairs
+// are cut into equal contiguous slices, one per thread, so that a record that
+// covers thousands of tiles does not hold up its wave. f(local tile, record
+// slot in the chunk, depth key) is called once per pair.
+constexpr uint32_t LIGHT = 16;
+constexpr int HB = 512;
+
+struct HeavyLds {
+  uint32_t pre[HB + 1];      // first pair of each staged record (chunk pair stream); [nb] = end
+  uint32_t geo0[HB];         // tx0 | ntx << 16
+  uint32_t geo1[HB];         // ty0 | record slot << 16
+  uint32_t key[HB];
+  uint64_t wsum[TH_THREADS / WAVE];
+};
+
+template <typename F>
+__device__ __forceinline__ void chunk_pairs(const ViewDev &cv, const ChunkRecs &cr, HeavyLds &hl, F f) {
+  const int tid = (int)threadIdx.x;
+  const unsigned lane = (unsigned)tid & (WAVE - 1), w = (unsigned)tid / WAVE;
+  uint32_t nh = 0, np = 0;
+#pragma unroll      // constant indices keep the record arrays in registers
+  for (int r = 0; r < TH_RPT; r++) {
+    const uint32_t c = cr.cnt[r];
+    if (c > LIGHT) {
+      nh++;
+      np += c;
+    } else if (c) {
+      for_each_local_tile(cv, cr.b[r], [&](uint32_t lt) { f(lt, (uint32_t)(r * TH_THREADS + tid), cr.b[r].key); });
+    }
+  }
+  // exclusive scan of (pairs | records << 40) over the workgroup
+  const uint64_t x = (uint64_t)np | ((uint64_t)nh << 40);
+  uint64_t inc = x;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const uint64_t y = __shfl_up(inc, d, WAVE);
+    if (lane >= (unsigned)d) inc += y;
+  }
+  if (lane == WAVE - 1) hl.wsum[w] = inc;
+  __syncthreads();
+  uint64_t pre = inc - x, tot = 0;
+#pragma unroll
+  for (int q = 0; q < TH_THREADS / WAVE; q++) {
+    const uint64_t t = hl.wsum[q];
+    pre += (unsigned)q < w ? t : 0ull;
+    tot += t;
+  }
+  const uint32_t NP = (uint32_t)(tot & ((1ull << 40) - 1)), NH = (uint32_t)(tot >> 40);
+  const uint32_t pbase = (uint32_t)(pre & ((1ull << 40) - 1)), hbase = (uint32_t)(pre >> 40);
+  for (uint32_t b0 = 0; b0 < NH; b0 += HB) {
+    __syncthreads();                                 // readers of the previous batch are done
+    uint32_t e = hbase, q = pbase;
+#pragma unroll
+    for (int r = 0; r < TH_RPT; r++) {
+      if (cr.cnt[r] > LIGHT) {
+        if (e >= b0 && e < b0 + HB) {
+          const uint32_t i = e - b0;
+          hl.pre[i] = q;
+          hl.geo0[i] = (uint32_t)cr.b[r].tx0 | ((uint32_t)cr.b[r].ntx << 16);
+          hl.geo1[i] = (uint32_t)cr.b[r].ty0 | ((uint32_t)(r * TH_THREADS + tid) << 16);
+          hl.key[i] = cr.b[r].key;
+        }
+        if (e == b0 + HB) hl.pre[HB] = q;
+        e++;
+        q += cr.cnt[r];
+      }
+    }
+    const int nb = (int)min((uint32_t)HB, NH - b0);
+    if (b0 + HB >= NH && tid == 0) hl.pre[nb] = NP;
+    __syncthreads();
+    const uint32_t q_lo = hl.pre[0], q_hi = hl.pre[nb];
+    const uint32_t per = (q_hi - q_lo + TH_THREADS - 1) / TH_THREADS;
+    const uint32_t q0 = q_lo + (uint32_t)tid * per, q1 = min(q0 + per, q_hi);
+    if (q0 >= q1) continue;
+    int lo = 0, hi = nb - 1;                          // last staged record starting at or before q0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (hl.pre[mid] <= q0)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    int i = lo;
+    uint32_t g0 = hl.geo0[i], g1 = hl.geo1[i], key = hl.key[i];
+    uint32_t rem = hl.pre[i + 1] - q0;               // pairs left in record i
+    uint32_t ntx = g0 >> 16, k = q0 - hl.pre[i];
+    uint32_t row = k / ntx, col = k - row * ntx;
+    int tx = (int)(g0 & 0xffffu) + (int)col;
+    if (tx >= cv.TW) tx -= cv.TW;
+    int ty = (int)(g1 & 0xffffu) + (int)row;
+    for (uint32_t qq = q0; qq < q1; qq++) {
+      f((uint32_t)(ty * cv.TW + tx), g1 >> 16, key);
+      if (--rem == 0) {
+        i = min(i + 1, nb - 1);
+        g0 = hl.geo0[i];
+        g1 = hl.geo1[i];
+        key = hl.key[i];
+        rem = hl.pre[i + 1] - hl.pre[i];
+        ntx = g0 >> 16;
+        col = 0;
+        tx = (int)(g0 & 0xffffu);
+        ty = (int)(g1 & 0xffffu);
+      } else {
+        col++;
+        if (++tx == cv.TW) tx = 0;
+        if (col == ntx) {
+          col = 0;
+          tx = (int)(g0 & 0xffffu);
+          ty++;
+        }
+      }
+    }
+  }
+}
+
 // grid: n_views * nchunk workgroups of TH_THREADS; dynamic LDS: 4 * max tiles per view.
 __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
                                                 const uint32_t *counts, uint32_t *M) {
   extern __shared__ uint32_t s_cnt[];
+  __shared__ HeavyLds hl;
   const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
   const ViewDev &cv = vt.v[v];
   const int T = cv.TW * cv.TH;
@@ -344,9 +461,7 @@ __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt,
   const int nvalid = min(TH_CHUNK, n - chunk * TH_CHUNK);
   load_chunk(bin, counts, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);
   __syncthreads();
-#pragma unroll      // constant indices keep the record arrays in registers
-  for (int r = 0; r < TH_RPT; r++)
-    if (cr.cnt[r]) for_each_local_tile(cv, cr.b[r], [&](uint32_t lt) { atomicAdd(&s_cnt[lt], 1u); });
+  chunk_pairs(cv, cr, hl, [&](uint32_t lt, uint32_t, uint32_t) { atomicAdd(&s_cnt[lt], 1u); });
   __syncthreads();
   uint32_t *row = M + mat_index(mt, cv, v, chunk, 0);
   for (int t = threadIdx.x; t < T; t += TH_THREADS) row[t] = s_cnt[t];
@@ -398,6 +513,7 @@ __global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable 
                                                    const uint32_t *tile_start, const int32_t *overflow,
                                                    uint64_t *words) {
   extern __shared__ uint32_t s_base[];
+  __shared__ HeavyLds hl;
   if (*overflow) return;
   const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
   const ViewDev &cv = vt.v[v];
@@ -408,12 +524,9 @@ __global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable 
   const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
   load_chunk(bin, counts, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
   __syncthreads();
-#pragma unroll      // constant indices keep the record arrays in registers
-  for (int r = 0; r < TH_RPT; r++) {
-    if (!cr.cnt[r]) continue;
-    const uint64_t w = ((uint64_t)cr.b[r].key << 32) | (uint64_t)(uint32_t)(rec0 + r * TH_THREADS + threadIdx.x);
-    for_each_local_tile(cv, cr.b[r], [&](uint32_t lt) { words[atomicAdd(&s_base[lt], 1u)] = w; });
-  }
+  chunk_pairs(cv, cr, hl, [&](uint32_t lt, uint32_t slot, uint32_t key) {
+    words[atomicAdd(&s_base[lt], 1u)] = ((uint64_t)key << 32) | (uint64_t)(uint32_t)(rec0 + slot);
+  });
 }
 
 // ---- segment sorts ---------------------------------------------------------------
