@@ -55,6 +55,22 @@ __device__ __forceinline__ float wave_sum8_transposed(const float (&v)[8]) {
   return e;
 }
 
+// The same transposed reduction for eight fp64 values.
+__device__ __forceinline__ double wave_sum8_transposed_f64(const double (&v)[8]) {
+  const unsigned lane = lane_id();
+  const bool b2 = lane & 4u, b1 = lane & 2u, b0 = lane & 1u;
+  double a[4], c[2];
+#pragma unroll
+  for (int j = 0; j < 4; j++) a[j] = (b2 ? v[j + 4] : v[j]) + dpp_f64<0x141, 0xf, false>(b2 ? v[j] : v[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; j++) c[j] = (b1 ? a[j + 2] : a[j]) + dpp_f64<0x4E, 0xf, false>(b1 ? a[j] : a[j + 2]);
+  double e = (b0 ? c[1] : c[0]) + dpp_f64<0xB1, 0xf, false>(b0 ? c[0] : c[1]);
+  e += dpp_f64<0x128, 0xf, false>(e);             // row rotate by 8: lane ^ 8
+  e += __shfl_xor(e, 16, WAVE);
+  e += __shfl_xor(e, 32, WAVE);
+  return e;
+}
+
 // Up to two fp64 and two fp32 ranges cleared by one launch.
 struct ZeroRanges {
   double *d0, *d1;
@@ -84,13 +100,19 @@ __global__ __launch_bounds__(256) void k_zero(ZeroRanges z) {
 template <int CM, bool LIDAR>
 __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int tile_begin) {
   constexpr int NF = LIDAR ? 1 : CM;        // fp32 values per entry: features (or depth)
-  __shared__ double2 s_uv[256];
-  __shared__ double2 s_ab[256];
-  __shared__ double2 s_co[256];
-  __shared__ float s_f[NF][256];
-  __shared__ uint32_t s_rid[256];
-  __shared__ double s_ag[6][256];           // du, dv, d_ca, d_cb, d_cc, d_opac
-  __shared__ float s_af[NF][256];           // d_feat (or d_depth)
+  constexpr int NFP = NF | 1;               // odd row stride: lanes of one entry hit distinct banks
+  constexpr int NG = (NF + 7) / 8;          // groups of eight for the transposed reduction
+  // entries staged per batch: fewer with many channels, so that two or more
+  // workgroups fit a CU's LDS
+  constexpr int BT = NF >= 64 ? 64 : 128;
+  __shared__ double2 s_uv[BT];
+  __shared__ double2 s_ab[BT];
+  __shared__ double2 s_co[BT];
+  constexpr int NFS = (NF + 3) & ~3;        // 16-byte rows: vector reads of an entry's features
+  __shared__ float s_f[BT][NFS];
+  __shared__ uint32_t s_rid[BT];
+  __shared__ double s_ag[BT][7];           // du, dv, d_ca, d_cb, d_cc, d_opac (odd stride)
+  __shared__ float s_af[BT][NFP];          // d_feat (or d_depth)
   __shared__ QuadLists s_l;
   __shared__ uint32_t s_maxlast;
   if (*A.overflow) return;
@@ -101,7 +123,8 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile];
   const uint32_t len = A.ranges[2 * gtile + 1] - start;
-  const unsigned lane = lane_id(), wq = threadIdx.x >> 6;
+  const unsigned lane = lane_id();
+  const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
   const size_t plane = (size_t)c.W * c.H;
   const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
@@ -109,9 +132,9 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   uint32_t lastp = 0;
   double T = 1.0;      // transmittance after the current entry
   float g[LIDAR ? 2 : CM];
-  float Sb[NF];        // colour (or depth) composited behind the current entry
-#pragma unroll
-  for (int ch = 0; ch < NF; ch++) Sb[ch] = 0.0f;
+  // behind the current entry: depth composited (spherical views), or the
+  // composited colour projected on the pixel's upstream gradient, sum_ch Sb_ch g_ch
+  float Sb = 0.0f;
   if (LIDAR) {
     g[0] = tp.inside ? A.dimg[pofs] : 0.0f;
     g[1] = tp.inside ? A.dimg[pofs + plane] : 0.0f;
@@ -129,11 +152,16 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   if (lastp) atomicMax(&s_maxlast, lastp);
   __syncthreads();
   const uint32_t maxlast = s_maxlast;
+  // deepest list position any pixel of this wave replays
+  uint32_t wlast = lastp;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) wlast = max(wlast, (uint32_t)__shfl_xor((int)wlast, d, WAVE));
+  wlast = (uint32_t)__builtin_amdgcn_readfirstlane((int)wlast);
   const long long vbase = (long long)view * A.n;
   const float amin = A.alpha_min, amax = A.alpha_max;
 
-  for (int hi = (int)maxlast; hi > 0; hi -= 256) {
-    const int lo = hi > 256 ? hi - 256 : 0;
+  for (int hi = (int)maxlast; hi > 0; hi -= BT) {
+    const int lo = hi > BT ? hi - BT : 0;
     const int cnt = hi - lo;
     unsigned mask = 0;
     if ((int)threadIdx.x < cnt) {
@@ -145,22 +173,23 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
       s_ab[threadIdx.x] = cn.ab;
       s_co[threadIdx.x] = cn.co;
       if (LIDAR) {
-        s_f[0][threadIdx.x] = A.aux[rid].depth;
+        s_f[threadIdx.x][0] = A.aux[rid].depth;
       } else {
         const long long id = (long long)rid - vbase;
 #pragma unroll
-        for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+        for (int ch = 0; ch < CM; ch++) s_f[threadIdx.x][ch] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
       }
 #pragma unroll
-      for (int q = 0; q < 6; q++) s_ag[q][threadIdx.x] = 0.0;
+      for (int q = 0; q < 6; q++) s_ag[threadIdx.x][q] = 0.0;
 #pragma unroll
-      for (int q = 0; q < NF; q++) s_af[q][threadIdx.x] = 0.0f;
+      for (int q = 0; q < NF; q++) s_af[threadIdx.x][q] = 0.0f;
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
     for (int k = s_l.cnt[wq] - 1; k >= 0; k--) {
       const int idx = s_l.idx[wq][k];
       const uint32_t pos = (uint32_t)(lo + idx);
+      if (pos >= wlast) continue;               // beyond every pixel of the wave
       const double2 ab = s_ab[idx], co = s_co[idx];
       float G, og;
       double dx, dy;
@@ -178,19 +207,24 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         const double Tkd = T / (1.0 - (double)al);
         const float Tk = (float)Tkd;
         float da = 0.0f;
+        const float wk = Tk * al;
         if (LIDAR) {
-          const float dep = s_f[0][idx];
-          vf[0] = Tk * al * g[0];
-          da = Tk * (dep - Sb[0]) * g[0] + (float)(Tfin / (1.0 - (double)al)) * g[1];
-          Sb[0] = __builtin_fmaf(al, dep, om * Sb[0]);
+          const float dep = s_f[idx][0];
+          vf[0] = wk * g[0];
+          da = Tk * (dep - Sb) * g[0] + (float)(Tfin / (1.0 - (double)al)) * g[1];
+          Sb = __builtin_fmaf(al, dep, om * Sb);
         } else {
+          // d loss / d alpha = T_k sum_ch (f_ch - Sb_ch) g_ch, and sum_ch Sb_ch g_ch
+          // follows the same blend as Sb: one dot product per entry
+          float fg = 0.0f;
 #pragma unroll
           for (int ch = 0; ch < CM; ch++) {
-            const float f = s_f[ch][idx];
-            vf[ch] = Tk * al * g[ch];
-            da = __builtin_fmaf(Tk * (f - Sb[ch]), g[ch], da);
-            Sb[ch] = __builtin_fmaf(al, f, om * Sb[ch]);
+            const float f = s_f[idx][ch];
+            vf[ch] = wk * g[ch];
+            fg = __builtin_fmaf(f, g[ch], fg);
           }
+          da = Tk * (fg - Sb);
+          Sb = __builtin_fmaf(al, fg, om * Sb);
         }
         T = Tkd;
         if (!(og > amax)) {              // alpha is the constant amax where clamped
@@ -204,35 +238,59 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
           vg[4] = dp * 0.5 * dy * dy;
         }
       }
+      {
+        double v8[8];
 #pragma unroll
-      for (int q = 0; q < 6; q++) {
-        const double r = row_sum_to_last_f64(vg[q]);
-        if ((lane & 15u) == 15u) atomicAdd(&s_ag[q][idx], r);
+        for (int q = 0; q < 8; q++) v8[q] = q < 6 ? vg[q] : 0.0;
+        const double r = wave_sum8_transposed_f64(v8);
+        if (lane < 6u) atomicAdd(&s_ag[idx][lane], r);
       }
+      if constexpr (NF >= 3) {
+        // wave totals, transposed: lane l < NF adds channel l
+        float tot[NG];
 #pragma unroll
-      for (int q = 0; q < NF; q++) {
-        const float r = row_sum_to_last(vf[q]);
-        if ((lane & 15u) == 15u) atomicAdd(&s_af[q][idx], r);
+        for (int gq = 0; gq < NG; gq++) {
+          float v8[8];
+#pragma unroll
+          for (int j = 0; j < 8; j++) v8[j] = gq * 8 + j < NF ? vf[gq * 8 + j] : 0.0f;
+          tot[gq] = wave_sum8_transposed(v8);
+        }
+        float x = tot[0];
+#pragma unroll
+        for (int gq = 1; gq < NG; gq++) x = (lane >> 3) == (unsigned)gq ? tot[gq] : x;
+        if (lane < (unsigned)NF) atomicAdd(&s_af[idx][lane], x);
+      } else {
+#pragma unroll
+        for (int q = 0; q < NF; q++) {
+          const float r = row_sum_to_last(vf[q]);
+          if ((lane & 15u) == 15u) atomicAdd(&s_af[idx][q], r);
+        }
       }
     }
     __syncthreads();
-    if ((int)threadIdx.x < cnt) {
-      const uint32_t rid = s_rid[threadIdx.x];
+    // Flush: one wave per entry, its lanes over the entry's values, so that each
+    // atomic instruction covers one or two cache lines of the record's rows.
+    for (int e = wq; e < cnt; e += 4) {
+      const uint32_t rid = s_rid[e];
       double *dg = A.accg + (size_t)rid * ACC_G;
-#pragma unroll
-      for (int q = 0; q < 6; q++) {
-        const double x = s_ag[q][threadIdx.x];
-        if (x != 0.0) atomicAdd(dg + q, x);
+      if (lane < 6u) {
+        const double x = s_ag[e][lane];
+        if (x != 0.0) atomicAdd(dg + lane, x);
       }
       if (LIDAR) {
-        const float x = s_af[0][threadIdx.x];
-        if (x != 0.0f) atomicAdd(dg + 6, (double)x);
+        if (lane == 6u) {
+          const float x = s_af[e][0];
+          if (x != 0.0f) atomicAdd(dg + 6, (double)x);
+        }
       } else {
         double *df = A.accf + (size_t)rid * A.C;
 #pragma unroll
-        for (int q = 0; q < CM; q++) {
-          const float x = s_af[q][threadIdx.x];
-          if (q < A.C && x != 0.0f) atomicAdd(df + q, (double)x);
+        for (int q0 = 0; q0 < CM; q0 += WAVE) {
+          const int q = q0 + (int)lane;
+          if (q < CM && q < A.C) {
+            const float x = s_af[e][q];
+            if (x != 0.0f) atomicAdd(df + q, (double)x);
+          }
         }
       }
     }
@@ -261,7 +319,8 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
   __shared__ int s_flags[256];
   __shared__ float s_f[CM][256];
   __shared__ uint32_t s_rid[256];
-  __shared__ float s_acc[NV][256];
+  constexpr int NVP = NV | 1;                 // odd row stride of the LDS sums
+  __shared__ float s_acc[256][NVP];
   __shared__ uint32_t s_top[256 * SPLAT_TOPK_MAX];
   __shared__ QuadLists s_l;
   __shared__ uint32_t s_npos;
@@ -324,7 +383,7 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
 #pragma unroll
       for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
 #pragma unroll
-      for (int q = 0; q < NV; q++) s_acc[q][threadIdx.x] = 0.0f;
+      for (int q = 0; q < NV; q++) s_acc[threadIdx.x][q] = 0.0f;
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
@@ -375,24 +434,30 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
         const float (&vg)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * gq]);
         const float r = wave_sum8_transposed(vg);
         const int q = 8 * gq + (int)lane;
-        if (lane < 8u && q < NV && r != 0.0f) atomicAdd(&s_acc[q][idx], r);
+        if (lane < 8u && q < NV && r != 0.0f) atomicAdd(&s_acc[idx][q], r);
       }
     }
     __syncthreads();
-    if (threadIdx.x < cnt) {
-      float v[NV];
-      bool any = false;
+    // Flush into the record's fp64 row (dq0, dq1, dq2, d_reff, d_opac, d_feat...):
+    // LPE lanes per entry over its values, so that one atomic instruction covers
+    // a few whole rows instead of one value of 64 rows.
+    {
+      constexpr int LPE = NV <= 8 ? 8 : NV <= 16 ? 16 : NV <= 32 ? 32 : 64;
+      constexpr int EPI = WAVE / LPE;
+      const int sub = (int)lane / LPE, ql = (int)lane % LPE;
+      for (int e0 = wq * EPI; e0 < (int)cnt; e0 += 4 * EPI) {
+        const int e = e0 + sub;
+        if (e < (int)cnt) {
+          double *row = A.accg + (size_t)s_rid[e] * (5 + A.C);
 #pragma unroll
-      for (int q = 0; q < NV; q++) {
-        v[q] = s_acc[q][threadIdx.x];
-        any |= v[q] != 0.0f;
-      }
-      if (any) {
-        // one fp64 row per record: dq0, dq1, dq2, d_reff, d_opac, d_feat...
-        double *row = A.accg + (size_t)s_rid[threadIdx.x] * (5 + A.C);
-#pragma unroll
-        for (int q = 0; q < NV; q++)
-          if ((q < 5 || q - 5 < A.C) && v[q] != 0.0f) atomicAdd(row + q, (double)v[q]);
+          for (int q0 = 0; q0 < NV; q0 += LPE) {
+            const int q = q0 + ql;
+            if (q < NV && (q < 5 || q - 5 < A.C)) {
+              const float x = s_acc[e][q];
+              if (x != 0.0f) atomicAdd(row + q, (double)x);
+            }
+          }
+        }
       }
     }
     __syncthreads();
@@ -587,9 +652,8 @@ __device__ void jacobian_and_derivs(const ViewDev &c, const double m[3], double 
   }
 }
 
-__global__ __launch_bounds__(256) void k_proj_bwd_gauss(ViewTable vt, ProjBwdArgs P, int vbeg, int vend) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= P.n) return;
+// Geometry chain rule of one Gaussian (fp64), views summed.
+__device__ __forceinline__ void gauss_prim_grads(const ViewTable &vt, const ProjBwdArgs &P, int vbeg, int vend, int i) {
   double gpos[3] = {0, 0, 0}, gs[3] = {0, 0, 0}, gq[4] = {0, 0, 0, 0}, gop = 0;
   if (P.kind == SPLAT_PRIM_GAUSS2D) {
     const double s = P.scale[i];
@@ -708,13 +772,22 @@ __global__ __launch_bounds__(256) void k_proj_bwd_gauss(ViewTable vt, ProjBwdArg
   if (P.grot && P.kind == SPLAT_PRIM_GAUSS3D)
     for (int a = 0; a < 4; a++) put(P.grot, 4 * (size_t)i + a, gq[a], P.accumulate);
   if (P.gop) put(P.gop, i, gop, P.accumulate);
-  if (P.gfeat)
-    for (int ch = 0; ch < P.C; ch++) {
-      double sum = 0;
-      for (int v = vbeg; v < vend; v++)
-        if (vt.v[v].kind != SPLAT_CAM_SPHERICAL) sum += P.accf[((size_t)v * P.n + i) * P.C + ch];
-      put(P.gfeat, (size_t)i * P.C + ch, sum, P.accumulate);
-    }
+}
+
+// One thread per Gaussian for the geometry; the block's feature gradients
+// ([primitive][channel], views summed) then go element by element, coalesced.
+__global__ __launch_bounds__(256) void k_proj_bwd_gauss(ViewTable vt, ProjBwdArgs P, int vbeg, int vend) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < P.n) gauss_prim_grads(vt, P, vbeg, vend, i);
+  if (!P.gfeat) return;
+  const size_t e1 = (size_t)min((long long)(blockIdx.x + 1) * blockDim.x, (long long)P.n) * P.C;
+  const size_t plane = (size_t)P.n * P.C;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x * P.C + threadIdx.x; e < e1; e += blockDim.x) {
+    double sum = 0;
+    for (int v = vbeg; v < vend; v++)
+      if (vt.v[v].kind != SPLAT_CAM_SPHERICAL) sum += P.accf[(size_t)v * plane + e];
+    put(P.gfeat, e, sum, P.accumulate);
+  }
 }
 
 template <int CM>
