@@ -26,8 +26,8 @@
 //                                 tile start + chunk prefix + a rank from an LDS
 //                                 atomic
 //   k_seg_sort                    segments up to SEG_WAVE pairs: one wave each,
-//                                 bitonic in registers and lane shuffles
-//   k_seg_long                    longer segments from a work queue, one
+//                                 bitonic in registers and lane shuffles; then
+//                                 longer segments from a work queue, one
 //                                 workgroup each: merge sort in LDS up to NV
 //                                 pairs, an MSD split into LDS-sized buckets
 //                                 beyond
@@ -41,8 +41,8 @@
 namespace {
 
 constexpr int SCAN_BLOCK = 256;
-constexpr int TH_THREADS = 512;     // workgroup of the counting passes
-constexpr int TH_RPT = 8;           // records per thread in the counting passes
+constexpr int TH_THREADS = 1024;    // workgroup of the counting passes
+constexpr int TH_RPT = 4;           // records per thread in the counting passes
 constexpr int TH_CHUNK = TH_THREADS * TH_RPT;
 constexpr int SEG_WAVE = 512;       // segments up to this length: one wave sorts them
 constexpr int TILE_SCAN1_MAX = 1 << 16;   // tiles scanned by a single workgroup
@@ -53,7 +53,7 @@ constexpr int LE = 16;              // words per thread in the long-segment sort
 constexpr int NV = LT * LE;         // words one workgroup sorts in LDS (64 KiB)
 constexpr int NV_PHYS = NV + NV / LE;   // one pad word after every LE words
 constexpr int MAXLVL = 8;           // MSD split levels (8 bits of the word range each)
-constexpr int LONG_GRID = 512;      // workgroups of the long-segment sort (two per CU)
+constexpr int SORT_GRID = 512;      // workgroups of the segment sort (two per CU)
 
 // Block-wide exclusive scan of one value per thread (256 threads); returns the
 // exclusive prefix and writes the block total to *total.
@@ -593,17 +593,14 @@ __device__ void bitonic_regs(uint64_t (&e)[E], uint32_t P, uint32_t base, uint64
   }
 }
 
-// Segments of at most SEG_WAVE pairs: one wave per tile, four tiles per
-// workgroup, bitonic with eight words per lane and the rest of the network
-// through lane shuffles (no LDS, no barriers).
-__global__ __launch_bounds__(256) void k_seg_sort(const uint32_t *ranges, const uint64_t *words,
-                                                   const int32_t *overflow, uint64_t *keys, uint32_t *vals, int tiles) {
-  if (*overflow) return;
-  const unsigned lane = lane_id();
-  const int own = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  if (own >= tiles) return;
-  const uint32_t start = ranges[2 * own], len = ranges[2 * own + 1] - start;
+// Segments of at most SEG_WAVE pairs: one wave per tile, bitonic with eight
+// words per lane and the rest of the network through lane shuffles (no LDS,
+// no barriers).
+__device__ __forceinline__ void wave_sort_tile(const uint32_t *ranges, const uint64_t *words, uint64_t *keys,
+                                               uint32_t *vals, int t) {
+  const uint32_t start = ranges[2 * t], len = ranges[2 * t + 1] - start;
   if (len == 0 || len > SEG_WAVE) return;
+  const unsigned lane = lane_id();
   uint32_t P = 2;
   while (P < len) P <<= 1;
   const uint32_t base = lane * 8;
@@ -613,7 +610,7 @@ __global__ __launch_bounds__(256) void k_seg_sort(const uint32_t *ranges, const 
   bitonic_regs<8>(e, P, base, nullptr);        // P <= 64 * 8: never reaches the LDS stages
 #pragma unroll
   for (int a = 0; a < 8; a++)
-    if (base + a < len) write_pair(keys, vals, start + base + a, (uint32_t)own, e[a]);
+    if (base + a < len) write_pair(keys, vals, start + base + a, (uint32_t)t, e[a]);
 }
 
 // ---- long segments: merge sort in LDS, MSD split beyond NV -----------------------
@@ -830,19 +827,25 @@ __device__ void msd_split(const uint64_t *src, uint64_t *dst, int len, uint32_t 
   __syncthreads();                                   // before any thread reads them back
 }
 
-// Segments longer than SEG_WAVE, one workgroup per tile from a work queue (the
-// tiles above NV first). Up to NV pairs: lds_sort straight from the bucketed
-// words. Beyond: MSD split into the key array (used as scratch), then every run
+// Every segment sorted on its own. First each wave sorts the short segments
+// (at most SEG_WAVE pairs) of its share of the tiles; then the workgroups take
+// the longer segments one per workgroup from a work queue (the tiles above NV
+// first). Up to NV pairs: lds_sort straight from the bucketed words. Beyond: MSD split into the key array (used as scratch), then every run
 // of adjacent buckets that fits NV words is sorted as one segment; a bucket
 // above NV is split again into the bucketed-word array, and so on, alternating.
 // Words are unique, so the offset range loses 8 bits per level and a bucket on
 // level MAXLVL - 1 holds at most one word: the split never goes deeper.
-__global__ __launch_bounds__(LT) void k_seg_long(const uint32_t *ranges, uint64_t *words, const int32_t *overflow,
+__global__ __launch_bounds__(LT) void k_seg_sort(const uint32_t *ranges, uint64_t *words, const int32_t *overflow,
                                                   uint64_t *keys, uint32_t *vals, uint32_t *live,
                                                   const uint32_t *list, int tiles) {
   __shared__ uint64_t s[NV_PHYS];
   __shared__ SplitLds sl;
   if (*overflow) return;
+  {
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
+    for (int t = (int)blockIdx.x * (LT / WAVE) + wave; t < tiles; t += (int)gridDim.x * (LT / WAVE))
+      wave_sort_tile(ranges, words, keys, vals, t);
+  }
   const int nh = (int)live[1], nall = nh + (int)live[2];
   if (nall == 0) return;
   const int tid = (int)threadIdx.x;
@@ -993,9 +996,7 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
     hipLaunchKernelGGL(k_bucket, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, overflow, ws.cursor,
                        ws.words);
   }
-  hipLaunchKernelGGL(k_seg_sort, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream, ranges, ws.words, overflow,
-                     keys, vals, (int)tiles);
-  hipLaunchKernelGGL(k_seg_long, dim3(LONG_GRID), dim3(LT), 0, stream, ranges, ws.words, overflow, keys, vals, ws.live,
+  hipLaunchKernelGGL(k_seg_sort, dim3(SORT_GRID), dim3(LT), 0, stream, ranges, ws.words, overflow, keys, vals, ws.live,
                      ws.list, (int)tiles);
   SPLAT_LAUNCH_CHECK();
   return SPLAT_OK;

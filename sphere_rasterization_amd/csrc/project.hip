@@ -94,25 +94,31 @@ struct PrimArgs {
   double gamma, alpha_min;
 };
 
+// One (view, primitive): the binning record and pair count go straight to
+// memory; the drawing and backward records into the workgroup's LDS slots dd
+// and aa. Returns false for a culled primitive (slots untouched: nothing reads
+// a culled record's drawing or backward data).
 template <int KIND>
-__global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjLayout L, uint32_t *counts) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= P.n) return;
-  const int view = blockIdx.y;
-  const long long k = (long long)view * P.n + i;
-  const ViewDev &c = vt.v[view];
-  double o = (double)P.opacity[i];
+__device__ __forceinline__ bool project_one(const ViewDev &c, const PrimArgs &P, const ProjLayout &L, uint32_t *counts,
+                                            long long k, int i, DrawRec &dd, AuxRec &aa) {
+  double o;
+  if (KIND != SPLAT_PRIM_SPHERE) o = (double)P.opacity[i];
 
   if (KIND == SPLAT_PRIM_SPHERE) {
+    // all five inputs in flight together (the opacity would otherwise be
+    // loaded after the culling tests, one memory latency later)
+    float px = P.pos[3 * i], py = P.pos[3 * i + 1], pz = P.pos[3 * i + 2], pr = P.scale[i], po = P.opacity[i];
+    asm volatile("" : "+v"(px), "+v"(py), "+v"(pz), "+v"(pr), "+v"(po));
+    o = (double)po;
     double q[3];
-    sensor_point(c, (double)P.pos[3 * i], (double)P.pos[3 * i + 1], (double)P.pos[3 * i + 2], q);
-    double r = (double)P.scale[i];
+    sensor_point(c, (double)px, (double)py, (double)pz, q);
+    double r = (double)pr;
     double fx = (double)c.fx, fy = (double)c.fy;
     double fmin = fx < fy ? fx : fy;
     double rfl = 0.75 * q[2] / fmin;               // every sphere keeps at least one pixel
     double re = r >= rfl ? r : rfl;
     double zf = q[2] - re;
-    if (!(zf > (double)c.znear) || !(zf > 0.0) || !isfinite(r) || !(r > 0.0)) { write_culled(L, k, counts); return; }
+    if (!(zf > (double)c.znear) || !(zf > 0.0) || !isfinite(r) || !(r > 0.0)) { write_culled(L, k, counts); return false; }
     double den = q[2] * q[2] - re * re;
     double sx = sqrt(q[0] * q[0] + q[2] * q[2] - re * re);
     double sy = sqrt(q[1] * q[1] + q[2] * q[2] - re * re);
@@ -120,9 +126,9 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
     double xh = fx * ((q[0] * q[2] + re * sx) / den) + (double)c.cx;
     double yl = fy * ((q[1] * q[2] - re * sy) / den) + (double)c.cy;
     double yh = fy * ((q[1] * q[2] + re * sy) / den) + (double)c.cy;
-    if (!isfinite(xl) || !isfinite(xh) || !isfinite(yl) || !isfinite(yh)) { write_culled(L, k, counts); return; }
+    if (!isfinite(xl) || !isfinite(xh) || !isfinite(yl) || !isfinite(yh)) { write_culled(L, k, counts); return false; }
     Rect rc = make_rect(c, xl, xh, yl, yh);
-    if (!rc.valid) { write_culled(L, k, counts); return; }
+    if (!rc.valid) { write_culled(L, k, counts); return false; }
     float key = (float)zf;
     write_rect(L, k, counts, rc, key);
     double u = fx * q[0] / q[2] + (double)c.cx;
@@ -142,13 +148,13 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
     d.w = (float)(o * e);
     d.e = (float)bnd;
     d.i0 = rc.i0; d.i1 = rc.i1; d.j0 = rc.j0; d.j1 = rc.j1;
-    L.draw[k] = d;
+    dd = d;
     AuxRec a;
     a.x = (float)q[0]; a.y = (float)q[1]; a.z = (float)q[2]; a.w = (float)re;
     a.opac = (float)o; a.zhat = (float)zhat; a.depth = (float)zf;
     a.flags = (float)(floored | (gated << 1));
-    L.aux[k] = a;
-    return;
+    aa = a;
+    return true;
   }
 
   double u, v, sxx, sxy, syy, depth;
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
     sensor_point(c, (double)P.pos[3 * i], (double)P.pos[3 * i + 1], (double)P.pos[3 * i + 2], m);
     double J[6];
     if (c.kind == SPLAT_CAM_PINHOLE) {
-      if (!(m[2] > (double)c.znear)) { write_culled(L, k, counts); return; }
+      if (!(m[2] > (double)c.znear)) { write_culled(L, k, counts); return false; }
       depth = m[2];
       double fx = c.fx, fy = c.fy;
       J[0] = fx / m[2];
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
     } else {
       double rho2 = m[0] * m[0] + m[1] * m[1];
       double rr = sqrt(rho2 + m[2] * m[2]);
-      if (!(rr > (double)c.znear) || !(rho2 > 0.0)) { write_culled(L, k, counts); return; }
+      if (!(rr > (double)c.znear) || !(rho2 > 0.0)) { write_culled(L, k, counts); return false; }
       depth = rr;
       double rho = sqrt(rho2);
       double r2 = rho2 + m[2] * m[2];
@@ -236,11 +242,11 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
     syy = U[3] * T[3] + U[4] * T[4] + U[5] * T[5];
   }
   double det = sxx * syy - sxy * sxy;
-  if (!(det > 0.0) || !(depth > 0.0) || !isfinite(u) || !isfinite(v)) { write_culled(L, k, counts); return; }
+  if (!(det > 0.0) || !(depth > 0.0) || !isfinite(u) || !isfinite(v)) { write_culled(L, k, counts); return false; }
   double hx = sqrt(kSupport * sxx), hy = sqrt(kSupport * syy);
-  if (!isfinite(hx) || !isfinite(hy)) { write_culled(L, k, counts); return; }
+  if (!isfinite(hx) || !isfinite(hy)) { write_culled(L, k, counts); return false; }
   Rect rc = make_rect(c, u - hx, u + hx, v - hy, v + hy);
-  if (!rc.valid) { write_culled(L, k, counts); return; }
+  if (!rc.valid) { write_culled(L, k, counts); return false; }
   write_rect(L, k, counts, rc, (float)depth);
   DrawRec d;
   d.u = u;
@@ -264,11 +270,42 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
       if (dr.valid) { d.i0 = dr.i0; d.i1 = dr.i1; d.j0 = dr.j0; d.j1 = dr.j1; }
     }
   }
-  L.draw[k] = d;
+  dd = d;
   AuxRec a;
   a.x = (float)depth; a.y = 0.f; a.z = 0.f; a.w = 0.f;
   a.opac = (float)o; a.zhat = 0.f; a.depth = (float)depth; a.flags = 0.f;
-  L.aux[k] = a;
+  aa = a;
+  return true;
+}
+
+// Thread per (view, primitive); grid (ceil(n / 256), views). The drawing (64 B)
+// and backward (32 B) records are staged in LDS and leave as whole contiguous
+// blocks: stored from registers, each lane's 16-byte pieces would land 64 or
+// 32 bytes apart and the partial-line writes run at half the write bandwidth.
+template <int KIND>
+__global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjLayout L, uint32_t *counts) {
+  __shared__ DrawRec s_d[256];
+  __shared__ AuxRec s_a[256];
+  __shared__ unsigned char s_vis[256];
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int view = blockIdx.y;
+  const ViewDev &c = vt.v[view];
+  bool vis = false;
+  if (i < P.n) vis = project_one<KIND>(c, P, L, counts, (long long)view * P.n + i, i, s_d[threadIdx.x], s_a[threadIdx.x]);
+  s_vis[threadIdx.x] = vis ? 1 : 0;
+  __syncthreads();
+  // only visible records' pieces are stored (a view may cull most of the scene)
+  const int nblk = min((int)blockDim.x, P.n - (int)(blockIdx.x * blockDim.x));
+  const long long k0 = (long long)view * P.n + (long long)blockIdx.x * blockDim.x;
+  constexpr int DW = sizeof(DrawRec) / 16, AW = sizeof(AuxRec) / 16;
+  uint4 *gd = reinterpret_cast<uint4 *>(L.draw + k0);
+  const uint4 *sd = reinterpret_cast<const uint4 *>(s_d);
+  for (int j = threadIdx.x; j < nblk * DW; j += blockDim.x)
+    if (s_vis[j / DW]) gd[j] = sd[j];
+  uint4 *ga = reinterpret_cast<uint4 *>(L.aux + k0);
+  const uint4 *sa = reinterpret_cast<const uint4 *>(s_a);
+  for (int j = threadIdx.x; j < nblk * AW; j += blockDim.x)
+    if (s_vis[j / AW]) ga[j] = sa[j];
 }
 
 }  // namespace
