@@ -536,78 +536,90 @@ __device__ __forceinline__ void write_pair(uint64_t *keys, uint32_t *vals, uint3
   vals[pos] = (uint32_t)w;
 }
 
-// Compare-exchange of register elements a and a|J of one thread (J < E).
-template <int J, int E>
-__device__ __forceinline__ void cx_local(uint64_t (&e)[E], uint32_t base, uint32_t k) {
-#pragma unroll
-  for (int a = 0; a < E; a++) {
-    if (a & J) continue;
-    const int b = a | J;
-    const bool up = ((base + a) & k) == 0;
-    const bool lt = e[a] < e[b];
-    const uint64_t lo = lt ? e[a] : e[b], hi = lt ? e[b] : e[a];
-    e[a] = up ? lo : hi;
-    e[b] = up ? hi : lo;
+// Value of lane (lane ^ M) for a 32-bit value, M a power of two below 64: DPP
+// quad permutes for 1 and 2, a half-row mirror (lane ^ 7) followed by a quad
+// reversal (lane ^ 3) for 4, a row rotation by 8 for 8, a swizzle for 16 and
+// a lane permute through the LDS crossbar for 32.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x, unsigned lane) {
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, false);
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, false);
+  } else if constexpr (M == 4) {
+    const int y = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(y, 0x1B, 0xf, 0xf, false);
+  } else if constexpr (M == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false);
+  } else if constexpr (M == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+  } else {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane ^ 32u) << 2), (int)x);
   }
 }
 
-// Bitonic sort of P = 2^m words held E per thread (thread t holds t*E .. t*E+E-1).
-// A stage (k, j) pairs element x with x ^ j: inside the thread when j < E, with
-// lane t ^ (j/E) of the same wave by a lane shuffle when j < 64 E, through LDS
-// otherwise (at most three such stages). Element x keeps the smaller word when
-// it is the lower of its pair in an ascending block or the upper in a
-// descending one; for j >= E that choice is the same for all of a thread's
-// elements. Words are distinct (padding aside), so one compare decides.
-template <int E>
-__device__ void bitonic_regs(uint64_t (&e)[E], uint32_t P, uint32_t base, uint64_t *s) {
-  for (uint32_t k = 2; k <= P; k <<= 1) {
-    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
-      if (j >= (uint32_t)E) {
-        const bool keep_min = ((base & j) == 0) == ((base & k) == 0);
-        if (j >= 64u * E) {
-          __syncthreads();
+template <int M>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v, unsigned lane) {
+  const uint32_t lo = lane_xor32<M>((uint32_t)v, lane), hi = lane_xor32<M>((uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One stage (K, J) of the bitonic network over 512 words, lane l holding words
+// 8 l .. 8 l + 7. Word x pairs with x ^ J and keeps the smaller of the two
+// when it is the lower one of an ascending block or the upper one of a
+// descending block (block direction: bit K of x clear = ascending). For
+// J >= 8 the partner is in lane l ^ (J / 8) and the choice is the same for all
+// eight words of a lane; below, partners are in the same lane.
+template <int K, int J>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&e)[8], unsigned lane) {
+  if constexpr (J >= 8) {
+    constexpr int M = J / 8;
+    const bool lower = (lane & (unsigned)M) == 0u;
+    const bool asc = K >= 512 ? true : (lane & (unsigned)(K / 8)) == 0u;
+    const bool keep_min = lower == asc;
 #pragma unroll
-          for (int a = 0; a < E; a++) s[base + a] = e[a];
-          __syncthreads();
+    for (int a = 0; a < 8; a++) {
+      const uint64_t o = lane_xor64<M>(e[a], lane);
+      e[a] = ((o < e[a]) == keep_min) ? o : e[a];
+    }
+  } else {
 #pragma unroll
-          for (int a = 0; a < E; a++) {
-            const uint64_t o = s[(base + a) ^ j];
-            e[a] = ((o < e[a]) == keep_min) ? o : e[a];
-          }
-        } else {
-          const int m = (int)(j / E);
-#pragma unroll
-          for (int a = 0; a < E; a++) {
-            const uint64_t o = __shfl_xor(e[a], m, WAVE);
-            e[a] = ((o < e[a]) == keep_min) ? o : e[a];
-          }
-        }
-      } else if (j == 4) {
-        if constexpr (E > 4) cx_local<4, E>(e, base, k);
-      } else if (j == 2) {
-        if constexpr (E > 2) cx_local<2, E>(e, base, k);
-      } else {
-        cx_local<1, E>(e, base, k);
-      }
+    for (int a = 0; a < 8; a++) {
+      if (a & J) continue;
+      const int b = a | J;
+      const bool asc = K < 8 ? (a & K) == 0 : (K >= 512 ? true : (lane & (unsigned)(K / 8)) == 0u);
+      const uint64_t x = e[a], y = e[b];
+      const bool sw = (y < x) == asc;
+      e[a] = sw ? y : x;
+      e[b] = sw ? x : y;
     }
   }
 }
 
-// Segments of at most SEG_WAVE pairs: one wave per tile, bitonic with eight
-// words per lane and the rest of the network through lane shuffles (no LDS,
-// no barriers).
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge_level(uint64_t (&e)[8], unsigned lane) {
+  bitonic_stage<K, J>(e, lane);
+  if constexpr (J > 1) bitonic_merge_level<K, J / 2>(e, lane);
+}
+
+template <int K>
+__device__ __forceinline__ void bitonic512(uint64_t (&e)[8], unsigned lane) {
+  bitonic_merge_level<K, K / 2>(e, lane);
+  if constexpr (K < 512) bitonic512<K * 2>(e, lane);
+}
+
+// Segments of at most SEG_WAVE pairs: one wave per tile, padded to 512 words
+// with all-ones words (they sort last), the whole network unrolled.
 __device__ __forceinline__ void wave_sort_tile(const uint32_t *ranges, const uint64_t *words, uint64_t *keys,
                                                uint32_t *vals, int t) {
   const uint32_t start = ranges[2 * t], len = ranges[2 * t + 1] - start;
   if (len == 0 || len > SEG_WAVE) return;
   const unsigned lane = lane_id();
-  uint32_t P = 2;
-  while (P < len) P <<= 1;
   const uint32_t base = lane * 8;
   uint64_t e[8];
 #pragma unroll
   for (int a = 0; a < 8; a++) e[a] = base + a < len ? words[start + base + a] : ~0ull;
-  bitonic_regs<8>(e, P, base, nullptr);        // P <= 64 * 8: never reaches the LDS stages
+  bitonic512<2>(e, lane);
 #pragma unroll
   for (int a = 0; a < 8; a++)
     if (base + a < len) write_pair(keys, vals, start + base + a, (uint32_t)t, e[a]);
