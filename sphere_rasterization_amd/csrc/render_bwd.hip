@@ -310,18 +310,20 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
 // atomic per value.
 // ---------------------------------------------------------------------------
 template <int CM>
-__global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int tile_begin) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_bwd_sphere(ViewTable vt, BwdArgs A, int tile_begin) {
   constexpr int NV = 5 + CM;                  // dq0, dq1, dq2, d_reff, d_opac, d_feat...
   constexpr int NG = (NV + 7) / 8;            // groups of eight for the reduction
-  __shared__ double2 s_a[256];                // normalised centre (ax, ay)
-  __shared__ double2 s_Ai[256];               // A, 1 / r_eff
-  __shared__ float4 s_x[256];                 // qz, oe, 1/o + zhat/gamma, o/gamma
-  __shared__ int s_flags[256];
-  __shared__ float s_f[CM][256];
-  __shared__ uint32_t s_rid[256];
+  constexpr int BT = 128;                     // entries staged per batch (six workgroups fit a CU)
+  constexpr int TKS = SPLAT_TOPK_MAX + 1;     // odd stride of the per-pixel recorded positions
+  __shared__ double2 s_a[BT];                // normalised centre (ax, ay)
+  __shared__ double2 s_Ai[BT];               // A, 1 / r_eff
+  __shared__ float4 s_x[BT];                 // qz, oe, 1/o + zhat/gamma, o/gamma
+  __shared__ int s_flags[BT];
+  __shared__ float s_f[CM][BT];
+  __shared__ uint32_t s_rid[BT];
   constexpr int NVP = NV | 1;                 // odd row stride of the LDS sums
-  __shared__ float s_acc[256][NVP];
-  __shared__ uint32_t s_top[256 * SPLAT_TOPK_MAX];
+  __shared__ float s_acc[BT][NVP];
+  __shared__ uint32_t s_top[256 * TKS];
   __shared__ QuadLists s_l;
   __shared__ uint32_t s_npos;
   if (*A.overflow) return;
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
     Cimg[ch] = ok ? A.img[pofs + ch * plane] : 0.0f;
   }
   // recorded positions, local to the tile and ascending
-  uint32_t *my_top = s_top + threadIdx.x * SPLAT_TOPK_MAX;
+  uint32_t *my_top = s_top + threadIdx.x * TKS;
   int ntop = 0;
   for (int s = 0; s < K && tp.inside; s++) {
     const int t = A.topk[p * K + s];
@@ -358,7 +360,12 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
   if (tp.inside) invN = 1.0f / A.norm[p];
   if (threadIdx.x == 0) s_npos = 0;
   __syncthreads();
-  if (ntop) atomicMax(&s_npos, my_top[ntop - 1] + 1);
+  {
+    uint32_t hi = ntop ? my_top[ntop - 1] + 1 : 0u;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, WAVE));
+    if (lane == 0 && hi) atomicMax(&s_npos, hi);
+  }
   __syncthreads();
   const uint32_t npos = s_npos;
   int nxt = 0;
@@ -367,8 +374,8 @@ __global__ __launch_bounds__(256) void k_bwd_sphere(ViewTable vt, BwdArgs A, int
   const float igam = 1.0f / A.gamma;
   const long long vbase = (long long)view * A.n;
 
-  for (uint32_t b = 0; b < npos; b += 256) {
-    const uint32_t cnt = min(256u, npos - b);
+  for (uint32_t b = 0; b < npos; b += BT) {
+    const uint32_t cnt = min((uint32_t)BT, npos - b);
     unsigned mask = 0;
     if (threadIdx.x < cnt) {
       const uint32_t rid = A.vals[start + b + threadIdx.x];

@@ -24,7 +24,7 @@ namespace {
 // Spheres
 // ---------------------------------------------------------------------------
 template <int CM>
-__global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   // One staged entry = NE 16-byte slots at a common stride, so every read of an
   // entry uses one LDS address with constant offsets: three slots of D / g
   // coefficients (fp64 pairs), then (o exp(o zhat / gamma), stop limit bound /
@@ -33,7 +33,6 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   constexpr int NE = 3 + NF4;
   __shared__ float4 s_e[NE][256];
   __shared__ QuadLists s_l;
-  __shared__ int s_top[256 * SPLAT_TOPK_MAX];
   if (*A.overflow) return;
   const int gtile = blockIdx.x;
   const int view = view_of_tile(vt, gtile);
@@ -49,8 +48,9 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   for (int ch = 0; ch < CM; ch++) S[ch] = A.bg_weight * A.bg[ch];
   const int K = A.top_k;
   int ntop = 0;
-  bool need = K > 0;                    // still recording contributing spheres
-  int *my_top = s_top + threadIdx.x * K;
+  // still recording contributing spheres (straight into the top-K buffer)
+  bool need = K > 0 && A.topk != nullptr && tp.inside;
+  int *my_top = need ? A.topk + (c.pix_off + (long long)tp.j * c.W + tp.i) * K : nullptr;
   bool active = tp.inside;
   const long long vbase = (long long)view * A.n;
 
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
     if (ch < A.C) img[ch * plane] = S[ch] * inv;
   if (A.norm) A.norm[p] = N;
   if (A.topk)
-    for (int q = 0; q < K; q++) A.topk[p * K + q] = q < ntop ? my_top[q] : -1;
+    for (int q = ntop; q < K; q++) A.topk[p * K + q] = -1;
 }
 
 // ---------------------------------------------------------------------------
