@@ -499,43 +499,74 @@ __device__ __forceinline__ bool rec_live(const BinRec &b) { return b.ntx != 0; }
 // registers. Each block stores its twelve sums and k_cam_final adds them up in
 // block order (deterministic, and no atomics contend on twelve outputs; a
 // device-scope fence per block would write back the L2 of every XCD).
+template <int CM>
 __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs P, int vbeg, int vend, int cam_view) {
+  // Outputs of 256 spheres go through LDS and leave as contiguous runs: from
+  // registers, the 3- (and C-) float rows of neighbouring lanes would be written
+  // one float per instruction, a third of each line at a time.
+  constexpr int CS = CM <= 4 ? CM : 1;         // features staged up to four channels
   __shared__ double s_red[12][4];
+  __shared__ float s_pos[256 * 3];
+  __shared__ float s_feat[256 * CS];
   const int S = 5 + P.C;
   double cam[12];
 #pragma unroll
   for (int q = 0; q < 12; q++) cam[q] = 0.0;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < P.n; i += gridDim.x * blockDim.x) {
+  for (int i0 = blockIdx.x * 256; i0 < P.n; i0 += gridDim.x * 256) {
+    const int i = i0 + (int)threadIdx.x;
+    const int nb = min(256, P.n - i0);
     double dp[3] = {0, 0, 0}, dr = 0, dop = 0;
-    for (int v = vbeg; v < vend; v++) {
-      const ViewDev &c = vt.v[v];
-      const double *A = P.accg + ((size_t)v * P.n + i) * S;     // zero for culled records
-      const double dq[3] = {A[0], A[1], A[2]};
+    if (i < P.n) {
+      for (int v = vbeg; v < vend; v++) {
+        const ViewDev &c = vt.v[v];
+        const double *A = P.accg + ((size_t)v * P.n + i) * S;     // zero for culled records
+        const double dq[3] = {A[0], A[1], A[2]};
 #pragma unroll
-      for (int a = 0; a < 3; a++)
-        dp[a] += (double)c.R[a] * dq[0] + (double)c.R[3 + a] * dq[1] + (double)c.R[6 + a] * dq[2];   // R^T dq
-      dr += A[3];
-      dop += A[4];
-      if (v == cam_view) {
-        const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
+        for (int a = 0; a < 3; a++)
+          dp[a] += (double)c.R[a] * dq[0] + (double)c.R[3 + a] * dq[1] + (double)c.R[6 + a] * dq[2];   // R^T dq
+        dr += A[3];
+        dop += A[4];
+        if (v == cam_view) {
+          const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
 #pragma unroll
-        for (int a = 0; a < 3; a++) {
+          for (int a = 0; a < 3; a++) {
 #pragma unroll
-          for (int b = 0; b < 3; b++) cam[3 * a + b] = __builtin_fma(dq[a], pp[b], cam[3 * a + b]);
-          cam[9 + a] += dq[a];
+            for (int b = 0; b < 3; b++) cam[3 * a + b] = __builtin_fma(dq[a], pp[b], cam[3 * a + b]);
+            cam[9 + a] += dq[a];
+          }
+        }
+      }
+      if (P.gscale) put(P.gscale, i, dr, P.accumulate);
+      if (P.gop) put(P.gop, i, dop, P.accumulate);
+    }
+    if (P.gpos) {
+      if (i < P.n)
+#pragma unroll
+        for (int a = 0; a < 3; a++) s_pos[3 * threadIdx.x + a] = (float)dp[a];
+      __syncthreads();
+      float *out = P.gpos + 3 * (size_t)i0;
+      for (int j = threadIdx.x; j < 3 * nb; j += 256) out[j] = P.accumulate ? out[j] + s_pos[j] : s_pos[j];
+    }
+    if (P.gfeat) {
+      if (CM <= 4) {
+        if (i < P.n)
+          for (int ch = 0; ch < P.C; ch++) {
+            double f = 0;
+            for (int v = vbeg; v < vend; v++) f += P.accg[((size_t)v * P.n + i) * S + 5 + ch];
+            s_feat[P.C * threadIdx.x + ch] = (float)f;
+          }
+        __syncthreads();
+        float *out = P.gfeat + (size_t)P.C * i0;
+        for (int j = threadIdx.x; j < P.C * nb; j += 256) out[j] = P.accumulate ? out[j] + s_feat[j] : s_feat[j];
+      } else if (i < P.n) {
+        for (int ch = 0; ch < P.C; ch++) {
+          double f = 0;
+          for (int v = vbeg; v < vend; v++) f += P.accg[((size_t)v * P.n + i) * S + 5 + ch];
+          put(P.gfeat, (size_t)i * P.C + ch, f, P.accumulate);
         }
       }
     }
-    if (P.gpos)
-      for (int a = 0; a < 3; a++) put(P.gpos, 3 * (size_t)i + a, dp[a], P.accumulate);
-    if (P.gscale) put(P.gscale, i, dr, P.accumulate);
-    if (P.gop) put(P.gop, i, dop, P.accumulate);
-    if (P.gfeat)
-      for (int ch = 0; ch < P.C; ch++) {
-        double f = 0;
-        for (int v = vbeg; v < vend; v++) f += P.accg[((size_t)v * P.n + i) * S + 5 + ch];
-        put(P.gfeat, (size_t)i * P.C + ch, f, P.accumulate);
-      }
+    __syncthreads();                           // LDS reuse by the next 256 spheres
   }
   if (cam_view < 0) return;
   const unsigned lane = lane_id(), w = threadIdx.x / WAVE;
@@ -873,7 +904,16 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
       const bool cam = gr->cam_R || gr->cam_t;
       const unsigned nb = (unsigned)min((pr->n + 255) / 256, SPLAT_CAM_BLOCKS);
       const int cam_view = cam && vend - vbeg == 1 ? vbeg : -1;
-      hipLaunchKernelGGL(k_sphere_grads, dim3(nb), dim3(256), 0, stream, vt, P, vbeg, vend, cam_view);
+      if (channel_bucket(A.C) <= 4) {
+        switch (channel_bucket(A.C)) {
+          case 1: hipLaunchKernelGGL(k_sphere_grads<1>, dim3(nb), dim3(256), 0, stream, vt, P, vbeg, vend, cam_view); break;
+          case 2: hipLaunchKernelGGL(k_sphere_grads<2>, dim3(nb), dim3(256), 0, stream, vt, P, vbeg, vend, cam_view); break;
+          case 3: hipLaunchKernelGGL(k_sphere_grads<3>, dim3(nb), dim3(256), 0, stream, vt, P, vbeg, vend, cam_view); break;
+          default: hipLaunchKernelGGL(k_sphere_grads<4>, dim3(nb), dim3(256), 0, stream, vt, P, vbeg, vend, cam_view); break;
+        }
+      } else {
+        hipLaunchKernelGGL(k_sphere_grads<8>, dim3(nb), dim3(256), 0, stream, vt, P, vbeg, vend, cam_view);
+      }
       if (cam_view >= 0) hipLaunchKernelGGL(k_cam_final, dim3(1), dim3(256), 0, stream, P, (int)nb, cam_view);
       if (cam && vend - vbeg > 1)
         hipLaunchKernelGGL(k_cam_grad_sphere, dim3(min(nb, 512u), vend - vbeg), dim3(256), 0, stream, P, vbeg);
