@@ -394,6 +394,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
+    // the wave walks its quadrant's list (a recorded sphere is never split
+    // over several steps, as with per-block lists, where the reduction and
+    // the gradient arithmetic would run once per block it reaches)
     const int lc = __builtin_amdgcn_readfirstlane(s_l.cnt[wq]);
     for (int k = 0; k < lc; k++) {
       const int idx = __builtin_amdgcn_readfirstlane((int)s_l.idx[wq][k]);

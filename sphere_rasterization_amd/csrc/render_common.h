@@ -51,12 +51,15 @@ struct TilePix {
 };
 
 // Thread tid of a tile's workgroup: wave w = tid / 64 owns the 8x8 quadrant
-// (w & 1, w >> 1) of the 16x16 tile, lane l its pixel (l & 7, l >> 3).
+// (w & 1, w >> 1) of the 16x16 tile, its 16-lane group g = (tid / 16) & 3 the
+// 4x4 block (g & 1, g >> 1) of that quadrant, and lane l the pixel
+// (l & 3, (l >> 2) & 3) of the block.
 __device__ __forceinline__ TilePix tile_pixel(const ViewDev &c, int gtile, unsigned tid) {
   const int lt = gtile - c.tile_off;
   const int ty = lt / c.TW, tx = lt - ty * c.TW;
-  const unsigned w = tid >> 6, l = tid & 63u;
-  const int li = (int)((w & 1u) * 8u + (l & 7u)), lj = (int)((w >> 1) * 8u + (l >> 3));
+  const unsigned w = tid >> 6, g = (tid >> 4) & 3u, l = tid & 15u;
+  const int li = (int)((w & 1u) * 8u + (g & 1u) * 4u + (l & 3u));
+  const int lj = (int)((w >> 1) * 8u + (g >> 1) * 4u + (l >> 2));
   TilePix t;
   t.i = tx * TILE + li;
   t.j = ty * TILE + lj;
@@ -109,6 +112,67 @@ __device__ __forceinline__ void build_quad_lists(QuadLists &L, unsigned mask) {
     }
   }
   if (tid < 4) L.cnt[tid] = L.wcnt[0][tid] + L.wcnt[1][tid] + L.wcnt[2][tid] + L.wcnt[3][tid];
+  __syncthreads();
+}
+
+// Which 4x4 blocks of the tile at (x0, y0) the pixel rectangle of d reaches:
+// bit 4 w + g for block g of wave w's quadrant (as in tile_pixel).
+__device__ __forceinline__ unsigned block_mask(const TilePix &tp, const DrawRec &d) {
+  const int x0 = (int)tp.x0, y0 = (int)tp.y0;
+  unsigned cm = 0, rm = 0;
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    cm |= (unsigned)((d.i0 <= x0 + 4 * c + 3) & (d.i1 >= x0 + 4 * c)) << c;
+    rm |= (unsigned)((d.j0 <= y0 + 4 * c + 3) & (d.j1 >= y0 + 4 * c)) << c;
+  }
+  unsigned m = 0;
+#pragma unroll
+  for (int ry = 0; ry < 4; ry++)
+#pragma unroll
+    for (int cx = 0; cx < 4; cx++) {
+      const int bit = 4 * ((cx >> 1) + 2 * (ry >> 1)) + (cx & 1) + 2 * (ry & 1);
+      m |= ((cm >> cx) & (rm >> ry) & 1u) << bit;
+    }
+  return m;
+}
+
+// Per-block lists of the staged batch (in batch order): each 16-lane group then
+// walks only the entries that reach its 4x4 block.
+template <int B>
+struct BlockLists {
+  unsigned char idx[16][B];   // B: entries staged per batch
+  int cnt[16];
+  int woff[4][16];        // per wave: first slot of its entries in each list
+};
+
+// All 256 threads call this with their staged entry's mask (0 if none); it
+// synchronises three times and leaves L ready to read.
+template <int B>
+__device__ __forceinline__ void build_block_lists(BlockLists<B> &L, unsigned mask) {
+  const unsigned tid = threadIdx.x, lane = tid & 63u, sw = tid >> 6;
+  const uint64_t below = lane ? (~0ull >> (64u - lane)) : 0ull;
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    const uint64_t b = __builtin_amdgcn_ballot_w64(((mask >> q) & 1u) != 0u);
+    if (lane == 0) L.woff[sw][q] = __popcll(b);
+  }
+  __syncthreads();
+  if (tid < 16) {
+    int run = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; s2++) {
+      const int c = L.woff[s2][tid];
+      L.woff[s2][tid] = run;
+      run += c;
+    }
+    L.cnt[tid] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    const uint64_t b = __builtin_amdgcn_ballot_w64(((mask >> q) & 1u) != 0u);
+    if ((mask >> q) & 1u) L.idx[q][L.woff[sw][q] + __popcll(b & below)] = (unsigned char)tid;
+  }
   __syncthreads();
 }
 

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   constexpr int NF4 = (CM + 2 + 3) / 4;
   constexpr int NE = 3 + NF4;
   __shared__ float4 s_e[NE][256];
-  __shared__ QuadLists s_l;
+  __shared__ BlockLists<256> s_l;
   if (*A.overflow) return;
   const int gtile = blockIdx.x;
   const int view = view_of_tile(vt, gtile);
@@ -41,6 +41,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
   const SphereRay ray = sphere_ray(c, tp);
   const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // this wave's quadrant
+  const int sb = wq * 4 + (int)((threadIdx.x >> 4) & 3u);                  // this lane's 4x4 block
   const float tau = A.tau;
   float N = A.bg_weight;
   float S[CM];
@@ -73,31 +74,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       for (int ch = 0; ch < 4 * NF4 - 2; ch++) t[2 + ch] = ch < CM && ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
 #pragma unroll
       for (int f = 0; f < NF4; f++) s_e[3 + f][threadIdx.x] = make_float4(t[4 * f], t[4 * f + 1], t[4 * f + 2], t[4 * f + 3]);
-      mask = quadrant_mask(tp, d);
+      mask = block_mask(tp, d);
     }
-    build_quad_lists(s_l, mask);
-    // the list, its length and every index are the same for the whole wave
-    const int cnt = __builtin_amdgcn_readfirstlane(s_l.cnt[wq]);
+    build_block_lists(s_l, mask);
+    // Each 16-lane group walks the list of its own 4x4 block, so one step of
+    // the wave handles up to four different entries. cmin / cmax: shortest and
+    // longest of the wave's four lists (uniform).
+    const int cnt = s_l.cnt[sb];
+    const int c0 = s_l.cnt[4 * wq], c1 = s_l.cnt[4 * wq + 1], c2 = s_l.cnt[4 * wq + 2], c3 = s_l.cnt[4 * wq + 3];
+    const int cmin = __builtin_amdgcn_readfirstlane(min(min(c0, c1), min(c2, c3)));
+    const int cmax = __builtin_amdgcn_readfirstlane(max(max(c0, c1), max(c2, c3)));
+    const unsigned char *lst = s_l.idx[sb];
     // One pass over four entries; REC: some lane of the wave still records its
     // first contributing spheres (only the first few hits of each pixel do).
-    // FULL: all four entries exist (no end-of-list checks inside the group).
+    // FULL: all four entries exist in every group's list; otherwise a lane past
+    // its list's end reads staged slot 0 (always filled, finite) and is masked.
     auto four_entries = [&](auto REC, auto FULL, int k, uint32_t four) {
 #pragma unroll
       for (int u = 0; u < 4; u++) {
-        if constexpr (!decltype(FULL)::value)
-          if (k + u >= cnt) break;
-        const int idx = (int)((four >> (8 * u)) & 0xffu);
+        bool valid = true;
+        int idx = (int)((four >> (8 * u)) & 0xffu);
+        if constexpr (!decltype(FULL)::value) {
+          if (k + u >= cmax) break;
+          valid = k + u < cnt;
+          idx = valid ? idx : 0;
+        }
         float t[4 * NF4];
 #pragma unroll
         for (int f = 0; f < NF4; f++) {
           const float4 x = s_e[3 + f][idx];
           t[4 * f] = x.x; t[4 * f + 1] = x.y; t[4 * f + 2] = x.z; t[4 * f + 3] = x.w;
         }
-        active = active & !(N > t[1]);           // no later sphere can matter (& : no short-circuit branch)
+        active = active & !(valid & (N > t[1]));  // no later sphere can matter (& : no short-circuit branch)
         const double num = sphere_num(ray, __builtin_bit_cast(double2, s_e[0][idx]),
                                       __builtin_bit_cast(double2, s_e[1][idx]),
                                       __builtin_bit_cast(double2, s_e[2][idx]));
-        const bool hit = active & (num > 0.0);
+        const bool hit = active & valid & (num > 0.0);
         // 0 or 1 times a finite weight: straight-line code, no branch around it
         const float w = (hit ? 1.0f : 0.0f) * (t[0] * (float)(num * ray.g));
         N += w;
@@ -117,11 +129,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     };
     if (ballot64(active)) {
       bool recording = ballot64(need && active) != 0;
-      const int cnt4 = cnt & ~3;
+      const int cmin4 = cmin & ~3;
       int k = 0;
-      for (; k < cnt4; k += 4) {
-        const uint32_t four =
-            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(&s_l.idx[wq][k]));
+      for (; k < cmin4; k += 4) {
+        const uint32_t four = *reinterpret_cast<const uint32_t *>(lst + k);
         if (recording) {
           four_entries(std::true_type{}, std::true_type{}, k, four);
           recording = ballot64(need && active) != 0;
@@ -130,10 +141,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
         }
         if (ballot64(active) == 0) break;
       }
-      if (k == cnt4 && k < cnt && ballot64(active)) {     // the last one to three entries
-        const uint32_t four =
-            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(&s_l.idx[wq][k]));
-        four_entries(std::true_type{}, std::false_type{}, k, four);
+      if (k == cmin4) {                          // the groups' remaining entries
+        for (; k < cmax && ballot64(active); k += 4) {
+          const uint32_t four = *reinterpret_cast<const uint32_t *>(lst + k);
+          four_entries(std::true_type{}, std::false_type{}, k, four);
+        }
       }
     }
     if (__syncthreads_count(active) == 0) break;
