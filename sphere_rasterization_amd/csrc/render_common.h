@@ -296,10 +296,9 @@ __device__ __forceinline__ float splat_alpha(const ViewDev &c, double pxr, doubl
                                              double &dx, double &dy) {
   dx = pxr - uv.x;
   dy = pyr - uv.y;
-  if (LIDAR) {
+  if (LIDAR) {                                    // columns wrap: the nearer image of the centre
     const double half = 0.5 * (double)c.W;
-    if (dx >= half) dx -= (double)c.W;
-    else if (dx < -half) dx += (double)c.W;
+    dx = dx >= half ? dx - (double)c.W : (dx < -half ? dx + (double)c.W : dx);
   }
   const double power = __builtin_fma(dx, __builtin_fma(ab.x, dx, ab.y * dy), (co.x * dy) * dy);
   G = __expf(-(float)power);

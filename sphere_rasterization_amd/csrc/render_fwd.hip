@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
   if ((c.kind == SPLAT_CAM_SPHERICAL) != LIDAR) return;
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
-  const unsigned wq = threadIdx.x >> 6;
+  const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // this wave's quadrant
   // Transmittance runs in fp64 (same issue rate as fp32 on CDNA4): it is the
   // product of every (1 - alpha) so far and the backward divides it back out.
   double T = 1.0;
@@ -216,22 +216,46 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
-    const int cnt = s_l.cnt[wq];
-    if (ballot64(active)) {
-      for (int k = 0; k < cnt; k++) {
-        const int idx = s_l.idx[wq][k];
-        float G, og;
-        double dx, dy;
-        const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
-        const bool hit = active && al >= amin;
-        const float w = hit ? (float)(T * (double)al) : 0.0f;
+    // the list, its length and every index are the same for the whole wave
+    const int cnt = __builtin_amdgcn_readfirstlane(s_l.cnt[wq]);
+    // one entry: straight-line code (non-short-circuit tests, the weight a 0/1
+    // factor times a finite product)
+    auto one = [&](int idx) {
+      float G, og;
+      double dx, dy;
+      const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+      const bool hit = active & (al >= amin);
+      const float w = (hit ? 1.0f : 0.0f) * (float)(T * (double)al);
 #pragma unroll
-        for (int ch = 0; ch < NF; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][idx], S[ch]);
-        T = hit ? T * (1.0 - (double)al) : T;
-        last = hit ? b - start + (uint32_t)idx + 1u : last;
-        active = active && !(T < tmin);            // include, then stop
-        if ((k & 3) == 3 && ballot64(active) == 0) break;
+      for (int ch = 0; ch < NF; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][idx], S[ch]);
+      T = hit ? T * (1.0 - (double)al) : T;
+      last = hit ? b - start + (uint32_t)idx + 1u : last;
+      active = active & !(T < tmin);            // include, then stop
+    };
+    if (NF > 8) {
+      // many channels: one entry per step keeps the staged features out of registers
+      if (ballot64(active))
+        for (int k = 0; k < cnt; k++) {
+          one(__builtin_amdgcn_readfirstlane((int)s_l.idx[wq][k]));
+          if ((k & 3) == 3 && ballot64(active) == 0) break;
+        }
+    } else if (ballot64(active)) {
+      const int cnt4 = cnt & ~3;
+      bool live = true;
+      for (int k = 0; k < cnt4; k += 4) {
+        const uint32_t four =
+            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(&s_l.idx[wq][k]));
+        one((int)(four & 0xffu));
+        one((int)((four >> 8) & 0xffu));
+        one((int)((four >> 16) & 0xffu));
+        one((int)(four >> 24));
+        if (ballot64(active) == 0) {
+          live = false;
+          break;
+        }
       }
+      if (live)
+        for (int k = cnt4; k < cnt; k++) one(__builtin_amdgcn_readfirstlane((int)s_l.idx[wq][k]));
     }
     if (__syncthreads_count(active) == 0) break;
   }
