@@ -186,16 +186,16 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
-    for (int k = s_l.cnt[wq] - 1; k >= 0; k--) {
-      const int idx = s_l.idx[wq][k];
+    // One entry of the wave's list (uniform index), back to front.
+    auto entry = [&](const int idx) {
       const uint32_t pos = (uint32_t)(lo + idx);
-      if (pos >= wlast) continue;               // beyond every pixel of the wave
+      if (pos >= wlast) return;                 // beyond every pixel of the wave
       const double2 ab = s_ab[idx], co = s_co[idx];
       float G, og;
       double dx, dy;
       const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
-      const bool act = pos < lastp && al >= amin;
-      if (ballot64(act) == 0) continue;
+      const bool act = (pos < lastp) & (al >= amin);
+      if (ballot64(act) == 0) return;
       double vg[6];
       float vf[NF];
 #pragma unroll
@@ -265,6 +265,19 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
           const float r = row_sum_to_last(vf[q]);
           if ((lane & 15u) == 15u) atomicAdd(&s_af[idx][q], r);
         }
+      }
+        };
+    {
+      const int cnt_q = __builtin_amdgcn_readfirstlane(s_l.cnt[wq]);
+      int k = cnt_q - 1;
+      for (; k >= 0 && ((k + 1) & 3); k--) entry(__builtin_amdgcn_readfirstlane((int)s_l.idx[wq][k]));
+      for (; k >= 3; k -= 4) {                  // four indices per list read
+        const uint32_t four =
+            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(&s_l.idx[wq][k - 3]));
+        entry((int)(four >> 24));
+        entry((int)((four >> 16) & 0xffu));
+        entry((int)((four >> 8) & 0xffu));
+        entry((int)(four & 0xffu));
       }
     }
     __syncthreads();
