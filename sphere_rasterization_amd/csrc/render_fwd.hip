@@ -164,22 +164,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
 }
 
 // ---------------------------------------------------------------------------
-// Gaussian splats (alpha blending); LIDAR = spherical view rendering
-// expected depth and opacity.
+// Gaussian splats (alpha blending) in pinhole views.
 // ---------------------------------------------------------------------------
-template <int CM, bool LIDAR>
-__global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
-  constexpr int NF = LIDAR ? 1 : CM;
+template <int CM>
+__global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A, int tile_begin) {
+  constexpr int NF = CM;
   __shared__ double2 s_uv[256];     // tile-relative centre
   __shared__ double2 s_ab[256];     // a/2, b
   __shared__ double2 s_co[256];     // c/2, opacity
   __shared__ float s_f[NF][256];    // features, or depth for spherical views
   __shared__ QuadLists s_l;
   if (*A.overflow) return;
-  const int gtile = blockIdx.x;
+  const int gtile = tile_begin + (int)blockIdx.x;
   const int view = view_of_tile(vt, gtile);
   const ViewDev &c = vt.v[view];
-  if ((c.kind == SPLAT_CAM_SPHERICAL) != LIDAR) return;
+  if (c.kind == SPLAT_CAM_SPHERICAL) return;
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
   const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // this wave's quadrant
@@ -202,17 +201,13 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
     if (e < end) {
       const uint32_t rid = A.vals[e];
       const DrawRec d = A.draw[rid];
-      s_uv[threadIdx.x] = stage_uv(c, tp, d, LIDAR);
+      s_uv[threadIdx.x] = stage_uv(c, tp, d, false);
       const Conic cn = stage_conic(d);
       s_ab[threadIdx.x] = cn.ab;
       s_co[threadIdx.x] = cn.co;
-      if (LIDAR) {
-        s_f[0][threadIdx.x] = A.aux[rid].depth;
-      } else {
-        const long long id = (long long)rid - vbase;
+      const long long id = (long long)rid - vbase;
 #pragma unroll
-        for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
-      }
+      for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
@@ -223,7 +218,7 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
     auto one = [&](int idx) {
       float G, og;
       double dx, dy;
-      const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+      const float al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
       const bool hit = active & (al >= amin);
       const float w = (hit ? 1.0f : 0.0f) * (float)(T * (double)al);
 #pragma unroll
@@ -263,26 +258,200 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A) {
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
   const size_t plane = (size_t)c.W * c.H;
   float *img = A.img + c.img_off + (size_t)tp.j * c.W + tp.i;
-  if (LIDAR) {
-    img[0] = S[0];
-    img[plane] = (float)(1.0 - T);
-  } else {
 #pragma unroll
-    for (int ch = 0; ch < CM; ch++)
-      if (ch < A.C) img[ch * plane] = S[ch];
+  for (int ch = 0; ch < CM; ch++)
+    if (ch < A.C) img[ch * plane] = S[ch];
+  if (A.T_final) A.T_final[p] = (float)T;
+  if (A.last) A.last[p] = last;
+}
+
+// ---------------------------------------------------------------------------
+// Spherical (lidar) views: long tile lists split four ways inside the tile.
+// A range view's tiles hold lists tens of thousands of entries long, and a ray
+// that sees sky walks thousands of them before (if ever) its transmittance
+// stops it; with one wave per 8x8 quadrant the few longest tiles set the
+// kernel's time. Here a workgroup of 1024 threads stages 1024 entries per
+// batch, and four waves share each quadrant: the wave quadrant list is cut
+// into four consecutive parts, each walked from T = 1 (partial colour S_j,
+// transmittance T_j, last entry). The parts are then chained per pixel:
+// S += T S_j, T *= T_j, as long as T T_j stays at or above T_min (T is
+// non-increasing along a part, so no entry of it can have stopped the pixel).
+// Otherwise the stop lies inside part j, and its wave walks that part again
+// from the chained T and S with the ordinary per-entry stop.
+// ---------------------------------------------------------------------------
+constexpr int LB = 1024;                 // threads and staged entries per batch
+
+__global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int tile_begin) {
+  __shared__ double2 s_uv[LB];           // tile-relative centre
+  __shared__ double2 s_ab[LB];           // a/2, b
+  __shared__ double2 s_co[LB];           // c/2, opacity
+  __shared__ float s_dep[LB];            // range
+  __shared__ uint16_t s_idx[4][LB];      // per-quadrant lists of the batch
+  __shared__ int s_woff[16][4];          // per wave: first slot of its entries in each list
+  __shared__ int s_cnt[4];
+  __shared__ float s_pS[4][256];         // per part and pixel: partial colour,
+  __shared__ double s_pT[4][256];        //   transmittance,
+  __shared__ uint32_t s_pL[4][256];      //   last composited entry (0: none)
+  if (*A.overflow) return;
+  const int gtile = tile_begin + (int)blockIdx.x;
+  const int view = view_of_tile(vt, gtile);
+  const ViewDev &c = vt.v[view];
+  if (c.kind != SPLAT_CAM_SPHERICAL) return;
+  const unsigned tid = threadIdx.x, pix = tid & 255u;
+  const int part = __builtin_amdgcn_readfirstlane((int)(tid >> 8));           // 0..3
+  const int wq = __builtin_amdgcn_readfirstlane((int)((tid >> 6) & 3u));     // quadrant
+  const unsigned lane = tid & 63u, sw = tid >> 6;
+  const TilePix tp = tile_pixel(c, gtile, pix);
+  const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
+  // running state of this thread's pixel (the same in all four copies)
+  double T = 1.0;
+  float S = 0.0f;
+  uint32_t last = 0;
+  bool active = tp.inside;
+  const float amin = A.alpha_min, amax = A.alpha_max;
+  const double tmin = (double)A.T_min;
+  const double pxr = tp.pxr, pyr = tp.pyr;
+
+  for (uint32_t b = start; b < end; b += LB) {
+    const uint32_t e = b + tid;
+    unsigned mask = 0;
+    if (e < end) {
+      const uint32_t rid = A.vals[e];
+      const DrawRec d = A.draw[rid];
+      s_uv[tid] = stage_uv(c, tp, d, true);
+      const Conic cn = stage_conic(d);
+      s_ab[tid] = cn.ab;
+      s_co[tid] = cn.co;
+      s_dep[tid] = A.aux[rid].depth;
+      mask = quadrant_mask(tp, d);
+    }
+    // per-quadrant lists, in batch order
+    const uint64_t below = lane ? (~0ull >> (64u - lane)) : 0ull;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint64_t bq = ballot64(((mask >> q) & 1u) != 0u);
+      if (lane == 0) s_woff[sw][q] = __popcll(bq);
+    }
+    __syncthreads();
+    if (tid < 4) {
+      int run = 0;
+      for (int w2 = 0; w2 < 16; w2++) {
+        const int x = s_woff[w2][tid];
+        s_woff[w2][tid] = run;
+        run += x;
+      }
+      s_cnt[tid] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint64_t bq = ballot64(((mask >> q) & 1u) != 0u);
+      if ((mask >> q) & 1u) s_idx[q][s_woff[sw][q] + __popcll(bq & below)] = (uint16_t)tid;
+    }
+    __syncthreads();
+    // this wave's part of its quadrant's list
+    const int L = __builtin_amdgcn_readfirstlane(s_cnt[wq]);
+    const int k0 = (L * part) / 4, k1 = (L * (part + 1)) / 4;
+    auto one = [&](int idx, double &Tx, float &Sx, uint32_t &lx, bool &ax) {
+      float G, og;
+      double dx, dy;
+      const float al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+      const bool hit = ax & (al >= amin);
+      const float w = (hit ? 1.0f : 0.0f) * (float)(Tx * (double)al);
+      Sx = __builtin_fmaf(w, s_dep[idx], Sx);
+      Tx = hit ? Tx * (1.0 - (double)al) : Tx;
+      lx = hit ? b - start + (uint32_t)idx + 1u : lx;
+      ax = ax & !(Tx < tmin);
+    };
+    // 1. the part from T = 1 (a local stop below T_min ends it: the chained T is smaller)
+    {
+      double Tj = 1.0;
+      float Sj = 0.0f;
+      uint32_t lj = 0;
+      bool aj = active;
+      for (int k = k0; k < k1; k++) {
+        one(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]), Tj, Sj, lj, aj);
+        if (((k - k0) & 3) == 3 && ballot64(aj) == 0) break;
+      }
+      s_pS[part][pix] = Sj;
+      s_pT[part][pix] = Tj;
+      s_pL[part][pix] = lj;
+    }
+    __syncthreads();
+    // 2. chain the parts (every copy of the pixel computes the same)
+    int stop_part = -1;
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (stop_part < 0) {
+          const double Tj = s_pT[j][pix];
+          if (T * Tj >= tmin) {
+            S = __builtin_fmaf((float)T, s_pS[j][pix], S);
+            const uint32_t lj = s_pL[j][pix];
+            last = lj ? lj : last;
+            T *= Tj;
+          } else {
+            stop_part = j;
+          }
+        }
+      }
+    }
+    __syncthreads();                               // the partials are read before step 3 reuses them
+    // 3. the part holding the stop, walked again from the chained state
+    if (ballot64(stop_part == part)) {
+      bool ax = stop_part == part;
+      double Tx = T;
+      float Sx = S;
+      uint32_t lx = last;
+      for (int k = k0; k < k1; k++) {
+        one(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]), Tx, Sx, lx, ax);
+        if (((k - k0) & 3) == 3 && ballot64(ax) == 0) break;
+      }
+      if (stop_part == part) {
+        s_pS[0][pix] = Sx;
+        s_pT[0][pix] = Tx;
+        s_pL[0][pix] = lx;
+      }
+    }
+    __syncthreads();
+    if (stop_part >= 0) {                          // stopped in this batch: final state
+      S = s_pS[0][pix];
+      T = s_pT[0][pix];
+      last = s_pL[0][pix];
+      active = false;
+    }
+    if (__syncthreads_count(active) == 0) break;
   }
+  if (part != 0 || !tp.inside) return;
+  const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
+  const size_t plane = (size_t)c.W * c.H;
+  float *img = A.img + c.img_off + (size_t)tp.j * c.W + tp.i;
+  img[0] = S;
+  img[plane] = (float)(1.0 - T);
   if (A.T_final) A.T_final[p] = (float)T;
   if (A.last) A.last[p] = last;
 }
 
 template <int CM>
-int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, bool has_pin, bool has_sph, hipStream_t stream) {
+int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t stream) {
   dim3 grid(vt.total_tiles), block(256);
   if (kind == SPLAT_PRIM_SPHERE) {
     hipLaunchKernelGGL(k_fwd_sphere<CM>, grid, block, 0, stream, vt, A);
   } else {
-    if (has_pin) hipLaunchKernelGGL((k_fwd_alpha<CM, false>), grid, block, 0, stream, vt, A);
-    if (has_sph) hipLaunchKernelGGL((k_fwd_alpha<1, true>), grid, block, 0, stream, vt, A);
+    // one launch per run of consecutive views of one kind, over that run's tiles only
+    for (int v0 = 0; v0 < vt.n;) {
+      const int kind0 = vt.v[v0].kind;
+      int v1 = v0 + 1;
+      while (v1 < vt.n && vt.v[v1].kind == kind0) v1++;
+      const int t0 = vt.v[v0].tile_off, t1 = v1 < vt.n ? vt.v[v1].tile_off : vt.total_tiles;
+      if (t1 > t0) {
+        if (kind0 == SPLAT_CAM_SPHERICAL)
+          hipLaunchKernelGGL(k_fwd_lidar, dim3(t1 - t0), dim3(LB), 0, stream, vt, A, t0);
+        else
+          hipLaunchKernelGGL(k_fwd_alpha<CM>, dim3(t1 - t0), block, 0, stream, vt, A, t0);
+      }
+      v0 = v1;
+    }
   }
   SPLAT_LAUNCH_CHECK();
   return SPLAT_OK;
@@ -292,20 +461,15 @@ int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, bool has_pin,
 
 int launch_render_fwd(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t stream) {
   if (vt.total_tiles == 0) return SPLAT_OK;
-  bool has_pin = false, has_sph = false;
-  for (int v = 0; v < vt.n; v++) {
-    if (vt.v[v].kind == SPLAT_CAM_SPHERICAL) has_sph = true;
-    else has_pin = true;
-  }
   switch (channel_bucket(A.C)) {
-    case 1: return launch_fwd_cm<1>(vt, A, kind, has_pin, has_sph, stream);
-    case 2: return launch_fwd_cm<2>(vt, A, kind, has_pin, has_sph, stream);
-    case 3: return launch_fwd_cm<3>(vt, A, kind, has_pin, has_sph, stream);
-    case 4: return launch_fwd_cm<4>(vt, A, kind, has_pin, has_sph, stream);
-    case 8: return launch_fwd_cm<8>(vt, A, kind, has_pin, has_sph, stream);
-    case 16: return launch_fwd_cm<16>(vt, A, kind, has_pin, has_sph, stream);
-    case 32: return launch_fwd_cm<32>(vt, A, kind, has_pin, has_sph, stream);
-    case 64: return launch_fwd_cm<64>(vt, A, kind, has_pin, has_sph, stream);
+    case 1: return launch_fwd_cm<1>(vt, A, kind, stream);
+    case 2: return launch_fwd_cm<2>(vt, A, kind, stream);
+    case 3: return launch_fwd_cm<3>(vt, A, kind, stream);
+    case 4: return launch_fwd_cm<4>(vt, A, kind, stream);
+    case 8: return launch_fwd_cm<8>(vt, A, kind, stream);
+    case 16: return launch_fwd_cm<16>(vt, A, kind, stream);
+    case 32: return launch_fwd_cm<32>(vt, A, kind, stream);
+    case 64: return launch_fwd_cm<64>(vt, A, kind, stream);
   }
   return SPLAT_ERR_UNSUPPORTED;
 }
