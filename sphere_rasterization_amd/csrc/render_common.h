@@ -298,7 +298,8 @@ __device__ __forceinline__ float splat_alpha(const ViewDev &c, double pxr, doubl
   dy = pyr - uv.y;
   if (LIDAR) {                                    // columns wrap: the nearer image of the centre
     const double half = 0.5 * (double)c.W;
-    dx = dx >= half ? dx - (double)c.W : (dx < -half ? dx + (double)c.W : dx);
+    const double up = dx >= half ? (double)c.W : 0.0, dn = dx < -half ? (double)c.W : 0.0;
+    dx = dx - up + dn;                              // selects, no branch; exact (one of them is 0)
   }
   const double power = __builtin_fma(dx, __builtin_fma(ab.x, dx, ab.y * dy), (co.x * dy) * dy);
   G = __expf(-(float)power);

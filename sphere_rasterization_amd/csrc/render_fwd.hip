@@ -363,16 +363,31 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
       lx = hit ? b - start + (uint32_t)idx + 1u : lx;
       ax = ax & !(Tx < tmin);
     };
+    // the wave's walk over list positions [k0, k1): single entries up to a
+    // multiple of four, then four indices per LDS read (their records are
+    // read ahead of the dependent arithmetic), until no lane is left
+    auto walk = [&](double &Tx, float &Sx, uint32_t &lx, bool &ax) {
+      int k = k0;
+      for (; k < k1 && (k & 3); k++) one(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]), Tx, Sx, lx, ax);
+      for (; k + 4 <= k1; k += 4) {
+        if (ballot64(ax) == 0) return;
+        const uint64_t four = *reinterpret_cast<const uint64_t *>(&s_idx[wq][k]);
+        const uint32_t lo4 = __builtin_amdgcn_readfirstlane((uint32_t)four);
+        const uint32_t hi4 = __builtin_amdgcn_readfirstlane((uint32_t)(four >> 32));
+        one((int)(lo4 & 0xffffu), Tx, Sx, lx, ax);
+        one((int)(lo4 >> 16), Tx, Sx, lx, ax);
+        one((int)(hi4 & 0xffffu), Tx, Sx, lx, ax);
+        one((int)(hi4 >> 16), Tx, Sx, lx, ax);
+      }
+      for (; k < k1; k++) one(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]), Tx, Sx, lx, ax);
+    };
     // 1. the part from T = 1 (a local stop below T_min ends it: the chained T is smaller)
     {
       double Tj = 1.0;
       float Sj = 0.0f;
       uint32_t lj = 0;
       bool aj = active;
-      for (int k = k0; k < k1; k++) {
-        one(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]), Tj, Sj, lj, aj);
-        if (((k - k0) & 3) == 3 && ballot64(aj) == 0) break;
-      }
+      walk(Tj, Sj, lj, aj);
       s_pS[part][pix] = Sj;
       s_pT[part][pix] = Tj;
       s_pL[part][pix] = lj;
@@ -403,10 +418,7 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
       double Tx = T;
       float Sx = S;
       uint32_t lx = last;
-      for (int k = k0; k < k1; k++) {
-        one(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]), Tx, Sx, lx, ax);
-        if (((k - k0) & 3) == 3 && ballot64(ax) == 0) break;
-      }
+      walk(Tx, Sx, lx, ax);
       if (stop_part == part) {
         s_pS[0][pix] = Sx;
         s_pT[0][pix] = Tx;
