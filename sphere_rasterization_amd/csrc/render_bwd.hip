@@ -97,9 +97,9 @@ __global__ __launch_bounds__(256) void k_zero(ZeroRanges z) {
 // geometric terms of the offset (dx, dy); those terms and their sums are fp64,
 // colour and opacity terms fp32.
 // ---------------------------------------------------------------------------
-template <int CM, bool LIDAR>
+template <int CM>
 __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int tile_begin) {
-  constexpr int NF = LIDAR ? 1 : CM;        // fp32 values per entry: features (or depth)
+  constexpr int NF = CM;                    // fp32 values per entry: features
   constexpr int NFP = NF | 1;               // odd row stride: lanes of one entry hit distinct banks
   constexpr int NG = (NF + 7) / 8;          // groups of eight for the transposed reduction
   // entries staged per batch: fewer with many channels, so that two or more
@@ -112,14 +112,14 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   __shared__ float s_f[BT][NFS];
   __shared__ uint32_t s_rid[BT];
   __shared__ double s_ag[BT][7];           // du, dv, d_ca, d_cb, d_cc, d_opac (odd stride)
-  __shared__ float s_af[BT][NFP];          // d_feat (or d_depth)
+  __shared__ float s_af[BT][NFP];          // d_feat
   __shared__ QuadLists s_l;
   __shared__ uint32_t s_maxlast;
   if (*A.overflow) return;
   const int gtile = tile_begin + blockIdx.x;
   const int view = view_of_tile(vt, gtile);
   const ViewDev &c = vt.v[view];
-  if ((c.kind == SPLAT_CAM_SPHERICAL) != LIDAR) return;
+  if (c.kind == SPLAT_CAM_SPHERICAL) return;
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile];
   const uint32_t len = A.ranges[2 * gtile + 1] - start;
@@ -131,22 +131,16 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   const double pxr = tp.pxr, pyr = tp.pyr;
   uint32_t lastp = 0;
   double T = 1.0;      // transmittance after the current entry
-  float g[LIDAR ? 2 : CM];
-  // behind the current entry: depth composited (spherical views), or the
-  // composited colour projected on the pixel's upstream gradient, sum_ch Sb_ch g_ch
+  float g[CM];
+  // behind the current entry: the composited colour projected on the pixel's
+  // upstream gradient, sum_ch Sb_ch g_ch
   float Sb = 0.0f;
-  if (LIDAR) {
-    g[0] = tp.inside ? A.dimg[pofs] : 0.0f;
-    g[1] = tp.inside ? A.dimg[pofs + plane] : 0.0f;
-  } else {
 #pragma unroll
-    for (int ch = 0; ch < CM; ch++) g[ch] = (tp.inside && ch < A.C) ? A.dimg[pofs + ch * plane] : 0.0f;
-  }
+  for (int ch = 0; ch < CM; ch++) g[ch] = (tp.inside && ch < A.C) ? A.dimg[pofs + ch * plane] : 0.0f;
   if (tp.inside) {
     lastp = min(A.last[p], len);     // a forward buffer never exceeds the tile's list
     T = (double)A.T_final[p];
   }
-  const double Tfin = T;
   if (threadIdx.x == 0) s_maxlast = 0;
   __syncthreads();
   if (lastp) atomicMax(&s_maxlast, lastp);
@@ -168,17 +162,13 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
       const uint32_t rid = A.vals[start + lo + threadIdx.x];
       const DrawRec d = A.draw[rid];
       s_rid[threadIdx.x] = rid;
-      s_uv[threadIdx.x] = stage_uv(c, tp, d, LIDAR);
+      s_uv[threadIdx.x] = stage_uv(c, tp, d, false);
       const Conic cn = stage_conic(d);
       s_ab[threadIdx.x] = cn.ab;
       s_co[threadIdx.x] = cn.co;
-      if (LIDAR) {
-        s_f[threadIdx.x][0] = A.aux[rid].depth;
-      } else {
-        const long long id = (long long)rid - vbase;
+      const long long id = (long long)rid - vbase;
 #pragma unroll
-        for (int ch = 0; ch < CM; ch++) s_f[threadIdx.x][ch] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
-      }
+      for (int ch = 0; ch < CM; ch++) s_f[threadIdx.x][ch] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
 #pragma unroll
       for (int q = 0; q < 6; q++) s_ag[threadIdx.x][q] = 0.0;
 #pragma unroll
@@ -193,7 +183,7 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
       const double2 ab = s_ab[idx], co = s_co[idx];
       float G, og;
       double dx, dy;
-      const float al = splat_alpha<LIDAR>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
+      const float al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
       const bool act = (pos < lastp) & (al >= amin);
       if (ballot64(act) == 0) return;
       double vg[6];
@@ -208,24 +198,17 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         const float Tk = (float)Tkd;
         float da = 0.0f;
         const float wk = Tk * al;
-        if (LIDAR) {
-          const float dep = s_f[idx][0];
-          vf[0] = wk * g[0];
-          da = Tk * (dep - Sb) * g[0] + (float)(Tfin / (1.0 - (double)al)) * g[1];
-          Sb = __builtin_fmaf(al, dep, om * Sb);
-        } else {
-          // d loss / d alpha = T_k sum_ch (f_ch - Sb_ch) g_ch, and sum_ch Sb_ch g_ch
-          // follows the same blend as Sb: one dot product per entry
-          float fg = 0.0f;
+        // d loss / d alpha = T_k sum_ch (f_ch - Sb_ch) g_ch, and sum_ch Sb_ch g_ch
+        // follows the same blend as Sb: one dot product per entry
+        float fg = 0.0f;
 #pragma unroll
-          for (int ch = 0; ch < CM; ch++) {
-            const float f = s_f[idx][ch];
-            vf[ch] = wk * g[ch];
-            fg = __builtin_fmaf(f, g[ch], fg);
-          }
-          da = Tk * (fg - Sb);
-          Sb = __builtin_fmaf(al, fg, om * Sb);
+        for (int ch = 0; ch < CM; ch++) {
+          const float f = s_f[idx][ch];
+          vf[ch] = wk * g[ch];
+          fg = __builtin_fmaf(f, g[ch], fg);
         }
+        da = Tk * (fg - Sb);
+        Sb = __builtin_fmaf(al, fg, om * Sb);
         T = Tkd;
         if (!(og > amax)) {              // alpha is the constant amax where clamped
           vg[5] = (double)(G * da);
@@ -290,21 +273,248 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         const double x = s_ag[e][lane];
         if (x != 0.0) atomicAdd(dg + lane, x);
       }
-      if (LIDAR) {
-        if (lane == 6u) {
-          const float x = s_af[e][0];
-          if (x != 0.0f) atomicAdd(dg + 6, (double)x);
-        }
-      } else {
-        double *df = A.accf + (size_t)rid * A.C;
+      double *df = A.accf + (size_t)rid * A.C;
 #pragma unroll
-        for (int q0 = 0; q0 < CM; q0 += WAVE) {
-          const int q = q0 + (int)lane;
-          if (q < CM && q < A.C) {
-            const float x = s_af[e][q];
-            if (x != 0.0f) atomicAdd(df + q, (double)x);
-          }
+      for (int q0 = 0; q0 < CM; q0 += WAVE) {
+        const int q = q0 + (int)lane;
+        if (q < CM && q < A.C) {
+          const float x = s_af[e][q];
+          if (x != 0.0f) atomicAdd(df + q, (double)x);
         }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Spherical (lidar) views, reverse pass. A lidar tile's list can hold tens of
+// thousands of entries, and one wave walking it back to front sets the
+// kernel's length. Four waves share each quadrant's list of a batch of BL
+// entries, one contiguous part each:
+//  1. every wave composites its part front to back from T = 1 for its pixels
+//     (only entries before the pixel's `last`): the part's transmittance P_j
+//     and depth A_j;
+//  2. the reverse pass through part j maps the state after it (T, Sb) to
+//     (T / P_j, A_j + P_j Sb), so each wave chains the later parts' (P, A)
+//     onto the state after the batch to get the state after its own part;
+//  3. each wave replays its part back to front from that state, as the
+//     single-wave replay does, and the chain through all four parts is the
+//     state after the preceding batch.
+// Sb is the depth composited behind the current entry, normalised by the
+// transmittance before it. Gradients w.r.t. the entry's alpha: depth output
+// T_k (depth_k - Sb) g_depth; opacity output 1 - T_final: T_final / (1 - alpha_k)
+// g_opacity.
+// ---------------------------------------------------------------------------
+constexpr int BL = 512;                  // entries staged per batch
+
+__global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int tile_begin) {
+  __shared__ double2 s_uv[BL];
+  __shared__ double2 s_ab[BL];
+  __shared__ double2 s_co[BL];
+  __shared__ float s_dep[BL];
+  __shared__ uint32_t s_rid[BL];
+  __shared__ __align__(16) uint16_t s_idx[4][BL];  // per-quadrant lists of the batch
+  __shared__ int s_woff[16][4];
+  __shared__ int s_cnt[4];
+  __shared__ double s_ag[BL][7];           // du, dv, d_ca, d_cb, d_cc, d_opac (odd stride)
+  __shared__ float s_af[BL];               // d_depth
+  __shared__ float s_pA[4][256];           // per part and pixel: depth composited from T = 1,
+  __shared__ double s_pT[4][256];          //   and the part's transmittance
+  __shared__ uint32_t s_maxlast;
+  if (*A.overflow) return;
+  const int gtile = tile_begin + (int)blockIdx.x;
+  const int view = view_of_tile(vt, gtile);
+  const ViewDev &c = vt.v[view];
+  if (c.kind != SPLAT_CAM_SPHERICAL) return;
+  const unsigned tid = threadIdx.x, pix = tid & 255u;
+  const int part = __builtin_amdgcn_readfirstlane((int)(tid >> 8));           // 0..3
+  const int wq = __builtin_amdgcn_readfirstlane((int)((tid >> 6) & 3u));     // quadrant
+  const unsigned lane = tid & 63u, sw = tid >> 6;
+  const TilePix tp = tile_pixel(c, gtile, pix);
+  const uint32_t start = A.ranges[2 * gtile];
+  const uint32_t len = A.ranges[2 * gtile + 1] - start;
+  const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
+  const size_t plane = (size_t)c.W * c.H;
+  const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
+  const double pxr = tp.pxr, pyr = tp.pyr;
+  uint32_t lastp = 0;
+  double T = 1.0;                          // after the batch (the same in all four copies)
+  float Sb = 0.0f;
+  const float g0 = tp.inside ? A.dimg[pofs] : 0.0f;           // d loss / d depth
+  const float g1 = tp.inside ? A.dimg[pofs + plane] : 0.0f;   // d loss / d opacity
+  if (tp.inside) {
+    lastp = min(A.last[p], len);
+    T = (double)A.T_final[p];
+  }
+  const double Tfin = T;
+  if (tid == 0) s_maxlast = 0;
+  __syncthreads();
+  if (lastp) atomicMax(&s_maxlast, lastp);
+  __syncthreads();
+  const uint32_t maxlast = s_maxlast;
+  uint32_t wlast = lastp;                  // deepest position a pixel of the wave replays
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) wlast = max(wlast, (uint32_t)__shfl_xor((int)wlast, d, WAVE));
+  wlast = (uint32_t)__builtin_amdgcn_readfirstlane((int)wlast);
+  const float amin = A.alpha_min, amax = A.alpha_max;
+  const uint64_t below = lane ? (~0ull >> (64u - lane)) : 0ull;
+
+  for (int hi = (int)maxlast; hi > 0; hi -= BL) {
+    const int lo = hi > BL ? hi - BL : 0;
+    const int cnt = hi - lo;
+    unsigned mask = 0;
+    if ((int)tid < cnt) {
+      const uint32_t rid = A.vals[start + lo + tid];
+      const DrawRec d = A.draw[rid];
+      s_rid[tid] = rid;
+      s_uv[tid] = stage_uv(c, tp, d, true);
+      const Conic cn = stage_conic(d);
+      s_ab[tid] = cn.ab;
+      s_co[tid] = cn.co;
+      s_dep[tid] = A.aux[rid].depth;
+#pragma unroll
+      for (int q = 0; q < 7; q++) s_ag[tid][q] = 0.0;
+      s_af[tid] = 0.0f;
+      mask = quadrant_mask(tp, d);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint64_t bq = ballot64(((mask >> q) & 1u) != 0u);
+      if (lane == 0) s_woff[sw][q] = __popcll(bq);
+    }
+    __syncthreads();
+    if (tid < 4) {
+      int run = 0;
+      for (int w2 = 0; w2 < 16; w2++) {
+        const int x = s_woff[w2][tid];
+        s_woff[w2][tid] = run;
+        run += x;
+      }
+      s_cnt[tid] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint64_t bq = ballot64(((mask >> q) & 1u) != 0u);
+      if ((mask >> q) & 1u) s_idx[q][s_woff[sw][q] + __popcll(bq & below)] = (uint16_t)tid;
+    }
+    __syncthreads();
+    const int L = __builtin_amdgcn_readfirstlane(s_cnt[wq]);
+    const int k0 = (L * part) / 4, k1 = (L * (part + 1)) / 4;
+
+    // 1. the part front to back from T = 1
+    {
+      double Pt = 1.0;
+      float Ax = 0.0f;
+      auto fwd = [&](const int idx) {
+        const uint32_t pos = (uint32_t)(lo + idx);
+        if (pos >= wlast) return;
+        float G, og;
+        double dx, dy;
+        const float al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+        const bool hit = (pos < lastp) & (al >= amin);
+        const float w = (hit ? 1.0f : 0.0f) * (float)(Pt * (double)al);
+        Ax = __builtin_fmaf(w, s_dep[idx], Ax);
+        Pt = hit ? Pt * (1.0 - (double)al) : Pt;
+      };
+      int k = k0;
+      for (; k < k1 && (k & 3); k++) fwd(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]));
+      for (; k + 4 <= k1; k += 4) {
+        const uint64_t four = *reinterpret_cast<const uint64_t *>(&s_idx[wq][k]);
+        const uint32_t lo4 = __builtin_amdgcn_readfirstlane((uint32_t)four);
+        const uint32_t hi4 = __builtin_amdgcn_readfirstlane((uint32_t)(four >> 32));
+        if ((uint32_t)lo + (lo4 & 0xffffu) >= wlast) break;   // positions increase along the list
+        fwd((int)(lo4 & 0xffffu));
+        fwd((int)(lo4 >> 16));
+        fwd((int)(hi4 & 0xffffu));
+        fwd((int)(hi4 >> 16));
+      }
+      for (; k < k1; k++) fwd(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]));
+      s_pT[part][pix] = Pt;
+      s_pA[part][pix] = Ax;
+    }
+    __syncthreads();
+    // 2. the state after this wave's part, and after the preceding batch
+    double Te = T;
+    float Se = Sb;
+#pragma unroll
+    for (int j = 3; j >= 0; j--) {
+      if (j == part) {
+        Te = T;
+        Se = Sb;
+      }
+      const double Pj = s_pT[j][pix];
+      T = T / Pj;
+      Sb = __builtin_fmaf((float)Pj, Sb, s_pA[j][pix]);
+    }
+    // 3. the part back to front
+    auto entry = [&](const int idx) {
+      const uint32_t pos = (uint32_t)(lo + idx);
+      if (pos >= wlast) return;
+      const double2 ab = s_ab[idx], co = s_co[idx];
+      float G, og;
+      double dx, dy;
+      const float al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
+      const bool act = (pos < lastp) & (al >= amin);
+      if (ballot64(act) == 0) return;
+      double vg[6];
+      float vf = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 6; q++) vg[q] = 0.0;
+      if (act) {
+        const float om = 1.0f - al;
+        const double Tkd = Te / (1.0 - (double)al);
+        const float Tk = (float)Tkd;
+        const float dep = s_dep[idx];
+        vf = Tk * al * g0;
+        const float da = Tk * (dep - Se) * g0 + (float)(Tfin / (1.0 - (double)al)) * g1;
+        Se = __builtin_fmaf(al, dep, om * Se);
+        Te = Tkd;
+        if (!(og > amax)) {              // alpha is the constant amax where clamped
+          vg[5] = (double)(G * da);
+          const double dp = -(double)al * (double)da;     // d loss / d power
+          const double ha = ab.x, bb = ab.y, hc = co.x;   // a/2, b, c/2
+          vg[0] = -dp * (2.0 * ha * dx + bb * dy);
+          vg[1] = -dp * (bb * dx + 2.0 * hc * dy);
+          vg[2] = dp * 0.5 * dx * dx;
+          vg[3] = dp * dx * dy;
+          vg[4] = dp * 0.5 * dy * dy;
+        }
+      }
+      double v8[8];
+#pragma unroll
+      for (int q = 0; q < 8; q++) v8[q] = q < 6 ? vg[q] : 0.0;
+      const double r = wave_sum8_transposed_f64(v8);
+      if (lane < 6u) atomicAdd(&s_ag[idx][lane], r);
+      const float rf = row_sum_to_last(vf);
+      if ((lane & 15u) == 15u) atomicAdd(&s_af[idx], rf);
+    };
+    {
+      int k = k1 - 1;
+      for (; k >= k0 && ((k + 1) & 3); k--) entry(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]));
+      for (; k - 3 >= k0; k -= 4) {             // four indices per list read
+        const uint64_t four = *reinterpret_cast<const uint64_t *>(&s_idx[wq][k - 3]);
+        const uint32_t lo4 = __builtin_amdgcn_readfirstlane((uint32_t)four);
+        const uint32_t hi4 = __builtin_amdgcn_readfirstlane((uint32_t)(four >> 32));
+        entry((int)(hi4 >> 16));
+        entry((int)(hi4 & 0xffffu));
+        entry((int)(lo4 >> 16));
+        entry((int)(lo4 & 0xffffu));
+      }
+      for (; k >= k0; k--) entry(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]));
+    }
+    __syncthreads();
+    // flush: one wave per entry, lanes over the entry's values
+    for (int e = (int)sw; e < cnt; e += 16) {
+      const uint32_t rid = s_rid[e];
+      double *dg = A.accg + (size_t)rid * ACC_G;
+      if (lane < 6u) {
+        const double x = s_ag[e][lane];
+        if (x != 0.0) atomicAdd(dg + lane, x);
+      } else if (lane == 6u) {
+        const float x = s_af[e];
+        if (x != 0.0f) atomicAdd(dg + 6, (double)x);
       }
     }
     __syncthreads();
@@ -845,13 +1055,25 @@ __global__ __launch_bounds__(256) void k_proj_bwd_gauss(ViewTable vt, ProjBwdArg
 }
 
 template <int CM>
-void launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begin, int ntiles, bool has_pin,
-                   bool has_sph, hipStream_t stream) {
+void launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begin, int ntiles, int vbeg, int vend,
+                   hipStream_t stream) {
   if (kind == SPLAT_PRIM_SPHERE) {
     hipLaunchKernelGGL(k_bwd_sphere<CM>, dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
   } else {
-    if (has_pin) hipLaunchKernelGGL((k_bwd_alpha<CM, false>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
-    if (has_sph) hipLaunchKernelGGL((k_bwd_alpha<1, true>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
+    // one launch per run of consecutive views of one kind, over that run's tiles only
+    for (int v0 = vbeg; v0 < vend;) {
+      const int kind0 = vt.v[v0].kind;
+      int v1 = v0 + 1;
+      while (v1 < vend && vt.v[v1].kind == kind0) v1++;
+      const int t0 = vt.v[v0].tile_off, t1 = v1 < vt.n ? vt.v[v1].tile_off : vt.total_tiles;
+      if (t1 > t0) {
+        if (kind0 == SPLAT_CAM_SPHERICAL)
+          hipLaunchKernelGGL(k_bwd_lidar, dim3(t1 - t0), dim3(1024), 0, stream, vt, A, t0);
+        else
+          hipLaunchKernelGGL(k_bwd_alpha<CM>, dim3(t1 - t0), dim3(256), 0, stream, vt, A, t0);
+      }
+      v0 = v1;
+    }
   }
 }
 
@@ -888,21 +1110,16 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   const int tile_begin = vt.v[vbeg].tile_off;
   const int tile_end = vend < vt.n ? vt.v[vend].tile_off : vt.total_tiles;
   const int ntiles = tile_end - tile_begin;
-  bool has_pin = false, has_sph = false;
-  for (int v = vbeg; v < vend; v++) {
-    if (vt.v[v].kind == SPLAT_CAM_SPHERICAL) has_sph = true;
-    else has_pin = true;
-  }
   if (ntiles > 0) {
     switch (channel_bucket(A.C)) {
-      case 1: launch_bwd_cm<1>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
-      case 2: launch_bwd_cm<2>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
-      case 3: launch_bwd_cm<3>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
-      case 4: launch_bwd_cm<4>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
-      case 8: launch_bwd_cm<8>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
-      case 16: launch_bwd_cm<16>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
-      case 32: launch_bwd_cm<32>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
-      default: launch_bwd_cm<64>(vt, A, pr->kind, tile_begin, ntiles, has_pin, has_sph, stream); break;
+      case 1: launch_bwd_cm<1>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 2: launch_bwd_cm<2>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 3: launch_bwd_cm<3>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 4: launch_bwd_cm<4>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 8: launch_bwd_cm<8>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 16: launch_bwd_cm<16>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 32: launch_bwd_cm<32>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      default: launch_bwd_cm<64>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
     }
     SPLAT_LAUNCH_CHECK();
   }
