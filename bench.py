@@ -101,15 +101,6 @@ def main():
     dimg = torch.from_numpy(np.concatenate([g.reshape(-1) for g in g_np])).to(dev)
     want = ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t")
     grads = rz.alloc_grads(want)
-    # camera and lidar views go through separate backward calls
-    groups, v = [], 0
-    while v < rz.V:
-        kind = scene.cams[v].kind
-        e = v
-        while e < rz.V and scene.cams[e].kind == kind:
-            e += 1
-        groups.append((v, e - v))
-        v = e
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -124,8 +115,8 @@ def main():
         rz.render_fwd()
         if ev is not None:
             ev[3].record()
-        for gi, (b, cnt) in enumerate(groups):
-            rz.backward(dimg, grads=grads, view_begin=b, view_count=cnt, accumulate=gi > 0)
+        # all views in one call (camera and lidar views run separate kernels)
+        rz.backward(dimg, grads=grads)
         if ev is not None:
             ev[4].record()
 

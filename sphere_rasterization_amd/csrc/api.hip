@@ -1,10 +1,13 @@
 // extern "C" entry points of libsplat: argument checks on the host, view-table
-// construction, then kernel launches on the caller's stream. No allocation, no
-// host synchronisation, no global mutable state.
+// construction, then kernel launches on the caller's stream. No allocation of
+// device memory and no host synchronisation; the only global state is one side
+// stream per device (created on first use, see side_begin).
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "render_common.h"
 #include "splat_internal.h"
@@ -19,6 +22,55 @@ int launch_render_fwd(const ViewTable &vt, const FwdArgs &A, int kind, hipStream
 size_t bwd_workspace_bytes(long long nrec, int C);
 int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, const BinRec *bin,
                       const splat_grads *gr, hipStream_t stream);
+
+namespace {
+
+struct SideStream {
+  std::mutex mu;                 // held from side_begin to side_end
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+
+}  // namespace
+
+int side_begin(hipStream_t main, hipStream_t *side) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPLAT_ERR_HIP;
+  SideStream &ss = g_side[dev];
+  ss.mu.lock();
+  if (!ss.s) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) ss.s = nullptr;
+    if (ss.s && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) ss.fork = nullptr;
+    if (ss.s && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) ss.join = nullptr;
+    if (!ss.s || !ss.fork || !ss.join) {
+      if (ss.fork) (void)hipEventDestroy(ss.fork);
+      if (ss.s) (void)hipStreamDestroy(ss.s);
+      ss.s = nullptr;
+      ss.fork = ss.join = nullptr;
+      ss.mu.unlock();
+      return SPLAT_ERR_HIP;
+    }
+  }
+  if (hipEventRecord(ss.fork, main) != hipSuccess || hipStreamWaitEvent(ss.s, ss.fork, 0) != hipSuccess) {
+    ss.mu.unlock();
+    return SPLAT_ERR_HIP;
+  }
+  *side = ss.s;
+  return SPLAT_OK;
+}
+
+int side_end(hipStream_t main, hipStream_t side) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPLAT_ERR_HIP;
+  SideStream &ss = g_side[dev];
+  int rc = SPLAT_OK;
+  if (side != ss.s || hipEventRecord(ss.join, ss.s) != hipSuccess || hipStreamWaitEvent(main, ss.join, 0) != hipSuccess)
+    rc = SPLAT_ERR_HIP;
+  ss.mu.unlock();
+  return rc;
+}
 
 namespace {
 

@@ -1055,26 +1055,40 @@ __global__ __launch_bounds__(256) void k_proj_bwd_gauss(ViewTable vt, ProjBwdArg
 }
 
 template <int CM>
-void launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begin, int ntiles, int vbeg, int vend,
+int launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begin, int ntiles, int vbeg, int vend,
                    hipStream_t stream) {
   if (kind == SPLAT_PRIM_SPHERE) {
     hipLaunchKernelGGL(k_bwd_sphere<CM>, dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
   } else {
-    // one launch per run of consecutive views of one kind, over that run's tiles only
-    for (int v0 = vbeg; v0 < vend;) {
-      const int kind0 = vt.v[v0].kind;
-      int v1 = v0 + 1;
-      while (v1 < vend && vt.v[v1].kind == kind0) v1++;
-      const int t0 = vt.v[v0].tile_off, t1 = v1 < vt.n ? vt.v[v1].tile_off : vt.total_tiles;
-      if (t1 > t0) {
-        if (kind0 == SPLAT_CAM_SPHERICAL)
-          hipLaunchKernelGGL(k_bwd_lidar, dim3(t1 - t0), dim3(1024), 0, stream, vt, A, t0);
-        else
-          hipLaunchKernelGGL(k_bwd_alpha<CM>, dim3(t1 - t0), dim3(256), 0, stream, vt, A, t0);
-      }
-      v0 = v1;
+    // one launch per run of consecutive views of one kind, over that run's
+    // tiles only; with both kinds present the camera views run on the side
+    // stream, the spherical views (dispatched first) on the caller's
+    bool has_pin = false, has_sph = false;
+    for (int v = vbeg; v < vend; v++) (vt.v[v].kind == SPLAT_CAM_SPHERICAL ? has_sph : has_pin) = true;
+    hipStream_t side = stream;
+    const bool fork = has_pin && has_sph;
+    if (fork) {
+      const int rc = side_begin(stream, &side);
+      if (rc != SPLAT_OK) return rc;
     }
+    for (int pass = 0; pass < 2; pass++) {
+      for (int v0 = vbeg; v0 < vend;) {
+        const int kind0 = vt.v[v0].kind;
+        int v1 = v0 + 1;
+        while (v1 < vend && vt.v[v1].kind == kind0) v1++;
+        const int t0 = vt.v[v0].tile_off, t1 = v1 < vt.n ? vt.v[v1].tile_off : vt.total_tiles;
+        if (t1 > t0) {
+          if (pass == 0 && kind0 == SPLAT_CAM_SPHERICAL)
+            hipLaunchKernelGGL(k_bwd_lidar, dim3(t1 - t0), dim3(1024), 0, stream, vt, A, t0);
+          else if (pass == 1 && kind0 != SPLAT_CAM_SPHERICAL)
+            hipLaunchKernelGGL(k_bwd_alpha<CM>, dim3(t1 - t0), dim3(256), 0, side, vt, A, t0);
+        }
+        v0 = v1;
+      }
+    }
+    if (fork) return side_end(stream, side);
   }
+  return SPLAT_OK;
 }
 
 }  // namespace
@@ -1111,16 +1125,18 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   const int tile_end = vend < vt.n ? vt.v[vend].tile_off : vt.total_tiles;
   const int ntiles = tile_end - tile_begin;
   if (ntiles > 0) {
+    int rc = SPLAT_OK;
     switch (channel_bucket(A.C)) {
-      case 1: launch_bwd_cm<1>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
-      case 2: launch_bwd_cm<2>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
-      case 3: launch_bwd_cm<3>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
-      case 4: launch_bwd_cm<4>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
-      case 8: launch_bwd_cm<8>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
-      case 16: launch_bwd_cm<16>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
-      case 32: launch_bwd_cm<32>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
-      default: launch_bwd_cm<64>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 1: rc = launch_bwd_cm<1>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 2: rc = launch_bwd_cm<2>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 3: rc = launch_bwd_cm<3>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 4: rc = launch_bwd_cm<4>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 8: rc = launch_bwd_cm<8>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 16: rc = launch_bwd_cm<16>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      case 32: rc = launch_bwd_cm<32>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
+      default: rc = launch_bwd_cm<64>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
     }
+    if (rc != SPLAT_OK) return rc;
     SPLAT_LAUNCH_CHECK();
   }
   ProjBwdArgs P;

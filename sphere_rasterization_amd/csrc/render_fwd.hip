@@ -450,19 +450,38 @@ int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t s
   if (kind == SPLAT_PRIM_SPHERE) {
     hipLaunchKernelGGL(k_fwd_sphere<CM>, grid, block, 0, stream, vt, A);
   } else {
-    // one launch per run of consecutive views of one kind, over that run's tiles only
-    for (int v0 = 0; v0 < vt.n;) {
-      const int kind0 = vt.v[v0].kind;
-      int v1 = v0 + 1;
-      while (v1 < vt.n && vt.v[v1].kind == kind0) v1++;
-      const int t0 = vt.v[v0].tile_off, t1 = v1 < vt.n ? vt.v[v1].tile_off : vt.total_tiles;
-      if (t1 > t0) {
-        if (kind0 == SPLAT_CAM_SPHERICAL)
-          hipLaunchKernelGGL(k_fwd_lidar, dim3(t1 - t0), dim3(LB), 0, stream, vt, A, t0);
-        else
-          hipLaunchKernelGGL(k_fwd_alpha<CM>, dim3(t1 - t0), block, 0, stream, vt, A, t0);
+    // one launch per run of consecutive views of one kind, over that run's
+    // tiles only. With both kinds present the camera views run on the side
+    // stream, which first waits for an event of the caller's stream: the
+    // spherical views, launched on the caller's stream, are dispatched first
+    // (all their workgroups are resident at once), so their long lists start
+    // early and camera tiles fill the compute units they leave
+    bool has_pin = false, has_sph = false;
+    for (int v = 0; v < vt.n; v++) (vt.v[v].kind == SPLAT_CAM_SPHERICAL ? has_sph : has_pin) = true;
+    hipStream_t side = stream;
+    const bool fork = has_pin && has_sph;
+    if (fork) {
+      const int rc = side_begin(stream, &side);
+      if (rc != SPLAT_OK) return rc;
+    }
+    for (int pass = 0; pass < 2; pass++) {
+      for (int v0 = 0; v0 < vt.n;) {
+        const int kind0 = vt.v[v0].kind;
+        int v1 = v0 + 1;
+        while (v1 < vt.n && vt.v[v1].kind == kind0) v1++;
+        const int t0 = vt.v[v0].tile_off, t1 = v1 < vt.n ? vt.v[v1].tile_off : vt.total_tiles;
+        if (t1 > t0) {
+          if (pass == 0 && kind0 == SPLAT_CAM_SPHERICAL)
+            hipLaunchKernelGGL(k_fwd_lidar, dim3(t1 - t0), dim3(LB), 0, stream, vt, A, t0);
+          else if (pass == 1 && kind0 != SPLAT_CAM_SPHERICAL)
+            hipLaunchKernelGGL(k_fwd_alpha<CM>, dim3(t1 - t0), block, 0, side, vt, A, t0);
+        }
+        v0 = v1;
       }
-      v0 = v1;
+    }
+    if (fork) {
+      const int rc = side_end(stream, side);
+      if (rc != SPLAT_OK) return rc;
     }
   }
   SPLAT_LAUNCH_CHECK();

@@ -191,6 +191,16 @@ __device__ __forceinline__ unsigned lane_id() { return __builtin_amdgcn_mbcnt_hi
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // HIP error check used by the host-side launchers.
+// A second stream per device on which the pinhole-view compositors run beside
+// the spherical ones: a lidar tile list can be far longer than any camera
+// tile's, and on one stream the camera views would wait for it.
+// side_begin makes the side stream wait for `main` and holds the device's lock
+// until side_end, which makes `main` wait for the side stream; every side_begin
+// that returns SPLAT_OK is followed by side_end. The stream and its two events
+// are created on first use and kept until the process ends.
+int side_begin(hipStream_t main, hipStream_t *side);
+int side_end(hipStream_t main, hipStream_t side);
+
 #define SPLAT_LAUNCH_CHECK()                                   \
   do {                                                         \
     if (hipPeekAtLastError() != hipSuccess) {                  \
