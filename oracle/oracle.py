@@ -57,8 +57,8 @@ def lib():
         L.or_get_pairs.argtypes = [vp, vp, vp, vp]
         L.or_render.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.or_render_bruteforce.argtypes = [vp, ip, vp, vp, vp, vp]
-        L.or_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.or_backward_mag.argtypes = [vp] * 17
+        L.or_backward.argtypes = [vp] * 11
+        L.or_backward_mag.argtypes = [vp] * 19
         _lib = L
     return _lib
 
@@ -235,7 +235,7 @@ class Oracle:
             return dict(pos=np.zeros((n, pd)), scale=np.zeros((n, sd)) if sd > 1 else np.zeros(n),
                         rot=np.zeros((n, 4)) if self.kind == 1 else None, opacity=np.zeros(n),
                         feat=np.zeros((n, Cc)) if Cc > 0 else None, cam_R=np.zeros((self.V, 3, 3)),
-                        cam_t=np.zeros((self.V, 3)))
+                        cam_t=np.zeros((self.V, 3)), cam_K=np.zeros((self.V, 4)))
 
         o = outs()
         acc = np.zeros((self.V * n, G_OFF + Cc))
@@ -244,9 +244,10 @@ class Oracle:
         if with_mag:
             m = outs()
             lib().or_backward_mag(*args, *[_vp(m[k]) for k in ("pos", "scale", "rot", "opacity", "feat",
-                                                               "cam_R", "cam_t")])
+                                                               "cam_R", "cam_t")],
+                                  _vp(o["cam_K"]), _vp(m["cam_K"]))
             o["mag"] = m
         else:
-            lib().or_backward(*args)
+            lib().or_backward(*args, _vp(o["cam_K"]))
         o["acc"] = acc
         return o

@@ -668,7 +668,7 @@ void or_render_bruteforce(const octx *X, int v, double *img, double *T, double *
  * terms that cancel is only accurate relative to the sum of magnitudes). It
  * plays no part in the gradient itself. */
 static void pixel_backward(const octx *X, long long gpix, const double *g, double *loc, double *mloc, int NG,
-                           otrace *tr, int tr_cap) {
+                           otrace *tr, int tr_cap, double *kacc, double *kmag) {
   int C = X->C;
   opix P;
   int v = find_view(X, gpix);
@@ -706,11 +706,28 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
       for (int a = 0; a < 3; a++) A[a] += ddist2 * (2.0 * q[a] - 2.0 * qd * r->d[a] / r->dd);
       A[2] += dzhat * (-1.0 / (c->zfar - c->znear));
       if (!o->floored) A[3] += dD * 2.0 * r->dist2 / (r2 * o->r_eff);
+      /* Intrinsics (Pulsar 3.2 and appendix A: gradients for focal length and
+         sensor placement). The pixel's ray d = ((px - cx)/fx, (py - cy)/fy, 1)
+         moves with them; d dist2 / d d_a = -2 (q.d)/|d|^2 (q_a - (q.d) d_a/|d|^2),
+         d d_a / d f_a = -d_a / f_a, d d_a / d c_a = -1 / f_a. The one-pixel floor
+         of r_eff is held fixed, as for the position. */
+      for (int a = 0; a < 2; a++) {
+        double f = a == 0 ? c->fx : c->fy;
+        double gd = ddist2 * (-2.0 * qd / r->dd) * (q[a] - qd * r->d[a] / r->dd);
+        kacc[a] += gd * (-r->d[a] / f);
+        kacc[2 + a] += gd * (-1.0 / f);
+      }
       if (M) {
         double mD = mdw * oo * e, mz = mdw * r->w * oo / X->gamma, m2 = mD / r2;
         for (int a = 0; a < 3; a++) M[a] += m2 * (2.0 * fabs(q[a]) + 2.0 * fabs(qd * r->d[a]) / r->dd);
         M[2] += mz / (c->zfar - c->znear);
         if (!o->floored) M[3] += mD * 2.0 * r->dist2 / (r2 * o->r_eff);
+        for (int a = 0; a < 2; a++) {
+          double f = a == 0 ? c->fx : c->fy;
+          double mg = m2 * 2.0 * fabs(qd) / r->dd * (fabs(q[a]) + fabs(qd * r->d[a]) / r->dd);
+          kmag[a] += mg * fabs(r->d[a]) / f;
+          kmag[2 + a] += mg / f;
+        }
       }
     }
     return;
@@ -929,15 +946,20 @@ typedef struct {
 /* Backward. dimg: concatenated per-view [Cv][H][W] float32 upstream gradients
  * (Cv = C for pinhole views, 2 = (depth, opacity) for spherical views).
  * Outputs are written (not accumulated). acc_out (optional) receives the
- * per-record 2D accumulators [V*n][8+C]. mag (optional) receives the running
+ * per-record 2D accumulators [V*n][8+C]. dK [V][4] receives the gradient
+ * w.r.t. each view's fx, fy, cx, cy (spheres; zero for Gaussians), summed per
+ * tile and then over tiles in order; mK (optional) its magnitudes. mag (optional) receives the running
  * magnitudes of every output, in the outputs' layouts. */
 static void backward_core(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
-                          double *dop, double *dfeat, double *dR, double *dt, double *acc_out, const omag *mag) {
+                          double *dop, double *dfeat, double *dR, double *dt, double *acc_out, double *dK,
+                          double *mK, const omag *mag) {
   int C = X->C, NG = G_OFF + C;
   long long NV = (long long)X->V * X->n;
   double *acc = (double *)calloc((size_t)NV * NG + 1, sizeof(double));
   double *macc = mag ? (double *)calloc((size_t)NV * NG + 1, sizeof(double)) : NULL;
   long long ntile = X->total_tiles;
+  memset(dK, 0, sizeof(double) * 4 * (size_t)X->V);
+  if (mK) memset(mK, 0, sizeof(double) * 4 * (size_t)X->V);
   /* Tiles run in parallel; each accumulates by tile-list position into a private
      buffer, merged into the per-record sums in tile order (deterministic). */
   #pragma omp parallel
@@ -965,6 +987,7 @@ static void backward_core(const octx *X, const float *dimg, double *dpos, double
       for (int u = 0; u < v; u++)
         gv += (size_t)(X->cams[u].kind == CAM_SPHERICAL ? 2 : C) * X->cams[u].width * X->cams[u].height;
       int any = 0;
+      double kt[4] = {0, 0, 0, 0}, kmt[4] = {0, 0, 0, 0};
       for (long long p = 0; p < len * NG; p++) loc[p] = 0.0;
       if (mloc) for (long long p = 0; p < len * NG; p++) mloc[p] = 0.0;
       for (int jj = 0; jj < TILE && len > 0; jj++)
@@ -979,10 +1002,14 @@ static void backward_core(const octx *X, const float *dimg, double *dpos, double
           }
           if (!nz) continue;
           any = 1;
-          pixel_backward(X, c->pix_off + (long long)j * c->width + i, g, loc, mloc, NG, tr, (int)len);
+          pixel_backward(X, c->pix_off + (long long)j * c->width + i, g, loc, mloc, NG, tr, (int)len, kt, kmt);
         }
       #pragma omp ordered
       {
+        for (int a = 0; a < 4; a++) {
+          dK[4 * v + a] += kt[a];
+          if (mK) mK[4 * v + a] += kmt[a];
+        }
         if (any)
           for (long long p = s; p < e; p++) {
             double *B = acc + (size_t)X->pair_id[p] * NG;
@@ -1062,15 +1089,16 @@ static void backward_core(const octx *X, const float *dimg, double *dpos, double
 }
 
 void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
-                 double *dop, double *dfeat, double *dR, double *dt, double *acc_out) {
-  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, NULL);
+                 double *dop, double *dfeat, double *dR, double *dt, double *acc_out, double *dK) {
+  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, dK, NULL, NULL);
 }
 
 /* Same as or_backward, plus the magnitudes (zero-initialised by the caller,
  * same layouts as the gradients; mfeat and mrot may be NULL when absent). */
 void or_backward_mag(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
                      double *dop, double *dfeat, double *dR, double *dt, double *acc_out, double *mpos,
-                     double *mscale, double *mrot, double *mop, double *mfeat, double *mR, double *mt) {
+                     double *mscale, double *mrot, double *mop, double *mfeat, double *mR, double *mt,
+                     double *dK, double *mK) {
   omag m = {mpos, mscale, mrot, mop, mfeat, mR, mt};
-  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, &m);
+  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, dK, mK, &m);
 }

@@ -45,11 +45,13 @@ def _fd_check(scene, g_views, names, rtol=2e-5, extra=None):
     return an
 
 
-def _fd_camera(scene, g_views, an, rtol=2e-5):
+def _fd_camera(scene, g_views, an, rtol=2e-5, intrinsics=False):
+    """R, t (and with intrinsics: fx, fy, cx, cy, packed at 15..18) by central differences."""
     packed = O.pack_cams(scene.cams)
     base = packed.copy()
+    blocks = [(3, "cam_R", 9), (12, "cam_t", 3)] + ([(15, "cam_K", 4)] if intrinsics else [])
     for v in range(len(scene.cams)):
-        for j, (lo, name, shape) in enumerate(((3, "cam_R", 9), (12, "cam_t", 3))):
+        for j, (lo, name, shape) in enumerate(blocks):
             fd = np.zeros(shape)
             for k in range(shape):
                 h = 1e-6
@@ -120,7 +122,7 @@ def test_fd_spheres_with_camera():
     assert not pr["gated"].any() and not pr["floored"].any()
     g = _g(rng, sc)
     an = _fd_check(sc, g, ["pos", "scale", "opacity", "feat"])
-    _fd_camera(sc, g, an)
+    _fd_camera(sc, g, an, intrinsics=True)
     # camera gradient is the sum of per-sphere sensor-space gradients
     dq = an["acc"][:, :3]
     np.testing.assert_allclose(an["cam_t"][0], dq.sum(0), rtol=1e-12)
@@ -236,7 +238,7 @@ def test_autograd_xcheck_gauss3d():
 
 def test_autograd_xcheck_spheres():
     """Dense normalized sphere blending in torch float64 (first-5 truncation via detach)
-    with autograd equals the oracle's reverse pass, camera R and t included."""
+    with autograd equals the oracle's reverse pass, camera R, t and intrinsics included."""
     rng = np.random.default_rng(32)
     n, W, H = 60, 40, 36
     R = TS.rotation(rng)
@@ -257,13 +259,14 @@ def test_autograd_xcheck_spheres():
          for k in ("pos", "scale", "opacity", "feat")}
     Rc = torch.tensor(np.asarray(cam.R, np.float64), requires_grad=True)
     tc = torch.tensor(np.asarray(cam.t, np.float64), requires_grad=True)
+    Kc = torch.tensor([cam.fx, cam.fy, cam.cx, cam.cy], dtype=torch.float64, requires_grad=True)
     q = P["pos"] @ Rc.T + tc
     gam = float(np.float32(0.3))
     zhat = (21.0 - q[:, 2]) / 20.0
     e = torch.exp(P["opacity"] * zhat / gam)
     ys, xs = torch.meshgrid(torch.arange(H, dtype=torch.float64) + 0.5,
                             torch.arange(W, dtype=torch.float64) + 0.5, indexing="ij")
-    d = torch.stack([(xs - cam.cx) / cam.fx, (ys - cam.cy) / cam.fy, torch.ones_like(xs)], -1).view(-1, 3)
+    d = torch.stack([(xs - Kc[2]) / Kc[0], (ys - Kc[3]) / Kc[1], torch.ones_like(xs)], -1).view(-1, 3)
     dd = (d * d).sum(1)
     qd = d @ q.T                                             # [pix, n]
     dist2 = (q * q).sum(1)[None] - qd ** 2 / dd[:, None]
@@ -288,6 +291,7 @@ def test_autograd_xcheck_spheres():
         np.testing.assert_allclose(an[k], ref, rtol=1e-9, atol=1e-11 * np.abs(ref).max(), err_msg=k)
     np.testing.assert_allclose(an["cam_R"][0], Rc.grad.numpy(), rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(an["cam_t"][0], tc.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(an["cam_K"][0], Kc.grad.numpy(), rtol=1e-9, atol=1e-12)
 
 
 # ---- term magnitudes (the bound the gradient tolerance uses) ----------------
