@@ -101,11 +101,17 @@ typedef struct {
 
 /* Gradient outputs (DEVICE); NULL = not requested (skipped, nothing written).
  * Shapes follow the inputs; cam_R [n_views][9], cam_t [n_views][3] (spheres only).
+ * cam_K [n_views][4]: d loss / d (fx, fy, cx, cy) of each view, spheres only
+ * (Pulsar section 3.2 and appendix A: gradients for the focal length and the
+ * sensor placement); the pixel rays move with the intrinsics, while the
+ * one-pixel radius floor, the tile rectangles and the gate are held fixed.
+ * A non-NULL cam_K with Gaussian primitives returns SPLAT_ERR_UNSUPPORTED.
  * accumulate = 0: outputs are overwritten (zeroed on-stream first);
  * accumulate = 1: the call's gradients are added to what the buffers hold. */
 typedef struct {
   float *pos, *scale, *rot, *opacity, *feat;
   float *cam_R, *cam_t;
+  float *cam_K;
   int32_t accumulate;
 } splat_grads;
 

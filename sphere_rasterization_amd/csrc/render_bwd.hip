@@ -593,6 +593,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   const uint32_t npos = s_npos;
   int nxt = 0;
   uint32_t tgt = ntop ? my_top[0] : 0xffffffffu;
+  // d loss / d (ray x, ray y) summed over the pixel's recorded spheres
+  double kgx = 0.0, kgy = 0.0;
   const double inv_span = 1.0 / ((double)c.zfar - (double)c.znear);
   const float igam = 1.0f / A.gamma;
   const long long vbase = (long long)view * A.n;
@@ -654,10 +656,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
           const double dd2 = -dD * Ai.y * Ai.y;
           const double c1 = (ray.x * sx + ray.y * sy) * ray.g;
           const double k2 = 2.0 * dd2 * (double)x.x;
-          v[0] = (float)(k2 * (c1 * ray.x - sx));
-          v[1] = (float)(k2 * (c1 * ray.y - sy));
+          const double gq0 = k2 * (c1 * ray.x - sx), gq1 = k2 * (c1 * ray.y - sy);
+          v[0] = (float)gq0;
+          v[1] = (float)gq1;
           v[2] = (float)(k2 * c1 - dz * inv_span);
           if (!(flags & 1)) v[3] = (float)(dD * 2.0 * (1.0 - Dd) * Ai.y);
+          // the ray: d dist^2 / d d = -((q.d) / |d|^2) d dist^2 / d q, with
+          // (q.d) / |d|^2 = qz (1 - c1)
+          const double s = (double)x.x * (1.0 - c1);
+          kgx = kgx - s * gq0;
+          kgy = kgy - s * gq1;
         }
         nxt++;
         tgt = nxt < ntop ? my_top[nxt] : 0xffffffffu;
@@ -695,6 +703,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     }
     __syncthreads();
   }
+  if (A.kslot) {
+    // intrinsics: the ray (x, y) = ((px - cx) / fx, (py - cy) / fy); per wave
+    // the pixels' (d/dfx, d/dfy, d/dcx, d/dcy) are summed, lanes 0..3 add them
+    const double ifx = 1.0 / (double)c.fx, ify = 1.0 / (double)c.fy;
+    double v8[8];
+    v8[0] = -kgx * ray.x * ifx;
+    v8[1] = -kgy * ray.y * ify;
+    v8[2] = -kgx * ifx;
+    v8[3] = -kgy * ify;
+#pragma unroll
+    for (int q = 4; q < 8; q++) v8[q] = 0.0;
+    const double r = wave_sum8_transposed_f64(v8);
+    if (lane < 4u) atomicAdd(A.kslot + ((size_t)view * SPLAT_K_SLOTS + blockIdx.x % SPLAT_K_SLOTS) * 4 + lane, r);
+  }
+}
+
+// Sum of the intrinsic-gradient slots of each view, in slot order.
+__global__ __launch_bounds__(256) void k_cam_K_final(const double *kslot, float *gK, int vbeg, int vend,
+                                                     int accumulate) {
+  const int v = vbeg + (int)(threadIdx.x >> 2), a = (int)(threadIdx.x & 3u);
+  if (v >= vend) return;
+  const double *row = kslot + (size_t)v * SPLAT_K_SLOTS * 4 + a;
+  double s = 0.0;
+  for (int k = 0; k < SPLAT_K_SLOTS; k++) s += row[4 * k];
+  if (accumulate) gK[4 * v + a] += (float)s;
+  else gK[4 * v + a] = (float)s;
 }
 
 // ---------------------------------------------------------------------------
@@ -1105,6 +1139,10 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   if (sph) {
     z.d0 = A.accg + r0 * (5 + A.C);
     z.nd0 = (r1 - r0) * (5 + A.C);
+    if (A.kslot) {
+      z.d1 = A.kslot + (size_t)vbeg * SPLAT_K_SLOTS * 4;
+      z.nd1 = (long long)(vend - vbeg) * SPLAT_K_SLOTS * 4;
+    }
   } else {
     z.d0 = A.accg + r0 * ACC_G;
     z.nd0 = (r1 - r0) * ACC_G;
@@ -1137,6 +1175,9 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
       default: rc = launch_bwd_cm<64>(vt, A, pr->kind, tile_begin, ntiles, vbeg, vend, stream); break;
     }
     if (rc != SPLAT_OK) return rc;
+    if (sph && A.kslot)
+      hipLaunchKernelGGL(k_cam_K_final, dim3(1), dim3(256), 0, stream, A.kslot, gr->cam_K, vbeg, vend,
+                         gr->accumulate);
     SPLAT_LAUNCH_CHECK();
   }
   ProjBwdArgs P;

@@ -41,6 +41,7 @@ struct BwdArgs {
   double *accg;           // Gaussians: [records][ACC_G]; spheres: [records][5 + C] (all values)
   double *accf;           // Gaussians: [records][C]; unused for spheres
   double *cam_part;       // [SPLAT_CAM_BLOCKS][12] per-block camera sums (spheres)
+  double *kslot;          // [views][SPLAT_K_SLOTS][4] intrinsic-gradient sums, or NULL (not requested)
 };
 
 struct TilePix {

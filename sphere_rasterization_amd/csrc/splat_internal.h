@@ -116,16 +116,22 @@ static inline size_t proj_bytes(long long nrec) {
 // After the accumulators: per-block camera partial sums of the sphere gradient
 // pass ([SPLAT_CAM_BLOCKS][12] fp64).
 #define SPLAT_CAM_BLOCKS 1024
+// Then the intrinsic-gradient slots of the sphere reverse pass: per view,
+// SPLAT_K_SLOTS rows of (fx, fy, cx, cy) fp64 sums; compositor block b adds
+// into row b mod SPLAT_K_SLOTS, so that few blocks share an address.
+#define SPLAT_K_SLOTS 256
 
 struct AccLayout {
   double *g;
   double *f;
   double *cam;
+  double *kslot;
 };
 
 static inline size_t acc_bytes(long long nrec, int C) {
   return proj_align(sizeof(double) * ACC_G * (size_t)nrec) + proj_align(sizeof(double) * (size_t)nrec * C) +
-         proj_align(sizeof(double) * 12 * SPLAT_CAM_BLOCKS);
+         proj_align(sizeof(double) * 12 * SPLAT_CAM_BLOCKS) +
+         proj_align(sizeof(double) * 4 * SPLAT_K_SLOTS * SPLAT_MAX_VIEWS);
 }
 
 static inline AccLayout acc_layout(void *base, long long nrec, int C) {
@@ -133,7 +139,8 @@ static inline AccLayout acc_layout(void *base, long long nrec, int C) {
   char *p = (char *)base;
   a.g = (double *)p;    p += proj_align(sizeof(double) * ACC_G * (size_t)nrec);
   a.f = (double *)p;    p += proj_align(sizeof(double) * (size_t)nrec * C);
-  a.cam = (double *)p;
+  a.cam = (double *)p;  p += proj_align(sizeof(double) * 12 * SPLAT_CAM_BLOCKS);
+  a.kslot = (double *)p;
   return a;
 }
 

@@ -143,7 +143,7 @@ class Rasterizer:
         self.render_fwd()
         return self.img
 
-    def backward(self, dimg: torch.Tensor, want=("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t"),
+    def backward(self, dimg: torch.Tensor, want=("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t", "cam_K"),
                  view_begin: int = 0, view_count: Optional[int] = None, grads=None, accumulate=False):
         if view_count is None:
             view_count = self.V - view_begin
@@ -153,7 +153,7 @@ class Rasterizer:
         if grads is None:
             grads = self.alloc_grads(want)
         g = L.splat_grads()
-        for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t"):
+        for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t", "cam_K"):
             setattr(g, k, _ptr(grads.get(k)))
         g.accumulate = 1 if accumulate else 0
         L.splat_render_bwd(self.c_cams, self.V, view_begin, view_count, self.c_prims, self.c_params,
@@ -165,10 +165,11 @@ class Rasterizer:
     def alloc_grads(self, want) -> Dict[str, torch.Tensor]:
         out = {}
         for k in want:
-            if k in ("cam_R", "cam_t"):
+            if k in ("cam_R", "cam_t", "cam_K"):
                 if self.kind != 2:
                     continue
-                out[k] = torch.zeros((self.V, 9 if k == "cam_R" else 3), dtype=torch.float32, device=self.device)
+                out[k] = torch.zeros((self.V, {"cam_R": 9, "cam_t": 3, "cam_K": 4}[k]), dtype=torch.float32,
+                                     device=self.device)
             else:
                 src = self.t.get(k)
                 if src is None:

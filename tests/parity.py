@@ -170,7 +170,7 @@ def compare_backward(rz, orc, ref, g_views, masked=None, names=None, view_groups
             grads = rz.backward(dimg, view_begin=b, view_count=c, grads=grads, accumulate=grads is not None)
     torch.cuda.synchronize()
     og = orc.backward(masked, with_mag=True)
-    names = names or [k for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t") if k in grads]
+    names = names or [k for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t", "cam_K") if k in grads]
     worst = 0.0
     per = {}
     for k in names:
