@@ -106,6 +106,8 @@ class Oracle:
         self.kind, self.n, self.C = s.kind, s.n, s.channels
         self.cams = list(cams if cams is not None else s.cams)
         self.V = len(self.cams)
+        if s.kind != 2 and any(c.kind == 2 for c in self.cams):
+            raise ValueError("orthographic views are defined for spheres only")
         self.params = params if params is not None else s.params
         self.K = self.params.top_k
         pick = lambda a, b: _d(a if a is not None else b)

@@ -31,7 +31,7 @@
 #endif
 
 enum { PRIM_GAUSS2D = 0, PRIM_GAUSS3D = 1, PRIM_SPHERE = 2 };
-enum { CAM_PINHOLE = 0, CAM_SPHERICAL = 1 };
+enum { CAM_PINHOLE = 0, CAM_SPHERICAL = 1, CAM_ORTHO = 2 };
 
 /* near-tie flag bits (per pixel) */
 enum {
@@ -201,12 +201,32 @@ static void project_one(const octx *X, int view, int i, orec *o) {
     double q[3];
     cam_xform(c, p, q);
     double fmin = c->fx < c->fy ? c->fx : c->fy;
-    double rfl = 0.75 * q[2] / fmin;          /* at least one pixel (Pulsar B.1.1) */
+    int ortho = c->kind == CAM_ORTHO;
+    /* at least one pixel (Pulsar B.1.1): a projected radius of 0.75 px */
+    double rfl = ortho ? 0.75 / fmin : 0.75 * q[2] / fmin;
     double re = r >= rfl ? r : rfl;
     o->m[0] = q[0]; o->m[1] = q[1]; o->m[2] = q[2];
     o->r = r; o->r_eff = re; o->floored = r < rfl;
     double zf = q[2] - re;
     if (!(zf > c->znear) || !(zf > 0.0) || !isfinite(r) || !(r > 0.0)) { set_rect_empty(o); return; }
+    if (ortho) {
+      /* parallel projection: the sphere's outline is the circle of radius r_eff */
+      double xl = c->fx * (q[0] - re) + c->cx, xh = c->fx * (q[0] + re) + c->cx;
+      double yl = c->fy * (q[1] - re) + c->cy, yh = c->fy * (q[1] + re) + c->cy;
+      if (!isfinite(xl) || !isfinite(xh) || !isfinite(yl) || !isfinite(yh)) { set_rect_empty(o); return; }
+      o->u = c->fx * q[0] + c->cx;
+      o->v = c->fy * q[1] + c->cy;
+      o->depth = zf;
+      o->key_depth = (float)zf;
+      double span = c->zfar - c->znear;
+      o->zhat = (c->zfar - q[2]) / span;
+      o->e = exp(o->opac * o->zhat / X->gamma);
+      o->b = exp(((c->zfar - (double)o->key_depth) / span) / X->gamma);
+      double area = M_PI * (c->fx * r) * (c->fy * r);
+      o->gated = !(area > 3.0);
+      set_rect(c, o, xl, xh, yl, yh);
+      return;
+    }
     /* tangent planes through the sensor origin, trig-free (Pulsar B.1.1) */
     double den = q[2] * q[2] - re * re;
     double sx = sqrt(q[0] * q[0] + q[2] * q[2] - re * re);
@@ -230,6 +250,7 @@ static void project_one(const octx *X, int view, int i, orec *o) {
     return;
   }
   double m[3], u, v, sxx, sxy, syy;
+  if (c->kind == CAM_ORTHO) { set_rect_empty(o); return; }   /* orthographic views: spheres only */
   if (X->kind == PRIM_GAUSS2D) {
     u = (double)X->pos[2 * i];
     v = (double)X->pos[2 * i + 1];
@@ -429,13 +450,35 @@ void or_get_pairs(const octx *X, uint64_t *keys, uint32_t *vals, uint32_t *range
 /* Per-pixel compositing                                                      */
 /* ------------------------------------------------------------------------- */
 
+/* The ray through pixel centre (px, py) in sensor coordinates, o + s d. Pulsar
+ * B.1.1 treats two sphere cameras. Pinhole: o = 0, d = ((px - cx)/fx,
+ * (py - cy)/fy, 1). Orthographic: every ray runs along +z, o = ((px - cx)/fx,
+ * (py - cy)/fy, 0) and d = (0, 0, 1) (fx, fy in pixels per world unit). */
+static void pixel_ray(const ocam *c, double px, double py, double o[3], double d[3]) {
+  double x = (px - c->cx) / c->fx, y = (py - c->cy) / c->fy;
+  if (c->kind == CAM_ORTHO) {
+    o[0] = x; o[1] = y; o[2] = 0.0;
+    d[0] = 0.0; d[1] = 0.0; d[2] = 1.0;
+  } else {
+    o[0] = 0.0; o[1] = 0.0; o[2] = 0.0;
+    d[0] = x; d[1] = y; d[2] = 1.0;
+  }
+}
+
+/* Squared orthogonal distance of point q from the ray o + s d (Pulsar A). */
+static double ray_dist2(const double q[3], const double o[3], const double d[3], double dd) {
+  double e[3] = {q[0] - o[0], q[1] - o[1], q[2] - o[2]};
+  double ed = e[0] * d[0] + e[1] * d[1] + e[2] * d[2];
+  return e[0] * e[0] + e[1] * e[1] + e[2] * e[2] - ed * ed / dd;
+}
+
 typedef struct {          /* per-entry trace kept for the backward pass */
   int idx;                /* position in the tile list */
   uint32_t rec;
   double alpha, T_before, G, dx, dy;   /* alpha path */
   int clamped;
   double w, D, dist2;                  /* sphere path */
-  double d[3], dd;
+  double o[3], d[3], dd;
 } otrace;
 
 typedef struct {
@@ -473,7 +516,8 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
   for (int k = 0; k < 16; k++) P->top[k] = -1;
   double px = (double)i + 0.5, py = (double)j + 0.5;
   if (X->kind == PRIM_SPHERE) {
-    double d[3] = {(px - c->cx) / c->fx, (py - c->cy) / c->fy, 1.0};
+    double ro[3], d[3];
+    pixel_ray(c, px, py, ro, d);
     double dd = d[0] * d[0] + d[1] * d[1] + d[2] * d[2];
     double N = X->bg_weight;
     double S[64];
@@ -484,10 +528,7 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       double lim = X->tau * N;
       if (fabs(o->b - lim) <= 2e-5 * lim) P->flags |= FLAG_SPH_STOP;
       if (o->b < lim) break;                                   /* early stop (Pulsar 3.2, B.1.3) */
-      const double *q = o->m;
-      double qd = q[0] * d[0] + q[1] * d[1] + q[2] * d[2];
-      double qq = q[0] * q[0] + q[1] * q[1] + q[2] * q[2];
-      double dist2 = qq - qd * qd / dd;                        /* orthogonal ray distance^2 */
+      double dist2 = ray_dist2(o->m, ro, d, dd);               /* orthogonal ray distance^2 */
       double r2 = o->r_eff * o->r_eff;
       double D = 1.0 - dist2 / r2;
       if (fabs(D) < 1e-8 && P->ntop < X->K) P->flags |= FLAG_SPH_EDGE;
@@ -503,7 +544,8 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
         if (tr && ntr < tr_cap) {
           otrace *r = &tr[ntr++];
           r->idx = (int)(p - s); r->rec = X->pair_id[p]; r->w = w; r->D = D; r->dist2 = dist2;
-          r->d[0] = d[0]; r->d[1] = d[1]; r->d[2] = d[2]; r->dd = dd;
+          for (int a = 0; a < 3; a++) { r->o[a] = ro[a]; r->d[a] = d[a]; }
+          r->dd = dd;
         }
       }
     }
@@ -601,16 +643,15 @@ void or_render_bruteforce(const octx *X, int v, double *img, double *T, double *
       int ntop = 0;
       if (top) for (int k = 0; k < X->K; k++) top[q * X->K + k] = -1;
       if (X->kind == PRIM_SPHERE) {
-        double d[3] = {(px - c->cx) / c->fx, (py - c->cy) / c->fy, 1.0};
+        double ro[3], d[3];
+        pixel_ray(c, px, py, ro, d);
         double dd = d[0] * d[0] + d[1] * d[1] + d[2] * d[2];
         double Nn = X->bg_weight, S[64];
         for (int ch = 0; ch < C; ch++) S[ch] = X->bg_weight * X->bg[ch];
         for (int k = 0; k < m; k++) {
           const orec *o = &X->rec[ord[k].id];
           if (o->b < X->tau * Nn) break;
-          const double *qq = o->m;
-          double qd = qq[0] * d[0] + qq[1] * d[1] + qq[2] * d[2];
-          double dist2 = (qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2]) - qd * qd / dd;
+          double dist2 = ray_dist2(o->m, ro, d, dd);
           double r2 = o->r_eff * o->r_eff;
           if (!(dist2 < r2)) continue;
           double w = o->opac * (1.0 - dist2 / r2) * o->e;
@@ -701,20 +742,29 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
       double dzhat = dw * r->w * oo / X->gamma;
       double r2 = o->r_eff * o->r_eff;
       double ddist2 = -dD / r2;
-      const double *q = o->m;
+      /* dist2 = |e|^2 - (e.d)^2/|d|^2 with e = q - o: d dist2 / d q = 2 (e - (e.d) d/|d|^2) */
+      double q[3] = {o->m[0] - r->o[0], o->m[1] - r->o[1], o->m[2] - r->o[2]};
       double qd = q[0] * r->d[0] + q[1] * r->d[1] + q[2] * r->d[2];
       for (int a = 0; a < 3; a++) A[a] += ddist2 * (2.0 * q[a] - 2.0 * qd * r->d[a] / r->dd);
       A[2] += dzhat * (-1.0 / (c->zfar - c->znear));
       if (!o->floored) A[3] += dD * 2.0 * r->dist2 / (r2 * o->r_eff);
       /* Intrinsics (Pulsar 3.2 and appendix A: gradients for focal length and
-         sensor placement). The pixel's ray d = ((px - cx)/fx, (py - cy)/fy, 1)
-         moves with them; d dist2 / d d_a = -2 (q.d)/|d|^2 (q_a - (q.d) d_a/|d|^2),
-         d d_a / d f_a = -d_a / f_a, d d_a / d c_a = -1 / f_a. The one-pixel floor
-         of r_eff is held fixed, as for the position. */
+         sensor placement). x = (px - cx)/fx and y = (py - cy)/fy move with them,
+         d x / d fx = -x / fx, d x / d cx = -1 / fx. Pinhole: (x, y) are d's first
+         components, d dist2 / d d_a = -2 (e.d)/|d|^2 (e_a - (e.d) d_a/|d|^2).
+         Orthographic: (x, y) are o's, d dist2 / d o_a = -d dist2 / d q_a. The
+         one-pixel floor of r_eff is held fixed, as for the position. */
       for (int a = 0; a < 2; a++) {
         double f = a == 0 ? c->fx : c->fy;
-        double gd = ddist2 * (-2.0 * qd / r->dd) * (q[a] - qd * r->d[a] / r->dd);
-        kacc[a] += gd * (-r->d[a] / f);
+        double gd, xa;
+        if (c->kind == CAM_ORTHO) {
+          gd = -ddist2 * (2.0 * q[a] - 2.0 * qd * r->d[a] / r->dd);
+          xa = r->o[a];
+        } else {
+          gd = ddist2 * (-2.0 * qd / r->dd) * (q[a] - qd * r->d[a] / r->dd);
+          xa = r->d[a];
+        }
+        kacc[a] += gd * (-xa / f);
         kacc[2 + a] += gd * (-1.0 / f);
       }
       if (M) {
@@ -724,8 +774,15 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
         if (!o->floored) M[3] += mD * 2.0 * r->dist2 / (r2 * o->r_eff);
         for (int a = 0; a < 2; a++) {
           double f = a == 0 ? c->fx : c->fy;
-          double mg = m2 * 2.0 * fabs(qd) / r->dd * (fabs(q[a]) + fabs(qd * r->d[a]) / r->dd);
-          kmag[a] += mg * fabs(r->d[a]) / f;
+          double mg, xa;
+          if (c->kind == CAM_ORTHO) {
+            mg = m2 * (2.0 * fabs(q[a]) + 2.0 * fabs(qd * r->d[a]) / r->dd);
+            xa = r->o[a];
+          } else {
+            mg = m2 * 2.0 * fabs(qd) / r->dd * (fabs(q[a]) + fabs(qd * r->d[a]) / r->dd);
+            xa = r->d[a];
+          }
+          kmag[a] += mg * fabs(xa) / f;
           kmag[2 + a] += mg / f;
         }
       }

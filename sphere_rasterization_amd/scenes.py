@@ -28,6 +28,7 @@ PRIM_SPHERE = 2
 
 CAM_PINHOLE = 0
 CAM_SPHERICAL = 1
+CAM_ORTHO = 2          # orthographic (spheres only): u = fx x + cx, v = fy y + cy
 
 
 def _f32(x) -> float:

@@ -340,3 +340,84 @@ def test_magnitudes_equal_grads_when_terms_share_a_sign():
                                                            sc.cams[0].width))).astype(np.float32)]
     a = orc.backward(g, with_mag=True)
     np.testing.assert_allclose(a["mag"]["feat"], a["feat"], rtol=1e-12, atol=1e-300)
+
+
+# ---- orthographic sphere camera ---------------------------------------------
+
+def _ortho_scene(rng, n, W, H, f=(6.0, 5.5), c=None, params=None, R=None, t=(0.1, -0.05, 0.2)):
+    R = np.eye(3) if R is None else R
+    c = c or (W / 2 - 0.3, H / 2 + 0.2)
+    cam = S.Camera(S.CAM_ORTHO, W, H, R, t, fx=f[0], fy=f[1], cx=c[0], cy=c[1], znear=1.0, zfar=21.0)
+    # sensor positions inside the view, world positions by inverting q = R p + t
+    loc = np.stack([(rng.uniform(0.15, 0.85, n) * W - c[0]) / f[0],
+                    (rng.uniform(0.15, 0.85, n) * H - c[1]) / f[1], rng.uniform(3, 9, n)], 1)
+    p = np.linalg.solve(np.asarray(cam.R, np.float64), (loc - np.asarray(cam.t, np.float64)).T).T
+    return cam, p
+
+
+def test_fd_spheres_orthographic():
+    """Orthographic view: positions, radii, opacities, features, R, t and intrinsics
+    against central differences of the oracle's own forward."""
+    rng = np.random.default_rng(41)
+    n = 4
+    cam, p = _ortho_scene(rng, n, 32, 30, R=TS.rotation(rng) * 0.3 + np.eye(3))
+    sc = TS.spheres(p, rng.uniform(0.6, 1.2, n), rng.uniform(0.3, 0.9, n), rng.uniform(0, 1, (n, 3)),
+                    [cam], params=S.Params(tau=0.0, gamma=0.5))
+    pr = O.Oracle(sc).proj()
+    assert not pr["gated"].any() and not pr["floored"].any()
+    g = _g(rng, sc)
+    an = _fd_check(sc, g, ["pos", "scale", "opacity", "feat"])
+    _fd_camera(sc, g, an, intrinsics=True)
+
+
+def test_autograd_xcheck_spheres_orthographic():
+    """Dense orthographic sphere blending in torch float64: rays along +z from
+    ((px - cx)/fx, (py - cy)/fy, 0), so dist^2 = (qx - ox)^2 + (qy - oy)^2; first-5
+    truncation via detach. Image and every gradient, intrinsics included."""
+    rng = np.random.default_rng(42)
+    n, W, H = 50, 40, 36
+    cam, p = _ortho_scene(rng, n, W, H, f=(5.0, 4.6), R=TS.rotation(rng), t=(0.2, 0.1, 0.3))
+    sc = TS.spheres(p, rng.uniform(0.4, 1.1, n), rng.uniform(0.2, 1.0, n), rng.uniform(0, 1, (n, 3)),
+                    [cam], params=S.Params(tau=0.0, gamma=0.3))
+    orc = O.Oracle(sc)
+    pr = orc.proj()
+    assert not pr["gated"].any() and not pr["floored"].any()
+    r = orc.render_views()[0]
+    assert (r["flags"] == 0).all() and (r["ncontrib"] > 5).any()
+    g = _g(rng, sc)
+    an = orc.backward(g)
+    P = {k: torch.tensor(np.asarray(getattr(sc, k), np.float64), requires_grad=True)
+         for k in ("pos", "scale", "opacity", "feat")}
+    Rc = torch.tensor(np.asarray(cam.R, np.float64), requires_grad=True)
+    tc = torch.tensor(np.asarray(cam.t, np.float64), requires_grad=True)
+    Kc = torch.tensor([cam.fx, cam.fy, cam.cx, cam.cy], dtype=torch.float64, requires_grad=True)
+    q = P["pos"] @ Rc.T + tc
+    gam = float(np.float32(0.3))
+    e = torch.exp(P["opacity"] * (21.0 - q[:, 2]) / 20.0 / gam)
+    ys, xs = torch.meshgrid(torch.arange(H, dtype=torch.float64) + 0.5,
+                            torch.arange(W, dtype=torch.float64) + 0.5, indexing="ij")
+    ox = ((xs - Kc[2]) / Kc[0]).reshape(-1, 1)
+    oy = ((ys - Kc[3]) / Kc[1]).reshape(-1, 1)
+    dist2 = (q[None, :, 0] - ox) ** 2 + (q[None, :, 1] - oy) ** 2
+    D = 1 - dist2 / P["scale"][None] ** 2
+    key = (q[:, 2] - P["scale"]).detach().numpy().astype(np.float32).view(np.uint32)
+    order = np.lexsort((np.arange(n), key))
+    with torch.no_grad():
+        hit = D > 0
+        rank = torch.cumsum(hit[:, order].to(torch.int64), 1)
+        first5 = torch.zeros_like(hit)
+        first5[:, order] = hit[:, order] & (rank <= 5)
+    w = torch.where(hit, P["opacity"][None] * D * e[None], torch.zeros_like(D))
+    w_live = torch.where(first5, w, torch.zeros_like(w))
+    w_dead = torch.where(first5, torch.zeros_like(w), w).detach()
+    N = 1.0 + (w_live + w_dead).sum(1)
+    img = (w_live @ P["feat"] + w_dead @ P["feat"].detach()) / N[:, None]
+    loss = (img.T * torch.tensor(g[0].reshape(3, -1), dtype=torch.float64)).sum()
+    loss.backward()
+    np.testing.assert_allclose(r["img"].reshape(3, -1), img.detach().numpy().T, atol=1e-12)
+    for k in ("pos", "scale", "opacity", "feat"):
+        ref = P[k].grad.numpy()
+        np.testing.assert_allclose(an[k], ref, rtol=1e-9, atol=1e-11 * np.abs(ref).max(), err_msg=k)
+    np.testing.assert_allclose(an["cam_R"][0], Rc.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(an["cam_t"][0], tc.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(an["cam_K"][0], Kc.grad.numpy(), rtol=1e-9, atol=1e-12)

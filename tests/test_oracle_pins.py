@@ -288,6 +288,91 @@ def test_tangent_box_contains_every_hit_pixel():
             assert d[int(v), int(u)] < pr["r_eff"][i]
 
 
+# ------------------------------------------------ orthographic sphere camera
+
+def _ortho_cam(W, H, fx=8.0, fy=7.5, cx=None, cy=None, t=(0.0, 0.0, 0.0)):
+    return S.Camera(S.CAM_ORTHO, W, H, np.eye(3), t, fx=fx, fy=fy, cx=W / 2 if cx is None else cx,
+                    cy=H / 2 if cy is None else cy, znear=1.0, zfar=21.0)
+
+
+def _ortho_spheres(rng, n, W, H, rmin=0.01, rmax=0.6):
+    cam = _ortho_cam(W, H)
+    u, v = rng.uniform(-2, W + 2, n), rng.uniform(-2, H + 2, n)
+    p = np.stack([(u - cam.cx) / cam.fx, (v - cam.cy) / cam.fy, rng.uniform(2, 20, n)], 1)
+    r = np.exp(rng.uniform(math.log(rmin), math.log(rmax), n))
+    return TS.spheres(p, r, rng.uniform(0.1, 1.0, n), rng.uniform(0, 1, (n, 3)), [cam])
+
+
+def _ortho_dist(q, cam, W, H):
+    """Distance of q from each pixel's ray, a line parallel to the optical axis
+    through ((px - cx)/fx, (py - cy)/fy) in the sensor frame."""
+    ys, xs = np.mgrid[0:H, 0:W] + 0.5
+    return np.hypot((xs - cam.cx) / cam.fx - q[0], (ys - cam.cy) / cam.fy - q[1])
+
+
+def test_ortho_sphere_single_closed_form():
+    """One sphere seen by an orthographic camera: C = w f / (w + w_bg) with
+    w = o (1 - dist^2/r^2) exp(o zhat / gamma), dist the offset from the axis-parallel ray."""
+    W, H = 40, 32
+    cam = _ortho_cam(W, H, t=(0.1, -0.2, 0.5))
+    prm = S.Params(gamma=1.0)
+    p, r, o, f = f64([0.3, -0.2, 5.0]), f64(1.5), f64(0.6), f64([0.25, 0.75])
+    sc = TS.spheres([p], [r], [o], [f], [cam], params=prm)
+    res = O.Oracle(sc).render_views()[0]
+    q = p + f64(cam.t)
+    dist = _ortho_dist(q, cam, W, H)
+    D = np.clip(1 - dist ** 2 / r ** 2, 0, None)
+    w = o * D * np.exp(o * ((21.0 - q[2]) / 20.0) / 1.0)
+    exp = w[None] * f[:, None, None] / (w + 1.0)[None]
+    np.testing.assert_allclose(res["img"], exp, atol=1e-12)
+    np.testing.assert_allclose(res["N"], 1.0 + w, rtol=1e-12)
+    # the disc covers about pi (fx r)(fy r) pixel centres
+    assert abs((D > 0).sum() - math.pi * cam.fx * r * cam.fy * r) < 0.1 * math.pi * cam.fx * r * cam.fy * r
+
+
+def test_ortho_depth_moves_only_the_weight():
+    """Orthographic projection: moving a sphere along the optical axis keeps its
+    footprint; with no background weight a lone sphere's colour is its feature."""
+    W, H = 24, 24
+    cam = _ortho_cam(W, H)
+    prm = S.Params(gamma=1.0, bg_weight=0.0, tau=0.0)
+    out = []
+    for z in (3.0, 11.0):
+        sc = TS.spheres([[0.2, -0.3, z]], [1.0], [0.7], [[0.4, 0.9]], [cam], params=prm)
+        out.append(O.Oracle(sc).render_views()[0])
+    np.testing.assert_array_equal(out[0]["ncontrib"], out[1]["ncontrib"])
+    hit = out[0]["ncontrib"] > 0
+    assert hit.sum() > 20
+    np.testing.assert_allclose(out[0]["img"][:, hit], np.array([[0.4], [0.9]]) * np.ones(hit.sum()), rtol=1e-6)
+
+
+def test_ortho_box_contains_every_hit_pixel():
+    """Brute-force ray test over all pixels for 600 spheres under the orthographic
+    camera: every pixel within r_eff of its ray lies inside the box; every sphere
+    whose centre projects into the image keeps at least one pixel (one-pixel floor)."""
+    rng = np.random.default_rng(19)
+    W, H = 64, 56
+    sc = _ortho_spheres(rng, 600, W, H, rmin=0.003, rmax=1.2)
+    cam = sc.cams[0]
+    pr = O.Oracle(sc).proj()
+    nfloor = 0
+    for i in range(sc.n):
+        if not pr["valid"][i]:
+            continue
+        q = np.array([pr["m0"][i], pr["m1"][i], pr["m2"][i]])
+        d = _ortho_dist(q, cam, W, H)
+        ys, xs = np.nonzero(d < pr["r_eff"][i])
+        if len(xs):
+            assert xs.min() >= pr["x0"][i] and xs.max() <= pr["x1"][i]
+            assert ys.min() >= pr["y0"][i] and ys.max() <= pr["y1"][i]
+        u = cam.fx * q[0] + cam.cx
+        v = cam.fy * q[1] + cam.cy
+        if 0 <= u < W and 0 <= v < H:
+            assert d[int(v), int(u)] < pr["r_eff"][i]
+        nfloor += int(pr["floored"][i])
+    assert nfloor > 10
+
+
 # ---------------------------------------------------------------- tiles and sort
 
 def _lexsort_pairs(orc):
@@ -308,7 +393,7 @@ def _lexsort_pairs(orc):
     return (tiles[order].astype(np.uint64) << np.uint64(32)) | bits[order].astype(np.uint64), ids[order]
 
 
-@pytest.mark.parametrize("which", ["2d", "3d", "sphere", "lidar"])
+@pytest.mark.parametrize("which", ["2d", "3d", "sphere", "ortho", "lidar"])
 def test_sort_order_equals_lexsort(which):
     rng = np.random.default_rng(3)
     if which == "2d":
@@ -317,6 +402,8 @@ def test_sort_order_equals_lexsort(which):
         sc = S.gauss3d(n=20000, width=96, height=80)
     elif which == "sphere":
         sc = TS.random_spheres(rng, 3000, 80, 64, 70.0, rmin=0.01, rmax=0.2)
+    elif which == "ortho":
+        sc = _ortho_spheres(rng, 3000, 80, 64)
     else:
         sc = S.gauss3d(n=2000)
         sc.cams = [TS.lidar(256, 32, t=[0.0, 0.0, 0.0])]
@@ -332,7 +419,7 @@ def test_sort_order_equals_lexsort(which):
         assert ranges[tile, 0] == sel[0] and ranges[tile, 1] == sel[-1] + 1
 
 
-@pytest.mark.parametrize("which", ["2d", "3d", "sphere", "lidar"])
+@pytest.mark.parametrize("which", ["2d", "3d", "sphere", "ortho", "lidar"])
 def test_tile_lists_equal_bruteforce(which):
     """Compositing over each tile's list equals compositing over every primitive in
     global (depth bits, id) order with no tiles at all, bit for bit."""
@@ -343,6 +430,8 @@ def test_tile_lists_equal_bruteforce(which):
         sc = S.gauss3d(n=20000, width=96, height=80)
     elif which == "sphere":
         sc = TS.random_spheres(rng, 3000, 80, 64, 70.0, rmin=0.01, rmax=0.2)
+    elif which == "ortho":
+        sc = _ortho_spheres(rng, 3000, 80, 64)
     else:
         sc = S.gauss3d(n=3000)
         sc.cams = [TS.lidar(256, 32)]
