@@ -55,7 +55,8 @@ typedef enum {
 
 typedef enum {
   SPLAT_CAM_PINHOLE = 0,
-  SPLAT_CAM_SPHERICAL = 1       /* lidar-like range view: columns = azimuth, rows = elevation */
+  SPLAT_CAM_SPHERICAL = 1,      /* lidar-like range view: columns = azimuth, rows = elevation */
+  SPLAT_CAM_ORTHOGRAPHIC = 2    /* parallel projection along +z (spheres only, Pulsar B.1.1) */
 } splat_cam_kind;
 
 #define SPLAT_MAX_VIEWS 16
@@ -63,6 +64,10 @@ typedef enum {
 
 /* HOST struct, one per view. Sensor point q = R x + t (R row-major).
  * Pinhole (x right, y down, z forward): u = fx qx/qz + cx, v = fy qy/qz + cy.
+ * Orthographic (same axes; spheres only, other primitives return
+ *   SPLAT_ERR_UNSUPPORTED): u = fx qx + cx, v = fy qy + cy with fx, fy in pixels per
+ *   world unit; the ray of pixel centre (px, py) runs along +z through
+ *   ((px - cx)/fx, (py - cy)/fy, 0), and a sphere keeps a radius of at least 0.75 px.
  * Spherical (x forward, y left, z up; width must be a multiple of 16):
  *   u = (pi - atan2(qy, qx)) W / (2 pi), v = (el_max - atan2(qz, |q_xy|)) H / (el_max - el_min).
  * znear culls (depth <= znear); for spheres znear/zfar also normalise depth. */

@@ -103,13 +103,14 @@ int build_views(const splat_camera *cams, int n_views, int channels, ViewTable *
   for (int v = 0; v < n_views; v++) {
     const splat_camera &c = cams[v];
     ViewDev &d = vt->v[v];
-    CHECK(c.kind == SPLAT_CAM_PINHOLE || c.kind == SPLAT_CAM_SPHERICAL, SPLAT_ERR_INVALID_ARG, "camera kind");
+    CHECK(c.kind == SPLAT_CAM_PINHOLE || c.kind == SPLAT_CAM_SPHERICAL || c.kind == SPLAT_CAM_ORTHOGRAPHIC,
+          SPLAT_ERR_INVALID_ARG, "camera kind");
     CHECK(c.width > 0 && c.height > 0 && c.width <= (1 << 20) && c.height <= (1 << 20), SPLAT_ERR_INVALID_ARG,
           "camera size");
     for (int k = 0; k < 9; k++) CHECK(isfinite(c.R[k]), SPLAT_ERR_INVALID_ARG, "camera R not finite");
     for (int k = 0; k < 3; k++) CHECK(isfinite(c.t[k]), SPLAT_ERR_INVALID_ARG, "camera t not finite");
     CHECK(isfinite(c.znear) && isfinite(c.zfar) && c.znear >= 0.0f, SPLAT_ERR_INVALID_ARG, "camera depth range");
-    if (c.kind == SPLAT_CAM_PINHOLE) {
+    if (c.kind != SPLAT_CAM_SPHERICAL) {
       CHECK(isfinite(c.fx) && isfinite(c.fy) && c.fx > 0.0f && c.fy > 0.0f, SPLAT_ERR_INVALID_ARG, "focal length");
       CHECK(isfinite(c.cx) && isfinite(c.cy), SPLAT_ERR_INVALID_ARG, "principal point");
     } else {
@@ -148,18 +149,20 @@ int check_prims(const splat_prims *p, const ViewTable &vt) {
   CHECK(p->n >= 0, SPLAT_ERR_INVALID_ARG, "negative n");
   CHECK(p->channels >= 0 && p->channels <= SPLAT_MAX_CHANNELS, SPLAT_ERR_INVALID_ARG, "channels out of range");
   CHECK((long long)vt.n * p->n < (1ll << 32) - 1, SPLAT_ERR_INVALID_ARG, "too many records");
-  bool any_pin = false, any_sph = false;
+  bool any_pin = false, any_sph = false, any_orth = false;
   for (int v = 0; v < vt.n; v++) {
     if (vt.v[v].kind == SPLAT_CAM_SPHERICAL) any_sph = true;
+    else if (vt.v[v].kind == SPLAT_CAM_ORTHOGRAPHIC) any_orth = true;
     else any_pin = true;
   }
-  if (p->kind == SPLAT_PRIM_SPHERE) CHECK(!any_sph, SPLAT_ERR_UNSUPPORTED, "spheres need pinhole views");
+  if (p->kind == SPLAT_PRIM_SPHERE) CHECK(!any_sph, SPLAT_ERR_UNSUPPORTED, "spheres need pinhole or orthographic views");
+  else CHECK(!any_orth, SPLAT_ERR_UNSUPPORTED, "orthographic views are for spheres only");
   if (p->kind == SPLAT_PRIM_GAUSS2D) CHECK(!any_sph, SPLAT_ERR_UNSUPPORTED, "screen-space Gaussians need pinhole views");
   if (p->n == 0) return SPLAT_OK;
   CHECK(p->pos && p->scale && p->opacity, SPLAT_ERR_INVALID_ARG, "missing primitive arrays");
   if (p->kind == SPLAT_PRIM_GAUSS3D) CHECK(p->rot != nullptr, SPLAT_ERR_INVALID_ARG, "missing rotations");
   if (p->kind == SPLAT_PRIM_GAUSS2D) CHECK(p->depth != nullptr, SPLAT_ERR_INVALID_ARG, "missing depths");
-  if (any_pin) CHECK(p->channels >= 1 && p->feat != nullptr, SPLAT_ERR_INVALID_ARG, "missing features");
+  if (any_pin || any_orth) CHECK(p->channels >= 1 && p->feat != nullptr, SPLAT_ERR_INVALID_ARG, "missing features");
   return SPLAT_OK;
 }
 

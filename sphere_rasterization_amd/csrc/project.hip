@@ -115,34 +115,48 @@ __device__ __forceinline__ bool project_one(const ViewDev &c, const PrimArgs &P,
     double r = (double)pr;
     double fx = (double)c.fx, fy = (double)c.fy;
     double fmin = fx < fy ? fx : fy;
-    double rfl = 0.75 * q[2] / fmin;               // every sphere keeps at least one pixel
+    const bool orth = c.kind == SPLAT_CAM_ORTHOGRAPHIC;
+    // every sphere keeps at least one pixel: a projected radius of 0.75 px
+    double rfl = orth ? 0.75 / fmin : 0.75 * q[2] / fmin;
     double re = r >= rfl ? r : rfl;
     double zf = q[2] - re;
     if (!(zf > (double)c.znear) || !(zf > 0.0) || !isfinite(r) || !(r > 0.0)) { write_culled(L, k, counts); return false; }
-    double den = q[2] * q[2] - re * re;
-    double sx = sqrt(q[0] * q[0] + q[2] * q[2] - re * re);
-    double sy = sqrt(q[1] * q[1] + q[2] * q[2] - re * re);
-    double xl = fx * ((q[0] * q[2] - re * sx) / den) + (double)c.cx;
-    double xh = fx * ((q[0] * q[2] + re * sx) / den) + (double)c.cx;
-    double yl = fy * ((q[1] * q[2] - re * sy) / den) + (double)c.cy;
-    double yh = fy * ((q[1] * q[2] + re * sy) / den) + (double)c.cy;
+    double xl, xh, yl, yh;
+    if (orth) {
+      // parallel projection: the outline is the circle of radius r_eff
+      xl = fx * (q[0] - re) + (double)c.cx;
+      xh = fx * (q[0] + re) + (double)c.cx;
+      yl = fy * (q[1] - re) + (double)c.cy;
+      yh = fy * (q[1] + re) + (double)c.cy;
+    } else {
+      // tangent planes through the sensor origin
+      double den = q[2] * q[2] - re * re;
+      double sx = sqrt(q[0] * q[0] + q[2] * q[2] - re * re);
+      double sy = sqrt(q[1] * q[1] + q[2] * q[2] - re * re);
+      xl = fx * ((q[0] * q[2] - re * sx) / den) + (double)c.cx;
+      xh = fx * ((q[0] * q[2] + re * sx) / den) + (double)c.cx;
+      yl = fy * ((q[1] * q[2] - re * sy) / den) + (double)c.cy;
+      yh = fy * ((q[1] * q[2] + re * sy) / den) + (double)c.cy;
+    }
     if (!isfinite(xl) || !isfinite(xh) || !isfinite(yl) || !isfinite(yh)) { write_culled(L, k, counts); return false; }
     Rect rc = make_rect(c, xl, xh, yl, yh);
     if (!rc.valid) { write_culled(L, k, counts); return false; }
     float key = (float)zf;
     write_rect(L, k, counts, rc, key);
-    double u = fx * q[0] / q[2] + (double)c.cx;
-    double v = fy * q[1] / q[2] + (double)c.cy;
+    double u = (orth ? fx * q[0] : fx * q[0] / q[2]) + (double)c.cx;
+    double v = (orth ? fy * q[1] : fy * q[1] / q[2]) + (double)c.cy;
     double span = (double)c.zfar - (double)c.znear;
     double zhat = ((double)c.zfar - q[2]) / span;
     double e = exp(o * zhat / P.gamma);
     double bnd = exp((((double)c.zfar - (double)key) / span) / P.gamma);
-    double area = kPi * (fx * r / q[2]) * (fy * r / q[2]);
+    double area = orth ? kPi * (fx * r) * (fy * r) : kPi * (fx * r / q[2]) * (fy * r / q[2]);
     int floored = r < rfl, gated = !(area > 3.0);
     DrawRec d;
-    d.u = q[0] / q[2];                 // normalised centre a = q / qz
-    d.v = q[1] / q[2];
-    d.a = q[2] * q[2] / (re * re);     // A = qz^2 / r_eff^2
+    // pinhole: normalised centre a = q / qz and A = qz^2 / r_eff^2;
+    // orthographic: (qx, qy) and A = 1 / r_eff^2
+    d.u = orth ? q[0] : q[0] / q[2];
+    d.v = orth ? q[1] : q[1] / q[2];
+    d.a = orth ? 1.0 / (re * re) : q[2] * q[2] / (re * re);
     d.b = u;                           // projected centre (pixels), informational
     d.c = v;
     d.w = (float)(o * e);

@@ -598,6 +598,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   const double inv_span = 1.0 / ((double)c.zfar - (double)c.znear);
   const float igam = 1.0f / A.gamma;
   const long long vbase = (long long)view * A.n;
+  // orthographic views: a = (qx, qy), the ray along +z through (x, y, 0); dist^2 =
+  // |(x, y) - a|^2, whose gradient in q is -2 (sx, sy, 0) (no cross term, no qz scale)
+  const bool orth = c.kind == SPLAT_CAM_ORTHOGRAPHIC;
+  const double crs = orth ? 0.0 : 1.0;
 
   for (uint32_t b = 0; b < npos; b += BT) {
     const uint32_t cnt = min((uint32_t)BT, npos - b);
@@ -637,7 +641,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
         const float oe = x.y;
         // D = 1 - A g |a x d|^2 with a x d from the offsets sx = x - ax, sy = y - ay
         const double sx = ray.x - aa.x, sy = ray.y - aa.y;
-        const double cr = aa.x * sy - aa.y * sx;
+        const double cr = (aa.x * sy - aa.y * sx) * crs;
         const double Dd = 1.0 - Ai.x * ray.g * (sx * sx + sy * sy + cr * cr);
         const float w = oe * (float)Dd;
         float dw = 0.0f;
@@ -654,16 +658,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
           const double dD = (double)dw * (double)oe;
           const double dz = (double)dw * (double)w * (double)x.w;
           const double dd2 = -dD * Ai.y * Ai.y;
-          const double c1 = (ray.x * sx + ray.y * sy) * ray.g;
-          const double k2 = 2.0 * dd2 * (double)x.x;
+          const double c1 = (ray.x * sx + ray.y * sy) * ray.g * crs;
+          const double k2 = 2.0 * dd2 * (orth ? 1.0 : (double)x.x);
           const double gq0 = k2 * (c1 * ray.x - sx), gq1 = k2 * (c1 * ray.y - sy);
           v[0] = (float)gq0;
           v[1] = (float)gq1;
           v[2] = (float)(k2 * c1 - dz * inv_span);
           if (!(flags & 1)) v[3] = (float)(dD * 2.0 * (1.0 - Dd) * Ai.y);
           // the ray: d dist^2 / d d = -((q.d) / |d|^2) d dist^2 / d q, with
-          // (q.d) / |d|^2 = qz (1 - c1)
-          const double s = (double)x.x * (1.0 - c1);
+          // (q.d) / |d|^2 = qz (1 - c1); orthographic: d dist^2 / d (x, y) = -d dist^2 / d (qx, qy)
+          const double s = orth ? 1.0 : (double)x.x * (1.0 - c1);
           kgx = kgx - s * gq0;
           kgy = kgy - s * gq1;
         }

@@ -200,10 +200,14 @@ static inline int channel_bucket(int C) {
 // the terms reach (8 px / r_px)^2 while near the rim their sum is ~D, and a
 // dominant sphere's weight is proportional to D there. On CDNA4 an fp64 FMA
 // issues at the non-packed fp32 rate.
+// Orthographic views: the pixel's ray runs along +z through (x, y, 0), the
+// record holds a = (qx, qy) and A = 1 / r_eff^2, and D = 1 - A |(x, y) - a|^2,
+// the same quadratic with g = 1.
 // ---------------------------------------------------------------------------
 struct SphereRay {
-  double x, y;       // normalised ray direction (x, y, 1) through the pixel centre
-  double g;          // 1 / (1 + x^2 + y^2)
+  double x, y;       // (x, y) = ((px - cx) / fx, (py - cy) / fy): the ray direction
+                     // (x, y, 1) (pinhole) or the ray origin (x, y, 0) (orthographic)
+  double g;          // 1 / (1 + x^2 + y^2) (pinhole), 1 (orthographic)
   double X, Y;       // pixel centre minus tile centre (pixels)
 };
 
@@ -212,7 +216,7 @@ __device__ __forceinline__ SphereRay sphere_ray(const ViewDev &c, const TilePix 
   const double ifx = 1.0 / (double)c.fx, ify = 1.0 / (double)c.fy;
   r.x = ((double)tp.i + 0.5 - (double)c.cx) * ifx;
   r.y = ((double)tp.j + 0.5 - (double)c.cy) * ify;
-  r.g = 1.0 / (1.0 + r.x * r.x + r.y * r.y);
+  r.g = c.kind == SPLAT_CAM_ORTHOGRAPHIC ? 1.0 : 1.0 / (1.0 + r.x * r.x + r.y * r.y);
   r.X = (double)tp.pxr - 8.0;
   r.Y = (double)tp.pyr - 8.0;
   return r;
@@ -228,6 +232,18 @@ __device__ __forceinline__ SphereQuad sphere_quad(const ViewDev &c, const TilePi
   const double xc = ((double)tp.x0 + 8.0 - (double)c.cx) * ifx;     // tile-centre ray
   const double yc = ((double)tp.y0 + 8.0 - (double)c.cy) * ify;
   const double ax = d.u, ay = d.v, A = d.a;
+  if (c.kind == SPLAT_CAM_ORTHOGRAPHIC) {
+    // D = 1 - A ((xc - ax + X / fx)^2 + (yc - ay + Y / fy)^2)
+    const double ex = xc - ax, ey = yc - ay;
+    SphereQuad q;
+    q.q01.x = 1.0 - A * (ex * ex + ey * ey);
+    q.q01.y = -2.0 * A * ex * ifx;
+    q.q23.x = -2.0 * A * ey * ify;
+    q.q23.y = -A * ifx * ifx;
+    q.q45.x = 0.0;
+    q.q45.y = -A * ify * ify;
+    return q;
+  }
   // a x d = alpha + beta X + gamma Y, component by component
   const double al0 = ay - yc, ga0 = -ify;
   const double al1 = xc - ax, be1 = ifx;
@@ -252,14 +268,6 @@ __device__ __forceinline__ double sphere_num(const SphereRay &r, const double2 q
   return __builtin_fma(r.Y, v, num);
 }
 
-// Direct form for the backward: D and the normalised offsets sx = x - ax, sy = y - ay.
-__device__ __forceinline__ double sphere_D_direct(const SphereRay &r, const DrawRec &d, double &sx, double &sy) {
-  sx = r.x - d.u;
-  sy = r.y - d.v;
-  const double cr = d.u * sy - d.v * sx;
-  const double s = sx * sx + sy * sy + cr * cr;
-  return 1.0 - d.a * r.g * s;
-}
 
 // ---------------------------------------------------------------------------
 // Gaussians.

@@ -180,6 +180,27 @@ def pulsar_spheres(seed=3, n=1_000_000, width=1024, height=1024) -> Scene:
                  name="spheres_1m_1024")
 
 
+def ortho_spheres(seed=21, n=300_000, width=600, height=450, px_per_unit=100.0) -> Scene:
+    """Spheres under an orthographic camera (px_per_unit pixels per world unit):
+    uniform in image position, depth U(2, 20), radius log-uniform [0.005, 0.05]
+    (0.5 to 5 px), opacity U(0.1, 1), 3 feature channels."""
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(0.0, width, size=n)
+    v = rng.uniform(0.0, height, size=n)
+    z = rng.uniform(2.0, 20.0, size=n)
+    r = np.exp(rng.uniform(math.log(0.005), math.log(0.05), size=n))
+    o = rng.uniform(0.1, 1.0, size=n)
+    f = rng.uniform(0.0, 1.0, size=(n, 3))
+    cx, cy = width / 2 - 0.25, height / 2 + 0.5
+    qc = np.stack([(u - cx) / px_per_unit, (v - cy) / px_per_unit, z], axis=1)
+    R0 = _rot_y(10.0)
+    t0 = np.array([0.1, -0.2, 0.3])
+    p = (qc - t0) @ R0          # R0^T (q - t0), row-vector form
+    cam = Camera(CAM_ORTHO, width, height, R0, t0, fx=px_per_unit, fy=0.95 * px_per_unit, cx=cx, cy=cy,
+                 znear=1.0, zfar=21.0)
+    return Scene(PRIM_SPHERE, n, 3, _c32(p), _c32(r), _c32(o), _c32(f), cams=[cam], name="spheres_ortho")
+
+
 def _driving_geometry(rng, n):
     n_ground = int(round(0.6 * n))
     n_clust = int(round(0.3 * n))

@@ -53,6 +53,11 @@ def test_ragged_spheres():
     _run(sc, 7, "spheres 150k @1000x600 ragged")
 
 
+def test_orthographic_spheres():
+    # parallel projection: 300k spheres on 600x450 (ragged tiles), intrinsics gradients included
+    _run(S.ortho_spheres(), 9, "spheres 300k @600x450 orthographic")
+
+
 def test_ragged_gauss3d():
     sc = S.gauss3d(seed=12, n=30_000, width=500, height=300)
     _run(sc, 8, "gauss3d 30k @500x300 ragged")

@@ -76,3 +76,27 @@ def test_argument_errors_are_returned_before_any_launch():
     assert rc == L.SPLAT_ERR_CAPACITY
     rc = lib.splat_bin_sort(cams, 1, 10, 8, 8, -1, 8, 8, 8, 8, 8, 8, ws, None)
     assert rc == L.SPLAT_ERR_INVALID_ARG
+
+
+def test_orthographic_views_and_intrinsic_gradients_are_sphere_only():
+    """An orthographic view with Gaussian primitives, and intrinsic gradients
+    requested for Gaussians, are refused on the host (no launch)."""
+    from sphere_rasterization_amd.raster import make_cams, make_params
+    sc = S.pulsar_spheres(n=10)
+    prm, _ = make_params(sc.params, 3)
+    orth = make_cams([S.Camera(S.CAM_ORTHO, 64, 48, np.eye(3), np.zeros(3), fx=10.0, fy=10.0, cx=32.0, cy=24.0,
+                               znear=1.0, zfar=21.0)])
+    assert L.splat_total_tiles(orth, 1) == 4 * 3
+    bad = make_cams([S.Camera(S.CAM_ORTHO, 64, 48, np.eye(3), np.zeros(3), fx=0.0, fy=10.0, cx=32.0, cy=24.0)])
+    assert L.splat_total_tiles(bad, 1) == -1          # scale must be positive
+    lib = L.lib()
+    pr = L.splat_prims()
+    pr.kind, pr.n, pr.channels = 1, 10, 3
+    pr.pos = pr.scale = pr.rot = pr.opacity = pr.feat = 8
+    assert lib.splat_project(orth, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_UNSUPPORTED
+    pin = make_cams(sc.cams)
+    g = L.splat_grads()
+    g.cam_K = 8
+    rc = lib.splat_render_bwd(pin, 1, 0, 1, C.byref(pr), C.byref(prm), 8, 8, 8, 8, 8, 8, 8, None, None, 8,
+                              C.byref(g), 8, 1 << 40, None)
+    assert rc == L.SPLAT_ERR_UNSUPPORTED
