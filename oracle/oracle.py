@@ -57,8 +57,8 @@ def lib():
         L.or_get_pairs.argtypes = [vp, vp, vp, vp]
         L.or_render.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.or_render_bruteforce.argtypes = [vp, ip, vp, vp, vp, vp]
-        L.or_backward.argtypes = [vp] * 11
-        L.or_backward_mag.argtypes = [vp] * 19
+        L.or_backward.argtypes = [vp] * 11 + [C.c_int]
+        L.or_backward_mag.argtypes = [vp] * 19 + [C.c_int]
         _lib = L
     return _lib
 
@@ -218,8 +218,11 @@ class Oracle:
                     N=N.reshape(c.height, c.width), top=top[:, :self.K].reshape(c.height, c.width, self.K))
 
     # ---- backward -------------------------------------------------------
-    def backward(self, dimg_views, with_mag: bool = False) -> dict:
+    def backward(self, dimg_views, with_mag: bool = False, normalize: bool = False) -> dict:
         """dimg_views: list of [Cv,H,W] arrays (one per view). Returns float64 grads.
+
+        normalize (spheres): sphere gradients averaged over their contributing pixels,
+        camera contributions divided by projected area and 1e-3 (Pulsar B.2).
 
         with_mag adds "mag": for every gradient the sum of the magnitudes of the
         terms that make it up (a bound for what rounding in the terms can do to
@@ -247,9 +250,9 @@ class Oracle:
             m = outs()
             lib().or_backward_mag(*args, *[_vp(m[k]) for k in ("pos", "scale", "rot", "opacity", "feat",
                                                                "cam_R", "cam_t")],
-                                  _vp(o["cam_K"]), _vp(m["cam_K"]))
+                                  _vp(o["cam_K"]), _vp(m["cam_K"]), int(normalize))
             o["mag"] = m
         else:
-            lib().or_backward(*args, _vp(o["cam_K"]))
+            lib().or_backward(*args, _vp(o["cam_K"]), int(normalize))
         o["acc"] = acc
         return o

@@ -697,7 +697,8 @@ void or_render_bruteforce(const octx *X, int v, double *img, double *T, double *
 
 /* Per-record 2D accumulator layout, NG = 8 + C doubles:
  * Gaussians: [du, dv, d_ca, d_cb, d_cc, d_opac, d_depth, 0, d_feat...]
- * spheres:   [dq0, dq1, dq2, d_reff, d_opac, 0, 0, 0, d_feat...]          */
+ * spheres:   [dq0, dq1, dq2, d_reff, d_opac, count, 0, 0, d_feat...]
+ * (count: pixels whose recorded spheres include the record)               */
 #define G_OFF 8
 
 /* Reverse pass of one pixel; loc[list position][NG] accumulates.
@@ -724,6 +725,7 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
       double *A = loc + (size_t)r->idx * NG;
       double *M = mloc ? mloc + (size_t)r->idx * NG : NULL;
       double dw = 0.0, mdw = 0.0;
+      A[5] += 1.0;
       for (int ch = 0; ch < C; ch++) {
         double f = X->feat[(size_t)id * C + ch];
         A[G_OFF + ch] += g[ch] * r->w / N;
@@ -1005,11 +1007,14 @@ typedef struct {
  * Outputs are written (not accumulated). acc_out (optional) receives the
  * per-record 2D accumulators [V*n][8+C]. dK [V][4] receives the gradient
  * w.r.t. each view's fx, fy, cx, cy (spheres; zero for Gaussians), summed per
- * tile and then over tiles in order; mK (optional) its magnitudes. mag (optional) receives the running
- * magnitudes of every output, in the outputs' layouts. */
+ * tile and then over tiles in order; mK (optional) its magnitudes. mag
+ * (optional) receives the running magnitudes of every output, in the outputs'
+ * layouts. normalize (spheres): Pulsar B.2's normalisation, sphere gradients
+ * averaged over their contributing pixels, camera contributions divided by the
+ * projected area and by 1e-3; the intrinsic gradients stay raw per-pixel sums. */
 static void backward_core(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
                           double *dop, double *dfeat, double *dR, double *dt, double *acc_out, double *dK,
-                          double *mK, const omag *mag) {
+                          double *mK, const omag *mag, int normalize) {
   int C = X->C, NG = G_OFF + C;
   long long NV = (long long)X->V * X->n;
   double *acc = (double *)calloc((size_t)NV * NG + 1, sizeof(double));
@@ -1102,6 +1107,21 @@ static void backward_core(const octx *X, const float *dimg, double *dpos, double
       project_backward(X, k, A, lpos, ls, lr, &lo);
       if (dfeat) for (int ch = 0; ch < C; ch++) dfeat[(size_t)i * C + ch] += A[G_OFF + ch];
     }
+    /* Pulsar B.2 normalisation: a sphere's gradients averaged over the pixels that
+       sent it gradients (its recorded contributions, all views of the call) */
+    double sc = 1.0;
+    if (normalize && X->kind == PRIM_SPHERE) {
+      double cnt = 0.0;
+      for (int v = 0; v < X->V; v++) {
+        long long k = (long long)v * n + i;
+        if (X->rec[k].valid) cnt += acc[(size_t)k * NG + 5];
+      }
+      sc = cnt > 0.0 ? 1.0 / cnt : 0.0;
+      for (int a = 0; a < 3; a++) lpos[a] *= sc;
+      ls[0] *= sc;
+      lo *= sc;
+      if (dfeat) for (int ch = 0; ch < C; ch++) dfeat[(size_t)i * C + ch] *= sc;
+    }
     for (int a = 0; a < pd; a++) dpos[(size_t)i * pd + a] = lpos[a];
     for (int a = 0; a < sd; a++) dscale[(size_t)i * sd + a] = ls[a];
     if (drot) for (int a = 0; a < 4; a++) drot[(size_t)i * 4 + a] = lr[a];
@@ -1113,8 +1133,11 @@ static void backward_core(const octx *X, const float *dimg, double *dpos, double
         if (!X->rec[k].valid) continue;
         const double *M = macc + (size_t)k * NG;
         project_backward_mag(X, k, M, mp, ms, mr, &mo);
-        if (mag->feat) for (int ch = 0; ch < C; ch++) mag->feat[(size_t)i * C + ch] += M[G_OFF + ch];
+        if (mag->feat) for (int ch = 0; ch < C; ch++) mag->feat[(size_t)i * C + ch] += M[G_OFF + ch] * sc;
       }
+      for (int a = 0; a < 3; a++) mp[a] *= sc;
+      ms[0] *= sc;
+      mo *= sc;
       for (int a = 0; a < pd; a++) mag->pos[(size_t)i * pd + a] = mp[a];
       for (int a = 0; a < sd; a++) mag->scale[(size_t)i * sd + a] = ms[a];
       if (mag->rot) for (int a = 0; a < 4; a++) mag->rot[(size_t)i * 4 + a] = mr[a];
@@ -1122,20 +1145,31 @@ static void backward_core(const octx *X, const float *dimg, double *dpos, double
     }
   }
   if (X->kind == PRIM_SPHERE) {
-    /* camera: sphere-wise contributions summed over all spheres (Pulsar B.2) */
+    /* camera: sphere-wise contributions summed over all spheres (Pulsar B.2).
+       Normalised: each sphere's contribution divided by its projected area in
+       pixels, pi (fx r_eff / qz)(fy r_eff / qz) (orthographic: pi (fx r_eff)(fy r_eff)),
+       and by 1e-3. */
     for (int v = 0; v < X->V; v++)
       for (int i = 0; i < n; i++) {
         long long k = (long long)v * n + i;
         if (!X->rec[k].valid) continue;
         const double *A = acc + (size_t)k * NG;
+        const orec *o = &X->rec[k];
+        const ocam *c = &X->cams[v];
+        double sc = 1.0;
+        if (normalize) {
+          double iz = c->kind == CAM_ORTHO ? 1.0 : 1.0 / o->m[2];
+          double area = M_PI * (c->fx * o->r_eff * iz) * (c->fy * o->r_eff * iz);
+          sc = 1.0 / (area * 1e-3);
+        }
         double p[3] = {X->pos[3 * i], X->pos[3 * i + 1], X->pos[3 * i + 2]};
         for (int a = 0; a < 3; a++) {
-          for (int b = 0; b < 3; b++) dR[9 * v + 3 * a + b] += A[a] * p[b];
-          dt[3 * v + a] += A[a];
+          for (int b = 0; b < 3; b++) dR[9 * v + 3 * a + b] += A[a] * sc * p[b];
+          dt[3 * v + a] += A[a] * sc;
           if (mag) {
             const double *M = macc + (size_t)k * NG;
-            for (int b = 0; b < 3; b++) mag->R[9 * v + 3 * a + b] += M[a] * fabs(p[b]);
-            mag->t[3 * v + a] += M[a];
+            for (int b = 0; b < 3; b++) mag->R[9 * v + 3 * a + b] += M[a] * sc * fabs(p[b]);
+            mag->t[3 * v + a] += M[a] * sc;
           }
         }
       }
@@ -1146,8 +1180,9 @@ static void backward_core(const octx *X, const float *dimg, double *dpos, double
 }
 
 void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
-                 double *dop, double *dfeat, double *dR, double *dt, double *acc_out, double *dK) {
-  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, dK, NULL, NULL);
+                 double *dop, double *dfeat, double *dR, double *dt, double *acc_out, double *dK,
+                 int normalize) {
+  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, dK, NULL, NULL, normalize);
 }
 
 /* Same as or_backward, plus the magnitudes (zero-initialised by the caller,
@@ -1155,7 +1190,7 @@ void or_backward(const octx *X, const float *dimg, double *dpos, double *dscale,
 void or_backward_mag(const octx *X, const float *dimg, double *dpos, double *dscale, double *drot,
                      double *dop, double *dfeat, double *dR, double *dt, double *acc_out, double *mpos,
                      double *mscale, double *mrot, double *mop, double *mfeat, double *mR, double *mt,
-                     double *dK, double *mK) {
+                     double *dK, double *mK, int normalize) {
   omag m = {mpos, mscale, mrot, mop, mfeat, mR, mt};
-  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, dK, mK, &m);
+  backward_core(X, dimg, dpos, dscale, drot, dop, dfeat, dR, dt, acc_out, dK, mK, &m, normalize);
 }

@@ -421,3 +421,44 @@ def test_autograd_xcheck_spheres_orthographic():
     np.testing.assert_allclose(an["cam_R"][0], Rc.grad.numpy(), rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(an["cam_t"][0], tc.grad.numpy(), rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(an["cam_K"][0], Kc.grad.numpy(), rtol=1e-9, atol=1e-12)
+
+
+# ---- Pulsar's gradient normalisation ------------------------------------------
+
+@pytest.mark.parametrize("ortho", [False, True])
+def test_gradient_normalisation(ortho):
+    """Normalised sphere gradients are the raw ones divided by the number of pixels
+    that recorded the sphere (counted here from the top-K maps); camera gradients sum
+    each sphere's sensor-space gradient times p^T over its projected area (pixels,
+    from r_eff and qz) and 1e-3; intrinsic gradients are unchanged."""
+    rng = np.random.default_rng(61 + ortho)
+    W, H = 48, 40
+    if ortho:
+        cam, p = _ortho_scene(rng, 300, W, H, f=(5.0, 5.5), R=TS.rotation(rng))
+        sc = TS.spheres(p, np.exp(rng.uniform(np.log(0.05), np.log(1.0), 300)), rng.uniform(0.1, 1.0, 300),
+                        rng.uniform(0, 1, (300, 3)), [cam])
+    else:
+        sc = TS.random_spheres(rng, 300, W, H, 48.0, rmin=0.02, rmax=0.6)
+        cam = sc.cams[0]
+    orc = O.Oracle(sc)
+    r = orc.render_views()[0]
+    g = _g(rng, sc)
+    raw = orc.backward(g)
+    nrm = orc.backward(g, normalize=True)
+    top = r["top"]
+    cnt = np.bincount(top[top >= 0].ravel(), minlength=sc.n).astype(np.float64)
+    assert (cnt > 1).sum() > 50 and (cnt == 0).any()
+    inv = np.where(cnt > 0, 1.0 / np.maximum(cnt, 1.0), 0.0)
+    for k in ("pos", "scale", "opacity", "feat"):
+        a = np.asarray(raw[k], np.float64)
+        exp = a * inv.reshape((-1,) + (1,) * (a.ndim - 1))
+        np.testing.assert_allclose(nrm[k], exp, rtol=1e-12, atol=1e-300, err_msg=k)
+    pr = orc.proj()
+    valid = pr["valid"].astype(bool)
+    iz = np.ones(sc.n) if ortho else 1.0 / np.where(valid, pr["m2"], 1.0)
+    area = math.pi * (cam.fx * pr["r_eff"] * iz) * (cam.fy * pr["r_eff"] * iz)
+    w = np.where(valid, 1.0 / (np.where(valid, area, 1.0) * 1e-3), 0.0)
+    dq = raw["acc"][:, :3] * w[:, None]
+    np.testing.assert_allclose(nrm["cam_t"][0], dq.sum(0), rtol=1e-10)
+    np.testing.assert_allclose(nrm["cam_R"][0], dq.T @ np.asarray(sc.pos, np.float64), rtol=1e-10)
+    np.testing.assert_allclose(nrm["cam_K"], raw["cam_K"], rtol=0, atol=0)
