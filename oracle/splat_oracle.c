@@ -1062,7 +1062,9 @@ static void backward_core(const octx *X, const float *dimg, double *dpos, double
             g[ch] = (double)gv[(size_t)ch * c->width * c->height + (size_t)j * c->width + i];
             nz |= g[ch] != 0.0;
           }
-          if (!nz) continue;
+          /* spheres: a pixel whose upstream gradient is zero still counts among the
+             pixels a recorded sphere contributes to (gradient normalisation) */
+          if (!nz && X->kind != PRIM_SPHERE) continue;
           any = 1;
           pixel_backward(X, c->pix_off + (long long)j * c->width + i, g, loc, mloc, NG, tr, (int)len, kt, kmt);
         }

@@ -462,3 +462,20 @@ def test_gradient_normalisation(ortho):
     np.testing.assert_allclose(nrm["cam_t"][0], dq.sum(0), rtol=1e-10)
     np.testing.assert_allclose(nrm["cam_R"][0], dq.T @ np.asarray(sc.pos, np.float64), rtol=1e-10)
     np.testing.assert_allclose(nrm["cam_K"], raw["cam_K"], rtol=0, atol=0)
+
+
+def test_normalisation_counts_pixels_with_zero_upstream_gradient():
+    """A pixel with dL/dimg = 0 still counts among the pixels that recorded a
+    sphere: zeroing the upstream gradient over half the image leaves the counts
+    (hence the normalised gradient of a sphere seen only in the other half) as they were."""
+    rng = np.random.default_rng(71)
+    sc = TS.random_spheres(rng, 200, 40, 32, 40.0, rmin=0.05, rmax=0.5)
+    orc = O.Oracle(sc)
+    g = _g(rng, sc)
+    g0 = [x.copy() for x in g]
+    g0[0][:, :, 20:] = 0.0
+    a = orc.backward(g0, normalize=True)
+    r = orc.render_views()[0]
+    top = r["top"]
+    cnt = np.bincount(top[top >= 0].ravel(), minlength=sc.n).astype(np.float64)
+    np.testing.assert_array_equal(a["acc"][:, 5], cnt)
