@@ -112,12 +112,19 @@ typedef struct {
  * one-pixel radius floor, the tile rectangles and the gate are held fixed.
  * A non-NULL cam_K with Gaussian primitives returns SPLAT_ERR_UNSUPPORTED.
  * accumulate = 0: outputs are overwritten (zeroed on-stream first);
- * accumulate = 1: the call's gradients are added to what the buffers hold. */
+ * accumulate = 1: the call's gradients are added to what the buffers hold.
+ * normalize = 1 (spheres only; Pulsar B.2): each sphere's position, radius,
+ * opacity and feature gradients are divided by the number of pixels of the
+ * call's views that recorded it among their top_k; each sphere's camera (R, t)
+ * contribution is divided by its projected area in pixels, pi (fx r_eff / qz)
+ * (fy r_eff / qz) (orthographic: pi (fx r_eff)(fy r_eff)), and by 1e-3. cam_K
+ * stays the raw sum. normalize = 1 with Gaussians returns SPLAT_ERR_UNSUPPORTED. */
 typedef struct {
   float *pos, *scale, *rot, *opacity, *feat;
   float *cam_R, *cam_t;
   float *cam_K;
   int32_t accumulate;
+  int32_t normalize;
 } splat_grads;
 
 /* ---- size queries (host only, no device work) ---------------------------- */

@@ -46,7 +46,8 @@ class splat_params(C.Structure):
 class splat_grads(C.Structure):
     _fields_ = [("pos", C.c_void_p), ("scale", C.c_void_p), ("rot", C.c_void_p),
                 ("opacity", C.c_void_p), ("feat", C.c_void_p), ("cam_R", C.c_void_p),
-                ("cam_t", C.c_void_p), ("cam_K", C.c_void_p), ("accumulate", C.c_int32)]
+                ("cam_t", C.c_void_p), ("cam_K", C.c_void_p), ("accumulate", C.c_int32),
+                ("normalize", C.c_int32)]
 
 
 class SplatError(RuntimeError):

@@ -280,6 +280,7 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   } else {
     CHECK(T_final && last, SPLAT_ERR_INVALID_ARG, "Gaussian backward needs T_final and last");
     CHECK(grads->cam_K == nullptr, SPLAT_ERR_UNSUPPORTED, "intrinsic gradients are for spheres only");
+    CHECK(!grads->normalize, SPLAT_ERR_UNSUPPORTED, "gradient normalisation is for spheres only");
   }
   CHECK(workspace != nullptr, SPLAT_ERR_INVALID_ARG, "NULL workspace");
   CHECK(ws_bytes >= bwd_workspace_bytes((long long)n_views * prims->n, prims->channels), SPLAT_ERR_CAPACITY,
@@ -297,6 +298,7 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   A.accf = acc.f;
   A.cam_part = acc.cam;
   A.kslot = grads->cam_K ? acc.kslot : nullptr;
+  A.cnt = grads->normalize ? acc.cnt : nullptr;
   return launch_render_bwd(vt, view_begin, view_begin + view_count, A, prims, L.bin, grads, stream);
 }
 

@@ -75,7 +75,8 @@ __device__ __forceinline__ double wave_sum8_transposed_f64(const double (&v)[8])
 struct ZeroRanges {
   double *d0, *d1;
   float *f0, *f1;
-  long long nd0, nd1, nf0, nf1;
+  uint32_t *u0;
+  long long nd0, nd1, nf0, nf1, nu0;
 };
 
 __global__ __launch_bounds__(256) void k_zero(ZeroRanges z) {
@@ -86,7 +87,9 @@ __global__ __launch_bounds__(256) void k_zero(ZeroRanges z) {
   i -= z.nd1;
   if (i < z.nf0) { z.f0[i] = 0.0f; return; }
   i -= z.nf0;
-  if (i < z.nf1) z.f1[i] = 0.0f;
+  if (i < z.nf1) { z.f1[i] = 0.0f; return; }
+  i -= z.nf1;
+  if (i < z.nu0) z.u0[i] = 0u;
 }
 
 
@@ -547,6 +550,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   constexpr int NVP = NV | 1;                 // odd row stride of the LDS sums
   __shared__ float s_acc[BT][NVP];
   __shared__ uint32_t s_top[256 * TKS];
+  __shared__ uint32_t s_cnt[BT];             // pixels recording the entry (normalisation)
   __shared__ QuadLists s_l;
   __shared__ uint32_t s_npos;
   if (*A.overflow) return;
@@ -620,6 +624,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
 #pragma unroll
       for (int q = 0; q < NV; q++) s_acc[threadIdx.x][q] = 0.0f;
+      s_cnt[threadIdx.x] = 0u;
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
@@ -630,7 +635,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     for (int k = 0; k < lc; k++) {
       const int idx = __builtin_amdgcn_readfirstlane((int)s_l.idx[wq][k]);
       const bool mine = tgt == b + (uint32_t)idx;
-      if (ballot64(mine) == 0) continue;
+      const uint64_t bm = ballot64(mine);
+      if (bm == 0) continue;
+      if (A.cnt && lane == 0u) atomicAdd(&s_cnt[idx], (uint32_t)__popcll(bm));
       float v[NG * 8];
 #pragma unroll
       for (int q = 0; q < NG * 8; q++) v[q] = 0.0f;
@@ -694,6 +701,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
         const int e = e0 + sub;
         if (e < (int)cnt) {
           double *row = A.accg + (size_t)s_rid[e] * (5 + A.C);
+          if (A.cnt && ql == 0) {
+            const uint32_t n = s_cnt[e];
+            if (n) atomicAdd(A.cnt + s_rid[e], n);
+          }
 #pragma unroll
           for (int q0 = 0; q0 < NV; q0 += LPE) {
             const int q = q0 + ql;
@@ -742,6 +753,8 @@ struct ProjBwdArgs {
   int kind, n, C;
   const float *pos, *scale, *rot;
   const BinRec *bin;
+  const AuxRec *aux;
+  const uint32_t *cnt;      // spheres, normalised gradients: pixels that recorded each record
   const double *accg;
   const double *accf;
   double *cam_part;
@@ -755,6 +768,18 @@ __device__ __forceinline__ void put(float *p, size_t i, double x, int accumulate
 }
 
 __device__ __forceinline__ bool rec_live(const BinRec &b) { return b.ntx != 0; }
+
+// Weight of a record's camera-gradient contribution: 1, or under Pulsar's
+// normalisation (B.2) 1 / (projected area in pixels x 1e-3), the area
+// pi (fx r_eff / qz)(fy r_eff / qz) (orthographic: pi (fx r_eff)(fy r_eff)).
+__device__ __forceinline__ double cam_weight(const ViewDev &c, const ProjBwdArgs &P, size_t rec) {
+  if (!P.cnt) return 1.0;
+  if (!rec_live(P.bin[rec])) return 0.0;
+  const AuxRec a = P.aux[rec];
+  const double re = (double)a.w, iz = c.kind == SPLAT_CAM_ORTHOGRAPHIC ? 1.0 : 1.0 / (double)a.z;
+  const double area = 3.141592653589793 * ((double)c.fx * re * iz) * ((double)c.fy * re * iz);
+  return 1.0 / (area * 1e-3);
+}
 
 // Spheres, one fp64 accumulator row of 5 + C values per record. Grid-stride over
 // spheres: the chain rule sums R^T dq, d_reff, d_opac and the features over the
@@ -779,7 +804,7 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
   for (int i0 = blockIdx.x * 256; i0 < P.n; i0 += gridDim.x * 256) {
     const int i = i0 + (int)threadIdx.x;
     const int nb = min(256, P.n - i0);
-    double dp[3] = {0, 0, 0}, dr = 0, dop = 0;
+    double dp[3] = {0, 0, 0}, dr = 0, dop = 0, nrm = 1.0;
     if (i < P.n) {
       for (int v = vbeg; v < vend; v++) {
         const ViewDev &c = vt.v[v];
@@ -792,13 +817,25 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
         dop += A[4];
         if (v == cam_view) {
           const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
+          const double cw = cam_weight(c, P, (size_t)v * P.n + i);
 #pragma unroll
           for (int a = 0; a < 3; a++) {
+            const double dw = dq[a] * cw;
 #pragma unroll
-            for (int b = 0; b < 3; b++) cam[3 * a + b] = __builtin_fma(dq[a], pp[b], cam[3 * a + b]);
-            cam[9 + a] += dq[a];
+            for (int b = 0; b < 3; b++) cam[3 * a + b] = __builtin_fma(dw, pp[b], cam[3 * a + b]);
+            cam[9 + a] += dw;
           }
         }
+      }
+      if (P.cnt) {
+        // averaged over the pixels that recorded the sphere (all views of the call)
+        uint32_t ct = 0;
+        for (int v = vbeg; v < vend; v++) ct += P.cnt[(size_t)v * P.n + i];
+        nrm = ct ? 1.0 / (double)ct : 0.0;
+#pragma unroll
+        for (int a = 0; a < 3; a++) dp[a] *= nrm;
+        dr *= nrm;
+        dop *= nrm;
       }
       if (P.gscale) put(P.gscale, i, dr, P.accumulate);
       if (P.gop) put(P.gop, i, dop, P.accumulate);
@@ -817,7 +854,7 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
           for (int ch = 0; ch < P.C; ch++) {
             double f = 0;
             for (int v = vbeg; v < vend; v++) f += P.accg[((size_t)v * P.n + i) * S + 5 + ch];
-            s_feat[P.C * threadIdx.x + ch] = (float)f;
+            s_feat[P.C * threadIdx.x + ch] = (float)(f * nrm);
           }
         __syncthreads();
         float *out = P.gfeat + (size_t)P.C * i0;
@@ -826,7 +863,7 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
         for (int ch = 0; ch < P.C; ch++) {
           double f = 0;
           for (int v = vbeg; v < vend; v++) f += P.accg[((size_t)v * P.n + i) * S + 5 + ch];
-          put(P.gfeat, (size_t)i * P.C + ch, f, P.accumulate);
+          put(P.gfeat, (size_t)i * P.C + ch, f * nrm, P.accumulate);
         }
       }
     }
@@ -873,16 +910,18 @@ __global__ __launch_bounds__(256) void k_cam_final(ProjBwdArgs P, int nparts, in
 
 // Camera gradient of view vbeg + blockIdx.y when one call covers several views
 // (same sums as above, one view per grid row).
-__global__ __launch_bounds__(256) void k_cam_grad_sphere(ProjBwdArgs P, int vbeg) {
+__global__ __launch_bounds__(256) void k_cam_grad_sphere(ViewTable vt, ProjBwdArgs P, int vbeg) {
   __shared__ double s_red[12][4];
   const int v = vbeg + blockIdx.y;
   const int S = 5 + P.C;
   double cam[12];
 #pragma unroll
   for (int q = 0; q < 12; q++) cam[q] = 0.0;
+  const ViewDev &c = vt.v[v];
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < P.n; i += gridDim.x * blockDim.x) {
     const double *A = P.accg + ((size_t)v * P.n + i) * S;
-    const double dq[3] = {A[0], A[1], A[2]};
+    const double cw = cam_weight(c, P, (size_t)v * P.n + i);
+    const double dq[3] = {A[0] * cw, A[1] * cw, A[2] * cw};
     const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
 #pragma unroll
     for (int a = 0; a < 3; a++) {
@@ -1147,6 +1186,10 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
       z.d1 = A.kslot + (size_t)vbeg * SPLAT_K_SLOTS * 4;
       z.nd1 = (long long)(vend - vbeg) * SPLAT_K_SLOTS * 4;
     }
+    if (A.cnt) {
+      z.u0 = A.cnt + r0;
+      z.nu0 = r1 - r0;
+    }
   } else {
     z.d0 = A.accg + r0 * ACC_G;
     z.nd0 = (r1 - r0) * ACC_G;
@@ -1160,7 +1203,7 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
     z.nf1 = gr->cam_t ? 3ll * vt.n : 0;
   }
 
-  const long long nz = z.nd0 + z.nd1 + z.nf0 + z.nf1;
+  const long long nz = z.nd0 + z.nd1 + z.nf0 + z.nf1 + z.nu0;
   if (nz > 0) hipLaunchKernelGGL(k_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, z);
   SPLAT_LAUNCH_CHECK();
   const int tile_begin = vt.v[vbeg].tile_off;
@@ -1188,6 +1231,7 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   P.kind = pr->kind; P.n = pr->n; P.C = A.C;
   P.pos = pr->pos; P.scale = pr->scale; P.rot = pr->rot;
   P.bin = bin; P.accg = A.accg; P.accf = A.accf; P.cam_part = A.cam_part;
+  P.aux = A.aux; P.cnt = sph ? A.cnt : nullptr;
   P.gpos = gr->pos; P.gscale = gr->scale; P.grot = gr->rot; P.gop = gr->opacity; P.gfeat = gr->feat;
   P.gR = gr->cam_R; P.gt = gr->cam_t;
   P.accumulate = gr->accumulate;
@@ -1210,7 +1254,7 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
       }
       if (cam_view >= 0) hipLaunchKernelGGL(k_cam_final, dim3(1), dim3(256), 0, stream, P, (int)nb, cam_view);
       if (cam && vend - vbeg > 1)
-        hipLaunchKernelGGL(k_cam_grad_sphere, dim3(min(nb, 512u), vend - vbeg), dim3(256), 0, stream, P, vbeg);
+        hipLaunchKernelGGL(k_cam_grad_sphere, dim3(min(nb, 512u), vend - vbeg), dim3(256), 0, stream, vt, P, vbeg);
     }
     else hipLaunchKernelGGL(k_proj_bwd_gauss, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
     SPLAT_LAUNCH_CHECK();

@@ -42,6 +42,7 @@ struct BwdArgs {
   double *accf;           // Gaussians: [records][C]; unused for spheres
   double *cam_part;       // [SPLAT_CAM_BLOCKS][12] per-block camera sums (spheres)
   double *kslot;          // [views][SPLAT_K_SLOTS][4] intrinsic-gradient sums, or NULL (not requested)
+  uint32_t *cnt;          // [records] pixels that recorded the sphere, or NULL (no normalisation)
 };
 
 struct TilePix {

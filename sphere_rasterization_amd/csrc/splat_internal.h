@@ -121,17 +121,21 @@ static inline size_t proj_bytes(long long nrec) {
 // into row b mod SPLAT_K_SLOTS, so that few blocks share an address.
 #define SPLAT_K_SLOTS 256
 
+// Last, per record, the number of pixels that recorded it (gradient
+// normalisation of spheres).
 struct AccLayout {
   double *g;
   double *f;
   double *cam;
   double *kslot;
+  uint32_t *cnt;
 };
 
 static inline size_t acc_bytes(long long nrec, int C) {
   return proj_align(sizeof(double) * ACC_G * (size_t)nrec) + proj_align(sizeof(double) * (size_t)nrec * C) +
          proj_align(sizeof(double) * 12 * SPLAT_CAM_BLOCKS) +
-         proj_align(sizeof(double) * 4 * SPLAT_K_SLOTS * SPLAT_MAX_VIEWS);
+         proj_align(sizeof(double) * 4 * SPLAT_K_SLOTS * SPLAT_MAX_VIEWS) +
+         proj_align(sizeof(uint32_t) * (size_t)nrec);
 }
 
 static inline AccLayout acc_layout(void *base, long long nrec, int C) {
@@ -140,7 +144,8 @@ static inline AccLayout acc_layout(void *base, long long nrec, int C) {
   a.g = (double *)p;    p += proj_align(sizeof(double) * ACC_G * (size_t)nrec);
   a.f = (double *)p;    p += proj_align(sizeof(double) * (size_t)nrec * C);
   a.cam = (double *)p;  p += proj_align(sizeof(double) * 12 * SPLAT_CAM_BLOCKS);
-  a.kslot = (double *)p;
+  a.kslot = (double *)p; p += proj_align(sizeof(double) * 4 * SPLAT_K_SLOTS * SPLAT_MAX_VIEWS);
+  a.cnt = (uint32_t *)p;
   return a;
 }
 

@@ -144,7 +144,8 @@ class Rasterizer:
         return self.img
 
     def backward(self, dimg: torch.Tensor, want=("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t", "cam_K"),
-                 view_begin: int = 0, view_count: Optional[int] = None, grads=None, accumulate=False):
+                 view_begin: int = 0, view_count: Optional[int] = None, grads=None, accumulate=False,
+                 normalize=False):
         if view_count is None:
             view_count = self.V - view_begin
         if self.bwd_ws is None:
@@ -156,6 +157,7 @@ class Rasterizer:
         for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t", "cam_K"):
             setattr(g, k, _ptr(grads.get(k)))
         g.accumulate = 1 if accumulate else 0
+        g.normalize = 1 if normalize else 0
         L.splat_render_bwd(self.c_cams, self.V, view_begin, view_count, self.c_prims, self.c_params,
                            _ptr(self.proj), _ptr(self.vals), _ptr(self.tile_ranges), _ptr(self.overflow),
                            _ptr(self.img), _ptr(self.T_final), _ptr(self.last), _ptr(self.norm), _ptr(self.topk),

@@ -154,7 +154,7 @@ def grad_check(name, got, ref, mag=None):
     return worst
 
 
-def compare_backward(rz, orc, ref, g_views, masked=None, names=None, view_groups=None):
+def compare_backward(rz, orc, ref, g_views, masked=None, names=None, view_groups=None, normalize=False):
     """Run both backward passes on the same (flag-masked) upstream gradient.
 
     view_groups: list of (view_begin, view_count) GPU calls accumulating into one
@@ -163,13 +163,14 @@ def compare_backward(rz, orc, ref, g_views, masked=None, names=None, view_groups
         masked, _ = masked_grads(orc, g_views)
     dimg = torch.from_numpy(np.concatenate([m.reshape(-1) for m in masked])).to(rz.device)
     if view_groups is None:
-        grads = rz.backward(dimg)
+        grads = rz.backward(dimg, normalize=normalize)
     else:
         grads = None
         for b, c in view_groups:
-            grads = rz.backward(dimg, view_begin=b, view_count=c, grads=grads, accumulate=grads is not None)
+            grads = rz.backward(dimg, view_begin=b, view_count=c, grads=grads, accumulate=grads is not None,
+                                normalize=normalize)
     torch.cuda.synchronize()
-    og = orc.backward(masked, with_mag=True)
+    og = orc.backward(masked, with_mag=True, normalize=normalize)
     names = names or [k for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t", "cam_K") if k in grads]
     worst = 0.0
     per = {}

@@ -20,7 +20,7 @@ def _rz(scene, **kw):
     return Rasterizer(scene, device="cuda", **kw)
 
 
-def _run(scene, grad_seed, name, check_grads=True, view_groups=None):
+def _run(scene, grad_seed, name, check_grads=True, view_groups=None, normalize=False):
     _log(f"[case] {name}: n={scene.n} views={len(scene.cams)} kind={scene.kind}")
     rz = _rz(scene)
     rz.forward()
@@ -29,7 +29,7 @@ def _run(scene, grad_seed, name, check_grads=True, view_groups=None):
     _log(f"  fwd ok pairs={st.get('pairs')} img_err={st['img_err']:.2e} flagged={st['flag_frac']:.2e}")
     if check_grads:
         g = S.upstream_grads(scene, grad_seed)
-        bw = compare_backward(rz, orc, None, g, view_groups=view_groups)
+        bw = compare_backward(rz, orc, None, g, view_groups=view_groups, normalize=normalize)
         _log(f"  bwd ok worst={bw['worst']:.3f} " + " ".join(f"{k}={v:.2f}" for k, v in bw["per"].items()))
     return rz, orc
 
@@ -56,6 +56,14 @@ def test_ragged_spheres():
 def test_orthographic_spheres():
     # parallel projection: 300k spheres on 600x450 (ragged tiles), intrinsics gradients included
     _run(S.ortho_spheres(), 9, "spheres 300k @600x450 orthographic")
+
+
+def test_normalised_sphere_gradients():
+    # Pulsar's gradient normalisation (per-sphere averaging, camera over area and 1e-3)
+    _run(S.pulsar_spheres(seed=23, n=200_000, width=640, height=480), 10, "spheres 200k @640x480 normalised",
+         normalize=True)
+    _run(S.ortho_spheres(seed=24, n=150_000), 11, "spheres 150k @600x450 orthographic normalised",
+         normalize=True)
 
 
 def test_ragged_gauss3d():

@@ -100,3 +100,18 @@ def test_orthographic_views_and_intrinsic_gradients_are_sphere_only():
     rc = lib.splat_render_bwd(pin, 1, 0, 1, C.byref(pr), C.byref(prm), 8, 8, 8, 8, 8, 8, 8, None, None, 8,
                               C.byref(g), 8, 1 << 40, None)
     assert rc == L.SPLAT_ERR_UNSUPPORTED
+
+
+def test_gradient_normalisation_is_sphere_only():
+    from sphere_rasterization_amd.raster import make_cams, make_params
+    sc = S.pulsar_spheres(n=10)
+    prm, _ = make_params(sc.params, 3)
+    lib = L.lib()
+    pr = L.splat_prims()
+    pr.kind, pr.n, pr.channels = 1, 10, 3
+    pr.pos = pr.scale = pr.rot = pr.opacity = pr.feat = 8
+    g = L.splat_grads()
+    g.normalize = 1
+    rc = lib.splat_render_bwd(make_cams(sc.cams), 1, 0, 1, C.byref(pr), C.byref(prm), 8, 8, 8, 8, 8, 8, 8, None,
+                              None, 8, C.byref(g), 8, 1 << 40, None)
+    assert rc == L.SPLAT_ERR_UNSUPPORTED
