@@ -90,7 +90,7 @@ def pack_cams(cams) -> np.ndarray:
 def pack_params(params, channels) -> np.ndarray:
     bg = np.zeros(channels) if params.background is None else np.asarray(params.background, np.float64)
     head = [params.alpha_min, params.alpha_max, params.T_min, params.gamma, params.bg_weight,
-            params.tau, params.top_k]
+            params.tau, params.top_k, params.top_by_depth]
     return np.ascontiguousarray(np.concatenate([np.asarray(head, np.float64), bg]))
 
 
@@ -205,6 +205,8 @@ class Oracle:
         return out
 
     def render_bruteforce(self, view=0) -> dict:
+        if self.params.top_by_depth:
+            raise ValueError("the brute-force renderer records the first top_k contributions only")
         c = self.cams[view]
         hw = c.width * c.height
         Cm = max(self.C, 2)

@@ -39,7 +39,8 @@ enum {
   FLAG_T_STOP = 2,      /* transmittance within 2e-4 (relative) of the stop threshold */
   FLAG_CLAMP = 4,       /* opacity*G within 1e-5 (relative) of the 0.99 clamp */
   FLAG_SPH_EDGE = 8,    /* a sphere's distance factor within 1e-8 of 0 (top-K may flip) */
-  FLAG_SPH_STOP = 16    /* a stop bound within 2e-5 (relative) of tau*N */
+  FLAG_SPH_STOP = 16,   /* a stop bound within 2e-5 (relative) of tau*N */
+  FLAG_SPH_ZTIE = 32    /* closest-K by depth: K-th and next intersection depth within 1e-5 (relative) */
 };
 
 #define CAM_STRIDE 24
@@ -72,6 +73,7 @@ typedef struct {
 
 typedef struct {
   int kind, n, C, V, K;
+  int top_by_depth;             /* spheres: record the K closest intersections, not the first K */
   double *pos, *scale, *rot, *opac, *depth, *feat;   /* inputs, promoted to double */
   double alpha_min, alpha_max, T_min, gamma, bg_weight, tau;
   double *bg;
@@ -330,8 +332,9 @@ octx *or_create(int kind, int n, int C, const double *pos, const double *scale, 
   X->feat = feat ? dup_d(feat, (long long)n * C) : NULL;
   X->alpha_min = params[0]; X->alpha_max = params[1]; X->T_min = params[2];
   X->gamma = params[3]; X->bg_weight = params[4]; X->tau = params[5]; X->K = (int)params[6];
+  X->top_by_depth = (int)params[7];
   X->bg = (double *)calloc((size_t)(C > 0 ? C : 1), sizeof(double));
-  for (int c = 0; c < C; c++) X->bg[c] = params[7 + c];
+  for (int c = 0; c < C; c++) X->bg[c] = params[8 + c];
   X->cams = (ocam *)calloc((size_t)V, sizeof(ocam));
   long long toff = 0, poff = 0;
   for (int v = 0; v < V; v++) {
@@ -465,6 +468,16 @@ static void pixel_ray(const ocam *c, double px, double py, double o[3], double d
   }
 }
 
+/* Depth (sensor z) of the point where the ray o + s d enters the sphere of
+ * centre q and radius r: the smaller root s of |o + s d - q|^2 = r^2. */
+static double ray_entry_depth(const double q[3], const double o[3], const double d[3], double dd, double r) {
+  double e[3] = {q[0] - o[0], q[1] - o[1], q[2] - o[2]};
+  double ed = e[0] * d[0] + e[1] * d[1] + e[2] * d[2];
+  double disc = ed * ed - dd * (e[0] * e[0] + e[1] * e[1] + e[2] * e[2] - r * r);
+  double sroot = (ed - sqrt(disc > 0.0 ? disc : 0.0)) / dd;
+  return o[2] + sroot * d[2];
+}
+
 /* Squared orthogonal distance of point q from the ray o + s d (Pulsar A). */
 static double ray_dist2(const double q[3], const double o[3], const double d[3], double dd) {
   double e[3] = {q[0] - o[0], q[1] - o[1], q[2] - o[2]};
@@ -522,6 +535,12 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
     double N = X->bg_weight;
     double S[64];
     for (int ch = 0; ch < C; ch++) S[ch] = X->bg_weight * X->bg[ch];
+    /* closest-K mode (Pulsar B.1.3 and B.1.4 keep each pixel's closest five
+       intersections): the K + 1 contributing spheres of smallest entry depth so
+       far, ordered by (depth, list position) */
+    int topd = X->top_by_depth, nc = 0;
+    double cz[17];
+    otrace ctr[17];
     for (long long p = s; p < e; p++) {
       const orec *o = &X->rec[X->pair_id[p]];
       P->processed++;
@@ -531,7 +550,7 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       double dist2 = ray_dist2(o->m, ro, d, dd);               /* orthogonal ray distance^2 */
       double r2 = o->r_eff * o->r_eff;
       double D = 1.0 - dist2 / r2;
-      if (fabs(D) < 1e-8 && P->ntop < X->K) P->flags |= FLAG_SPH_EDGE;
+      if (fabs(D) < 1e-8 && (topd || P->ntop < X->K)) P->flags |= FLAG_SPH_EDGE;
       if (!(dist2 < r2)) continue;
       double w = o->opac * D * o->e;
       N += w;
@@ -539,6 +558,22 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       for (int ch = 0; ch < C; ch++) S[ch] += w * X->feat[(size_t)id * C + ch];
       P->ncontrib++;
       P->last = p - s + 1;
+      if (topd) {
+        double z = ray_entry_depth(o->m, ro, d, dd, o->r_eff);
+        int at = nc;                                   /* insertion point: later positions lose ties */
+        while (at > 0 && z < cz[at - 1]) at--;
+        if (at <= X->K) {
+          int last = nc < X->K + 1 ? nc : X->K;
+          for (int k = last; k > at; k--) { cz[k] = cz[k - 1]; ctr[k] = ctr[k - 1]; }
+          cz[at] = z;
+          otrace *r = &ctr[at];
+          r->idx = (int)(p - s); r->rec = X->pair_id[p]; r->w = w; r->D = D; r->dist2 = dist2;
+          for (int a = 0; a < 3; a++) { r->o[a] = ro[a]; r->d[a] = d[a]; }
+          r->dd = dd;
+          if (nc < X->K + 1) nc++;
+        }
+        continue;
+      }
       if (P->ntop < X->K) {
         P->top[P->ntop++] = (int32_t)id;
         if (tr && ntr < tr_cap) {
@@ -548,6 +583,20 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
           r->dd = dd;
         }
       }
+    }
+    if (topd) {
+      int k = nc < X->K ? nc : X->K;
+      if (nc > X->K && fabs(cz[X->K] - cz[X->K - 1]) <= 1e-5 * fabs(cz[X->K - 1])) P->flags |= FLAG_SPH_ZTIE;
+      /* the selected ones in list order (the order the reverse pass walks) */
+      for (int a = 1; a < k; a++)
+        for (int b = a; b > 0 && ctr[b].idx < ctr[b - 1].idx; b--) {
+          otrace tmp = ctr[b]; ctr[b] = ctr[b - 1]; ctr[b - 1] = tmp;
+        }
+      for (int a = 0; a < k; a++) {
+        P->top[a] = (int32_t)(ctr[a].rec % (uint32_t)X->n);
+        if (tr && ntr < tr_cap) tr[ntr++] = ctr[a];
+      }
+      P->ntop = k;
     }
     P->N = N;
     for (int ch = 0; ch < C; ch++) P->col[ch] = S[ch] / N;

@@ -444,3 +444,71 @@ def test_tile_lists_equal_bruteforce(which):
         np.testing.assert_array_equal(a["top"], b["top"])
     else:
         np.testing.assert_array_equal(a["T"], b["T"])
+
+
+# ------------------------------------- closest-K recording (Pulsar B.1.3, B.1.4)
+
+def _entry_depths(pr, cam, W, H, ortho):
+    """Per pixel and sphere: sensor depth where the pixel's ray enters the sphere
+    (inf if it misses), from the closest-approach point minus the half chord."""
+    ys, xs = np.mgrid[0:H, 0:W] + 0.5
+    x = ((xs - cam.cx) / cam.fx).reshape(-1, 1)
+    y = ((ys - cam.cy) / cam.fy).reshape(-1, 1)
+    q = np.stack([pr["m0"], pr["m1"], pr["m2"]], 1)[None]           # [1, n, 3]
+    r = pr["r_eff"][None]
+    if ortho:
+        dist2 = (q[..., 0] - x) ** 2 + (q[..., 1] - y) ** 2
+        z = q[..., 2] - np.sqrt(np.maximum(r ** 2 - dist2, 0.0))
+    else:
+        d = np.stack([x, y, np.ones_like(x)], -1)                    # [pix, 1, 3]
+        dn = np.linalg.norm(d, axis=-1)
+        cross = np.cross(q, d)
+        dist2 = (cross ** 2).sum(-1) / dn ** 2
+        s_c = (q * d).sum(-1) / dn ** 2                               # closest approach
+        z = s_c - np.sqrt(np.maximum(r ** 2 - dist2, 0.0)) / dn      # d_z = 1: s is the depth
+    return np.where((dist2 < r ** 2) & pr["valid"].astype(bool)[None], z, np.inf)
+
+
+@pytest.mark.parametrize("ortho", [False, True])
+def test_closest_k_by_entry_depth_bruteforce(ortho):
+    """With no early stop every hit contributes, so the recorded spheres are the K
+    hits of smallest entry depth (list order breaks ties), reported in list order."""
+    rng = np.random.default_rng(31 + ortho)
+    W, H, K = 40, 32, 5
+    if ortho:
+        sc = _ortho_spheres(rng, 400, W, H, rmin=0.3, rmax=2.0)
+    else:
+        sc = TS.random_spheres(rng, 400, W, H, 40.0, rmin=0.1, rmax=0.8)
+    sc.params = S.Params(tau=0.0, top_k=K, top_by_depth=1)
+    orc = O.Oracle(sc)
+    r = orc.render_views()[0]
+    assert (r["flags"] == 0).mean() > 0.99
+    pr = orc.proj()
+    z = _entry_depths(pr, sc.cams[0], W, H, ortho)
+    order = np.lexsort((np.arange(sc.n), pr["key_bits"]))              # list order of the spheres
+    rank = np.empty(sc.n, np.int64)
+    rank[order] = np.arange(sc.n)
+    top = r["top"].reshape(-1, K)
+    ok = (r["flags"].reshape(-1) == 0)
+    nhit_many = 0
+    for p in np.nonzero(ok)[0]:
+        hits = np.nonzero(np.isfinite(z[p]))[0]
+        sel = hits[np.lexsort((rank[hits], z[p, hits]))][:K]
+        want = sel[np.argsort(rank[sel])]
+        got = top[p][top[p] >= 0]
+        np.testing.assert_array_equal(got, want, err_msg=f"pixel {p}")
+        nhit_many += len(hits) > K
+    assert nhit_many > 200                                              # selection actually matters
+
+
+def test_closest_k_equals_first_k_when_all_fit():
+    """When no pixel has more than K hits both recording rules keep every hit."""
+    rng = np.random.default_rng(35)
+    sc = TS.random_spheres(rng, 60, 40, 32, 40.0, rmin=0.05, rmax=0.3)
+    sc.params = S.Params(tau=0.0, top_k=8)
+    a = O.Oracle(sc).render_views()[0]
+    assert a["ncontrib"].max() <= 8 and a["ncontrib"].max() >= 2
+    sc.params = S.Params(tau=0.0, top_k=8, top_by_depth=1)
+    b = O.Oracle(sc).render_views()[0]
+    np.testing.assert_array_equal(a["top"], b["top"])
+    np.testing.assert_array_equal(a["img"], b["img"])
