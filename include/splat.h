@@ -102,6 +102,13 @@ typedef struct {
   float gamma, bg_weight, tau;
   int32_t top_k;                 /* 1..8 */
   const float *background;       /* HOST [channels] or NULL (= 0) */
+  /* Spheres: 0 records each pixel's first top_k contributing spheres in list
+   * order; 1 records the top_k contributing spheres whose surface the pixel's ray
+   * enters first (smallest sensor depth of the entry point, list order breaking
+   * ties; Pulsar B.1.3 and B.1.4 keep the closest five intersections). Either way
+   * topk lists them in list order and only they receive gradients. Must be 0 for
+   * Gaussians. */
+  int32_t top_by_depth;
 } splat_params;
 
 /* Gradient outputs (DEVICE); NULL = not requested (skipped, nothing written).

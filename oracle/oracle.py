@@ -21,6 +21,7 @@ NPD, NPI = 17, 13
 G_OFF = 8
 
 FLAG_ALPHA_MIN, FLAG_T_STOP, FLAG_CLAMP, FLAG_SPH_EDGE, FLAG_SPH_STOP = 1, 2, 4, 8, 16
+FLAG_SPH_ZTIE = 32          # closest-K recording: K-th and next entry depth nearly equal
 IMAGE_FLAGS = FLAG_ALPHA_MIN | FLAG_T_STOP | FLAG_SPH_EDGE | FLAG_SPH_STOP
 
 

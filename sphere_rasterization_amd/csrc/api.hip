@@ -177,6 +177,9 @@ int check_params(const splat_params *m, int kind) {
     CHECK(isfinite(m->tau) && m->tau >= 0.0f, SPLAT_ERR_INVALID_ARG, "tau must be >= 0");
     CHECK(isfinite(m->bg_weight) && m->bg_weight > 0.0f, SPLAT_ERR_INVALID_ARG, "bg_weight must be > 0");
     CHECK(m->top_k >= 1 && m->top_k <= SPLAT_TOPK_MAX, SPLAT_ERR_INVALID_ARG, "top_k must be in 1..8");
+    CHECK(m->top_by_depth == 0 || m->top_by_depth == 1, SPLAT_ERR_INVALID_ARG, "top_by_depth must be 0 or 1");
+  } else {
+    CHECK(m->top_by_depth == 0, SPLAT_ERR_UNSUPPORTED, "top_by_depth is for spheres only");
   }
   return SPLAT_OK;
 }
@@ -250,7 +253,7 @@ int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *p
   CHECK(prims->n > 0, SPLAT_ERR_INVALID_ARG, "render needs at least one primitive");
   FwdArgs A;
   memset(&A, 0, sizeof(A));
-  A.n = prims->n; A.C = prims->channels; A.top_k = prm->top_k;
+  A.n = prims->n; A.C = prims->channels; A.top_k = prm->top_k; A.top_by_depth = prm->top_by_depth;
   A.alpha_min = prm->alpha_min; A.alpha_max = prm->alpha_max; A.T_min = prm->T_min;
   A.tau = prm->tau; A.bg_weight = prm->bg_weight;
   for (int c = 0; c < A.C; c++) A.bg[c] = prm->background ? prm->background[c] : 0.0f;

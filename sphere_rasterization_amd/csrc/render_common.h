@@ -8,6 +8,7 @@
 
 struct FwdArgs {
   int n, C, top_k;
+  int top_by_depth;       // spheres: record the top_k closest entry points, not the first top_k
   float alpha_min, alpha_max, T_min, tau, bg_weight;
   const DrawRec *draw;
   const AuxRec *aux;

@@ -23,14 +23,18 @@ namespace {
 // ---------------------------------------------------------------------------
 // Spheres
 // ---------------------------------------------------------------------------
-template <int CM>
+// TOPD: record each pixel's top_k contributing spheres of smallest entry depth
+// (sensor z where the ray enters the sphere) instead of the first top_k.
+template <int CM, bool TOPD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   // One staged entry = NE 16-byte slots at a common stride, so every read of an
   // entry uses one LDS address with constant offsets: three slots of D / g
   // coefficients (fp64 pairs), then (o exp(o zhat / gamma), stop limit bound /
   // tau, features...) in fp32.
   constexpr int NF4 = (CM + 2 + 3) / 4;
-  constexpr int NE = 3 + NF4;
+  // closest-K recording adds one slot: (qz, ax, ay, r_eff), with a = 0 for
+  // orthographic views, so that the entry depth is g (qz (a.d) - r_eff sqrt(D / g))
+  constexpr int NE = 3 + NF4 + (TOPD ? 1 : 0);
   __shared__ float4 s_e[NE][256];
   __shared__ BlockLists<256> s_l;
   if (*A.overflow) return;
@@ -52,6 +56,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   // still recording contributing spheres (straight into the top-K buffer)
   bool need = K > 0 && A.topk != nullptr && tp.inside;
   int *my_top = need ? A.topk + (c.pix_off + (long long)tp.j * c.W + tp.i) * K : nullptr;
+  // closest-K: the best top_k (entry depth, list position) so far, ascending;
+  // slots from K on hold -inf and never change
+  float bz[TOPD ? SPLAT_TOPK_MAX : 1];
+  uint32_t bp[TOPD ? SPLAT_TOPK_MAX : 1];
+  if constexpr (TOPD) {
+#pragma unroll
+    for (int j = 0; j < SPLAT_TOPK_MAX; j++) {
+      bz[j] = j < K ? __builtin_huge_valf() : -__builtin_huge_valf();
+      bp[j] = 0xffffffffu;
+    }
+  }
+  const bool orth = c.kind == SPLAT_CAM_ORTHOGRAPHIC;
   bool active = tp.inside;
   const long long vbase = (long long)view * A.n;
 
@@ -74,6 +90,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       for (int ch = 0; ch < 4 * NF4 - 2; ch++) t[2 + ch] = ch < CM && ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
 #pragma unroll
       for (int f = 0; f < NF4; f++) s_e[3 + f][threadIdx.x] = make_float4(t[4 * f], t[4 * f + 1], t[4 * f + 2], t[4 * f + 3]);
+      if constexpr (TOPD) {
+        const AuxRec ax = A.aux[rid];
+        s_e[3 + NF4][threadIdx.x] = make_float4(ax.z, orth ? 0.0f : (float)d.u, orth ? 0.0f : (float)d.v, ax.w);
+      }
       mask = block_mask(tp, d);
     }
     build_block_lists(s_l, mask);
@@ -117,11 +137,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
         for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch]);
         if constexpr (decltype(REC)::value) {
           const bool rec = hit & need;
-          if (ballot64(rec)) {                   // most entries record nothing
-            if (rec) {
-              my_top[ntop] = (int)(b + (uint32_t)idx);
-              ntop++;
-              need = ntop < K;
+          if constexpr (TOPD) {
+            const float4 g4 = s_e[3 + NF4][idx];            // qz, ax, ay, r_eff
+            if (ballot64(rec)) {
+              if (rec) {
+                const float ad = __builtin_fmaf(g4.y, (float)ray.x, __builtin_fmaf(g4.z, (float)ray.y, 1.0f));
+                float z = (float)ray.g * (g4.x * ad - g4.w * sqrtf((float)num));
+                uint32_t pz = b + (uint32_t)idx;
+                // insertion: a strictly closer entry displaces (earlier positions win ties)
+#pragma unroll
+                for (int j = 0; j < SPLAT_TOPK_MAX; j++) {
+                  const bool sw = z < bz[j];
+                  const float tz = bz[j];
+                  const uint32_t tq = bp[j];
+                  bz[j] = sw ? z : tz;
+                  bp[j] = sw ? pz : tq;
+                  z = sw ? tz : z;
+                  pz = sw ? tq : pz;
+                }
+              }
+            }
+            // no later entry can come closer once the K-th best lies in front of
+            // this entry's front depth (later fronts are not nearer; margin for
+            // the rounding of the key and of the entry depths)
+            float kth = bz[0];
+#pragma unroll
+            for (int j = 1; j < SPLAT_TOPK_MAX; j++) kth = fmaxf(kth, bz[j]);
+            need = need & !(valid & active & (kth < (g4.x - g4.w) * (1.0f - 1e-5f)));
+          } else {
+            if (ballot64(rec)) {                   // most entries record nothing
+              if (rec) {
+                my_top[ntop] = (int)(b + (uint32_t)idx);
+                ntop++;
+                need = ntop < K;
+              }
             }
           }
         }
@@ -159,8 +208,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   for (int ch = 0; ch < CM; ch++)
     if (ch < A.C) img[ch * plane] = S[ch] * inv;
   if (A.norm) A.norm[p] = N;
-  if (A.topk)
+  if constexpr (TOPD) {
+    if (A.topk) {
+      // list order: sort the positions (empty slots, 0xffffffff, go last)
+#pragma unroll
+      for (int a = 0; a < SPLAT_TOPK_MAX; a++)
+#pragma unroll
+        for (int j = 0; j + 1 < SPLAT_TOPK_MAX - a; j++) {
+          const uint32_t lo = min(bp[j], bp[j + 1]), hi = max(bp[j], bp[j + 1]);
+          bp[j] = lo;
+          bp[j + 1] = hi;
+        }
+#pragma unroll
+      for (int q = 0; q < SPLAT_TOPK_MAX; q++)
+        if (q < K) A.topk[p * K + q] = bp[q] == 0xffffffffu ? -1 : (int)bp[q];
+    }
+  } else if (A.topk) {
     for (int q = ntop; q < K; q++) A.topk[p * K + q] = -1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -448,7 +513,10 @@ template <int CM>
 int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t stream) {
   dim3 grid(vt.total_tiles), block(256);
   if (kind == SPLAT_PRIM_SPHERE) {
-    hipLaunchKernelGGL(k_fwd_sphere<CM>, grid, block, 0, stream, vt, A);
+    if (A.top_by_depth)
+      hipLaunchKernelGGL((k_fwd_sphere<CM, true>), grid, block, 0, stream, vt, A);
+    else
+      hipLaunchKernelGGL((k_fwd_sphere<CM, false>), grid, block, 0, stream, vt, A);
   } else {
     // one launch per run of consecutive views of one kind, over that run's
     // tiles only. With both kinds present the camera views run on the side

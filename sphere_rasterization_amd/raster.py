@@ -35,6 +35,7 @@ def make_params(p: Params, channels: int):
     s = L.splat_params()
     s.alpha_min, s.alpha_max, s.T_min = p.alpha_min, p.alpha_max, p.T_min
     s.gamma, s.bg_weight, s.tau, s.top_k = p.gamma, p.bg_weight, p.tau, int(p.top_k)
+    s.top_by_depth = int(getattr(p, "top_by_depth", 0))
     keep = None
     if p.background is not None:
         keep = (C.c_float * channels)(*[float(x) for x in np.asarray(p.background, np.float32)[:channels]])

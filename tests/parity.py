@@ -118,7 +118,9 @@ def compare_forward(rz, orc, ref=None, pix=None, check_bins=True):
         rel = np.abs(g["N"][ok] - r["N"][ok]) / np.abs(r["N"][ok])
         stats["N_rel"] = float(rel.max()) if len(rel) else 0.0
         assert stats["N_rel"] <= 1e-4, f"norm rel error {stats['N_rel']:.3e}"
-        bad = (g["top"][ok] != r["top"][ok]).any(axis=1)
+        # a near tie of entry depths (closest-K recording) leaves the recorded set open
+        tok = ok & ((flags & O.FLAG_SPH_ZTIE) == 0)
+        bad = (g["top"][tok] != r["top"][tok]).any(axis=1)
         assert not bad.any(), f"top-K ids differ at {bad.sum()} pixels"
     return stats
 

@@ -66,6 +66,16 @@ def test_normalised_sphere_gradients():
          normalize=True)
 
 
+def test_closest_five_spheres():
+    # each pixel records the five contributing spheres its ray enters first
+    sc = S.pulsar_spheres(seed=25, n=300_000, width=640, height=480)
+    sc.params = S.Params(top_by_depth=1)
+    _run(sc, 12, "spheres 300k @640x480 closest five")
+    so = S.ortho_spheres(seed=26, n=150_000)
+    so.params = S.Params(top_by_depth=1)
+    _run(so, 13, "spheres 150k @600x450 orthographic closest five")
+
+
 def test_ragged_gauss3d():
     sc = S.gauss3d(seed=12, n=30_000, width=500, height=300)
     _run(sc, 8, "gauss3d 30k @500x300 ragged")
