@@ -535,7 +535,9 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
 // to the entry's LDS slot; each touched entry leaves the tile with one global
 // atomic per value.
 // ---------------------------------------------------------------------------
-template <int CM>
+// EXT: the call asks for intrinsic gradients or gradient normalisation (their
+// per-contribution work is compiled out of the plain reverse pass).
+template <int CM, bool EXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_bwd_sphere(ViewTable vt, BwdArgs A, int tile_begin) {
   constexpr int NV = 5 + CM;                  // dq0, dq1, dq2, d_reff, d_opac, d_feat...
   constexpr int NG = (NV + 7) / 8;            // groups of eight for the reduction
@@ -637,7 +639,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       const bool mine = tgt == b + (uint32_t)idx;
       const uint64_t bm = ballot64(mine);
       if (bm == 0) continue;
-      if (A.cnt && lane == 0u) atomicAdd(&s_cnt[idx], (uint32_t)__popcll(bm));
+      if constexpr (EXT)
+        if (A.cnt && lane == 0u) atomicAdd(&s_cnt[idx], (uint32_t)__popcll(bm));
       float v[NG * 8];
 #pragma unroll
       for (int q = 0; q < NG * 8; q++) v[q] = 0.0f;
@@ -675,8 +678,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
           // the ray: d dist^2 / d d = -((q.d) / |d|^2) d dist^2 / d q, with
           // (q.d) / |d|^2 = qz (1 - c1); orthographic: d dist^2 / d (x, y) = -d dist^2 / d (qx, qy)
           const double s = orth ? 1.0 : (double)x.x * (1.0 - c1);
-          kgx = kgx - s * gq0;
-          kgy = kgy - s * gq1;
+          if constexpr (EXT) {
+            kgx = kgx - s * gq0;
+            kgy = kgy - s * gq1;
+          }
         }
         nxt++;
         tgt = nxt < ntop ? my_top[nxt] : 0xffffffffu;
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
         const int e = e0 + sub;
         if (e < (int)cnt) {
           double *row = A.accg + (size_t)s_rid[e] * (5 + A.C);
-          if (A.cnt && ql == 0) {
+          if (EXT && A.cnt && ql == 0) {
             const uint32_t n = s_cnt[e];
             if (n) atomicAdd(A.cnt + s_rid[e], n);
           }
@@ -718,7 +723,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     }
     __syncthreads();
   }
-  if (A.kslot) {
+  if (EXT && A.kslot) {
     // intrinsics: the ray (x, y) = ((px - cx) / fx, (py - cy) / fy); per wave
     // the pixels' (d/dfx, d/dfy, d/dcx, d/dcy) are summed, lanes 0..3 add them
     const double ifx = 1.0 / (double)c.fx, ify = 1.0 / (double)c.fy;
@@ -1135,7 +1140,10 @@ template <int CM>
 int launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begin, int ntiles, int vbeg, int vend,
                    hipStream_t stream) {
   if (kind == SPLAT_PRIM_SPHERE) {
-    hipLaunchKernelGGL(k_bwd_sphere<CM>, dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
+    if (A.kslot || A.cnt)
+      hipLaunchKernelGGL((k_bwd_sphere<CM, true>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
+    else
+      hipLaunchKernelGGL((k_bwd_sphere<CM, false>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
   } else {
     // one launch per run of consecutive views of one kind, over that run's
     // tiles only; with both kinds present the camera views run on the side
