@@ -200,6 +200,34 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
                      const splat_grads *grads, void *workspace, size_t ws_bytes,
                      hipStream_t stream);
 
+/* ---- per-frame parameter assembly ---------------------------------------------
+ * NuRec's profiling page ("Fusing small kernels and removing synchronizations"):
+ * the per-frame interpolate step that assembles the primitives' parameters before
+ * rendering, fused into one kernel. The page does not say what is interpolated;
+ * here each primitive carries its centre and rotation quaternion at n_keys keyframe
+ * times. For time t the bracketing keyframes k, k1 (key_times[k] <= t <=
+ * key_times[k1]; t outside the range clamps to the end frame) and w = (t - t_k) /
+ * (t_k1 - t_k) give
+ *   pos = (1 - w) key_pos[k] + w key_pos[k1],
+ *   rot = (1 - w) key_rot[k] + w s key_rot[k1],  s = -1 if their dot product < 0
+ * (normalised linear interpolation on the shorter arc; splat_project normalises).
+ * key_times: HOST [n_keys], finite, strictly increasing. key_pos [n_keys][n][3],
+ * key_rot [n_keys][n][4], pos [n][3], rot [n][4]: DEVICE, caller-owned; rotation
+ * buffers 16-byte aligned. A NULL key_pos/pos (or key_rot/rot) pair skips that
+ * output. Argument errors return SPLAT_ERR_INVALID_ARG before any launch. */
+int splat_interpolate(const float *key_times, int n_keys, float t, int n, const float *key_pos,
+                      const float *key_rot, float *pos, float *rot, hipStream_t stream);
+
+/* Reverse of splat_interpolate: ADDS the gradients w.r.t. the bracketing keyframes'
+ * centres and rotations (frames k and k1 of d_key_pos [n_keys][n][3], d_key_rot
+ * [n_keys][n][4]; the other frames are not touched, so the caller zeroes the buffers
+ * once and can sum several frames) given d_pos [n][3], d_rot [n][4]. The sign s is a
+ * discrete choice and carries no gradient. key_rot is needed for s when d_rot is
+ * given. NULL d_pos/d_key_pos (or d_rot/d_key_rot) skips that part. */
+int splat_interpolate_bwd(const float *key_times, int n_keys, float t, int n, const float *key_rot,
+                          const float *d_pos, const float *d_rot, float *d_key_pos, float *d_key_rot,
+                          hipStream_t stream);
+
 const char *splat_status_string(int status);
 
 #ifdef __cplusplus

@@ -20,7 +20,7 @@ SPLAT_MAX_VIEWS, SPLAT_MAX_CHANNELS = 16, 64
 
 EXPORTS = ["splat_projected_bytes", "splat_total_tiles", "splat_sort_workspace_bytes",
            "splat_bwd_workspace_bytes", "splat_project", "splat_bin_sort", "splat_render_fwd",
-           "splat_render_bwd", "splat_status_string"]
+           "splat_render_bwd", "splat_interpolate", "splat_interpolate_bwd", "splat_status_string"]
 
 
 class splat_camera(C.Structure):
@@ -86,6 +86,11 @@ def lib():
         L.splat_render_bwd.restype = i32
         L.splat_render_bwd.argtypes = [cam_p, i32, i32, i32, C.POINTER(splat_prims), C.POINTER(splat_params),
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, C.POINTER(splat_grads), vp, sz, vp]
+        fp = C.POINTER(C.c_float)
+        L.splat_interpolate.restype = i32
+        L.splat_interpolate.argtypes = [fp, i32, C.c_float, i32, vp, vp, vp, vp, vp]
+        L.splat_interpolate_bwd.restype = i32
+        L.splat_interpolate_bwd.argtypes = [fp, i32, C.c_float, i32, vp, vp, vp, vp, vp, vp]
         L.splat_status_string.restype = C.c_char_p
         L.splat_status_string.argtypes = [i32]
         _L = L
@@ -145,3 +150,20 @@ def splat_render_bwd(cams, n_views, view_begin, view_count, prims, params, proj,
                                                              C.byref(params), proj, vals, tile_ranges, overflow, img,
                                                              T_final, last, norm, topk, dL_dimg, C.byref(grads),
                                                              workspace, ws_bytes, stream))
+
+
+def _times(key_times):
+    kt = (C.c_float * len(key_times))(*[float(x) for x in key_times])
+    return kt, len(key_times)
+
+
+def splat_interpolate(key_times, t, n, key_pos, key_rot, pos, rot, stream):
+    kt, nk = _times(key_times)
+    return _check("splat_interpolate", lib().splat_interpolate(kt, nk, float(t), n, key_pos, key_rot, pos, rot,
+                                                               stream))
+
+
+def splat_interpolate_bwd(key_times, t, n, key_rot, d_pos, d_rot, d_key_pos, d_key_rot, stream):
+    kt, nk = _times(key_times)
+    return _check("splat_interpolate_bwd", lib().splat_interpolate_bwd(kt, nk, float(t), n, key_rot, d_pos, d_rot,
+                                                                       d_key_pos, d_key_rot, stream))

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsplat.so")
-SOURCES = ["api.hip", "project.hip", "binsort.hip", "render_fwd.hip", "render_bwd.hip"]
+SOURCES = ["api.hip", "project.hip", "binsort.hip", "render_fwd.hip", "render_bwd.hip", "assemble.hip"]
 ARCH = os.environ.get("SPLAT_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

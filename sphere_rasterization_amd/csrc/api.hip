@@ -22,6 +22,10 @@ int launch_render_fwd(const ViewTable &vt, const FwdArgs &A, int kind, hipStream
 size_t bwd_workspace_bytes(long long nrec, int C);
 int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, const BinRec *bin,
                       const splat_grads *gr, hipStream_t stream);
+int launch_assemble(const float *key_pos, const float *key_rot, int k, int k1, float w, long long n, float *pos,
+                    float *rot, hipStream_t stream);
+int launch_assemble_bwd(const float *key_rot, int k, int k1, float w, long long n, const float *d_pos,
+                        const float *d_rot, float *d_key_pos, float *d_key_rot, hipStream_t stream);
 
 namespace {
 
@@ -184,6 +188,32 @@ int check_params(const splat_params *m, int kind) {
   return SPLAT_OK;
 }
 
+// Keyframe bracket of time t: frames k, k1 and the weight of k1 (host, fp64).
+int key_bracket(const float *key_times, int n_keys, float t, int *k, int *k1, float *w) {
+  CHECK(key_times != nullptr && n_keys >= 1, SPLAT_ERR_INVALID_ARG, "key times");
+  CHECK(isfinite(t), SPLAT_ERR_INVALID_ARG, "time not finite");
+  for (int i = 0; i < n_keys; i++) {
+    CHECK(isfinite(key_times[i]), SPLAT_ERR_INVALID_ARG, "key time not finite");
+    CHECK(i == 0 || key_times[i] > key_times[i - 1], SPLAT_ERR_INVALID_ARG, "key times must increase");
+  }
+  if (n_keys == 1 || t <= key_times[0]) {
+    *k = *k1 = 0;
+    *w = 0.0f;
+  } else if (t >= key_times[n_keys - 1]) {
+    *k = *k1 = n_keys - 1;
+    *w = 0.0f;
+  } else {
+    int i = 0;
+    while (!(key_times[i] <= t && t < key_times[i + 1])) i++;
+    *k = i;
+    *k1 = i + 1;
+    *w = (float)(((double)t - (double)key_times[i]) / ((double)key_times[i + 1] - (double)key_times[i]));
+  }
+  return SPLAT_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -303,6 +333,37 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   A.kslot = grads->cam_K ? acc.kslot : nullptr;
   A.cnt = grads->normalize ? acc.cnt : nullptr;
   return launch_render_bwd(vt, view_begin, view_begin + view_count, A, prims, L.bin, grads, stream);
+}
+
+int splat_interpolate(const float *key_times, int n_keys, float t, int n, const float *key_pos,
+                      const float *key_rot, float *pos, float *rot, hipStream_t stream) {
+  int k = 0, k1 = 0;
+  float w = 0.0f;
+  int st = key_bracket(key_times, n_keys, t, &k, &k1, &w);
+  if (st) return st;
+  CHECK(n >= 0, SPLAT_ERR_INVALID_ARG, "negative n");
+  const bool do_pos = key_pos && pos, do_rot = key_rot && rot;
+  CHECK(do_pos || do_rot || n == 0, SPLAT_ERR_INVALID_ARG, "nothing to assemble");
+  CHECK(!do_rot || (aligned16(key_rot) && aligned16(rot)), SPLAT_ERR_INVALID_ARG, "rotation buffers not 16-byte aligned");
+  return launch_assemble(do_pos ? key_pos : nullptr, do_rot ? key_rot : nullptr, k, k1, w, n, pos, rot, stream);
+}
+
+int splat_interpolate_bwd(const float *key_times, int n_keys, float t, int n, const float *key_rot,
+                          const float *d_pos, const float *d_rot, float *d_key_pos, float *d_key_rot,
+                          hipStream_t stream) {
+  int k = 0, k1 = 0;
+  float w = 0.0f;
+  int st = key_bracket(key_times, n_keys, t, &k, &k1, &w);
+  if (st) return st;
+  CHECK(n >= 0, SPLAT_ERR_INVALID_ARG, "negative n");
+  const bool do_pos = d_pos && d_key_pos, do_rot = d_rot && d_key_rot;
+  if (do_rot) {
+    CHECK(k == k1 || key_rot != nullptr, SPLAT_ERR_INVALID_ARG, "key_rot needed for the rotation gradient");
+    CHECK(aligned16(d_rot) && aligned16(d_key_rot) && (!key_rot || aligned16(key_rot)), SPLAT_ERR_INVALID_ARG,
+          "rotation buffers not 16-byte aligned");
+  }
+  return launch_assemble_bwd(key_rot, k, k1, w, n, do_pos ? d_pos : nullptr, do_rot ? d_rot : nullptr,
+                             do_pos ? d_key_pos : nullptr, do_rot ? d_key_rot : nullptr, stream);
 }
 
 const char *splat_status_string(int status) {

@@ -201,3 +201,25 @@ class Rasterizer:
     def pairs(self):
         n = int(self.num_pairs.item())
         return self.keys[:n], self.vals[:n]
+
+
+def interpolate(key_times, t: float, key_pos: torch.Tensor, key_rot: torch.Tensor):
+    """Assemble one frame's centres [n,3] and rotations [n,4] from keyframe tensors
+    key_pos [K,n,3] and key_rot [K,n,4] (device, float32) at time t."""
+    n = key_pos.shape[1]
+    pos = torch.empty((n, 3), dtype=torch.float32, device=key_pos.device)
+    rot = torch.empty((n, 4), dtype=torch.float32, device=key_pos.device)
+    L.splat_interpolate(list(key_times), t, n, _ptr(key_pos), _ptr(key_rot), _ptr(pos), _ptr(rot), _stream())
+    return pos, rot
+
+
+def interpolate_backward(key_times, t: float, key_rot: torch.Tensor, d_pos, d_rot, d_key_pos=None, d_key_rot=None):
+    """Add the keyframe gradients of one frame (d_key_* zero-initialised if not given)."""
+    K, n = key_rot.shape[0], key_rot.shape[1]
+    if d_key_pos is None:
+        d_key_pos = torch.zeros((K, n, 3), dtype=torch.float32, device=key_rot.device)
+    if d_key_rot is None:
+        d_key_rot = torch.zeros((K, n, 4), dtype=torch.float32, device=key_rot.device)
+    L.splat_interpolate_bwd(list(key_times), t, n, _ptr(key_rot), _ptr(d_pos), _ptr(d_rot), _ptr(d_key_pos),
+                            _ptr(d_key_rot), _stream())
+    return d_key_pos, d_key_rot

@@ -131,3 +131,16 @@ def test_top_by_depth_values():
     pr.rot = 8
     prm, _ = make_params(S.Params(top_by_depth=1), 3)
     assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_UNSUPPORTED
+
+
+def test_interpolate_argument_errors():
+    lib = L.lib()
+    good = (C.c_float * 3)(0.0, 1.0, 2.0)
+    bad = (C.c_float * 3)(0.0, 2.0, 1.0)
+    assert lib.splat_interpolate(bad, 3, 0.5, 10, 16, 16, 16, 16, None) == L.SPLAT_ERR_INVALID_ARG
+    assert lib.splat_interpolate(good, 0, 0.5, 10, 16, 16, 16, 16, None) == L.SPLAT_ERR_INVALID_ARG
+    assert lib.splat_interpolate(good, 3, float("nan"), 10, 16, 16, 16, 16, None) == L.SPLAT_ERR_INVALID_ARG
+    assert lib.splat_interpolate(good, 3, 0.5, -1, 16, 16, 16, 16, None) == L.SPLAT_ERR_INVALID_ARG
+    assert lib.splat_interpolate(good, 3, 0.5, 10, None, None, None, None, None) == L.SPLAT_ERR_INVALID_ARG
+    assert lib.splat_interpolate(good, 3, 0.5, 10, 16, 20, 16, 16, None) == L.SPLAT_ERR_INVALID_ARG   # misaligned
+    assert lib.splat_interpolate_bwd(good, 3, 0.5, 10, None, 16, 16, 16, 16, None) == L.SPLAT_ERR_INVALID_ARG
