@@ -71,6 +71,9 @@ def parse():
                          "5: the same scene from 6 cameras 1280x720 and a 2048x64 lidar view")
     ap.add_argument("--hbm-copy", action="store_true",
                     help="also time a plain 1 GiB device copy and report the measured HBM bandwidth")
+    ap.add_argument("--assemble", action="store_true",
+                    help="instead of the rendering step, time the per-frame parameter assembly (keyframe "
+                         "interpolation of 2M primitives, 4 keyframes) and its reverse pass against the HBM peak")
     return ap.parse_args()
 
 
@@ -92,6 +95,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.assemble:
+        print(json.dumps(assemble_bench(args, torch, dev)), flush=True)
+        return
     wl = args.workload
     scene = S.make_config(wl)
     pixels = sum(c.width * c.height for c in scene.cams)
@@ -169,6 +175,61 @@ def main():
     if args.hbm_copy:
         out["hbm_copy_GBps"] = hbm_copy(torch, dev)
     print(json.dumps(out), flush=True)
+
+
+# Per-frame assembly, algorithmic HBM bytes per primitive: forward reads the two
+# bracketing keyframes' centre and rotation (2 x 28 B) and writes 28 B; the
+# reverse pass reads the upstream gradients (28 B) and both rotations (32 B, for
+# the shorter-arc sign) and adds into both keyframes' gradient rows (2 x 28 B read
+# and written).
+ASM_FWD_BYTES = 84
+ASM_BWD_BYTES = 28 + 32 + 112
+
+
+def assemble_bench(args, torch, dev):
+    import numpy as np
+    from sphere_rasterization_amd import _lib as L
+    from sphere_rasterization_amd.raster import _ptr, _stream
+    K, n = 4, 2_000_000
+    rng = np.random.default_rng(7)
+    times = np.cumsum(rng.uniform(0.05, 0.2, K)).astype(np.float32)
+    t = float(np.float32(times[1] + 0.37 * (times[2] - times[1])))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    kp = torch.randn((K, n, 3), device=dev, generator=gen)
+    kr = torch.randn((K, n, 4), device=dev, generator=gen)
+    pos = torch.empty((n, 3), device=dev)
+    rot = torch.empty((n, 4), device=dev)
+    gp = torch.randn((n, 3), device=dev, generator=gen)
+    gq = torch.randn((n, 4), device=dev, generator=gen)
+    dkp = torch.zeros((K, n, 3), device=dev)
+    dkq = torch.zeros((K, n, 4), device=dev)
+    fwd = lambda: L.splat_interpolate(list(times), t, n, _ptr(kp), _ptr(kr), _ptr(pos), _ptr(rot), _stream())
+    bwd = lambda: L.splat_interpolate_bwd(list(times), t, n, _ptr(kr), _ptr(gp), _ptr(gq), _ptr(dkp), _ptr(dkq),
+                                          _stream())
+    res = {}
+    for name, fn, nbytes in (("forward", fwd, ASM_FWD_BYTES), ("reverse", bwd, ASM_BWD_BYTES)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        gbs = nbytes * n / (ms / 1e3) / 1e9
+        res[name] = {"ms": round(ms, 5), "bytes_per_launch": nbytes * n,
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+    f = res["forward"]
+    return {"metric": "Mprimitives/s assembled per frame (keyframe interpolation)",
+            "value": round(n / (f["ms"] / 1e3) / 1e6, 1), "unit": "Mprimitives/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": f["ms"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "assemble_2m_4keys", "primitives": n, "keyframes": K},
+            "roofline": f["roofline"], "reverse": res["reverse"]}
 
 
 def hbm_copy(torch, dev, mib=1024, reps=10):
