@@ -91,7 +91,7 @@ def pack_cams(cams) -> np.ndarray:
 def pack_params(params, channels) -> np.ndarray:
     bg = np.zeros(channels) if params.background is None else np.asarray(params.background, np.float64)
     head = [params.alpha_min, params.alpha_max, params.T_min, params.gamma, params.bg_weight,
-            params.tau, params.top_k, params.top_by_depth]
+            params.tau, params.top_k, params.top_by_depth, getattr(params, "max_shift", 0)]
     return np.ascontiguousarray(np.concatenate([np.asarray(head, np.float64), bg]))
 
 

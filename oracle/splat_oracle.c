@@ -74,6 +74,7 @@ typedef struct {
 typedef struct {
   int kind, n, C, V, K;
   int top_by_depth;             /* spheres: record the K closest intersections, not the first K */
+  int max_shift;                /* spheres: report the normalisation relative to a per-pixel shift */
   double *pos, *scale, *rot, *opac, *depth, *feat;   /* inputs, promoted to double */
   double alpha_min, alpha_max, T_min, gamma, bg_weight, tau;
   double *bg;
@@ -333,8 +334,9 @@ octx *or_create(int kind, int n, int C, const double *pos, const double *scale, 
   X->alpha_min = params[0]; X->alpha_max = params[1]; X->T_min = params[2];
   X->gamma = params[3]; X->bg_weight = params[4]; X->tau = params[5]; X->K = (int)params[6];
   X->top_by_depth = (int)params[7];
+  X->max_shift = (int)params[8];
   X->bg = (double *)calloc((size_t)(C > 0 ? C : 1), sizeof(double));
-  for (int c = 0; c < C; c++) X->bg[c] = params[8 + c];
+  for (int c = 0; c < C; c++) X->bg[c] = params[9 + c];
   X->cams = (ocam *)calloc((size_t)V, sizeof(ocam));
   long long toff = 0, poff = 0;
   for (int v = 0; v < V; v++) {
@@ -497,6 +499,7 @@ typedef struct {          /* per-entry trace kept for the backward pass */
 typedef struct {
   double col[64 + 2];
   double T, N, dep;
+  double shift;         /* spheres, max-shift: max(0, largest log-weight of a contributing sphere) */
   long long last, ncontrib, processed;
   int32_t top[16];
   int ntop, flags;
@@ -545,7 +548,8 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       const orec *o = &X->rec[X->pair_id[p]];
       P->processed++;
       double lim = X->tau * N;
-      if (fabs(o->b - lim) <= 2e-5 * lim) P->flags |= FLAG_SPH_STOP;
+      /* max-shift: the kernels compare the bound in the log domain in fp32 */
+      if (fabs(o->b - lim) <= (X->max_shift ? 1e-4 : 2e-5) * lim) P->flags |= FLAG_SPH_STOP;
       if (o->b < lim) break;                                   /* early stop (Pulsar 3.2, B.1.3) */
       double dist2 = ray_dist2(o->m, ro, d, dd);               /* orthogonal ray distance^2 */
       double r2 = o->r_eff * o->r_eff;
@@ -557,6 +561,10 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       uint32_t id = X->pair_id[p] % (uint32_t)X->n;
       for (int ch = 0; ch < C; ch++) S[ch] += w * X->feat[(size_t)id * C + ch];
       P->ncontrib++;
+      {
+        double lw = log(o->opac) + o->opac * o->zhat / X->gamma;   /* log of o exp(o zhat / gamma) */
+        if (lw > P->shift) P->shift = lw;
+      }
       P->last = p - s + 1;
       if (topd) {
         double z = ray_entry_depth(o->m, ro, d, dd, o->r_eff);
@@ -656,9 +664,10 @@ void or_render(const octx *X, long long npix, const long long *pix, double *img,
     opix P;
     composite(X, g, &P, NULL, 0);
     for (int ch = 0; ch < Cm; ch++) img[q * Cm + ch] = P.col[ch];
-    if (T) T[q] = P.T;
+    /* max-shift (spheres): T carries the shift m, N the normalisation times exp(-m) */
+    if (T) T[q] = X->max_shift && X->kind == PRIM_SPHERE ? P.shift : P.T;
     if (last) last[q] = P.last;
-    if (N) N[q] = P.N;
+    if (N) N[q] = X->max_shift && X->kind == PRIM_SPHERE ? P.N * exp(-P.shift) : P.N;
     if (top) for (int k = 0; k < X->K; k++) top[q * X->K + k] = P.top[k];
     if (flags) flags[q] = P.flags;
     if (processed) processed[q] = P.processed;

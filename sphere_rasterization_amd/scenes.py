@@ -79,6 +79,7 @@ class Params:
     top_k: int = 5
     background: Optional[np.ndarray] = None   # [channels] float32 or None (= 0)
     top_by_depth: int = 0      # spheres: 1 = record the top_k closest intersections, not the first top_k
+    max_shift: int = 0         # spheres: 1 = weights relative to a per-pixel shift (needed for gamma < 1/88)
 
     def __post_init__(self):
         for k in ("alpha_min", "alpha_max", "T_min", "gamma", "bg_weight", "tau"):

@@ -512,3 +512,61 @@ def test_closest_k_equals_first_k_when_all_fit():
     b = O.Oracle(sc).render_views()[0]
     np.testing.assert_array_equal(a["top"], b["top"])
     np.testing.assert_array_equal(a["img"], b["img"])
+
+
+# ---------------------------------------------- max-shifted sphere normalisation
+
+def test_max_shift_single_sphere_small_gamma():
+    """gamma = 1/200: the weight o D exp(o zhat / gamma) reaches e^100 and more. With
+    the shift m = ln o + o zhat / gamma the reported normalisation is D + exp(-m)
+    where the sphere is hit (w_bg = 1) and exp(0) = 1 elsewhere, T carries m (0 where
+    nothing contributes), and the colour is the plain w f / (w + 1)."""
+    W = H = 32
+    cam = TS.pinhole(W, H, 32.0, znear=1.0, zfar=21.0)
+    prm = S.Params(gamma=0.005, max_shift=1, tau=0.0)
+    q, r, o, f = f64([0.3, -0.2, 5.0]), f64(0.5), f64(0.6), f64([0.25, 0.75])
+    sc = TS.spheres([q], [r], [o], [f], [cam], params=prm)
+    res = O.Oracle(sc).render_views()[0]
+    gam = f64(float(np.float32(0.005)))
+    lam = math.log(o) + o * ((21.0 - q[2]) / 20.0) / gam
+    assert lam > 88.0
+    D = np.clip(1 - _ray_dist(q, cam, W, H) ** 2 / r ** 2, 0, None)
+    hit = D > 0
+    np.testing.assert_allclose(res["N"][hit], D[hit] + math.exp(-lam), rtol=1e-12)
+    np.testing.assert_allclose(res["N"][~hit], 1.0, rtol=0)
+    np.testing.assert_allclose(res["T"][hit], lam, rtol=1e-12)
+    assert (res["T"][~hit] == 0).all()
+    w_rel = D[hit]                                           # w exp(-lam)
+    np.testing.assert_allclose(res["img"][:, hit], f[:, None] * (w_rel / (w_rel + math.exp(-lam)))[None],
+                               rtol=1e-12)
+
+
+def test_max_shift_only_rescales_the_normalisation():
+    """At gamma = 0.02 (no overflow either way) the shifted run gives the same image,
+    top-K and gradients; its N times exp(T) is the unshifted N, and T is the largest
+    log-weight of the pixel's hits, or 0 (brute force over the spheres, tau = 0)."""
+    rng = np.random.default_rng(37)
+    W, H = 40, 32
+    sc = TS.random_spheres(rng, 300, W, H, 40.0, rmin=0.05, rmax=0.5)
+    sc.params = S.Params(tau=0.0)
+    a = O.Oracle(sc)
+    ra = a.render_views()[0]
+    sc.params = S.Params(tau=0.0, max_shift=1)
+    b = O.Oracle(sc)
+    rb = b.render_views()[0]
+    np.testing.assert_array_equal(ra["img"], rb["img"])
+    np.testing.assert_array_equal(ra["top"], rb["top"])
+    np.testing.assert_allclose(rb["N"] * np.exp(rb["T"]), ra["N"], rtol=1e-12)
+    pr = a.proj()
+    lam = np.log(pr["opac"]) + pr["opac"] * pr["zhat"] / float(np.float32(0.02))
+    cam = sc.cams[0]
+    want = np.zeros((H, W))
+    for i in np.nonzero(pr["valid"])[0]:
+        q = np.array([pr["m0"][i], pr["m1"][i], pr["m2"][i]])
+        d = _ray_dist(q, cam, W, H)
+        want = np.where(d < pr["r_eff"][i], np.maximum(want, lam[i]), want)
+    np.testing.assert_allclose(rb["T"], want, rtol=1e-12, atol=0)
+    g = [np.random.default_rng(3).standard_normal((3, H, W)).astype(np.float32)]
+    ga, gb = a.backward(g), b.backward(g)
+    for k in ("pos", "scale", "opacity", "feat", "cam_R", "cam_t"):
+        np.testing.assert_array_equal(ga[k], gb[k])
