@@ -109,6 +109,13 @@ typedef struct {
    * topk lists them in list order and only they receive gradients. Must be 0 for
    * Gaussians. */
   int32_t top_by_depth;
+  /* Spheres: 1 blends relative to a per-pixel shift m = max(0, largest ln(o) +
+   * o zhat / gamma of a contributing sphere), so that no weight overflows fp32
+   * (required for gamma < 1/88, where exp(o zhat / gamma) can exceed the fp32
+   * range). The image is unchanged; norm holds the normalisation times exp(-m),
+   * and T_final (spheres: otherwise unused) receives m, which splat_render_bwd
+   * then reads (T_final must be given to both calls). Must be 0 for Gaussians. */
+  int32_t max_shift;
 } splat_params;
 
 /* Gradient outputs (DEVICE); NULL = not requested (skipped, nothing written).

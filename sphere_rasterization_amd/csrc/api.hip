@@ -12,8 +12,8 @@
 #include "render_common.h"
 #include "splat_internal.h"
 
-int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, double alpha_min, void *proj,
-                   uint32_t *counts, hipStream_t stream);
+int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, double alpha_min, int max_shift,
+                   void *proj, uint32_t *counts, hipStream_t stream);
 size_t sort_workspace_bytes(const ViewTable &vt, int n, long long capacity);
 int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t *counts, long long capacity,
                     uint64_t *keys, uint32_t *vals, uint32_t *ranges, int64_t *num_pairs, int32_t *overflow,
@@ -182,8 +182,12 @@ int check_params(const splat_params *m, int kind) {
     CHECK(isfinite(m->bg_weight) && m->bg_weight > 0.0f, SPLAT_ERR_INVALID_ARG, "bg_weight must be > 0");
     CHECK(m->top_k >= 1 && m->top_k <= SPLAT_TOPK_MAX, SPLAT_ERR_INVALID_ARG, "top_k must be in 1..8");
     CHECK(m->top_by_depth == 0 || m->top_by_depth == 1, SPLAT_ERR_INVALID_ARG, "top_by_depth must be 0 or 1");
+    CHECK(m->max_shift == 0 || m->max_shift == 1, SPLAT_ERR_INVALID_ARG, "max_shift must be 0 or 1");
+    CHECK(m->max_shift || m->gamma >= 1.0f / 88.0f, SPLAT_ERR_INVALID_ARG,
+          "gamma below 1/88 overflows fp32 sphere weights: set max_shift");
   } else {
     CHECK(m->top_by_depth == 0, SPLAT_ERR_UNSUPPORTED, "top_by_depth is for spheres only");
+    CHECK(m->max_shift == 0, SPLAT_ERR_UNSUPPORTED, "max_shift is for spheres only");
   }
   return SPLAT_OK;
 }
@@ -249,7 +253,8 @@ int splat_project(const splat_camera *cams, int n_views, const splat_prims *prim
   if ((st = check_params(prm, prims->kind))) return st;
   if (prims->n == 0) return SPLAT_OK;
   CHECK(proj && pair_counts, SPLAT_ERR_INVALID_ARG, "proj / pair_counts NULL");
-  return launch_project(vt, prims, (double)prm->gamma, (double)prm->alpha_min, proj, pair_counts, stream);
+  return launch_project(vt, prims, (double)prm->gamma, (double)prm->alpha_min, prm->max_shift, proj, pair_counts,
+                        stream);
 }
 
 int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *proj, const uint32_t *pair_counts,
@@ -284,6 +289,7 @@ int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *p
   FwdArgs A;
   memset(&A, 0, sizeof(A));
   A.n = prims->n; A.C = prims->channels; A.top_k = prm->top_k; A.top_by_depth = prm->top_by_depth;
+  A.max_shift = prm->max_shift;
   A.alpha_min = prm->alpha_min; A.alpha_max = prm->alpha_max; A.T_min = prm->T_min;
   A.tau = prm->tau; A.bg_weight = prm->bg_weight;
   for (int c = 0; c < A.C; c++) A.bg[c] = prm->background ? prm->background[c] : 0.0f;
@@ -310,6 +316,7 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   CHECK(proj && vals && tile_ranges && overflow && dL_dimg, SPLAT_ERR_INVALID_ARG, "NULL input");
   if (prims->kind == SPLAT_PRIM_SPHERE) {
     CHECK(img && norm && topk, SPLAT_ERR_INVALID_ARG, "sphere backward needs img, norm and topk");
+    CHECK(!prm->max_shift || T_final, SPLAT_ERR_INVALID_ARG, "max-shifted backward needs T_final (the shifts)");
   } else {
     CHECK(T_final && last, SPLAT_ERR_INVALID_ARG, "Gaussian backward needs T_final and last");
     CHECK(grads->cam_K == nullptr, SPLAT_ERR_UNSUPPORTED, "intrinsic gradients are for spheres only");
@@ -322,6 +329,7 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   memset(&A, 0, sizeof(A));
   A.n = prims->n; A.C = prims->channels; A.top_k = prm->top_k;
   A.alpha_min = prm->alpha_min; A.alpha_max = prm->alpha_max; A.gamma = prm->gamma;
+  A.max_shift = prims->kind == SPLAT_PRIM_SPHERE ? prm->max_shift : 0;
   ProjLayout L = proj_layout(const_cast<void *>(proj), (long long)n_views * prims->n);
   A.draw = L.draw; A.aux = L.aux; A.vals = vals; A.ranges = tile_ranges; A.overflow = overflow;
   A.feat = prims->feat; A.img = img; A.T_final = T_final; A.last = last; A.norm = norm; A.topk = topk;

@@ -92,6 +92,7 @@ struct PrimArgs {
   int kind, n;
   const float *pos, *scale, *rot, *opacity, *depth;
   double gamma, alpha_min;
+  int max_shift;      // spheres: draw records carry log-weights (see below)
 };
 
 // One (view, primitive): the binning record and pair count go straight to
@@ -159,8 +160,15 @@ __device__ __forceinline__ bool project_one(const ViewDev &c, const PrimArgs &P,
     d.a = orth ? 1.0 / (re * re) : q[2] * q[2] / (re * re);
     d.b = u;                           // projected centre (pixels), informational
     d.c = v;
-    d.w = (float)(o * e);
-    d.e = (float)bnd;
+    if (P.max_shift) {
+      // logs: ln(o exp(o zhat / gamma)) and ln(bound); the compositors blend
+      // relative to a per-pixel shift, so nothing overflows for small gamma
+      d.w = (float)(log(o) + o * zhat / P.gamma);
+      d.e = (float)((((double)c.zfar - (double)key) / span) / P.gamma);
+    } else {
+      d.w = (float)(o * e);
+      d.e = (float)bnd;
+    }
     d.i0 = rc.i0; d.i1 = rc.i1; d.j0 = rc.j0; d.j1 = rc.j1;
     dd = d;
     AuxRec a;
@@ -324,8 +332,8 @@ __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjL
 
 }  // namespace
 
-int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, double alpha_min, void *proj,
-                   uint32_t *counts, hipStream_t stream) {
+int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, double alpha_min, int max_shift,
+                   void *proj, uint32_t *counts, hipStream_t stream) {
   long long nrec = (long long)vt.n * pr->n;
   if (nrec == 0) return SPLAT_OK;
   PrimArgs P;
@@ -333,6 +341,7 @@ int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, dou
   P.pos = pr->pos; P.scale = pr->scale; P.rot = pr->rot; P.opacity = pr->opacity; P.depth = pr->depth;
   P.gamma = gamma;
   P.alpha_min = alpha_min;
+  P.max_shift = max_shift;
   ProjLayout L = proj_layout(proj, nrec);
   const dim3 grid((unsigned)((pr->n + 255) / 256), (unsigned)vt.n);
   if (pr->kind == SPLAT_PRIM_SPHERE)

@@ -587,6 +587,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     my_top[ntop++] = lp;
   }
   if (tp.inside) invN = 1.0f / A.norm[p];
+  // max-shifted blending: weights (and norm) relative to exp(m), m from the forward
+  const float msh = (A.max_shift && tp.inside) ? A.T_final[p] : 0.0f;
   if (threadIdx.x == 0) s_npos = 0;
   __syncthreads();
   {
@@ -648,7 +650,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
         const double2 aa = s_a[idx], Ai = s_Ai[idx];
         const float4 x = s_x[idx];
         const int flags = s_flags[idx];
-        const float oe = x.y;
+        const float oe = A.max_shift ? __expf(x.y - msh) : x.y;     // o exp(o zhat / gamma) [/ exp(m)]
         // D = 1 - A g |a x d|^2 with a x d from the offsets sx = x - ax, sy = y - ay
         const double sx = ray.x - aa.x, sy = ray.y - aa.y;
         const double cr = (aa.x * sy - aa.y * sx) * crs;

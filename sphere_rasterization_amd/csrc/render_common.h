@@ -9,6 +9,7 @@
 struct FwdArgs {
   int n, C, top_k;
   int top_by_depth;       // spheres: record the top_k closest entry points, not the first top_k
+  int max_shift;          // spheres: draw records hold log-weights; blend relative to a per-pixel shift
   float alpha_min, alpha_max, T_min, tau, bg_weight;
   const DrawRec *draw;
   const AuxRec *aux;
@@ -44,6 +45,7 @@ struct BwdArgs {
   double *cam_part;       // [SPLAT_CAM_BLOCKS][12] per-block camera sums (spheres)
   double *kslot;          // [views][SPLAT_K_SLOTS][4] intrinsic-gradient sums, or NULL (not requested)
   uint32_t *cnt;          // [records] pixels that recorded the sphere, or NULL (no normalisation)
+  int max_shift;          // spheres: weights relative to the per-pixel shift held in T_final
 };
 
 struct TilePix {

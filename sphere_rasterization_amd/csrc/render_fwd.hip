@@ -25,7 +25,11 @@ namespace {
 // ---------------------------------------------------------------------------
 // TOPD: record each pixel's top_k contributing spheres of smallest entry depth
 // (sensor z where the ray enters the sphere) instead of the first top_k.
-template <int CM, bool TOPD>
+// MS: max-shifted blending. The records hold lambda = ln(o exp(o zhat / gamma))
+// and beta = ln(bound); each pixel keeps its sums relative to exp(m), m the
+// largest lambda so far (at least 0), rescaling them when a contributing sphere
+// raises m, and tests the stop in the log domain: beta - ln tau < m + ln N.
+template <int CM, bool TOPD, bool MS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
   // One staged entry = NE 16-byte slots at a common stride, so every read of an
   // entry uses one LDS address with constant offsets: three slots of D / g
@@ -48,6 +52,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   const int sb = wq * 4 + (int)((threadIdx.x >> 4) & 3u);                  // this lane's 4x4 block
   const float tau = A.tau;
   float N = A.bg_weight;
+  float msh = 0.0f;                              // MS: the shift m
+  float lgn = MS ? __logf(A.bg_weight) : 0.0f;  // MS: m + ln N
   float S[CM];
 #pragma unroll
   for (int ch = 0; ch < CM; ch++) S[ch] = A.bg_weight * A.bg[ch];
@@ -83,9 +89,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       s_e[1][threadIdx.x] = __builtin_bit_cast(float4, q.q23);
       s_e[2][threadIdx.x] = __builtin_bit_cast(float4, q.q45);
       float t[4 * NF4];
-      // stop when bound < tau N, i.e. N > bound / tau (never when tau = 0)
+      // stop when bound < tau N, i.e. N > bound / tau (never when tau = 0);
+      // MS: lambda, and beta - ln tau against m + ln N
       t[0] = d.w;
-      t[1] = tau > 0.0f ? d.e / tau : __builtin_huge_valf();
+      if constexpr (MS)
+        t[1] = tau > 0.0f ? d.e - __logf(tau) : __builtin_huge_valf();
+      else
+        t[1] = tau > 0.0f ? d.e / tau : __builtin_huge_valf();
 #pragma unroll
       for (int ch = 0; ch < 4 * NF4 - 2; ch++) t[2 + ch] = ch < CM && ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
 #pragma unroll
@@ -125,16 +135,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
           const float4 x = s_e[3 + f][idx];
           t[4 * f] = x.x; t[4 * f + 1] = x.y; t[4 * f + 2] = x.z; t[4 * f + 3] = x.w;
         }
-        active = active & !(valid & (N > t[1]));  // no later sphere can matter (& : no short-circuit branch)
+        // no later sphere can matter (& : no short-circuit branch)
+        if constexpr (MS)
+          active = active & !(valid & (t[1] < lgn));
+        else
+          active = active & !(valid & (N > t[1]));
         const double num = sphere_num(ray, __builtin_bit_cast(double2, s_e[0][idx]),
                                       __builtin_bit_cast(double2, s_e[1][idx]),
                                       __builtin_bit_cast(double2, s_e[2][idx]));
         const bool hit = active & valid & (num > 0.0);
-        // 0 or 1 times a finite weight: straight-line code, no branch around it
-        const float w = (hit ? 1.0f : 0.0f) * (t[0] * (float)(num * ray.g));
-        N += w;
+        if constexpr (MS) {
+          if (ballot64(hit)) {
+            const float sh = hit ? fmaxf(msh, t[0]) : msh;
+            const float rs = __expf(msh - sh);             // 1 unless the shift rises
+            // a select, not a 0/1 factor: a lane without a hit may hold lambda > m
+            const float w = hit ? __expf(t[0] - sh) * (float)(num * ray.g) : 0.0f;
+            N = __builtin_fmaf(N, rs, w);
 #pragma unroll
-        for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch]);
+            for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch] * rs);
+            msh = sh;
+            lgn = hit ? msh + __logf(N) : lgn;
+          }
+        } else {
+          // 0 or 1 times a finite weight: straight-line code, no branch around it
+          const float w = (hit ? 1.0f : 0.0f) * (t[0] * (float)(num * ray.g));
+          N += w;
+#pragma unroll
+          for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch]);
+        }
         if constexpr (decltype(REC)::value) {
           const bool rec = hit & need;
           if constexpr (TOPD) {
@@ -208,6 +236,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   for (int ch = 0; ch < CM; ch++)
     if (ch < A.C) img[ch * plane] = S[ch] * inv;
   if (A.norm) A.norm[p] = N;
+  if constexpr (MS) {
+    if (A.T_final) A.T_final[p] = msh;
+  }
   if constexpr (TOPD) {
     if (A.topk) {
       // list order: sort the positions (empty slots, 0xffffffff, go last)
@@ -513,10 +544,14 @@ template <int CM>
 int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t stream) {
   dim3 grid(vt.total_tiles), block(256);
   if (kind == SPLAT_PRIM_SPHERE) {
-    if (A.top_by_depth)
-      hipLaunchKernelGGL((k_fwd_sphere<CM, true>), grid, block, 0, stream, vt, A);
+    if (A.top_by_depth && A.max_shift)
+      hipLaunchKernelGGL((k_fwd_sphere<CM, true, true>), grid, block, 0, stream, vt, A);
+    else if (A.top_by_depth)
+      hipLaunchKernelGGL((k_fwd_sphere<CM, true, false>), grid, block, 0, stream, vt, A);
+    else if (A.max_shift)
+      hipLaunchKernelGGL((k_fwd_sphere<CM, false, true>), grid, block, 0, stream, vt, A);
     else
-      hipLaunchKernelGGL((k_fwd_sphere<CM, false>), grid, block, 0, stream, vt, A);
+      hipLaunchKernelGGL((k_fwd_sphere<CM, false, false>), grid, block, 0, stream, vt, A);
   } else {
     // one launch per run of consecutive views of one kind, over that run's
     // tiles only. With both kinds present the camera views run on the side

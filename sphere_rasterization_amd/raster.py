@@ -36,6 +36,7 @@ def make_params(p: Params, channels: int):
     s.alpha_min, s.alpha_max, s.T_min = p.alpha_min, p.alpha_max, p.T_min
     s.gamma, s.bg_weight, s.tau, s.top_k = p.gamma, p.bg_weight, p.tau, int(p.top_k)
     s.top_by_depth = int(getattr(p, "top_by_depth", 0))
+    s.max_shift = int(getattr(p, "max_shift", 0))
     keep = None
     if p.background is not None:
         keep = (C.c_float * channels)(*[float(x) for x in np.asarray(p.background, np.float32)[:channels]])
@@ -77,7 +78,9 @@ class Rasterizer:
         self.overflow = torch.zeros(1, dtype=torch.int32, device=dev)
         self.img = torch.empty(sum(self.img_sizes), dtype=torch.float32, device=dev)
         sph = self.kind == 2
-        self.T_final = None if sph else torch.empty(self.total_pix, dtype=torch.float32, device=dev)
+        # spheres use T_final only for the per-pixel shift of max-shifted blending
+        need_T = (not sph) or bool(getattr(scene.params, "max_shift", 0))
+        self.T_final = torch.empty(self.total_pix, dtype=torch.float32, device=dev) if need_T else None
         self.last = None if sph else torch.empty(self.total_pix, dtype=torch.int32, device=dev)
         K = scene.params.top_k
         self.norm = torch.empty(self.total_pix, dtype=torch.float32, device=dev) if sph else None

@@ -122,6 +122,16 @@ def test_parameter_assembly():
     _log("  assemble ok")
 
 
+def test_max_shifted_spheres():
+    # gamma = 1/200: unshifted weights exp(o zhat / gamma) would overflow fp32
+    sc = S.pulsar_spheres(seed=27, n=200_000, width=640, height=480)
+    sc.params = S.Params(gamma=0.005, max_shift=1)
+    _run(sc, 14, "spheres 200k @640x480 gamma 1/200 max-shifted")
+    s2 = S.pulsar_spheres(seed=28, n=150_000, width=512, height=384)
+    s2.params = S.Params(max_shift=1, top_by_depth=1)
+    _run(s2, 15, "spheres 150k @512x384 max-shifted, closest five")
+
+
 def test_ragged_gauss3d():
     sc = S.gauss3d(seed=12, n=30_000, width=500, height=300)
     _run(sc, 8, "gauss3d 30k @500x300 ragged")

@@ -144,3 +144,20 @@ def test_interpolate_argument_errors():
     assert lib.splat_interpolate(good, 3, 0.5, 10, None, None, None, None, None) == L.SPLAT_ERR_INVALID_ARG
     assert lib.splat_interpolate(good, 3, 0.5, 10, 16, 20, 16, 16, None) == L.SPLAT_ERR_INVALID_ARG   # misaligned
     assert lib.splat_interpolate_bwd(good, 3, 0.5, 10, None, 16, 16, 16, 16, None) == L.SPLAT_ERR_INVALID_ARG
+
+
+def test_small_gamma_needs_max_shift():
+    from sphere_rasterization_amd.raster import make_cams, make_params
+    sc = S.pulsar_spheres(n=10)
+    cams = make_cams(sc.cams)
+    lib = L.lib()
+    pr = L.splat_prims()
+    pr.kind, pr.n, pr.channels = 2, 10, 3
+    pr.pos = pr.scale = pr.opacity = pr.feat = 8
+    prm, _ = make_params(S.Params(gamma=0.005), 3)
+    assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
+    prm, _ = make_params(S.Params(gamma=0.02, max_shift=3), 3)
+    assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
+    pr.kind, pr.rot = 1, 8
+    prm, _ = make_params(S.Params(max_shift=1), 3)
+    assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_UNSUPPORTED
