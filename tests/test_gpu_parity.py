@@ -105,6 +105,12 @@ def test_parameter_assembly():
         tie = A.sign_ties(times, t32, kr)
         dq = np.abs(rot.cpu().numpy() - rq)[~tie]
         assert (dq <= 4 * u * mq[~tie] + 1e-30).all(), float((dq / (mq[~tie] + 1e-30)).max())
+    # one keyframe, and no primitives: the single frame, and nothing to do
+    p1, q1 = interpolate(times[:1], float(times[0]) + 0.5, kp_d[:1, :1000], kr_d[:1, :1000])
+    torch.cuda.synchronize()
+    assert torch.equal(p1, kp_d[0, :1000]) and torch.equal(q1, kr_d[0, :1000])
+    p0, q0 = interpolate(times, float(times[1]), kp_d[:, :0], kr_d[:, :0])
+    assert p0.shape == (0, 3) and q0.shape == (0, 4)
     # reverse pass at an interior time
     t32 = float(np.float32(ts[3]))
     gp = rng.standard_normal((n, 3)).astype(np.float32)
@@ -227,6 +233,24 @@ def test_spheres_two_views():
     _log(f"  bwd (one call) worst={bw['worst']:.3f}")
     bw = compare_backward(rz, orc, None, g, view_groups=[(0, 1), (1, 1)])
     _log(f"  bwd (per view) worst={bw['worst']:.3f}")
+
+
+def test_sphere_option_edges():
+    """Option corners: closest-K with top_k 1 and 8; max-shift without early stop at
+    gamma = 1/250; a pinhole and an orthographic view in one call with intrinsic
+    gradients and normalisation (one call over both views)."""
+    base = S.pulsar_spheres(seed=29, n=60_000, width=320, height=240)
+    for k in (1, 8):
+        sc = S.pulsar_spheres(seed=29, n=60_000, width=320, height=240)
+        sc.params = S.Params(top_k=k, top_by_depth=1)
+        _run(sc, 16 + k, f"spheres 60k @320x240 closest {k}")
+    sc = S.pulsar_spheres(seed=30, n=60_000, width=320, height=240)
+    sc.params = S.Params(gamma=0.004, tau=0.0, max_shift=1)
+    _run(sc, 19, "spheres 60k @320x240 gamma 1/250 max-shifted, no early stop")
+    sc = S.Scene(S.PRIM_SPHERE, base.n, 3, base.pos, base.scale, base.opacity, base.feat,
+                 cams=[base.cams[0], S.Camera(S.CAM_ORTHO, 300, 220, base.cams[0].R, base.cams[0].t, fx=30.0,
+                                              fy=28.0, cx=150.0, cy=110.0, znear=1.0, zfar=21.0)])
+    _run(sc, 20, "spheres 60k: pinhole 320x240 + orthographic 300x220, normalised", normalize=True)
 
 
 def test_all_culled_and_single():
