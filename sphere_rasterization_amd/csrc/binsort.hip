@@ -17,9 +17,9 @@
 //   k_thist                       each workgroup counts the tiles of a chunk of
 //                                 one view's records in LDS and stores the counts
 //                                 as one row of the view's [chunk][tile] matrix
-//   k_col_sum, k_col_offsets      per tile (column): for every chunk the
+//   k_col_scan                    per tile (column): for every chunk the
 //                                 exclusive prefix over earlier chunks, and the
-//                                 tile's pair total
+//                                 tile's pair total (16 waves per 64 columns)
 //   k_tile_scan1                  exclusive scan over tiles (one workgroup):
 //                                 tile ranges, pair total, overflow, tile starts
 //   k_tscatter                    each pair's word into its tile's segment, at
@@ -47,7 +47,6 @@ constexpr int TH_CHUNK = TH_THREADS * TH_RPT;
 constexpr int SEG_WAVE = 512;       // segments up to this length: one wave sorts them
 constexpr int TILE_SCAN1_MAX = 1 << 16;   // tiles scanned by a single workgroup
 constexpr int LDS_TILES = 16384;    // tiles of one view held as LDS counters (64 KiB)
-constexpr int COL_ROWS = 16;        // matrix rows (chunks) per thread in the column scan
 constexpr int LT = 512;             // threads of the long-segment sort
 constexpr int LE = 16;              // words per thread in the long-segment sort
 constexpr int NV = LT * LE;         // words one workgroup sorts in LDS (64 KiB)
@@ -467,44 +466,47 @@ __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt,
   for (int t = threadIdx.x; t < T; t += TH_THREADS) row[t] = s_cnt[t];
 }
 
-// Column (tile) partial sums over groups of COL_ROWS chunks: S[group][gtile].
-// grid: (ceil(tiles / 256), ngroups).
-__global__ __launch_bounds__(256) void k_col_sum(ViewTable vt, MatTable mt, int nchunk, const uint32_t *M,
-                                                  uint32_t *S) {
-  const int gt = blockIdx.x * 256 + threadIdx.x;
-  if (gt >= vt.total_tiles) return;
-  const int v = view_of_tile(vt, gt);
-  const ViewDev &cv = vt.v[v];
-  const int t = gt - cv.tile_off, c0 = blockIdx.y * COL_ROWS;
-  uint32_t s = 0;
-#pragma unroll
-  for (int r = 0; r < COL_ROWS; r++)
-    if (c0 + r < nchunk) s += M[mat_index(mt, cv, v, c0 + r, t)];
-  S[(size_t)blockIdx.y * vt.total_tiles + gt] = s;
-}
-
 // Matrix entries become the exclusive prefix over earlier chunks of the same
-// tile; the group's starting prefix is the sum of the earlier groups' partial
-// sums, and the last group also writes the tile's pair count.
-__global__ __launch_bounds__(256) void k_col_offsets(ViewTable vt, MatTable mt, int nchunk, int ngroups,
-                                                      const uint32_t *S, uint32_t *M, uint32_t *tile_cnt) {
-  const int gt = blockIdx.x * 256 + threadIdx.x;
-  if (gt >= vt.total_tiles) return;
-  const int v = view_of_tile(vt, gt);
-  const ViewDev &cv = vt.v[v];
-  const int t = gt - cv.tile_off, c0 = blockIdx.y * COL_ROWS;
-  uint32_t run = 0;
+// tile, and tile_cnt gets each tile's pair count. One workgroup per 64 tiles:
+// lane l of every wave owns tile 64 b + l, and the 16 waves split the chunks into
+// consecutive ranges; each wave sums its range, the waves' sums are scanned in
+// LDS, then each wave rewrites its range as running prefixes.
+constexpr int CS_WAVES = 16;
+
+__global__ __launch_bounds__(CS_WAVES * 64) void k_col_scan(ViewTable vt, MatTable mt, int nchunk, uint32_t *M,
+                                                            uint32_t *tile_cnt) {
+  __shared__ uint32_t s_part[CS_WAVES][64];
+  const int w = (int)(threadIdx.x >> 6), l = (int)(threadIdx.x & 63u);
+  const int gt = (int)blockIdx.x * 64 + l;
+  const bool ok = gt < vt.total_tiles;
+  const int q = (nchunk + CS_WAVES - 1) / CS_WAVES;
+  const int c0 = w * q, c1 = min(c0 + q, nchunk);
+  long long base = 0, stride = 0;
+  if (ok) {
+    const int v = view_of_tile(vt, gt);
+    const ViewDev &cv = vt.v[v];
+    base = mat_index(mt, cv, v, 0, gt - cv.tile_off);
+    stride = (long long)cv.TW * cv.TH;
+  }
+  uint32_t s = 0;
+  if (ok) {
 #pragma unroll 8
-  for (int g = 0; g < (int)blockIdx.y; g++) run += S[(size_t)g * vt.total_tiles + gt];
-#pragma unroll
-  for (int r = 0; r < COL_ROWS; r++)
-    if (c0 + r < nchunk) {
-      const long long i = mat_index(mt, cv, v, c0 + r, t);
+    for (int c = c0; c < c1; c++) s += M[base + c * stride];
+  }
+  s_part[w][l] = s;
+  __syncthreads();
+  uint32_t run = 0;
+  for (int w2 = 0; w2 < w; w2++) run += s_part[w2][l];
+  if (ok) {
+#pragma unroll 8
+    for (int c = c0; c < c1; c++) {
+      const long long i = base + c * stride;
       const uint32_t x = M[i];
       M[i] = run;
       run += x;
     }
-  if ((int)blockIdx.y == ngroups - 1) tile_cnt[gt] = run;
+    if (w == CS_WAVES - 1) tile_cnt[gt] = run;
+  }
 }
 
 // Same chunks as k_thist: words to tile start + chunk prefix + LDS rank.
@@ -912,13 +914,12 @@ struct SortWs {
   uint32_t *live;       // [0] live pairs, [1] [2] long-segment list counts, [3] queue head
   uint32_t *list;       // [2 * tiles] long-segment work lists
   uint32_t *mat;        // per-chunk tile counts (LDS counting path)
-  uint32_t *colsum;     // [groups][tiles]
   size_t bytes;
 };
 
 struct CountPlan {
   bool lds;             // every view's tiles fit the LDS counters
-  int nchunk, ngroups, max_tiles;
+  int nchunk, max_tiles;
   long long mat_elems;
   MatTable mt;
 };
@@ -926,7 +927,6 @@ struct CountPlan {
 CountPlan count_plan(const ViewTable &vt, int n) {
   CountPlan cp{};
   cp.nchunk = (n + TH_CHUNK - 1) / TH_CHUNK;
-  cp.ngroups = (cp.nchunk + COL_ROWS - 1) / COL_ROWS;
   cp.lds = n > 0;
   long long off = 0;
   for (int v = 0; v < vt.n; v++) {
@@ -936,7 +936,6 @@ CountPlan count_plan(const ViewTable &vt, int n) {
     cp.mt.off[v] = off;
     off += (long long)cp.nchunk * T;
   }
-  if (cp.ngroups > 65535) cp.lds = false;   // grid.y of the column kernels
   cp.mat_elems = cp.lds ? off : 0;
   return cp;
 }
@@ -953,7 +952,6 @@ SortWs sort_ws_layout(void *base, const ViewTable &vt, int n, long long capacity
   w.live = (uint32_t *)p;       p += proj_align(sizeof(uint32_t) * 4);
   w.list = (uint32_t *)p;       p += proj_align(sizeof(uint32_t) * 2 * (size_t)tiles);
   w.mat = (uint32_t *)p;        p += proj_align(sizeof(uint32_t) * (size_t)cp.mat_elems);
-  w.colsum = (uint32_t *)p;     p += proj_align(sizeof(uint32_t) * (size_t)(cp.lds ? cp.ngroups * tiles : 0));
   w.bytes = (size_t)(p - (char *)base);
   return w;
 }
@@ -981,10 +979,8 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
     const unsigned grid = (unsigned)(vt.n * cp.nchunk);
     hipLaunchKernelGGL(k_thist, dim3(grid), dim3(TH_THREADS), lds_bytes, stream, vt, cp.mt, n, cp.nchunk, L.bin,
                        counts, ws.mat);
-    hipLaunchKernelGGL(k_col_sum, dim3(tile_blocks, cp.ngroups), dim3(256), 0, stream, vt, cp.mt, cp.nchunk, ws.mat,
-                       ws.colsum);
-    hipLaunchKernelGGL(k_col_offsets, dim3(tile_blocks, cp.ngroups), dim3(256), 0, stream, vt, cp.mt, cp.nchunk,
-                       cp.ngroups, ws.colsum, ws.mat, ws.cursor);
+    hipLaunchKernelGGL(k_col_scan, dim3((unsigned)((tiles + 63) / 64)), dim3(CS_WAVES * 64), 0, stream, vt, cp.mt,
+                       cp.nchunk, ws.mat, ws.cursor);
   } else {
     hipLaunchKernelGGL(k_fill_u32, dim3(tile_blocks), dim3(256), 0, stream, ws.cursor, tiles, 0u);
     if (rec_blocks)
