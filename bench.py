@@ -38,7 +38,7 @@ OPS_PER_HIT_BASE = 5          # + one fma per channel
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 276405165
+FWD_TRAFFIC_BYTES = 276427243
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")

@@ -17,8 +17,9 @@
 //   k_thist                       each workgroup counts the tiles of a chunk of
 //                                 one view's records in LDS and stores the counts
 //                                 as one row of the view's [chunk][tile] matrix
-//   k_col_scan                    per tile (column): for every chunk the
-//                                 exclusive prefix over earlier chunks, and the
+//                                 (rows in XCD-major chunk order)
+//   k_col_scan                    per tile (column): for every row the
+//                                 exclusive prefix over earlier rows, and the
 //                                 tile's pair total (16 waves per 64 columns)
 //   k_tile_scan1                  exclusive scan over tiles (one workgroup):
 //                                 tile ranges, pair total, overflow, tile starts
@@ -54,11 +55,11 @@ constexpr int NV_PHYS = NV + NV / LE;   // one pad word after every LE words
 constexpr int MAXLVL = 8;           // MSD split levels (8 bits of the word range each)
 constexpr int SORT_GRID = 512;      // workgroups of the segment sort (two per CU)
 
-// Block-wide exclusive scan of one value per thread (256 threads); returns the
+// Block-wide exclusive scan of one value per thread (NT threads); returns the
 // exclusive prefix and writes the block total to *total.
-template <typename T>
+template <typename T, int NT = SCAN_BLOCK>
 __device__ T block_exclusive_scan(T x, T *total) {
-  __shared__ T s_w[SCAN_BLOCK / WAVE];
+  __shared__ T s_w[NT / WAVE];
   unsigned lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
   T inc = x;
 #pragma unroll
@@ -70,7 +71,7 @@ __device__ T block_exclusive_scan(T x, T *total) {
   __syncthreads();
   T wbase = 0, tot = 0;
 #pragma unroll
-  for (int k = 0; k < SCAN_BLOCK / WAVE; k++) {
+  for (int k = 0; k < NT / WAVE; k++) {
     T t = s_w[k];
     if ((unsigned)k < w) wbase += t;
     tot += t;
@@ -193,31 +194,37 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_ranges(uint32_t *cnt_cursor
 // Single workgroup, up to TILE_SCAN1_MAX tiles: pair total, overflow flag and
 // live count first, then, without overflow, the exclusive scan that writes the
 // tile ranges and turns the counts into tile starts. Every thread owns
-// TOP_ITEMS consecutive tiles per round; up to SCAN_BLOCK * TOP_ITEMS tiles in all
-// keep their counts in registers between the two phases. The same scan (three
+// TS_ITEMS consecutive tiles per round, so one wave's loads and stores cover a
+// contiguous 1-2 KiB span (with 16 tiles per thread each wave instruction
+// touched 64 cache lines, and one CU issues them all); up to
+// TS_THREADS * TS_ITEMS tiles in all keep their counts in registers between the
+// two phases. The same scan (three
 // fields packed in one 64-bit value) lists the tiles for the long-segment sort:
 // list[0..) those with more than NV pairs in tile order, list[m..) those with
 // SEG_WAVE < pairs <= NV; live[1], live[2] count them, live[3] = 0 is the queue
 // head.
-__device__ __forceinline__ void load_counts(const uint32_t *cnt, int m, int t0, uint32_t (&x)[TOP_ITEMS]) {
+constexpr int TS_THREADS = 1024;
+constexpr int TS_ITEMS = 4;
+
+__device__ __forceinline__ void load_counts(const uint32_t *cnt, int m, int t0, uint32_t (&x)[TS_ITEMS]) {
 #pragma unroll
-  for (int r = 0; r < TOP_ITEMS; r++) x[r] = t0 + r < m ? cnt[t0 + r] : 0u;
+  for (int r = 0; r < TS_ITEMS; r++) x[r] = t0 + r < m ? cnt[t0 + r] : 0u;
 }
 
-__global__ __launch_bounds__(SCAN_BLOCK) void k_tile_scan1(uint32_t *cnt_start, int m, long long capacity,
+__global__ __launch_bounds__(TS_THREADS) void k_tile_scan1(uint32_t *cnt_start, int m, long long capacity,
                                                             int64_t *num_pairs, int32_t *overflow, uint32_t *live,
                                                             uint32_t *ranges, uint32_t *list) {
   __shared__ int s_of;
-  constexpr int ROUND = SCAN_BLOCK * TOP_ITEMS;
-  uint32_t x[TOP_ITEMS];
+  constexpr int ROUND = TS_THREADS * TS_ITEMS;
+  uint32_t x[TS_ITEMS];
   unsigned long long part = 0;
   for (int base = 0; base < m; base += ROUND) {
-    load_counts(cnt_start, m, base + (int)threadIdx.x * TOP_ITEMS, x);
+    load_counts(cnt_start, m, base + (int)threadIdx.x * TS_ITEMS, x);
 #pragma unroll
-    for (int r = 0; r < TOP_ITEMS; r++) part += x[r];
+    for (int r = 0; r < TS_ITEMS; r++) part += x[r];
   }
   unsigned long long total;
-  block_exclusive_scan<unsigned long long>(part, &total);
+  block_exclusive_scan<unsigned long long, TS_THREADS>(part, &total);
   if (threadIdx.x == 0) {
     const int of = total > (unsigned long long)capacity ? 1 : 0;
     *num_pairs = (int64_t)total;
@@ -231,11 +238,11 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_scan1(uint32_t *cnt_start, 
   // at most ROUND < 2^16, so the packed fields never carry into each other
   uint32_t carry = 0, carry_h = 0, carry_m = 0;
   for (int base = 0; base < m; base += ROUND) {
-    const int t0 = base + (int)threadIdx.x * TOP_ITEMS;
+    const int t0 = base + (int)threadIdx.x * TS_ITEMS;
     if (m > ROUND) load_counts(cnt_start, m, t0, x);   // one round: still in registers
     uint32_t sum = 0, nh = 0, nm = 0;
 #pragma unroll
-    for (int r = 0; r < TOP_ITEMS; r++) {
+    for (int r = 0; r < TS_ITEMS; r++) {
       sum += x[r];
       nh += x[r] > (uint32_t)NV ? 1u : 0u;
       nm += (x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV) ? 1u : 0u;
@@ -243,11 +250,11 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_scan1(uint32_t *cnt_start, 
     const unsigned long long packed =
         (unsigned long long)sum | ((unsigned long long)nh << 32) | ((unsigned long long)nm << 48);
     unsigned long long tot;
-    const unsigned long long pre = block_exclusive_scan<unsigned long long>(packed, &tot);
+    const unsigned long long pre = block_exclusive_scan<unsigned long long, TS_THREADS>(packed, &tot);
     uint32_t run = carry + (uint32_t)pre;
     uint32_t ph = carry_h + (uint32_t)((pre >> 32) & 0xffffu), pm = carry_m + (uint32_t)(pre >> 48);
 #pragma unroll
-    for (int r = 0; r < TOP_ITEMS; r++) {
+    for (int r = 0; r < TS_ITEMS; r++) {
       if (t0 + r < m) {
         cnt_start[t0 + r] = run;
         ranges[2 * (t0 + r)] = x[r] ? run : 0u;
@@ -293,8 +300,21 @@ struct MatTable {
   long long off[SPLAT_MAX_VIEWS];
 };
 
-__device__ __forceinline__ long long mat_index(const MatTable &mt, const ViewDev &cv, int v, int chunk, int t) {
-  return mt.off[v] + (long long)chunk * (cv.TW * cv.TH) + t;
+__device__ __forceinline__ long long mat_index(const MatTable &mt, const ViewDev &cv, int v, int row, int t) {
+  return mt.off[v] + (long long)row * (cv.TW * cv.TH) + t;
+}
+
+// Matrix row of a chunk: the rows hold the chunks in XCD-major order, chunks
+// c = 0, 8, 16, ... first, then 1, 9, 17, ..., and so on. Workgroups go to the
+// eight XCDs round-robin, so the k_tscatter workgroups of one residue class
+// share an XCD (and its L2); with the prefix over rows in this order each XCD
+// fills one contiguous run of every tile's segment. In plain chunk order
+// neighbouring words of a segment came from different XCDs, each L2 wrote the
+// line back partially and every 8-byte word cost a 32-byte sector. Any order is
+// correct: the segment is sorted afterwards.
+__device__ __forceinline__ int chunk_row(int chunk, int nchunk) {
+  const int a = nchunk >> 3, b = nchunk & 7, g = chunk & 7;   // residues below b hold a + 1 chunks
+  return g * a + min(g, b) + (chunk >> 3);
 }
 
 // Records of one chunk, loaded up front (every thread TH_RPT of them, coalesced).
@@ -462,13 +482,13 @@ __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt,
   __syncthreads();
   chunk_pairs(cv, cr, hl, [&](uint32_t lt, uint32_t, uint32_t) { atomicAdd(&s_cnt[lt], 1u); });
   __syncthreads();
-  uint32_t *row = M + mat_index(mt, cv, v, chunk, 0);
+  uint32_t *row = M + mat_index(mt, cv, v, chunk_row(chunk, nchunk), 0);
   for (int t = threadIdx.x; t < T; t += TH_THREADS) row[t] = s_cnt[t];
 }
 
-// Matrix entries become the exclusive prefix over earlier chunks of the same
+// Matrix entries become the exclusive prefix over earlier rows of the same
 // tile, and tile_cnt gets each tile's pair count. One workgroup per 64 tiles:
-// lane l of every wave owns tile 64 b + l, and the 16 waves split the chunks into
+// lane l of every wave owns tile 64 b + l, and the 16 waves split the rows into
 // consecutive ranges; each wave sums its range, the waves' sums are scanned in
 // LDS, then each wave rewrites its range as running prefixes.
 constexpr int CS_WAVES = 16;
@@ -520,7 +540,7 @@ __global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable 
   const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
   const ViewDev &cv = vt.v[v];
   const int T = cv.TW * cv.TH;
-  const uint32_t *row = M + mat_index(mt, cv, v, chunk, 0);
+  const uint32_t *row = M + mat_index(mt, cv, v, chunk_row(chunk, nchunk), 0);
   for (int t = threadIdx.x; t < T; t += TH_THREADS) s_base[t] = tile_start[cv.tile_off + t] + row[t];
   ChunkRecs cr;
   const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
@@ -611,20 +631,45 @@ __device__ __forceinline__ void bitonic512(uint64_t (&e)[8], unsigned lane) {
 }
 
 // Segments of at most SEG_WAVE pairs: one wave per tile, padded to 512 words
-// with all-ones words (they sort last), the whole network unrolled.
+// with all-ones words (they sort last), the whole network unrolled. The network
+// wants lane l to hold words 8 l .. 8 l + 7; global memory is read and written
+// with lane l on words l + 64 a instead (each wave access one contiguous run)
+// and the wave transposes through its own 576 words of LDS, one pad word after
+// every eight so that the blocked accesses (72-byte lane stride) spread over
+// the banks. LDS operations of one wave complete in order, so no barrier is
+// needed between a lane's write and another lane's read.
+constexpr int WS_LDS = SEG_WAVE + SEG_WAVE / 8;
+
+__device__ __forceinline__ int wslot(int x) { return x + (x >> 3); }
+
 __device__ __forceinline__ void wave_sort_tile(const uint32_t *ranges, const uint64_t *words, uint64_t *keys,
-                                               uint32_t *vals, int t) {
+                                               uint32_t *vals, int t, uint64_t *sw) {
   const uint32_t start = ranges[2 * t], len = ranges[2 * t + 1] - start;
   if (len == 0 || len > SEG_WAVE) return;
   const unsigned lane = lane_id();
-  const uint32_t base = lane * 8;
   uint64_t e[8];
 #pragma unroll
-  for (int a = 0; a < 8; a++) e[a] = base + a < len ? words[start + base + a] : ~0ull;
-  bitonic512<2>(e, lane);
+  for (int a = 0; a < 8; a++) {
+    const uint32_t x = lane + 64u * a;
+    e[a] = x < len ? words[start + x] : ~0ull;
+  }
 #pragma unroll
-  for (int a = 0; a < 8; a++)
-    if (base + a < len) write_pair(keys, vals, start + base + a, (uint32_t)t, e[a]);
+  for (int a = 0; a < 8; a++) sw[wslot((int)lane + 64 * a)] = e[a];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int a = 0; a < 8; a++) e[a] = sw[wslot(8 * (int)lane + a)];
+  bitonic512<2>(e, lane);
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int a = 0; a < 8; a++) sw[wslot(8 * (int)lane + a)] = e[a];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int a = 0; a < 8; a++) {
+    const uint32_t x = lane + 64u * a;
+    const uint64_t w = sw[wslot((int)x)];
+    if (x < len) write_pair(keys, vals, start + x, (uint32_t)t, w);
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
 // ---- long segments: merge sort in LDS, MSD split beyond NV -----------------------
@@ -856,9 +901,11 @@ __global__ __launch_bounds__(LT) void k_seg_sort(const uint32_t *ranges, uint64_
   __shared__ SplitLds sl;
   if (*overflow) return;
   {
+    static_assert((LT / WAVE) * WS_LDS <= NV_PHYS, "wave-sort LDS regions exceed the sort buffer");
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
+    uint64_t *sw = s + wave * WS_LDS;
     for (int t = (int)blockIdx.x * (LT / WAVE) + wave; t < tiles; t += (int)gridDim.x * (LT / WAVE))
-      wave_sort_tile(ranges, words, keys, vals, t);
+      wave_sort_tile(ranges, words, keys, vals, t, sw);
   }
   const int nh = (int)live[1], nall = nh + (int)live[2];
   if (nall == 0) return;
@@ -987,7 +1034,7 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
       hipLaunchKernelGGL(k_tile_count, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, ws.cursor);
   }
   if (tiles <= TILE_SCAN1_MAX) {
-    hipLaunchKernelGGL(k_tile_scan1, dim3(1), dim3(SCAN_BLOCK), 0, stream, ws.cursor, (int)tiles, capacity, num_pairs,
+    hipLaunchKernelGGL(k_tile_scan1, dim3(1), dim3(TS_THREADS), 0, stream, ws.cursor, (int)tiles, capacity, num_pairs,
                        overflow, ws.live, ranges, ws.list);
   } else {
     hipLaunchKernelGGL(k_scan_reduce, dim3(nscan), dim3(SCAN_BLOCK), 0, stream, ws.cursor, tiles, ws.block_sums);

@@ -793,7 +793,7 @@ __device__ __forceinline__ double cam_weight(const ViewDev &c, const ProjBwdArgs
 // views; when the call covers one view, the same pass forms that view's camera
 // gradient (Pulsar B.2: dL/dR = sum_k dq_k p_k^T, dL/dt = sum_k dq_k) in fp64
 // registers. Each block stores its twelve sums and k_cam_final adds them up in
-// block order (deterministic, and no atomics contend on twelve outputs; a
+// a fixed order (deterministic, and no atomics contend on twelve outputs; a
 // device-scope fence per block would write back the L2 of every XCD).
 template <int CM>
 __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs P, int vbeg, int vend, int cam_view) {
@@ -890,28 +890,45 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
   }
 }
 
-// One block: the per-block camera sums of k_sphere_grads, added in block order.
-__global__ __launch_bounds__(256) void k_cam_final(ProjBwdArgs P, int nparts, int cam_view) {
-  __shared__ double s_red[12][4];
-  double cam[12];
+// One block: the per-block camera sums of k_sphere_grads (nparts rows of twelve
+// doubles) added in a fixed order. With 768 threads (a multiple of twelve),
+// thread t reads the doubles e = t + 768 k, all of sum t mod 12: every wave
+// load covers one contiguous 512-byte run (a row of twelve per thread touched
+// ~48 cache lines per wave load) and the sixteen loads of a pass are
+// independent, so they are in flight together. The 768 partial sums then fold
+// in LDS by strides of 192, 48 and 12 (each a multiple of twelve).
+constexpr int CAMF_THREADS = 768;
+constexpr int CAMF_LOADS = 16;
+
+__global__ __launch_bounds__(CAMF_THREADS) void k_cam_final(ProjBwdArgs P, int nparts, int cam_view) {
+  __shared__ double s_acc[CAMF_THREADS];
+  const int t = (int)threadIdx.x;
+  const int ne = 12 * nparts;
+  double acc = 0.0;
+  for (int e0 = t; e0 < ne; e0 += CAMF_THREADS * CAMF_LOADS) {
+    double x[CAMF_LOADS];
 #pragma unroll
-  for (int q = 0; q < 12; q++) cam[q] = 0.0;
-#pragma unroll 4
-  for (int b = threadIdx.x; b < nparts; b += blockDim.x)
+    for (int k = 0; k < CAMF_LOADS; k++) {
+      const int e = e0 + CAMF_THREADS * k;
+      x[k] = e < ne ? P.cam_part[e] : 0.0;
+    }
 #pragma unroll
-    for (int q = 0; q < 12; q++) cam[q] += P.cam_part[12 * b + q];
-  const unsigned lane = lane_id(), w = threadIdx.x / WAVE;
-#pragma unroll
-  for (int q = 0; q < 12; q++) {
-    const double t = wave_sum_f64(cam[q]);
-    if (lane == 0) s_red[q][w] = t;
+    for (int k = 0; k < CAMF_LOADS; k++) acc += x[k];
   }
+  s_acc[t] = acc;
   __syncthreads();
-  if (threadIdx.x < 12) {
-    const int q = threadIdx.x;
-    const double t = s_red[q][0] + s_red[q][1] + s_red[q][2] + s_red[q][3];
-    if (q < 9 && P.gR) P.gR[9 * cam_view + q] += (float)t;
-    if (q >= 9 && P.gt) P.gt[3 * cam_view + (q - 9)] += (float)t;
+#pragma unroll
+  for (int h = CAMF_THREADS / 4; h >= 12; h /= 4) {
+    double s = 0.0;
+    if (t < h) s = s_acc[t] + s_acc[t + h] + s_acc[t + 2 * h] + s_acc[t + 3 * h];
+    __syncthreads();
+    if (t < h) s_acc[t] = s;
+    __syncthreads();
+  }
+  if (t < 12) {
+    const double tot = s_acc[t];
+    if (t < 9 && P.gR) P.gR[9 * cam_view + t] += (float)tot;
+    if (t >= 9 && P.gt) P.gt[3 * cam_view + (t - 9)] += (float)tot;
   }
 }
 
@@ -1262,7 +1279,7 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
       } else {
         hipLaunchKernelGGL(k_sphere_grads<8>, dim3(nb), dim3(256), 0, stream, vt, P, vbeg, vend, cam_view);
       }
-      if (cam_view >= 0) hipLaunchKernelGGL(k_cam_final, dim3(1), dim3(256), 0, stream, P, (int)nb, cam_view);
+      if (cam_view >= 0) hipLaunchKernelGGL(k_cam_final, dim3(1), dim3(CAMF_THREADS), 0, stream, P, (int)nb, cam_view);
       if (cam && vend - vbeg > 1)
         hipLaunchKernelGGL(k_cam_grad_sphere, dim3(min(nb, 512u), vend - vbeg), dim3(256), 0, stream, vt, P, vbeg);
     }
