@@ -800,11 +800,21 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
   // Outputs of 256 spheres go through LDS and leave as contiguous runs: from
   // registers, the 3- (and C-) float rows of neighbouring lanes would be written
   // one float per instruction, a third of each line at a time.
+  // Up to four channels (there C = CM) the accumulator rows (5 + C doubles) of
+  // the 256 spheres come in through LDS too: RL lanes per row, each wave load
+  // one contiguous run, all of a thread's loads in flight together; read
+  // straight, a lane's row sat 64 bytes from its neighbour's and every load
+  // touched 32 lines. One pad double per staged row spreads the per-lane row
+  // reads over the banks.
   constexpr int CS = CM <= 4 ? CM : 1;         // features staged up to four channels
+  constexpr bool STAGE = CM <= 4;
+  constexpr int RS = STAGE ? 5 + CM + 1 : 1;   // staged row stride (doubles)
+  constexpr int RL = 5 + CM <= 8 ? 8 : 16;     // lanes per staged row; also the loads per thread
   __shared__ double s_red[12][4];
   __shared__ float s_pos[256 * 3];
   __shared__ float s_feat[256 * CS];
-  const int S = 5 + P.C;
+  __shared__ double s_row[256 * RS];
+  const int S = STAGE ? 5 + CM : 5 + P.C;
   double cam[12];
 #pragma unroll
   for (int q = 0; q < 12; q++) cam[q] = 0.0;
@@ -812,16 +822,40 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
     const int i = i0 + (int)threadIdx.x;
     const int nb = min(256, P.n - i0);
     double dp[3] = {0, 0, 0}, dr = 0, dop = 0, nrm = 1.0;
-    if (i < P.n) {
-      for (int v = vbeg; v < vend; v++) {
-        const ViewDev &c = vt.v[v];
-        const double *A = P.accg + ((size_t)v * P.n + i) * S;     // zero for culled records
+    double fs[CS];
+#pragma unroll
+    for (int ch = 0; ch < CS; ch++) fs[ch] = 0.0;
+    for (int v = vbeg; v < vend; v++) {
+      const ViewDev &c = vt.v[v];
+      const double *A;
+      if constexpr (STAGE) {
+        const double *src = P.accg + ((size_t)v * P.n + i0) * S;   // zero for culled records
+        constexpr int RP = 256 / RL;              // rows per pass
+        const int k = (int)(threadIdx.x % RL), r0 = (int)(threadIdx.x / RL);
+        const double *sp = src + r0 * S + k;
+        double x[RL];
+#pragma unroll
+        for (int q = 0; q < RL; q++) x[q] = r0 + RP * q < nb && k < S ? sp[RP * S * q] : 0.0;
+#pragma unroll
+        for (int q = 0; q < RL; q++)
+          if (k < S) s_row[(r0 + RP * q) * RS + k] = x[q];
+        __syncthreads();
+        A = s_row + threadIdx.x * RS;
+      } else {
+        A = P.accg + ((size_t)v * P.n + i) * S;
+      }
+      if (i < P.n) {
         const double dq[3] = {A[0], A[1], A[2]};
 #pragma unroll
         for (int a = 0; a < 3; a++)
           dp[a] += (double)c.R[a] * dq[0] + (double)c.R[3 + a] * dq[1] + (double)c.R[6 + a] * dq[2];   // R^T dq
         dr += A[3];
         dop += A[4];
+        if constexpr (STAGE) {
+#pragma unroll
+          for (int ch = 0; ch < CS; ch++)
+            if (ch < P.C) fs[ch] += A[5 + ch];
+        }
         if (v == cam_view) {
           const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
           const double cw = cam_weight(c, P, (size_t)v * P.n + i);
@@ -834,6 +868,9 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
           }
         }
       }
+      if constexpr (STAGE) __syncthreads();   // staged rows read before the next view's
+    }
+    if (i < P.n) {
       if (P.cnt) {
         // averaged over the pixels that recorded the sphere (all views of the call)
         uint32_t ct = 0;
@@ -856,13 +893,11 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
       for (int j = threadIdx.x; j < 3 * nb; j += 256) out[j] = P.accumulate ? out[j] + s_pos[j] : s_pos[j];
     }
     if (P.gfeat) {
-      if (CM <= 4) {
+      if constexpr (STAGE) {
         if (i < P.n)
-          for (int ch = 0; ch < P.C; ch++) {
-            double f = 0;
-            for (int v = vbeg; v < vend; v++) f += P.accg[((size_t)v * P.n + i) * S + 5 + ch];
-            s_feat[P.C * threadIdx.x + ch] = (float)(f * nrm);
-          }
+#pragma unroll
+          for (int ch = 0; ch < CS; ch++)
+            if (ch < P.C) s_feat[P.C * threadIdx.x + ch] = (float)(fs[ch] * nrm);
         __syncthreads();
         float *out = P.gfeat + (size_t)P.C * i0;
         for (int j = threadIdx.x; j < P.C * nb; j += 256) out[j] = P.accumulate ? out[j] + s_feat[j] : s_feat[j];
