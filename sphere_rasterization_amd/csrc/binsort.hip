@@ -23,6 +23,7 @@
 //                                 tile's pair total (16 waves per 64 columns)
 //   k_tile_scan1                  exclusive scan over tiles (one workgroup):
 //                                 tile ranges, pair total, overflow, tile starts
+//                                 (one-view calls: inside k_tscatter instead)
 //   k_tscatter                    each pair's word into its tile's segment, at
 //                                 tile start + chunk prefix + a rank from an LDS
 //                                 atomic
@@ -529,19 +530,105 @@ __global__ __launch_bounds__(CS_WAVES * 64) void k_col_scan(ViewTable vt, MatTab
   }
 }
 
+// Where the tile scan writes its results (see k_tile_scan1).
+struct ScanOut {
+  long long capacity;
+  int64_t *num_pairs;
+  int32_t *overflow;
+  uint32_t *live;
+  uint32_t *ranges;
+  uint32_t *list;
+};
+
+constexpr int FS_MAX = 8;                       // tiles per thread in the fused tile scan (T <= 8192)
+
+// The tile scan of k_tile_scan1 inside every scatter workgroup of a one-view
+// call with T <= FS_MAX * TH_THREADS tiles (a one-workgroup kernel costs ~6 us
+// of launch and latency; the counts come from L2). Every workgroup scans all T counts; s_base[t]
+// gets tile start + this chunk's row entry; workgroup 0 writes the pair total,
+// the overflow flag and the list counters, and workgroup w the tile ranges and
+// long-segment list entries of tiles [w T / nw, (w + 1) T / nw). Every
+// workgroup reaches the same overflow decision; returns false on overflow.
+__device__ bool fused_tile_scan(const uint32_t *cnt, int T, const uint32_t *row, uint32_t *s_base, const ScanOut &so,
+                                int w, int nw) {
+  const int ipt = (T + TH_THREADS - 1) / TH_THREADS;
+  const int t0 = (int)threadIdx.x * ipt;
+  uint32_t x[FS_MAX];
+  unsigned long long part = 0;
+  uint32_t sum = 0, nh = 0, nm = 0;
+#pragma unroll
+  for (int r = 0; r < FS_MAX; r++) {
+    x[r] = r < ipt && t0 + r < T ? cnt[t0 + r] : 0u;
+    part += x[r];
+    sum += x[r];
+    nh += x[r] > (uint32_t)NV ? 1u : 0u;
+    nm += (x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV) ? 1u : 0u;
+  }
+  unsigned long long total;
+  block_exclusive_scan<unsigned long long, TH_THREADS>(part, &total);
+  const bool of = total > (unsigned long long)so.capacity;
+  if (w == 0 && threadIdx.x == 0) {
+    *so.num_pairs = (int64_t)total;
+    *so.overflow = of ? 1 : 0;
+    so.live[0] = of ? 0u : (uint32_t)total;
+  }
+  if (of) return false;
+  // below the capacity (< 2^32) from here on, and the list counts are at most
+  // T < 2^16: the packed fields never carry into each other
+  const unsigned long long packed =
+      (unsigned long long)sum | ((unsigned long long)nh << 32) | ((unsigned long long)nm << 48);
+  unsigned long long tot;
+  const unsigned long long pre = block_exclusive_scan<unsigned long long, TH_THREADS>(packed, &tot);
+  uint32_t run = (uint32_t)pre, ph = (uint32_t)((pre >> 32) & 0xffffu), pm = (uint32_t)(pre >> 48);
+  const int s0 = (int)((long long)w * T / nw), s1 = (int)((long long)(w + 1) * T / nw);
+#pragma unroll
+  for (int r = 0; r < FS_MAX; r++) {
+    const int t = t0 + r;
+    if (r < ipt && t < T) {
+      s_base[t] = run + row[t];
+      if (t >= s0 && t < s1) {
+        so.ranges[2 * t] = x[r] ? run : 0u;
+        so.ranges[2 * t + 1] = x[r] ? run + x[r] : 0u;
+        if (x[r] > (uint32_t)NV)
+          so.list[ph] = (uint32_t)t;
+        else if (x[r] > (uint32_t)SEG_WAVE)
+          so.list[T + pm] = (uint32_t)t;
+      }
+      ph += x[r] > (uint32_t)NV ? 1u : 0u;
+      pm += (x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV) ? 1u : 0u;
+    }
+    run += x[r];
+  }
+  if (w == 0 && threadIdx.x == 0) {
+    so.live[1] = (uint32_t)((tot >> 32) & 0xffffu);
+    so.live[2] = (uint32_t)(tot >> 48);
+    so.live[3] = 0u;
+  }
+  return true;
+}
+
 // Same chunks as k_thist: words to tile start + chunk prefix + LDS rank.
+// FUSED (one view): tile_start holds the tile counts and the tile scan runs
+// here (fused_tile_scan); otherwise k_tile_scan1 has turned them into starts.
+template <bool FUSED>
 __global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
                                                    const uint32_t *counts, const uint32_t *M,
                                                    const uint32_t *tile_start, const int32_t *overflow,
-                                                   uint64_t *words) {
+                                                   uint64_t *words, ScanOut so) {
   extern __shared__ uint32_t s_base[];
   __shared__ HeavyLds hl;
-  if (*overflow) return;
+  if constexpr (!FUSED) {
+    if (*overflow) return;
+  }
   const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
   const ViewDev &cv = vt.v[v];
   const int T = cv.TW * cv.TH;
   const uint32_t *row = M + mat_index(mt, cv, v, chunk_row(chunk, nchunk), 0);
-  for (int t = threadIdx.x; t < T; t += TH_THREADS) s_base[t] = tile_start[cv.tile_off + t] + row[t];
+  if constexpr (FUSED) {
+    if (!fused_tile_scan(tile_start, T, row, s_base, so, chunk, nchunk)) return;
+  } else {
+    for (int t = threadIdx.x; t < T; t += TH_THREADS) s_base[t] = tile_start[cv.tile_off + t] + row[t];
+  }
   ChunkRecs cr;
   const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
   load_chunk(bin, counts, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
@@ -1033,7 +1120,12 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
     if (rec_blocks)
       hipLaunchKernelGGL(k_tile_count, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, ws.cursor);
   }
-  if (tiles <= TILE_SCAN1_MAX) {
+  // one view of at most FS_MAX * TH_THREADS tiles: the tile scan runs inside k_tscatter
+  const bool fused = cp.lds && vt.n == 1 && tiles <= (long long)FS_MAX * TH_THREADS;
+  const ScanOut so{capacity, num_pairs, overflow, ws.live, ranges, ws.list};
+  if (fused) {
+    // nothing here
+  } else if (tiles <= TILE_SCAN1_MAX) {
     hipLaunchKernelGGL(k_tile_scan1, dim3(1), dim3(TS_THREADS), 0, stream, ws.cursor, (int)tiles, capacity, num_pairs,
                        overflow, ws.live, ranges, ws.list);
   } else {
@@ -1044,9 +1136,12 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
                        overflow, ranges, ws.live, ws.list);
   }
   SPLAT_LAUNCH_CHECK();
-  if (cp.lds) {
-    hipLaunchKernelGGL(k_tscatter, dim3((unsigned)(vt.n * cp.nchunk)), dim3(TH_THREADS), lds_bytes, stream, vt, cp.mt,
-                       n, cp.nchunk, L.bin, counts, ws.mat, ws.cursor, overflow, ws.words);
+  if (fused) {
+    hipLaunchKernelGGL(k_tscatter<true>, dim3((unsigned)cp.nchunk), dim3(TH_THREADS), lds_bytes, stream, vt, cp.mt, n,
+                       cp.nchunk, L.bin, counts, ws.mat, ws.cursor, overflow, ws.words, so);
+  } else if (cp.lds) {
+    hipLaunchKernelGGL(k_tscatter<false>, dim3((unsigned)(vt.n * cp.nchunk)), dim3(TH_THREADS), lds_bytes, stream, vt,
+                       cp.mt, n, cp.nchunk, L.bin, counts, ws.mat, ws.cursor, overflow, ws.words, so);
   } else if (rec_blocks) {
     hipLaunchKernelGGL(k_bucket, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, overflow, ws.cursor,
                        ws.words);
