@@ -319,23 +319,27 @@ __device__ __forceinline__ int chunk_row(int chunk, int nchunk) {
 }
 
 // Records of one chunk, loaded up front (every thread TH_RPT of them, coalesced).
+// A record's pair count is its rectangle's tile count, ntx (ty1 - ty0 + 1), the
+// value splat_project also stores in pair_counts (culled records are all zero):
+// one load per record instead of the count and then the record.
 struct ChunkRecs {
   uint32_t cnt[TH_RPT];
   BinRec b[TH_RPT];
 };
 
-__device__ __forceinline__ void load_chunk(const BinRec *bin, const uint32_t *counts, long long rec0, int nvalid,
-                                           ChunkRecs &cr) {
+__device__ __forceinline__ void load_chunk(const BinRec *bin, long long rec0, int nvalid, ChunkRecs &cr) {
 #pragma unroll
   for (int r = 0; r < TH_RPT; r++) {
     const int j = r * TH_THREADS + (int)threadIdx.x;
-    cr.cnt[r] = j < nvalid ? counts[rec0 + j] : 0u;
+    if (j < nvalid) {
+      cr.b[r] = bin[rec0 + j];
+    } else {
+      cr.b[r].key = 0u; cr.b[r].tx0 = 0; cr.b[r].ntx = 0; cr.b[r].ty0 = 0; cr.b[r].ty1 = 0; cr.b[r].pad = 0u;
+    }
   }
 #pragma unroll
-  for (int r = 0; r < TH_RPT; r++) {
-    const int j = r * TH_THREADS + (int)threadIdx.x;
-    if (cr.cnt[r]) cr.b[r] = bin[rec0 + j];
-  }
+  for (int r = 0; r < TH_RPT; r++)
+    cr.cnt[r] = (uint32_t)cr.b[r].ntx * (uint32_t)((int)cr.b[r].ty1 - (int)cr.b[r].ty0 + 1);
 }
 
 // View-local tile ids of one record's rectangle.
@@ -470,7 +474,7 @@ __device__ __forceinline__ void chunk_pairs(const ViewDev &cv, const ChunkRecs &
 
 // grid: n_views * nchunk workgroups of TH_THREADS; dynamic LDS: 4 * max tiles per view.
 __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
-                                                const uint32_t *counts, uint32_t *M) {
+                                                uint32_t *M) {
   extern __shared__ uint32_t s_cnt[];
   __shared__ HeavyLds hl;
   const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt,
   for (int t = threadIdx.x; t < T; t += TH_THREADS) s_cnt[t] = 0;
   ChunkRecs cr;
   const int nvalid = min(TH_CHUNK, n - chunk * TH_CHUNK);
-  load_chunk(bin, counts, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);
+  load_chunk(bin, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);
   __syncthreads();
   chunk_pairs(cv, cr, hl, [&](uint32_t lt, uint32_t, uint32_t) { atomicAdd(&s_cnt[lt], 1u); });
   __syncthreads();
@@ -612,7 +616,7 @@ __device__ bool fused_tile_scan(const uint32_t *cnt, int T, const uint32_t *row,
 // here (fused_tile_scan); otherwise k_tile_scan1 has turned them into starts.
 template <bool FUSED>
 __global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
-                                                   const uint32_t *counts, const uint32_t *M,
+                                                   const uint32_t *M,
                                                    const uint32_t *tile_start, const int32_t *overflow,
                                                    uint64_t *words, ScanOut so) {
   extern __shared__ uint32_t s_base[];
@@ -631,7 +635,7 @@ __global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable 
   }
   ChunkRecs cr;
   const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
-  load_chunk(bin, counts, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
+  load_chunk(bin, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
   __syncthreads();
   chunk_pairs(cv, cr, hl, [&](uint32_t lt, uint32_t slot, uint32_t key) {
     words[atomicAdd(&s_base[lt], 1u)] = ((uint64_t)key << 32) | (uint64_t)(uint32_t)(rec0 + slot);
@@ -1112,7 +1116,7 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
   if (cp.lds) {
     const unsigned grid = (unsigned)(vt.n * cp.nchunk);
     hipLaunchKernelGGL(k_thist, dim3(grid), dim3(TH_THREADS), lds_bytes, stream, vt, cp.mt, n, cp.nchunk, L.bin,
-                       counts, ws.mat);
+                       ws.mat);
     hipLaunchKernelGGL(k_col_scan, dim3((unsigned)((tiles + 63) / 64)), dim3(CS_WAVES * 64), 0, stream, vt, cp.mt,
                        cp.nchunk, ws.mat, ws.cursor);
   } else {
@@ -1138,10 +1142,10 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
   SPLAT_LAUNCH_CHECK();
   if (fused) {
     hipLaunchKernelGGL(k_tscatter<true>, dim3((unsigned)cp.nchunk), dim3(TH_THREADS), lds_bytes, stream, vt, cp.mt, n,
-                       cp.nchunk, L.bin, counts, ws.mat, ws.cursor, overflow, ws.words, so);
+                       cp.nchunk, L.bin, ws.mat, ws.cursor, overflow, ws.words, so);
   } else if (cp.lds) {
     hipLaunchKernelGGL(k_tscatter<false>, dim3((unsigned)(vt.n * cp.nchunk)), dim3(TH_THREADS), lds_bytes, stream, vt,
-                       cp.mt, n, cp.nchunk, L.bin, counts, ws.mat, ws.cursor, overflow, ws.words, so);
+                       cp.mt, n, cp.nchunk, L.bin, ws.mat, ws.cursor, overflow, ws.words, so);
   } else if (rec_blocks) {
     hipLaunchKernelGGL(k_bucket, dim3(rec_blocks), dim3(256), 0, stream, vt, n, L.bin, counts, overflow, ws.cursor,
                        ws.words);
