@@ -157,7 +157,10 @@ size_t splat_bwd_workspace_bytes(int n_views, int n, int channels);
 /* Project every (view, primitive): the per-primitive "Step 0" of Pulsar appendix B.1.1
  * (enclosing rectangle, depth, blending constants) and EWA splatting for Gaussians.
  * proj: [splat_projected_bytes] opaque records. pair_counts: [n_views*n] uint32, the
- * number of tiles each record overlaps (0 = culled: behind znear, degenerate, off image). */
+ * number of tiles each record overlaps (0 = culled: behind znear, degenerate, off image).
+ * Spheres with up to four channels: the records also keep a copy of each primitive's
+ * features (read from prims->feat here), which splat_render_fwd and splat_render_bwd
+ * use; re-project after changing the features. */
 int splat_project(const splat_camera *cams, int n_views, const splat_prims *prims,
                   const splat_params *prm, void *proj, uint32_t *pair_counts, hipStream_t stream);
 

@@ -89,8 +89,8 @@ __device__ void write_rect(const ProjLayout &L, long long k, uint32_t *counts, c
 }
 
 struct PrimArgs {
-  int kind, n;
-  const float *pos, *scale, *rot, *opacity, *depth;
+  int kind, n, C;
+  const float *pos, *scale, *rot, *opacity, *depth, *feat;
   double gamma, alpha_min;
   int max_shift;      // spheres: draw records carry log-weights (see below)
 };
@@ -158,8 +158,20 @@ __device__ __forceinline__ bool project_one(const ViewDev &c, const PrimArgs &P,
     d.u = orth ? q[0] : q[0] / q[2];
     d.v = orth ? q[1] : q[1] / q[2];
     d.a = orth ? 1.0 / (re * re) : q[2] * q[2] / (re * re);
-    d.b = u;                           // projected centre (pixels), informational
-    d.c = v;
+    if (P.C <= SPLAT_REC_FEAT) {
+      // the features ride in the record: the compositors' staging then fetches one
+      // record per list entry instead of the record and a separate feature row
+      float f[SPLAT_REC_FEAT] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (P.feat)
+#pragma unroll
+        for (int ch = 0; ch < SPLAT_REC_FEAT; ch++)
+          if (ch < P.C) f[ch] = P.feat[(size_t)i * P.C + ch];
+      d.b = __builtin_bit_cast(double, make_float2(f[0], f[1]));
+      d.c = __builtin_bit_cast(double, make_float2(f[2], f[3]));
+    } else {
+      d.b = u;                         // projected centre (pixels), informational
+      d.c = v;
+    }
     if (P.max_shift) {
       // logs: ln(o exp(o zhat / gamma)) and ln(bound); the compositors blend
       // relative to a per-pixel shift, so nothing overflows for small gamma
@@ -342,6 +354,8 @@ int launch_project(const ViewTable &vt, const splat_prims *pr, double gamma, dou
   P.gamma = gamma;
   P.alpha_min = alpha_min;
   P.max_shift = max_shift;
+  P.C = pr->channels;
+  P.feat = pr->feat;
   ProjLayout L = proj_layout(proj, nrec);
   const dim3 grid((unsigned)((pr->n + 255) / 256), (unsigned)vt.n);
   if (pr->kind == SPLAT_PRIM_SPHERE)

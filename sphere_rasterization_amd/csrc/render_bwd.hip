@@ -625,7 +625,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       s_x[threadIdx.x] = make_float4(ax.z, d.w, 1.0f / ax.opac + ax.zhat * igam, ax.opac * igam);
       s_flags[threadIdx.x] = (int)ax.flags;
 #pragma unroll
-      for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      for (int ch = 0; ch < CM; ch++) {
+        if constexpr (CM <= SPLAT_REC_FEAT)
+          s_f[ch][threadIdx.x] = rec_feat(d, ch);              // here C = CM: features in the record
+        else
+          s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      }
 #pragma unroll
       for (int q = 0; q < NV; q++) s_acc[threadIdx.x][q] = 0.0f;
       s_cnt[threadIdx.x] = 0u;

@@ -97,7 +97,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       else
         t[1] = tau > 0.0f ? d.e / tau : __builtin_huge_valf();
 #pragma unroll
-      for (int ch = 0; ch < 4 * NF4 - 2; ch++) t[2 + ch] = ch < CM && ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      for (int ch = 0; ch < 4 * NF4 - 2; ch++) {
+        if constexpr (CM <= SPLAT_REC_FEAT)
+          t[2 + ch] = ch < CM ? rec_feat(d, ch) : 0.0f;       // here C = CM: features in the record
+        else
+          t[2 + ch] = ch < CM && ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      }
 #pragma unroll
       for (int f = 0; f < NF4; f++) s_e[3 + f][threadIdx.x] = make_float4(t[4 * f], t[4 * f + 1], t[4 * f + 2], t[4 * f + 3]);
       if constexpr (TOPD) {

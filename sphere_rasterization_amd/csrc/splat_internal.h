@@ -53,7 +53,9 @@ struct __align__(16) BinRec {
 //  Gaussians: projected mean (u, v), conic (a, b, c) with power = (a dx^2 + 2 b dx dy + c dy^2)/2,
 //             w = opacity, e unused.
 //  Spheres:   (u, v) = normalised centre (qx/qz, qy/qz), a = A = qz^2 / r_eff^2,
-//             (b, c) = projected centre in pixels, w = o exp(o zhat / gamma), e = stop bound.
+//             (b, c) = the features as four fp32 (up to SPLAT_REC_FEAT channels, zero
+//             padded; more channels: projected centre in pixels), w = o exp(o zhat / gamma),
+//             e = stop bound.
 // Positions and the quadratic form stay fp64: an elongated footprint makes the three
 // conic terms cancel by the covariance's condition number, and per-pixel offsets from
 // a far tile need the full mantissa.
@@ -61,6 +63,8 @@ struct __align__(16) BinRec {
 // cannot contribute (Gaussians: opacity-aware alpha support; spheres: tangent box);
 // the compositors use it to give each wave of a tile only the entries that reach
 // its quadrant.
+constexpr int SPLAT_REC_FEAT = 4;   // sphere features carried in the draw record up to this many channels
+
 struct __align__(16) DrawRec {
   double u, v;
   double a, b, c;
@@ -71,6 +75,12 @@ struct __align__(16) DrawRec {
 // Backward-only part.
 //  Gaussians: depth (range for spherical views) in x; rest unused.
 //  Spheres:   sensor-frame centre q, r_eff, opacity, zhat, flags (bit0 floored, bit1 gated).
+// Sphere feature ch kept in a draw record (channels <= SPLAT_REC_FEAT).
+__device__ __forceinline__ float rec_feat(const DrawRec &d, int ch) {
+  const float2 f = __builtin_bit_cast(float2, ch < 2 ? d.b : d.c);
+  return (ch & 1) ? f.y : f.x;
+}
+
 struct __align__(16) AuxRec {
   float x, y, z, w;
   float opac, zhat, depth, flags;
