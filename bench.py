@@ -44,13 +44,14 @@ FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
 FWD_TRAFFIC_SHA256 = "b3f01b4e147b55772b338b89e6567c0ab527f0eba9cb2e29c745c6c3aba6b267"
 # Algorithmic HBM bytes of the projection and binning stages:
-#   projection: per primitive read position, radius, opacity (20 B), write the
-#     bin, draw and aux records and the pair count (16 + 64 + 32 + 4 B)
+#   projection: per primitive read position, radius, opacity and the three
+#     features (20 + 12 B), write the bin, draw and backward records and the
+#     pair count (16 + 64 + 16 + 4 B)
 #   binning: per record the 16-byte bin record twice (counting and scatter
 #     passes, 32 B; the pair count is its rectangle's tile count); per pair the
 #     bucketed word written and read (16 B) and the sorted key and value
 #     written (12 B)
-PROJECT_BYTES_PER_PRIM = 20 + 16 + 64 + 32 + 4
+PROJECT_BYTES_PER_PRIM = 20 + 12 + 16 + 64 + 16 + 4
 BIN_BYTES_PER_REC = 32
 BIN_BYTES_PER_PAIR = 28
 

@@ -184,8 +184,8 @@ __device__ __forceinline__ bool project_one(const ViewDev &c, const PrimArgs &P,
     d.i0 = rc.i0; d.i1 = rc.i1; d.j0 = rc.j0; d.j1 = rc.j1;
     dd = d;
     AuxRec a;
-    a.x = (float)q[0]; a.y = (float)q[1]; a.z = (float)q[2]; a.w = (float)re;
-    a.opac = (float)o; a.zhat = (float)zhat; a.depth = (float)zf;
+    a.z = (float)q[2]; a.w = (float)re;
+    a.opac = (float)o;
     a.flags = (float)(floored | (gated << 1));
     aa = a;
     return true;
@@ -306,8 +306,8 @@ __device__ __forceinline__ bool project_one(const ViewDev &c, const PrimArgs &P,
   }
   dd = d;
   AuxRec a;
-  a.x = (float)depth; a.y = 0.f; a.z = 0.f; a.w = 0.f;
-  a.opac = (float)o; a.zhat = 0.f; a.depth = (float)depth; a.flags = 0.f;
+  a.z = (float)depth; a.w = 0.f;
+  a.opac = (float)o; a.flags = 0.f;
   aa = a;
   return true;
 }

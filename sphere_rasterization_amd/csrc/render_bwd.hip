@@ -375,7 +375,7 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       const Conic cn = stage_conic(d);
       s_ab[tid] = cn.ab;
       s_co[tid] = cn.co;
-      s_dep[tid] = A.aux[rid].depth;
+      s_dep[tid] = A.aux[rid].z;
 #pragma unroll
       for (int q = 0; q < 7; q++) s_ag[tid][q] = 0.0;
       s_af[tid] = 0.0f;
@@ -611,18 +611,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   const bool orth = c.kind == SPLAT_CAM_ORTHOGRAPHIC;
   const double crs = orth ? 0.0 : 1.0;
 
+  // list entries read one batch ahead (npos never passes the tile's list end)
+  uint32_t rid_next = threadIdx.x < npos ? A.vals[start + threadIdx.x] : 0u;
   for (uint32_t b = 0; b < npos; b += BT) {
     const uint32_t cnt = min((uint32_t)BT, npos - b);
+    const uint32_t rid_cur = rid_next;
+    if (b + BT + threadIdx.x < npos) rid_next = A.vals[start + b + BT + threadIdx.x];
     unsigned mask = 0;
     if (threadIdx.x < cnt) {
-      const uint32_t rid = A.vals[start + b + threadIdx.x];
+      const uint32_t rid = rid_cur;
       const DrawRec d = A.draw[rid];
       const AuxRec ax = A.aux[rid];
       const long long id = (long long)rid - vbase;
       s_rid[threadIdx.x] = rid;
       s_a[threadIdx.x] = make_double2(d.u, d.v);
       s_Ai[threadIdx.x] = make_double2(d.a, 1.0 / (double)ax.w);
-      s_x[threadIdx.x] = make_float4(ax.z, d.w, 1.0f / ax.opac + ax.zhat * igam, ax.opac * igam);
+      const float zhat = (float)(((double)c.zfar - (double)ax.z) * inv_span);
+      s_x[threadIdx.x] = make_float4(ax.z, d.w, 1.0f / ax.opac + zhat * igam, ax.opac * igam);
       s_flags[threadIdx.x] = (int)ax.flags;
 #pragma unroll
       for (int ch = 0; ch < CM; ch++) {

@@ -76,12 +76,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   const bool orth = c.kind == SPLAT_CAM_ORTHOGRAPHIC;
   bool active = tp.inside;
   const long long vbase = (long long)view * A.n;
+  // list entries are read one batch ahead: the record gathers of a batch then
+  // wait for one load, not two in a row
+  uint32_t rid_next = start + threadIdx.x < end ? A.vals[start + threadIdx.x] : 0u;
 
   for (uint32_t b = start; b < end; b += 256) {
     const uint32_t e = b + threadIdx.x;
+    const uint32_t rid_cur = rid_next;
+    if (e + 256u < end) rid_next = A.vals[e + 256u];
     unsigned mask = 0;
     if (e < end) {
-      const uint32_t rid = A.vals[e];
+      const uint32_t rid = rid_cur;
       const DrawRec d = A.draw[rid];
       const long long id = (long long)rid - vbase;
       const SphereQuad q = sphere_quad(c, tp, d);
@@ -423,7 +428,7 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
       const Conic cn = stage_conic(d);
       s_ab[tid] = cn.ab;
       s_co[tid] = cn.co;
-      s_dep[tid] = A.aux[rid].depth;
+      s_dep[tid] = A.aux[rid].z;
       mask = quadrant_mask(tp, d);
     }
     // per-quadrant lists, in batch order

@@ -73,18 +73,19 @@ struct __align__(16) DrawRec {
 };
 
 // Backward-only part.
-//  Gaussians: depth (range for spherical views) in x; rest unused.
-//  Spheres:   sensor-frame centre q, r_eff, opacity, zhat, flags (bit0 floored, bit1 gated).
+//  Gaussians: depth (range for spherical views) in z; rest unused.
+//  Spheres:   sensor-frame depth qz in z, r_eff in w, opacity, flags (bit0 floored,
+//             bit1 gated); the normalised device depth (zfar - qz) / (zfar - znear) is
+//             formed again where it is needed.
+struct __align__(16) AuxRec {
+  float z, w, opac, flags;
+};
+
 // Sphere feature ch kept in a draw record (channels <= SPLAT_REC_FEAT).
 __device__ __forceinline__ float rec_feat(const DrawRec &d, int ch) {
   const float2 f = __builtin_bit_cast(float2, ch < 2 ? d.b : d.c);
   return (ch & 1) ? f.y : f.x;
 }
-
-struct __align__(16) AuxRec {
-  float x, y, z, w;
-  float opac, zhat, depth, flags;
-};
 
 struct ProjLayout {
   BinRec *bin;
