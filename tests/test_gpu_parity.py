@@ -270,6 +270,40 @@ def test_all_culled_and_single():
     _run(sc2, 4, "single gaussian")
 
 
+def test_empty_primitive_set():
+    """No primitives: splat_project launches nothing, splat_bin_sort (the counting
+    fallback with a zero record count) reports zero pairs, a clear overflow flag and
+    empty ranges for every tile over pre-filled garbage, and the render calls reject
+    n = 0 before any launch."""
+    import ctypes as C
+    from sphere_rasterization_amd import _lib as L
+    from sphere_rasterization_amd.raster import make_cams, make_params
+    _log("[case] empty primitive set: n=0, 1 view 128x96")
+    sc = S.pulsar_spheres(n=10, width=128, height=96)
+    cams = make_cams(sc.cams)
+    prm, _ = make_params(sc.params, 3)
+    pr = L.splat_prims()
+    pr.kind, pr.n, pr.channels = S.PRIM_SPHERE, 0, 3
+    lib = L.lib()
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), None, None, stream) == L.SPLAT_OK
+    tiles = int(lib.splat_total_tiles(cams, 1))
+    assert tiles == 8 * 6
+    ranges = torch.full((tiles, 2), 7, dtype=torch.int32, device="cuda")
+    num = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    of = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+    ws_bytes = L.splat_sort_workspace_bytes(cams, 1, 0, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    rc = lib.splat_bin_sort(cams, 1, 0, None, None, 0, None, None, ranges.data_ptr(), num.data_ptr(), of.data_ptr(),
+                            ws.data_ptr(), ws_bytes, stream)
+    assert rc == L.SPLAT_OK
+    torch.cuda.synchronize()
+    assert int(num.item()) == 0 and int(of.item()) == 0
+    assert int(ranges.abs().sum().item()) == 0
+    assert lib.splat_render_fwd(cams, 1, C.byref(pr), C.byref(prm), None, None, None, of.data_ptr(), None, None,
+                                None, None, None, stream) == L.SPLAT_ERR_INVALID_ARG
+
+
 def test_overflow_then_regrow():
     sc = S.gauss3d(seed=5, n=20_000, width=256, height=256)
     _log("[case] overflow regrow")
