@@ -1184,15 +1184,20 @@ __device__ __forceinline__ void gauss_prim_grads(const ViewTable &vt, const Proj
   if (P.gop) put(P.gop, i, gop, P.accumulate);
 }
 
-// One thread per Gaussian for the geometry; the block's feature gradients
-// ([primitive][channel], views summed) then go element by element, coalesced.
+// One thread per Gaussian for the geometry (fp64 chain rule, ~220 VGPRs: two
+// waves per SIMD).
 __global__ __launch_bounds__(256) void k_proj_bwd_gauss(ViewTable vt, ProjBwdArgs P, int vbeg, int vend) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < P.n) gauss_prim_grads(vt, P, vbeg, vend, i);
-  if (!P.gfeat) return;
-  const size_t e1 = (size_t)min((long long)(blockIdx.x + 1) * blockDim.x, (long long)P.n) * P.C;
+}
+
+// Feature gradients of Gaussians ([primitive][channel], the call's pinhole views
+// summed), element by element and coalesced. A kernel of their own: inside the
+// geometry kernel this stream (fp64 sums in, fp32 gradients out; 768 MB for 2M
+// primitives with 32 channels) ran at that kernel's two waves per SIMD.
+__global__ __launch_bounds__(256) void k_feat_grads_gauss(ViewTable vt, ProjBwdArgs P, int vbeg, int vend) {
   const size_t plane = (size_t)P.n * P.C;
-  for (size_t e = (size_t)blockIdx.x * blockDim.x * P.C + threadIdx.x; e < e1; e += blockDim.x) {
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < plane; e += (size_t)gridDim.x * blockDim.x) {
     double sum = 0;
     for (int v = vbeg; v < vend; v++)
       if (vt.v[v].kind != SPLAT_CAM_SPHERICAL) sum += P.accf[(size_t)v * plane + e];
@@ -1328,7 +1333,14 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
       if (cam && vend - vbeg > 1)
         hipLaunchKernelGGL(k_cam_grad_sphere, dim3(min(nb, 512u), vend - vbeg), dim3(256), 0, stream, vt, P, vbeg);
     }
-    else hipLaunchKernelGGL(k_proj_bwd_gauss, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
+    else {
+      hipLaunchKernelGGL(k_proj_bwd_gauss, grid, dim3(256), 0, stream, vt, P, vbeg, vend);
+      if (P.gfeat) {
+        const long long ne = (long long)pr->n * A.C;
+        const unsigned fb = (unsigned)min((ne + 255) / 256, 8192ll);
+        if (ne > 0) hipLaunchKernelGGL(k_feat_grads_gauss, dim3(fb), dim3(256), 0, stream, vt, P, vbeg, vend);
+      }
+    }
     SPLAT_LAUNCH_CHECK();
   }
   return SPLAT_OK;
