@@ -132,13 +132,19 @@ typedef struct {
  * call's views that recorded it among their top_k; each sphere's camera (R, t)
  * contribution is divided by its projected area in pixels, pi (fx r_eff / qz)
  * (fy r_eff / qz) (orthographic: pi (fx r_eff)(fy r_eff)), and by 1e-3. cam_K
- * stays the raw sum. normalize = 1 with Gaussians returns SPLAT_ERR_UNSUPPORTED. */
+ * stays the raw sum. normalize = 1 with Gaussians returns SPLAT_ERR_UNSUPPORTED.
+ * sums_cleared = 1 (spheres only, otherwise ignored): the caller states that the
+ * splat_render_fwd call before this one on the stream was given this call's workspace
+ * (so it cleared the sums the reverse pass accumulates into) and that no
+ * splat_render_bwd has used the workspace since; the call then skips that clearing.
+ * Stating it falsely gives wrong gradients; 0 is always correct. */
 typedef struct {
   float *pos, *scale, *rot, *opacity, *feat;
   float *cam_R, *cam_t;
   float *cam_K;
   int32_t accumulate;
   int32_t normalize;
+  int32_t sums_cleared;
 } splat_grads;
 
 /* ---- size queries (host only, no device work) ---------------------------- */
@@ -188,12 +194,19 @@ int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *pro
  *     the first top_k contributing spheres, its index into the sorted keys/vals arrays of
  *     splat_bin_sort (-1 padded); vals[index] - view*n is the primitive id. Together they
  *     are the backward buffer of Pulsar B.1.4. Sphere outputs need capacity < 2^31.
- *     T_final/last may be NULL for spheres, norm/topk for Gaussians. */
+ *     T_final/last may be NULL for spheres, norm/topk for Gaussians.
+ * bwd_workspace (optional, spheres; NULL, and ignored for Gaussians): the workspace of the
+ *   splat_render_bwd call that follows on this stream, bwd_ws_bytes >=
+ *   splat_bwd_workspace_bytes, 16-byte aligned. The forward then also clears the sums the
+ *   reverse pass accumulates into, in workgroups appended to its grid that run while its
+ *   longest tiles finish; that call can then pass splat_grads.sums_cleared = 1 and skip
+ *   its own clearing. Errors: SPLAT_ERR_CAPACITY (too small), SPLAT_ERR_INVALID_ARG
+ *   (misaligned). */
 int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *prims,
                      const splat_params *prm, const void *proj, const uint32_t *vals,
                      const uint32_t *tile_ranges, const int32_t *overflow, float *img,
                      float *T_final, uint32_t *last, float *norm, int32_t *topk,
-                     hipStream_t stream);
+                     void *bwd_workspace, size_t bwd_ws_bytes, hipStream_t stream);
 
 /* Reverse pass for views [view_begin, view_begin + view_count): per-pixel gradients
  * reduced per primitive within each wavefront before global atomics, then the chain

@@ -48,7 +48,7 @@ class splat_grads(C.Structure):
     _fields_ = [("pos", C.c_void_p), ("scale", C.c_void_p), ("rot", C.c_void_p),
                 ("opacity", C.c_void_p), ("feat", C.c_void_p), ("cam_R", C.c_void_p),
                 ("cam_t", C.c_void_p), ("cam_K", C.c_void_p), ("accumulate", C.c_int32),
-                ("normalize", C.c_int32)]
+                ("normalize", C.c_int32), ("sums_cleared", C.c_int32)]
 
 
 class SplatError(RuntimeError):
@@ -83,7 +83,7 @@ def lib():
         L.splat_bin_sort.argtypes = [cam_p, i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.splat_render_fwd.restype = i32
         L.splat_render_fwd.argtypes = [cam_p, i32, C.POINTER(splat_prims), C.POINTER(splat_params), vp, vp, vp,
-                                       vp, vp, vp, vp, vp, vp, vp]
+                                       vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.splat_render_bwd.restype = i32
         L.splat_render_bwd.argtypes = [cam_p, i32, i32, i32, C.POINTER(splat_prims), C.POINTER(splat_params),
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, C.POINTER(splat_grads), vp, sz, vp]
@@ -139,10 +139,10 @@ def splat_bin_sort(cams, n_views, n, proj, pair_counts, capacity, keys, vals, ti
 
 
 def splat_render_fwd(cams, n_views, prims, params, proj, vals, tile_ranges, overflow, img, T_final, last, norm, topk,
-                     stream):
+                     bwd_workspace, bwd_ws_bytes, stream):
     return _check("splat_render_fwd", lib().splat_render_fwd(cams, n_views, C.byref(prims), C.byref(params), proj,
                                                              vals, tile_ranges, overflow, img, T_final, last, norm,
-                                                             topk, stream))
+                                                             topk, bwd_workspace, bwd_ws_bytes, stream))
 
 
 def splat_render_bwd(cams, n_views, view_begin, view_count, prims, params, proj, vals, tile_ranges, overflow, img,

@@ -277,7 +277,8 @@ int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *pro
 
 int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *prims, const splat_params *prm,
                      const void *proj, const uint32_t *vals, const uint32_t *tile_ranges, const int32_t *overflow,
-                     float *img, float *T_final, uint32_t *last, float *norm, int32_t *topk, hipStream_t stream) {
+                     float *img, float *T_final, uint32_t *last, float *norm, int32_t *topk, void *bwd_workspace,
+                     size_t bwd_ws_bytes, hipStream_t stream) {
   ViewTable vt;
   int st = build_views(cams, n_views, prims ? prims->channels : 0, &vt);
   if (st) return st;
@@ -296,6 +297,20 @@ int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *p
   ProjLayout L = proj_layout(const_cast<void *>(proj), (long long)n_views * prims->n);
   A.draw = L.draw; A.aux = L.aux; A.vals = vals; A.ranges = tile_ranges; A.overflow = overflow;
   A.feat = prims->feat; A.img = img; A.T_final = T_final; A.last = last; A.norm = norm; A.topk = topk;
+  if (bwd_workspace && prims->kind == SPLAT_PRIM_SPHERE) {
+    const long long nrec = (long long)n_views * prims->n;
+    CHECK(((uintptr_t)bwd_workspace & 15u) == 0, SPLAT_ERR_INVALID_ARG, "backward workspace not 16-byte aligned");
+    CHECK(bwd_ws_bytes >= bwd_workspace_bytes(nrec, prims->channels), SPLAT_ERR_CAPACITY,
+          "backward workspace smaller than splat_bwd_workspace_bytes");
+    const AccLayout acc = acc_layout(bwd_workspace, nrec, prims->channels);
+    A.clr[0] = reinterpret_cast<uint4 *>(acc.g);        // rows of 5 + C doubles
+    A.nclr[0] = (nrec * (5 + prims->channels) * (long long)sizeof(double) + 15) / 16;
+    A.clr[1] = reinterpret_cast<uint4 *>(acc.kslot);    // intrinsic-gradient slots of every view
+    A.nclr[1] = ((long long)n_views * SPLAT_K_SLOTS * 4 * (long long)sizeof(double) + 15) / 16;
+    A.clr[2] = reinterpret_cast<uint4 *>(acc.cnt);      // recording-pixel counts
+    A.nclr[2] = (nrec * (long long)sizeof(uint32_t) + 15) / 16;
+    A.clear = 1;
+  }
   return launch_render_fwd(vt, A, prims->kind, stream);
 }
 

@@ -79,17 +79,24 @@ struct ZeroRanges {
   long long nd0, nd1, nf0, nf1, nu0;
 };
 
+constexpr int ZERO_GRID = 4096;
+
+// Grid-stride over the ranges in order (at most ZERO_GRID workgroups).
 __global__ __launch_bounds__(256) void k_zero(ZeroRanges z) {
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < z.nd0) { z.d0[i] = 0.0; return; }
-  i -= z.nd0;
-  if (i < z.nd1) { z.d1[i] = 0.0; return; }
-  i -= z.nd1;
-  if (i < z.nf0) { z.f0[i] = 0.0f; return; }
-  i -= z.nf0;
-  if (i < z.nf1) { z.f1[i] = 0.0f; return; }
-  i -= z.nf1;
-  if (i < z.nu0) z.u0[i] = 0u;
+  const long long n = z.nd0 + z.nd1 + z.nf0 + z.nf1 + z.nu0;
+  for (long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x; i0 < n;
+       i0 += (long long)gridDim.x * blockDim.x) {
+    long long i = i0;
+    if (i < z.nd0) { z.d0[i] = 0.0; continue; }
+    i -= z.nd0;
+    if (i < z.nd1) { z.d1[i] = 0.0; continue; }
+    i -= z.nd1;
+    if (i < z.nf0) { z.f0[i] = 0.0f; continue; }
+    i -= z.nf0;
+    if (i < z.nf1) { z.f1[i] = 0.0f; continue; }
+    i -= z.nf1;
+    if (i < z.nu0) z.u0[i] = 0u;
+  }
 }
 
 
@@ -777,6 +784,7 @@ struct ProjBwdArgs {
   double *cam_part;
   float *gpos, *gscale, *grot, *gop, *gfeat, *gR, *gt;
   int accumulate;
+  int cam_store;            // k_cam_final stores R, t instead of adding (nothing zeroed them)
 };
 
 __device__ __forceinline__ void put(float *p, size_t i, double x, int accumulate) {
@@ -972,8 +980,8 @@ __global__ __launch_bounds__(CAMF_THREADS) void k_cam_final(ProjBwdArgs P, int n
   }
   if (t < 12) {
     const double tot = s_acc[t];
-    if (t < 9 && P.gR) P.gR[9 * cam_view + t] += (float)tot;
-    if (t >= 9 && P.gt) P.gt[3 * cam_view + (t - 9)] += (float)tot;
+    float *o = t < 9 ? (P.gR ? P.gR + 9 * cam_view + t : nullptr) : (P.gt ? P.gt + 3 * cam_view + (t - 9) : nullptr);
+    if (o) *o = P.cam_store ? (float)tot : *o + (float)tot;
   }
 }
 
@@ -1256,7 +1264,9 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   const bool sph = pr->kind == SPLAT_PRIM_SPHERE;
   const long long r0 = (long long)vbeg * A.n, r1 = (long long)vend * A.n;
   ZeroRanges z{};
-  if (sph) {
+  if (sph && gr->sums_cleared) {
+    // the forward before this call cleared every sum of the workspace
+  } else if (sph) {
     z.d0 = A.accg + r0 * (5 + A.C);
     z.nd0 = (r1 - r0) * (5 + A.C);
     if (A.kslot) {
@@ -1273,7 +1283,9 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
     z.d1 = A.accf + r0 * A.C;
     z.nd1 = (r1 - r0) * A.C;
   }
-  if (!gr->accumulate) {
+  // one view, overwritten: the camera pass below stores R and t outright
+  const bool cam_store = sph && !gr->accumulate && vt.n == 1;
+  if (!gr->accumulate && !cam_store) {
     z.f0 = gr->cam_R;
     z.nf0 = gr->cam_R ? 9ll * vt.n : 0;
     z.f1 = gr->cam_t;
@@ -1281,7 +1293,8 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   }
 
   const long long nz = z.nd0 + z.nd1 + z.nf0 + z.nf1 + z.nu0;
-  if (nz > 0) hipLaunchKernelGGL(k_zero, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, z);
+  if (nz > 0)
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)min((nz + 255) / 256, (long long)ZERO_GRID)), dim3(256), 0, stream, z);
   SPLAT_LAUNCH_CHECK();
   const int tile_begin = vt.v[vbeg].tile_off;
   const int tile_end = vend < vt.n ? vt.v[vend].tile_off : vt.total_tiles;
@@ -1312,6 +1325,7 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   P.gpos = gr->pos; P.gscale = gr->scale; P.grot = gr->rot; P.gop = gr->opacity; P.gfeat = gr->feat;
   P.gR = gr->cam_R; P.gt = gr->cam_t;
   P.accumulate = gr->accumulate;
+  P.cam_store = cam_store ? 1 : 0;
   if (pr->n > 0) {
     dim3 grid((pr->n + 255) / 256);
     if (sph) {

@@ -6,6 +6,10 @@
 
 #define SPLAT_TOPK_MAX 8
 
+// Workgroups appended to the sphere forward's grid to clear the reverse pass's
+// sums (when the caller hands over the reverse pass's workspace).
+constexpr int FWD_CLEAR_BLOCKS = 256;
+
 struct FwdArgs {
   int n, C, top_k;
   int top_by_depth;       // spheres: record the top_k closest entry points, not the first top_k
@@ -23,6 +27,11 @@ struct FwdArgs {
   float *norm;
   int32_t *topk;
   float bg[SPLAT_MAX_CHANNELS];
+  // spheres, optional: the reverse pass's sums to clear (16-byte units; clear:
+  // FWD_CLEAR_BLOCKS workgroups after the tiles' do it)
+  int clear;
+  uint4 *clr[3];
+  long long nclr[3];
 };
 
 struct BwdArgs {

@@ -42,6 +42,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   __shared__ float4 s_e[NE][256];
   __shared__ BlockLists<256> s_l;
   if (*A.overflow) return;
+  if ((int)blockIdx.x >= vt.total_tiles) {
+    // one of FWD_CLEAR_BLOCKS workgroups after the tiles': clear the reverse
+    // pass's sums (the reverse pass then skips its clearing). Dispatched last,
+    // they run on the CUs that the longest tiles leave idle at the end.
+    const int cb = (int)blockIdx.x - vt.total_tiles;
+    const long long nthr = (long long)FWD_CLEAR_BLOCKS * blockDim.x;
+    const long long t0 = (long long)cb * blockDim.x + threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < 3; r++)
+      for (long long k = t0; k < A.nclr[r]; k += nthr) A.clr[r][k] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   const int gtile = blockIdx.x;
   const int view = view_of_tile(vt, gtile);
   const ViewDev &c = vt.v[view];
@@ -553,6 +565,7 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
 template <int CM>
 int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t stream) {
   dim3 grid(vt.total_tiles), block(256);
+  if (kind == SPLAT_PRIM_SPHERE && A.clear) grid.x += FWD_CLEAR_BLOCKS;
   if (kind == SPLAT_PRIM_SPHERE) {
     if (A.top_by_depth && A.max_shift)
       hipLaunchKernelGGL((k_fwd_sphere<CM, true, true>), grid, block, 0, stream, vt, A);

@@ -86,6 +86,7 @@ class Rasterizer:
         self.norm = torch.empty(self.total_pix, dtype=torch.float32, device=dev) if sph else None
         self.topk = torch.empty(self.total_pix * K, dtype=torch.int32, device=dev) if sph else None
         self.bwd_ws = None
+        self.sums_cleared = False   # the last forward cleared the backward's sums (spheres)
         self.capacity = 0
         self._alloc_pairs(capacity if capacity is not None else max(1024, 4 * V * n))
 
@@ -122,9 +123,14 @@ class Rasterizer:
                          _ptr(self.overflow), _ptr(self.sort_ws), self.sort_ws_bytes, _stream())
 
     def render_fwd(self):
+        # spheres: once a backward has allocated its workspace, the forward clears the
+        # sums the next backward accumulates into (the library skips its own clearing)
+        ws = self.bwd_ws if self.kind == 2 else None
         L.splat_render_fwd(self.c_cams, self.V, self.c_prims, self.c_params, _ptr(self.proj), _ptr(self.vals),
                            _ptr(self.tile_ranges), _ptr(self.overflow), _ptr(self.img), _ptr(self.T_final),
-                           _ptr(self.last), _ptr(self.norm), _ptr(self.topk), _stream())
+                           _ptr(self.last), _ptr(self.norm), _ptr(self.topk), _ptr(ws),
+                           self.bwd_ws_bytes if ws is not None else 0, _stream())
+        self.sums_cleared = ws is not None
 
     def ensure_capacity(self, slack: float = 1.25) -> bool:
         """Read the pair count (one small device->host copy); grow and re-bin on
@@ -162,6 +168,9 @@ class Rasterizer:
             setattr(g, k, _ptr(grads.get(k)))
         g.accumulate = 1 if accumulate else 0
         g.normalize = 1 if normalize else 0
+        # only the first backward after a clearing forward may skip the clearing
+        g.sums_cleared = 1 if self.sums_cleared else 0
+        self.sums_cleared = False
         L.splat_render_bwd(self.c_cams, self.V, view_begin, view_count, self.c_prims, self.c_params,
                            _ptr(self.proj), _ptr(self.vals), _ptr(self.tile_ranges), _ptr(self.overflow),
                            _ptr(self.img), _ptr(self.T_final), _ptr(self.last), _ptr(self.norm), _ptr(self.topk),

@@ -301,7 +301,7 @@ def test_empty_primitive_set():
     assert int(num.item()) == 0 and int(of.item()) == 0
     assert int(ranges.abs().sum().item()) == 0
     assert lib.splat_render_fwd(cams, 1, C.byref(pr), C.byref(prm), None, None, None, of.data_ptr(), None, None,
-                                None, None, None, stream) == L.SPLAT_ERR_INVALID_ARG
+                                None, None, None, None, 0, stream) == L.SPLAT_ERR_INVALID_ARG
 
 
 def test_overflow_then_regrow():

@@ -65,7 +65,7 @@ def test_argument_errors_are_returned_before_any_launch():
     pr.kind = 2
     prm.top_k = 9
     assert lib.splat_render_fwd(cams, 1, C.byref(pr), C.byref(prm), None, None, None, None, None, None, None, None,
-                                None, None) == L.SPLAT_ERR_INVALID_ARG
+                                None, None, 0, None) == L.SPLAT_ERR_INVALID_ARG
     lid = make_cams([S.Camera(S.CAM_SPHERICAL, 128, 32, np.eye(3), np.zeros(3), el_min_deg=-10, el_max_deg=10)])
     prm.top_k = 5
     pr.pos = pr.scale = pr.opacity = pr.feat = 8
