@@ -235,6 +235,38 @@ def test_spheres_two_views():
     _log(f"  bwd (per view) worst={bw['worst']:.3f}")
 
 
+def test_forward_clears_backward_sums():
+    """A sphere forward handed the reverse pass's workspace clears the sums it
+    accumulates into: with the workspace filled with NaN bytes before that forward,
+    the reverse pass told so (sums_cleared) gives what a self-clearing reverse pass
+    gave, for one view (camera R, t stored outright) and for two views (R, t zeroed
+    and added); the reverse pass after it clears for itself again."""
+    for views in (1, 2):
+        sc = S.pulsar_spheres(seed=33, n=40_000, width=256, height=192)
+        if views == 2:
+            c0 = sc.cams[0]
+            R1 = S._rot_y(8.0) @ np.asarray(c0.R)
+            sc.cams = [c0, S.Camera(S.CAM_PINHOLE, 224, 176, R1, [0.2, -0.1, 0.3], fx=240.0, fy=236.0, cx=110.0,
+                                    cy=90.0, znear=1.0, zfar=21.0)]
+        _log(f"[case] forward-cleared reverse sums, {views} view(s)")
+        rz = _rz(sc)
+        rz.forward()
+        assert not rz.sums_cleared                      # no workspace yet: the reverse pass clears
+        dimg = torch.randn(rz.img.shape, generator=torch.Generator(device="cuda").manual_seed(7), device="cuda")
+        want = ("pos", "scale", "opacity", "feat", "cam_R", "cam_t", "cam_K")
+        ref = {k: v.clone() for k, v in rz.backward(dimg, want=want).items()}
+        rz.bwd_ws.fill_(0xFF)                           # NaN in every fp64 sum
+        rz.forward()
+        assert rz.sums_cleared
+        for rnd in range(2):                            # skipping the clearing, then clearing again
+            got = rz.backward(dimg, want=want)
+            torch.cuda.synchronize()
+            assert not rz.sums_cleared
+            for k in want:
+                assert torch.isfinite(got[k]).all(), (views, rnd, k)
+                torch.testing.assert_close(got[k], ref[k], rtol=1e-5, atol=1e-5 * float(ref[k].abs().max()) + 1e-12)
+
+
 def test_sphere_option_edges():
     """Option corners: closest-K with top_k 1 and 8; max-shift without early stop at
     gamma = 1/250; a pinhole and an orthographic view in one call with intrinsic
