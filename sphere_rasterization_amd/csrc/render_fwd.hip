@@ -41,11 +41,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   constexpr int NE = 3 + NF4 + (TOPD ? 1 : 0);
   __shared__ float4 s_e[NE][256];
   __shared__ BlockLists<256> s_l;
-  if (*A.overflow) return;
   if ((int)blockIdx.x >= vt.total_tiles) {
     // one of FWD_CLEAR_BLOCKS workgroups after the tiles': clear the reverse
     // pass's sums (the reverse pass then skips its clearing). Dispatched last,
-    // they run on the CUs that the longest tiles leave idle at the end.
+    // they run on the CUs that the longest tiles leave idle at the end. They
+    // clear even after a pair overflow, so that the caller's word that the sums
+    // are clear always holds.
     const int cb = (int)blockIdx.x - vt.total_tiles;
     const long long nthr = (long long)FWD_CLEAR_BLOCKS * blockDim.x;
     const long long t0 = (long long)cb * blockDim.x + threadIdx.x;
@@ -54,6 +55,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       for (long long k = t0; k < A.nclr[r]; k += nthr) A.clr[r][k] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
+  if (*A.overflow) return;
   const int gtile = blockIdx.x;
   const int view = view_of_tile(vt, gtile);
   const ViewDev &c = vt.v[view];

@@ -267,6 +267,31 @@ def test_forward_clears_backward_sums():
                 torch.testing.assert_close(got[k], ref[k], rtol=1e-5, atol=1e-5 * float(ref[k].abs().max()) + 1e-12)
 
 
+def test_sphere_overflow_after_clearing_forward():
+    """A pair overflow makes the sphere forward write nothing, but its appended
+    workgroups still clear the reverse pass's sums: the reverse pass told so then
+    finds no stale sums of the step before, and every gradient is zero."""
+    sc = S.pulsar_spheres(seed=35, n=20_000, width=128, height=96)
+    _log("[case] sphere overflow after a clearing forward")
+    rz = _rz(sc)
+    rz.forward()
+    dimg = torch.randn(rz.img.shape, generator=torch.Generator(device="cuda").manual_seed(9), device="cuda")
+    want = ("pos", "scale", "opacity", "feat", "cam_R", "cam_t", "cam_K")
+    g0 = rz.backward(dimg, want=want)                  # leaves non-zero sums in the workspace
+    torch.cuda.synchronize()
+    assert float(g0["pos"].abs().max()) > 0.0
+    rz._alloc_pairs(100)
+    rz.project()
+    rz.bin_sort()
+    rz.render_fwd()
+    torch.cuda.synchronize()
+    assert int(rz.overflow.item()) == 1 and rz.sums_cleared
+    g = rz.backward(dimg, want=want)
+    torch.cuda.synchronize()
+    for k in want:
+        assert torch.isfinite(g[k]).all() and float(g[k].abs().max()) == 0.0, k
+
+
 def test_sphere_option_edges():
     """Option corners: closest-K with top_k 1 and 8; max-shift without early stop at
     gamma = 1/250; a pinhole and an orthographic view in one call with intrinsic
