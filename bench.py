@@ -38,11 +38,11 @@ OPS_PER_HIT_BASE = 5          # + one fma per channel
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 261257520
+FWD_TRAFFIC_BYTES = 261162464
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
-FWD_TRAFFIC_SHA256 = "b6455cb73f1b158794337ed08cc7d3ad442615011c79684fbad8861e68c9949b"
+FWD_TRAFFIC_SHA256 = "f010a7bd1e70e995f9315096df8a85402e7d7933133188bb498ad72e0ae1b480"
 # Algorithmic HBM bytes of the projection and binning stages:
 #   projection: per primitive read position, radius, opacity and the three
 #     features (20 + 12 B), write the bin, draw and backward records and the
