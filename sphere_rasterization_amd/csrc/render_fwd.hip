@@ -251,10 +251,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     }
     if (__syncthreads_count(active) == 0) break;
   }
-  if (!tp.inside) return;
-  const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
+  // the pixel again from the thread index: nothing of it stays live over the walk
+  // (kept live, it spilled to scratch)
+  const TilePix tq = tile_pixel(c, gtile, threadIdx.x);
+  if (!tq.inside) return;
+  const long long p = c.pix_off + (long long)tq.j * c.W + tq.i;
   const size_t plane = (size_t)c.W * c.H;
-  float *img = A.img + c.img_off + (size_t)tp.j * c.W + tp.i;
+  float *img = A.img + c.img_off + (size_t)tq.j * c.W + tq.i;
   const float inv = 1.0f / N;
 #pragma unroll
   for (int ch = 0; ch < CM; ch++)
