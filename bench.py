@@ -38,11 +38,11 @@ OPS_PER_HIT_BASE = 5          # + one fma per channel
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 261162464
+FWD_TRAFFIC_BYTES = 210637709
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
-FWD_TRAFFIC_SHA256 = "f010a7bd1e70e995f9315096df8a85402e7d7933133188bb498ad72e0ae1b480"
+FWD_TRAFFIC_SHA256 = "e8c85bf7b5fd546051e7d95c864bc7b88fbc8dcef44b7ae727f06827abbf7956"
 # Algorithmic HBM bytes of the projection and binning stages:
 #   projection: per primitive read position, radius, opacity and the three
 #     features (20 + 12 B), write the bin, draw and backward records and the
