@@ -53,6 +53,19 @@ def test_ragged_spheres():
     _run(sc, 7, "spheres 150k @1000x600 ragged")
 
 
+def test_sphere_channel_counts():
+    """Sphere features of one and four channels (carried in the draw records) and of six
+    channels (gathered from the feature array by the compositors), each against the
+    oracle, forward and reverse pass."""
+    base = S.pulsar_spheres(seed=37, n=40_000, width=200, height=150)
+    rng = np.random.default_rng(38)
+    for ch in (1, 4, 6):
+        feat = np.ascontiguousarray(rng.uniform(0.0, 1.0, size=(base.n, ch)).astype(np.float32))
+        sc = S.Scene(S.PRIM_SPHERE, base.n, ch, base.pos, base.scale, base.opacity, feat, cams=base.cams,
+                     params=base.params)
+        _run(sc, 40 + ch, f"spheres 40k @200x150, {ch} channels")
+
+
 def test_orthographic_spheres():
     # parallel projection: 300k spheres on 600x450 (ragged tiles), intrinsics gradients included
     _run(S.ortho_spheres(), 9, "spheres 300k @600x450 orthographic")
