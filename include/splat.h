@@ -70,7 +70,10 @@ typedef enum {
  *   ((px - cx)/fx, (py - cy)/fy, 0), and a sphere keeps a radius of at least 0.75 px.
  * Spherical (x forward, y left, z up; width must be a multiple of 16):
  *   u = (pi - atan2(qy, qx)) W / (2 pi), v = (el_max - atan2(qz, |q_xy|)) H / (el_max - el_min).
- * znear culls (depth <= znear); for spheres znear/zfar also normalise depth. */
+ * znear culls (depth <= znear); for spheres znear/zfar also normalise depth: a
+ * sphere view needs zfar > znear (else SPLAT_ERR_INVALID_ARG), and a sphere is
+ * culled unless its front depth qz - r_eff, rounded to fp32, lies in (znear, zfar):
+ * behind the far plane the early-stop bound would not hold (Pulsar sec. 3.2). */
 typedef struct {
   int32_t kind, width, height;
   float R[9], t[3];

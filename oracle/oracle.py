@@ -109,6 +109,8 @@ class Oracle:
         self.V = len(self.cams)
         if s.kind != 2 and any(c.kind == 2 for c in self.cams):
             raise ValueError("orthographic views are defined for spheres only")
+        if s.kind == 2 and any(not c.zfar > c.znear for c in self.cams):
+            raise ValueError("sphere views need zfar > znear (the normalised depth divides by the span)")
         self.params = params if params is not None else s.params
         self.K = self.params.top_k
         pick = lambda a, b: _d(a if a is not None else b)

@@ -212,6 +212,14 @@ static void project_one(const octx *X, int view, int i, orec *o) {
     o->r = r; o->r_eff = re; o->floored = r < rfl;
     double zf = q[2] - re;
     if (!(zf > c->znear) || !(zf > 0.0) || !isfinite(r) || !(r > 0.0)) { set_rect_empty(o); return; }
+    /* Beyond the far plane the normalised depth is negative, and a smaller
+       opacity then gives a larger weight exp(o zhat / gamma): the stop bound
+       exp(zhat(front) / gamma) would no longer bound the weights behind it
+       (Pulsar sec. 3.2, Figure 3). Such spheres lie outside the depth range the
+       normalised device depth spans and are culled; the test is on the fp32 key
+       depth, from which the bound is formed, so every drawn sphere has a
+       positive bound exponent. */
+    if (!((double)(float)zf < c->zfar)) { set_rect_empty(o); return; }
     if (ortho) {
       /* parallel projection: the sphere's outline is the circle of radius r_eff */
       double xl = c->fx * (q[0] - re) + c->cx, xh = c->fx * (q[0] + re) + c->cx;

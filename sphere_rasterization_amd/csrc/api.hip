@@ -159,7 +159,12 @@ int check_prims(const splat_prims *p, const ViewTable &vt) {
     else if (vt.v[v].kind == SPLAT_CAM_ORTHOGRAPHIC) any_orth = true;
     else any_pin = true;
   }
-  if (p->kind == SPLAT_PRIM_SPHERE) CHECK(!any_sph, SPLAT_ERR_UNSUPPORTED, "spheres need pinhole or orthographic views");
+  if (p->kind == SPLAT_PRIM_SPHERE) {
+    CHECK(!any_sph, SPLAT_ERR_UNSUPPORTED, "spheres need pinhole or orthographic views");
+    // the normalised device depth (zfar - qz) / (zfar - znear) needs a positive span
+    for (int v = 0; v < vt.n; v++)
+      CHECK(vt.v[v].zfar > vt.v[v].znear, SPLAT_ERR_INVALID_ARG, "sphere views need zfar > znear");
+  }
   else CHECK(!any_orth, SPLAT_ERR_UNSUPPORTED, "orthographic views are for spheres only");
   if (p->kind == SPLAT_PRIM_GAUSS2D) CHECK(!any_sph, SPLAT_ERR_UNSUPPORTED, "screen-space Gaussians need pinhole views");
   if (p->n == 0) return SPLAT_OK;

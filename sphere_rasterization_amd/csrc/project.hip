@@ -122,6 +122,11 @@ __device__ __forceinline__ bool project_one(const ViewDev &c, const PrimArgs &P,
     double re = r >= rfl ? r : rfl;
     double zf = q[2] - re;
     if (!(zf > (double)c.znear) || !(zf > 0.0) || !isfinite(r) || !(r > 0.0)) { write_culled(L, k, counts); return false; }
+    // beyond the far plane zhat < 0, where a lower opacity weighs more and the
+    // stop bound exp(zhat(front) / gamma) no longer bounds the spheres behind
+    // (Pulsar sec. 3.2, Figure 3): culled, tested on the fp32 key depth the
+    // bound is formed from
+    if (!((double)(float)zf < (double)c.zfar)) { write_culled(L, k, counts); return false; }
     double xl, xh, yl, yh;
     if (orth) {
       // parallel projection: the outline is the circle of radius r_eff

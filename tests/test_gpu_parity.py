@@ -53,6 +53,21 @@ def test_ragged_spheres():
     _run(sc, 7, "spheres 150k @1000x600 ragged")
 
 
+def test_spheres_behind_the_far_plane():
+    """Depths U(2, 30) against zfar = 21: spheres whose fp32 front depth is not
+    below zfar are culled on both sides (beyond it the stop bound would not hold),
+    those straddling it are drawn; forward and reverse pass."""
+    sc = S.pulsar_spheres(seed=61, n=120_000, width=320, height=240)
+    rng = np.random.default_rng(62)
+    cam = sc.cams[0]
+    z = rng.uniform(2.0, 30.0, sc.n)
+    u, v = rng.uniform(0, 320, sc.n), rng.uniform(0, 240, sc.n)
+    qs = np.stack([z * (u - cam.cx) / cam.fx, z * (v - cam.cy) / cam.fy, z], 1)
+    R, t = cam.R.astype(np.float64), cam.t.astype(np.float64)
+    sc.pos = np.ascontiguousarray(((qs - t) @ R).astype(np.float32))
+    _run(sc, 63, "spheres 120k @320x240 depths beyond zfar")
+
+
 def test_sphere_channel_counts():
     """Sphere features of one and four channels (carried in the draw records) and of six
     channels (gathered from the feature array by the compositors), each against the

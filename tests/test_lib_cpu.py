@@ -161,3 +161,18 @@ def test_small_gamma_needs_max_shift():
     pr.kind, pr.rot = 1, 8
     prm, _ = make_params(S.Params(max_shift=1), 3)
     assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_UNSUPPORTED
+
+
+def test_sphere_views_need_a_depth_span():
+    """Spheres normalise depth by zfar - znear: a view with zfar <= znear is
+    refused on the host (no launch)."""
+    from sphere_rasterization_amd.raster import make_cams, make_params
+    prm, _ = make_params(S.Params(), 3)
+    lib = L.lib()
+    pr = L.splat_prims()
+    pr.kind, pr.n, pr.channels = 2, 10, 3
+    pr.pos = pr.scale = pr.opacity = pr.feat = 8
+    for zn, zf in ((1.0, 1.0), (5.0, 2.0)):
+        cams = make_cams([S.Camera(S.CAM_PINHOLE, 64, 64, np.eye(3), np.zeros(3), fx=64.0, fy=64.0, cx=32.0,
+                                   cy=32.0, znear=zn, zfar=zf)])
+        assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_INVALID_ARG

@@ -249,18 +249,204 @@ def test_sphere_blend_is_commutative():
     np.testing.assert_allclose(other["N"], base["N"], rtol=1e-12)
 
 
-def test_sphere_early_stop_bound():
-    """|C_stop - C_nostop| <= (N_nostop - N_stop) / N_nostop * max|f - C_stop|."""
-    rng = np.random.default_rng(6)
-    sc = TS.random_spheres(rng, 4000, 64, 64, 64.0, rmin=0.02, rmax=0.3)
-    on = O.Oracle(sc).render_views()[0]
+def _sphere_walk_inputs(sc):
+    """Per sphere, from the raw inputs: sensor centre q, drawn radius r_eff, the
+    stop bound b = exp(zhat(fp32 front depth) / gamma) and the exponent of the
+    depth factor o zhat(qz) / gamma (Pulsar sec. 3.2 and appendix A), written
+    here from the definitions, not taken from the oracle's projection."""
+    cam, prm = sc.cams[0], sc.params
+    R, t = f64(cam.R), f64(cam.t)
+    q = f64(sc.pos) @ R.T + t
+    r, o = f64(sc.scale), f64(sc.opacity)
+    fmin = min(float(cam.fx), float(cam.fy))
+    ortho = cam.kind == S.CAM_ORTHO
+    rfl = np.full_like(r, 0.75 / fmin) if ortho else 0.75 * q[:, 2] / fmin
+    re = np.maximum(r, rfl)
+    front32 = (q[:, 2] - re).astype(np.float32).astype(np.float64)
+    span = float(cam.zfar) - float(cam.znear)
+    g = float(prm.gamma)
+    b = np.exp((float(cam.zfar) - front32) / span / g)
+    ex = o * (float(cam.zfar) - q[:, 2]) / span / g
+    return q, re, o, b, ex
+
+
+def _pixel_rays(cam, xs, ys):
+    x, y = (xs + 0.5 - float(cam.cx)) / float(cam.fx), (ys + 0.5 - float(cam.cy)) / float(cam.fy)
+    if cam.kind == S.CAM_ORTHO:
+        org = np.stack([x, y, np.zeros_like(x)], -1)
+        d = np.tile([0.0, 0.0, 1.0], (len(x), 1))
+    else:
+        org = np.zeros((len(x), 3))
+        d = np.stack([x, y, np.ones_like(x)], -1)
+    return org, d
+
+
+def _stop_walk(sc, orc):
+    """For every pixel, walk its tile's list (the oracle's sorted lists, pinned
+    by the lexsort and brute-force tile-list tests) with the stop rule of
+    Pulsar sec. 3.2 / Figure 3 and sec. B.1.3: stop at the first entry whose
+    bound b < tau * N, N = bg_weight + the weights composited so far.
+    Returns per pixel (row-major): the expected processed count, whether the
+    rule fired, N at the end,
+    the largest weight of any hitting sphere at or after the stop, and the
+    smallest relative gap |b - tau N| / (tau N) over the entries it tested."""
+    cam, prm = sc.cams[0], sc.params
+    W, H = cam.width, cam.height
+    q, re, o, b, ex = _sphere_walk_inputs(sc)
+    _, vals, ranges = orc.pairs()
+    tau, bgw = float(prm.tau), float(prm.bg_weight)
+    proc = np.zeros(W * H, np.int64)
+    fired = np.zeros(W * H, bool)
+    Nend = np.zeros(W * H)
+    wmax_after = np.zeros(W * H)
+    gap = np.full(W * H, np.inf)
+    for ty in range(cam.tiles_y):
+        for tx in range(cam.tiles_x):
+            s0, e0 = ranges[ty * cam.tiles_x + tx]
+            ys, xs = np.mgrid[ty * 16:min(ty * 16 + 16, H), tx * 16:min(tx * 16 + 16, W)]
+            xs, ys = xs.reshape(-1).astype(np.float64), ys.reshape(-1).astype(np.float64)
+            pix = (ys * W + xs).astype(np.int64)
+            ids = vals[s0:e0].astype(np.int64)
+            L = len(ids)
+            if L == 0:
+                proc[pix], Nend[pix] = 0, bgw
+                continue
+            org, d = _pixel_rays(cam, xs, ys)
+            e = q[ids][None, :, :] - org[:, None, :]
+            ed = np.einsum("plk,pk->pl", e, d)
+            dist2 = np.einsum("plk,plk->pl", e, e) - ed ** 2 / np.einsum("pk,pk->p", d, d)[:, None]
+            r2 = re[ids] ** 2
+            hit = dist2 < r2[None]
+            w = np.where(hit, o[ids][None] * (1.0 - dist2 / r2[None]) * np.exp(ex[ids])[None], 0.0)
+            Npre = np.cumsum(np.concatenate([np.full((len(pix), 1), bgw), w], 1), axis=1)[:, :L]
+            lim = tau * Npre
+            stop = b[ids][None] < lim
+            has = stop.any(1)
+            si = np.where(has, np.argmax(stop, 1), L)
+            proc[pix] = np.where(has, si + 1, L)
+            fired[pix] = has
+            Nend[pix] = np.where(has, Npre[np.arange(len(pix)), np.minimum(si, L - 1)], Npre[:, -1] + w[:, -1])
+            after = np.arange(L)[None] >= si[:, None]
+            wmax_after[pix] = np.where(after, w, 0.0).max(1)
+            tested = np.arange(L)[None] <= si[:, None]
+            rel = np.abs(b[ids][None] - lim) / lim
+            gap[pix] = np.where(tested, rel, np.inf).min(1)
+    return proc, fired, Nend, wmax_after, gap
+
+
+@pytest.mark.parametrize("camera", ["pinhole", "orthographic"])
+def test_sphere_stop_rule_bruteforce(camera):
+    """The oracle stops every pixel exactly where the rule b < tau N first holds
+    (every entry before it had b >= tau N at its turn), and the rule is sound:
+    every sphere at or after the stop weighs less than tau N_stop at that pixel
+    (Pulsar sec. 3.2, Figure 3: the aggregated weight bounds the remainder).
+    Dense scene with spheres behind the far plane too, so that many pixels stop
+    with spheres close behind the stopping one."""
+    rng = np.random.default_rng(61)
+    W = H = 48
+    if camera == "pinhole":
+        cam = TS.pinhole(W, H, 48.0, znear=1.0, zfar=21.0)
+        sc = TS.random_spheres(rng, 6000, W, H, 48.0, zmin=2.0, zmax=30.0, rmin=0.05, rmax=0.6, cam=cam)
+    else:
+        cam = _ortho_cam(W, H)
+        sc = _ortho_spheres(rng, 6000, W, H, rmin=0.2, rmax=1.5)
+        sc.pos[:, 2] = rng.uniform(2.0, 30.0, sc.n).astype(np.float32)
+    orc = O.Oracle(sc)
+    res = orc.render_views()[0]
+    proc, fired, Nend, wmax_after, gap = _stop_walk(sc, orc)
+    got_proc = res["processed"].reshape(-1)
+    got_N = res["N"].reshape(-1)
+    clear = gap > 1e-9                      # no bound within rounding of tau N
+    assert clear.mean() > 0.999
+    np.testing.assert_array_equal(got_proc[clear], proc[clear])
+    np.testing.assert_allclose(got_N[clear], Nend[clear], rtol=1e-10)
+    tau = float(sc.params.tau)
+    assert (wmax_after < tau * got_N).all(), "a sphere dropped by the stop outweighs tau * N"
+    # the rule fires at most pixels, with spheres close behind the stopping one:
+    # a bound 20x too small would drop a sphere of weight >= tau N somewhere
+    assert fired.mean() > 0.5
+    assert (wmax_after > 0.05 * tau * got_N).sum() > 10
+
+
+def test_sphere_stop_position_hand_built():
+    """Four spheres on the ray of pixel (7, 7), each hit at its centre (D = 1).
+    With gamma = 0.02, tau = 1e-5, znear 1, zfar 21, the weights are
+    w = exp((21 - z) / 20 / 0.02) and the bounds b = exp((21 - (z - r)) / 20 / 0.02).
+    A (z = 2) makes N ~ 4.3e20; B (z = 6.2) has b/(tau N) ~ 9.6: it is drawn;
+    C (z = 8) has b/(tau N) ~ 0.11: the pixel stops there, so C and D are not
+    composited. A bound off by a factor of 5 either way moves the stop."""
+    W = H = 16
+    cam = TS.pinhole(W, H, 16.0, znear=1.0, zfar=21.0)
+    d = np.array([(7.5 - 8.0) / 16.0, (7.5 - 8.0) / 16.0, 1.0])
+    zs = [2.0, 6.2, 8.0, 9.0]
+    p = np.stack([z * d for z in zs])
+    r = [0.5] * 4
+    f = [[1.0, 0.0], [0.0, 1.0], [0.5, 0.5], [0.25, 0.75]]
+    sc = TS.spheres(p, r, [1.0] * 4, f, [cam])
+    prm = sc.params
+    g, tau = float(prm.gamma), float(prm.tau)
+    P = f64(sc.pos)
+    zq = P[:, 2]
+    front = (zq - f64(sc.scale)).astype(np.float32).astype(np.float64)
+    w = np.exp((21.0 - zq) / 20.0 / g)
+    b = np.exp((21.0 - front) / 20.0 / g)
+    N = [1.0]
+    for k in range(4):
+        N.append(N[-1] + w[k])
+    ratios = [b[k] / (tau * N[k]) for k in range(4)]
+    assert ratios[0] > 1e10 and 5 < ratios[1] < 20 and 0.05 < ratios[2] < 0.2
+    res = O.Oracle(sc).render_views()[0]
+    assert res["processed"][7, 7] == 3 and res["ncontrib"][7, 7] == 2
+    np.testing.assert_allclose(res["N"][7, 7], N[2], rtol=1e-9)
+    col = (w[0] * f64(f[0]) + w[1] * f64(f[1])) / N[2]
+    np.testing.assert_allclose(res["img"][:, 7, 7], col, rtol=1e-9)
+    assert list(res["top"][7, 7, :3]) == [0, 1, -1]
+    # tau = 0 never stops: all four are composited
     sc.params = S.Params(tau=0.0)
-    off = O.Oracle(sc).render_views()[0]
-    assert (on["processed"] <= off["processed"]).all() and (on["processed"] < off["processed"]).any()
-    n2 = off["N"] - on["N"]
-    assert (n2 >= -1e-9 * off["N"]).all()
-    bound = n2 / off["N"] * 1.0 + 1e-12
-    assert (np.abs(on["img"] - off["img"]).max(axis=0) <= bound).all()
+    res0 = O.Oracle(sc).render_views()[0]
+    assert res0["processed"][7, 7] == 4 and res0["ncontrib"][7, 7] == 4
+    np.testing.assert_allclose(res0["N"][7, 7], N[4], rtol=1e-9)
+
+
+def test_spheres_behind_the_far_plane_are_culled():
+    """A sphere whose fp32 front depth is not below zfar is culled: there the
+    normalised depth is negative, a smaller opacity weighs more, and the stop
+    bound would not hold. A bound exp(zhat(front)/gamma) of 3.7e-6 (front at
+    zfar + span/4) would otherwise stop a background-only pixel (tau N = 1e-5)
+    ahead of a sphere of opacity 0.1 weighing ~0.03. A sphere straddling zfar
+    (front in front of it) is drawn."""
+    W = H = 16
+    cam = TS.pinhole(W, H, 16.0, znear=1.0, zfar=21.0)
+    d = np.array([(7.5 - 8.0) / 16.0, (7.5 - 8.0) / 16.0, 1.0])
+    # E: front 26 = zfar + span/4; F: o = 0.1 behind it; G: straddles zfar
+    p = np.stack([26.5 * d, 27.0 * d, 21.3 * d])
+    sc = TS.spheres(p, [0.5, 0.5, 0.5], [1.0, 0.1, 0.8], [[1.0], [0.5], [0.25]], [cam])
+    orc = O.Oracle(sc)
+    pr = orc.proj()
+    assert list(pr["valid"]) == [0, 0, 1] and list(pr["ntiles"]) == [0, 0, 1]
+    res = orc.render_views()[0]
+    zq = f64(sc.pos)[2, 2]
+    g = float(sc.params.gamma)
+    D = 1.0 - _ray_dist(f64(sc.pos)[2], cam, W, H)[7, 7] ** 2 / 0.25
+    w = float(np.float32(0.8)) * D * np.exp(float(np.float32(0.8)) * (21.0 - zq) / 20.0 / g)
+    np.testing.assert_allclose(res["img"][0, 7, 7], w * 0.25 / (1.0 + w), rtol=1e-9)
+    # the key depth decides: a front just below zfar in double that rounds to
+    # zfar in fp32 is culled as well
+    hit = None
+    for r32 in np.float32(2.0) + np.arange(64, dtype=np.float32) * np.float32(1e-5):
+        z = np.float32(21.0) + r32
+        for _ in range(8):
+            re = max(float(r32), 0.75 * float(z) / 16.0)
+            zf = float(z) - re
+            if zf < 21.0 and float(np.float32(zf)) == 21.0:
+                hit = (z, r32)
+                break
+            z = np.nextafter(z, np.float32(0.0), dtype=np.float32)
+        if hit:
+            break
+    assert hit is not None
+    one = TS.spheres(np.array([[0.0, 0.0, float(hit[0])]]), [float(hit[1])], [1.0], [[1.0]], [cam])
+    assert O.Oracle(one).proj()["valid"][0] == 0
 
 
 def test_tangent_box_contains_every_hit_pixel():
