@@ -95,7 +95,9 @@ typedef struct {
 
 /* HOST struct. Gaussian alpha blending: alpha = min(alpha_max, o exp(-power)); entries
  * with alpha < alpha_min are skipped; a pixel stops after the entry that brings its
- * transmittance below T_min. Sphere blending: w = o D exp(o zhat / gamma) with
+ * transmittance below T_min (Gaussians: T_min >= 1e-30, else SPLAT_ERR_INVALID_ARG,
+ * so that the fp32 T_final the reverse pass divides back from cannot underflow).
+ * Sphere blending: w = o D exp(o zhat / gamma) with
  * D = 1 - dist^2/r^2 (orthogonal ray distance), zhat = (zfar - qz)/(zfar - znear);
  * colour = (sum w f + bg_weight bg) / (sum w + bg_weight); a pixel stops at the first
  * sphere whose bound exp(zhat(front depth)/gamma) < tau * (sum w + bg_weight); the first

@@ -22,7 +22,12 @@ G_OFF = 8
 
 FLAG_ALPHA_MIN, FLAG_T_STOP, FLAG_CLAMP, FLAG_SPH_EDGE, FLAG_SPH_STOP = 1, 2, 4, 8, 16
 FLAG_SPH_ZTIE = 32          # closest-K recording: K-th and next entry depth nearly equal
-IMAGE_FLAGS = FLAG_ALPHA_MIN | FLAG_T_STOP | FLAG_SPH_EDGE | FLAG_SPH_STOP
+FLAG_UNRESOLVED = 64        # more near-tie decisions along one outcome than render_alts enumerates
+# near-tie decisions whose two outcomes render_alts enumerates (both are correct)
+DECISION_FLAGS = FLAG_ALPHA_MIN | FLAG_T_STOP | FLAG_SPH_EDGE | FLAG_SPH_STOP
+IMAGE_FLAGS = DECISION_FLAGS
+MAX_TIES = 3
+EPS_ALPHA = 1.5e-6          # relative error bound of an fp32 alpha (see the C source)
 
 
 def build(force: bool = True) -> str:
@@ -56,7 +61,9 @@ def lib():
         L.or_bin.restype = C.c_longlong
         L.or_bin.argtypes = [vp]
         L.or_get_pairs.argtypes = [vp, vp, vp, vp]
-        L.or_render.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.or_render.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.or_render_alts.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.or_set_branches.argtypes = [vp, vp]
         L.or_render_bruteforce.argtypes = [vp, ip, vp, vp, vp, vp]
         L.or_backward.argtypes = [vp] * 11 + [C.c_int]
         L.or_backward_mag.argtypes = [vp] * 19 + [C.c_int]
@@ -183,10 +190,46 @@ class Oracle:
         flags = np.zeros(cnt, np.int32)
         proc = np.zeros(cnt, np.int64)
         ncon = np.zeros(cnt, np.int64)
+        errb = np.zeros(cnt)
         lib().or_render(self.h, cnt, _vp(pix), _vp(img), _vp(T), _vp(last), _vp(N), _vp(top),
-                        _vp(flags), _vp(proc), _vp(ncon))
+                        _vp(flags), _vp(proc), _vp(ncon), _vp(errb))
         return dict(img=img, T=T, last=last, N=N, top=top[:, :self.K], flags=flags,
-                    processed=proc, ncontrib=ncon)
+                    processed=proc, ncontrib=ncon, errb=errb)
+
+    def render_alts(self, pix) -> dict:
+        """Every outcome of the given pixels over their near-tie decisions (both
+        outcomes of each of the first MAX_TIES ties met are correct). Arrays
+        [npix, 2^MAX_TIES, ...]; slots a >= nalt[q] are unused; mask[q, a] is the
+        flip mask that gives outcome a (0: the default outcome)."""
+        if self.npairs is None:
+            self.bin()
+        pix = np.ascontiguousarray(np.asarray(pix, dtype=np.int64))
+        cnt, NA, Cm, K = len(pix), 1 << MAX_TIES, max(self.C, 2), max(self.K, 1)
+        nalt = np.zeros(cnt, np.int32)
+        mask = np.zeros((cnt, NA), np.int32)
+        img = np.zeros((cnt, NA, Cm))
+        T = np.zeros((cnt, NA))
+        last = np.zeros((cnt, NA), np.int64)
+        N = np.zeros((cnt, NA))
+        top = np.zeros((cnt, NA, K), np.int32)
+        unres = np.zeros(cnt, np.int32)
+        if cnt:
+            lib().or_render_alts(self.h, cnt, _vp(pix), _vp(nalt), _vp(mask), _vp(img), _vp(T), _vp(last),
+                                 _vp(N), _vp(top), _vp(unres))
+        return dict(nalt=nalt, mask=mask, img=img, T=T, last=last, N=N, top=top[:, :, :self.K],
+                    unresolved=unres.astype(bool))
+
+    def set_branches(self, branch):
+        """Per global pixel, the flip mask (render_alts) the reverse pass follows;
+        None: the default outcome everywhere."""
+        if branch is None:
+            self._branch = None
+            lib().or_set_branches(self.h, None)
+            return
+        b = np.ascontiguousarray(np.asarray(branch, dtype=np.int32))
+        assert b.shape == (self.total_pix,)
+        self._branch = b
+        lib().or_set_branches(self.h, _vp(b))
 
     def render_views(self) -> list:
         """Full images per view as dicts of [C,H,W] / [H,W] arrays."""

@@ -33,15 +33,34 @@
 enum { PRIM_GAUSS2D = 0, PRIM_GAUSS3D = 1, PRIM_SPHERE = 2 };
 enum { CAM_PINHOLE = 0, CAM_SPHERICAL = 1, CAM_ORTHO = 2 };
 
-/* near-tie flag bits (per pixel) */
+/* Near ties: decisions that an fp32 evaluation of the same step may take the
+ * other way. The windows are the rounding error of such an evaluation (single
+ * precision alpha from an fp32 exponential, transmittance carried in double,
+ * the sphere normalisation summed in single precision in list order), with a
+ * margin of about two:
+ *   EPS_ALPHA   relative error of alpha = o exp(-power) with power rounded to
+ *               fp32 (|power| <= ln 255 where alpha can reach the threshold: 3.3e-7),
+ *               the exponential through exp2 of an fp32 product (3.3e-7 plus a
+ *               couple of ulps) and the product with o (6e-8): 8.5e-7 in all;
+ *   T           after entry k relative error EPS_ALPHA * sum over the unclamped
+ *               composited entries j <= k of alpha_j / (1 - alpha_j);
+ *   sphere N    relative error u * (sum over hits of N after the hit + 3 w) / N,
+ *               u = 2^-24 (sequential fp32 sum of fp32 products), plus one
+ *               rounding of the bound and one of its division by tau.
+ * A pixel's flags say which kinds of tie it met. */
 enum {
-  FLAG_ALPHA_MIN = 1,   /* an alpha within 1e-5 (relative) of the skip threshold */
-  FLAG_T_STOP = 2,      /* transmittance within 2e-4 (relative) of the stop threshold */
-  FLAG_CLAMP = 4,       /* opacity*G within 1e-5 (relative) of the 0.99 clamp */
+  FLAG_ALPHA_MIN = 1,   /* an alpha within EPS_ALPHA (relative) of the skip threshold */
+  FLAG_T_STOP = 2,      /* transmittance within its error bound of the stop threshold */
+  FLAG_CLAMP = 4,       /* opacity*G within EPS_ALPHA (relative) of the clamp */
   FLAG_SPH_EDGE = 8,    /* a sphere's distance factor within 1e-8 of 0 (top-K may flip) */
-  FLAG_SPH_STOP = 16,   /* a stop bound within 2e-5 (relative) of tau*N */
-  FLAG_SPH_ZTIE = 32    /* closest-K by depth: K-th and next intersection depth within 1e-5 (relative) */
+  FLAG_SPH_STOP = 16,   /* a stop bound within the error bound of tau*N */
+  FLAG_SPH_ZTIE = 32,   /* closest-K by depth: K-th and next intersection depth within 2e-6 (relative) */
+  FLAG_UNRESOLVED = 64  /* more near ties along one outcome than the alternatives enumerate */
 };
+#define EPS_ALPHA 1.5e-6
+#define U32 (1.0 / 16777216.0)
+/* near-tie decisions whose both outcomes the alternatives enumerate */
+#define MAX_TIES 3
 
 #define CAM_STRIDE 24
 #define TILE 16
@@ -86,6 +105,8 @@ typedef struct {
   long long *tile_start;        /* [total_tiles+1] */
   uint32_t *pair_id;            /* [npairs] record index v*n+i, sorted per tile */
   uint32_t *pair_bits;          /* [npairs] fp32 depth bits */
+  int32_t *branch;              /* [total_pix] or NULL: per pixel, which near-tie decisions the
+                                   backward flips (bit e: the e-th tie met along the way) */
 } octx;
 
 static int pdim(int kind) { return kind == PRIM_GAUSS2D ? 2 : 3; }
@@ -324,6 +345,7 @@ void or_destroy(octx *X) {
   if (!X) return;
   free(X->pos); free(X->scale); free(X->rot); free(X->opac); free(X->depth); free(X->feat);
   free(X->bg); free(X->cams); free(X->rec); free(X->tile_start); free(X->pair_id); free(X->pair_bits);
+  free(X->branch);
   free(X);
 }
 
@@ -478,21 +500,26 @@ static void pixel_ray(const ocam *c, double px, double py, double o[3], double d
   }
 }
 
+/* Squared orthogonal distance of point q from the ray o + s d (Pulsar A):
+ * |e x d|^2 / |d|^2 with e = q - o. (The equal form |e|^2 - (e.d)^2/|d|^2
+ * cancels |q|^2 ~ 400 against r^2 ~ 1e-5 and keeps only ~1e-9 of D.) */
+static double ray_dist2(const double q[3], const double o[3], const double d[3], double dd) {
+  double e[3] = {q[0] - o[0], q[1] - o[1], q[2] - o[2]};
+  double c0 = e[1] * d[2] - e[2] * d[1];
+  double c1 = e[2] * d[0] - e[0] * d[2];
+  double c2 = e[0] * d[1] - e[1] * d[0];
+  return (c0 * c0 + c1 * c1 + c2 * c2) / dd;
+}
+
 /* Depth (sensor z) of the point where the ray o + s d enters the sphere of
- * centre q and radius r: the smaller root s of |o + s d - q|^2 = r^2. */
+ * centre q and radius r: the smaller root s of |o + s d - q|^2 = r^2, i.e.
+ * s = ((e.d) - sqrt(|d|^2 (r^2 - dist^2))) / |d|^2. */
 static double ray_entry_depth(const double q[3], const double o[3], const double d[3], double dd, double r) {
   double e[3] = {q[0] - o[0], q[1] - o[1], q[2] - o[2]};
   double ed = e[0] * d[0] + e[1] * d[1] + e[2] * d[2];
-  double disc = ed * ed - dd * (e[0] * e[0] + e[1] * e[1] + e[2] * e[2] - r * r);
+  double disc = dd * (r * r - ray_dist2(q, o, d, dd));
   double sroot = (ed - sqrt(disc > 0.0 ? disc : 0.0)) / dd;
   return o[2] + sroot * d[2];
-}
-
-/* Squared orthogonal distance of point q from the ray o + s d (Pulsar A). */
-static double ray_dist2(const double q[3], const double o[3], const double d[3], double dd) {
-  double e[3] = {q[0] - o[0], q[1] - o[1], q[2] - o[2]};
-  double ed = e[0] * d[0] + e[1] * d[1] + e[2] * d[2];
-  return e[0] * e[0] + e[1] * e[1] + e[2] * e[2] - ed * ed / dd;
 }
 
 typedef struct {          /* per-entry trace kept for the backward pass */
@@ -511,7 +538,17 @@ typedef struct {
   long long last, ncontrib, processed;
   int32_t top[16];
   int ntop, flags;
+  int nties;            /* near-tie decisions met */
+  double errb;          /* Gaussians: relative error bound of T; spheres: of N */
 } opix;
+
+/* A near-tie decision: the e-th one met takes the other outcome when bit e of
+ * flip is set. */
+static int tie_choice(opix *P, unsigned flip, int decision) {
+  int e = P->nties++;
+  if (e < 31 && ((flip >> e) & 1u)) decision = !decision;
+  return decision;
+}
 
 static int find_view(const octx *X, long long gpix) {
   int v = 0;
@@ -527,8 +564,9 @@ static double wrap_dx(double dx, int W) {
 }
 
 /* Composite one pixel over its tile's sorted list. tr (optional) receives the
- * composited entries in front-to-back order; returns their number. */
-static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_cap) {
+ * composited entries in front-to-back order; returns their number. flip picks
+ * the other outcome at near-tie decisions (see tie_choice). */
+static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_cap, unsigned flip) {
   int v = find_view(X, gpix);
   const ocam *c = &X->cams[v];
   long long lp = gpix - c->pix_off;
@@ -552,20 +590,38 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
     int topd = X->top_by_depth, nc = 0;
     double cz[17];
     otrace ctr[17];
+    double nsum = 0.0;          /* sum over hits of N after the hit + 3 w: rounding of an fp32 N */
     for (long long p = s; p < e; p++) {
       const orec *o = &X->rec[X->pair_id[p]];
       P->processed++;
       double lim = X->tau * N;
-      /* max-shift: the kernels compare the bound in the log domain in fp32 */
-      if (fabs(o->b - lim) <= (X->max_shift ? 1e-4 : 2e-5) * lim) P->flags |= FLAG_SPH_STOP;
-      if (o->b < lim) break;                                   /* early stop (Pulsar 3.2, B.1.3) */
+      int stop = o->b < lim;                                   /* early stop (Pulsar 3.2, B.1.3) */
+      double win = 2.0 * U32 * (4.0 + nsum / N);
+      if (X->max_shift && lim > 0.0) {
+        /* max-shift: an fp32 comparison of beta - ln tau with m + ln(N exp(-m)),
+           beta = ln b and m the shift so far; each term rounds relative to its
+           size, so the window is u times their magnitudes (doubled) */
+        double beta = log(o->b), ltau = log(X->tau), lnN = log(N), m = P->shift;
+        win += 2.0 * U32 * (fabs(beta) + fabs(beta - ltau) + 2.0 * fabs(ltau) + fabs(m) + 2.0 * fabs(lnN - m) +
+                            fabs(lnN) + 8.0);
+      }
+      if (lim > 0.0 && fabs(o->b - lim) <= win * lim) {
+        P->flags |= FLAG_SPH_STOP;
+        stop = tie_choice(P, flip, stop);
+      }
+      if (stop) break;
       double dist2 = ray_dist2(o->m, ro, d, dd);               /* orthogonal ray distance^2 */
       double r2 = o->r_eff * o->r_eff;
       double D = 1.0 - dist2 / r2;
-      if (fabs(D) < 1e-8 && (topd || P->ntop < X->K)) P->flags |= FLAG_SPH_EDGE;
-      if (!(dist2 < r2)) continue;
+      int hit = dist2 < r2;
+      if (fabs(D) < 1e-8 && (topd || P->ntop < X->K)) {
+        P->flags |= FLAG_SPH_EDGE;
+        hit = tie_choice(P, flip, hit);
+      }
+      if (!hit) continue;
       double w = o->opac * D * o->e;
       N += w;
+      nsum += N + 3.0 * fabs(w);
       uint32_t id = X->pair_id[p] % (uint32_t)X->n;
       for (int ch = 0; ch < C; ch++) S[ch] += w * X->feat[(size_t)id * C + ch];
       P->ncontrib++;
@@ -602,7 +658,8 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
     }
     if (topd) {
       int k = nc < X->K ? nc : X->K;
-      if (nc > X->K && fabs(cz[X->K] - cz[X->K - 1]) <= 1e-5 * fabs(cz[X->K - 1])) P->flags |= FLAG_SPH_ZTIE;
+      /* the kernels form entry depths in fp32 to about 5 ulps */
+      if (nc > X->K && fabs(cz[X->K] - cz[X->K - 1]) <= 2e-6 * fabs(cz[X->K - 1])) P->flags |= FLAG_SPH_ZTIE;
       /* the selected ones in list order (the order the reverse pass walks) */
       for (int a = 1; a < k; a++)
         for (int b = a; b > 0 && ctr[b].idx < ctr[b - 1].idx; b--) {
@@ -615,12 +672,14 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       P->ntop = k;
     }
     P->N = N;
+    P->errb = U32 * nsum / N;
     for (int ch = 0; ch < C; ch++) P->col[ch] = S[ch] / N;
     return ntr;
   }
   /* alpha compositing of Gaussian splats, front to back */
   int lidar = c->kind == CAM_SPHERICAL;
   double T = 1.0, dep = 0.0;
+  double tsens = 0.0;         /* sum of alpha / (1 - alpha) over unclamped composited entries */
   double Ccol[64];
   for (int ch = 0; ch < C; ch++) Ccol[ch] = 0.0;
   for (long long p = s; p < e; p++) {
@@ -632,9 +691,13 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
     double G = exp(-power);
     double og = o->opac * G;
     double a = og > X->alpha_max ? X->alpha_max : og;
-    if (fabs(og - X->alpha_max) <= 1e-5 * X->alpha_max) P->flags |= FLAG_CLAMP;
-    if (fabs(a - X->alpha_min) <= 1e-5 * X->alpha_min) P->flags |= FLAG_ALPHA_MIN;
-    if (a < X->alpha_min) continue;
+    if (fabs(og - X->alpha_max) <= EPS_ALPHA * X->alpha_max) P->flags |= FLAG_CLAMP;
+    int skip = a < X->alpha_min;
+    if (fabs(a - X->alpha_min) <= EPS_ALPHA * X->alpha_min) {
+      P->flags |= FLAG_ALPHA_MIN;
+      skip = tie_choice(P, flip, skip);
+    }
+    if (skip) continue;
     double w = T * a;
     uint32_t id = X->pair_id[p] % (uint32_t)X->n;
     if (!lidar)
@@ -647,40 +710,91 @@ static int composite(const octx *X, long long gpix, opix *P, otrace *tr, int tr_
       r->dx = dx; r->dy = dy; r->clamped = og > X->alpha_max;
     }
     T = T * (1.0 - a);
+    if (!(og > X->alpha_max)) tsens += a / (1.0 - a);          /* a clamped alpha is exact */
     P->ncontrib++;
     P->last = p - s + 1;
-    if (fabs(T - X->T_min) <= 2e-4 * X->T_min) P->flags |= FLAG_T_STOP;
-    if (T < X->T_min) break;                                   /* include, then stop */
+    int stop = T < X->T_min;                                   /* include, then stop */
+    if (fabs(T - X->T_min) <= (EPS_ALPHA * tsens + 1e-12) * X->T_min) {
+      P->flags |= FLAG_T_STOP;
+      stop = tie_choice(P, flip, stop);
+    }
+    if (stop) break;
   }
   P->T = T;
+  P->errb = EPS_ALPHA * tsens;
   if (!lidar) for (int ch = 0; ch < C; ch++) P->col[ch] = Ccol[ch];
   else { P->col[0] = dep; P->col[1] = 1.0 - T; }
   P->dep = dep;
   return ntr;
 }
 
+/* One pixel's outputs into slot q of the output arrays. */
+static void put_pixel(const octx *X, const opix *P, long long q, double *img, double *T, long long *last,
+                      double *N, int32_t *top) {
+  int Cm = X->C > 2 ? X->C : 2;
+  for (int ch = 0; ch < Cm; ch++) img[q * Cm + ch] = P->col[ch];
+  /* max-shift (spheres): T carries the shift m, N the normalisation times exp(-m) */
+  if (T) T[q] = X->max_shift && X->kind == PRIM_SPHERE ? P->shift : P->T;
+  if (last) last[q] = P->last;
+  if (N) N[q] = X->max_shift && X->kind == PRIM_SPHERE ? P->N * exp(-P->shift) : P->N;
+  if (top) for (int k = 0; k < X->K; k++) top[q * X->K + k] = P->top[k];
+}
+
 /* Forward over npix global pixel ids (or all pixels when pix == NULL).
- * img: [npix][Cmax] with Cmax = max(C, 2); top: [npix][K]. */
+ * img: [npix][Cmax] with Cmax = max(C, 2); top: [npix][K]. errb (optional):
+ * the relative error bound of an fp32 evaluation's T (Gaussians) or N (spheres). */
 void or_render(const octx *X, long long npix, const long long *pix, double *img, double *T,
                long long *last, double *N, int32_t *top, int32_t *flags, long long *processed,
-               long long *ncontrib) {
-  int Cm = X->C > 2 ? X->C : 2;
+               long long *ncontrib, double *errb) {
   long long cnt = pix ? npix : X->total_pix;
   #pragma omp parallel for schedule(dynamic, 256)
   for (long long q = 0; q < cnt; q++) {
     long long g = pix ? pix[q] : q;
     opix P;
-    composite(X, g, &P, NULL, 0);
-    for (int ch = 0; ch < Cm; ch++) img[q * Cm + ch] = P.col[ch];
-    /* max-shift (spheres): T carries the shift m, N the normalisation times exp(-m) */
-    if (T) T[q] = X->max_shift && X->kind == PRIM_SPHERE ? P.shift : P.T;
-    if (last) last[q] = P.last;
-    if (N) N[q] = X->max_shift && X->kind == PRIM_SPHERE ? P.N * exp(-P.shift) : P.N;
-    if (top) for (int k = 0; k < X->K; k++) top[q * X->K + k] = P.top[k];
-    if (flags) flags[q] = P.flags;
+    composite(X, g, &P, NULL, 0, 0u);
+    put_pixel(X, &P, q, img, T, last, N, top);
+    if (flags) flags[q] = P.flags | (P.nties > MAX_TIES ? FLAG_UNRESOLVED : 0);
     if (processed) processed[q] = P.processed;
     if (ncontrib) ncontrib[q] = P.ncontrib;
+    if (errb) errb[q] = P.errb;
   }
+}
+
+/* Every outcome of each given pixel over its near-tie decisions: flip mask m
+ * (bit e: the e-th tie met takes the other outcome) for all m < 2^MAX_TIES
+ * whose set bits all fall on ties the path meets. Per pixel q, nalt[q]
+ * outcomes in slots q * 2^MAX_TIES + a: mask, img, T, last, N, top (layouts of
+ * or_render). unresolved[q] = 1 when some outcome meets more than MAX_TIES
+ * ties (the later ones are then left at their default outcome). */
+void or_render_alts(const octx *X, long long npix, const long long *pix, int32_t *nalt, int32_t *mask,
+                    double *img, double *T, long long *last, double *N, int32_t *top, int32_t *unresolved) {
+  const int NA = 1 << MAX_TIES;
+  #pragma omp parallel for schedule(dynamic, 16)
+  for (long long q = 0; q < npix; q++) {
+    int na = 0, unres = 0;
+    for (int m = 0; m < NA; m++) {
+      opix P;
+      composite(X, pix[q], &P, NULL, 0, (unsigned)m);
+      int met = P.nties < MAX_TIES ? P.nties : MAX_TIES;
+      if (P.nties > MAX_TIES) unres = 1;
+      if ((unsigned)m >> met) continue;                  /* flips a tie this path never meets */
+      long long slot = q * NA + na;
+      mask[slot] = m;
+      put_pixel(X, &P, slot, img, T, last, N, top);
+      na++;
+    }
+    nalt[q] = na;
+    unresolved[q] = unres;
+  }
+}
+
+/* Per global pixel, the flip mask its reverse pass takes (NULL: none). */
+void or_set_branches(octx *X, const int32_t *branch) {
+  free(X->branch);
+  X->branch = NULL;
+  if (!branch) return;
+  X->branch = (int32_t *)malloc(sizeof(int32_t) * (size_t)(X->total_pix + 1));
+  memcpy(X->branch, branch, sizeof(int32_t) * (size_t)X->total_pix);
 }
 
 /* Brute force: every valid record, globally sorted by (depth bits, id), with
@@ -781,7 +895,7 @@ static void pixel_backward(const octx *X, long long gpix, const double *g, doubl
   opix P;
   int v = find_view(X, gpix);
   const ocam *c = &X->cams[v];
-  int ntr = composite(X, gpix, &P, tr, tr_cap);
+  int ntr = composite(X, gpix, &P, tr, tr_cap, X->branch ? (unsigned)X->branch[gpix] : 0u);
   if (X->kind == PRIM_SPHERE) {
     double N = P.N;
     for (int k = 0; k < ntr; k++) {

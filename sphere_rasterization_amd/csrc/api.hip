@@ -191,6 +191,10 @@ int check_params(const splat_params *m, int kind) {
     CHECK(m->max_shift || m->gamma >= 1.0f / 88.0f, SPLAT_ERR_INVALID_ARG,
           "gamma below 1/88 overflows fp32 sphere weights: set max_shift");
   } else {
+    // the reverse pass rebuilds each entry's transmittance from the fp32 T_final
+    // by dividing out (1 - alpha): a T_min that lets T_final underflow fp32 would
+    // zero or garble those gradients
+    CHECK(m->T_min >= 1e-30f, SPLAT_ERR_INVALID_ARG, "T_min below 1e-30 underflows the stored transmittance");
     CHECK(m->top_by_depth == 0, SPLAT_ERR_UNSUPPORTED, "top_by_depth is for spheres only");
     CHECK(m->max_shift == 0, SPLAT_ERR_UNSUPPORTED, "max_shift is for spheres only");
   }

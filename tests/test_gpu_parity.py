@@ -20,17 +20,21 @@ def _rz(scene, **kw):
     return Rasterizer(scene, device="cuda", **kw)
 
 
-def _run(scene, grad_seed, name, check_grads=True, view_groups=None, normalize=False):
+def _run(scene, grad_seed, name, check_grads=True, view_groups=None, normalize=False, fwd_kw=None):
     _log(f"[case] {name}: n={scene.n} views={len(scene.cams)} kind={scene.kind}")
     rz = _rz(scene)
     rz.forward()
     orc = O.Oracle(scene)
-    st = compare_forward(rz, orc)
-    _log(f"  fwd ok pairs={st.get('pairs')} img_err={st['img_err']:.2e} flagged={st['flag_frac']:.2e}")
+    st = compare_forward(rz, orc, **(fwd_kw or {}))
+    _log(f"  fwd ok pairs={st.get('pairs')} img_err={st['img_err']:.2e} near-tie={st['flag_frac']:.2e} "
+         f"other-outcome={st['alt_taken']} grad-masked={st['masked_frac']:.2e} "
+         f"T_model={st.get('T_model', 0):.2f} N_model={st.get('N_model', 0):.2f}")
     if check_grads:
         g = S.upstream_grads(scene, grad_seed)
         bw = compare_backward(rz, orc, None, g, view_groups=view_groups, normalize=normalize)
         _log(f"  bwd ok worst={bw['worst']:.3f} " + " ".join(f"{k}={v:.2f}" for k, v in bw["per"].items()))
+        _log("  sum-term audit: " + " ".join(f"{k}:{a['worst_nomag']:.2f}/{a['need_mag']}of{a['n']}"
+                                             for k, a in bw["audit"].items()))
     return rz, orc
 
 

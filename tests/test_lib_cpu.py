@@ -176,3 +176,18 @@ def test_sphere_views_need_a_depth_span():
         cams = make_cams([S.Camera(S.CAM_PINHOLE, 64, 64, np.eye(3), np.zeros(3), fx=64.0, fy=64.0, cx=32.0,
                                    cy=32.0, znear=zn, zfar=zf)])
         assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
+
+
+def test_gaussian_T_min_floor():
+    """A transmittance threshold that would let the stored fp32 T_final underflow
+    (the reverse pass divides it back) is refused for Gaussians."""
+    from sphere_rasterization_amd.raster import make_cams, make_params
+    sc = S.gauss3d(n=10)
+    cams = make_cams(sc.cams)
+    lib = L.lib()
+    pr = L.splat_prims()
+    pr.kind, pr.n, pr.channels = 1, 10, 3
+    pr.pos = pr.scale = pr.rot = pr.opacity = pr.feat = 8
+    for tmin in (0.0, 1e-35):
+        prm, _ = make_params(S.Params(T_min=tmin), 3)
+        assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
