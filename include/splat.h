@@ -190,6 +190,20 @@ int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *pro
                    uint32_t *tile_ranges, int64_t *num_pairs, int32_t *overflow, void *workspace,
                    size_t ws_bytes, hipStream_t stream);
 
+/* splat_bin_sort without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, outputs and errors as splat_bin_sort; the workspace is
+ * a fixed device array of SPLAT_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends. Calls whose splat_sort_workspace_bytes exceeds it return
+ * SPLAT_ERR_CAPACITY before any launch. The call allocates nothing (its first call on a
+ * device only looks up that device's copy of the array). Every call on one GPU shares
+ * that array: calls that overlap on one GPU (several streams or threads) race and must
+ * be serialised by the caller. */
+#define SPLAT_NOALLOC_SCRATCH_BYTES (64u << 20)
+int splat_bin_sort_noalloc(const splat_camera *cams, int n_views, int n, const void *proj,
+                           const uint32_t *pair_counts, int64_t capacity, uint64_t *keys, uint32_t *vals,
+                           uint32_t *tile_ranges, int64_t *num_pairs, int32_t *overflow, hipStream_t stream);
+
 /* Composite front to back per pixel, one workgroup per tile with the tile's list staged
  * through LDS in batches (Pulsar B.1.2-B.1.4; NuRec rendering kernel).
  *   img: image layout above.

@@ -18,8 +18,11 @@ SPLAT_PRIM_GAUSS2D, SPLAT_PRIM_GAUSS3D, SPLAT_PRIM_SPHERE = 0, 1, 2
 SPLAT_CAM_PINHOLE, SPLAT_CAM_SPHERICAL = 0, 1
 SPLAT_MAX_VIEWS, SPLAT_MAX_CHANNELS = 16, 64
 
+# include/splat.h: size of the fixed device array splat_bin_sort_noalloc sorts in
+SPLAT_NOALLOC_SCRATCH_BYTES = 64 << 20
+
 EXPORTS = ["splat_projected_bytes", "splat_total_tiles", "splat_sort_workspace_bytes",
-           "splat_bwd_workspace_bytes", "splat_project", "splat_bin_sort", "splat_render_fwd",
+           "splat_bwd_workspace_bytes", "splat_project", "splat_bin_sort", "splat_bin_sort_noalloc", "splat_render_fwd",
            "splat_render_bwd", "splat_interpolate", "splat_interpolate_bwd", "splat_status_string"]
 
 
@@ -81,6 +84,8 @@ def lib():
         L.splat_project.argtypes = [cam_p, i32, C.POINTER(splat_prims), C.POINTER(splat_params), vp, vp, vp]
         L.splat_bin_sort.restype = i32
         L.splat_bin_sort.argtypes = [cam_p, i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.splat_bin_sort_noalloc.restype = i32
+        L.splat_bin_sort_noalloc.argtypes = [cam_p, i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp]
         L.splat_render_fwd.restype = i32
         L.splat_render_fwd.argtypes = [cam_p, i32, C.POINTER(splat_prims), C.POINTER(splat_params), vp, vp, vp,
                                        vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -136,6 +141,13 @@ def splat_bin_sort(cams, n_views, n, proj, pair_counts, capacity, keys, vals, ti
     return _check("splat_bin_sort", lib().splat_bin_sort(cams, n_views, n, proj, pair_counts, capacity, keys, vals,
                                                          tile_ranges, num_pairs, overflow, workspace, ws_bytes,
                                                          stream))
+
+
+def splat_bin_sort_noalloc(cams, n_views, n, proj, pair_counts, capacity, keys, vals, tile_ranges, num_pairs,
+                           overflow, stream):
+    return _check("splat_bin_sort_noalloc", lib().splat_bin_sort_noalloc(cams, n_views, n, proj, pair_counts,
+                                                                         capacity, keys, vals, tile_ranges,
+                                                                         num_pairs, overflow, stream))
 
 
 def splat_render_fwd(cams, n_views, prims, params, proj, vals, tile_ranges, overflow, img, T_final, last, norm, topk,

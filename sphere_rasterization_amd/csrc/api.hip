@@ -284,6 +284,60 @@ int splat_bin_sort(const splat_camera *cams, int n_views, int n, const void *pro
                          stream);
 }
 
+// ---- splat_bin_sort_noalloc: the sort workspace in a fixed device array ----
+// For callers that cannot allocate device memory. The array is file-scope device
+// memory: its name in host code is only a host-side stand-in, so host code uses the
+// address hipGetSymbolAddress gives on each device (looked up once per device on
+// that device's first call), never the name itself.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[SPLAT_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddr {
+  std::once_flag once;
+  void *ptr = nullptr;
+  int rc = SPLAT_OK;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// The calling thread's current device's copy of scratch (or an error).
+int scratch_address(void **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fail(SPLAT_ERR_HIP, "current device");
+  ScratchAddr &sa = g_scratch[dev];
+  std::call_once(sa.once, [&sa]() {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      sa.rc = SPLAT_ERR_HIP;
+      return;
+    }
+    sa.ptr = p;
+  });
+  if (sa.rc != SPLAT_OK) return fail(sa.rc, "scratch symbol address");
+  *ptr = sa.ptr;
+  return SPLAT_OK;
+}
+
+}  // namespace
+
+int splat_bin_sort_noalloc(const splat_camera *cams, int n_views, int n, const void *proj,
+                           const uint32_t *pair_counts, int64_t capacity, uint64_t *keys, uint32_t *vals,
+                           uint32_t *tile_ranges, int64_t *num_pairs, int32_t *overflow, hipStream_t stream) {
+  ViewTable vt;
+  int st = build_views(cams, n_views, 1, &vt);
+  if (st) return st;
+  CHECK(n >= 0 && (long long)n_views * n < (1ll << 32) - 1, SPLAT_ERR_INVALID_ARG, "n out of range");
+  CHECK(capacity >= 0 && capacity < (1ll << 32) - 1, SPLAT_ERR_INVALID_ARG, "capacity out of range");
+  CHECK(tile_ranges && num_pairs && overflow, SPLAT_ERR_INVALID_ARG, "NULL output");
+  CHECK(n == 0 || (proj && pair_counts), SPLAT_ERR_INVALID_ARG, "NULL input");
+  CHECK(capacity == 0 || (keys && vals), SPLAT_ERR_INVALID_ARG, "NULL keys / vals");
+  CHECK(sort_workspace_bytes(vt, n, capacity) <= (size_t)SPLAT_NOALLOC_SCRATCH_BYTES, SPLAT_ERR_CAPACITY,
+        "sort workspace exceeds SPLAT_NOALLOC_SCRATCH_BYTES");
+  void *ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return launch_bin_sort(vt, n, proj, pair_counts, capacity, keys, vals, tile_ranges, num_pairs, overflow, ws, stream);
+}
+
 int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *prims, const splat_params *prm,
                      const void *proj, const uint32_t *vals, const uint32_t *tile_ranges, const int32_t *overflow,
                      float *img, float *T_final, uint32_t *last, float *norm, int32_t *topk, void *bwd_workspace,

@@ -191,3 +191,19 @@ def test_gaussian_T_min_floor():
     for tmin in (0.0, 1e-35):
         prm, _ = make_params(S.Params(T_min=tmin), 3)
         assert lib.splat_project(cams, 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
+
+
+def test_noalloc_sort_size_limit_on_host():
+    """splat_bin_sort_noalloc: the header's array size matches the binding's, and a
+    workspace beyond it is refused on the host (no device touched)."""
+    src = open(os.path.join(ROOT, "include", "splat.h")).read()
+    m = re.search(r"#define SPLAT_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.SPLAT_NOALLOC_SCRATCH_BYTES
+    from sphere_rasterization_amd.raster import make_cams
+    sc = S.pulsar_spheres(n=10)
+    cams = make_cams(sc.cams)
+    big = 16 << 20
+    assert L.splat_sort_workspace_bytes(cams, 1, 10, big) > L.SPLAT_NOALLOC_SCRATCH_BYTES
+    lib = L.lib()
+    assert lib.splat_bin_sort_noalloc(cams, 1, 10, 8, 8, big, 8, 8, 8, 8, 8, None) == L.SPLAT_ERR_CAPACITY
+    assert lib.splat_bin_sort_noalloc(cams, 1, 10, 8, 8, 100, 8, 8, None, 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
