@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -28,13 +29,35 @@ if ROOT not in sys.path:
 
 METRIC = "Mpixels/s fwd+bwd at 1M primitives, 1024x1024; % of VALU/HBM roofline"
 # MI355X: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz = 39.3 T single-issue fp32 lane-ops/s
-# (packed fp32 doubles the FLOP count but is not used); HBM3E 8 TB/s.
+# (packed fp32 doubles the FLOP count but is not used; an fp64 FMA issues at the same
+# per-lane rate); HBM3E 8 TB/s.
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
-# Algorithmic VALU lane-ops of the sphere compositor (see the design notes):
-# per list entry a pixel examines before it stops, and per contributing sphere.
-OPS_PER_ENTRY = 15
-OPS_PER_HIT_BASE = 5          # + one fma per channel
+# Algorithmic work of the sphere path per unit (the method's work, not the
+# instructions a kernel issues):
+#   forward compositor: per list entry a pixel examines before it stops 7 lane-ops
+#     (ray distance, scale, compare, bound compare); per contributing sphere 7 + C
+#     (D, weight, normalisation, C colour FMAs, top-K bookkeeping); the counts are
+#     the oracle's exact per-pixel totals over the frame
+#   reverse compositor: per recorded (pixel, sphere) 45 lane-ops of gradient
+#     arithmetic; per (8x8 pixel quadrant, recorded sphere) 48 (eight values
+#     reduced over the wave in six steps)
+#   projection: read position, radius, opacity (20 B), write a 48-byte record
+#     and the pair count (4 B) per sphere
+#   binning: scan 8 B per sphere; emit 20 B per sphere + 12 B per pair; sort
+#     24 B per pair per 8-bit pass over 32 depth bits + ceil(log2 tiles) tile
+#     bits; tile ranges 8 B per pair + 8 B per tile
+#   gradient tail (chain rule + camera sum): ~60 B per sphere
+OPS_PER_ENTRY = 7
+OPS_PER_HIT_BASE = 7          # + one fma per channel
+OPS_PER_RECORDED = 45
+OPS_PER_WAVE_SPHERE = 48
+PROJECT_BYTES_PER_PRIM = 20 + 48 + 4
+SCAN_BYTES_PER_PRIM = 8
+EMIT_BYTES_PER_PRIM, EMIT_BYTES_PER_PAIR = 20, 12
+SORT_BYTES_PER_PAIR_PASS = 24
+RANGE_BYTES_PER_PAIR, RANGE_BYTES_PER_TILE = 8, 8
+GRAD_BYTES_PER_PRIM = 60
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
@@ -43,17 +66,17 @@ FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
 FWD_TRAFFIC_SHA256 = "e8c85bf7b5fd546051e7d95c864bc7b88fbc8dcef44b7ae727f06827abbf7956"
-# Algorithmic HBM bytes of the projection and binning stages:
-#   projection: per primitive read position, radius, opacity and the three
-#     features (20 + 12 B), write the bin, draw and backward records and the
-#     pair count (16 + 64 + 16 + 4 B)
-#   binning: per record the 16-byte bin record twice (counting and scatter
-#     passes, 32 B; the pair count is its rectangle's tile count); per pair the
-#     bucketed word written and read (16 B) and the sorted key and value
-#     written (12 B)
-PROJECT_BYTES_PER_PRIM = 20 + 12 + 16 + 64 + 16 + 4
-BIN_BYTES_PER_REC = 32
-BIN_BYTES_PER_PAIR = 28
+BIN_KERNELS = ("k_thist", "k_col_scan", "k_tscatter", "k_seg_sort", "k_tile_scan1", "k_scan_reduce", "k_scan_top",
+               "k_tile_ranges", "k_fill_u32", "k_tile_count", "k_bucket")
+
+
+def binning_bytes(n, npairs, total_tiles):
+    """Algorithmic HBM bytes of scan, emit, sort and tile ranges (see above)."""
+    bits = 32 + max(1, math.ceil(math.log2(max(total_tiles, 2))))
+    passes = math.ceil(bits / 8)
+    return (SCAN_BYTES_PER_PRIM * n + EMIT_BYTES_PER_PRIM * n + EMIT_BYTES_PER_PAIR * npairs
+            + SORT_BYTES_PER_PAIR_PASS * passes * npairs + RANGE_BYTES_PER_PAIR * npairs
+            + RANGE_BYTES_PER_TILE * total_tiles), passes
 
 
 def parse():
@@ -63,7 +86,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=1024,
-                    help="image rows the CPU oracle renders (fwd + bwd) for the baseline")
+                    help="image rows the CPU oracle renders (fwd + bwd) on all host cores for the baseline")
+    ap.add_argument("--cpu-1t-rows", type=int, default=1024,
+                    help="image rows the CPU oracle renders (fwd + bwd) on one thread")
+    ap.add_argument("--no-kernel-profile", action="store_true",
+                    help="skip the pass that takes per-kernel device times with torch.profiler")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run three plain device copies of this many MiB (read + write of a "
                          "known size, to scale hardware byte counters)")
@@ -170,6 +197,9 @@ def main():
              for i, s in enumerate(stages)}
     value = pixels / (ms / 1e3) / 1e6
     npairs = int(rz.num_pairs.item())
+    ktimes = None
+    if not args.no_kernel_profile:
+        ktimes = kernel_times(torch, step, min(args.steps, 20))
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "Mpixels/s", "n_gpus": 1,
@@ -186,11 +216,11 @@ def main():
         out["metric"] = f"Mpixels/s fwd+bwd, {WORKLOAD_NAMES[wl]}"
     cpu = None
     if not args.no_cpu_baseline and wl == 3:
-        cpu = cpu_baseline(scene, g_np, args.cpu_sample_rows)
+        cpu = cpu_baseline(scene, g_np, args.cpu_sample_rows, args.cpu_1t_rows)
         out["cpu_baseline"] = cpu["json"]
     if wl == 3:
         out["roofline"] = roofline(fwd_kernel_ms, cpu, scene)
-        out["stage_hbm"] = stage_hbm(st_ms, scene.n, npairs)
+        out["kernels"] = kernel_rooflines(ktimes, cpu, scene, npairs, rz.total_tiles)
     if args.hbm_copy:
         out["hbm_copy_GBps"] = hbm_copy(torch, dev)
     print(json.dumps(out), flush=True)
@@ -277,50 +307,155 @@ def sources_digest(paths):
     return h.hexdigest()
 
 
-def stage_hbm(st_ms, n, npairs):
-    """Projection and binning against the HBM peak, from their algorithmic bytes."""
+def kernel_times(torch, step, steps):
+    """Average device time per launch (us) of every library kernel over `steps`
+    steps, taken with torch.profiler (a diagnostic pass after the timed steps)."""
+    import re
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+        out = {}
+        for e in prof.key_averages():
+            m = re.search(r"(k_\w+)(<[^()]*>)?\(", e.key)
+            if not m:
+                continue
+            name = m.group(1) + (m.group(2) or "")
+            us = float(getattr(e, "device_time", 0.0) or 0.0)
+            out[name] = {"us": round(us, 3), "launches_per_step": round(e.count / steps, 3)}
+        return out or None
+    except Exception as ex:                  # the profiler is a diagnostic: never fail the run
+        print(f"kernel profile skipped: {ex}", file=sys.stderr)
+        return None
+
+
+def _frac(work, us, peak, unit_scale):
+    achieved = work / (us * 1e-6) / unit_scale
+    return round(achieved, 3), round(achieved / peak, 4)
+
+
+def kernel_rooflines(kt, cpu, scene, npairs, total_tiles):
+    """Each stage's kernels against their own roofline, with the survey's
+    algorithmic units (see the constants above) and the profiled device times."""
+    if not kt:
+        return None
+    pick = lambda pre: {k: v for k, v in kt.items() if k.split("<")[0] == pre}
+    tsum = lambda d: sum(v["us"] * v["launches_per_step"] for v in d.values())
+    n, C = scene.n, scene.channels
     out = {}
-    for name, nbytes in (("project", PROJECT_BYTES_PER_PRIM * n),
-                         ("bin_sort", BIN_BYTES_PER_REC * n + BIN_BYTES_PER_PAIR * npairs)):
-        gbs = nbytes / (st_ms[name] / 1e3) / 1e9
-        out[name] = {"bytes": nbytes, "GB/s": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    proj = pick("k_project")
+    if proj:
+        b = PROJECT_BYTES_PER_PRIM * n
+        a, f = _frac(b, tsum(proj), HBM_PEAK_GBS, 1e9)
+        out["project"] = {"kernels": sorted(proj), "us": round(tsum(proj), 2), "bound": "hbm", "bytes": b,
+                          "achieved": a, "unit": "GB/s", "frac": f}
+    bink = {k: v for k, v in kt.items() if k.split("<")[0] in BIN_KERNELS}
+    if bink:
+        b, passes = binning_bytes(n, npairs, total_tiles)
+        a, f = _frac(b, tsum(bink), HBM_PEAK_GBS, 1e9)
+        out["bin_sort"] = {"kernels": sorted(bink), "us": round(tsum(bink), 2), "bound": "hbm", "bytes": b,
+                           "radix_passes_counted": passes, "achieved": a, "unit": "GB/s", "frac": f}
+        if proj:
+            b2 = b + PROJECT_BYTES_PER_PRIM * n
+            us2 = tsum(bink) + tsum(proj)
+            a, f = _frac(b2, us2, HBM_PEAK_GBS, 1e9)
+            out["project_bin_sort"] = {"us": round(us2, 2), "bound": "hbm", "bytes": b2, "achieved": a,
+                                       "unit": "GB/s", "frac": f}
+    full = cpu is not None and cpu["rows"] == cpu["H"]
+    fwd = pick("k_fwd_sphere")
+    if fwd:
+        e = {"kernels": sorted(fwd), "us": round(tsum(fwd), 2), "bound": "alu", "unit": "Tops/s"}
+        if full:
+            ops = cpu["processed"] * OPS_PER_ENTRY + cpu["hits"] * (OPS_PER_HIT_BASE + C)
+            e["ops"] = ops
+            e["achieved"], e["frac"] = _frac(ops, tsum(fwd), VALU_PEAK_TOPS, 1e12)
+        out["render_fwd"] = e
+    bwd = pick("k_bwd_sphere")
+    if bwd:
+        e = {"kernels": sorted(bwd), "us": round(tsum(bwd), 2), "bound": "alu", "unit": "Tops/s"}
+        if full:
+            ops = cpu["recorded"] * OPS_PER_RECORDED + cpu["wave_spheres"] * OPS_PER_WAVE_SPHERE
+            e["ops"] = ops
+            e["achieved"], e["frac"] = _frac(ops, tsum(bwd), VALU_PEAK_TOPS, 1e12)
+        out["render_bwd"] = e
+    tail = {k: v for k, v in kt.items() if k.split("<")[0] in ("k_sphere_grads", "k_cam_final", "k_zero")}
+    if tail:
+        b = GRAD_BYTES_PER_PRIM * n
+        a, f = _frac(b, tsum(tail), HBM_PEAK_GBS, 1e9)
+        out["grad_tail"] = {"kernels": sorted(tail), "us": round(tsum(tail), 2), "bound": "hbm", "bytes": b,
+                            "achieved": a, "unit": "GB/s", "frac": f}
+    out["all_kernels_us"] = {k: v["us"] for k, v in sorted(kt.items())}
     return out
 
 
-def cpu_baseline(scene, g_np, rows):
-    """Oracle forward + backward on the host over the first `rows` image rows."""
+def _oracle_frame(O, scene, g_np, rows):
+    """Oracle on the first `rows` image rows: projection and binning of every
+    sphere, then compositing and reverse pass of those rows' pixels. Returns the
+    wall times (s) and the forward outputs."""
+    import numpy as np
+    W = scene.cams[0].width
+    t0 = time.perf_counter()
+    orc = O.Oracle(scene)
+    orc.bin()
+    t1 = time.perf_counter()
+    pix = np.arange(rows * W, dtype=np.int64)
+    r = orc.render(pix)
+    t2 = time.perf_counter()
+    g = [np.array(x, copy=True) for x in g_np]
+    g[0][:, rows:, :] = 0.0
+    orc.backward(g)
+    t3 = time.perf_counter()
+    orc.close()
+    return dict(prep=t1 - t0, fwd=t2 - t1, bwd=t3 - t2, r=r)
+
+
+def cpu_baseline(scene, g_np, rows, rows_1t):
+    """The CPU oracle on the host: all its threads over the first `rows` rows, then
+    one thread over the first `rows_1t` rows; each reports the sampled pixels over
+    its wall time (projection and binning of every sphere included)."""
     import numpy as np
     from oracle import oracle as O
     H, W = scene.cams[0].height, scene.cams[0].width
     rows = max(1, min(rows, H))
-    t0 = time.perf_counter()
-    orc = O.Oracle(scene)
-    orc.bin()
-    pix = np.arange(rows * W, dtype=np.int64)
-    r = orc.render(pix)
-    g = [np.array(x, copy=True) for x in g_np]
-    g[0][:, rows:, :] = 0.0
-    orc.backward(g)
-    dt = time.perf_counter() - t0
-    cores = os.cpu_count() or 1
+    rows_1t = max(1, min(rows_1t, H))
+    nthr = O.threads()
+    a = _oracle_frame(O, scene, g_np, rows)
+    O.threads(1)
     try:
-        cores = int(os.environ.get("OMP_NUM_THREADS", cores))
-    except ValueError:
-        pass
-    mpix = rows * W / dt / 1e6
-    return {"json": {"value": round(mpix, 4), "unit": "Mpixels/s", "cores": cores, "kind": "oracle",
-                     "sample": f"first {rows} of {H} rows of the 1M-sphere 1024x1024 frame: projection and "
-                               f"binning of all spheres, compositing and reverse pass of {rows * W} pixels "
-                               f"(fp64, {dt:.1f} s wall)"},
+        b = _oracle_frame(O, scene, g_np, rows_1t)
+    finally:
+        O.threads(nthr)
+    wall = a["prep"] + a["fwd"] + a["bwd"]
+    mpix = rows * W / wall / 1e6
+    wall1 = b["prep"] + b["fwd"] + b["bwd"]
+    r = a["r"]
+    top = r["top"]
+    pix = np.arange(rows * W, dtype=np.int64)
+    quad = (pix // W // 8) * ((W + 7) // 8) + (pix % W) // 8
+    rec = top >= 0
+    qid = np.unique(quad[:, None].repeat(top.shape[1], 1)[rec] * scene.n + top[rec])
+    return {"json": {"value": round(mpix, 4), "unit": "Mpixels/s", "cores": nthr, "kind": "oracle",
+                     "sample": f"first {rows} of {H} rows of the 1M-sphere 1024x1024 frame on {nthr} threads: "
+                               f"projection and binning of all spheres, compositing and reverse pass of "
+                               f"{rows * W} pixels (fp64, {wall:.1f} s wall)",
+                     "fwd_s": round(a["prep"] + a["fwd"], 3), "bwd_s": round(a["bwd"], 3),
+                     "one_thread": {"value": round(rows_1t * W / wall1 / 1e6, 4), "unit": "Mpixels/s",
+                                    "cores": 1, "fwd_s": round(b["prep"] + b["fwd"], 3),
+                                    "bwd_s": round(b["bwd"], 3),
+                                    "sample": f"first {rows_1t} of {H} rows on one thread: projection and binning "
+                                              f"of all spheres, compositing and reverse pass of {rows_1t * W} "
+                                              f"pixels ({wall1:.1f} s wall)"}},
             "processed": int(r["processed"].sum()), "hits": int(r["ncontrib"].sum()),
-            "rows": rows, "H": H}
+            "recorded": int(rec.sum()), "wave_spheres": int(len(qid)), "rows": rows, "H": H}
 
 
 def roofline(fwd_ms, cpu, scene):
     """Forward compositor against the single-issue VALU peak, from the oracle's
-    exact count of list entries examined and contributions made per pixel;
-    fwd_ms: the kernel's median time over the timed steps (HIP events on its stream)."""
+    exact count of list entries examined and contributions made per pixel in the
+    survey's units (7 lane-ops per entry, 7 + C per contribution); fwd_ms: the
+    kernel's median time over the timed steps (HIP events on its stream)."""
     traffic = FWD_TRAFFIC_BYTES if sources_digest(FWD_TRAFFIC_SOURCES) == FWD_TRAFFIC_SHA256 else None
     if cpu is None or cpu["rows"] != cpu["H"]:
         return {"bound": "alu", "kernel": "k_fwd_sphere", "achieved": None, "peak": round(VALU_PEAK_TOPS, 2),
@@ -329,7 +464,7 @@ def roofline(fwd_ms, cpu, scene):
     achieved = ops / (fwd_ms / 1e3) / 1e12
     return {"bound": "alu", "kernel": "k_fwd_sphere", "achieved": round(achieved, 3),
             "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s", "frac": round(achieved / VALU_PEAK_TOPS, 4),
-            "traffic": traffic, "ops_per_launch": ops}
+            "traffic": traffic, "ops_per_launch": ops, "kernel_ms": round(fwd_ms, 4)}
 
 
 if __name__ == "__main__":

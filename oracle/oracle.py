@@ -64,11 +64,18 @@ def lib():
         L.or_render.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.or_render_alts.argtypes = [vp, C.c_longlong, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.or_set_branches.argtypes = [vp, vp]
+        L.or_threads.restype = C.c_int
+        L.or_threads.argtypes = [C.c_int]
         L.or_render_bruteforce.argtypes = [vp, ip, vp, vp, vp, vp]
         L.or_backward.argtypes = [vp] * 11 + [C.c_int]
         L.or_backward_mag.argtypes = [vp] * 19 + [C.c_int]
         _lib = L
     return _lib
+
+
+def threads(n: int = 0) -> int:
+    """Threads of the oracle's parallel loops; n > 0 sets them first."""
+    return int(lib().or_threads(int(n)))
 
 
 def _d(a):

@@ -390,6 +390,17 @@ octx *or_create(int kind, int n, int C, const double *pos, const double *scale, 
   return X;
 }
 
+/* OpenMP threads the oracle's parallel loops use (n > 0 sets them). */
+int or_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 long long or_total_tiles(const octx *X) { return X->total_tiles; }
 long long or_total_pix(const octx *X) { return X->total_pix; }
 

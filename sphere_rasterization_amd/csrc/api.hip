@@ -136,6 +136,9 @@ int build_views(const splat_camera *cams, int n_views, int channels, ViewTable *
     memcpy(d.t, c.t, sizeof(d.t));
     d.fx = c.fx; d.fy = c.fy; d.cx = c.cx; d.cy = c.cy;
     d.el_min = c.el_min_deg; d.el_max = c.el_max_deg; d.znear = c.znear; d.zfar = c.zfar;
+    d.ifx = c.kind == SPLAT_CAM_SPHERICAL ? 0.0 : 1.0 / (double)c.fx;
+    d.ify = c.kind == SPLAT_CAM_SPHERICAL ? 0.0 : 1.0 / (double)c.fy;
+    d.ispan = c.zfar > c.znear ? 1.0 / ((double)c.zfar - (double)c.znear) : 0.0;
     toff += (long long)d.TW * d.TH;
     poff += (long long)c.width * c.height;
     ioff += (long long)d.chan * c.width * c.height;
@@ -407,6 +410,7 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   memset(&A, 0, sizeof(A));
   A.n = prims->n; A.C = prims->channels; A.top_k = prm->top_k;
   A.alpha_min = prm->alpha_min; A.alpha_max = prm->alpha_max; A.gamma = prm->gamma;
+  A.igamma = (float)(1.0 / (double)prm->gamma);
   A.max_shift = prims->kind == SPLAT_PRIM_SPHERE ? prm->max_shift : 0;
   ProjLayout L = proj_layout(const_cast<void *>(proj), (long long)n_views * prims->n);
   A.draw = L.draw; A.aux = L.aux; A.vals = vals; A.ranges = tile_ranges; A.overflow = overflow;

@@ -533,224 +533,288 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
 
 // ---------------------------------------------------------------------------
 // Sphere backward over the first top_k contributing spheres of each pixel.
-// The forward recorded each one as its index in the sorted pair list, i.e. a
-// position in this tile's list. The tile list is staged in batches up to the
-// deepest recorded position of the tile; each wave walks the entries that reach
-// its quadrant, and a lane contributes when the entry is the next of its
-// recorded spheres. The wave's contributions to an entry are summed with a
-// transposed reduction (one value per 8-lane group), so one lane per value adds
-// to the entry's LDS slot; each touched entry leaves the tile with one global
-// atomic per value.
+// The forward recorded each one as its index in the sorted pair list (ascending
+// per pixel). Each wave (an 8x8 quadrant of the tile) visits only the entries
+// its pixels recorded: the wave-wide minimum of the lanes' next recorded index
+// picks the entry, the lanes that recorded it form their gradient terms, the
+// wave sums them with a transposed reduction (value q ends in the lanes of
+// 8-lane group q) and one lane per value adds the sum to the record's fp64 row.
+// A step costs the same whether one lane or all 64 recorded the entry, so the
+// number of steps is the number of distinct spheres the quadrant's pixels
+// recorded (11 on average at 1M spheres, 1024x1024), not the length of the
+// tile list up to the deepest recorded entry.
+// The next entry's record is requested before the current one is processed.
+// Records are read with vector loads of a wave-uniform address: their wait
+// counter is in order and separate from the LDS one, so the LDS reads of the
+// loop do not wait for the prefetch (scalar loads share a counter with LDS and
+// return out of order, and every LDS wait would have waited for them too).
 // ---------------------------------------------------------------------------
+// x + x[lane ^ 32] and x + x[lane ^ 16] in every lane, with the gfx950 lane swaps
+// (VALU; no LDS traffic). v_permlane32_swap exchanges the upper half of its first
+// register with the lower half of its second, v_permlane16_swap the odd rows of
+// the first with the even rows of the second; given two copies of x, the two
+// results add up to the pair sum in every lane. The two results are copied to
+// plain integers before the bit casts: bit-casting an element of the returned
+// pair directly read the first element for both.
+__device__ __forceinline__ float add_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned a = r[0], b = r[1];
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned a = r[0], b = r[1];
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// Wave-wide minimum (uniform): butterflies within each 16-lane row, then the
+// row pairs and halves through the lane swaps.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u32<0xB1>(x));     // lane ^ 1
+  x = min(x, dpp_u32<0x4E>(x));     // lane ^ 2
+  x = min(x, dpp_u32<0x141>(x));    // 8-lane mirror
+  x = min(x, dpp_u32<0x140>(x));    // 16-lane mirror
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const uint32_t a = r[0], b = r[1];
+    x = min(a, b);
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const uint32_t a = r[0], b = r[1];
+    x = min(a, b);
+  }
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
+// wave_sum8_transposed with the two cross-row steps on the lane swaps.
+__device__ __forceinline__ float wave_sum8_transposed_swap(const float (&v)[8]) {
+  const unsigned lane = lane_id();
+  const bool b2 = lane & 4u, b1 = lane & 2u, b0 = lane & 1u;
+  float a[4], c[2];
+#pragma unroll
+  for (int j = 0; j < 4; j++) a[j] = (b2 ? v[j + 4] : v[j]) + dpp_f32<0x141>(b2 ? v[j] : v[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; j++) c[j] = (b1 ? a[j + 2] : a[j]) + dpp_f32<0x4E>(b1 ? a[j] : a[j + 2]);
+  float e = (b0 ? c[1] : c[0]) + dpp_f32<0xB1>(b0 ? c[0] : c[1]);
+  e += dpp_f32<0x128>(e);                         // row rotate by 8: lane ^ 8
+  return add_xor32(add_xor16(e));
+}
+
+// One recorded entry: what the gradient terms need (wave-uniform values).
+template <int CM>
+struct SphEntry {
+  double u, v, a;        // normalised centre (orthographic: (qx, qy)), A = qz^2 / r_eff^2
+  float oe;              // o exp(o zhat / gamma) (max-shift: its log)
+  float qz, reff, opac;
+  float flags;           // bit 0 floored, bit 1 gated (converted where used: a conversion here
+                         // would wait for the load right after it is issued)
+  float f[CM];
+};
+
+template <int CM>
+__device__ __forceinline__ SphEntry<CM> sph_entry(uint32_t rid, long long vbase, int C, const DrawRec *draw,
+                                                  const AuxRec *aux, const float *feat) {
+  SphEntry<CM> e;
+  const DrawRec &d = draw[rid];
+  const AuxRec &ax = aux[rid];
+  e.u = d.u;
+  e.v = d.v;
+  e.a = d.a;
+  e.oe = d.w;
+  e.qz = ax.z;
+  e.reff = ax.w;
+  e.opac = ax.opac;
+  e.flags = ax.flags;
+#pragma unroll
+  for (int ch = 0; ch < CM; ch++) {
+    if constexpr (CM <= SPLAT_REC_FEAT)
+      e.f[ch] = rec_feat(d, ch);                                    // here C = CM: features in the record
+    else
+      e.f[ch] = ch < C ? feat[(size_t)((long long)rid - vbase) * C + ch] : 0.0f;
+  }
+  return e;
+}
+
 // EXT: the call asks for intrinsic gradients or gradient normalisation (their
 // per-contribution work is compiled out of the plain reverse pass).
 template <int CM, bool EXT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_bwd_sphere(ViewTable vt, BwdArgs A, int tile_begin) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_bwd_sphere(
+    ViewTable vt, BwdArgs A, int tile_begin) {
   constexpr int NV = 5 + CM;                  // dq0, dq1, dq2, d_reff, d_opac, d_feat...
   constexpr int NG = (NV + 7) / 8;            // groups of eight for the reduction
-  constexpr int BT = 128;                     // entries staged per batch (six workgroups fit a CU)
-  constexpr int TKS = SPLAT_TOPK_MAX + 1;     // odd stride of the per-pixel recorded positions
-  __shared__ double2 s_a[BT];                // normalised centre (ax, ay)
-  __shared__ double2 s_Ai[BT];               // A, 1 / r_eff
-  __shared__ float4 s_x[BT];                 // qz, oe, 1/o + zhat/gamma, o/gamma
-  __shared__ int s_flags[BT];
-  __shared__ float s_f[CM][BT];
-  __shared__ uint32_t s_rid[BT];
-  constexpr int NVP = NV | 1;                 // odd row stride of the LDS sums
-  __shared__ float s_acc[BT][NVP];
-  __shared__ uint32_t s_top[256 * TKS];
-  __shared__ uint32_t s_cnt[BT];             // pixels recording the entry (normalisation)
-  __shared__ QuadLists s_l;
-  __shared__ uint32_t s_npos;
+  constexpr int TKS = SPLAT_TOPK_MAX + 1;     // odd stride (in pairs) of the per-pixel recorded entries
+  constexpr uint32_t NONE = 0xffffffffu;
+  __shared__ uint2 s_top[256 * TKS];          // per pixel: (recorded index, record id), ascending
   if (*A.overflow) return;
   const int gtile = tile_begin + blockIdx.x;
   const int view = view_of_tile(vt, gtile);
   const ViewDev &c = vt.v[view];
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
-  const uint32_t start = A.ranges[2 * gtile];
-  const uint32_t len = A.ranges[2 * gtile + 1] - start;
+  const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
   const SphereRay ray = sphere_ray(c, tp);
   const unsigned lane = lane_id();
-  const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
   const size_t plane = (size_t)c.W * c.H;
   const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
   const int K = A.top_k;
-  float g[CM], Cimg[CM];
-  float invN = 0.0f;
-#pragma unroll
-  for (int ch = 0; ch < CM; ch++) {
-    const bool ok = tp.inside && ch < A.C;
-    g[ch] = ok ? A.dimg[pofs + ch * plane] : 0.0f;
-    Cimg[ch] = ok ? A.img[pofs + ch * plane] : 0.0f;
-  }
-  // recorded positions, local to the tile and ascending
-  uint32_t *my_top = s_top + threadIdx.x * TKS;
+  const long long vbase = (long long)view * A.n;
+  // recorded entries (indices into the sorted pairs, ascending), this tile's only,
+  // with their record ids (all loads in flight together)
+  uint2 *my_top = s_top + threadIdx.x * TKS;
   int ntop = 0;
-  for (int s = 0; s < K && tp.inside; s++) {
-    const int t = A.topk[p * K + s];
-    const uint32_t lp = (uint32_t)t - start;
-    if (t < 0 || lp >= len) break;
-    my_top[ntop++] = lp;
+  {
+    int t[SPLAT_TOPK_MAX];
+#pragma unroll
+    for (int s = 0; s < SPLAT_TOPK_MAX; s++) t[s] = (s < K && tp.inside) ? A.topk[p * K + s] : -1;
+    bool go = true;
+#pragma unroll
+    for (int s = 0; s < SPLAT_TOPK_MAX; s++) {
+      go = go && t[s] >= 0 && (uint32_t)t[s] >= start && (uint32_t)t[s] < end;
+      ntop += go ? 1 : 0;
+    }
+    uint32_t r[SPLAT_TOPK_MAX];
+#pragma unroll
+    for (int s = 0; s < SPLAT_TOPK_MAX; s++) r[s] = s < ntop ? A.vals[t[s]] : 0u;
+#pragma unroll
+    for (int s = 0; s < SPLAT_TOPK_MAX; s++)
+      if (s < ntop) my_top[s] = make_uint2((uint32_t)t[s], r[s]);
+    my_top[ntop] = make_uint2(NONE, 0u);
   }
-  if (tp.inside) invN = 1.0f / A.norm[p];
+  // per pixel: g / N and (g / N) . C, for the feature and weight terms
+  float gi[CM];
+  float gC = 0.0f;
+  {
+    const float invN = tp.inside ? 1.0f / A.norm[p] : 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < CM; ch++) {
+      const bool ok = tp.inside && ch < A.C;
+      gi[ch] = ok ? A.dimg[pofs + ch * plane] * invN : 0.0f;
+      gC = __builtin_fmaf(gi[ch], ok ? A.img[pofs + ch * plane] : 0.0f, gC);
+    }
+  }
   // max-shifted blending: weights (and norm) relative to exp(m), m from the forward
   const float msh = (A.max_shift && tp.inside) ? A.T_final[p] : 0.0f;
-  if (threadIdx.x == 0) s_npos = 0;
-  __syncthreads();
-  {
-    uint32_t hi = ntop ? my_top[ntop - 1] + 1 : 0u;
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, WAVE));
-    if (lane == 0 && hi) atomicMax(&s_npos, hi);
-  }
-  __syncthreads();
-  const uint32_t npos = s_npos;
-  int nxt = 0;
-  uint32_t tgt = ntop ? my_top[0] : 0xffffffffu;
   // d loss / d (ray x, ray y) summed over the pixel's recorded spheres
-  double kgx = 0.0, kgy = 0.0;
-  const double inv_span = 1.0 / ((double)c.zfar - (double)c.znear);
-  const float igam = 1.0f / A.gamma;
-  const long long vbase = (long long)view * A.n;
+  float kgx = 0.0f, kgy = 0.0f;
+  const float inv_span = (float)c.ispan;
+  const float igam = A.igamma;
   // orthographic views: a = (qx, qy), the ray along +z through (x, y, 0); dist^2 =
   // |(x, y) - a|^2, whose gradient in q is -2 (sx, sy, 0) (no cross term, no qz scale)
   const bool orth = c.kind == SPLAT_CAM_ORTHOGRAPHIC;
   const double crs = orth ? 0.0 : 1.0;
+  const float rxf = (float)ray.x, ryf = (float)ray.y, rgf = (float)ray.g * (orth ? 0.0f : 1.0f);
+  const int rowlen = 5 + A.C;
 
-  // list entries read one batch ahead (npos never passes the tile's list end)
-  uint32_t rid_next = threadIdx.x < npos ? A.vals[start + threadIdx.x] : 0u;
-  for (uint32_t b = 0; b < npos; b += BT) {
-    const uint32_t cnt = min((uint32_t)BT, npos - b);
-    const uint32_t rid_cur = rid_next;
-    if (b + BT + threadIdx.x < npos) rid_next = A.vals[start + b + BT + threadIdx.x];
-    unsigned mask = 0;
-    if (threadIdx.x < cnt) {
-      const uint32_t rid = rid_cur;
-      const DrawRec d = A.draw[rid];
-      const AuxRec ax = A.aux[rid];
-      const long long id = (long long)rid - vbase;
-      s_rid[threadIdx.x] = rid;
-      s_a[threadIdx.x] = make_double2(d.u, d.v);
-      s_Ai[threadIdx.x] = make_double2(d.a, 1.0 / (double)ax.w);
-      const float zhat = (float)(((double)c.zfar - (double)ax.z) * inv_span);
-      s_x[threadIdx.x] = make_float4(ax.z, d.w, 1.0f / ax.opac + zhat * igam, ax.opac * igam);
-      s_flags[threadIdx.x] = (int)ax.flags;
+  int nxt = 0;
+  uint2 cur_t = my_top[0];
+  uint32_t m = wave_min_u32(cur_t.x);
+  // the record id of entry m, from the first lane whose next entry it is
+  // (NONE: 0, the first record)
+  auto rid_of = [&](uint32_t mm) {
+    const int l = __builtin_amdgcn_readfirstlane((int)__ffsll((long long)ballot64(cur_t.x == mm)) - 1);
+    const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)cur_t.y, l & 63);
+    return mm != NONE ? r : 0u;
+  };
+  // One step: entry m (record e, id rid) is processed while the next entry's
+  // record is requested into en / rid_n; m becomes the next entry.
+  auto step = [&](const SphEntry<CM> &e, uint32_t rid, SphEntry<CM> &en, uint32_t &rid_n) {
+    const bool mine = cur_t.x == m;
+    if (mine) {
+      nxt++;
+      cur_t = my_top[nxt];
+    }
+    // requested unconditionally (record 0 after the last entry: any record is a
+    // valid address), so that the number of loads in flight is the same on every
+    // path and the wait for this step's record does not also wait for them
+    const uint32_t mn = wave_min_u32(cur_t.x);
+    rid_n = rid_of(mn);
+    en = sph_entry<CM>(rid_n, vbase, A.C, A.draw, A.aux, A.feat);
+    if constexpr (EXT)
+      if (A.cnt) {
+        const uint64_t bm = ballot64(mine);
+        if (lane == 0u) atomicAdd(A.cnt + rid, (uint32_t)__popcll(bm));
+      }
+    float v[NG * 8];
+#pragma unroll
+    for (int q = 0; q < NG * 8; q++) v[q] = 0.0f;
+    if (mine) {
+      const int flags = (int)e.flags;
+      const float oe = A.max_shift ? __expf(e.oe - msh) : e.oe;   // o exp(o zhat / gamma) [/ exp(m)]
+      // t = dist^2 / r_eff^2 = A g |a x d|^2 (fp64: near the rim D = 1 - t is a
+      // small difference), a x d from the offsets sx = x - ax, sy = y - ay
+      const double sx = ray.x - e.u, sy = ray.y - e.v;
+      const double cr = (e.u * sy - e.v * sx) * crs;
+      const double t = e.a * ray.g * (sx * sx + sy * sy + cr * cr);
+      const float w = oe * (float)(1.0 - t);
+      float dw = -gC;
 #pragma unroll
       for (int ch = 0; ch < CM; ch++) {
-        if constexpr (CM <= SPLAT_REC_FEAT)
-          s_f[ch][threadIdx.x] = rec_feat(d, ch);              // here C = CM: features in the record
-        else
-          s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+        v[5 + ch] = gi[ch] * w;
+        dw = __builtin_fmaf(gi[ch], e.f[ch], dw);
       }
-#pragma unroll
-      for (int q = 0; q < NV; q++) s_acc[threadIdx.x][q] = 0.0f;
-      s_cnt[threadIdx.x] = 0u;
-      mask = quadrant_mask(tp, d);
-    }
-    build_quad_lists(s_l, mask);
-    // the wave walks its quadrant's list (a recorded sphere is never split
-    // over several steps, as with per-block lists, where the reduction and
-    // the gradient arithmetic would run once per block it reaches)
-    const int lc = __builtin_amdgcn_readfirstlane(s_l.cnt[wq]);
-    for (int k = 0; k < lc; k++) {
-      const int idx = __builtin_amdgcn_readfirstlane((int)s_l.idx[wq][k]);
-      const bool mine = tgt == b + (uint32_t)idx;
-      const uint64_t bm = ballot64(mine);
-      if (bm == 0) continue;
-      if constexpr (EXT)
-        if (A.cnt && lane == 0u) atomicAdd(&s_cnt[idx], (uint32_t)__popcll(bm));
-      float v[NG * 8];
-#pragma unroll
-      for (int q = 0; q < NG * 8; q++) v[q] = 0.0f;
-      if (mine) {
-        const double2 aa = s_a[idx], Ai = s_Ai[idx];
-        const float4 x = s_x[idx];
-        const int flags = s_flags[idx];
-        const float oe = A.max_shift ? __expf(x.y - msh) : x.y;     // o exp(o zhat / gamma) [/ exp(m)]
-        // D = 1 - A g |a x d|^2 with a x d from the offsets sx = x - ax, sy = y - ay
-        const double sx = ray.x - aa.x, sy = ray.y - aa.y;
-        const double cr = (aa.x * sy - aa.y * sx) * crs;
-        const double Dd = 1.0 - Ai.x * ray.g * (sx * sx + sy * sy + cr * cr);
-        const float w = oe * (float)Dd;
-        float dw = 0.0f;
-#pragma unroll
-        for (int ch = 0; ch < CM; ch++) {
-          v[5 + ch] = g[ch] * w * invN;
-          dw = __builtin_fmaf(g[ch], s_f[ch][idx] - Cimg[ch], dw);
-        }
-        dw *= invN;
-        v[4] = dw * w * x.z;
-        if (!(flags & 2)) {
-          // dist^2 = |q|^2 - (q.d)^2 / |d|^2 has gradient 2 q_perp, with
-          // q_perp = qz ((d.delta) g d - delta), delta = (sx, sy, 0).
-          const double dD = (double)dw * (double)oe;
-          const double dz = (double)dw * (double)w * (double)x.w;
-          const double dd2 = -dD * Ai.y * Ai.y;
-          const double c1 = (ray.x * sx + ray.y * sy) * ray.g * crs;
-          const double k2 = 2.0 * dd2 * (orth ? 1.0 : (double)x.x);
-          const double gq0 = k2 * (c1 * ray.x - sx), gq1 = k2 * (c1 * ray.y - sy);
-          v[0] = (float)gq0;
-          v[1] = (float)gq1;
-          v[2] = (float)(k2 * c1 - dz * inv_span);
-          if (!(flags & 1)) v[3] = (float)(dD * 2.0 * (1.0 - Dd) * Ai.y);
-          // the ray: d dist^2 / d d = -((q.d) / |d|^2) d dist^2 / d q, with
-          // (q.d) / |d|^2 = qz (1 - c1); orthographic: d dist^2 / d (x, y) = -d dist^2 / d (qx, qy)
-          const double s = orth ? 1.0 : (double)x.x * (1.0 - c1);
-          if constexpr (EXT) {
-            kgx = kgx - s * gq0;
-            kgy = kgy - s * gq1;
-          }
-        }
-        nxt++;
-        tgt = nxt < ntop ? my_top[nxt] : 0xffffffffu;
-      }
-#pragma unroll
-      for (int gq = 0; gq < NG; gq++) {
-        const float (&vg)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * gq]);
-        const float r = wave_sum8_transposed(vg);
-        const int q = 8 * gq + (int)lane;
-        if (lane < 8u && q < NV && r != 0.0f) atomicAdd(&s_acc[idx][q], r);
-      }
-    }
-    __syncthreads();
-    // Flush into the record's fp64 row (dq0, dq1, dq2, d_reff, d_opac, d_feat...):
-    // LPE lanes per entry over its values, so that one atomic instruction covers
-    // a few whole rows instead of one value of 64 rows.
-    {
-      constexpr int LPE = NV <= 8 ? 8 : NV <= 16 ? 16 : NV <= 32 ? 32 : 64;
-      constexpr int EPI = WAVE / LPE;
-      const int sub = (int)lane / LPE, ql = (int)lane % LPE;
-      for (int e0 = wq * EPI; e0 < (int)cnt; e0 += 4 * EPI) {
-        const int e = e0 + sub;
-        if (e < (int)cnt) {
-          double *row = A.accg + (size_t)s_rid[e] * (5 + A.C);
-          if (EXT && A.cnt && ql == 0) {
-            const uint32_t n = s_cnt[e];
-            if (n) atomicAdd(A.cnt + s_rid[e], n);
-          }
-#pragma unroll
-          for (int q0 = 0; q0 < NV; q0 += LPE) {
-            const int q = q0 + ql;
-            if (q < NV && (q < 5 || q - 5 < A.C)) {
-              const float x = s_acc[e][q];
-              if (x != 0.0f) atomicAdd(row + q, (double)x);
-            }
-          }
+      const float zhat = ((float)c.zfar - e.qz) * inv_span;
+      const float xz = __builtin_amdgcn_rcpf(e.opac) + zhat * igam;     // d ln w / d o (D fixed)
+      v[4] = dw * w * xz;
+      if (!(flags & 2)) {
+        // dist^2 = |q|^2 - (q.d)^2 / |d|^2 has gradient 2 q_perp, with
+        // q_perp = qz ((d.delta) g d - delta), delta = (sx, sy, 0)
+        const float ir = __builtin_amdgcn_rcpf(e.reff);
+        const float dD = dw * oe;
+        const float dz = dw * w * (e.opac * igam);
+        const float sxf = (float)sx, syf = (float)sy;
+        const float c1 = (rxf * sxf + ryf * syf) * rgf;
+        const float k2 = -2.0f * dD * ir * ir * (orth ? 1.0f : e.qz);
+        const float gq0 = k2 * (c1 * rxf - sxf), gq1 = k2 * (c1 * ryf - syf);
+        v[0] = gq0;
+        v[1] = gq1;
+        v[2] = k2 * c1 - dz * inv_span;
+        if (!(flags & 1)) v[3] = 2.0f * dD * (float)t * ir;
+        // the ray: d dist^2 / d d = -((q.d) / |d|^2) d dist^2 / d q, with
+        // (q.d) / |d|^2 = qz (1 - c1); orthographic: d dist^2 / d (x, y) = -d dist^2 / d (qx, qy)
+        if constexpr (EXT) {
+          const float sc = orth ? 1.0f : e.qz * (1.0f - c1);
+          kgx = kgx - sc * gq0;
+          kgy = kgy - sc * gq1;
         }
       }
     }
-    __syncthreads();
+    double *row = A.accg + (size_t)rid * rowlen;
+#pragma unroll
+    for (int gq = 0; gq < NG; gq++) {
+      const float (&vg)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * gq]);
+      const float r = wave_sum8_transposed_swap(vg);
+      const int q = 8 * gq + (int)lane;
+      if (lane < 8u && q < rowlen && r != 0.0f) atomicAdd(row + q, (double)r);
+    }
+    m = mn;
+  };
+  // two record buffers used in turn (no copy of the prefetched record per step)
+  SphEntry<CM> e0, e1;
+  uint32_t r0 = 0u, r1 = 0u;
+  if (m != NONE) {
+    r0 = rid_of(m);
+    e0 = sph_entry<CM>(r0, vbase, A.C, A.draw, A.aux, A.feat);
+  }
+  while (m != NONE) {
+    step(e0, r0, e1, r1);
+    if (m == NONE) break;
+    step(e1, r1, e0, r0);
   }
   if (EXT && A.kslot) {
     // intrinsics: the ray (x, y) = ((px - cx) / fx, (py - cy) / fy); per wave
     // the pixels' (d/dfx, d/dfy, d/dcx, d/dcy) are summed, lanes 0..3 add them
-    const double ifx = 1.0 / (double)c.fx, ify = 1.0 / (double)c.fy;
     double v8[8];
-    v8[0] = -kgx * ray.x * ifx;
-    v8[1] = -kgy * ray.y * ify;
-    v8[2] = -kgx * ifx;
-    v8[3] = -kgy * ify;
+    v8[0] = -(double)kgx * ray.x * c.ifx;
+    v8[1] = -(double)kgy * ray.y * c.ify;
+    v8[2] = -(double)kgx * c.ifx;
+    v8[3] = -(double)kgy * c.ify;
 #pragma unroll
     for (int q = 4; q < 8; q++) v8[q] = 0.0;
     const double r = wave_sum8_transposed_f64(v8);

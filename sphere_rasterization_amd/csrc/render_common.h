@@ -37,6 +37,7 @@ struct FwdArgs {
 struct BwdArgs {
   int n, C, top_k;
   float alpha_min, alpha_max, gamma;
+  float igamma;           // 1 / gamma (host)
   const DrawRec *draw;
   const AuxRec *aux;
   const uint32_t *vals;
@@ -226,7 +227,7 @@ struct SphereRay {
 
 __device__ __forceinline__ SphereRay sphere_ray(const ViewDev &c, const TilePix &tp) {
   SphereRay r;
-  const double ifx = 1.0 / (double)c.fx, ify = 1.0 / (double)c.fy;
+  const double ifx = c.ifx, ify = c.ify;
   r.x = ((double)tp.i + 0.5 - (double)c.cx) * ifx;
   r.y = ((double)tp.j + 0.5 - (double)c.cy) * ify;
   r.g = c.kind == SPLAT_CAM_ORTHOGRAPHIC ? 1.0 : 1.0 / (1.0 + r.x * r.x + r.y * r.y);
@@ -241,7 +242,7 @@ struct SphereQuad {
 
 // Coefficients of D / g over the tile of tp (d: the sphere's draw record).
 __device__ __forceinline__ SphereQuad sphere_quad(const ViewDev &c, const TilePix &tp, const DrawRec &d) {
-  const double ifx = 1.0 / (double)c.fx, ify = 1.0 / (double)c.fy;
+  const double ifx = c.ifx, ify = c.ify;
   const double xc = ((double)tp.x0 + 8.0 - (double)c.cx) * ifx;     // tile-centre ray
   const double yc = ((double)tp.y0 + 8.0 - (double)c.cy) * ify;
   const double ax = d.u, ay = d.v, A = d.a;

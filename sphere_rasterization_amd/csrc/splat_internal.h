@@ -22,6 +22,8 @@ struct ViewDev {
   float R[9], t[3];
   float fx, fy, cx, cy;
   float el_min, el_max, znear, zfar;
+  double ifx, ify;      // 1 / fx, 1 / fy (host, correctly rounded)
+  double ispan;         // 1 / (zfar - znear) (host)
 };
 
 struct ViewTable {
