@@ -40,8 +40,8 @@ HBM_PEAK_GBS = 8000.0
 #     (D, weight, normalisation, C colour FMAs, top-K bookkeeping); the counts are
 #     the oracle's exact per-pixel totals over the frame
 #   reverse compositor: per recorded (pixel, sphere) 45 lane-ops of gradient
-#     arithmetic; per (8x8 pixel quadrant, recorded sphere) 48 (eight values
-#     reduced over the wave in six steps)
+#     arithmetic; per (8x8 pixel quadrant, recorded sphere) the 8 x 63 additions
+#     that reduce its eight values over the quadrant's 64 pixels
 #   projection: read position, radius, opacity (20 B), write a 48-byte record
 #     and the pair count (4 B) per sphere
 #   binning: scan 8 B per sphere; emit 20 B per sphere + 12 B per pair; sort
@@ -51,7 +51,7 @@ HBM_PEAK_GBS = 8000.0
 OPS_PER_ENTRY = 7
 OPS_PER_HIT_BASE = 7          # + one fma per channel
 OPS_PER_RECORDED = 45
-OPS_PER_WAVE_SPHERE = 48
+OPS_PER_WAVE_SPHERE = 8 * 63
 PROJECT_BYTES_PER_PRIM = 20 + 48 + 4
 SCAN_BYTES_PER_PRIM = 8
 EMIT_BYTES_PER_PRIM, EMIT_BYTES_PER_PAIR = 20, 12
