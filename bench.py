@@ -89,6 +89,9 @@ def parse():
                     help="image rows the CPU oracle renders (fwd + bwd) on all host cores for the baseline")
     ap.add_argument("--cpu-1t-rows", type=int, default=1024,
                     help="image rows the CPU oracle renders (fwd + bwd) on one thread")
+    ap.add_argument("--atomic-direct-max", type=int, default=0,
+                    help="spheres: entries recorded by at most this many lanes of a wavefront add their gradient "
+                         "terms lane by lane instead of after the wavefront reduction (0: always reduce)")
     ap.add_argument("--no-kernel-profile", action="store_true",
                     help="skip the pass that takes per-kernel device times with torch.profiler")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -151,7 +154,7 @@ def main():
         if ev is not None:
             ev[3].record()
         # all views in one call (camera and lidar views run separate kernels)
-        rz.backward(dimg, grads=grads)
+        rz.backward(dimg, grads=grads, atomic_direct_max=args.atomic_direct_max)
         if ev is not None:
             ev[4].record()
 
@@ -164,7 +167,7 @@ def main():
         ev[0].record()
         rz.render_fwd()
         ev[1].record()
-        rz.backward(dimg, grads=grads)
+        rz.backward(dimg, grads=grads, atomic_direct_max=args.atomic_direct_max)
 
     for _ in range(args.warmup):
         step()

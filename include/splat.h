@@ -142,7 +142,14 @@ typedef struct {
  * splat_render_fwd call before this one on the stream was given this call's workspace
  * (so it cleared the sums the reverse pass accumulates into) and that no
  * splat_render_bwd has used the workspace since; the call then skips that clearing.
- * Stating it falsely gives wrong gradients; 0 is always correct. */
+ * Stating it falsely gives wrong gradients; 0 is always correct.
+ * atomic_direct_max (spheres, up to four channels, without cam_K or normalize;
+ * otherwise ignored): 0 (default) sums every recorded sphere's terms over the
+ * wavefront before its global atomic adds; k > 0 lets the lanes of a wavefront
+ * add their own terms with global atomics when at most k of them recorded the
+ * sphere (the split between in-register reduction and atomic units of DISTWAR,
+ * arXiv author page abstract). Same gradients up to summation order; on gfx950 it
+ * measured slower for every k, so 0 is the default. Negative values are rejected. */
 typedef struct {
   float *pos, *scale, *rot, *opacity, *feat;
   float *cam_R, *cam_t;
@@ -150,6 +157,7 @@ typedef struct {
   int32_t accumulate;
   int32_t normalize;
   int32_t sums_cleared;
+  int32_t atomic_direct_max;
 } splat_grads;
 
 /* ---- size queries (host only, no device work) ---------------------------- */

@@ -51,7 +51,8 @@ class splat_grads(C.Structure):
     _fields_ = [("pos", C.c_void_p), ("scale", C.c_void_p), ("rot", C.c_void_p),
                 ("opacity", C.c_void_p), ("feat", C.c_void_p), ("cam_R", C.c_void_p),
                 ("cam_t", C.c_void_p), ("cam_K", C.c_void_p), ("accumulate", C.c_int32),
-                ("normalize", C.c_int32), ("sums_cleared", C.c_int32)]
+                ("normalize", C.c_int32), ("sums_cleared", C.c_int32),
+                ("atomic_direct_max", C.c_int32)]
 
 
 class SplatError(RuntimeError):

@@ -403,6 +403,7 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
     CHECK(grads->cam_K == nullptr, SPLAT_ERR_UNSUPPORTED, "intrinsic gradients are for spheres only");
     CHECK(!grads->normalize, SPLAT_ERR_UNSUPPORTED, "gradient normalisation is for spheres only");
   }
+  CHECK(grads->atomic_direct_max >= 0, SPLAT_ERR_INVALID_ARG, "atomic_direct_max must be >= 0");
   CHECK(workspace != nullptr, SPLAT_ERR_INVALID_ARG, "NULL workspace");
   CHECK(ws_bytes >= bwd_workspace_bytes((long long)n_views * prims->n, prims->channels), SPLAT_ERR_CAPACITY,
         "backward workspace too small");
@@ -422,6 +423,7 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   A.cam_part = acc.cam;
   A.kslot = grads->cam_K ? acc.kslot : nullptr;
   A.cnt = grads->normalize ? acc.cnt : nullptr;
+  A.direct_max = prims->kind == SPLAT_PRIM_SPHERE ? grads->atomic_direct_max : 0;
   return launch_render_bwd(vt, view_begin, view_begin + view_count, A, prims, L.bin, grads, stream);
 }
 

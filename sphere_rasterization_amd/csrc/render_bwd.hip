@@ -643,8 +643,11 @@ __device__ __forceinline__ SphEntry<CM> sph_entry(uint32_t rid, long long vbase,
 }
 
 // EXT: the call asks for intrinsic gradients or gradient normalisation (their
-// per-contribution work is compiled out of the plain reverse pass).
-template <int CM, bool EXT>
+// per-contribution work is compiled out of the plain reverse pass). DIRECT:
+// entries recorded by at most A.direct_max lanes of a wave skip the wave
+// reduction and add lane by lane (a separate instance: in the default one no
+// atomic is conditional on the lane count, which keeps its memory waits exact).
+template <int CM, bool EXT, bool DIRECT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_bwd_sphere(
     ViewTable vt, BwdArgs A, int tile_begin) {
   constexpr int NV = 5 + CM;                  // dq0, dq1, dq2, d_reff, d_opac, d_feat...
@@ -786,12 +789,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       }
     }
     double *row = A.accg + (size_t)rid * rowlen;
+    bool reduce = true;
+    if constexpr (DIRECT) {
+      // few lanes recorded the entry: they add their values straight to the
+      // row (global atomics resolved in L2) instead of the wave reduction
+      // (DISTWAR's split between in-register reduction and atomic units)
+      reduce = __popcll(ballot64(mine)) > A.direct_max;
+      if (!reduce && mine) {
 #pragma unroll
-    for (int gq = 0; gq < NG; gq++) {
-      const float (&vg)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * gq]);
-      const float r = wave_sum8_transposed_swap(vg);
-      const int q = 8 * gq + (int)lane;
-      if (lane < 8u && q < rowlen && r != 0.0f) atomicAdd(row + q, (double)r);
+        for (int q = 0; q < NV; q++)
+          if (q < rowlen) atomicAdd(row + q, (double)v[q]);
+      }
+    }
+    if (reduce) {
+#pragma unroll
+      for (int gq = 0; gq < NG; gq++) {
+        const float (&vg)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * gq]);
+        const float r = wave_sum8_transposed_swap(vg);
+        const int q = 8 * gq + (int)lane;
+        if (lane < 8u && q < rowlen && r != 0.0f) atomicAdd(row + q, (double)r);
+      }
     }
     m = mn;
   };
@@ -1283,6 +1300,8 @@ int launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begi
   if (kind == SPLAT_PRIM_SPHERE) {
     if (A.kslot || A.cnt)
       hipLaunchKernelGGL((k_bwd_sphere<CM, true>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
+    else if (CM <= 4 && A.direct_max > 0)
+      hipLaunchKernelGGL((k_bwd_sphere<CM, false, CM <= 4>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
     else
       hipLaunchKernelGGL((k_bwd_sphere<CM, false>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
   } else {

@@ -56,6 +56,7 @@ struct BwdArgs {
   double *kslot;          // [views][SPLAT_K_SLOTS][4] intrinsic-gradient sums, or NULL (not requested)
   uint32_t *cnt;          // [records] pixels that recorded the sphere, or NULL (no normalisation)
   int max_shift;          // spheres: weights relative to the per-pixel shift held in T_final
+  int direct_max;         // spheres: entries recorded by at most this many lanes add lane by lane
 };
 
 struct TilePix {

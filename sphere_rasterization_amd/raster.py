@@ -155,7 +155,7 @@ class Rasterizer:
 
     def backward(self, dimg: torch.Tensor, want=("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t", "cam_K"),
                  view_begin: int = 0, view_count: Optional[int] = None, grads=None, accumulate=False,
-                 normalize=False):
+                 normalize=False, atomic_direct_max: int = 0):
         if view_count is None:
             view_count = self.V - view_begin
         if self.bwd_ws is None:
@@ -168,6 +168,7 @@ class Rasterizer:
             setattr(g, k, _ptr(grads.get(k)))
         g.accumulate = 1 if accumulate else 0
         g.normalize = 1 if normalize else 0
+        g.atomic_direct_max = int(atomic_direct_max)
         # only the first backward after a clearing forward may skip the clearing
         g.sums_cleared = 1 if self.sums_cleared else 0
         self.sums_cleared = False

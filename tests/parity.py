@@ -268,7 +268,8 @@ def grad_check(name, got, ref, mag=None, info=None):
     return worst
 
 
-def compare_backward(rz, orc, ref, g_views, masked=None, names=None, view_groups=None, normalize=False):
+def compare_backward(rz, orc, ref, g_views, masked=None, names=None, view_groups=None, normalize=False,
+                     bwd_kw=None):
     """Run both backward passes on the same (flag-masked) upstream gradient.
 
     view_groups: list of (view_begin, view_count) GPU calls accumulating into one
@@ -276,13 +277,14 @@ def compare_backward(rz, orc, ref, g_views, masked=None, names=None, view_groups
     if masked is None:
         masked, _ = masked_grads(orc, g_views)
     dimg = torch.from_numpy(np.concatenate([m.reshape(-1) for m in masked])).to(rz.device)
+    kw = dict(bwd_kw or {})
     if view_groups is None:
-        grads = rz.backward(dimg, normalize=normalize)
+        grads = rz.backward(dimg, normalize=normalize, **kw)
     else:
         grads = None
         for b, c in view_groups:
             grads = rz.backward(dimg, view_begin=b, view_count=c, grads=grads, accumulate=grads is not None,
-                                normalize=normalize)
+                                normalize=normalize, **kw)
     torch.cuda.synchronize()
     og = orc.backward(masked, with_mag=True, normalize=normalize)
     names = names or [k for k in ("pos", "scale", "rot", "opacity", "feat", "cam_R", "cam_t", "cam_K") if k in grads]

@@ -20,7 +20,7 @@ def _rz(scene, **kw):
     return Rasterizer(scene, device="cuda", **kw)
 
 
-def _run(scene, grad_seed, name, check_grads=True, view_groups=None, normalize=False, fwd_kw=None):
+def _run(scene, grad_seed, name, check_grads=True, view_groups=None, normalize=False, fwd_kw=None, bwd_kw=None):
     _log(f"[case] {name}: n={scene.n} views={len(scene.cams)} kind={scene.kind}")
     rz = _rz(scene)
     rz.forward()
@@ -31,7 +31,7 @@ def _run(scene, grad_seed, name, check_grads=True, view_groups=None, normalize=F
          f"T_model={st.get('T_model', 0):.2f} N_model={st.get('N_model', 0):.2f}")
     if check_grads:
         g = S.upstream_grads(scene, grad_seed)
-        bw = compare_backward(rz, orc, None, g, view_groups=view_groups, normalize=normalize)
+        bw = compare_backward(rz, orc, None, g, view_groups=view_groups, normalize=normalize, bwd_kw=bwd_kw)
         _log(f"  bwd ok worst={bw['worst']:.3f} " + " ".join(f"{k}={v:.2f}" for k, v in bw["per"].items()))
         _log("  sum-term audit: " + " ".join(f"{k}:{a['worst_nomag']:.2f}/{a['need_mag']}of{a['n']}"
                                              for k, a in bw["audit"].items()))
@@ -70,6 +70,15 @@ def test_spheres_behind_the_far_plane():
     R, t = cam.R.astype(np.float64), cam.t.astype(np.float64)
     sc.pos = np.ascontiguousarray(((qs - t) @ R).astype(np.float32))
     _run(sc, 63, "spheres 120k @320x240 depths beyond zfar")
+
+
+def test_sphere_direct_atomics():
+    """The reverse pass's lane-by-lane atomics for entries few lanes recorded
+    (atomic_direct_max, the DISTWAR-style split) give the oracle's gradients, with
+    thresholds that route a small and a large share of the entries that way."""
+    sc = S.pulsar_spheres(seed=64, n=150_000, width=400, height=300)
+    for k in (2, 16):
+        _run(sc, 65, f"spheres 150k @400x300, direct atomics up to {k} lanes", bwd_kw=dict(atomic_direct_max=k))
 
 
 def test_sphere_channel_counts():

@@ -207,3 +207,18 @@ def test_noalloc_sort_size_limit_on_host():
     lib = L.lib()
     assert lib.splat_bin_sort_noalloc(cams, 1, 10, 8, 8, big, 8, 8, 8, 8, 8, None) == L.SPLAT_ERR_CAPACITY
     assert lib.splat_bin_sort_noalloc(cams, 1, 10, 8, 8, 100, 8, 8, None, 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
+
+
+def test_negative_atomic_direct_max_is_rejected():
+    from sphere_rasterization_amd.raster import make_cams, make_params
+    sc = S.pulsar_spheres(n=10)
+    prm, _ = make_params(sc.params, 3)
+    lib = L.lib()
+    pr = L.splat_prims()
+    pr.kind, pr.n, pr.channels = 2, 10, 3
+    pr.pos = pr.scale = pr.opacity = pr.feat = 8
+    g = L.splat_grads()
+    g.atomic_direct_max = -1
+    rc = lib.splat_render_bwd(make_cams(sc.cams), 1, 0, 1, C.byref(pr), C.byref(prm), 8, 8, 8, 8, 8, None, None, 8,
+                              8, 8, C.byref(g), 8, 1 << 40, None)
+    assert rc == L.SPLAT_ERR_INVALID_ARG
