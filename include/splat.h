@@ -15,8 +15,14 @@
  *
  * Conventions for every call:
  *  - All array pointers are caller-owned DEVICE memory unless marked HOST.
- *    The library allocates nothing and keeps no mutable global state; calls
- *    on different streams may overlap freely.
+ *    The library allocates no device memory. Its global state, per device:
+ *    (a) one side stream and two events, created by the first render call
+ *    that composites Gaussians in both pinhole and spherical views (unless
+ *    splat_params.serial_views = 1), and a mutex that such a call holds while
+ *    it enqueues its work: those calls serialise their launches on one device
+ *    (not their execution), and their pinhole views share the side stream;
+ *    (b) the fixed device array of splat_bin_sort_noalloc. Every other call
+ *    touches no library state, and calls on different streams may overlap.
  *  - Floating point arrays are fp32, row-major, C-contiguous.
  *  - Work is enqueued on `stream` (0 = the null stream); no call blocks on
  *    the device. Argument errors are detected on the host and returned before
@@ -121,6 +127,12 @@ typedef struct {
    * and T_final (spheres: otherwise unused) receives m, which splat_render_bwd
    * then reads (T_final must be given to both calls). Must be 0 for Gaussians. */
   int32_t max_shift;
+  /* Gaussians, render calls over both pinhole and spherical views: 0 (default) runs
+   * the pinhole views on the library's side stream for the device, beside the
+   * spherical views on `stream` (forked from and joined back into `stream`, see the
+   * conventions above); 1 runs every kernel on `stream` alone, using no library state.
+   * Must be 0 or 1. */
+  int32_t serial_views;
 } splat_params;
 
 /* Gradient outputs (DEVICE); NULL = not requested (skipped, nothing written).

@@ -44,7 +44,7 @@ class splat_params(C.Structure):
     _fields_ = [("alpha_min", C.c_float), ("alpha_max", C.c_float), ("T_min", C.c_float),
                 ("gamma", C.c_float), ("bg_weight", C.c_float), ("tau", C.c_float),
                 ("top_k", C.c_int32), ("background", C.POINTER(C.c_float)), ("top_by_depth", C.c_int32),
-                ("max_shift", C.c_int32)]
+                ("max_shift", C.c_int32), ("serial_views", C.c_int32)]
 
 
 class splat_grads(C.Structure):

@@ -1,7 +1,8 @@
 // extern "C" entry points of libsplat: argument checks on the host, view-table
 // construction, then kernel launches on the caller's stream. No allocation of
-// device memory and no host synchronisation; the only global state is one side
-// stream per device (created on first use, see side_begin).
+// device memory and no host synchronisation. Global state per device: one side
+// stream with its two events and lock (created on first use, see side_begin),
+// and the array of splat_bin_sort_noalloc.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -184,6 +185,7 @@ int check_params(const splat_params *m, int kind) {
         "alpha parameters");
   CHECK(m->alpha_max > 0.0f && m->alpha_max < 1.0f, SPLAT_ERR_INVALID_ARG, "alpha_max must lie in (0, 1)");
   CHECK(m->alpha_min >= 0.0f && m->T_min >= 0.0f, SPLAT_ERR_INVALID_ARG, "negative thresholds");
+  CHECK(m->serial_views == 0 || m->serial_views == 1, SPLAT_ERR_INVALID_ARG, "serial_views must be 0 or 1");
   if (kind == SPLAT_PRIM_SPHERE) {
     CHECK(isfinite(m->gamma) && m->gamma > 0.0f, SPLAT_ERR_INVALID_ARG, "gamma must be > 0");
     CHECK(isfinite(m->tau) && m->tau >= 0.0f, SPLAT_ERR_INVALID_ARG, "tau must be >= 0");
@@ -357,6 +359,7 @@ int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *p
   memset(&A, 0, sizeof(A));
   A.n = prims->n; A.C = prims->channels; A.top_k = prm->top_k; A.top_by_depth = prm->top_by_depth;
   A.max_shift = prm->max_shift;
+  A.serial_views = prm->serial_views;
   A.alpha_min = prm->alpha_min; A.alpha_max = prm->alpha_max; A.T_min = prm->T_min;
   A.tau = prm->tau; A.bg_weight = prm->bg_weight;
   for (int c = 0; c < A.C; c++) A.bg[c] = prm->background ? prm->background[c] : 0.0f;
@@ -413,6 +416,7 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   A.alpha_min = prm->alpha_min; A.alpha_max = prm->alpha_max; A.gamma = prm->gamma;
   A.igamma = (float)(1.0 / (double)prm->gamma);
   A.max_shift = prims->kind == SPLAT_PRIM_SPHERE ? prm->max_shift : 0;
+  A.serial_views = prm->serial_views;
   ProjLayout L = proj_layout(const_cast<void *>(proj), (long long)n_views * prims->n);
   A.draw = L.draw; A.aux = L.aux; A.vals = vals; A.ranges = tile_ranges; A.overflow = overflow;
   A.feat = prims->feat; A.img = img; A.T_final = T_final; A.last = last; A.norm = norm; A.topk = topk;

@@ -1311,7 +1311,7 @@ int launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begi
     bool has_pin = false, has_sph = false;
     for (int v = vbeg; v < vend; v++) (vt.v[v].kind == SPLAT_CAM_SPHERICAL ? has_sph : has_pin) = true;
     hipStream_t side = stream;
-    const bool fork = has_pin && has_sph;
+    const bool fork = has_pin && has_sph && !A.serial_views;
     if (fork) {
       const int rc = side_begin(stream, &side);
       if (rc != SPLAT_OK) return rc;

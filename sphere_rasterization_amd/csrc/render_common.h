@@ -14,6 +14,7 @@ struct FwdArgs {
   int n, C, top_k;
   int top_by_depth;       // spheres: record the top_k closest entry points, not the first top_k
   int max_shift;          // spheres: draw records hold log-weights; blend relative to a per-pixel shift
+  int serial_views;       // Gaussians: camera and spherical views on the caller's stream only
   float alpha_min, alpha_max, T_min, tau, bg_weight;
   const DrawRec *draw;
   const AuxRec *aux;
@@ -57,6 +58,7 @@ struct BwdArgs {
   uint32_t *cnt;          // [records] pixels that recorded the sphere, or NULL (no normalisation)
   int max_shift;          // spheres: weights relative to the per-pixel shift held in T_final
   int direct_max;         // spheres: entries recorded by at most this many lanes add lane by lane
+  int serial_views;       // Gaussians: camera and spherical views on the caller's stream only
 };
 
 struct TilePix {

@@ -37,6 +37,7 @@ def make_params(p: Params, channels: int):
     s.gamma, s.bg_weight, s.tau, s.top_k = p.gamma, p.bg_weight, p.tau, int(p.top_k)
     s.top_by_depth = int(getattr(p, "top_by_depth", 0))
     s.max_shift = int(getattr(p, "max_shift", 0))
+    s.serial_views = int(getattr(p, "serial_views", 0))
     keep = None
     if p.background is not None:
         keep = (C.c_float * channels)(*[float(x) for x in np.asarray(p.background, np.float32)[:channels]])

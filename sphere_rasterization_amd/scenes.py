@@ -80,6 +80,7 @@ class Params:
     background: Optional[np.ndarray] = None   # [channels] float32 or None (= 0)
     top_by_depth: int = 0      # spheres: 1 = record the top_k closest intersections, not the first top_k
     max_shift: int = 0         # spheres: 1 = weights relative to a per-pixel shift (needed for gamma < 1/88)
+    serial_views: int = 0      # Gaussians: 1 = camera and spherical views on the caller's stream only
 
     def __post_init__(self):
         for k in ("alpha_min", "alpha_max", "T_min", "gamma", "bg_weight", "tau"):

@@ -255,6 +255,86 @@ def test_multiview_with_lidar():
         _log(f"  one call {k} worst={w:.3f}")
 
 
+def test_multiview_serial_views():
+    """splat_params.serial_views = 1 (every kernel on the caller's stream, no side
+    stream): the same forward outputs bit for bit as the forked call, and gradients
+    that agree with the oracle."""
+    sc = S.gauss3d(seed=14, n=20_000)
+    R1 = TS.rotation(np.random.default_rng(1))
+    sc.cams = [sc.cams[0],
+               S.Camera(S.CAM_PINHOLE, 320, 200, R1, [0.2, -0.1, 9.0], fx=300.0, fy=310.0, cx=160.0, cy=100.0,
+                        znear=0.2, zfar=100.0),
+               TS.lidar(512, 64, t=[0.0, 0.0, 0.0])]
+    _log("[case] multiview, serial views")
+    forked = _rz(sc)
+    forked.forward()
+    img_f, T_f, last_f = forked.img.clone(), forked.T_final.clone(), forked.last.clone()
+    sc.params = S.Params(serial_views=1)
+    rz = _rz(sc)
+    rz.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(rz.img, img_f) and torch.equal(rz.T_final, T_f) and torch.equal(rz.last, last_f)
+    orc = O.Oracle(sc)
+    compare_forward(rz, orc)
+    g = [np.random.default_rng(40 + v).standard_normal((sc.view_channels(v), c.height, c.width)).astype(np.float32)
+         for v, c in enumerate(sc.cams)]
+    bw = compare_backward(rz, orc, None, g)
+    _log(f"  bwd ok worst={bw['worst']:.3f}")
+
+
+def test_autograd_render():
+    """render() as a torch.autograd.Function: loss.backward() gives the oracle's
+    gradients for the primitive tensors and the camera R, t that require them; an
+    input that does not require grad gets none; a second render before the
+    backward is refused. Spheres, then 3D Gaussians."""
+    from sphere_rasterization_amd.autograd import render
+    from tests.parity import grad_check
+    sc = S.pulsar_spheres(seed=66, n=60_000, width=256, height=192)
+    _log("[case] autograd: spheres 60k @256x192 with camera R, t")
+    rz = _rz(sc)
+    pos = rz.t["pos"].clone().requires_grad_(True)
+    scale = rz.t["scale"].clone()                       # not asked for
+    opacity = rz.t["opacity"].clone().requires_grad_(True)
+    feat = rz.t["feat"].clone().requires_grad_(True)
+    cam_R = torch.tensor(np.asarray(sc.cams[0].R, np.float32)).reshape(1, 3, 3).requires_grad_(True)
+    cam_t = torch.tensor(np.asarray(sc.cams[0].t, np.float32)).reshape(1, 3).requires_grad_(True)
+    img = render(rz, pos=pos, scale=scale, opacity=opacity, feat=feat, cam_R=cam_R, cam_t=cam_t)
+    orc = O.Oracle(sc)
+    compare_forward(rz, orc)
+    masked, _ = masked_grads(orc, S.upstream_grads(sc, 67))
+    gm = torch.from_numpy(np.concatenate([m.reshape(-1) for m in masked])).cuda()
+    (img * gm).sum().backward()
+    og = orc.backward(masked, with_mag=True)
+    assert scale.grad is None
+    for name, t in (("pos", pos), ("opacity", opacity), ("feat", feat)):
+        w = grad_check(name, t.grad.cpu().numpy(), og[name].reshape(t.shape), og["mag"][name].reshape(t.shape))
+        _log(f"  {name} worst={w:.3f}")
+    for name, t in (("cam_R", cam_R), ("cam_t", cam_t)):
+        assert t.grad is not None and t.grad.device.type == "cpu"
+        w = grad_check(name, t.grad.numpy().reshape(-1), og[name].reshape(-1), og["mag"][name].reshape(-1))
+        _log(f"  {name} worst={w:.3f}")
+    # a render between a render and its backward leaves that backward nothing to use
+    img1 = render(rz, pos=pos, opacity=opacity, feat=feat)
+    render(rz, pos=pos, opacity=opacity, feat=feat)
+    with pytest.raises(RuntimeError):
+        img1.sum().backward()
+
+    gs = S.gauss3d(seed=68, n=30_000, width=320, height=240)
+    _log("[case] autograd: gauss3d 30k @320x240")
+    rz = _rz(gs)
+    ts = {k: rz.t[k].clone().requires_grad_(True) for k in ("pos", "scale", "rot", "opacity", "feat")}
+    img = render(rz, **ts)
+    orc = O.Oracle(gs)
+    compare_forward(rz, orc)
+    masked, _ = masked_grads(orc, S.upstream_grads(gs, 69))
+    gm = torch.from_numpy(np.concatenate([m.reshape(-1) for m in masked])).cuda()
+    (img * gm).sum().backward()
+    og = orc.backward(masked, with_mag=True)
+    for name, t in ts.items():
+        w = grad_check(name, t.grad.cpu().numpy(), og[name].reshape(t.shape), og["mag"][name].reshape(t.shape))
+        _log(f"  {name} worst={w:.3f}")
+
+
 def test_spheres_two_views():
     """Spheres seen by two pinhole views: one backward call over both views
     (per-view camera reduction), and one call per view accumulating."""

@@ -222,3 +222,14 @@ def test_negative_atomic_direct_max_is_rejected():
     rc = lib.splat_render_bwd(make_cams(sc.cams), 1, 0, 1, C.byref(pr), C.byref(prm), 8, 8, 8, 8, 8, None, None, 8,
                               8, 8, C.byref(g), 8, 1 << 40, None)
     assert rc == L.SPLAT_ERR_INVALID_ARG
+
+
+def test_serial_views_values():
+    from sphere_rasterization_amd.raster import make_cams, make_params
+    sc = S.gauss3d(n=10)
+    lib = L.lib()
+    pr = L.splat_prims()
+    pr.kind, pr.n, pr.channels = 1, 10, 3
+    pr.pos = pr.scale = pr.rot = pr.opacity = pr.feat = 8
+    prm, _ = make_params(S.Params(serial_views=2), 3)
+    assert lib.splat_project(make_cams(sc.cams), 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
