@@ -200,7 +200,8 @@ def test_tile_scan_beyond_one_workgroup():
     """More than 65536 tiles (the three-kernel tile scan, long-segment work lists
     filled with atomics) and a cluster of large Gaussians whose tiles hold up to
     12k pairs (the MSD split ahead of the LDS merge sort). Binning is compared in
-    full, the image on a pixel sample around and away from the cluster."""
+    full, the image on a pixel sample around and away from the cluster, and the
+    gradients of a reverse pass whose upstream gradient lives on that sample."""
     sc = S.gauss3d(seed=18, n=120_000, width=4160, height=4128)
     c = sc.cams[0]
     sc.cams = [S.Camera(S.CAM_PINHOLE, 4160, 4128, c.R, c.t, fx=1500.0, fy=1500.0, cx=2000.0, cy=2100.0,
@@ -216,8 +217,24 @@ def test_tile_scan_beyond_one_workgroup():
     prng = np.random.default_rng(6)
     pix = np.concatenate([prng.choice(4160 * 4128, 20_000, replace=False),
                           (2100 + prng.integers(-300, 300, 20_000)) * 4160 + 2000 + prng.integers(-300, 300, 20_000)])
-    st = compare_forward(rz, orc, pix=np.unique(pix).astype(np.int64))
+    pix = np.unique(pix).astype(np.int64)
+    st = compare_forward(rz, orc, pix=pix)
     _log(f"  fwd ok pairs={st.get('pairs')} img_err={st['img_err']:.2e} flagged={st['flag_frac']:.2e}")
+    # reverse pass with the upstream gradient on the sampled pixels only (those
+    # without a near tie), so the oracle's reverse pass composites just those
+    flags = orc.render(pix)["flags"]
+    keep = pix[flags == 0]
+    g = np.zeros((sc.channels, 4128, 4160), np.float32)
+    g.reshape(sc.channels, -1)[:, keep] = np.random.default_rng(7).standard_normal((sc.channels, len(keep)))
+    orc.set_branches(None)
+    dimg = torch.from_numpy(g.reshape(-1)).cuda()
+    grads = rz.backward(dimg)
+    torch.cuda.synchronize()
+    og = orc.backward([g], with_mag=True)
+    from tests.parity import grad_check
+    for k in ("pos", "scale", "rot", "opacity", "feat"):
+        w = grad_check(k, grads[k].cpu().numpy(), og[k].reshape(grads[k].shape), og["mag"][k].reshape(grads[k].shape))
+        _log(f"  bwd {k} worst={w:.3f} (upstream gradient on {len(keep)} pixels)")
 
 
 def test_multiview_with_lidar():
