@@ -61,11 +61,11 @@ GRAD_BYTES_PER_PRIM = 60
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 210637709
+FWD_TRAFFIC_BYTES = 210629607
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
-FWD_TRAFFIC_SHA256 = "e8c85bf7b5fd546051e7d95c864bc7b88fbc8dcef44b7ae727f06827abbf7956"
+FWD_TRAFFIC_SHA256 = "7d309d8281d0f43c9a07edf5fafcd39c8eaca6e380942834f43dbf05781b5809"
 BIN_KERNELS = ("k_thist", "k_col_scan", "k_tscatter", "k_seg_sort", "k_tile_scan1", "k_scan_reduce", "k_scan_top",
                "k_tile_ranges", "k_fill_u32", "k_tile_count", "k_bucket")
 
