@@ -317,34 +317,35 @@ __device__ __forceinline__ bool project_one(const ViewDev &c, const PrimArgs &P,
   return true;
 }
 
-// Thread per (view, primitive); grid (ceil(n / 256), views). The drawing (64 B)
-// and backward (32 B) records are staged in LDS and leave as whole contiguous
-// blocks: stored from registers, each lane's 16-byte pieces would land 64 or
-// 32 bytes apart and the partial-line writes run at half the write bandwidth.
+// Thread per (view, primitive); grid (ceil(n / 256), views). The drawing records
+// (64 B) are staged in LDS and leave as whole contiguous blocks: stored from
+// registers, each lane's 16-byte pieces would land 64 bytes apart and the
+// partial-line writes run at half the write bandwidth. The backward records
+// (16 B) are contiguous across the lanes already and are stored directly.
 template <int KIND>
 __global__ __launch_bounds__(256) void k_project(ViewTable vt, PrimArgs P, ProjLayout L, uint32_t *counts) {
   __shared__ DrawRec s_d[256];
-  __shared__ AuxRec s_a[256];
   __shared__ unsigned char s_vis[256];
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int view = blockIdx.y;
   const ViewDev &c = vt.v[view];
   bool vis = false;
-  if (i < P.n) vis = project_one<KIND>(c, P, L, counts, (long long)view * P.n + i, i, s_d[threadIdx.x], s_a[threadIdx.x]);
+  const long long k = (long long)view * P.n + i;
+  if (i < P.n) {
+    AuxRec a;
+    vis = project_one<KIND>(c, P, L, counts, k, i, s_d[threadIdx.x], a);
+    if (vis) L.aux[k] = a;
+  }
   s_vis[threadIdx.x] = vis ? 1 : 0;
   __syncthreads();
   // only visible records' pieces are stored (a view may cull most of the scene)
   const int nblk = min((int)blockDim.x, P.n - (int)(blockIdx.x * blockDim.x));
   const long long k0 = (long long)view * P.n + (long long)blockIdx.x * blockDim.x;
-  constexpr int DW = sizeof(DrawRec) / 16, AW = sizeof(AuxRec) / 16;
+  constexpr int DW = sizeof(DrawRec) / 16;
   uint4 *gd = reinterpret_cast<uint4 *>(L.draw + k0);
   const uint4 *sd = reinterpret_cast<const uint4 *>(s_d);
   for (int j = threadIdx.x; j < nblk * DW; j += blockDim.x)
     if (s_vis[j / DW]) gd[j] = sd[j];
-  uint4 *ga = reinterpret_cast<uint4 *>(L.aux + k0);
-  const uint4 *sa = reinterpret_cast<const uint4 *>(s_a);
-  for (int j = threadIdx.x; j < nblk * AW; j += blockDim.x)
-    if (s_vis[j / AW]) ga[j] = sa[j];
 }
 
 }  // namespace
