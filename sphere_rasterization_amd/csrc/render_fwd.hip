@@ -181,8 +181,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
             lgn = hit ? msh + __logf(N) : lgn;
           }
         } else {
-          // 0 or 1 times a finite weight: straight-line code, no branch around it
-          const float w = (hit ? 1.0f : 0.0f) * (t[0] * (float)(num * ray.g));
+          // the weight is formed on every lane (the empty asm keeps the compiler
+          // from moving it under a branch) and selected: straight-line code
+          float wx = t[0] * (float)(num * ray.g);
+          asm volatile("" : "+v"(wx));
+          const float w = hit ? wx : 0.0f;
           N += w;
 #pragma unroll
           for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch]);
