@@ -58,14 +58,24 @@ EMIT_BYTES_PER_PRIM, EMIT_BYTES_PER_PAIR = 20, 12
 SORT_BYTES_PER_PAIR_PASS = 24
 RANGE_BYTES_PER_PAIR, RANGE_BYTES_PER_TILE = 8, 8
 GRAD_BYTES_PER_PRIM = 60
+# The Gaussian workloads (parity cases, not the headline) by the same rules, the
+# survey's "other configs scale with N and P": projection reads the primitive's
+# inputs once (2D: centre, sigma, depth, opacity, 20 B; 3D: mean, scale,
+# rotation, opacity, 44 B) and writes a ~32-byte record and the pair count per
+# (view, primitive); the gradient tail reads each record's 2D gradients
+# ((2 + 3 + 1 + C) fp32, C the view's channels) and the inputs once, and writes
+# the inputs' gradients once (plus 4 B per feature channel)
+GAUSS_READ_BYTES = {0: 20, 1: 44}
+GAUSS_RECORD_BYTES = 32 + 4
+GAUSS_GRAD_WRITE_BYTES = {0: 8 + 4 + 4, 1: 44}
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 210629607
+FWD_TRAFFIC_BYTES = 210688948
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
-FWD_TRAFFIC_SHA256 = "7d309d8281d0f43c9a07edf5fafcd39c8eaca6e380942834f43dbf05781b5809"
+FWD_TRAFFIC_SHA256 = "d88527fe2f5a64127d75d959d5bd5e559a0d52abbba5e1409169d9ba3fcc7168"
 BIN_KERNELS = ("k_thist", "k_col_scan", "k_tscatter", "k_seg_sort", "k_tile_scan1", "k_scan_reduce", "k_scan_top",
                "k_tile_ranges", "k_fill_u32", "k_tile_count", "k_bucket")
 
@@ -223,7 +233,7 @@ def main():
         out["cpu_baseline"] = cpu["json"]
     if wl == 3:
         out["roofline"] = roofline(fwd_kernel_ms, cpu, scene)
-        out["kernels"] = kernel_rooflines(ktimes, cpu, scene, npairs, rz.total_tiles)
+    out["kernels"] = kernel_rooflines(ktimes, cpu, scene, npairs, rz.total_tiles)
     if args.hbm_copy:
         out["hbm_copy_GBps"] = hbm_copy(torch, dev)
     print(json.dumps(out), flush=True)
@@ -339,29 +349,49 @@ def _frac(work, us, peak, unit_scale):
     return round(achieved, 3), round(achieved / peak, 4)
 
 
+def project_bytes(scene):
+    """Algorithmic HBM bytes of the projection (see above)."""
+    V = len(scene.cams)
+    if scene.kind == 2:
+        return PROJECT_BYTES_PER_PRIM * V * scene.n
+    return GAUSS_READ_BYTES[scene.kind] * scene.n + GAUSS_RECORD_BYTES * V * scene.n
+
+
+def grad_tail_bytes(scene):
+    """Algorithmic HBM bytes of the gradient tail (see above)."""
+    if scene.kind == 2:
+        return GRAD_BYTES_PER_PRIM * scene.n
+    rows = sum(4 * (6 + scene.view_channels(v)) for v in range(len(scene.cams)))
+    return (rows + GAUSS_READ_BYTES[scene.kind] + GAUSS_GRAD_WRITE_BYTES[scene.kind] + 4 * scene.channels) * scene.n
+
+
 def kernel_rooflines(kt, cpu, scene, npairs, total_tiles):
     """Each stage's kernels against their own roofline, with the survey's
-    algorithmic units (see the constants above) and the profiled device times."""
+    algorithmic units (see the constants above) and the profiled device times.
+    The compositors' lane-op counts need the oracle's per-pixel totals over the
+    whole frame (the headline workload only); the other workloads' compositor
+    lines carry their times."""
     if not kt:
         return None
     pick = lambda pre: {k: v for k, v in kt.items() if k.split("<")[0] == pre}
     tsum = lambda d: sum(v["us"] * v["launches_per_step"] for v in d.values())
     n, C = scene.n, scene.channels
+    nrec = n * len(scene.cams)
     out = {}
     proj = pick("k_project")
     if proj:
-        b = PROJECT_BYTES_PER_PRIM * n
+        b = project_bytes(scene)
         a, f = _frac(b, tsum(proj), HBM_PEAK_GBS, 1e9)
         out["project"] = {"kernels": sorted(proj), "us": round(tsum(proj), 2), "bound": "hbm", "bytes": b,
                           "achieved": a, "unit": "GB/s", "frac": f}
     bink = {k: v for k, v in kt.items() if k.split("<")[0] in BIN_KERNELS}
     if bink:
-        b, passes = binning_bytes(n, npairs, total_tiles)
+        b, passes = binning_bytes(nrec, npairs, total_tiles)
         a, f = _frac(b, tsum(bink), HBM_PEAK_GBS, 1e9)
         out["bin_sort"] = {"kernels": sorted(bink), "us": round(tsum(bink), 2), "bound": "hbm", "bytes": b,
                            "radix_passes_counted": passes, "achieved": a, "unit": "GB/s", "frac": f}
         if proj:
-            b2 = b + PROJECT_BYTES_PER_PRIM * n
+            b2 = b + project_bytes(scene)
             us2 = tsum(bink) + tsum(proj)
             a, f = _frac(b2, us2, HBM_PEAK_GBS, 1e9)
             out["project_bin_sort"] = {"us": round(us2, 2), "bound": "hbm", "bytes": b2, "achieved": a,
@@ -383,9 +413,15 @@ def kernel_rooflines(kt, cpu, scene, npairs, total_tiles):
             e["ops"] = ops
             e["achieved"], e["frac"] = _frac(ops, tsum(bwd), VALU_PEAK_TOPS, 1e12)
         out["render_bwd"] = e
-    tail = {k: v for k, v in kt.items() if k.split("<")[0] in ("k_sphere_grads", "k_cam_final", "k_zero")}
+    for name, pre in (("render_fwd", ("k_fwd_alpha", "k_fwd_lidar")), ("render_bwd", ("k_bwd_alpha", "k_bwd_lidar"))):
+        ks = {k: v for k, v in kt.items() if k.split("<")[0] in pre}
+        if ks:
+            out[name] = {"kernels": sorted(ks), "us": round(tsum(ks), 2), "bound": "alu"}
+    tail = {k: v for k, v in kt.items()
+            if k.split("<")[0] in ("k_sphere_grads", "k_cam_final", "k_zero", "k_proj_bwd_gauss",
+                                    "k_feat_grads_gauss", "k_cam_grad_sphere")}
     if tail:
-        b = GRAD_BYTES_PER_PRIM * n
+        b = grad_tail_bytes(scene)
         a, f = _frac(b, tsum(tail), HBM_PEAK_GBS, 1e9)
         out["grad_tail"] = {"kernels": sorted(tail), "us": round(tsum(tail), 2), "bound": "hbm", "bytes": b,
                             "achieved": a, "unit": "GB/s", "frac": f}
