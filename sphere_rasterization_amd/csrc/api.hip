@@ -372,8 +372,8 @@ int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *p
     CHECK(bwd_ws_bytes >= bwd_workspace_bytes(nrec, prims->channels), SPLAT_ERR_CAPACITY,
           "backward workspace smaller than splat_bwd_workspace_bytes");
     const AccLayout acc = acc_layout(bwd_workspace, nrec, prims->channels);
-    A.clr[0] = reinterpret_cast<uint4 *>(acc.g);        // rows of 5 + C doubles
-    A.nclr[0] = (nrec * (5 + prims->channels) * (long long)sizeof(double) + 15) / 16;
+    A.clr[0] = reinterpret_cast<uint4 *>(acc.g);        // fp32 rows of 5 + C values (16-byte multiples)
+    A.nclr[0] = nrec * sph_row_stride(prims->channels) * (long long)sizeof(float) / 16;
     A.clr[1] = reinterpret_cast<uint4 *>(acc.kslot);    // intrinsic-gradient slots of every view
     A.nclr[1] = ((long long)n_views * SPLAT_K_SLOTS * 4 * (long long)sizeof(double) + 15) / 16;
     A.clr[2] = reinterpret_cast<uint4 *>(acc.cnt);      // recording-pixel counts
@@ -424,6 +424,8 @@ int splat_render_bwd(const splat_camera *cams, int n_views, int view_begin, int 
   AccLayout acc = acc_layout(workspace, (long long)n_views * prims->n, prims->channels);
   A.accg = acc.g;
   A.accf = acc.f;
+  A.accs = reinterpret_cast<float *>(acc.g);
+  A.rs = sph_row_stride(prims->channels);
   A.cam_part = acc.cam;
   A.kslot = grads->cam_K ? acc.kslot : nullptr;
   A.cnt = grads->normalize ? acc.cnt : nullptr;

@@ -538,7 +538,10 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
 // its pixels recorded: the wave-wide minimum of the lanes' next recorded index
 // picks the entry, the lanes that recorded it form their gradient terms, the
 // wave sums them with a transposed reduction (value q ends in the lanes of
-// 8-lane group q) and one lane per value adds the sum to the record's fp64 row.
+// 8-lane group q) and one lane per value adds the sum to the record's fp32 row
+// (a row takes one sum per quadrant that recorded the sphere: a few at 1M
+// spheres, hundreds for a sphere of 200 px radius, and the row's rounding stays
+// below that of the wave sums).
 // A step costs the same whether one lane or all 64 recorded the entry, so the
 // number of steps is the number of distinct spheres the quadrant's pixels
 // recorded (11 on average at 1M spheres, 1024x1024), not the length of the
@@ -788,7 +791,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
         }
       }
     }
-    double *row = A.accg + (size_t)rid * rowlen;
+    float *row = A.accs + (size_t)rid * A.rs;
     bool reduce = true;
     if constexpr (DIRECT) {
       // few lanes recorded the entry: they add their values straight to the
@@ -798,7 +801,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       if (!reduce && mine) {
 #pragma unroll
         for (int q = 0; q < NV; q++)
-          if (q < rowlen) atomicAdd(row + q, (double)v[q]);
+          if (q < rowlen) atomicAdd(row + q, v[q]);
       }
     }
     if (reduce) {
@@ -807,7 +810,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
         const float (&vg)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * gq]);
         const float r = wave_sum8_transposed_swap(vg);
         const int q = 8 * gq + (int)lane;
-        if (lane < 8u && q < rowlen && r != 0.0f) atomicAdd(row + q, (double)r);
+        if (lane < 8u && q < rowlen && r != 0.0f) atomicAdd(row + q, r);
       }
     }
     m = mn;
@@ -862,6 +865,8 @@ struct ProjBwdArgs {
   const uint32_t *cnt;      // spheres, normalised gradients: pixels that recorded each record
   const double *accg;
   const double *accf;
+  const float *accs;        // spheres: fp32 rows of 5 + C values, stride rs
+  int rs;
   double *cam_part;
   float *gpos, *gscale, *grot, *gop, *gfeat, *gR, *gt;
   int accumulate;
@@ -887,7 +892,7 @@ __device__ __forceinline__ double cam_weight(const ViewDev &c, const ProjBwdArgs
   return 1.0 / (area * 1e-3);
 }
 
-// Spheres, one fp64 accumulator row of 5 + C values per record. Grid-stride over
+// Spheres, one fp32 accumulator row of 5 + C values per record. Grid-stride over
 // spheres: the chain rule sums R^T dq, d_reff, d_opac and the features over the
 // views; when the call covers one view, the same pass forms that view's camera
 // gradient (Pulsar B.2: dL/dR = sum_k dq_k p_k^T, dL/dt = sum_k dq_k) in fp64
@@ -899,21 +904,17 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
   // Outputs of 256 spheres go through LDS and leave as contiguous runs: from
   // registers, the 3- (and C-) float rows of neighbouring lanes would be written
   // one float per instruction, a third of each line at a time.
-  // Up to four channels (there C = CM) the accumulator rows (5 + C doubles) of
-  // the 256 spheres come in through LDS too: RL lanes per row, each wave load
-  // one contiguous run, all of a thread's loads in flight together; read
-  // straight, a lane's row sat 64 bytes from its neighbour's and every load
-  // touched 32 lines. One pad double per staged row spreads the per-lane row
-  // reads over the banks.
+  // Up to four channels (there C = CM) a thread reads its sphere's accumulator
+  // row (RW floats, 16-byte aligned) with RW / 4 vector loads, all in flight
+  // together; neighbouring lanes' rows are adjacent, so the loads of a wave
+  // cover one contiguous run.
   constexpr int CS = CM <= 4 ? CM : 1;         // features staged up to four channels
   constexpr bool STAGE = CM <= 4;
-  constexpr int RS = STAGE ? 5 + CM + 1 : 1;   // staged row stride (doubles)
-  constexpr int RL = 5 + CM <= 8 ? 8 : 16;     // lanes per staged row; also the loads per thread
+  constexpr int RW = STAGE ? (5 + CM + 3) & ~3 : 4;   // row stride (floats) of the vector-load path
   __shared__ double s_red[12][4];
   __shared__ float s_pos[256 * 3];
   __shared__ float s_feat[256 * CS];
-  __shared__ double s_row[256 * RS];
-  const int S = STAGE ? 5 + CM : 5 + P.C;
+  const int S = P.rs;
   double cam[12];
 #pragma unroll
   for (int q = 0; q < 12; q++) cam[q] = 0.0;
@@ -926,22 +927,19 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
     for (int ch = 0; ch < CS; ch++) fs[ch] = 0.0;
     for (int v = vbeg; v < vend; v++) {
       const ViewDev &c = vt.v[v];
-      const double *A;
-      if constexpr (STAGE) {
-        const double *src = P.accg + ((size_t)v * P.n + i0) * S;   // zero for culled records
-        constexpr int RP = 256 / RL;              // rows per pass
-        const int k = (int)(threadIdx.x % RL), r0 = (int)(threadIdx.x / RL);
-        const double *sp = src + r0 * S + k;
-        double x[RL];
+      float A[STAGE ? RW : 5];
+      if (i < P.n) {
+        const float *row = P.accs + ((size_t)v * P.n + i) * S;   // zero for culled records
+        if constexpr (STAGE) {
 #pragma unroll
-        for (int q = 0; q < RL; q++) x[q] = r0 + RP * q < nb && k < S ? sp[RP * S * q] : 0.0;
+          for (int q = 0; q < RW / 4; q++) {
+            const float4 x = reinterpret_cast<const float4 *>(row)[q];
+            A[4 * q] = x.x; A[4 * q + 1] = x.y; A[4 * q + 2] = x.z; A[4 * q + 3] = x.w;
+          }
+        } else {
 #pragma unroll
-        for (int q = 0; q < RL; q++)
-          if (k < S) s_row[(r0 + RP * q) * RS + k] = x[q];
-        __syncthreads();
-        A = s_row + threadIdx.x * RS;
-      } else {
-        A = P.accg + ((size_t)v * P.n + i) * S;
+          for (int q = 0; q < 5; q++) A[q] = row[q];
+        }
       }
       if (i < P.n) {
         const double dq[3] = {A[0], A[1], A[2]};
@@ -967,7 +965,6 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
           }
         }
       }
-      if constexpr (STAGE) __syncthreads();   // staged rows read before the next view's
     }
     if (i < P.n) {
       if (P.cnt) {
@@ -1003,7 +1000,7 @@ __global__ __launch_bounds__(256) void k_sphere_grads(ViewTable vt, ProjBwdArgs 
       } else if (i < P.n) {
         for (int ch = 0; ch < P.C; ch++) {
           double f = 0;
-          for (int v = vbeg; v < vend; v++) f += P.accg[((size_t)v * P.n + i) * S + 5 + ch];
+          for (int v = vbeg; v < vend; v++) f += P.accs[((size_t)v * P.n + i) * S + 5 + ch];
           put(P.gfeat, (size_t)i * P.C + ch, f * nrm, P.accumulate);
         }
       }
@@ -1071,13 +1068,13 @@ __global__ __launch_bounds__(CAMF_THREADS) void k_cam_final(ProjBwdArgs P, int n
 __global__ __launch_bounds__(256) void k_cam_grad_sphere(ViewTable vt, ProjBwdArgs P, int vbeg) {
   __shared__ double s_red[12][4];
   const int v = vbeg + blockIdx.y;
-  const int S = 5 + P.C;
+  const int S = P.rs;
   double cam[12];
 #pragma unroll
   for (int q = 0; q < 12; q++) cam[q] = 0.0;
   const ViewDev &c = vt.v[v];
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < P.n; i += gridDim.x * blockDim.x) {
-    const double *A = P.accg + ((size_t)v * P.n + i) * S;
+    const float *A = P.accs + ((size_t)v * P.n + i) * S;
     const double cw = cam_weight(c, P, (size_t)v * P.n + i);
     const double dq[3] = {A[0] * cw, A[1] * cw, A[2] * cw};
     const double pp[3] = {P.pos[3 * i], P.pos[3 * i + 1], P.pos[3 * i + 2]};
@@ -1350,8 +1347,9 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   if (sph && gr->sums_cleared) {
     // the forward before this call cleared every sum of the workspace
   } else if (sph) {
-    z.d0 = A.accg + r0 * (5 + A.C);
-    z.nd0 = (r1 - r0) * (5 + A.C);
+    // fp32 rows of a multiple of four floats: cleared as doubles
+    z.d0 = reinterpret_cast<double *>(A.accs + r0 * A.rs);
+    z.nd0 = (r1 - r0) * A.rs / 2;
     if (A.kslot) {
       z.d1 = A.kslot + (size_t)vbeg * SPLAT_K_SLOTS * 4;
       z.nd1 = (long long)(vend - vbeg) * SPLAT_K_SLOTS * 4;
@@ -1404,6 +1402,7 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   P.kind = pr->kind; P.n = pr->n; P.C = A.C;
   P.pos = pr->pos; P.scale = pr->scale; P.rot = pr->rot;
   P.bin = bin; P.accg = A.accg; P.accf = A.accf; P.cam_part = A.cam_part;
+  P.accs = A.accs; P.rs = A.rs;
   P.aux = A.aux; P.cnt = sph ? A.cnt : nullptr;
   P.gpos = gr->pos; P.gscale = gr->scale; P.grot = gr->rot; P.gop = gr->opacity; P.gfeat = gr->feat;
   P.gR = gr->cam_R; P.gt = gr->cam_t;

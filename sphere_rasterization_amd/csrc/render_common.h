@@ -51,8 +51,10 @@ struct BwdArgs {
   const float *norm;
   const int32_t *topk;
   const float *dimg;
-  double *accg;           // Gaussians: [records][ACC_G]; spheres: [records][5 + C] (all values)
+  double *accg;           // Gaussians: [records][ACC_G]; unused for spheres
   double *accf;           // Gaussians: [records][C]; unused for spheres
+  float *accs;            // spheres: [records][rs] fp32 rows of 5 + C values
+  int rs;                 // spheres: row stride (floats)
   double *cam_part;       // [SPLAT_CAM_BLOCKS][12] per-block camera sums (spheres)
   double *kslot;          // [views][SPLAT_K_SLOTS][4] intrinsic-gradient sums, or NULL (not requested)
   uint32_t *cnt;          // [records] pixels that recorded the sphere, or NULL (no normalisation)

@@ -144,6 +144,12 @@ struct AccLayout {
   uint32_t *cnt;
 };
 
+// Sphere reverse-pass rows: fp32 [records][sph_row_stride(C)], the 5 + C values
+// (dq0, dq1, dq2, d_reff, d_opac, d_feat...) padded to a multiple of four floats
+// so that every row starts on a 16-byte boundary (they use the region of the
+// Gaussians' geometric and feature sums).
+__host__ __device__ static inline int sph_row_stride(int C) { return (5 + C + 3) & ~3; }
+
 static inline size_t acc_bytes(long long nrec, int C) {
   return proj_align(sizeof(double) * ACC_G * (size_t)nrec) + proj_align(sizeof(double) * (size_t)nrec * C) +
          proj_align(sizeof(double) * 12 * SPLAT_CAM_BLOCKS) +

@@ -57,6 +57,24 @@ def test_ragged_spheres():
     _run(sc, 7, "spheres 150k @1000x600 ragged")
 
 
+def test_large_spheres():
+    """Spheres of up to ~200 px radius in front of a dense field: a recorded
+    sphere's row then takes the sums of hundreds of 8x8 quadrants (the reverse
+    pass accumulates fp32 rows), and the pixels see long tile lists."""
+    sc = S.pulsar_spheres(seed=71, n=40_000, width=640, height=480)
+    rng = np.random.default_rng(72)
+    cam = sc.cams[0]
+    big = rng.random(sc.n) < 0.01
+    z = np.where(big, rng.uniform(2.0, 4.0, sc.n), rng.uniform(2.0, 20.0, sc.n))
+    u, v = rng.uniform(0, 640, sc.n), rng.uniform(0, 480, sc.n)
+    qs = np.stack([z * (u - cam.cx) / cam.fx, z * (v - cam.cy) / cam.fy, z], 1)
+    R, t = cam.R.astype(np.float64), cam.t.astype(np.float64)
+    sc.pos = np.ascontiguousarray(((qs - t) @ R).astype(np.float32))
+    r = np.where(big, np.exp(rng.uniform(np.log(0.1), np.log(0.6), sc.n)), sc.scale.astype(np.float64))
+    sc.scale = np.ascontiguousarray(r.astype(np.float32))
+    _run(sc, 73, "spheres 40k @640x480 with 1% of radius 0.1-0.6")
+
+
 def test_spheres_behind_the_far_plane():
     """Depths U(2, 30) against zfar = 21: spheres whose fp32 front depth is not
     below zfar are culled on both sides (beyond it the stop bound would not hold),
