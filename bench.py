@@ -71,11 +71,11 @@ GAUSS_GRAD_WRITE_BYTES = {0: 8 + 4 + 4, 1: 44}
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 210688948
+FWD_TRAFFIC_BYTES = 186486280
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
-FWD_TRAFFIC_SHA256 = "d88527fe2f5a64127d75d959d5bd5e559a0d52abbba5e1409169d9ba3fcc7168"
+FWD_TRAFFIC_SHA256 = "3e09651ec1f5e2240dbb77fbc1371c3823a985203675e45d6ebed98f18d70fa2"
 BIN_KERNELS = ("k_thist", "k_col_scan", "k_tscatter", "k_seg_sort", "k_tile_scan1", "k_scan_reduce", "k_scan_top",
                "k_tile_ranges", "k_fill_u32", "k_tile_count", "k_bucket")
 
@@ -498,7 +498,7 @@ def roofline(fwd_ms, cpu, scene):
     traffic = FWD_TRAFFIC_BYTES if sources_digest(FWD_TRAFFIC_SOURCES) == FWD_TRAFFIC_SHA256 else None
     if cpu is None or cpu["rows"] != cpu["H"]:
         return {"bound": "alu", "kernel": "k_fwd_sphere", "achieved": None, "peak": round(VALU_PEAK_TOPS, 2),
-                "unit": "Tops/s", "frac": None, "traffic": traffic}
+                "unit": "Tops/s", "frac": None, "traffic": traffic, "kernel_ms": round(fwd_ms, 4)}
     ops = cpu["processed"] * OPS_PER_ENTRY + cpu["hits"] * (OPS_PER_HIT_BASE + scene.channels)
     achieved = ops / (fwd_ms / 1e3) / 1e12
     return {"bound": "alu", "kernel": "k_fwd_sphere", "achieved": round(achieved, 3),
