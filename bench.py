@@ -405,7 +405,7 @@ def kernel_rooflines(kt, cpu, scene, npairs, total_tiles):
             e["ops"] = ops
             e["achieved"], e["frac"] = _frac(ops, tsum(fwd), VALU_PEAK_TOPS, 1e12)
         out["render_fwd"] = e
-    bwd = pick("k_bwd_sphere")
+    bwd = {k: v for k, v in kt.items() if k.split("<")[0] in ("k_bwd_sphere", "k_bwd_sphere_dense")}
     if bwd:
         e = {"kernels": sorted(bwd), "us": round(tsum(bwd), 2), "bound": "alu", "unit": "Tops/s"}
         if full:

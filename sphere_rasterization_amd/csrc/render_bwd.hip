@@ -645,6 +645,99 @@ __device__ __forceinline__ SphEntry<CM> sph_entry(uint32_t rid, long long vbase,
   return e;
 }
 
+// Per-pixel values the terms of a recorded sphere need.
+template <int CM>
+struct SphPix {
+  double x, y, g;          // the ray (x, y) and 1 / |d|^2 (orthographic: 1)
+  double crs;              // 1 pinhole, 0 orthographic (no cross term)
+  float gi[CM];            // g / N per channel
+  float gC;                // (g / N) . C
+  float msh;               // max-shifted blending: the pixel's shift m from the forward
+  float rxf, ryf, rgf;     // the ray in fp32 (rgf = 0 orthographic)
+  float inv_span, igam, zfar;
+  bool orth, max_shift;
+};
+
+template <int CM>
+__device__ __forceinline__ SphPix<CM> sph_pix(const ViewDev &c, const BwdArgs &A, const TilePix &tp,
+                                              const SphereRay &ray, long long p, size_t plane, size_t pofs) {
+  SphPix<CM> P;
+  P.x = ray.x;
+  P.y = ray.y;
+  P.g = ray.g;
+  // per pixel: g / N and (g / N) . C, for the feature and weight terms
+  P.gC = 0.0f;
+  const float invN = tp.inside ? 1.0f / A.norm[p] : 0.0f;
+#pragma unroll
+  for (int ch = 0; ch < CM; ch++) {
+    const bool ok = tp.inside && ch < A.C;
+    P.gi[ch] = ok ? A.dimg[pofs + ch * plane] * invN : 0.0f;
+    P.gC = __builtin_fmaf(P.gi[ch], ok ? A.img[pofs + ch * plane] : 0.0f, P.gC);
+  }
+  // max-shifted blending: weights (and norm) relative to exp(m), m from the forward
+  P.max_shift = A.max_shift != 0;
+  P.msh = (A.max_shift && tp.inside) ? A.T_final[p] : 0.0f;
+  P.inv_span = (float)c.ispan;
+  P.igam = A.igamma;
+  P.zfar = (float)c.zfar;
+  // orthographic views: a = (qx, qy), the ray along +z through (x, y, 0); dist^2 =
+  // |(x, y) - a|^2, whose gradient in q is -2 (sx, sy, 0) (no cross term, no qz scale)
+  P.orth = c.kind == SPLAT_CAM_ORTHOGRAPHIC;
+  P.crs = P.orth ? 0.0 : 1.0;
+  P.rxf = (float)ray.x;
+  P.ryf = (float)ray.y;
+  P.rgf = (float)ray.g * (P.orth ? 0.0f : 1.0f);
+  return P;
+}
+
+// The values one pixel adds for a recorded sphere, in row order (dq0, dq1, dq2,
+// d_reff, d_opac, d_feat...; v holds zeros on entry); returns the weight w. EXT:
+// the pixel's d loss / d (ray x, ray y) is added into (kgx, kgy).
+template <int CM, bool EXT>
+__device__ __forceinline__ float sph_terms(const SphPix<CM> &P, const SphEntry<CM> &e, float *v, float &kgx,
+                                           float &kgy) {
+  const int flags = (int)e.flags;
+  const float oe = P.max_shift ? __expf(e.oe - P.msh) : e.oe;   // o exp(o zhat / gamma) [/ exp(m)]
+  // t = dist^2 / r_eff^2 = A g |a x d|^2 (fp64: near the rim D = 1 - t is a
+  // small difference), a x d from the offsets sx = x - ax, sy = y - ay
+  const double sx = P.x - e.u, sy = P.y - e.v;
+  const double cr = (e.u * sy - e.v * sx) * P.crs;
+  const double t = e.a * P.g * (sx * sx + sy * sy + cr * cr);
+  const float w = oe * (float)(1.0 - t);
+  float dw = -P.gC;
+#pragma unroll
+  for (int ch = 0; ch < CM; ch++) {
+    v[5 + ch] = P.gi[ch] * w;
+    dw = __builtin_fmaf(P.gi[ch], e.f[ch], dw);
+  }
+  const float zhat = (P.zfar - e.qz) * P.inv_span;
+  const float xz = __builtin_amdgcn_rcpf(e.opac) + zhat * P.igam;     // d ln w / d o (D fixed)
+  v[4] = dw * w * xz;
+  if (!(flags & 2)) {
+    // dist^2 = |q|^2 - (q.d)^2 / |d|^2 has gradient 2 q_perp, with
+    // q_perp = qz ((d.delta) g d - delta), delta = (sx, sy, 0)
+    const float ir = __builtin_amdgcn_rcpf(e.reff);
+    const float dD = dw * oe;
+    const float dz = dw * w * (e.opac * P.igam);
+    const float sxf = (float)sx, syf = (float)sy;
+    const float c1 = (P.rxf * sxf + P.ryf * syf) * P.rgf;
+    const float k2 = -2.0f * dD * ir * ir * (P.orth ? 1.0f : e.qz);
+    const float gq0 = k2 * (c1 * P.rxf - sxf), gq1 = k2 * (c1 * P.ryf - syf);
+    v[0] = gq0;
+    v[1] = gq1;
+    v[2] = k2 * c1 - dz * P.inv_span;
+    if (!(flags & 1)) v[3] = 2.0f * dD * (float)t * ir;
+    // the ray: d dist^2 / d d = -((q.d) / |d|^2) d dist^2 / d q, with
+    // (q.d) / |d|^2 = qz (1 - c1); orthographic: d dist^2 / d (x, y) = -d dist^2 / d (qx, qy)
+    if constexpr (EXT) {
+      const float sc = P.orth ? 1.0f : e.qz * (1.0f - c1);
+      kgx = kgx - sc * gq0;
+      kgy = kgy - sc * gq1;
+    }
+  }
+  return w;
+}
+
 // EXT: the call asks for intrinsic gradients or gradient normalisation (their
 // per-contribution work is compiled out of the plain reverse pass). DIRECT:
 // entries recorded by at most A.direct_max lanes of a wave skip the wave
@@ -693,29 +786,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
       if (s < ntop) my_top[s] = make_uint2((uint32_t)t[s], r[s]);
     my_top[ntop] = make_uint2(NONE, 0u);
   }
-  // per pixel: g / N and (g / N) . C, for the feature and weight terms
-  float gi[CM];
-  float gC = 0.0f;
-  {
-    const float invN = tp.inside ? 1.0f / A.norm[p] : 0.0f;
-#pragma unroll
-    for (int ch = 0; ch < CM; ch++) {
-      const bool ok = tp.inside && ch < A.C;
-      gi[ch] = ok ? A.dimg[pofs + ch * plane] * invN : 0.0f;
-      gC = __builtin_fmaf(gi[ch], ok ? A.img[pofs + ch * plane] : 0.0f, gC);
-    }
-  }
-  // max-shifted blending: weights (and norm) relative to exp(m), m from the forward
-  const float msh = (A.max_shift && tp.inside) ? A.T_final[p] : 0.0f;
+  const SphPix<CM> P = sph_pix<CM>(c, A, tp, ray, p, plane, pofs);
   // d loss / d (ray x, ray y) summed over the pixel's recorded spheres
   float kgx = 0.0f, kgy = 0.0f;
-  const float inv_span = (float)c.ispan;
-  const float igam = A.igamma;
-  // orthographic views: a = (qx, qy), the ray along +z through (x, y, 0); dist^2 =
-  // |(x, y) - a|^2, whose gradient in q is -2 (sx, sy, 0) (no cross term, no qz scale)
-  const bool orth = c.kind == SPLAT_CAM_ORTHOGRAPHIC;
-  const double crs = orth ? 0.0 : 1.0;
-  const float rxf = (float)ray.x, ryf = (float)ray.y, rgf = (float)ray.g * (orth ? 0.0f : 1.0f);
   const int rowlen = 5 + A.C;
 
   int nxt = 0;
@@ -750,47 +823,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     float v[NG * 8];
 #pragma unroll
     for (int q = 0; q < NG * 8; q++) v[q] = 0.0f;
-    if (mine) {
-      const int flags = (int)e.flags;
-      const float oe = A.max_shift ? __expf(e.oe - msh) : e.oe;   // o exp(o zhat / gamma) [/ exp(m)]
-      // t = dist^2 / r_eff^2 = A g |a x d|^2 (fp64: near the rim D = 1 - t is a
-      // small difference), a x d from the offsets sx = x - ax, sy = y - ay
-      const double sx = ray.x - e.u, sy = ray.y - e.v;
-      const double cr = (e.u * sy - e.v * sx) * crs;
-      const double t = e.a * ray.g * (sx * sx + sy * sy + cr * cr);
-      const float w = oe * (float)(1.0 - t);
-      float dw = -gC;
-#pragma unroll
-      for (int ch = 0; ch < CM; ch++) {
-        v[5 + ch] = gi[ch] * w;
-        dw = __builtin_fmaf(gi[ch], e.f[ch], dw);
-      }
-      const float zhat = ((float)c.zfar - e.qz) * inv_span;
-      const float xz = __builtin_amdgcn_rcpf(e.opac) + zhat * igam;     // d ln w / d o (D fixed)
-      v[4] = dw * w * xz;
-      if (!(flags & 2)) {
-        // dist^2 = |q|^2 - (q.d)^2 / |d|^2 has gradient 2 q_perp, with
-        // q_perp = qz ((d.delta) g d - delta), delta = (sx, sy, 0)
-        const float ir = __builtin_amdgcn_rcpf(e.reff);
-        const float dD = dw * oe;
-        const float dz = dw * w * (e.opac * igam);
-        const float sxf = (float)sx, syf = (float)sy;
-        const float c1 = (rxf * sxf + ryf * syf) * rgf;
-        const float k2 = -2.0f * dD * ir * ir * (orth ? 1.0f : e.qz);
-        const float gq0 = k2 * (c1 * rxf - sxf), gq1 = k2 * (c1 * ryf - syf);
-        v[0] = gq0;
-        v[1] = gq1;
-        v[2] = k2 * c1 - dz * inv_span;
-        if (!(flags & 1)) v[3] = 2.0f * dD * (float)t * ir;
-        // the ray: d dist^2 / d d = -((q.d) / |d|^2) d dist^2 / d q, with
-        // (q.d) / |d|^2 = qz (1 - c1); orthographic: d dist^2 / d (x, y) = -d dist^2 / d (qx, qy)
-        if constexpr (EXT) {
-          const float sc = orth ? 1.0f : e.qz * (1.0f - c1);
-          kgx = kgx - sc * gq0;
-          kgy = kgy - sc * gq1;
-        }
-      }
-    }
+    if (mine) sph_terms<CM, EXT>(P, e, v, kgx, kgy);
     float *row = A.accs + (size_t)rid * A.rs;
     bool reduce = true;
     if constexpr (DIRECT) {
@@ -839,6 +872,152 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     for (int q = 4; q < 8; q++) v8[q] = 0.0;
     const double r = wave_sum8_transposed_f64(v8);
     if (lane < 4u) atomicAdd(A.kslot + ((size_t)view * SPLAT_K_SLOTS + blockIdx.x % SPLAT_K_SLOTS) * 4 + lane, r);
+  }
+}
+
+// The plain reverse pass over spheres (no intrinsic gradients, normalisation or
+// lane-by-lane atomics; at most SPH_DENSE_K recorded entries per pixel and three
+// channels, eight values per entry) in two phases.
+// Phase one: every lane forms the values of all its recorded entries, every lane
+// busy, the records of three slots in flight together, and keeps them in LDS
+// (24 bytes per slot, its own rows: the waves share nothing and need no barrier).
+// Phase two: the wave walks the distinct entries as the kernel above does, but a
+// step only takes the recording lanes' values, sums them over the wave and adds
+// the sums: the arithmetic no longer runs once per distinct entry with only the
+// lanes that recorded it active (29 of 64 on average at 1M spheres, 1024x1024).
+// The walk goes in order of record id (each lane's ids sorted in registers), so
+// that the wave minimum is the record itself and a step loads no record; the
+// slot a lane is at after a step is read from LDS one step before it is needed.
+// Five waves per SIMD (30 KB of LDS per workgroup) with 72 registers: with all
+// five records in flight at once the kernel needed more registers and spilled.
+constexpr int SPH_DENSE_K = 5;
+
+__device__ __forceinline__ void sort2(uint32_t &a, uint32_t &b) {
+  const uint32_t lo = min(a, b), hi = max(a, b);
+  a = lo;
+  b = hi;
+}
+
+template <int CM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_bwd_sphere_dense(ViewTable vt,
+                                                                                           BwdArgs A,
+                                                                                           int tile_begin) {
+  static_assert(5 + CM <= 8, "eight values per entry");
+  static_assert(SPH_DENSE_K == 5, "the sorting network below is for five ids");
+  constexpr int KD = SPH_DENSE_K;
+  constexpr uint32_t NONE = 0xffffffffu;
+  // slot s of pixel tid: values 0..3, then value 4 and the weight w (the feature
+  // values are g_ch / N w)
+  __shared__ float4 s_va[KD][256];
+  __shared__ float2 s_vb[KD][256];
+  if (*A.overflow) return;
+  const unsigned tid = threadIdx.x;
+  const int gtile = tile_begin + blockIdx.x;
+  const int view = view_of_tile(vt, gtile);
+  const ViewDev &c = vt.v[view];
+  const TilePix tp = tile_pixel(c, gtile, tid);
+  const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
+  const SphereRay ray = sphere_ray(c, tp);
+  const unsigned lane = lane_id();
+  const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
+  const size_t plane = (size_t)c.W * c.H;
+  const size_t pofs = c.img_off + (size_t)tp.j * c.W + tp.i;
+  const int K = A.top_k;
+  const long long vbase = (long long)view * A.n;
+  // record ids of this tile's recorded entries, ascending, NONE after the last
+  int ntop = 0;
+  uint32_t r[KD];
+  {
+    int t[KD];
+#pragma unroll
+    for (int s = 0; s < KD; s++) t[s] = (s < K && tp.inside) ? A.topk[p * K + s] : -1;
+    bool go = true;
+#pragma unroll
+    for (int s = 0; s < KD; s++) {
+      go = go && t[s] >= 0 && (uint32_t)t[s] >= start && (uint32_t)t[s] < end;
+      ntop += go ? 1 : 0;
+    }
+#pragma unroll
+    for (int s = 0; s < KD; s++) r[s] = s < ntop ? A.vals[t[s]] : NONE;
+    // a sorting network for five (nine compare-exchanges)
+    sort2(r[0], r[1]); sort2(r[3], r[4]); sort2(r[2], r[4]); sort2(r[2], r[3]); sort2(r[0], r[3]);
+    sort2(r[0], r[2]); sort2(r[1], r[4]); sort2(r[1], r[3]); sort2(r[1], r[2]);
+  }
+  const SphPix<CM> P = sph_pix<CM>(c, A, tp, ray, p, plane, pofs);
+  // phase one, over the slots some lane of the wave uses (record 0 stands in
+  // for a lane's empty slots: a wave that reaches it has at least one record)
+  int nmax = 0;
+#pragma unroll
+  for (int s = 0; s < KD; s++) nmax += ballot64(ntop > s) != 0 ? 1 : 0;
+  // (in groups of PG slots, the group's records in flight together: all five at
+  // once held more registers than five waves per SIMD allow)
+  constexpr int PG = 3;
+#pragma unroll
+  for (int s0 = 0; s0 < KD; s0 += PG) {
+    if (s0 >= nmax) break;
+    SphEntry<CM> e[PG];
+#pragma unroll
+    for (int j = 0; j < PG; j++) {
+      const int s = s0 + j;
+      if (s < KD && s < nmax) e[j] = sph_entry<CM>(r[s] != NONE ? r[s] : 0u, vbase, A.C, A.draw, A.aux, A.feat);
+    }
+#pragma unroll
+    for (int j = 0; j < PG; j++) {
+      const int s = s0 + j;
+      if (s >= KD || s >= nmax) break;
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; q++) v[q] = 0.0f;
+      float kx = 0.0f, ky = 0.0f;
+      const float w = sph_terms<CM, false>(P, e[j], v, kx, ky);
+      s_va[s][tid] = make_float4(v[0], v[1], v[2], v[3]);
+      s_vb[s][tid] = make_float2(v[4], w);
+    }
+  }
+  // phase two: a step takes the current slot's values from one register set and
+  // reads the slot the lane is at after the step (the next one if the lane
+  // recorded the entry, else the same) into the other; q0 is the lane's current
+  // id (the ids q0..q4 move down a place when the lane recorded the entry)
+  const int rowlen = 5 + A.C;
+  int nxt = 0;
+  float4 a0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), a1 = a0;
+  float2 b0 = make_float2(0.0f, 0.0f), b1 = b0;
+  if (nmax > 0) {
+    a0 = s_va[0][tid];
+    b0 = s_vb[0][tid];
+  }
+  uint32_t q0 = r[0], q1 = r[1], q2 = r[2], q3 = r[3], q4 = r[4];
+  uint32_t m = wave_min_u32(q0);
+  auto step = [&](const float4 &ca, const float2 &cb, float4 &na, float2 &nb) {
+    const bool mine = q0 == m;
+    float v[8];
+    const float w = mine ? cb.y : 0.0f;
+    v[0] = mine ? ca.x : 0.0f;
+    v[1] = mine ? ca.y : 0.0f;
+    v[2] = mine ? ca.z : 0.0f;
+    v[3] = mine ? ca.w : 0.0f;
+    v[4] = mine ? cb.x : 0.0f;
+#pragma unroll
+    for (int q = 5; q < 8; q++) v[q] = q - 5 < CM ? P.gi[q - 5 < CM ? q - 5 : 0] * w : 0.0f;
+    q0 = mine ? q1 : q0;
+    q1 = mine ? q2 : q1;
+    q2 = mine ? q3 : q2;
+    q3 = mine ? q4 : q3;
+    q4 = mine ? NONE : q4;
+    nxt += mine ? 1 : 0;
+    const int sl = min(nxt, KD - 1);
+    na = s_va[sl][tid];
+    nb = s_vb[sl][tid];
+    const uint32_t mn = wave_min_u32(q0);
+    const float sum = wave_sum8_transposed_swap(v);
+    float *row = A.accs + (size_t)m * A.rs;
+    if (lane < 8u && (int)lane < rowlen && sum != 0.0f) atomicAdd(row + lane, sum);
+    m = mn;
+  };
+  while (m != NONE) {
+    step(a0, b0, a1, b1);
+    if (m == NONE) break;
+    step(a1, b1, a0, b0);
   }
 }
 
@@ -1299,6 +1478,9 @@ int launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begi
       hipLaunchKernelGGL((k_bwd_sphere<CM, true>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
     else if (CM <= 4 && A.direct_max > 0)
       hipLaunchKernelGGL((k_bwd_sphere<CM, false, CM <= 4>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
+    else if (CM <= 3 && A.top_k <= SPH_DENSE_K)
+      hipLaunchKernelGGL((k_bwd_sphere_dense<CM <= 3 ? CM : 3>), dim3(ntiles), dim3(256), 0, stream, vt, A,
+                         tile_begin);
     else
       hipLaunchKernelGGL((k_bwd_sphere<CM, false>), dim3(ntiles), dim3(256), 0, stream, vt, A, tile_begin);
   } else {
