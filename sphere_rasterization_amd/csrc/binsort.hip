@@ -480,10 +480,10 @@ __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt,
   const int v = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
   const ViewDev &cv = vt.v[v];
   const int T = cv.TW * cv.TH;
-  for (int t = threadIdx.x; t < T; t += TH_THREADS) s_cnt[t] = 0;
   ChunkRecs cr;
   const int nvalid = min(TH_CHUNK, n - chunk * TH_CHUNK);
   load_chunk(bin, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);
+  for (int t = threadIdx.x; t < T; t += TH_THREADS) s_cnt[t] = 0;
   __syncthreads();
   chunk_pairs(cv, cr, hl, [&](uint32_t lt, uint32_t, uint32_t) { atomicAdd(&s_cnt[lt], 1u); });
   __syncthreads();
@@ -628,14 +628,16 @@ __global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable 
   const ViewDev &cv = vt.v[v];
   const int T = cv.TW * cv.TH;
   const uint32_t *row = M + mat_index(mt, cv, v, chunk_row(chunk, nchunk), 0);
+  // the chunk's records are requested first: their loads are in flight during
+  // the tile scan
+  ChunkRecs cr;
+  const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
+  load_chunk(bin, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
   if constexpr (FUSED) {
     if (!fused_tile_scan(tile_start, T, row, s_base, so, chunk, nchunk)) return;
   } else {
     for (int t = threadIdx.x; t < T; t += TH_THREADS) s_base[t] = tile_start[cv.tile_off + t] + row[t];
   }
-  ChunkRecs cr;
-  const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
-  load_chunk(bin, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
   __syncthreads();
   chunk_pairs(cv, cr, hl, [&](uint32_t lt, uint32_t slot, uint32_t key) {
     words[atomicAdd(&s_base[lt], 1u)] = ((uint64_t)key << 32) | (uint64_t)(uint32_t)(rec0 + slot);
