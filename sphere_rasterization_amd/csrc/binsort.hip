@@ -497,6 +497,7 @@ __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt,
 // consecutive ranges; each wave sums its range, the waves' sums are scanned in
 // LDS, then each wave rewrites its range as running prefixes.
 constexpr int CS_WAVES = 16;
+constexpr int CS_HOLD = 16;      // matrix entries a lane keeps in registers (nchunk <= 256)
 
 __global__ __launch_bounds__(CS_WAVES * 64) void k_col_scan(ViewTable vt, MatTable mt, int nchunk, uint32_t *M,
                                                             uint32_t *tile_cnt) {
@@ -513,22 +514,42 @@ __global__ __launch_bounds__(CS_WAVES * 64) void k_col_scan(ViewTable vt, MatTab
     base = mat_index(mt, cv, v, 0, gt - cv.tile_off);
     stride = (long long)cv.TW * cv.TH;
   }
+  // up to CS_HOLD entries per lane stay in registers between the sum and the
+  // rewrite (one read of the matrix); longer ranges are read twice
   uint32_t s = 0;
+  uint32_t xs[CS_HOLD];
+  const bool hold = q <= CS_HOLD;
   if (ok) {
+    if (hold) {
+#pragma unroll
+      for (int j = 0; j < CS_HOLD; j++) {
+        xs[j] = c0 + j < c1 ? M[base + (c0 + j) * stride] : 0u;
+        s += xs[j];
+      }
+    } else {
 #pragma unroll 8
-    for (int c = c0; c < c1; c++) s += M[base + c * stride];
+      for (int c = c0; c < c1; c++) s += M[base + c * stride];
+    }
   }
   s_part[w][l] = s;
   __syncthreads();
   uint32_t run = 0;
   for (int w2 = 0; w2 < w; w2++) run += s_part[w2][l];
   if (ok) {
+    if (hold) {
+#pragma unroll
+      for (int j = 0; j < CS_HOLD; j++) {
+        if (c0 + j < c1) M[base + (c0 + j) * stride] = run;
+        run += xs[j];
+      }
+    } else {
 #pragma unroll 8
-    for (int c = c0; c < c1; c++) {
-      const long long i = base + c * stride;
-      const uint32_t x = M[i];
-      M[i] = run;
-      run += x;
+      for (int c = c0; c < c1; c++) {
+        const long long i = base + c * stride;
+        const uint32_t x = M[i];
+        M[i] = run;
+        run += x;
+      }
     }
     if (w == CS_WAVES - 1) tile_cnt[gt] = run;
   }
