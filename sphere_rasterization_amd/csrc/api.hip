@@ -21,7 +21,7 @@ int launch_bin_sort(const ViewTable &vt, int n, const void *proj, const uint32_t
                     void *workspace, hipStream_t stream);
 int launch_render_fwd(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t stream);
 size_t bwd_workspace_bytes(long long nrec, int C);
-int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, const BinRec *bin,
+int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, BinArrays bin,
                       const splat_grads *gr, hipStream_t stream);
 int launch_assemble(const float *key_pos, const float *key_rot, int k, int k1, float w, long long n, float *pos,
                     float *rot, hipStream_t stream);

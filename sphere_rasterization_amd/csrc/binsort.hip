@@ -104,12 +104,12 @@ __device__ __forceinline__ void for_each_tile(const ViewDev &cv, const BinRec &b
   }
 }
 
-__global__ __launch_bounds__(256) void k_tile_count(ViewTable vt, int n, const BinRec *bin, const uint32_t *counts,
+__global__ __launch_bounds__(256) void k_tile_count(ViewTable vt, int n, BinArrays bin, const uint32_t *counts,
                                                      uint32_t *tile_cnt) {
   const long long k = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= (long long)vt.n * n || counts[k] == 0) return;
   const ViewDev &cv = vt.v[(int)(k / n)];
-  for_each_tile(cv, bin[k], [&](uint32_t gt) { atomicAdd(&tile_cnt[gt], 1u); });
+  for_each_tile(cv, bin_rect(bin, k), [&](uint32_t gt) { atomicAdd(&tile_cnt[gt], 1u); });
 }
 
 // ---- exclusive scan over tiles -------------------------------------------------
@@ -280,13 +280,13 @@ __global__ __launch_bounds__(TS_THREADS) void k_tile_scan1(uint32_t *cnt_start, 
 
 // ---- bucketing -------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_bucket(ViewTable vt, int n, const BinRec *bin, const uint32_t *counts,
+__global__ __launch_bounds__(256) void k_bucket(ViewTable vt, int n, BinArrays bin, const uint32_t *counts,
                                                  const int32_t *overflow, uint32_t *cursor, uint64_t *words) {
   if (*overflow) return;
   const long long k = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= (long long)vt.n * n || counts[k] == 0) return;
   const ViewDev &cv = vt.v[(int)(k / n)];
-  const BinRec b = bin[k];
+  const BinRec b = bin_full(bin, k);
   const uint64_t w = ((uint64_t)b.key << 32) | (uint64_t)(uint32_t)k;
   for_each_tile(cv, b, [&](uint32_t gt) {
     const uint32_t pos = atomicAdd(&cursor[gt], 1u);
@@ -327,14 +327,15 @@ struct ChunkRecs {
   BinRec b[TH_RPT];
 };
 
-__device__ __forceinline__ void load_chunk(const BinRec *bin, long long rec0, int nvalid, ChunkRecs &cr) {
+template <bool KEYS>
+__device__ __forceinline__ void load_chunk(const BinArrays &bin, long long rec0, int nvalid, ChunkRecs &cr) {
 #pragma unroll
   for (int r = 0; r < TH_RPT; r++) {
     const int j = r * TH_THREADS + (int)threadIdx.x;
     if (j < nvalid) {
-      cr.b[r] = bin[rec0 + j];
+      cr.b[r] = KEYS ? bin_full(bin, rec0 + j) : bin_rect(bin, rec0 + j);
     } else {
-      cr.b[r].key = 0u; cr.b[r].tx0 = 0; cr.b[r].ntx = 0; cr.b[r].ty0 = 0; cr.b[r].ty1 = 0; cr.b[r].pad = 0u;
+      cr.b[r].key = 0u; cr.b[r].tx0 = 0; cr.b[r].ntx = 0; cr.b[r].ty0 = 0; cr.b[r].ty1 = 0;
     }
   }
 #pragma unroll
@@ -473,7 +474,7 @@ __device__ __forceinline__ void chunk_pairs(const ViewDev &cv, const ChunkRecs &
 }
 
 // grid: n_views * nchunk workgroups of TH_THREADS; dynamic LDS: 4 * max tiles per view.
-__global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
+__global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt, int n, int nchunk, BinArrays bin,
                                                 uint32_t *M) {
   extern __shared__ uint32_t s_cnt[];
   __shared__ HeavyLds hl;
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(TH_THREADS) void k_thist(ViewTable vt, MatTable mt,
   const int T = cv.TW * cv.TH;
   ChunkRecs cr;
   const int nvalid = min(TH_CHUNK, n - chunk * TH_CHUNK);
-  load_chunk(bin, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);
+  load_chunk<false>(bin, (long long)v * n + (long long)chunk * TH_CHUNK, nvalid, cr);   // the keys are not needed
   for (int t = threadIdx.x; t < T; t += TH_THREADS) s_cnt[t] = 0;
   __syncthreads();
   chunk_pairs(cv, cr, hl, [&](uint32_t lt, uint32_t, uint32_t) { atomicAdd(&s_cnt[lt], 1u); });
@@ -636,7 +637,7 @@ __device__ bool fused_tile_scan(const uint32_t *cnt, int T, const uint32_t *row,
 // FUSED (one view): tile_start holds the tile counts and the tile scan runs
 // here (fused_tile_scan); otherwise k_tile_scan1 has turned them into starts.
 template <bool FUSED>
-__global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable mt, int n, int nchunk, const BinRec *bin,
+__global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable mt, int n, int nchunk, BinArrays bin,
                                                    const uint32_t *M,
                                                    const uint32_t *tile_start, const int32_t *overflow,
                                                    uint64_t *words, ScanOut so) {
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(TH_THREADS) void k_tscatter(ViewTable vt, MatTable 
   // the tile scan
   ChunkRecs cr;
   const long long rec0 = (long long)v * n + (long long)chunk * TH_CHUNK;
-  load_chunk(bin, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
+  load_chunk<true>(bin, rec0, min(TH_CHUNK, n - chunk * TH_CHUNK), cr);
   if constexpr (FUSED) {
     if (!fused_tile_scan(tile_start, T, row, s_base, so, chunk, nchunk)) return;
   } else {

@@ -72,9 +72,8 @@ __device__ __forceinline__ void sensor_point(const ViewDev &c, double x0, double
 }
 
 __device__ void write_culled(const ProjLayout &L, long long k, uint32_t *counts) {
-  BinRec b;
-  b.key = 0; b.tx0 = 0; b.ntx = 0; b.ty0 = 0; b.ty1 = 0; b.pad = 0;
-  L.bin[k] = b;
+  L.bin.key[k] = 0u;
+  L.bin.rect[k] = make_uint2(0u, 0u);
   counts[k] = 0;
 }
 
@@ -83,8 +82,8 @@ __device__ void write_rect(const ProjLayout &L, long long k, uint32_t *counts, c
   b.key = __float_as_uint(key_depth);
   b.tx0 = (uint16_t)r.tx0; b.ntx = (uint16_t)r.ntx;
   b.ty0 = (uint16_t)r.ty0; b.ty1 = (uint16_t)r.ty1;
-  b.pad = 0;
-  L.bin[k] = b;
+  L.bin.key[k] = b.key;
+  L.bin.rect[k] = pack_rect(b);
   counts[k] = (uint32_t)(r.ntx * (r.ty1 - r.ty0 + 1));
 }
 

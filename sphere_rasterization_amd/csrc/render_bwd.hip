@@ -1039,7 +1039,7 @@ __global__ __launch_bounds__(256) void k_cam_K_final(const double *kslot, float 
 struct ProjBwdArgs {
   int kind, n, C;
   const float *pos, *scale, *rot;
-  const BinRec *bin;
+  BinArrays bin;
   const AuxRec *aux;
   const uint32_t *cnt;      // spheres, normalised gradients: pixels that recorded each record
   const double *accg;
@@ -1057,14 +1057,14 @@ __device__ __forceinline__ void put(float *p, size_t i, double x, int accumulate
   else p[i] = (float)x;
 }
 
-__device__ __forceinline__ bool rec_live(const BinRec &b) { return b.ntx != 0; }
+__device__ __forceinline__ bool rec_live(const BinArrays &b, size_t rec) { return (b.rect[rec].x >> 16) != 0u; }
 
 // Weight of a record's camera-gradient contribution: 1, or under Pulsar's
 // normalisation (B.2) 1 / (projected area in pixels x 1e-3), the area
 // pi (fx r_eff / qz)(fy r_eff / qz) (orthographic: pi (fx r_eff)(fy r_eff)).
 __device__ __forceinline__ double cam_weight(const ViewDev &c, const ProjBwdArgs &P, size_t rec) {
   if (!P.cnt) return 1.0;
-  if (!rec_live(P.bin[rec])) return 0.0;
+  if (!rec_live(P.bin, rec)) return 0.0;
   const AuxRec a = P.aux[rec];
   const double re = (double)a.w, iz = c.kind == SPLAT_CAM_ORTHOGRAPHIC ? 1.0 : 1.0 / (double)a.z;
   const double area = 3.141592653589793 * ((double)c.fx * re * iz) * ((double)c.fy * re * iz);
@@ -1334,7 +1334,7 @@ __device__ __forceinline__ void gauss_prim_grads(const ViewTable &vt, const Proj
     const double s = P.scale[i];
     for (int v = vbeg; v < vend; v++) {
       const long long rec = (long long)v * P.n + i;
-      if (!rec_live(P.bin[rec])) continue;
+      if (!rec_live(P.bin, rec)) continue;
       const double *A = P.accg + (size_t)rec * ACC_G;
       gpos[0] += A[0];
       gpos[1] += A[1];
@@ -1360,7 +1360,7 @@ __device__ __forceinline__ void gauss_prim_grads(const ViewTable &vt, const Proj
     double dS3sum[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
     for (int v = vbeg; v < vend; v++) {
       const long long rec = (long long)v * P.n + i;
-      if (!rec_live(P.bin[rec])) continue;
+      if (!rec_live(P.bin, rec)) continue;
       const ViewDev &c = vt.v[v];
       const double *A = P.accg + (size_t)rec * ACC_G;
       double W[9];
@@ -1519,7 +1519,7 @@ int launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begi
 
 size_t bwd_workspace_bytes(long long nrec, int C) { return acc_bytes(nrec, C); }
 
-int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, const BinRec *bin,
+int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const splat_prims *pr, BinArrays bin,
                       const splat_grads *gr, hipStream_t stream) {
   // accumulator rows of the requested views only (spheres: one row of 5 + C
   // values per record; Gaussians: ACC_G geometric values and C features)

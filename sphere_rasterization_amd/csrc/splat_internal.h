@@ -43,13 +43,40 @@ __device__ __forceinline__ int view_of_tile(const ViewTable &vt, int gtile) {
 // ---------------------------------------------------------------------------
 // Projected records (structure of arrays inside the opaque proj buffer).
 // ---------------------------------------------------------------------------
-// Binning part, read by the emit kernel.
-struct __align__(16) BinRec {
+// Binning part, read by the counting and bucketing kernels: two arrays, so that
+// the counting reads the 8-byte tile rectangles alone.
+struct BinRec {          // a record's binning fields, in registers
   uint32_t key;          // fp32 bits of the depth key
   uint16_t tx0, ntx;     // tile columns tx0 .. tx0+ntx-1 (mod TW for spherical views)
   uint16_t ty0, ty1;     // tile rows (inclusive)
-  uint32_t pad;
 };
+
+struct BinArrays {
+  uint32_t *key;         // [records] depth keys
+  uint2 *rect;           // [records] (tx0 | ntx << 16, ty0 | ty1 << 16)
+};
+
+__host__ __device__ inline uint2 pack_rect(const BinRec &b) {
+  return make_uint2((uint32_t)b.tx0 | ((uint32_t)b.ntx << 16), (uint32_t)b.ty0 | ((uint32_t)b.ty1 << 16));
+}
+
+// Record k's rectangle (key 0) or its rectangle and key.
+__device__ inline BinRec bin_rect(const BinArrays &b, long long k) {
+  const uint2 r = b.rect[k];
+  BinRec o;
+  o.key = 0u;
+  o.tx0 = (uint16_t)(r.x & 0xffffu);
+  o.ntx = (uint16_t)(r.x >> 16);
+  o.ty0 = (uint16_t)(r.y & 0xffffu);
+  o.ty1 = (uint16_t)(r.y >> 16);
+  return o;
+}
+
+__device__ inline BinRec bin_full(const BinArrays &b, long long k) {
+  BinRec o = bin_rect(b, k);
+  o.key = b.key[k];
+  return o;
+}
 
 // Compositing part, staged into LDS by the render kernels (48 bytes).
 //  Gaussians: projected mean (u, v), conic (a, b, c) with power = (a dx^2 + 2 b dx dy + c dy^2)/2,
@@ -90,7 +117,7 @@ __device__ __forceinline__ float rec_feat(const DrawRec &d, int ch) {
 }
 
 struct ProjLayout {
-  BinRec *bin;
+  BinArrays bin;
   DrawRec *draw;
   AuxRec *aux;
 };
@@ -100,8 +127,10 @@ static inline size_t proj_align(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline ProjLayout proj_layout(void *base, long long nrec) {
   char *p = (char *)base;
   ProjLayout L;
-  L.bin = (BinRec *)p;
-  p += proj_align(sizeof(BinRec) * (size_t)nrec);
+  L.bin.key = (uint32_t *)p;
+  p += proj_align(sizeof(uint32_t) * (size_t)nrec);
+  L.bin.rect = (uint2 *)p;
+  p += proj_align(sizeof(uint2) * (size_t)nrec);
   L.draw = (DrawRec *)p;
   p += proj_align(sizeof(DrawRec) * (size_t)nrec);
   L.aux = (AuxRec *)p;
@@ -109,7 +138,8 @@ static inline ProjLayout proj_layout(void *base, long long nrec) {
 }
 
 static inline size_t proj_bytes(long long nrec) {
-  return proj_align(sizeof(BinRec) * (size_t)nrec) + proj_align(sizeof(DrawRec) * (size_t)nrec) +
+  return proj_align(sizeof(uint32_t) * (size_t)nrec) + proj_align(sizeof(uint2) * (size_t)nrec) +
+         proj_align(sizeof(DrawRec) * (size_t)nrec) +
          proj_align(sizeof(AuxRec) * (size_t)nrec);
 }
 
