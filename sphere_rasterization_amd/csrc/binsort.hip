@@ -673,25 +673,35 @@ __device__ __forceinline__ void write_pair(uint64_t *keys, uint32_t *vals, uint3
   vals[pos] = (uint32_t)w;
 }
 
-// Value of lane (lane ^ M) for a 32-bit value, M a power of two below 64: DPP
-// quad permutes for 1 and 2, a half-row mirror (lane ^ 7) followed by a quad
-// reversal (lane ^ 3) for 4, a row rotation by 8 for 8, a swizzle for 16 and
-// a lane permute through the LDS crossbar for 32.
+// Value of lane (lane ^ M) for a 32-bit value, M a power of two below 64 or
+// one less than a power of two: DPP quad permutes for 1, 2 and 3, a half-row
+// mirror for 7 (followed by a quad reversal for 4), a row mirror for 15, a row
+// rotation by 8 for 8, swizzles for 16 and 31 and a lane permute through the
+// LDS crossbar for 32 and 63.
 template <int M>
 __device__ __forceinline__ uint32_t lane_xor32(uint32_t x, unsigned lane) {
   if constexpr (M == 1) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, false);
   } else if constexpr (M == 2) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, false);
+  } else if constexpr (M == 3) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x1B, 0xf, 0xf, false);
   } else if constexpr (M == 4) {
     const int y = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, false);
     return (uint32_t)__builtin_amdgcn_mov_dpp(y, 0x1B, 0xf, 0xf, false);
+  } else if constexpr (M == 7) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, false);
   } else if constexpr (M == 8) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false);
+  } else if constexpr (M == 15) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xf, 0xf, false);
   } else if constexpr (M == 16) {
     return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+  } else if constexpr (M == 31) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x7C1F);
   } else {
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane ^ 32u) << 2), (int)x);
+    static_assert(M == 32 || M == 63, "lane_xor32: unsupported lane mask");
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane ^ (unsigned)M) << 2), (int)x);
   }
 }
 
@@ -701,52 +711,83 @@ __device__ __forceinline__ uint64_t lane_xor64(uint64_t v, unsigned lane) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// One stage (K, J) of the bitonic network over 512 words, lane l holding words
-// 8 l .. 8 l + 7. Word x pairs with x ^ J and keeps the smaller of the two
-// when it is the lower one of an ascending block or the upper one of a
-// descending block (block direction: bit K of x clear = ascending). For
-// J >= 8 the partner is in lane l ^ (J / 8) and the choice is the same for all
-// eight words of a lane; below, partners are in the same lane.
-template <int K, int J>
-__device__ __forceinline__ void bitonic_stage(uint64_t (&e)[8], unsigned lane) {
-  if constexpr (J >= 8) {
-    constexpr int M = J / 8;
-    const bool lower = (lane & (unsigned)M) == 0u;
-    const bool asc = K >= 512 ? true : (lane & (unsigned)(K / 8)) == 0u;
-    const bool keep_min = lower == asc;
+// Pad word of the in-register sorts: above every sort word and, read as fp64,
+// the largest finite number.
+constexpr uint64_t SORT_PAD = 0x7FEFFFFFFFFFFFFFull;
+
+// Ascending compare-exchange of two sort words inside one lane. A sort word's
+// high half is the bit pattern of a non-negative, non-NaN fp32 depth (0 to
+// 0x7F800000) and its top bit is clear, so read as fp64 every word, and the pad
+// above, is a non-negative finite number, and fp64 order is the unsigned
+// integer order (fp64 denormals are kept in these kernels, not flushed). One
+// fp64 minimum and one maximum replace a 64-bit compare and four selects; both
+// return one of their operands bit for bit.
+__device__ __forceinline__ void ce_asc(uint64_t &x, uint64_t &y) {
+  const double a = __longlong_as_double((long long)x), b = __longlong_as_double((long long)y);
+  // written out: the compiler's fmin / fmax first quiet possible signalling
+  // NaNs with an extra fp64 operation per operand, and no NaN ever reaches here
+  double lo, hi;
+  asm("v_min_f64 %0, %1, %2" : "=v"(lo) : "v"(a), "v"(b));
+  asm("v_max_f64 %0, %1, %2" : "=v"(hi) : "v"(a), "v"(b));
+  x = (uint64_t)__double_as_longlong(lo);
+  y = (uint64_t)__double_as_longlong(hi);
+}
+
+// Compare-exchange of word a of this lane with the same position of the
+// partner lane (value o): the lane keeps the smaller one when keep_min.
+__device__ __forceinline__ uint64_t ce_lane(uint64_t mine, uint64_t o, bool keep_min) {
+  return ((o < mine) == keep_min) ? o : mine;
+}
+
+// Bitonic sort of 512 words, lane l holding words 8 l .. 8 l + 7, in the form
+// whose comparators all point the same way: merge level K opens with word x
+// paired with x ^ (K - 1) (the upper half of each K-block mirrored onto the
+// lower), then pairs x with x ^ J for J = K / 4 .. 1, the lower word of every
+// pair keeping the smaller. Pairs more than eight words apart sit in different
+// lanes: x ^ (K - 1) is word 7 - a of lane l ^ (K / 8 - 1), x ^ J word a of lane
+// l ^ (J / 8), and the lower side is the lane with bit K / 16 (resp. J / 8)
+// clear. Pairs closer than that sit in one lane and need no direction.
+template <int K>
+__device__ __forceinline__ void flip_stage(uint64_t (&e)[8], unsigned lane) {
+  if constexpr (K <= 8) {
 #pragma unroll
-    for (int a = 0; a < 8; a++) {
-      const uint64_t o = lane_xor64<M>(e[a], lane);
-      e[a] = ((o < e[a]) == keep_min) ? o : e[a];
-    }
+    for (int a = 0; a < 8; a++)
+      if ((a & (K / 2)) == 0) ce_asc(e[a], e[a ^ (K - 1)]);
   } else {
+    constexpr int M = K / 8 - 1;
+    const bool keep_min = (lane & (unsigned)(K / 16)) == 0u;
+    uint64_t o[8];
 #pragma unroll
-    for (int a = 0; a < 8; a++) {
-      if (a & J) continue;
-      const int b = a | J;
-      const bool asc = K < 8 ? (a & K) == 0 : (K >= 512 ? true : (lane & (unsigned)(K / 8)) == 0u);
-      const uint64_t x = e[a], y = e[b];
-      const bool sw = (y < x) == asc;
-      e[a] = sw ? y : x;
-      e[b] = sw ? x : y;
-    }
+    for (int a = 0; a < 8; a++) o[a] = lane_xor64<M>(e[7 - a], lane);
+#pragma unroll
+    for (int a = 0; a < 8; a++) e[a] = ce_lane(e[a], o[a], keep_min);
   }
 }
 
-template <int K, int J>
-__device__ __forceinline__ void bitonic_merge_level(uint64_t (&e)[8], unsigned lane) {
-  bitonic_stage<K, J>(e, lane);
-  if constexpr (J > 1) bitonic_merge_level<K, J / 2>(e, lane);
+template <int J>
+__device__ __forceinline__ void half_stage(uint64_t (&e)[8], unsigned lane) {
+  if constexpr (J >= 8) {
+    constexpr int M = J / 8;
+    const bool keep_min = (lane & (unsigned)M) == 0u;
+#pragma unroll
+    for (int a = 0; a < 8; a++) e[a] = ce_lane(e[a], lane_xor64<M>(e[a], lane), keep_min);
+  } else {
+#pragma unroll
+    for (int a = 0; a < 8; a++)
+      if ((a & J) == 0) ce_asc(e[a], e[a | J]);
+  }
+  if constexpr (J > 1) half_stage<J / 2>(e, lane);
 }
 
 template <int K>
 __device__ __forceinline__ void bitonic512(uint64_t (&e)[8], unsigned lane) {
-  bitonic_merge_level<K, K / 2>(e, lane);
+  flip_stage<K>(e, lane);
+  if constexpr (K >= 4) half_stage<K / 4>(e, lane);
   if constexpr (K < 512) bitonic512<K * 2>(e, lane);
 }
 
 // Segments of at most SEG_WAVE pairs: one wave per tile, padded to 512 words
-// with all-ones words (they sort last), the whole network unrolled. The network
+// with the pad word (it sorts last), the whole network unrolled. The network
 // wants lane l to hold words 8 l .. 8 l + 7; global memory is read and written
 // with lane l on words l + 64 a instead (each wave access one contiguous run)
 // and the wave transposes through its own 576 words of LDS, one pad word after
@@ -766,7 +807,7 @@ __device__ __forceinline__ void wave_sort_tile(const uint32_t *ranges, const uin
 #pragma unroll
   for (int a = 0; a < 8; a++) {
     const uint32_t x = lane + 64u * a;
-    e[a] = x < len ? words[start + x] : ~0ull;
+    e[a] = x < len ? words[start + x] : SORT_PAD;
   }
 #pragma unroll
   for (int a = 0; a < 8; a++) sw[wslot((int)lane + 64 * a)] = e[a];
@@ -794,23 +835,20 @@ __device__ __forceinline__ void wave_sort_tile(const uint32_t *ranges, const uin
 // thread's and the blocked reads and writes spread over the banks.
 __device__ __forceinline__ int lslot(int x) { return x + x / LE; }
 
-// Ascending sort of one thread's LE words: bitonic network, every index and
-// direction known at compile time (80 compare-exchanges).
+// Ascending sort of one thread's LE words: the bitonic network in the form
+// with every comparator ascending (level k: a with a ^ (k - 1), then a with
+// a ^ j for j = k / 4 .. 1), every index known at compile time.
 __device__ __forceinline__ void sort_regs(uint64_t (&e)[LE]) {
 #pragma unroll
   for (int k = 2; k <= LE; k <<= 1) {
 #pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
+    for (int a = 0; a < LE; a++)
+      if ((a & (k >> 1)) == 0) ce_asc(e[a], e[a ^ (k - 1)]);
 #pragma unroll
-      for (int a = 0; a < LE; a++) {
-        if (a & j) continue;
-        const int b = a | j;
-        const bool up = (a & k) == 0;
-        const uint64_t x = e[a], y = e[b];
-        const bool sw = up ? (y < x) : (x < y);
-        e[a] = sw ? y : x;
-        e[b] = sw ? x : y;
-      }
+    for (int j = k >> 2; j > 0; j >>= 1) {
+#pragma unroll
+      for (int a = 0; a < LE; a++)
+        if ((a & j) == 0) ce_asc(e[a], e[a | j]);
     }
   }
 }
@@ -819,8 +857,8 @@ __device__ __forceinline__ void sort_regs(uint64_t (&e)[LE]) {
 // sorted runs of length R that contain o (the second run may be short or
 // empty). The split of the outputs between the runs comes from a binary search
 // along the cross diagonal (merge path); ties go to the first run, and the
-// only equal words are the all-ones padding, so every thread's split agrees
-// with its neighbours'. An exhausted run reads as all-ones.
+// only equal words are the pad words, so every thread's split agrees with its
+// neighbours'. An exhausted run reads as all-ones (above the pad).
 __device__ __forceinline__ void merge_round(const uint64_t *s, int R, int npad, int o, uint64_t (&e)[LE]) {
   const int a0 = o & ~(2 * R - 1), b0 = a0 + R;
   const int alen = min(R, npad - a0), blen = max(0, min(R, npad - b0));
@@ -856,7 +894,7 @@ __device__ __forceinline__ void merge_round(const uint64_t *s, int R, int npad, 
 
 // Sort len <= NV words of global memory in LDS by the whole workgroup and
 // write the final (tile << 32 | depth bits, record) pairs. The words are padded
-// to a multiple of LE with all-ones words (they sort last and are not written);
+// to a multiple of LE with the pad word (it sorts last and is not written);
 // every thread sorts its LE words in registers, then runs of LE, 2 LE, ... are
 // merged pairwise until one run remains.
 __device__ void lds_sort(const uint64_t *src, int len, uint64_t *kout, uint32_t *vout, uint32_t tile, uint64_t *s) {
@@ -866,7 +904,7 @@ __device__ void lds_sort(const uint64_t *src, int len, uint64_t *kout, uint32_t 
 #pragma unroll
   for (int r = 0; r < LE; r++) {
     const int i = r * LT + tid;
-    e[r] = i < len ? src[i] : ~0ull;
+    e[r] = i < len ? src[i] : SORT_PAD;
   }
   __syncthreads();                                   // earlier readers of s are done
 #pragma unroll
