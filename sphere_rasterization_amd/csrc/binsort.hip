@@ -779,11 +779,91 @@ __device__ __forceinline__ void half_stage(uint64_t (&e)[8], unsigned lane) {
   if constexpr (J > 1) half_stage<J / 2>(e, lane);
 }
 
+// From this merge level on, the wave sort moves its words between three
+// layouts through the wave's LDS region instead of exchanging them between
+// lanes, so that every compare-exchange pairs two registers of one lane:
+//   A: word x = 8 l + a           (register index a = bits 0-2 of x)
+//   B: word x = l + 64 a          (a = bits 6-8; also the global-memory layout)
+//   C: word x = (l & 7) + 8 a + 64 (l >> 3)   (a = bits 3-5)
+// A level's stages on bits 6-8 run in B, on bits 3-5 in C, on bits 0-2 in A.
+// Its opening stage (x against x ^ (K - 1)) becomes a stage on the top bit
+// alone, x against x ^ K / 2, once the upper half of every K-block is read in
+// reverse order: the words then form a bitonic sequence per block, and the
+// merge that follows keeps every comparator ascending.
+constexpr int SORT_TR_LEVEL = 256;
+
+// LDS slot (wslot) of the word that lane l, register a holds in a layout.
+__device__ __forceinline__ int slot_a(unsigned l, int a) { return 9 * (int)l + a; }
+__device__ __forceinline__ int slot_b(unsigned l, int a) { return (int)(l + (l >> 3)) + 72 * a; }
+__device__ __forceinline__ int slot_c(unsigned l, int a) { return (int)((l & 7u) + 72u * (l >> 3)) + 9 * a; }
+
+// Store the words from layout A.
+__device__ __forceinline__ void lay_store_a(const uint64_t (&e)[8], unsigned lane, uint64_t *sw) {
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int a = 0; a < 8; a++) sw[slot_a(lane, a)] = e[a];
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Read into layout B; with K > 0, the upper half of every K-block (K >= 128:
+// bit K / 2 of x is a register bit here) in reverse order: word x ^ (K / 2 - 1).
 template <int K>
-__device__ __forceinline__ void bitonic512(uint64_t (&e)[8], unsigned lane) {
-  flip_stage<K>(e, lane);
-  if constexpr (K >= 4) half_stage<K / 4>(e, lane);
-  if constexpr (K < 512) bitonic512<K * 2>(e, lane);
+__device__ __forceinline__ void lay_load_b(uint64_t (&e)[8], unsigned lane, const uint64_t *sw) {
+#pragma unroll
+  for (int a = 0; a < 8; a++) {
+    if (K > 0 && ((64 * a) & (K / 2)) != 0)
+      e[a] = sw[slot_b(lane ^ 63u, a ^ ((K / 2 - 1) >> 6))];
+    else
+      e[a] = sw[slot_b(lane, a)];
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void lay_b_to_c(uint64_t (&e)[8], unsigned lane, uint64_t *sw) {
+#pragma unroll
+  for (int a = 0; a < 8; a++) sw[slot_b(lane, a)] = e[a];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int a = 0; a < 8; a++) e[a] = sw[slot_c(lane, a)];
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void lay_c_to_a(uint64_t (&e)[8], unsigned lane, uint64_t *sw) {
+#pragma unroll
+  for (int a = 0; a < 8; a++) sw[slot_c(lane, a)] = e[a];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int a = 0; a < 8; a++) e[a] = sw[slot_a(lane, a)];
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Stages on register bits R, R - 1, .. 0: the register with the bit clear
+// keeps the smaller word.
+template <int R>
+__device__ __forceinline__ void reg_stages(uint64_t (&e)[8]) {
+#pragma unroll
+  for (int a = 0; a < 8; a++)
+    if (((a >> R) & 1) == 0) ce_asc(e[a], e[a | (1 << R)]);
+  if constexpr (R > 0) reg_stages<R - 1>(e);
+}
+
+template <int K>
+__device__ __forceinline__ void bitonic512(uint64_t (&e)[8], unsigned lane, uint64_t *sw) {
+  if constexpr (K >= SORT_TR_LEVEL) {
+    static_assert(K >= 128, "layout B holds bits 6-8 only");
+    constexpr int TOP = K == 128 ? 0 : K == 256 ? 1 : 2;   // register bit of x bit log2(K) - 1 in B
+    lay_store_a(e, lane, sw);
+    lay_load_b<K>(e, lane, sw);
+    reg_stages<TOP>(e);
+    lay_b_to_c(e, lane, sw);
+    reg_stages<2>(e);
+    lay_c_to_a(e, lane, sw);
+    reg_stages<2>(e);
+  } else {
+    flip_stage<K>(e, lane);
+    if constexpr (K >= 4) half_stage<K / 4>(e, lane);
+  }
+  if constexpr (K < 512) bitonic512<K * 2>(e, lane, sw);
 }
 
 // Segments of at most SEG_WAVE pairs: one wave per tile, padded to 512 words
@@ -814,7 +894,7 @@ __device__ __forceinline__ void wave_sort_tile(const uint32_t *ranges, const uin
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int a = 0; a < 8; a++) e[a] = sw[wslot(8 * (int)lane + a)];
-  bitonic512<2>(e, lane);
+  bitonic512<2>(e, lane, sw);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int a = 0; a < 8; a++) sw[wslot(8 * (int)lane + a)] = e[a];
