@@ -111,8 +111,8 @@ def parse():
                     help="1: 4096 screen-space Gaussians 128x128; 2: 100k 3D Gaussians 512x512; 3: 1M spheres "
                          "1024x1024 (default, the headline metric); 4: 2M Gaussians 1920x1080, 32 channels; "
                          "5: the same scene from 6 cameras 1280x720 and a 2048x64 lidar view")
-    ap.add_argument("--hbm-copy", action="store_true",
-                    help="also time a plain 1 GiB device copy and report the measured HBM bandwidth")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured peaks (sustained clock, FMA rate, copy and LDS bandwidth)")
     ap.add_argument("--assemble", action="store_true",
                     help="instead of the rendering step, time the per-frame parameter assembly (keyframe "
                          "interpolation of 2M primitives, 4 keyframes) and its reverse pass against the HBM peak")
@@ -234,8 +234,9 @@ def main():
     if wl == 3:
         out["roofline"] = roofline(fwd_kernel_ms, cpu, scene)
     out["kernels"] = kernel_rooflines(ktimes, cpu, scene, npairs, rz.total_tiles)
-    if args.hbm_copy:
-        out["hbm_copy_GBps"] = hbm_copy(torch, dev)
+    if not args.no_peaks:
+        out["measured_peaks"] = measured_peaks(torch, dev)
+        add_measured_fracs(out, out["measured_peaks"])
     print(json.dumps(out), flush=True)
 
 
@@ -294,21 +295,34 @@ def assemble_bench(args, torch, dev):
             "roofline": f["roofline"], "reverse": res["reverse"]}
 
 
-def hbm_copy(torch, dev, mib=1024, reps=10):
-    """Measured HBM bandwidth of a plain device copy (bytes read + written / time)."""
-    nf = mib * (1 << 20) // 4
-    src = torch.ones(nf, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / reps
-    return round(2 * nf * 4 / sec / 1e9, 1)
+def measured_peaks(torch, dev):
+    """Peaks measured on this GPU (sphere_rasterization_amd.peaks): the shader
+    clock sustained under a full-chip fp32 FMA loop and the single-issue FMA
+    rate it reaches, the HBM bandwidth of a 16-byte copy of 1 GiB, and the LDS
+    bandwidth of broadcast reads in the compositors' pattern."""
+    from sphere_rasterization_amd import peaks
+    return peaks.measure(torch, dev)
+
+
+def add_measured_fracs(out, peaks):
+    """Each stage's achieved figure against the measured peaks as well: HBM
+    stages against the copy bandwidth, the compositors' lane-ops against the
+    highest VALU rate measured (the fp32 FMA loop: its fp32 FMAs issue faster
+    than one wave64 instruction per four cycles, the fp64 loop runs at that
+    rate; its clock, under full FMA load, is below the compositors')."""
+    if not peaks:
+        return
+    valu = max(peaks["valu_fma_Tlane_ops"], peaks["valu_fma64_Tlane_ops"])
+    for e in (out.get("kernels") or {}).values():
+        if isinstance(e, dict) and e.get("achieved") is not None:
+            if e.get("bound") == "hbm":
+                e["frac_measured"] = round(e["achieved"] / peaks["hbm_copy_GBps"], 4)
+            elif e.get("bound") == "alu":
+                e["frac_measured"] = round(e["achieved"] / valu, 4)
+    r = out.get("roofline")
+    if r and r.get("achieved") is not None:
+        r["peak_measured"] = valu
+        r["frac_measured"] = round(r["achieved"] / valu, 4)
 
 
 def sources_digest(paths):

@@ -12,6 +12,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsplat.so")
 SOURCES = ["api.hip", "project.hip", "binsort.hip", "render_fwd.hip", "render_bwd.hip", "assemble.hip"]
+# measurement kernels (sustained clock, copy and LDS bandwidth), a library of their own
+PEAKS_LIB = os.path.join(HERE, "libsplat_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = os.environ.get("SPLAT_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -47,14 +50,15 @@ def build(verbose: bool = False) -> str:
             print(r.stderr, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES) + len(PEAKS_SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PEAKS_SOURCES))
+    for lib, part in ((LIB, objs[:len(SOURCES)]), (PEAKS_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + part
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed for {os.path.basename(lib)}:\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -233,3 +233,22 @@ def test_serial_views_values():
     pr.pos = pr.scale = pr.rot = pr.opacity = pr.feat = 8
     prm, _ = make_params(S.Params(serial_views=2), 3)
     assert lib.splat_project(make_cams(sc.cams), 1, C.byref(pr), C.byref(prm), 8, 8, None) == L.SPLAT_ERR_INVALID_ARG
+
+
+def test_peaks_library_exports_every_declared_symbol():
+    from sphere_rasterization_amd import peaks as PK
+    assert os.path.exists(PK.LIB_PATH), "build libsplat_peaks.so first"
+    src = open(os.path.join(ROOT, "include", "splat_peaks.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(splat_peaks_[a-z0-9_]+)\s*\(", src)))
+    out = subprocess.run(["nm", "-D", "--defined-only", PK.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (splat_peaks_[a-z0-9_]+)$", out, flags=re.M))
+    assert declared and sorted(PK.EXPORTS) == declared
+    assert not [d for d in declared if d not in exported]
+    lib = PK.load()
+    assert lib.splat_peaks_fma_per_iter() == 8 and lib.splat_peaks_lds_bytes_per_iter() == 128
+    # argument errors are returned before any launch
+    assert lib.splat_peaks_copy(None, None, 16, 1, None) == -1
+    assert lib.splat_peaks_lds(None, 1, 1, None) == -1
+    assert lib.splat_peaks_valu(None, None, 1, 1, None) == -1
+    assert lib.splat_peaks_valu64(None, None, 1, 1, None) == -1
