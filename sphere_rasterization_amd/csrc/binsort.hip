@@ -246,7 +246,7 @@ __global__ __launch_bounds__(TS_THREADS) void k_tile_scan1(uint32_t *cnt_start, 
     for (int r = 0; r < TS_ITEMS; r++) {
       sum += x[r];
       nh += x[r] > (uint32_t)NV ? 1u : 0u;
-      nm += (x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV) ? 1u : 0u;
+      nm += ((x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
     }
     const unsigned long long packed =
         (unsigned long long)sum | ((unsigned long long)nh << 32) | ((unsigned long long)nm << 48);
@@ -588,7 +588,7 @@ __device__ bool fused_tile_scan(const uint32_t *cnt, int T, const uint32_t *row,
     part += x[r];
     sum += x[r];
     nh += x[r] > (uint32_t)NV ? 1u : 0u;
-    nm += (x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV) ? 1u : 0u;
+    nm += ((x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
   }
   unsigned long long total;
   block_exclusive_scan<unsigned long long, TH_THREADS>(part, &total);
@@ -621,7 +621,7 @@ __device__ bool fused_tile_scan(const uint32_t *cnt, int T, const uint32_t *row,
           so.list[T + pm] = (uint32_t)t;
       }
       ph += x[r] > (uint32_t)NV ? 1u : 0u;
-      pm += (x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV) ? 1u : 0u;
+      pm += ((x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
     }
     run += x[r];
   }
@@ -1050,7 +1050,7 @@ __device__ void msd_split(const uint64_t *src, uint64_t *dst, int len, uint32_t 
     for (int r = 0; r < 4; r++) {
       const int i = i0 + r * LT + tid;
       mn = x[r] < mn ? x[r] : mn;
-      mx = (i < len) & (x[r] > mx) ? x[r] : mx;
+      mx = ((i < len) & (x[r] > mx)) ? x[r] : mx;
     }
   }
 #pragma unroll

@@ -30,7 +30,9 @@ namespace {
 // largest lambda so far (at least 0), rescaling them when a contributing sphere
 // raises m, and tests the stop in the log domain: beta - ln tau < m + ln N.
 template <int CM, bool TOPD, bool MS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6 : 1))) void k_fwd_sphere(ViewTable vt, FwdArgs A) {
+// (closest-K recording holds its list in registers and LDS: four waves per SIMD)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? (TOPD ? 4 : 6) : 1))) void k_fwd_sphere(
+    ViewTable vt, FwdArgs A) {
   // One staged entry = NE 16-byte slots at a common stride, so every read of an
   // entry uses one LDS address with constant offsets: three slots of D / g
   // coefficients (fp64 pairs), then (o exp(o zhat / gamma), stop limit bound /
