@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? (
   const TilePix tp = tile_pixel(c, gtile, threadIdx.x);
   const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
   const SphereRay ray = sphere_ray(c, tp);
+  const float gf = (float)ray.g;
   const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // this wave's quadrant
   const int sb = wq * 4 + (int)((threadIdx.x >> 4) & 3u);                  // this lane's 4x4 block
   const float tau = A.tau;
@@ -169,13 +170,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? (
         const double num = sphere_num(ray, __builtin_bit_cast(double2, s_e[0][idx]),
                                       __builtin_bit_cast(double2, s_e[1][idx]),
                                       __builtin_bit_cast(double2, s_e[2][idx]));
-        const bool hit = active & valid & (num > 0.0);
+        // D / g past the five fp64 FMAs goes to fp32: the sign test and the
+        // weight's product run at the fp32 rate (the sign is the fp64 one except
+        // for 0 < D / g < 1.4e-45, which rounds to zero)
+        float numf = (float)num;
+        asm volatile("" : "+v"(numf));                    // keeps the compiler from testing num instead
+        const bool hit = active & valid & (numf > 0.0f);
         if constexpr (MS) {
           if (ballot64(hit)) {
             const float sh = hit ? fmaxf(msh, t[0]) : msh;
             const float rs = __expf(msh - sh);             // 1 unless the shift rises
             // a select, not a 0/1 factor: a lane without a hit may hold lambda > m
-            const float w = hit ? __expf(t[0] - sh) * (float)(num * ray.g) : 0.0f;
+            const float w = hit ? __expf(t[0] - sh) * (numf * gf) : 0.0f;
             N = __builtin_fmaf(N, rs, w);
 #pragma unroll
             for (int ch = 0; ch < CM; ch++) S[ch] = __builtin_fmaf(w, t[2 + ch], S[ch] * rs);
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? (
         } else {
           // the weight is formed on every lane (the empty asm keeps the compiler
           // from moving it under a branch) and selected: straight-line code
-          float wx = t[0] * (float)(num * ray.g);
+          float wx = t[0] * (numf * gf);
           asm volatile("" : "+v"(wx));
           const float w = hit ? wx : 0.0f;
           N += w;
