@@ -28,7 +28,9 @@
 //                                 tile start + chunk prefix + a rank from an LDS
 //                                 atomic
 //   k_seg_sort                    segments up to SEG_WAVE pairs: one wave each,
-//                                 bitonic in registers and lane shuffles; then
+//                                 a bitonic network in registers (lane shuffles
+//                                 for the low merge levels, layouts moved through
+//                                 LDS for the top two); then
 //                                 longer segments from a work queue, one
 //                                 workgroup each: merge sort in LDS up to NV
 //                                 pairs, an MSD split into LDS-sized buckets
