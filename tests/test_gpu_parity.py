@@ -202,6 +202,31 @@ def test_ragged_gauss3d():
     _run(sc, 8, "gauss3d 30k @500x300 ragged")
 
 
+def test_sort_extreme_depths():
+    """Depth keys over the whole positive fp32 range: denormal depths (down to
+    1e-44), depths near the largest float, and many exact ties (broken by the
+    record index). The segment sort compares the (depth bits, record) words in
+    fp64 min/max and 64-bit integer compares, which order alike only for these
+    non-negative bit patterns; both the one-wave path (short tiles) and the
+    long-segment path must give the oracle's order bit for bit."""
+    for n, seed in ((3000, 41), (20000, 42)):
+        sc = S.tiny_2d(seed=seed, n=n)
+        rng = np.random.default_rng(seed + 100)
+        d = np.exp(rng.uniform(np.log(1e-44), np.log(3e38), size=n))
+        ties = rng.random(n) < 0.2
+        d[ties] = rng.choice(np.array([1e-44, 3e-39, 1.0, 2.5e38], dtype=np.float64), size=int(ties.sum()))
+        sc.depth = np.ascontiguousarray(d.astype(np.float32))
+        assert (sc.depth > 0).all() and np.isfinite(sc.depth).all()
+        _log(f"[case] gauss2d {n} @128x128 extreme depths")
+        rz = _rz(sc)
+        rz.forward()
+        orc = O.Oracle(sc)
+        npairs = compare_binning(rz, orc)
+        r = rz.tile_ranges.cpu().numpy().view(np.uint32).reshape(-1, 2).astype(np.int64)
+        _log(f"  binning ok pairs={npairs} longest tile={int((r[:, 1] - r[:, 0]).max())}")
+        orc.close()
+
+
 def test_long_tile_lists():
     """Thousands of pairs per tile: the segments take the long-segment sort."""
     sc = S.gauss3d(seed=15, n=400_000, width=128, height=96)
