@@ -252,3 +252,29 @@ def test_peaks_library_exports_every_declared_symbol():
     assert lib.splat_peaks_lds(None, 1, 1, None) == -1
     assert lib.splat_peaks_valu(None, None, 1, 1, None) == -1
     assert lib.splat_peaks_valu64(None, None, 1, 1, None) == -1
+
+
+def test_sort_word_order_reads_alike_as_fp64():
+    """The segment sort compares its (depth bits << 32 | record) words partly as
+    fp64 (v_min_f64 / v_max_f64) and partly as 64-bit unsigned integers, and
+    pads with the largest finite double. For words whose high half is a
+    non-negative fp32 bit pattern (zero, denormal, normal, infinity: every key
+    the projection writes) both readings must order alike, and none may be a
+    NaN."""
+    rng = np.random.default_rng(5)
+    hi = np.concatenate([
+        np.array([0, 1, 2, 0x007FFFFF, 0x00800000, 0x3F800000, 0x7F7FFFFF, 0x7F800000], np.uint64),
+        rng.integers(0, 0x7F800001, size=4000, dtype=np.uint64),
+    ])
+    lo = rng.integers(0, 1 << 32, size=hi.size, dtype=np.uint64)
+    lo[:8] = np.array([0, 1, 0xFFFFFFFF, 7, 0, 12345, 0xFFFFFFFF, 0xFFFFFFFF], np.uint64)
+    words = np.concatenate([(hi << np.uint64(32)) | lo, np.array([0x7FEFFFFFFFFFFFFF], np.uint64)])
+    as_f64 = words.view(np.float64)
+    assert np.isfinite(as_f64).all() and (as_f64 >= 0).all()
+    assert as_f64[-1] == np.finfo(np.float64).max and words[-1] > words[:-1].max()
+    np.testing.assert_array_equal(np.argsort(words, kind="stable"), np.argsort(as_f64, kind="stable"))
+    # pairwise: min / max of two words agree in both readings
+    a, b = words[:-1:2], words[1::2]
+    fa, fb = as_f64[:-1:2], as_f64[1::2]
+    np.testing.assert_array_equal(np.minimum(fa, fb).view(np.uint64), np.minimum(a, b))
+    np.testing.assert_array_equal(np.maximum(fa, fb).view(np.uint64), np.maximum(a, b))
