@@ -35,39 +35,67 @@ __device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
 
-// Eight values per lane summed over the wave, transposed: every lane l ends with
-// the total of v[l & 7]. Each exchange step halves the values a lane carries
-// (partner lanes keep opposite halves): the row half-mirror pairs lanes that
-// differ in bit 2 of the lane id, the quad permutes pair bits 1 and 0; what
-// is left is one value per lane, summed over the remaining lane bits 3..5.
-__device__ __forceinline__ float wave_sum8_transposed(const float (&v)[8]) {
-  const unsigned lane = lane_id();
-  const bool b2 = lane & 4u, b1 = lane & 2u, b0 = lane & 1u;
-  float a[4], c[2];
-#pragma unroll
-  for (int j = 0; j < 4; j++) a[j] = (b2 ? v[j + 4] : v[j]) + dpp_f32<0x141>(b2 ? v[j] : v[j + 4]);
-#pragma unroll
-  for (int j = 0; j < 2; j++) c[j] = (b1 ? a[j + 2] : a[j]) + dpp_f32<0x4E>(b1 ? a[j] : a[j + 2]);
-  float e = (b0 ? c[1] : c[0]) + dpp_f32<0xB1>(b0 ? c[0] : c[1]);
-  e += dpp_f32<0x128>(e);                         // row rotate by 8: lane ^ 8
-  e += __shfl_xor(e, 16, WAVE);
-  e += __shfl_xor(e, 32, WAVE);
-  return e;
+// Pair sums through the gfx950 lane swaps (VALU; no LDS traffic).
+// v_permlane32_swap exchanges the upper half of its first register with the
+// lower half of its second, so the two results of swapping (x, y) add up to
+// x[l] + x[l + 32] in lanes l < 32 and y[l - 32] + y[l] in lanes l >= 32.
+// v_permlane16_swap exchanges the odd 16-lane rows of the first register with
+// the even rows of the second: the sum holds x summed over rows (0, 1) and
+// (2, 3) in rows 0 and 2, and y the same way in rows 1 and 3. The results are
+// copied to plain integers before the bit casts: bit-casting an element of the
+// returned pair directly read the first element for both.
+__device__ __forceinline__ float swap_add32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  const unsigned a = r[0], b = r[1];
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float swap_add16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  const unsigned a = r[0], b = r[1];
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ double swap_add32(double x, double y) {
+  const unsigned long long bx = __builtin_bit_cast(unsigned long long, x), by = __builtin_bit_cast(unsigned long long, y);
+  const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)bx, (unsigned)by, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(bx >> 32), (unsigned)(by >> 32), false, false);
+  const unsigned l0 = lo[0], l1 = lo[1], h0 = hi[0], h1 = hi[1];
+  return __builtin_bit_cast(double, ((unsigned long long)h0 << 32) | l0) +
+         __builtin_bit_cast(double, ((unsigned long long)h1 << 32) | l1);
+}
+__device__ __forceinline__ double swap_add16(double x, double y) {
+  const unsigned long long bx = __builtin_bit_cast(unsigned long long, x), by = __builtin_bit_cast(unsigned long long, y);
+  const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)bx, (unsigned)by, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(bx >> 32), (unsigned)(by >> 32), false, false);
+  const unsigned l0 = lo[0], l1 = lo[1], h0 = hi[0], h1 = hi[1];
+  return __builtin_bit_cast(double, ((unsigned long long)h0 << 32) | l0) +
+         __builtin_bit_cast(double, ((unsigned long long)h1 << 32) | l1);
 }
 
-// The same transposed reduction for eight fp64 values.
-__device__ __forceinline__ double wave_sum8_transposed_f64(const double (&v)[8]) {
-  const unsigned lane = lane_id();
-  const bool b2 = lane & 4u, b1 = lane & 2u, b0 = lane & 1u;
-  double a[4], c[2];
+template <int CTRL>
+__device__ __forceinline__ double dpp_t(double x) { return dpp_f64<CTRL, 0xf, false>(x); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_t(float x) { return dpp_f32<CTRL>(x); }
+
+// Eight values per lane summed over the wave, transposed: every lane l ends with
+// the total of v[l >> 3] (value q in the lanes of 8-lane group q). Each step
+// halves the values a lane carries. The two lane swaps go first: a swap moves
+// whole halves or rows between two registers, so which value a lane keeps
+// follows from its lane id with no select (lane bit 5, then bit 4). Bit 3 takes
+// a select and a row rotate by 8; three DPP steps then sum each 8-lane group.
+template <typename T>
+__device__ __forceinline__ T wave_sum8_transposed(const T (&v)[8]) {
+  const bool b3 = lane_id() & 8u;
+  T a[4], c[2];
 #pragma unroll
-  for (int j = 0; j < 4; j++) a[j] = (b2 ? v[j + 4] : v[j]) + dpp_f64<0x141, 0xf, false>(b2 ? v[j] : v[j + 4]);
+  for (int j = 0; j < 4; j++) a[j] = swap_add32(v[j], v[j + 4]);     // value j + 4 b5
 #pragma unroll
-  for (int j = 0; j < 2; j++) c[j] = (b1 ? a[j + 2] : a[j]) + dpp_f64<0x4E, 0xf, false>(b1 ? a[j] : a[j + 2]);
-  double e = (b0 ? c[1] : c[0]) + dpp_f64<0xB1, 0xf, false>(b0 ? c[0] : c[1]);
-  e += dpp_f64<0x128, 0xf, false>(e);             // row rotate by 8: lane ^ 8
-  e += __shfl_xor(e, 16, WAVE);
-  e += __shfl_xor(e, 32, WAVE);
+  for (int j = 0; j < 2; j++) c[j] = swap_add16(a[j], a[j + 2]);     // value j + 2 b4 + 4 b5
+  T e = (b3 ? c[1] : c[0]) + dpp_t<0x128>(b3 ? c[0] : c[1]);         // row rotate by 8: lane ^ 8
+  e += dpp_t<0xB1>(e);                                                // lane ^ 1
+  e += dpp_t<0x4E>(e);                                                // lane ^ 2
+  e += dpp_t<0x141>(e);                                               // 8-lane mirror: the other quad
   return e;
 }
 
@@ -112,6 +140,7 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
   constexpr int NF = CM;                    // fp32 values per entry: features
   constexpr int NFP = NF | 1;               // odd row stride: lanes of one entry hit distinct banks
   constexpr int NG = (NF + 7) / 8;          // groups of eight for the transposed reduction
+  static_assert(NG <= 8, "one lane of an 8-lane group per group of channels");
   // entries staged per batch: fewer with many channels, so that two or more
   // workgroups fit a CU's LDS
   constexpr int BT = NF >= 64 ? 64 : 128;
@@ -235,11 +264,12 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         double v8[8];
 #pragma unroll
         for (int q = 0; q < 8; q++) v8[q] = q < 6 ? vg[q] : 0.0;
-        const double r = wave_sum8_transposed_f64(v8);
-        if (lane < 6u) atomicAdd(&s_ag[idx][lane], r);
+        const double r = wave_sum8_transposed(v8);
+        if (((lane & 7u) == 0u) & ((lane >> 3) < 6u)) atomicAdd(&s_ag[idx][lane >> 3], r);
       }
       if constexpr (NF >= 3) {
-        // wave totals, transposed: lane l < NF adds channel l
+        // wave totals, transposed: group gq's channel 8 gq + q ends in the lanes
+        // 8q..8q+7, and lane 8q + j adds that of group j
         float tot[NG];
 #pragma unroll
         for (int gq = 0; gq < NG; gq++) {
@@ -250,8 +280,9 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         }
         float x = tot[0];
 #pragma unroll
-        for (int gq = 1; gq < NG; gq++) x = (lane >> 3) == (unsigned)gq ? tot[gq] : x;
-        if (lane < (unsigned)NF) atomicAdd(&s_af[idx][lane], x);
+        for (int gq = 1; gq < NG; gq++) x = (lane & 7u) == (unsigned)gq ? tot[gq] : x;
+        const unsigned ch = 8u * (lane & 7u) + (lane >> 3);
+        if (((lane & 7u) < (unsigned)NG) & (ch < (unsigned)NF)) atomicAdd(&s_af[idx][ch], x);
       } else {
 #pragma unroll
         for (int q = 0; q < NF; q++) {
@@ -495,8 +526,8 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       double v8[8];
 #pragma unroll
       for (int q = 0; q < 8; q++) v8[q] = q < 6 ? vg[q] : 0.0;
-      const double r = wave_sum8_transposed_f64(v8);
-      if (lane < 6u) atomicAdd(&s_ag[idx][lane], r);
+      const double r = wave_sum8_transposed(v8);
+      if (((lane & 7u) == 0u) & ((lane >> 3) < 6u)) atomicAdd(&s_ag[idx][lane >> 3], r);
       const float rf = row_sum_to_last(vf);
       if ((lane & 15u) == 15u) atomicAdd(&s_af[idx], rf);
     };
@@ -552,28 +583,10 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
 // loop do not wait for the prefetch (scalar loads share a counter with LDS and
 // return out of order, and every LDS wait would have waited for them too).
 // ---------------------------------------------------------------------------
-// x + x[lane ^ 32] and x + x[lane ^ 16] in every lane, with the gfx950 lane swaps
-// (VALU; no LDS traffic). v_permlane32_swap exchanges the upper half of its first
-// register with the lower half of its second, v_permlane16_swap the odd rows of
-// the first with the even rows of the second; given two copies of x, the two
-// results add up to the pair sum in every lane. The two results are copied to
-// plain integers before the bit casts: bit-casting an element of the returned
-// pair directly read the first element for both.
-__device__ __forceinline__ float add_xor32(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const unsigned a = r[0], b = r[1];
-  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-__device__ __forceinline__ float add_xor16(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const unsigned a = r[0], b = r[1];
-  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-
-// Wave-wide minimum (uniform): butterflies within each 16-lane row, then the
-// row pairs and halves through the lane swaps.
+// Wave-wide minimum (uniform): butterflies within each 16-lane row leave every
+// lane with its row's minimum; row_bcast:15 then folds row 0 into row 1 and row
+// 2 into row 3, row_bcast:31 folds lane 31 into row 3, and lane 63 holds the
+// minimum. Rows outside a step's row mask take the identity ~0.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
@@ -583,31 +596,9 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   x = min(x, dpp_u32<0x4E>(x));     // lane ^ 2
   x = min(x, dpp_u32<0x141>(x));    // 8-lane mirror
   x = min(x, dpp_u32<0x140>(x));    // 16-lane mirror
-  {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    const uint32_t a = r[0], b = r[1];
-    x = min(a, b);
-  }
-  {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    const uint32_t a = r[0], b = r[1];
-    x = min(a, b);
-  }
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
-}
-
-// wave_sum8_transposed with the two cross-row steps on the lane swaps.
-__device__ __forceinline__ float wave_sum8_transposed_swap(const float (&v)[8]) {
-  const unsigned lane = lane_id();
-  const bool b2 = lane & 4u, b1 = lane & 2u, b0 = lane & 1u;
-  float a[4], c[2];
-#pragma unroll
-  for (int j = 0; j < 4; j++) a[j] = (b2 ? v[j + 4] : v[j]) + dpp_f32<0x141>(b2 ? v[j] : v[j + 4]);
-#pragma unroll
-  for (int j = 0; j < 2; j++) c[j] = (b1 ? a[j + 2] : a[j]) + dpp_f32<0x4E>(b1 ? a[j] : a[j + 2]);
-  float e = (b0 ? c[1] : c[0]) + dpp_f32<0xB1>(b0 ? c[0] : c[1]);
-  e += dpp_f32<0x128>(e);                         // row rotate by 8: lane ^ 8
-  return add_xor32(add_xor16(e));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x142, 0xa, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // One recorded entry: what the gradient terms need (wave-uniform values).
@@ -841,9 +832,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
 #pragma unroll
       for (int gq = 0; gq < NG; gq++) {
         const float (&vg)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * gq]);
-        const float r = wave_sum8_transposed_swap(vg);
-        const int q = 8 * gq + (int)lane;
-        if (lane < 8u && q < rowlen && r != 0.0f) atomicAdd(row + q, r);
+        const float r = wave_sum8_transposed(vg);
+        const int q = 8 * gq + (int)(lane >> 3);
+        if (((lane & 7u) == 0u) & (q < rowlen) & (r != 0.0f)) atomicAdd(row + q, r);
       }
     }
     m = mn;
@@ -862,7 +853,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
   }
   if (EXT && A.kslot) {
     // intrinsics: the ray (x, y) = ((px - cx) / fx, (py - cy) / fy); per wave
-    // the pixels' (d/dfx, d/dfy, d/dcx, d/dcy) are summed, lanes 0..3 add them
+    // the pixels' (d/dfx, d/dfy, d/dcx, d/dcy) are summed, lanes 0, 8, 16, 24 add them
     double v8[8];
     v8[0] = -(double)kgx * ray.x * c.ifx;
     v8[1] = -(double)kgy * ray.y * c.ify;
@@ -870,8 +861,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? 6
     v8[3] = -(double)kgy * c.ify;
 #pragma unroll
     for (int q = 4; q < 8; q++) v8[q] = 0.0;
-    const double r = wave_sum8_transposed_f64(v8);
-    if (lane < 4u) atomicAdd(A.kslot + ((size_t)view * SPLAT_K_SLOTS + blockIdx.x % SPLAT_K_SLOTS) * 4 + lane, r);
+    const double r = wave_sum8_transposed(v8);
+    if (((lane & 7u) == 0u) & ((lane >> 3) < 4u))
+      atomicAdd(A.kslot + ((size_t)view * SPLAT_K_SLOTS + blockIdx.x % SPLAT_K_SLOTS) * 4 + (lane >> 3), r);
   }
 }
 
@@ -1009,9 +1001,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
     na = s_va[sl][tid];
     nb = s_vb[sl][tid];
     const uint32_t mn = wave_min_u32(q0);
-    const float sum = wave_sum8_transposed_swap(v);
+    const float sum = wave_sum8_transposed(v);
     float *row = A.accs + (size_t)m * A.rs;
-    if (lane < 8u && (int)lane < rowlen && sum != 0.0f) atomicAdd(row + lane, sum);
+    if (((lane & 7u) == 0u) & ((int)(lane >> 3) < rowlen) & (sum != 0.0f)) atomicAdd(row + (lane >> 3), sum);
     m = mn;
   };
   while (m != NONE) {
