@@ -35,6 +35,22 @@ __device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
 
+// 1 / d and t / d for 0 < d <= 1 and normal t (here d = 1 - alpha, alpha at
+// most alpha_max < 1): the hardware reciprocal refined by two Newton steps, and
+// the quotient t r corrected once by its residual. Within an ulp or two of the
+// rounded quotient, without the scaling and fix-up steps that IEEE division
+// spends on the full exponent range.
+__device__ __forceinline__ double recip_unit(double d) {
+  double r = __builtin_amdgcn_rcp(d);
+  r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+  r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+  return r;
+}
+__device__ __forceinline__ double div_unit(double t, double d, double r) {
+  const double q = t * r;
+  return __builtin_fma(__builtin_fma(-d, q, t), r, q);
+}
+
 // Pair sums through the gfx950 lane swaps (VALU; no LDS traffic).
 // v_permlane32_swap exchanges the upper half of its first register with the
 // lower half of its second, so the two results of swapping (x, y) add up to
@@ -74,7 +90,7 @@ __device__ __forceinline__ double swap_add16(double x, double y) {
 }
 
 template <int CTRL>
-__device__ __forceinline__ double dpp_t(double x) { return dpp_f64<CTRL, 0xf, false>(x); }
+__device__ __forceinline__ double dpp_t(double x) { return dpp_f64<CTRL, 0xf, true>(x); }
 template <int CTRL>
 __device__ __forceinline__ float dpp_t(float x) { return dpp_f32<CTRL>(x); }
 
@@ -233,7 +249,8 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
       for (int q = 0; q < NF; q++) vf[q] = 0.0f;
       if (act) {
         const float om = 1.0f - al;
-        const double Tkd = T / (1.0 - (double)al);
+        const double dal = 1.0 - (double)al;
+        const double Tkd = div_unit(T, dal, recip_unit(dal));
         const float Tk = (float)Tkd;
         float da = 0.0f;
         const float wk = Tk * al;
@@ -505,11 +522,12 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       for (int q = 0; q < 6; q++) vg[q] = 0.0;
       if (act) {
         const float om = 1.0f - al;
-        const double Tkd = Te / (1.0 - (double)al);
+        const double dal = 1.0 - (double)al, ral = recip_unit(dal);
+        const double Tkd = div_unit(Te, dal, ral);
         const float Tk = (float)Tkd;
         const float dep = s_dep[idx];
         vf = Tk * al * g0;
-        const float da = Tk * (dep - Se) * g0 + (float)(Tfin / (1.0 - (double)al)) * g1;
+        const float da = Tk * (dep - Se) * g0 + (float)div_unit(Tfin, dal, ral) * g1;
         Se = __builtin_fmaf(al, dep, om * Se);
         Te = Tkd;
         if (!(og > amax)) {              // alpha is the constant amax where clamped
