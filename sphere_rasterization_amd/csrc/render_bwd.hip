@@ -241,41 +241,40 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
       const float al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
       const bool act = (pos < lastp) & (al >= amin);
       if (ballot64(act) == 0) return;
-      double vg[6];
+      // Straight-line code on every lane: a lane without this entry takes
+      // alpha = 0, which leaves T and Sb as they are (a division by 1) and
+      // zeroes its terms; only the clamp and the alpha gradient need selects.
+      const float ala = act ? al : 0.0f;
+      const float om = 1.0f - ala;
+      const double dal = 1.0 - (double)ala;
+      const double Tkd = div_unit(T, dal, recip_unit(dal));
+      const float Tk = (float)Tkd;
+      const float wk = Tk * ala;
+      // d loss / d alpha = T_k sum_ch (f_ch - Sb_ch) g_ch, and sum_ch Sb_ch g_ch
+      // follows the same blend as Sb: one dot product per entry
       float vf[NF];
+      float fg = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 6; q++) vg[q] = 0.0;
-#pragma unroll
-      for (int q = 0; q < NF; q++) vf[q] = 0.0f;
-      if (act) {
-        const float om = 1.0f - al;
-        const double dal = 1.0 - (double)al;
-        const double Tkd = div_unit(T, dal, recip_unit(dal));
-        const float Tk = (float)Tkd;
-        float da = 0.0f;
-        const float wk = Tk * al;
-        // d loss / d alpha = T_k sum_ch (f_ch - Sb_ch) g_ch, and sum_ch Sb_ch g_ch
-        // follows the same blend as Sb: one dot product per entry
-        float fg = 0.0f;
-#pragma unroll
-        for (int ch = 0; ch < CM; ch++) {
-          const float f = s_f[idx][ch];
-          vf[ch] = wk * g[ch];
-          fg = __builtin_fmaf(f, g[ch], fg);
-        }
-        da = Tk * (fg - Sb);
-        Sb = __builtin_fmaf(al, fg, om * Sb);
-        T = Tkd;
-        if (!(og > amax)) {              // alpha is the constant amax where clamped
-          vg[5] = (double)(G * da);
-          const double dp = -(double)al * (double)da;     // d loss / d power
-          const double ha = ab.x, bb = ab.y, hc = co.x;   // a/2, b, c/2
-          vg[0] = -dp * (2.0 * ha * dx + bb * dy);
-          vg[1] = -dp * (bb * dx + 2.0 * hc * dy);
-          vg[2] = dp * 0.5 * dx * dx;
-          vg[3] = dp * dx * dy;
-          vg[4] = dp * 0.5 * dy * dy;
-        }
+      for (int ch = 0; ch < CM; ch++) {
+        const float f = s_f[idx][ch];
+        vf[ch] = wk * g[ch];
+        fg = __builtin_fmaf(f, g[ch], fg);
+      }
+      const float da = Tk * (fg - Sb);
+      Sb = __builtin_fmaf(ala, fg, om * Sb);
+      T = Tkd;
+      // alpha is the constant amax where clamped
+      const bool geo = act & !(og > amax);
+      double vg[6];
+      vg[5] = geo ? (double)(G * da) : 0.0;
+      {
+        const double dp = geo ? -(double)ala * (double)da : 0.0;   // d loss / d power
+        const double ha = ab.x, bb = ab.y, hc = co.x;                // a/2, b, c/2
+        vg[0] = -dp * (2.0 * ha * dx + bb * dy);
+        vg[1] = -dp * (bb * dx + 2.0 * hc * dy);
+        vg[2] = dp * 0.5 * dx * dx;
+        vg[3] = dp * dx * dy;
+        vg[4] = dp * 0.5 * dy * dy;
       }
       {
         double v8[8];
@@ -516,30 +515,29 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       const float al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
       const bool act = (pos < lastp) & (al >= amin);
       if (ballot64(act) == 0) return;
+      // straight-line code on every lane, as in the camera pass: alpha = 0 for
+      // a lane without this entry
+      const float ala = act ? al : 0.0f;
+      const float om = 1.0f - ala;
+      const double dal = 1.0 - (double)ala, ral = recip_unit(dal);
+      const double Tkd = div_unit(Te, dal, ral);
+      const float Tk = (float)Tkd;
+      const float dep = s_dep[idx];
+      const float vf = Tk * ala * g0;
+      const float da = Tk * (dep - Se) * g0 + (float)div_unit(Tfin, dal, ral) * g1;
+      Se = __builtin_fmaf(ala, dep, om * Se);
+      Te = Tkd;
+      const bool geo = act & !(og > amax);    // alpha is the constant amax where clamped
       double vg[6];
-      float vf = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 6; q++) vg[q] = 0.0;
-      if (act) {
-        const float om = 1.0f - al;
-        const double dal = 1.0 - (double)al, ral = recip_unit(dal);
-        const double Tkd = div_unit(Te, dal, ral);
-        const float Tk = (float)Tkd;
-        const float dep = s_dep[idx];
-        vf = Tk * al * g0;
-        const float da = Tk * (dep - Se) * g0 + (float)div_unit(Tfin, dal, ral) * g1;
-        Se = __builtin_fmaf(al, dep, om * Se);
-        Te = Tkd;
-        if (!(og > amax)) {              // alpha is the constant amax where clamped
-          vg[5] = (double)(G * da);
-          const double dp = -(double)al * (double)da;     // d loss / d power
-          const double ha = ab.x, bb = ab.y, hc = co.x;   // a/2, b, c/2
-          vg[0] = -dp * (2.0 * ha * dx + bb * dy);
-          vg[1] = -dp * (bb * dx + 2.0 * hc * dy);
-          vg[2] = dp * 0.5 * dx * dx;
-          vg[3] = dp * dx * dy;
-          vg[4] = dp * 0.5 * dy * dy;
-        }
+      vg[5] = geo ? (double)(G * da) : 0.0;
+      {
+        const double dp = geo ? -(double)ala * (double)da : 0.0;   // d loss / d power
+        const double ha = ab.x, bb = ab.y, hc = co.x;                // a/2, b, c/2
+        vg[0] = -dp * (2.0 * ha * dx + bb * dy);
+        vg[1] = -dp * (bb * dx + 2.0 * hc * dy);
+        vg[2] = dp * 0.5 * dx * dx;
+        vg[3] = dp * dx * dy;
+        vg[4] = dp * 0.5 * dy * dy;
       }
       double v8[8];
 #pragma unroll
