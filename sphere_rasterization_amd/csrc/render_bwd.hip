@@ -421,11 +421,14 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
     const int lo = hi > BL ? hi - BL : 0;
     const int cnt = hi - lo;
     unsigned mask = 0;
+    int seam = 0;
     if ((int)tid < cnt) {
       const uint32_t rid = A.vals[start + lo + tid];
       const DrawRec d = A.draw[rid];
       s_rid[tid] = rid;
-      s_uv[tid] = stage_uv(c, tp, d, true);
+      const double2 uv = stage_uv(c, tp, d, true);
+      s_uv[tid] = uv;
+      seam = seam_flag(c, uv.x);
       const Conic cn = stage_conic(d);
       s_ab[tid] = cn.ab;
       s_co[tid] = cn.co;
@@ -454,9 +457,10 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const uint64_t bq = ballot64(((mask >> q) & 1u) != 0u);
-      if ((mask >> q) & 1u) s_idx[q][s_woff[sw][q] + __popcll(bq & below)] = (uint16_t)tid;
+      if ((mask >> q) & 1u) s_idx[q][s_woff[sw][q] + __popcll(bq & below)] = (uint16_t)((int)tid | seam);
     }
     __syncthreads();
+    // list entries: staged index | LIST_SEAM
     const int L = __builtin_amdgcn_readfirstlane(s_cnt[wq]);
     const int k0 = (L * part) / 4, k1 = (L * (part + 1)) / 4;
 
@@ -464,12 +468,16 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
     {
       double Pt = 1.0;
       float Ax = 0.0f;
-      auto fwd = [&](const int idx) {
+      auto fwd = [&](const int ie) {
+        const int idx = ie & (LIST_SEAM - 1);
         const uint32_t pos = (uint32_t)(lo + idx);
         if (pos >= wlast) return;
-        float G, og;
+        float G, og, al;
         double dx, dy;
-        const float al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+        if (ie & LIST_SEAM)                            // wave-uniform
+          al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+        else
+          al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
         const bool hit = (pos < lastp) & (al >= amin);
         const float w = (hit ? 1.0f : 0.0f) * (float)(Pt * (double)al);
         Ax = __builtin_fmaf(w, s_dep[idx], Ax);
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
         const uint64_t four = *reinterpret_cast<const uint64_t *>(&s_idx[wq][k]);
         const uint32_t lo4 = __builtin_amdgcn_readfirstlane((uint32_t)four);
         const uint32_t hi4 = __builtin_amdgcn_readfirstlane((uint32_t)(four >> 32));
-        if ((uint32_t)lo + (lo4 & 0xffffu) >= wlast) break;   // positions increase along the list
+        if ((uint32_t)lo + (lo4 & (LIST_SEAM - 1)) >= wlast) break;   // positions increase along the list
         fwd((int)(lo4 & 0xffffu));
         fwd((int)(lo4 >> 16));
         fwd((int)(hi4 & 0xffffu));
@@ -506,13 +514,17 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       Sb = __builtin_fmaf((float)Pj, Sb, s_pA[j][pix]);
     }
     // 3. the part back to front
-    auto entry = [&](const int idx) {
+    auto entry = [&](const int ie) {
+      const int idx = ie & (LIST_SEAM - 1);
       const uint32_t pos = (uint32_t)(lo + idx);
       if (pos >= wlast) return;
       const double2 ab = s_ab[idx], co = s_co[idx];
-      float G, og;
+      float G, og, al;
       double dx, dy;
-      const float al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
+      if (ie & LIST_SEAM)                              // wave-uniform
+        al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
+      else
+        al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
       const bool act = (pos < lastp) & (al >= amin);
       if (ballot64(act) == 0) return;
       // straight-line code on every lane, as in the camera pass: alpha = 0 for

@@ -334,3 +334,14 @@ __device__ __forceinline__ float splat_alpha(const ViewDev &c, double pxr, doubl
   og = (float)co.y * G;
   return fminf(amax, og);
 }
+
+// Spherical views: a batch list entry carries LIST_SEAM when its staged centre
+// (stage_uv: already the image of the centre nearest the tile centre) lies
+// within 8 columns of half a turn from the tile centre. A pixel of the tile is
+// at most 7.5 columns from that centre, so only for such an entry can the
+// other image be the nearer one for some pixel; every other entry takes
+// splat_alpha without the per-pixel wrap, which would leave it unchanged.
+constexpr int LIST_SEAM = 0x8000;
+__device__ __forceinline__ int seam_flag(const ViewDev &c, double tu) {
+  return fabs(tu - 8.0) >= 0.5 * (double)c.W - 8.0 ? LIST_SEAM : 0;
+}

@@ -449,10 +449,13 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
   for (uint32_t b = start; b < end; b += LB) {
     const uint32_t e = b + tid;
     unsigned mask = 0;
+    int seam = 0;
     if (e < end) {
       const uint32_t rid = A.vals[e];
       const DrawRec d = A.draw[rid];
-      s_uv[tid] = stage_uv(c, tp, d, true);
+      const double2 uv = stage_uv(c, tp, d, true);
+      s_uv[tid] = uv;
+      seam = seam_flag(c, uv.x);
       const Conic cn = stage_conic(d);
       s_ab[tid] = cn.ab;
       s_co[tid] = cn.co;
@@ -480,16 +483,20 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const uint64_t bq = ballot64(((mask >> q) & 1u) != 0u);
-      if ((mask >> q) & 1u) s_idx[q][s_woff[sw][q] + __popcll(bq & below)] = (uint16_t)tid;
+      if ((mask >> q) & 1u) s_idx[q][s_woff[sw][q] + __popcll(bq & below)] = (uint16_t)((int)tid | seam);
     }
     __syncthreads();
-    // this wave's part of its quadrant's list
+    // this wave's part of its quadrant's list (entries: staged index | LIST_SEAM)
     const int L = __builtin_amdgcn_readfirstlane(s_cnt[wq]);
     const int k0 = (L * part) / 4, k1 = (L * (part + 1)) / 4;
-    auto one = [&](int idx, double &Tx, float &Sx, uint32_t &lx, bool &ax) {
-      float G, og;
+    auto one = [&](int ie, double &Tx, float &Sx, uint32_t &lx, bool &ax) {
+      const int idx = ie & (LIST_SEAM - 1);
+      float G, og, al;
       double dx, dy;
-      const float al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+      if (ie & LIST_SEAM)                              // wave-uniform
+        al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
+      else
+        al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
       const bool hit = ax & (al >= amin);
       const float w = (hit ? 1.0f : 0.0f) * (float)(Tx * (double)al);
       Sx = __builtin_fmaf(w, s_dep[idx], Sx);

@@ -66,3 +66,25 @@ def rotation(rng):
     if np.linalg.det(Q) < 0:
         Q[:, 0] = -Q[:, 0]
     return Q
+
+
+def lidar_half_turn(seed=61, n_near=400, n_far=6000, W=256, H=32):
+    """A spherical camera at the origin inside a cloud of 3D Gaussians, 400 of
+    them 0.3-0.8 m from it with scales of 0.1-0.6 m: their footprints wrap
+    around more than half the panorama, so some tiles list entries centred near
+    their own antipode, where pixels of one tile find different images of the
+    centre nearest."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((n_near, 3))
+    v /= np.linalg.norm(v, axis=1, keepdims=True)
+    near = v * rng.uniform(0.3, 0.8, (n_near, 1))
+    far = rng.uniform(-5.0, 5.0, (n_far, 3))
+    mu = np.concatenate([near, far])
+    n = len(mu)
+    s = np.concatenate([np.exp(rng.uniform(math.log(0.1), math.log(0.6), (n_near, 3))),
+                        np.exp(rng.uniform(math.log(0.01), math.log(0.3), (n_far, 3)))])
+    q = S._unit_quats(rng, n)
+    o = 1.0 / (1.0 + np.exp(-rng.standard_normal(n)))
+    col = rng.uniform(0.0, 1.0, (n, 3))
+    return S.Scene(S.PRIM_GAUSS3D, n, 3, S._c32(mu), S._c32(s), S._c32(o), S._c32(col), rot=S._c32(q),
+                   cams=[lidar(W, H, t=[0.0, 0.0, 0.0])], name="lidar_half_turn")

@@ -315,6 +315,15 @@ def test_multiview_with_lidar():
         _log(f"  one call {k} worst={w:.3f}")
 
 
+def test_lidar_half_turn_footprints():
+    """Lidar view with Gaussians whose footprints wrap past half the panorama:
+    list entries centred near the antipode of their tile, where the column wrap
+    of each pixel's offset decides which image of the centre it sees (the
+    kernels take the per-pixel wrap for those entries only). Forward and
+    reverse pass against the oracle."""
+    _run(TS.lidar_half_turn(), 62, "gauss3d 6400 lidar 256x32, footprints past half a turn")
+
+
 def test_multiview_serial_views():
     """splat_params.serial_views = 1 (every kernel on the caller's stream, no side
     stream): the same forward outputs bit for bit as the forked call, and gradients

@@ -756,3 +756,27 @@ def test_max_shift_only_rescales_the_normalisation():
     ga, gb = a.backward(g), b.backward(g)
     for k in ("pos", "scale", "opacity", "feat", "cam_R", "cam_t"):
         np.testing.assert_array_equal(ga[k], gb[k])
+
+
+def test_lidar_half_turn_scene_reaches_the_antipode():
+    """The lidar half-turn parity scene lists entries centred within 8 columns of
+    the half turn from their tile's centre, and for some of them pixels of the
+    tile lie more than half a turn from the centre's image nearest the tile
+    centre: the case the per-pixel column wrap exists for."""
+    sc = TS.lidar_half_turn()
+    orc = O.Oracle(sc)
+    pr = orc.proj()
+    keys, vals, _ = orc.pairs()
+    W = sc.cams[0].width
+    TW = (W + 15) // 16
+    tile = (keys >> np.uint64(32)).astype(np.int64)
+    u = pr["u"][vals.astype(np.int64)]
+    tx = tile % TW
+    du = np.mod(u - (16 * tx + 8) + W / 2, W) - W / 2       # nearest image, from the tile centre
+    near = np.abs(du) >= W / 2 - 8
+    assert near.sum() >= 50
+    # pixel columns of those tiles that lie more than W/2 from that image
+    px = np.arange(16)[None, :] + 0.5 - 8.0                  # from the tile centre
+    off = px - du[near][:, None]
+    assert ((off >= W / 2) | (off < -W / 2)).sum() >= 100
+    orc.close()
