@@ -427,7 +427,7 @@ def kernel_rooflines(kt, cpu, scene, npairs, total_tiles):
             e["ops"] = ops
             e["achieved"], e["frac"] = _frac(ops, tsum(bwd), VALU_PEAK_TOPS, 1e12)
         out["render_bwd"] = e
-    for name, pre in (("render_fwd", ("k_fwd_alpha", "k_fwd_lidar")), ("render_bwd", ("k_bwd_alpha", "k_bwd_lidar"))):
+    for name, pre in (("render_fwd", ("k_fwd_alpha", "k_fwd_split")), ("render_bwd", ("k_bwd_alpha", "k_bwd_split"))):
         ks = {k: v for k, v in kt.items() if k.split("<")[0] in pre}
         if ks:
             out[name] = {"kernels": sorted(ks), "us": round(tsum(ks), 2), "bound": "alu"}

@@ -365,25 +365,32 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
 // ---------------------------------------------------------------------------
 constexpr int BL = 512;                  // entries staged per batch
 
-__global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int tile_begin) {
+// SPH = false: pinhole views with up to four channels (launches with few
+// tiles, as in the forward). There Sb is the blend of f . g over the channels
+// (f the entry's features, g the pixel's upstream gradient), so the per-part
+// state is still one value, and d loss / d alpha = T_k (f . g - Sb).
+template <int CM, bool SPH>
+__global__ __launch_bounds__(1024) void k_bwd_split(ViewTable vt, BwdArgs A, int tile_begin) {
+  constexpr int NF = SPH ? 1 : CM;         // range, or the features
+  constexpr int NFP = NF | 1;              // odd stride of the feature sums
   __shared__ double2 s_uv[BL];
   __shared__ double2 s_ab[BL];
   __shared__ double2 s_co[BL];
-  __shared__ float s_dep[BL];
+  __shared__ float s_f[BL][NF];
   __shared__ uint32_t s_rid[BL];
   __shared__ __align__(16) uint16_t s_idx[4][BL];  // per-quadrant lists of the batch
   __shared__ int s_woff[16][4];
   __shared__ int s_cnt[4];
   __shared__ double s_ag[BL][7];           // du, dv, d_ca, d_cb, d_cc, d_opac (odd stride)
-  __shared__ float s_af[BL];               // d_depth
-  __shared__ float s_pA[4][256];           // per part and pixel: depth composited from T = 1,
+  __shared__ float s_af[BL][NFP];          // d_depth, or d_feature
+  __shared__ float s_pA[4][256];           // per part and pixel: Sb composited from T = 1,
   __shared__ double s_pT[4][256];          //   and the part's transmittance
   __shared__ uint32_t s_maxlast;
   if (*A.overflow) return;
   const int gtile = tile_begin + (int)blockIdx.x;
   const int view = view_of_tile(vt, gtile);
   const ViewDev &c = vt.v[view];
-  if (c.kind != SPLAT_CAM_SPHERICAL) return;
+  if ((c.kind == SPLAT_CAM_SPHERICAL) != SPH) return;
   const unsigned tid = threadIdx.x, pix = tid & 255u;
   const int part = __builtin_amdgcn_readfirstlane((int)(tid >> 8));           // 0..3
   const int wq = __builtin_amdgcn_readfirstlane((int)((tid >> 6) & 3u));     // quadrant
@@ -398,8 +405,11 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
   uint32_t lastp = 0;
   double T = 1.0;                          // after the batch (the same in all four copies)
   float Sb = 0.0f;
-  const float g0 = tp.inside ? A.dimg[pofs] : 0.0f;           // d loss / d depth
-  const float g1 = tp.inside ? A.dimg[pofs + plane] : 0.0f;   // d loss / d opacity
+  // upstream gradient: d loss / d (depth, opacity), or per channel
+  float g[SPH ? 2 : NF];
+#pragma unroll
+  for (int ch = 0; ch < (SPH ? 2 : NF); ch++) g[ch] = tp.inside && (SPH || ch < A.C) ? A.dimg[pofs + ch * plane] : 0.0f;
+  const long long vbase = (long long)view * A.n;
   if (tp.inside) {
     lastp = min(A.last[p], len);
     T = (double)A.T_final[p];
@@ -426,16 +436,23 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       const uint32_t rid = A.vals[start + lo + tid];
       const DrawRec d = A.draw[rid];
       s_rid[tid] = rid;
-      const double2 uv = stage_uv(c, tp, d, true);
+      const double2 uv = stage_uv(c, tp, d, SPH);
       s_uv[tid] = uv;
-      seam = seam_flag(c, uv.x);
+      if constexpr (SPH) seam = seam_flag(c, uv.x);
       const Conic cn = stage_conic(d);
       s_ab[tid] = cn.ab;
       s_co[tid] = cn.co;
-      s_dep[tid] = A.aux[rid].z;
+      if constexpr (SPH) {
+        s_f[tid][0] = A.aux[rid].z;
+      } else {
+        const long long id = (long long)rid - vbase;
+#pragma unroll
+        for (int ch = 0; ch < NF; ch++) s_f[tid][ch] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      }
 #pragma unroll
       for (int q = 0; q < 7; q++) s_ag[tid][q] = 0.0;
-      s_af[tid] = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NF; q++) s_af[tid][q] = 0.0f;
       mask = quadrant_mask(tp, d);
     }
 #pragma unroll
@@ -464,6 +481,17 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
     const int L = __builtin_amdgcn_readfirstlane(s_cnt[wq]);
     const int k0 = (L * part) / 4, k1 = (L * (part + 1)) / 4;
 
+    // the value an entry blends into Sb: its range, or f . g
+    auto blend_value = [&](const int idx) {
+      if constexpr (SPH) {
+        return s_f[idx][0];
+      } else {
+        float fg = 0.0f;
+#pragma unroll
+        for (int ch = 0; ch < NF; ch++) fg = __builtin_fmaf(s_f[idx][ch], g[ch], fg);
+        return fg;
+      }
+    };
     // 1. the part front to back from T = 1
     {
       double Pt = 1.0;
@@ -474,13 +502,13 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
         if (pos >= wlast) return;
         float G, og, al;
         double dx, dy;
-        if (ie & LIST_SEAM)                            // wave-uniform
+        if (SPH && (ie & LIST_SEAM))                   // wave-uniform
           al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
         else
           al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
         const bool hit = (pos < lastp) & (al >= amin);
         const float w = (hit ? 1.0f : 0.0f) * (float)(Pt * (double)al);
-        Ax = __builtin_fmaf(w, s_dep[idx], Ax);
+        Ax = __builtin_fmaf(w, blend_value(idx), Ax);
         Pt = hit ? Pt * (1.0 - (double)al) : Pt;
       };
       int k = k0;
@@ -521,7 +549,7 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       const double2 ab = s_ab[idx], co = s_co[idx];
       float G, og, al;
       double dx, dy;
-      if (ie & LIST_SEAM)                              // wave-uniform
+      if (SPH && (ie & LIST_SEAM))                     // wave-uniform
         al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
       else
         al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], ab, co, amax, G, og, dx, dy);
@@ -534,10 +562,21 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       const double dal = 1.0 - (double)ala, ral = recip_unit(dal);
       const double Tkd = div_unit(Te, dal, ral);
       const float Tk = (float)Tkd;
-      const float dep = s_dep[idx];
-      const float vf = Tk * ala * g0;
-      const float da = Tk * (dep - Se) * g0 + (float)div_unit(Tfin, dal, ral) * g1;
-      Se = __builtin_fmaf(ala, dep, om * Se);
+      float vf[NF], da;
+      if constexpr (SPH) {
+        // depth output T_k (depth_k - Sb) g_depth; opacity output 1 - T_final
+        const float dep = s_f[idx][0];
+        vf[0] = Tk * ala * g[0];
+        da = Tk * (dep - Se) * g[0] + (float)div_unit(Tfin, dal, ral) * g[1];
+        Se = __builtin_fmaf(ala, dep, om * Se);
+      } else {
+        const float wk = Tk * ala;
+        const float fg = blend_value(idx);
+#pragma unroll
+        for (int ch = 0; ch < NF; ch++) vf[ch] = wk * g[ch];
+        da = Tk * (fg - Se);
+        Se = __builtin_fmaf(ala, fg, om * Se);
+      }
       Te = Tkd;
       const bool geo = act & !(og > amax);    // alpha is the constant amax where clamped
       double vg[6];
@@ -556,8 +595,20 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       for (int q = 0; q < 8; q++) v8[q] = q < 6 ? vg[q] : 0.0;
       const double r = wave_sum8_transposed(v8);
       if (((lane & 7u) == 0u) & ((lane >> 3) < 6u)) atomicAdd(&s_ag[idx][lane >> 3], r);
-      const float rf = row_sum_to_last(vf);
-      if ((lane & 15u) == 15u) atomicAdd(&s_af[idx], rf);
+      if constexpr (NF >= 3) {
+        // transposed: channel q ends in lanes 8q..8q+7
+        float v8[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) v8[q] = q < NF ? vf[q < NF ? q : 0] : 0.0f;
+        const float rf = wave_sum8_transposed(v8);
+        if (((lane & 7u) == 0u) & ((lane >> 3) < (unsigned)NF)) atomicAdd(&s_af[idx][lane >> 3], rf);
+      } else {
+#pragma unroll
+        for (int q = 0; q < NF; q++) {
+          const float rf = row_sum_to_last(vf[q]);
+          if ((lane & 15u) == 15u) atomicAdd(&s_af[idx][q], rf);
+        }
+      }
     };
     {
       int k = k1 - 1;
@@ -581,9 +632,12 @@ __global__ __launch_bounds__(1024) void k_bwd_lidar(ViewTable vt, BwdArgs A, int
       if (lane < 6u) {
         const double x = s_ag[e][lane];
         if (x != 0.0) atomicAdd(dg + lane, x);
-      } else if (lane == 6u) {
-        const float x = s_af[e];
+      } else if (SPH && lane == 6u) {
+        const float x = s_af[e][0];
         if (x != 0.0f) atomicAdd(dg + 6, (double)x);
+      } else if (!SPH && lane >= 8u && (int)lane - 8 < NF && (int)lane - 8 < A.C) {
+        const float x = s_af[e][lane - 8];
+        if (x != 0.0f) atomicAdd(A.accf + (size_t)rid * A.C + (lane - 8), (double)x);
       }
     }
     __syncthreads();
@@ -1523,7 +1577,9 @@ int launch_bwd_cm(const ViewTable &vt, const BwdArgs &A, int kind, int tile_begi
         const int t0 = vt.v[v0].tile_off, t1 = v1 < vt.n ? vt.v[v1].tile_off : vt.total_tiles;
         if (t1 > t0) {
           if (pass == 0 && kind0 == SPLAT_CAM_SPHERICAL)
-            hipLaunchKernelGGL(k_bwd_lidar, dim3(t1 - t0), dim3(1024), 0, stream, vt, A, t0);
+            hipLaunchKernelGGL((k_bwd_split<1, true>), dim3(t1 - t0), dim3(1024), 0, stream, vt, A, t0);
+          else if (pass == 1 && kind0 != SPLAT_CAM_SPHERICAL && split_pinhole<CM>(t1 - t0))
+            hipLaunchKernelGGL((k_bwd_split<CM <= 4 ? CM : 4, false>), dim3(t1 - t0), dim3(1024), 0, side, vt, A, t0);
           else if (pass == 1 && kind0 != SPLAT_CAM_SPHERICAL)
             hipLaunchKernelGGL(k_bwd_alpha<CM>, dim3(t1 - t0), dim3(256), 0, side, vt, A, t0);
         }

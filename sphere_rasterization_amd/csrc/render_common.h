@@ -341,6 +341,18 @@ __device__ __forceinline__ float splat_alpha(const ViewDev &c, double pxr, doubl
 // at most 7.5 columns from that centre, so only for such an entry can the
 // other image be the nearer one for some pixel; every other entry takes
 // splat_alpha without the per-pixel wrap, which would leave it unchanged.
+// Pinhole launches of at most SPLIT_TILES_MAX tiles (no more than the chip's
+// 256 compute units) with up to four channels composite with the spherical
+// views' split walk (four waves per quadrant list, the parts chained per
+// pixel): at four waves per tile such a launch leaves most SIMDs idle. With
+// more tiles the split costs more than it gains: its workgroup of 1024 threads
+// fits once per CU, the parts composite their entries twice in the reverse pass,
+// and in the forward pass a part cannot know that its pixels stopped in an
+// earlier one (1024 tiles, 100k Gaussians at 512x512: forward 76 -> 273 us).
+constexpr int SPLIT_TILES_MAX = 256;
+template <int CM>
+inline bool split_pinhole(int ntiles) { return CM <= 4 && ntiles <= SPLIT_TILES_MAX; }
+
 constexpr int LIST_SEAM = 0x8000;
 __device__ __forceinline__ int seam_flag(const ViewDev &c, double tu) {
   return fabs(tu - 8.0) >= 0.5 * (double)c.W - 8.0 ? LIST_SEAM : 0;

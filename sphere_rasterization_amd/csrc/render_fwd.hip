@@ -412,25 +412,30 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A, int 
 // non-increasing along a part, so no entry of it can have stopped the pixel).
 // Otherwise the stop lies inside part j, and its wave walks that part again
 // from the chained T and S with the ordinary per-entry stop.
+// SPH = false: the same walk for pinhole views with up to four channels, for
+// launches with few tiles (their four waves per tile left most SIMDs idle or
+// waiting for the last tiles).
 // ---------------------------------------------------------------------------
 constexpr int LB = 1024;                 // threads and staged entries per batch
 
-__global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int tile_begin) {
+template <int CM, bool SPH>
+__global__ __launch_bounds__(LB) void k_fwd_split(ViewTable vt, FwdArgs A, int tile_begin) {
+  constexpr int NF = SPH ? 1 : CM;       // composited values: range, or the features
   __shared__ double2 s_uv[LB];           // tile-relative centre
   __shared__ double2 s_ab[LB];           // a/2, b
   __shared__ double2 s_co[LB];           // c/2, opacity
-  __shared__ float s_dep[LB];            // range
+  __shared__ float s_f[NF][LB];          // range or features
   __shared__ uint16_t s_idx[4][LB];      // per-quadrant lists of the batch
   __shared__ int s_woff[16][4];          // per wave: first slot of its entries in each list
   __shared__ int s_cnt[4];
-  __shared__ float s_pS[4][256];         // per part and pixel: partial colour,
+  __shared__ float s_pS[4][NF][256];     // per part and pixel: partial colour,
   __shared__ double s_pT[4][256];        //   transmittance,
   __shared__ uint32_t s_pL[4][256];      //   last composited entry (0: none)
   if (*A.overflow) return;
   const int gtile = tile_begin + (int)blockIdx.x;
   const int view = view_of_tile(vt, gtile);
   const ViewDev &c = vt.v[view];
-  if (c.kind != SPLAT_CAM_SPHERICAL) return;
+  if ((c.kind == SPLAT_CAM_SPHERICAL) != SPH) return;
   const unsigned tid = threadIdx.x, pix = tid & 255u;
   const int part = __builtin_amdgcn_readfirstlane((int)(tid >> 8));           // 0..3
   const int wq = __builtin_amdgcn_readfirstlane((int)((tid >> 6) & 3u));     // quadrant
@@ -439,12 +444,15 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
   const uint32_t start = A.ranges[2 * gtile], end = A.ranges[2 * gtile + 1];
   // running state of this thread's pixel (the same in all four copies)
   double T = 1.0;
-  float S = 0.0f;
+  float S[NF];
+#pragma unroll
+  for (int ch = 0; ch < NF; ch++) S[ch] = 0.0f;
   uint32_t last = 0;
   bool active = tp.inside;
   const float amin = A.alpha_min, amax = A.alpha_max;
   const double tmin = (double)A.T_min;
   const double pxr = tp.pxr, pyr = tp.pyr;
+  const long long vbase = (long long)view * A.n;
 
   for (uint32_t b = start; b < end; b += LB) {
     const uint32_t e = b + tid;
@@ -453,13 +461,19 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
     if (e < end) {
       const uint32_t rid = A.vals[e];
       const DrawRec d = A.draw[rid];
-      const double2 uv = stage_uv(c, tp, d, true);
+      const double2 uv = stage_uv(c, tp, d, SPH);
       s_uv[tid] = uv;
-      seam = seam_flag(c, uv.x);
+      if constexpr (SPH) seam = seam_flag(c, uv.x);
       const Conic cn = stage_conic(d);
       s_ab[tid] = cn.ab;
       s_co[tid] = cn.co;
-      s_dep[tid] = A.aux[rid].z;
+      if constexpr (SPH) {
+        s_f[0][tid] = A.aux[rid].z;
+      } else {
+        const long long id = (long long)rid - vbase;
+#pragma unroll
+        for (int ch = 0; ch < NF; ch++) s_f[ch][tid] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      }
       mask = quadrant_mask(tp, d);
     }
     // per-quadrant lists, in batch order
@@ -489,17 +503,18 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
     // this wave's part of its quadrant's list (entries: staged index | LIST_SEAM)
     const int L = __builtin_amdgcn_readfirstlane(s_cnt[wq]);
     const int k0 = (L * part) / 4, k1 = (L * (part + 1)) / 4;
-    auto one = [&](int ie, double &Tx, float &Sx, uint32_t &lx, bool &ax) {
+    auto one = [&](int ie, double &Tx, float (&Sx)[NF], uint32_t &lx, bool &ax) {
       const int idx = ie & (LIST_SEAM - 1);
       float G, og, al;
       double dx, dy;
-      if (ie & LIST_SEAM)                              // wave-uniform
+      if (SPH && (ie & LIST_SEAM))                     // wave-uniform
         al = splat_alpha<true>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
       else
         al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
       const bool hit = ax & (al >= amin);
       const float w = (hit ? 1.0f : 0.0f) * (float)(Tx * (double)al);
-      Sx = __builtin_fmaf(w, s_dep[idx], Sx);
+#pragma unroll
+      for (int ch = 0; ch < NF; ch++) Sx[ch] = __builtin_fmaf(w, s_f[ch][idx], Sx[ch]);
       Tx = hit ? Tx * (1.0 - (double)al) : Tx;
       lx = hit ? b - start + (uint32_t)idx + 1u : lx;
       ax = ax & !(Tx < tmin);
@@ -507,7 +522,7 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
     // the wave's walk over list positions [k0, k1): single entries up to a
     // multiple of four, then four indices per LDS read (their records are
     // read ahead of the dependent arithmetic), until no lane is left
-    auto walk = [&](double &Tx, float &Sx, uint32_t &lx, bool &ax) {
+    auto walk = [&](double &Tx, float (&Sx)[NF], uint32_t &lx, bool &ax) {
       int k = k0;
       for (; k < k1 && (k & 3); k++) one(__builtin_amdgcn_readfirstlane((int)s_idx[wq][k]), Tx, Sx, lx, ax);
       for (; k + 4 <= k1; k += 4) {
@@ -525,11 +540,14 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
     // 1. the part from T = 1 (a local stop below T_min ends it: the chained T is smaller)
     {
       double Tj = 1.0;
-      float Sj = 0.0f;
+      float Sj[NF];
+#pragma unroll
+      for (int ch = 0; ch < NF; ch++) Sj[ch] = 0.0f;
       uint32_t lj = 0;
       bool aj = active;
       walk(Tj, Sj, lj, aj);
-      s_pS[part][pix] = Sj;
+#pragma unroll
+      for (int ch = 0; ch < NF; ch++) s_pS[part][ch][pix] = Sj[ch];
       s_pT[part][pix] = Tj;
       s_pL[part][pix] = lj;
     }
@@ -542,7 +560,8 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
         if (stop_part < 0) {
           const double Tj = s_pT[j][pix];
           if (T * Tj >= tmin) {
-            S = __builtin_fmaf((float)T, s_pS[j][pix], S);
+#pragma unroll
+            for (int ch = 0; ch < NF; ch++) S[ch] = __builtin_fmaf((float)T, s_pS[j][ch][pix], S[ch]);
             const uint32_t lj = s_pL[j][pix];
             last = lj ? lj : last;
             T *= Tj;
@@ -557,18 +576,22 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
     if (ballot64(stop_part == part)) {
       bool ax = stop_part == part;
       double Tx = T;
-      float Sx = S;
+      float Sx[NF];
+#pragma unroll
+      for (int ch = 0; ch < NF; ch++) Sx[ch] = S[ch];
       uint32_t lx = last;
       walk(Tx, Sx, lx, ax);
       if (stop_part == part) {
-        s_pS[0][pix] = Sx;
+#pragma unroll
+        for (int ch = 0; ch < NF; ch++) s_pS[0][ch][pix] = Sx[ch];
         s_pT[0][pix] = Tx;
         s_pL[0][pix] = lx;
       }
     }
     __syncthreads();
     if (stop_part >= 0) {                          // stopped in this batch: final state
-      S = s_pS[0][pix];
+#pragma unroll
+      for (int ch = 0; ch < NF; ch++) S[ch] = s_pS[0][ch][pix];
       T = s_pT[0][pix];
       last = s_pL[0][pix];
       active = false;
@@ -579,8 +602,14 @@ __global__ __launch_bounds__(LB) void k_fwd_lidar(ViewTable vt, FwdArgs A, int t
   const long long p = c.pix_off + (long long)tp.j * c.W + tp.i;
   const size_t plane = (size_t)c.W * c.H;
   float *img = A.img + c.img_off + (size_t)tp.j * c.W + tp.i;
-  img[0] = S;
-  img[plane] = (float)(1.0 - T);
+  if constexpr (SPH) {
+    img[0] = S[0];
+    img[plane] = (float)(1.0 - T);
+  } else {
+#pragma unroll
+    for (int ch = 0; ch < NF; ch++)
+      if (ch < A.C) img[ch * plane] = S[ch];
+  }
   if (A.T_final) A.T_final[p] = (float)T;
   if (A.last) A.last[p] = last;
 }
@@ -621,7 +650,9 @@ int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t s
         const int t0 = vt.v[v0].tile_off, t1 = v1 < vt.n ? vt.v[v1].tile_off : vt.total_tiles;
         if (t1 > t0) {
           if (pass == 0 && kind0 == SPLAT_CAM_SPHERICAL)
-            hipLaunchKernelGGL(k_fwd_lidar, dim3(t1 - t0), dim3(LB), 0, stream, vt, A, t0);
+            hipLaunchKernelGGL((k_fwd_split<1, true>), dim3(t1 - t0), dim3(LB), 0, stream, vt, A, t0);
+          else if (pass == 1 && kind0 != SPLAT_CAM_SPHERICAL && split_pinhole<CM>(t1 - t0))
+            hipLaunchKernelGGL((k_fwd_split<CM <= 4 ? CM : 4, false>), dim3(t1 - t0), dim3(LB), 0, side, vt, A, t0);
           else if (pass == 1 && kind0 != SPLAT_CAM_SPHERICAL)
             hipLaunchKernelGGL(k_fwd_alpha<CM>, dim3(t1 - t0), block, 0, side, vt, A, t0);
         }

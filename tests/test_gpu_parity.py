@@ -112,6 +112,21 @@ def test_sphere_channel_counts():
         _run(sc, 40 + ch, f"spheres 40k @200x150, {ch} channels")
 
 
+def test_gauss_channel_counts_few_tiles():
+    """3D Gaussians with one, two and four feature channels on an image of 160
+    tiles, where the camera compositors take the split walk (four waves per
+    quadrant list, parts chained per pixel; below the chip's compute-unit count),
+    and with five channels, which stays on the one-wave-per-quadrant kernels;
+    each against the oracle, forward and reverse pass."""
+    base = S.gauss3d(seed=44, n=20_000, width=256, height=160)
+    rng = np.random.default_rng(45)
+    for ch in (1, 2, 4, 5):
+        feat = np.ascontiguousarray(rng.uniform(0.0, 1.0, size=(base.n, ch)).astype(np.float32))
+        sc = S.Scene(S.PRIM_GAUSS3D, base.n, ch, base.pos, base.scale, base.opacity, feat, rot=base.rot,
+                     cams=base.cams, params=base.params)
+        _run(sc, 50 + ch, f"gauss3d 20k @256x160, {ch} channels")
+
+
 def test_orthographic_spheres():
     # parallel projection: 300k spheres on 600x450 (ragged tiles), intrinsics gradients included
     _run(S.ortho_spheres(), 9, "spheres 300k @600x450 orthographic")
