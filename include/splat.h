@@ -150,7 +150,7 @@ typedef struct {
  * contribution is divided by its projected area in pixels, pi (fx r_eff / qz)
  * (fy r_eff / qz) (orthographic: pi (fx r_eff)(fy r_eff)), and by 1e-3. cam_K
  * stays the raw sum. normalize = 1 with Gaussians returns SPLAT_ERR_UNSUPPORTED.
- * sums_cleared = 1 (spheres only, otherwise ignored): the caller states that the
+ * sums_cleared = 1: the caller states that the
  * splat_render_fwd call before this one on the stream was given this call's workspace
  * (so it cleared the sums the reverse pass accumulates into) and that no
  * splat_render_bwd has used the workspace since; the call then skips that clearing.
@@ -234,13 +234,14 @@ int splat_bin_sort_noalloc(const splat_camera *cams, int n_views, int n, const v
  *     splat_bin_sort (-1 padded); vals[index] - view*n is the primitive id. Together they
  *     are the backward buffer of Pulsar B.1.4. Sphere outputs need capacity < 2^31.
  *     T_final/last may be NULL for spheres, norm/topk for Gaussians.
- * bwd_workspace (optional, spheres; NULL, and ignored for Gaussians): the workspace of the
- *   splat_render_bwd call that follows on this stream, bwd_ws_bytes >=
- *   splat_bwd_workspace_bytes, 16-byte aligned. The forward then also clears the sums the
- *   reverse pass accumulates into, in workgroups appended to its grid that run while its
- *   longest tiles finish; that call can then pass splat_grads.sums_cleared = 1 and skip
- *   its own clearing. Errors: SPLAT_ERR_CAPACITY (too small), SPLAT_ERR_INVALID_ARG
- *   (misaligned). */
+ * bwd_workspace (optional, may be NULL): the workspace of the splat_render_bwd call that
+ *   follows on this stream, bwd_ws_bytes >= splat_bwd_workspace_bytes, 16-byte aligned.
+ *   The forward then also clears the sums the reverse pass accumulates into (spheres: in
+ *   workgroups appended to its grid that run while its longest tiles finish; Gaussians:
+ *   in a launch after the pinhole views' kernel, which runs beside the spherical views'
+ *   longest tiles when the call has both); that call can then pass
+ *   splat_grads.sums_cleared = 1 and skip its own clearing. Errors: SPLAT_ERR_CAPACITY
+ *   (too small), SPLAT_ERR_INVALID_ARG (misaligned). */
 int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *prims,
                      const splat_params *prm, const void *proj, const uint32_t *vals,
                      const uint32_t *tile_ranges, const int32_t *overflow, float *img,

@@ -366,11 +366,24 @@ int splat_render_fwd(const splat_camera *cams, int n_views, const splat_prims *p
   ProjLayout L = proj_layout(const_cast<void *>(proj), (long long)n_views * prims->n);
   A.draw = L.draw; A.aux = L.aux; A.vals = vals; A.ranges = tile_ranges; A.overflow = overflow;
   A.feat = prims->feat; A.img = img; A.T_final = T_final; A.last = last; A.norm = norm; A.topk = topk;
-  if (bwd_workspace && prims->kind == SPLAT_PRIM_SPHERE) {
+  if (bwd_workspace) {
     const long long nrec = (long long)n_views * prims->n;
     CHECK(((uintptr_t)bwd_workspace & 15u) == 0, SPLAT_ERR_INVALID_ARG, "backward workspace not 16-byte aligned");
     CHECK(bwd_ws_bytes >= bwd_workspace_bytes(nrec, prims->channels), SPLAT_ERR_CAPACITY,
           "backward workspace smaller than splat_bwd_workspace_bytes");
+  }
+  if (bwd_workspace && prims->kind != SPLAT_PRIM_SPHERE) {
+    // Gaussians: the fp64 geometric and feature sums of every record (each region
+    // starts on an aligned boundary and is padded past its end)
+    const long long nrec = (long long)n_views * prims->n;
+    const AccLayout acc = acc_layout(bwd_workspace, nrec, prims->channels);
+    A.clr[0] = reinterpret_cast<uint4 *>(acc.g);
+    A.nclr[0] = (nrec * ACC_G * (long long)sizeof(double) + 15) / 16;
+    A.clr[1] = reinterpret_cast<uint4 *>(acc.f);
+    A.nclr[1] = (nrec * prims->channels * (long long)sizeof(double) + 15) / 16;
+    A.clear = 1;
+  } else if (bwd_workspace) {
+    const long long nrec = (long long)n_views * prims->n;
     const AccLayout acc = acc_layout(bwd_workspace, nrec, prims->channels);
     A.clr[0] = reinterpret_cast<uint4 *>(acc.g);        // fp32 rows of 5 + C values (16-byte multiples)
     A.nclr[0] = nrec * sph_row_stride(prims->channels) * (long long)sizeof(float) / 16;

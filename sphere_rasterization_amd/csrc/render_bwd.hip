@@ -1602,7 +1602,7 @@ int launch_render_bwd(const ViewTable &vt, int vbeg, int vend, BwdArgs A, const 
   const bool sph = pr->kind == SPLAT_PRIM_SPHERE;
   const long long r0 = (long long)vbeg * A.n, r1 = (long long)vend * A.n;
   ZeroRanges z{};
-  if (sph && gr->sums_cleared) {
+  if (gr->sums_cleared) {
     // the forward before this call cleared every sum of the workspace
   } else if (sph) {
     // fp32 rows of a multiple of four floats: cleared as doubles

@@ -9,6 +9,7 @@
 // Workgroups appended to the sphere forward's grid to clear the reverse pass's
 // sums (when the caller hands over the reverse pass's workspace).
 constexpr int FWD_CLEAR_BLOCKS = 256;
+constexpr int FWD_CLEAR_GRID = 8192;     // workgroups of the Gaussians' clearing launch
 
 struct FwdArgs {
   int n, C, top_k;
@@ -28,8 +29,8 @@ struct FwdArgs {
   float *norm;
   int32_t *topk;
   float bg[SPLAT_MAX_CHANNELS];
-  // spheres, optional: the reverse pass's sums to clear (16-byte units; clear:
-  // FWD_CLEAR_BLOCKS workgroups after the tiles' do it)
+  // optional: the reverse pass's sums to clear (16-byte units; spheres: the
+  // FWD_CLEAR_BLOCKS workgroups after the tiles' do it, Gaussians: k_fwd_clear)
   int clear;
   uint4 *clr[3];
   long long nclr[3];

@@ -614,6 +614,18 @@ __global__ __launch_bounds__(LB) void k_fwd_split(ViewTable vt, FwdArgs A, int t
   if (A.last) A.last[p] = last;
 }
 
+// Gaussians given the reverse workspace: the reverse pass's sums cleared with
+// 16-byte stores, in a launch on the camera views' stream after their kernel.
+// With a spherical view in the call it runs beside the lidar tiles, whose
+// longest lists keep the caller's stream busy after the camera views are done.
+__global__ __launch_bounds__(256) void k_fwd_clear(FwdArgs A) {
+  const long long nthr = (long long)gridDim.x * blockDim.x;
+  const long long t0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+#pragma unroll
+  for (int r = 0; r < 3; r++)
+    for (long long k = t0; k < A.nclr[r]; k += nthr) A.clr[r][k] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 template <int CM>
 int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t stream) {
   dim3 grid(vt.total_tiles), block(256);
@@ -659,6 +671,7 @@ int launch_fwd_cm(const ViewTable &vt, const FwdArgs &A, int kind, hipStream_t s
         v0 = v1;
       }
     }
+    if (A.clear) hipLaunchKernelGGL(k_fwd_clear, dim3(FWD_CLEAR_GRID), dim3(256), 0, has_pin ? side : stream, A);
     if (fork) {
       const int rc = side_end(stream, side);
       if (rc != SPLAT_OK) return rc;

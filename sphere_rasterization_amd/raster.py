@@ -87,7 +87,7 @@ class Rasterizer:
         self.norm = torch.empty(self.total_pix, dtype=torch.float32, device=dev) if sph else None
         self.topk = torch.empty(self.total_pix * K, dtype=torch.int32, device=dev) if sph else None
         self.bwd_ws = None
-        self.sums_cleared = False   # the last forward cleared the backward's sums (spheres)
+        self.sums_cleared = False   # the last forward cleared the backward's sums
         self.capacity = 0
         self._alloc_pairs(capacity if capacity is not None else max(1024, 4 * V * n))
 
@@ -124,9 +124,9 @@ class Rasterizer:
                          _ptr(self.overflow), _ptr(self.sort_ws), self.sort_ws_bytes, _stream())
 
     def render_fwd(self):
-        # spheres: once a backward has allocated its workspace, the forward clears the
-        # sums the next backward accumulates into (the library skips its own clearing)
-        ws = self.bwd_ws if self.kind == 2 else None
+        # once a backward has allocated its workspace, the forward clears the sums
+        # the next backward accumulates into (the library skips its own clearing)
+        ws = self.bwd_ws
         L.splat_render_fwd(self.c_cams, self.V, self.c_prims, self.c_params, _ptr(self.proj), _ptr(self.vals),
                            _ptr(self.tile_ranges), _ptr(self.overflow), _ptr(self.img), _ptr(self.T_final),
                            _ptr(self.last), _ptr(self.norm), _ptr(self.topk), _ptr(ws),
