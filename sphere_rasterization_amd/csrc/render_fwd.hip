@@ -303,10 +303,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CM <= 4 ? (
 template <int CM>
 __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A, int tile_begin) {
   constexpr int NF = CM;
+  // features [entry][channel], read as 16-byte pieces (one read per four
+  // channels); from eight channels on the row stride has four floats more, so
+  // that the staging writes of neighbouring entries spread over the banks
+  constexpr int NF4 = (NF + 3) / 4;
+  constexpr int FS = 4 * NF4 + (NF >= 8 ? 4 : 0);
   __shared__ double2 s_uv[256];     // tile-relative centre
   __shared__ double2 s_ab[256];     // a/2, b
   __shared__ double2 s_co[256];     // c/2, opacity
-  __shared__ float s_f[NF][256];    // features, or depth for spherical views
+  __shared__ __align__(16) float s_f[256][FS];
   __shared__ QuadLists s_l;
   if (*A.overflow) return;
   const int gtile = tile_begin + (int)blockIdx.x;
@@ -341,7 +346,15 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A, int 
       s_co[threadIdx.x] = cn.co;
       const long long id = (long long)rid - vbase;
 #pragma unroll
-      for (int ch = 0; ch < CM; ch++) s_f[ch][threadIdx.x] = ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+      for (int q = 0; q < NF4; q++) {
+        float f[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const int ch = 4 * q + k;
+          f[k] = ch < NF && ch < A.C ? A.feat[(size_t)id * A.C + ch] : 0.0f;
+        }
+        *reinterpret_cast<float4 *>(&s_f[threadIdx.x][4 * q]) = make_float4(f[0], f[1], f[2], f[3]);
+      }
       mask = quadrant_mask(tp, d);
     }
     build_quad_lists(s_l, mask);
@@ -356,7 +369,13 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A, int 
       const bool hit = active & (al >= amin);
       const float w = (hit ? 1.0f : 0.0f) * (float)(T * (double)al);
 #pragma unroll
-      for (int ch = 0; ch < NF; ch++) S[ch] = __builtin_fmaf(w, s_f[ch][idx], S[ch]);
+      for (int q = 0; q < NF4; q++) {
+        const float4 f = *reinterpret_cast<const float4 *>(&s_f[idx][4 * q]);
+        const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          if (4 * q + k < NF) S[4 * q + k] = __builtin_fmaf(w, fv[k], S[4 * q + k]);
+      }
       T = hit ? T * (1.0 - (double)al) : T;
       last = hit ? b - start + (uint32_t)idx + 1u : last;
       active = active & !(T < tmin);            // include, then stop
