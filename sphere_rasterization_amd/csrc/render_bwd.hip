@@ -144,6 +144,19 @@ __global__ __launch_bounds__(256) void k_zero(ZeroRanges z) {
 }
 
 
+// Four fp32 values per lane summed over the wave, transposed: value q ends in
+// every lane of 16-lane row q. The lane swaps pair v_q with v_(q+2) across the
+// halves, then the results across rows; four DPP adds sum each row.
+__device__ __forceinline__ float wave_sum4_transposed(const float (&v)[4]) {
+  const float a0 = swap_add32(v[0], v[2]), a1 = swap_add32(v[1], v[3]);   // value (lane bit 5) * 2 + 0 or 1
+  float e = swap_add16(a0, a1);                                          // value = lane >> 4
+  e += dpp_f32<0xB1>(e);                                                 // lane ^ 1
+  e += dpp_f32<0x4E>(e);                                                 // lane ^ 2
+  e += dpp_f32<0x141>(e);                                                // 8-lane mirror
+  e += dpp_f32<0x140>(e);                                                // 16-lane mirror
+  return e;
+}
+
 // ---------------------------------------------------------------------------
 // Alpha blending backward: replay each pixel's list back to front from `last`,
 // recovering T before entry k as T_after / (1 - alpha_k) (fp64).
@@ -283,7 +296,14 @@ __global__ __launch_bounds__(256) void k_bwd_alpha(ViewTable vt, BwdArgs A, int 
         const double r = wave_sum8_transposed(v8);
         if (((lane & 7u) == 0u) & ((lane >> 3) < 6u)) atomicAdd(&s_ag[idx][lane >> 3], r);
       }
-      if constexpr (NF >= 3) {
+      if constexpr (NF >= 3 && NF <= 4) {
+        // wave totals, transposed: channel q ends in the lanes of row q
+        float v4[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) v4[q] = q < NF ? vf[q < NF ? q : 0] : 0.0f;
+        const float x = wave_sum4_transposed(v4);
+        if (((lane & 15u) == 0u) & ((lane >> 4) < (unsigned)NF)) atomicAdd(&s_af[idx][lane >> 4], x);
+      } else if constexpr (NF >= 3) {
         // wave totals, transposed: group gq's channel 8 gq + q ends in the lanes
         // 8q..8q+7, and lane 8q + j adds that of group j
         float tot[NG];
@@ -596,12 +616,12 @@ __global__ __launch_bounds__(1024) void k_bwd_split(ViewTable vt, BwdArgs A, int
       const double r = wave_sum8_transposed(v8);
       if (((lane & 7u) == 0u) & ((lane >> 3) < 6u)) atomicAdd(&s_ag[idx][lane >> 3], r);
       if constexpr (NF >= 3) {
-        // transposed: channel q ends in lanes 8q..8q+7
-        float v8[8];
+        // transposed: channel q ends in the lanes of row q
+        float v4[4];
 #pragma unroll
-        for (int q = 0; q < 8; q++) v8[q] = q < NF ? vf[q < NF ? q : 0] : 0.0f;
-        const float rf = wave_sum8_transposed(v8);
-        if (((lane & 7u) == 0u) & ((lane >> 3) < (unsigned)NF)) atomicAdd(&s_af[idx][lane >> 3], rf);
+        for (int q = 0; q < 4; q++) v4[q] = q < NF ? vf[q < NF ? q : 0] : 0.0f;
+        const float rf = wave_sum4_transposed(v4);
+        if (((lane & 15u) == 0u) & ((lane >> 4) < (unsigned)NF)) atomicAdd(&s_af[idx][lane >> 4], rf);
       } else {
 #pragma unroll
         for (int q = 0; q < NF; q++) {
