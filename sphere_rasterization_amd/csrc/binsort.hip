@@ -30,7 +30,8 @@
 //   k_seg_sort                    segments up to SEG_WAVE pairs: one wave each,
 //                                 a bitonic network in registers (lane shuffles
 //                                 for the low merge levels, layouts moved through
-//                                 LDS for the top two); then
+//                                 LDS for the top two); up to SEG_MED pairs: one
+//                                 wave each, merge rounds in its LDS region; then
 //                                 longer segments from a work queue, one
 //                                 workgroup each: merge sort in LDS up to NV
 //                                 pairs, an MSD split into LDS-sized buckets
@@ -49,6 +50,7 @@ constexpr int TH_THREADS = 1024;    // workgroup of the counting passes
 constexpr int TH_RPT = 4;           // records per thread in the counting passes
 constexpr int TH_CHUNK = TH_THREADS * TH_RPT;
 constexpr int SEG_WAVE = 512;       // segments up to this length: one wave sorts them
+constexpr int SEG_MED = 1024;       // up to this length: one wave merge-sorts them in LDS
 constexpr int TILE_SCAN1_MAX = 1 << 16;   // tiles scanned by a single workgroup
 constexpr int LDS_TILES = 16384;    // tiles of one view held as LDS counters (64 KiB)
 constexpr int LT = 512;             // threads of the long-segment sort
@@ -174,7 +176,7 @@ __device__ __forceinline__ void list_append(uint32_t *list, uint32_t *count, boo
 
 // Per tile: [start, end) (0, 0 when empty) and the bucket cursor (in place of the count).
 // Without overflow every prefix is below the capacity (< 2^32).
-// Tiles with more than SEG_WAVE pairs also go on the work lists of the
+// Tiles with more than SEG_MED pairs also go on the work lists of the
 // long-segment sort (unordered here): list[0..) those above NV, list[m..) the rest.
 __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_ranges(uint32_t *cnt_cursor, long long m,
                                                              const unsigned long long *block_sums,
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_ranges(uint32_t *cnt_cursor
     ranges[2 * t + 1] = c ? start + c : 0u;
   }
   list_append(list, &live[1], c > (uint32_t)NV, (uint32_t)t);
-  list_append(list + m, &live[2], c > (uint32_t)SEG_WAVE && c <= (uint32_t)NV, (uint32_t)t);
+  list_append(list + m, &live[2], c > (uint32_t)SEG_MED && c <= (uint32_t)NV, (uint32_t)t);
 }
 
 // Single workgroup, up to TILE_SCAN1_MAX tiles: pair total, overflow flag and
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void k_tile_ranges(uint32_t *cnt_cursor
 // two phases. The same scan (three
 // fields packed in one 64-bit value) lists the tiles for the long-segment sort:
 // list[0..) those with more than NV pairs in tile order, list[m..) those with
-// SEG_WAVE < pairs <= NV; live[1], live[2] count them, live[3] = 0 is the queue
+// SEG_MED < pairs <= NV; live[1], live[2] count them, live[3] = 0 is the queue
 // head.
 constexpr int TS_THREADS = 1024;
 constexpr int TS_ITEMS = 4;
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(TS_THREADS) void k_tile_scan1(uint32_t *cnt_start, 
     for (int r = 0; r < TS_ITEMS; r++) {
       sum += x[r];
       nh += x[r] > (uint32_t)NV ? 1u : 0u;
-      nm += ((x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
+      nm += ((x[r] > (uint32_t)SEG_MED) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
     }
     const unsigned long long packed =
         (unsigned long long)sum | ((unsigned long long)nh << 32) | ((unsigned long long)nm << 48);
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(TS_THREADS) void k_tile_scan1(uint32_t *cnt_start, 
         ranges[2 * (t0 + r) + 1] = x[r] ? run + x[r] : 0u;
         if (x[r] > (uint32_t)NV)
           list[ph++] = (uint32_t)(t0 + r);
-        else if (x[r] > (uint32_t)SEG_WAVE)
+        else if (x[r] > (uint32_t)SEG_MED)
           list[m + pm++] = (uint32_t)(t0 + r);
       }
       run += x[r];
@@ -590,7 +592,7 @@ __device__ bool fused_tile_scan(const uint32_t *cnt, int T, const uint32_t *row,
     part += x[r];
     sum += x[r];
     nh += x[r] > (uint32_t)NV ? 1u : 0u;
-    nm += ((x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
+    nm += ((x[r] > (uint32_t)SEG_MED) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
   }
   unsigned long long total;
   block_exclusive_scan<unsigned long long, TH_THREADS>(part, &total);
@@ -619,11 +621,11 @@ __device__ bool fused_tile_scan(const uint32_t *cnt, int T, const uint32_t *row,
         so.ranges[2 * t + 1] = x[r] ? run + x[r] : 0u;
         if (x[r] > (uint32_t)NV)
           so.list[ph] = (uint32_t)t;
-        else if (x[r] > (uint32_t)SEG_WAVE)
+        else if (x[r] > (uint32_t)SEG_MED)
           so.list[T + pm] = (uint32_t)t;
       }
       ph += x[r] > (uint32_t)NV ? 1u : 0u;
-      pm += ((x[r] > (uint32_t)SEG_WAVE) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
+      pm += ((x[r] > (uint32_t)SEG_MED) & (x[r] <= (uint32_t)NV)) ? 1u : 0u;
     }
     run += x[r];
   }
@@ -941,6 +943,7 @@ __device__ __forceinline__ void sort_regs(uint64_t (&e)[LE]) {
 // along the cross diagonal (merge path); ties go to the first run, and the
 // only equal words are the pad words, so every thread's split agrees with its
 // neighbours'. An exhausted run reads as all-ones (above the pad).
+template <int CAP = NV>
 __device__ __forceinline__ void merge_round(const uint64_t *s, int R, int npad, int o, uint64_t (&e)[LE]) {
   const int a0 = o & ~(2 * R - 1), b0 = a0 + R;
   const int alen = min(R, npad - a0), blen = max(0, min(R, npad - b0));
@@ -955,7 +958,7 @@ __device__ __forceinline__ void merge_round(const uint64_t *s, int R, int npad, 
   }
   int ia = a0 + lo, ib = b0 + diag - lo;
   const int ea = a0 + alen, eb = b0 + blen;
-  uint64_t a = s[lslot(min(ia, NV - 1))], b = s[lslot(min(ib, NV - 1))];
+  uint64_t a = s[lslot(min(ia, CAP - 1))], b = s[lslot(min(ib, CAP - 1))];
   a = ia < ea ? a : ~0ull;
   b = ib < eb ? b : ~0ull;
 #pragma unroll
@@ -967,7 +970,7 @@ __device__ __forceinline__ void merge_round(const uint64_t *s, int R, int npad, 
     ib += ta ? 0 : 1;
     const int nx = ta ? ia : ib;
     const bool ok = nx < (ta ? ea : eb);
-    uint64_t x = s[lslot(min(nx, NV - 1))];
+    uint64_t x = s[lslot(min(nx, CAP - 1))];
     x = ok ? x : ~0ull;
     a = ta ? x : a;
     b = ta ? b : x;
@@ -1022,6 +1025,57 @@ __device__ void lds_sort(const uint64_t *src, int len, uint64_t *kout, uint32_t 
     kout[i] = ((uint64_t)tile << 32) | (w >> 32);
     vout[i] = (uint32_t)w;
   }
+}
+
+// Segments of SEG_WAVE < len <= SEG_MED words: one wave, LE words per lane, the
+// register sort and merge rounds of lds_sort inside the wave's own LDS region
+// (WS_REGION words), with no workgroup barrier: LDS operations of one wave
+// complete in order. Eight such segments are sorted at once per workgroup,
+// where the work queue would give each its own workgroup of LT threads.
+constexpr int WS_REGION = SEG_MED + SEG_MED / LE;
+
+__device__ __forceinline__ void wave_merge_sort_tile(const uint32_t *ranges, const uint64_t *words, uint64_t *keys,
+                                                     uint32_t *vals, int t, uint64_t *sw) {
+  const uint32_t start = ranges[2 * t];
+  const int len = (int)(ranges[2 * t + 1] - start);
+  const int lane = (int)lane_id();
+  const int npad = (len + LE - 1) & ~(LE - 1);
+  uint64_t e[LE];
+#pragma unroll
+  for (int r = 0; r < LE; r++) {
+    const int i = r * WAVE + lane;
+    e[r] = i < len ? words[start + i] : SORT_PAD;
+  }
+#pragma unroll
+  for (int r = 0; r < LE; r++) {
+    const int i = r * WAVE + lane;
+    if (i < npad) sw[lslot(i)] = e[r];
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int o = lane * LE;
+  const bool act = o < npad;
+  if (act) {
+#pragma unroll
+    for (int k = 0; k < LE; k++) e[k] = sw[lane * (LE + 1) + k];
+    sort_regs(e);
+  }
+  for (int R = LE; R < npad; R <<= 1) {
+    __builtin_amdgcn_wave_barrier();
+    if (act) {
+#pragma unroll
+      for (int k = 0; k < LE; k++) sw[lane * (LE + 1) + k] = e[k];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (act) merge_round<SEG_MED>(sw, R, npad, o, e);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (act) {
+#pragma unroll
+    for (int k = 0; k < LE; k++) sw[lane * (LE + 1) + k] = e[k];
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < len; i += WAVE) write_pair(keys, vals, start + (uint32_t)i, (uint32_t)t, sw[lslot(i)]);
+  __builtin_amdgcn_wave_barrier();
 }
 
 struct SplitLds {
@@ -1122,7 +1176,7 @@ __device__ void msd_split(const uint64_t *src, uint64_t *dst, int len, uint32_t 
 }
 
 // Every segment sorted on its own. First each wave sorts the short segments
-// (at most SEG_WAVE pairs) of its share of the tiles; then the workgroups take
+// (at most SEG_MED pairs) of its share of the tiles; then the workgroups take
 // the longer segments one per workgroup from a work queue (the tiles above NV
 // first). Up to NV pairs: lds_sort straight from the bucketed words. Beyond: MSD split into the key array (used as scratch), then every run
 // of adjacent buckets that fits NV words is sorted as one segment; a bucket
@@ -1136,11 +1190,17 @@ __global__ __launch_bounds__(LT) void k_seg_sort(const uint32_t *ranges, uint64_
   __shared__ SplitLds sl;
   if (*overflow) return;
   {
-    static_assert((LT / WAVE) * WS_LDS <= NV_PHYS, "wave-sort LDS regions exceed the sort buffer");
+    static_assert(WS_LDS <= WS_REGION && (LT / WAVE) * WS_REGION <= NV_PHYS,
+                  "wave-sort LDS regions exceed the sort buffer");
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
-    uint64_t *sw = s + wave * WS_LDS;
-    for (int t = (int)blockIdx.x * (LT / WAVE) + wave; t < tiles; t += (int)gridDim.x * (LT / WAVE))
-      wave_sort_tile(ranges, words, keys, vals, t, sw);
+    uint64_t *sw = s + wave * WS_REGION;
+    for (int t = (int)blockIdx.x * (LT / WAVE) + wave; t < tiles; t += (int)gridDim.x * (LT / WAVE)) {
+      const uint32_t len = ranges[2 * t + 1] - ranges[2 * t];
+      if (len > (uint32_t)SEG_WAVE && len <= (uint32_t)SEG_MED)
+        wave_merge_sort_tile(ranges, words, keys, vals, t, sw);
+      else
+        wave_sort_tile(ranges, words, keys, vals, t, sw);
+    }
   }
   const int nh = (int)live[1], nall = nh + (int)live[2];
   if (nall == 0) return;
