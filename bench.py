@@ -71,7 +71,7 @@ GAUSS_GRAD_WRITE_BYTES = {0: 8 + 4 + 4, 1: 44}
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 186407598
+FWD_TRAFFIC_BYTES = 186406770
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
