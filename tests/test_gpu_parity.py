@@ -339,6 +339,18 @@ def test_lidar_half_turn_footprints():
     _run(TS.lidar_half_turn(), 62, "gauss3d 6400 lidar 256x32, footprints past half a turn")
 
 
+def test_two_small_pinhole_views():
+    """Two pinhole views of 48 and 24 tiles in one launch (the split camera
+    walk across views: each tile finds its view and pixel offsets), forward
+    and reverse pass against the oracle."""
+    sc = S.gauss3d(seed=46, n=20_000, width=128, height=96)
+    R1 = TS.rotation(np.random.default_rng(47))
+    sc.cams = [sc.cams[0],
+               S.Camera(S.CAM_PINHOLE, 96, 64, R1, [0.1, 0.2, 9.0], fx=120.0, fy=125.0, cx=48.0, cy=32.0,
+                        znear=0.2, zfar=100.0)]
+    _run(sc, 48, "gauss3d 20k, pinhole 128x96 + 96x64")
+
+
 def test_multiview_serial_views():
     """splat_params.serial_views = 1 (every kernel on the caller's stream, no side
     stream): the same forward outputs bit for bit as the forked call, and gradients
