@@ -367,6 +367,7 @@ __global__ __launch_bounds__(256) void k_fwd_alpha(ViewTable vt, FwdArgs A, int 
       double dx, dy;
       const float al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
       const bool hit = active & (al >= amin);
+      if (ballot64(hit) == 0) return;            // no pixel of the wave takes it: nothing changes
       const float w = (hit ? 1.0f : 0.0f) * (float)(T * (double)al);
 #pragma unroll
       for (int q = 0; q < NF4; q++) {
@@ -531,6 +532,7 @@ __global__ __launch_bounds__(LB) void k_fwd_split(ViewTable vt, FwdArgs A, int t
       else
         al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
       const bool hit = ax & (al >= amin);
+      if (ballot64(hit) == 0) return;            // no pixel of the wave takes it: nothing changes
       const float w = (hit ? 1.0f : 0.0f) * (float)(Tx * (double)al);
 #pragma unroll
       for (int ch = 0; ch < NF; ch++) Sx[ch] = __builtin_fmaf(w, s_f[ch][idx], Sx[ch]);
