@@ -527,6 +527,7 @@ __global__ __launch_bounds__(1024) void k_bwd_split(ViewTable vt, BwdArgs A, int
         else
           al = splat_alpha<false>(c, pxr, pyr, s_uv[idx], s_ab[idx], s_co[idx], amax, G, og, dx, dy);
         const bool hit = (pos < lastp) & (al >= amin);
+        if (ballot64(hit) == 0) return;          // no pixel of the wave takes it: nothing changes
         const float w = (hit ? 1.0f : 0.0f) * (float)(Pt * (double)al);
         Ax = __builtin_fmaf(w, blend_value(idx), Ax);
         Pt = hit ? Pt * (1.0 - (double)al) : Pt;
