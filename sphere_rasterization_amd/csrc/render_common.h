@@ -304,7 +304,7 @@ __device__ __forceinline__ double2 stage_uv(const ViewDev &c, const TilePix &tp,
   return make_double2(t, d.v - (double)tp.y0);
 }
 
-// Staged conic: (a/2, b) and (c/2, opacity) with power = (a dx^2 + 2 b dx dy + c dy^2) / 2.
+// Staged conic: (a/2, b) and (c/2, opacity as fp32 bits) with power = (a dx^2 + 2 b dx dy + c dy^2) / 2.
 struct Conic {
   double2 ab;
   double2 co;
@@ -313,7 +313,9 @@ struct Conic {
 __device__ __forceinline__ Conic stage_conic(const DrawRec &d) {
   Conic k;
   k.ab = make_double2(0.5 * d.a, d.b);
-  k.co = make_double2(0.5 * d.c, (double)d.w);
+  // opacity as fp32 bits in the low half of the second slot: read back without
+  // a conversion per entry
+  k.co = make_double2(0.5 * d.c, __builtin_bit_cast(double, (unsigned long long)__float_as_uint(d.w)));
   return k;
 }
 
@@ -332,7 +334,7 @@ __device__ __forceinline__ float splat_alpha(const ViewDev &c, double pxr, doubl
   }
   const double power = __builtin_fma(dx, __builtin_fma(ab.x, dx, ab.y * dy), (co.x * dy) * dy);
   G = __expf(-(float)power);
-  og = (float)co.y * G;
+  og = __uint_as_float((unsigned)__builtin_bit_cast(unsigned long long, co.y)) * G;
   return fminf(amax, og);
 }
 
