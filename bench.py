@@ -71,11 +71,11 @@ GAUSS_GRAD_WRITE_BYTES = {0: 8 + 4 + 4, 1: 44}
 # HBM bytes (read + written) per launch of the forward sphere compositor on this
 # workload, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size; they hold for the sources with this digest only.
-FWD_TRAFFIC_BYTES = 186398765
+FWD_TRAFFIC_BYTES = 186399035
 FWD_TRAFFIC_SOURCES = ("sphere_rasterization_amd/csrc/render_fwd.hip",
                        "sphere_rasterization_amd/csrc/render_common.h",
                        "sphere_rasterization_amd/csrc/splat_internal.h")
-FWD_TRAFFIC_SHA256 = "7aba0bc5c9a1790ecc500ba4a60c3579f08a435c06b6000d44808f55aa5b57e8"
+FWD_TRAFFIC_SHA256 = "818b483a06c12f81074d13769b1f6a59c185b3144b6c981626c2c4e0da705c4c"
 BIN_KERNELS = ("k_thist", "k_col_scan", "k_tscatter", "k_seg_sort", "k_tile_scan1", "k_scan_reduce", "k_scan_top",
                "k_tile_ranges", "k_fill_u32", "k_tile_count", "k_bucket")
 
